@@ -1,0 +1,209 @@
+"""ORACLE — fp64 CPU reference of the CSA / HCA hot path (test infrastructure).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The library under ``compressed_sparse_long_compress_amd``
+never imports it and shares no code with it.
+
+Thin ctypes wrappers over ``oracle.c``; every function returns fp64 (or exact
+integer) results computed by following the pages' steps in order.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build():
+    """Compile oracle.c with gcc (always recompiles)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", _SO, os.path.join(_HERE, "oracle.c"), "-lm"]
+    subprocess.check_call(cmd)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_SO):
+        build()
+    lib = ctypes.CDLL(_SO)
+    i64, i32, f64, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_void_p
+    lib.orc_bf16_to_f64.restype = f64
+    lib.orc_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.orc_e4m3_to_f64.restype = f64
+    lib.orc_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+    lib.orc_e2m1_to_f64.restype = f64
+    lib.orc_e2m1_to_f64.argtypes = [ctypes.c_uint8]
+    lib.orc_e8m0_to_f64.restype = f64
+    lib.orc_e8m0_to_f64.argtypes = [ctypes.c_uint8]
+    lib.orc_f64_to_bf16.restype = ctypes.c_uint16
+    lib.orc_f64_to_bf16.argtypes = [f64]
+    lib.orc_f64_to_e4m3.restype = ctypes.c_uint8
+    lib.orc_f64_to_e4m3.argtypes = [f64]
+    lib.orc_rope64.argtypes = [vp, f64, f64, ctypes.c_int]
+    lib.orc_compress.restype = ctypes.c_int
+    lib.orc_compress.argtypes = [vp, vp, i64, i64, i32, i32, f64, i64, vp, vp, vp]
+    lib.orc_index_scores.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, vp, vp, i64, i32, i64, vp]
+    lib.orc_topk.argtypes = [vp, i64, i64, vp, i32, i32, vp]
+    lib.orc_attend.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32, i32, vp, vp, vp, i64, vp, vp, vp, i64, i32,
+                               f64, f64, vp, vp]
+    lib.orc_index_exact_witness.restype = f64
+    lib.orc_index_exact_witness.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, vp, vp, i64, i32, i64]
+    _lib = lib
+    return lib
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+def _p(a):
+    return ctypes.c_void_p(a.ctypes.data) if a is not None else None
+
+
+# ---- scalar codecs --------------------------------------------------------
+def bf16_to_f64(h):
+    return _load().orc_bf16_to_f64(int(h))
+
+
+def e4m3_to_f64(c):
+    return _load().orc_e4m3_to_f64(int(c))
+
+
+def e2m1_to_f64(n):
+    return _load().orc_e2m1_to_f64(int(n))
+
+
+def e8m0_to_f64(b):
+    return _load().orc_e8m0_to_f64(int(b))
+
+
+def f64_to_bf16(x):
+    return _load().orc_f64_to_bf16(float(x))
+
+
+def f64_to_e4m3(x):
+    return _load().orc_f64_to_e4m3(float(x))
+
+
+def bf16_array_to_f64(a):
+    a = np.asarray(a, dtype=np.uint16)
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def e4m3_table():
+    return np.array([e4m3_to_f64(c) for c in range(256)], dtype=np.float64)
+
+
+def rope64(x, pos, base=10000.0, inverse=False):
+    v = np.array(x, dtype=np.float64).copy()
+    assert v.shape == (64,)
+    _load().orc_rope64(_p(v), float(pos), float(base), int(bool(inverse)))
+    return v
+
+
+def dequant_entries(nope, rope, scale):
+    """Stored entries -> fp64 [rows, d]."""
+    tab = e4m3_table()
+    nope = np.asarray(nope)
+    v = tab[nope] * np.asarray(scale, dtype=np.float64)[:, None]
+    return np.concatenate([v, bf16_array_to_f64(rope)], axis=1)
+
+
+# ---- pipeline steps --------------------------------------------------------
+def compress(kv, logits, tok0, m, rope_base=10000.0):
+    """kv [n_tok, d] bf16 bits, logits [n_tok] -> (nope, rope, scale) of the n_tok/m new entries, in order."""
+    kv = _c(kv, np.uint16)
+    logits = _c(logits, np.float32)
+    n_tok, d = kv.shape
+    assert tok0 % m == 0 and n_tok % m == 0 and n_tok > 0
+    nblk = n_tok // m
+    nope = np.zeros((nblk, d - 64), np.uint8)
+    rope = np.zeros((nblk, 64), np.uint16)
+    scale = np.zeros(nblk, np.float32)
+    rc = _load().orc_compress(_p(kv), _p(logits), tok0, n_tok, m, d, rope_base, nblk, _p(nope), _p(rope),
+                              _p(scale))
+    assert rc == 0
+    # entry J = tok0/m + b sits at slot J % nblk; put them back in order
+    order = (tok0 // m + np.arange(nblk)) % nblk
+    return nope[order], rope[order], scale[order]
+
+
+def compress_into(kv, logits, tok0, m, rope_base, nope, rope, scale):
+    """In-place variant: writes entry J at slot J % cap of existing arrays."""
+    kv = _c(kv, np.uint16)
+    logits = _c(logits, np.float32)
+    n_tok, d = kv.shape
+    cap = scale.shape[0]
+    assert nope.flags.c_contiguous and rope.flags.c_contiguous and scale.flags.c_contiguous
+    rc = _load().orc_compress(_p(kv), _p(logits), tok0, n_tok, m, d, rope_base, cap, _p(nope), _p(rope), _p(scale))
+    assert rc == 0
+
+
+def index_scores(iq, iq_scale, w, seq, pos, keys, key_scale, cap, m, n_cols):
+    """fp64 scores [T, n_cols] (-inf where not visible)."""
+    iq = _c(iq, np.uint8)
+    iq_scale = _c(iq_scale, np.uint8)
+    w = _c(w, np.float32)
+    seq = _c(seq, np.int32)
+    pos = _c(pos, np.int64)
+    keys = _c(keys, np.uint8)
+    key_scale = _c(key_scale, np.uint8)
+    T, h_i = w.shape
+    d_i = keys.shape[-1] * 2
+    out = np.empty((T, n_cols), np.float64)
+    _load().orc_index_scores(_p(iq), _p(iq_scale), _p(w), _p(seq), _p(pos), T, h_i, d_i, _p(keys), _p(key_scale),
+                             cap, m, n_cols, _p(out))
+    return out
+
+
+def index_exact_witness(iq, iq_scale, w, seq, pos, keys, key_scale, cap, m, n_cols):
+    """max over visible (t, j) of log2(sum|terms| / finest quantum); < 24 means exact in fp32."""
+    iq = _c(iq, np.uint8)
+    iq_scale = _c(iq_scale, np.uint8)
+    w = _c(w, np.float32)
+    seq = _c(seq, np.int32)
+    pos = _c(pos, np.int64)
+    keys = _c(keys, np.uint8)
+    key_scale = _c(key_scale, np.uint8)
+    T, h_i = w.shape
+    d_i = keys.shape[-1] * 2
+    return _load().orc_index_exact_witness(_p(iq), _p(iq_scale), _p(w), _p(seq), _p(pos), T, h_i, d_i, _p(keys),
+                                           _p(key_scale), cap, m, n_cols)
+
+
+def topk(scores, pos, m, k):
+    """scores [T, n_cols] float32 -> idx int32 [T, k] ascending, -1 padded."""
+    scores = _c(scores, np.float32)
+    pos = _c(pos, np.int64)
+    T, n_cols = scores.shape
+    idx = np.empty((T, k), np.int32)
+    _load().orc_topk(_p(scores), T, n_cols, _p(pos), m, k, _p(idx))
+    return idx
+
+
+def attend(q, seq, pos, comp, comp_cap, win, win_cap, W, m, sm_scale, rope_base=10000.0, idx=None):
+    """Attention over (selected | all visible) compressed entries + window.
+
+    q [T, H, d] bf16 bits; comp/win = (nope, rope, scale) arrays indexed by
+    seq*cap + slot.  Returns (out [T, H, d], lse [T, H]) in fp64."""
+    q = _c(q, np.uint16)
+    seq = _c(seq, np.int32)
+    pos = _c(pos, np.int64)
+    T, H, d = q.shape
+    cn, cr, cs = (_c(comp[0], np.uint8), _c(comp[1], np.uint16), _c(comp[2], np.float32))
+    wn, wr, ws = (_c(win[0], np.uint8), _c(win[1], np.uint16), _c(win[2], np.float32))
+    k = 0
+    if idx is not None:
+        idx = _c(idx, np.int32)
+        k = idx.shape[1]
+    out = np.empty((T, H, d), np.float64)
+    lse = np.empty((T, H), np.float64)
+    _load().orc_attend(_p(q), _p(seq), _p(pos), T, H, d, _p(idx), k, m, _p(cn), _p(cr), _p(cs), comp_cap, _p(wn),
+                       _p(wr), _p(ws), win_cap, W, sm_scale, rope_base, _p(out), _p(lse))
+    return out, lse

@@ -1,0 +1,415 @@
+/*
+ * ORACLE — plain, slow fp64 CPU reference of the CSA / HCA hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this code.  The library (HIP kernels and
+ * their C-ABI) never calls it and shares no code, header or table with it.
+ *
+ * Sources (pages about DeepSeek-V4):
+ *   [xmsumi]    xmsumi.com DeepSeek-V4 article: § CSA (压缩稀疏注意力),
+ *               § HCA (重度压缩注意力), § 关键技术细节 (key technical details),
+ *               § 百万Token 长上下文真实表现 (heterogeneous KV cache paragraph)
+ *   [hortopato] hortopato.cc wiki "DeepSeek-V4 — MoE nyelvmodellek milliós
+ *               kontextussal": CSA list (m=4, k=1024, window 128),
+ *               § Heavily Compressed Attention (HCA) (m'=128)
+ *   [zcldvi]    zcldvi.com V4 article, attention paragraphs (window branch in
+ *               both attentions; FP4 relevance score per compressed block;
+ *               E4M3 has two more exponent bits than E2M1)
+ *
+ * Every step follows the pages' order: compress -> index scores -> top-k ->
+ * attention over selected entries plus the sliding window (CSA), or over all
+ * compressed entries plus the window (HCA).  Where the pages leave a detail
+ * open, the reading taken is stated at the function.
+ *
+ * Parity pins: every function here is checked against closed forms,
+ * invariants, brute force or textbook/library routines by the CPU tests.
+ * Readings fixed only by convention (RoPE pairing/frequencies, the indexer
+ * formula, the FP8 scale rule, the planted-structure recipe) are
+ * "parity unpinned": no page value fixes them.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* exact decoders                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* bf16: the upper 16 bits of an IEEE binary32. */
+double orc_bf16_to_f64(uint16_t h) {
+    uint32_t b = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &b, 4);
+    return (double)f;
+}
+
+/* OCP FP8 E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits, no infinity,
+   S.1111.111 is NaN, largest finite 448, smallest subnormal 2^-9. */
+double orc_e4m3_to_f64(uint8_t c) {
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m, -9);
+    else v = ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* OCP FP4 E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit. */
+double orc_e2m1_to_f64(uint8_t nib) {
+    int s = (nib >> 3) & 1, e = (nib >> 1) & 3, m = nib & 1;
+    double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -v : v;
+}
+
+/* OCP E8M0 block scale: 2^(byte - 127); 0xFF is NaN. */
+double orc_e8m0_to_f64(uint8_t b) {
+    if (b == 0xFF) return NAN;
+    return ldexp(1.0, (int)b - 127);
+}
+
+/* ------------------------------------------------------------------------ */
+/* encoders for the compressed KV entry format                               */
+/* ------------------------------------------------------------------------ */
+
+/* x -> bf16 with round-to-nearest-even applied to the exact fp64 value. */
+uint16_t orc_f64_to_bf16(double x) {
+    if (x == 0.0) return signbit(x) ? 0x8000 : 0x0000;
+    double a = fabs(x);
+    int e;
+    frexp(a, &e);                   /* a in [2^(e-1), 2^e) */
+    int ex = e - 1;
+    if (ex < -126) ex = -126;       /* subnormal range: fixed quantum 2^-133 */
+    double q = ldexp(1.0, ex - 7);  /* bf16 keeps 8 significant bits */
+    double r = nearbyint(a / q) * q;
+    float f = (float)r;             /* exact: r has <= 9 significant bits */
+    uint32_t b;
+    memcpy(&b, &f, 4);
+    uint16_t h = (uint16_t)(b >> 16);
+    return x < 0 ? (uint16_t)(h | 0x8000) : h;
+}
+
+/* x -> E4M3FN with round-to-nearest-even, saturating to +-448 (the FP8 half
+   of the mixed-precision KV entry, [xmsumi § 关键技术细节]). */
+uint8_t orc_f64_to_e4m3(double x) {
+    double a = fabs(x);
+    uint8_t mag;
+    /* candidate grid: subnormals k*2^-9 (k<8), normals (8+k)*2^(E-10) */
+    if (a >= 448.0) {
+        mag = 0x7E;
+    } else if (a < ldexp(1.0, -6)) {
+        mag = (uint8_t)nearbyint(a * 512.0); /* 8 -> smallest normal, code 0x08 */
+    } else {
+        int e;
+        frexp(a, &e);
+        int E = e - 1;                       /* a in [2^E, 2^(E+1)) */
+        double q = ldexp(1.0, E - 3);        /* quantum in this binade */
+        double n = nearbyint(a / q);         /* 8..16 */
+        if (n >= 16.0) { n = 8.0; E += 1; }
+        int be = E + 7;
+        if (be > 15 || (be == 15 && n - 8.0 > 6.0)) mag = 0x7E;
+        else mag = (uint8_t)((be << 3) | (int)(n - 8.0));
+    }
+    if (mag == 0) return 0;
+    return x < 0 ? (uint8_t)(mag | 0x80) : mag;
+}
+
+/* ------------------------------------------------------------------------ */
+/* partial RoPE ([xmsumi § 关键技术细节]: rotary position only on the last 64   */
+/* dims of queries and KV entries, reverse compensation on the output).      */
+/* Reading: dims are paired (2i, 2i+1) inside those 64 dims, frequency        */
+/* theta_i = base^(-2i/64), angle = pos * theta_i in fp64.  parity unpinned   */
+/* beyond the invariants (norm, composition, identity at 0) the tests check.  */
+/* ------------------------------------------------------------------------ */
+void orc_rope64(double* x, double pos, double base, int inverse) {
+    for (int i = 0; i < 32; ++i) {
+        double theta = pow(base, -2.0 * i / 64.0);
+        double a = pos * theta;
+        if (inverse) a = -a;
+        double c = cos(a), s = sin(a);
+        double x0 = x[2 * i], x1 = x[2 * i + 1];
+        x[2 * i] = x0 * c - x1 * s;
+        x[2 * i + 1] = x0 * s + x1 * c;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* step 1: token compression ([xmsumi § CSA]: the KV entries of every m       */
+/* tokens merge by a weighted compression into one compressed entry;         */
+/* [hortopato] CSA list: sequence length drops to 1/m, m = 4; HCA uses        */
+/* m' = 128).                                                                */
+/*                                                                           */
+/* Readings: one scalar logit per token, weights = softmax over the m logits  */
+/* of a block; only complete blocks are compressed (the uncompressed tail    */
+/* stays in the state cache, [xmsumi § 百万Token]); the entry is roped at the  */
+/* position of the last token it covers, p_j = (j+1)m - 1; FP8 part uses one  */
+/* fp32 scale per entry, s = amax/448 over the non-RoPE dims (1 if amax = 0). */
+/*                                                                           */
+/* kv: n_tok x d bf16 tokens [tok0, tok0+n_tok); logits: n_tok floats.        */
+/* Entry J = tok0/m + b lands in slot J % cap of the outputs.                 */
+/* Returns 0, or -1 when tok0 or n_tok is not a multiple of m.                */
+/* ------------------------------------------------------------------------ */
+int orc_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t n_tok, int32_t m, int32_t d,
+                 double rope_base, int64_t cap, uint8_t* nope, uint16_t* rope, float* scale) {
+    if (m <= 0 || tok0 % m != 0 || n_tok % m != 0 || d < 64 || cap <= 0) return -1;
+    const int dn = d - 64;
+    const int64_t nblk = n_tok / m;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t b = 0; b < nblk; ++b) {
+        double* w = (double*)malloc(sizeof(double) * (size_t)m);
+        double* c = (double*)calloc((size_t)d, sizeof(double));
+        /* softmax over the block's logits */
+        double mx = -INFINITY;
+        for (int i = 0; i < m; ++i) mx = fmax(mx, (double)logits[b * m + i]);
+        double z = 0.0;
+        for (int i = 0; i < m; ++i) { w[i] = exp((double)logits[b * m + i] - mx); z += w[i]; }
+        for (int i = 0; i < m; ++i) w[i] /= z;
+        /* weighted merge */
+        for (int i = 0; i < m; ++i) {
+            const uint16_t* x = kv + (b * m + i) * (int64_t)d;
+            for (int e = 0; e < d; ++e) c[e] += w[i] * orc_bf16_to_f64(x[e]);
+        }
+        /* RoPE on the last 64 dims at the last covered token */
+        int64_t J = tok0 / m + b;
+        double pj = (double)((J + 1) * (int64_t)m - 1);
+        orc_rope64(c + dn, pj, rope_base, 0);
+        /* mixed-precision store */
+        double amax = 0.0;
+        for (int e = 0; e < dn; ++e) amax = fmax(amax, fabs(c[e]));
+        float s = amax > 0.0 ? (float)(amax / 448.0) : 1.0f;
+        int64_t slot = J % cap;
+        scale[slot] = s;
+        for (int e = 0; e < dn; ++e) nope[slot * dn + e] = orc_f64_to_e4m3(c[e] / (double)s);
+        for (int e = 0; e < 64; ++e) rope[slot * 64 + e] = orc_f64_to_bf16(c[dn + e]);
+        free(w);
+        free(c);
+    }
+    return 0;
+}
+
+/* Dequantise one stored entry (slot) into d doubles. */
+static void entry_f64(const uint8_t* nope, const uint16_t* rope, const float* scale, int dn, int64_t slot,
+                      double* out) {
+    double s = (double)scale[slot];
+    for (int e = 0; e < dn; ++e) out[e] = s * orc_e4m3_to_f64(nope[slot * dn + e]);
+    for (int e = 0; e < 64; ++e) out[dn + e] = orc_bf16_to_f64(rope[slot * 64 + e]);
+}
+
+/* number of compressed entries visible to a query at position t: complete
+   blocks only, entry j covers tokens jm .. jm+m-1 */
+static inline int64_t n_visible(int64_t t, int32_t m) { return (t + 1) / m; }
+
+/* ------------------------------------------------------------------------ */
+/* step 2: lightning-indexer scores ([xmsumi § CSA]: a lightweight indexer   */
+/* picks the most relevant compressed entries per query token;               */
+/* [xmsumi § 关键技术细节]: its internal attention runs in FP4; [zcldvi]: FP4  */
+/* relevance of each query token to each compressed block).                  */
+/*                                                                           */
+/* Reading (parity unpinned): score[t,j] = sum_h w[t,h] * max(0, <q[t,h], k_j>) */
+/* over MXFP4-dequantised vectors, one key per compressed entry; columns j  */
+/* with j >= visible(t) are -inf.  Computed exactly in fp64 and rounded once */
+/* to fp32.                                                                  */
+/*                                                                           */
+/* q: T x h_i x d_i/2 packed E2M1 (element 2i low nibble), q_scale: T x h_i x */
+/* d_i/32 E8M0, w: T x h_i, keys: rows [seq*cap + j], data d_i/2 bytes and    */
+/* d_i/32 scales per row.                                                     */
+/* ------------------------------------------------------------------------ */
+static double mx_elem(const uint8_t* data, const uint8_t* scl, int64_t row, int d_i, int c) {
+    uint8_t byte = data[row * (d_i / 2) + c / 2];
+    uint8_t nib = (c & 1) ? (byte >> 4) : (byte & 15);
+    return orc_e2m1_to_f64(nib) * orc_e8m0_to_f64(scl[row * (d_i / 32) + c / 32]);
+}
+
+void orc_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
+                      const int64_t* pos, int64_t T, int32_t h_i, int32_t d_i, const uint8_t* kdata,
+                      const uint8_t* kscale, int64_t cap, int32_t m, int64_t n_cols, double* scores) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+        double* qd = (double*)malloc(sizeof(double) * (size_t)h_i * d_i);
+        for (int h = 0; h < h_i; ++h)
+            for (int c = 0; c < d_i; ++c) qd[h * d_i + c] = mx_elem(q, q_scale, t * h_i + h, d_i, c);
+        double* kd = (double*)malloc(sizeof(double) * (size_t)d_i);
+        int64_t nv = n_visible(pos[t], m);
+        int64_t base = (int64_t)seq[t] * cap;
+        for (int64_t j = 0; j < n_cols; ++j) {
+            if (j >= nv) { scores[t * n_cols + j] = -INFINITY; continue; }
+            for (int c = 0; c < d_i; ++c) kd[c] = mx_elem(kdata, kscale, base + j, d_i, c);
+            double acc = 0.0;
+            for (int h = 0; h < h_i; ++h) {
+                double dot = 0.0;
+                for (int c = 0; c < d_i; ++c) dot += qd[h * d_i + c] * kd[c];
+                acc += (double)w[t * h_i + h] * (dot > 0.0 ? dot : 0.0);
+            }
+            scores[t * n_cols + j] = acc;
+        }
+        free(kd);
+        free(qd);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* step 3: top-k selection ([xmsumi § CSA]: top-k compressed entries per     */
+/* query token; [hortopato] CSA list: k = 1024).                              */
+/*                                                                           */
+/* Reading: among the visible columns, the min(k, visible) largest scores    */
+/* under the order (score descending, index ascending); ties go to the lower */
+/* index; output in ascending index order, padded with -1.                   */
+/* ------------------------------------------------------------------------ */
+typedef struct { float s; int32_t j; } sj_t;
+
+static int cmp_desc(const void* a, const void* b) {
+    const sj_t* x = (const sj_t*)a;
+    const sj_t* y = (const sj_t*)b;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return (x->j < y->j) ? -1 : (x->j > y->j);
+}
+
+static int cmp_i32(const void* a, const void* b) {
+    int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+    return (x > y) - (x < y);
+}
+
+void orc_topk(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos, int32_t m, int32_t k,
+              int32_t* idx) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t nv = n_visible(pos[t], m);
+        if (nv > n_cols) nv = n_cols;
+        sj_t* v = (sj_t*)malloc(sizeof(sj_t) * (size_t)(nv > 0 ? nv : 1));
+        for (int64_t j = 0; j < nv; ++j) { v[j].s = scores[t * n_cols + j]; v[j].j = (int32_t)j; }
+        qsort(v, (size_t)nv, sizeof(sj_t), cmp_desc);
+        int64_t take = nv < k ? nv : k;
+        int32_t* out = idx + t * (int64_t)k;
+        for (int64_t a = 0; a < take; ++a) out[a] = v[a].j;
+        qsort(out, (size_t)take, sizeof(int32_t), cmp_i32);
+        for (int64_t a = take; a < k; ++a) out[a] = -1;
+        free(v);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* step 4: multi-query attention ([xmsumi § CSA]: attention only over the     */
+/* selected compressed entries, plus a sliding-window branch over the most   */
+/* recent tokens; [hortopato] CSA list: window 128; [xmsumi § HCA] and        */
+/* [hortopato § HCA]: no selection, dense attention over every compressed     */
+/* entry; [zcldvi]: both attentions add the window branch).                  */
+/*                                                                           */
+/* Readings: one KV vector per entry serves as key and value (one shared KV   */
+/* head); the key set is the selected entries (idx >= 0 and visible) or, when */
+/* idx is NULL, every visible entry at ratio m, together with the raw window  */
+/* tokens max(0, t-W+1) .. t stored at slot p % win_cap of the window ring;  */
+/* duplicates are kept; one softmax over the union (what a log-sum-exp merge */
+/* of the two branches gives); the query is roped at t and the output's RoPE */
+/* dims are rotated back by -t (the reverse compensation of                  */
+/* [xmsumi § 关键技术细节]).  Empty key set -> zero output, lse = -inf.        */
+/*                                                                           */
+/* q: T x H x d bf16 (before RoPE).  out: T x H x d, lse: T x H (fp64).       */
+/* ------------------------------------------------------------------------ */
+void orc_attend(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int32_t H, int32_t d,
+                const int32_t* idx, int32_t k, int32_t m, const uint8_t* c_nope, const uint16_t* c_rope,
+                const float* c_scale, int64_t c_cap, const uint8_t* w_nope, const uint16_t* w_rope,
+                const float* w_scale, int64_t w_cap, int32_t W, double sm_scale, double rope_base, double* out,
+                double* lse) {
+    const int dn = d - 64;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t tp = pos[t];
+        int64_t nv = n_visible(tp, m);
+        int64_t cbase = (int64_t)seq[t] * c_cap, wbase = (int64_t)seq[t] * w_cap;
+        /* gather the key set */
+        int64_t lo = tp - W + 1 < 0 ? 0 : tp - W + 1;
+        int64_t n_win = W > 0 ? tp - lo + 1 : 0;
+        int64_t n_cmp_max = idx ? k : nv;
+        double* keys = (double*)malloc(sizeof(double) * (size_t)(n_cmp_max + n_win + 1) * d);
+        int64_t n = 0;
+        if (idx) {
+            for (int a = 0; a < k; ++a) {
+                int32_t j = idx[t * (int64_t)k + a];
+                if (j < 0 || j >= nv) continue;
+                entry_f64(c_nope, c_rope, c_scale, dn, cbase + j, keys + n * d);
+                ++n;
+            }
+        } else {
+            for (int64_t j = 0; j < nv; ++j) { entry_f64(c_nope, c_rope, c_scale, dn, cbase + j, keys + n * d); ++n; }
+        }
+        for (int64_t p = lo; p < lo + n_win; ++p) {
+            entry_f64(w_nope, w_rope, w_scale, dn, wbase + (p % w_cap), keys + n * d);
+            ++n;
+        }
+        double* qh = (double*)malloc(sizeof(double) * (size_t)d);
+        double* s = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        for (int h = 0; h < H; ++h) {
+            const uint16_t* qr = q + (t * H + h) * (int64_t)d;
+            for (int e = 0; e < d; ++e) qh[e] = orc_bf16_to_f64(qr[e]);
+            orc_rope64(qh + dn, (double)tp, rope_base, 0);
+            double* o = out + (t * H + h) * (int64_t)d;
+            for (int e = 0; e < d; ++e) o[e] = 0.0;
+            if (n == 0) { lse[t * H + h] = -INFINITY; continue; }
+            double mx = -INFINITY;
+            for (int64_t u = 0; u < n; ++u) {
+                double dot = 0.0;
+                for (int e = 0; e < d; ++e) dot += qh[e] * keys[u * d + e];
+                s[u] = sm_scale * dot;
+                mx = fmax(mx, s[u]);
+            }
+            double z = 0.0;
+            for (int64_t u = 0; u < n; ++u) z += exp(s[u] - mx);
+            double l = mx + log(z);
+            for (int64_t u = 0; u < n; ++u) {
+                double p = exp(s[u] - l);
+                for (int e = 0; e < d; ++e) o[e] += p * keys[u * d + e];
+            }
+            orc_rope64(o + dn, (double)tp, rope_base, 1);
+            lse[t * H + h] = l;
+        }
+        free(s);
+        free(qh);
+        free(keys);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Exactness witness for step 2: for every visible (t, j), the sum of the    */
+/* absolute values of all product terms, counted in units of the finest     */
+/* quantum any term can carry, must stay below 2^24 so every partial sum in  */
+/* any order is exact in fp32.  Returns the largest log2 of that ratio over   */
+/* the checked rows, or +inf when a head weight is not a power of two.       */
+/* ------------------------------------------------------------------------ */
+double orc_index_exact_witness(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
+                               const int64_t* pos, int64_t T, int32_t h_i, int32_t d_i, const uint8_t* kdata,
+                               const uint8_t* kscale, int64_t cap, int32_t m, int64_t n_cols) {
+    double worst = -INFINITY;
+    const int nb = d_i / 32;
+    for (int64_t t = 0; t < T; ++t)
+        for (int h = 0; h < h_i; ++h) {
+            int e;
+            double fr = frexp((double)w[t * h_i + h], &e);
+            if (fr != 0.5) return INFINITY;
+        }
+#pragma omp parallel for schedule(dynamic, 1) reduction(max : worst)
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t nv = n_visible(pos[t], m);
+        if (nv > n_cols) nv = n_cols;
+        int64_t base = (int64_t)seq[t] * cap;
+        for (int64_t j = 0; j < nv; ++j) {
+            double absum = 0.0, quantum = INFINITY;
+            for (int h = 0; h < h_i; ++h) {
+                double wh = (double)w[t * h_i + h];
+                for (int b = 0; b < nb; ++b) {
+                    double sq = orc_e8m0_to_f64(q_scale[(t * h_i + h) * nb + b]);
+                    double sk = orc_e8m0_to_f64(kscale[(base + j) * nb + b]);
+                    double unit = 0.25 * sq * sk * wh; /* E2M1 x E2M1 products are multiples of 1/4 */
+                    if (unit < quantum) quantum = unit;
+                    for (int c = b * 32; c < b * 32 + 32; ++c)
+                        absum += fabs(mx_elem(q, q_scale, t * h_i + h, d_i, c) * mx_elem(kdata, kscale, base + j, d_i, c)) * wh;
+                }
+            }
+            if (absum > 0.0) {
+                double r = log2(absum / quantum);
+                if (r > worst) worst = r;
+            }
+        }
+    }
+    return worst;
+}

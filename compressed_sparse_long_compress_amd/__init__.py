@@ -1,0 +1,247 @@
+"""libcsa Python binding: CSA / HCA attention kernels for MI355X (gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of
+``libcsa.so`` (built by ``build.py``).  PyTorch supplies device memory and the
+current stream.  There is no CPU fallback: importing this package fails
+loudly when the library is missing.
+
+Calls (same names as the C ABI in include/csa.h):
+  csa_compress, csa_index_scores, csa_topk, csa_sparse_mqa, hca_dense_mqa
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libcsa.so not found at {LIB_PATH}: build it with "
+                      "`python -m compressed_sparse_long_compress_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+CSA_OK, CSA_EINVAL, CSA_EUNSUPPORTED, CSA_EHIP, CSA_EWORKSPACE = 0, -1, -2, -3, -4
+
+
+class _Kv(ctypes.Structure):
+    _fields_ = [("nope", ctypes.c_void_p), ("rope", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("cap", ctypes.c_int64)]
+
+
+class _IdxKeys(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("cap", ctypes.c_int64)]
+
+
+_vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+_lib.csa_compress.argtypes = [_vp, _vp, _i64, _i64, _i32, _i32, _f32, _i32, _Kv, _vp]
+_lib.csa_index_scores.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _IdxKeys, _i32, _i64, _vp, _vp]
+_lib.csa_topk_workspace.restype = _sz
+_lib.csa_topk_workspace.argtypes = [_i64, _i64, _i32]
+_lib.csa_topk.argtypes = [_vp, _i64, _i64, _vp, _i32, _i32, _vp, _vp, _sz, _vp]
+_lib.csa_mqa_workspace.restype = _sz
+_lib.csa_mqa_workspace.argtypes = [_i64, _i32, _i32, _i64]
+_lib.csa_sparse_mqa.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _i32, _Kv, _Kv, _i32, _f32, _f32, _vp,
+                                _vp, _vp, _sz, _vp]
+_lib.hca_dense_mqa.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _Kv, _Kv, _i32, _f32, _f32, _vp, _vp,
+                               _vp, _sz, _vp]
+_lib.csa_last_error.restype = ctypes.c_char_p
+_lib.csa_version.restype = ctypes.c_int
+
+EXPORTS = ["csa_compress", "csa_index_scores", "csa_topk_workspace", "csa_topk", "csa_mqa_workspace",
+           "csa_sparse_mqa", "hca_dense_mqa", "csa_last_error", "csa_version"]
+
+
+class CsaError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"libcsa error {code}: {msg}")
+        self.code = code
+
+
+def _check(rc):
+    if rc != CSA_OK:
+        raise CsaError(rc, _lib.csa_last_error().decode())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def version():
+    return _lib.csa_version()
+
+
+class KvCache:
+    """Mixed-precision entries: nope uint8 [rows, d-64], rope bf16 [rows, 64], scale fp32 [rows]; rows = n_seq*cap."""
+
+    def __init__(self, nope, rope, scale, cap):
+        _need(nope, "nope", torch.uint8, 2)
+        _need(rope, "rope", torch.bfloat16, 2)
+        _need(scale, "scale", torch.float32, 1)
+        if rope.shape[1] != 64 or nope.shape[0] != rope.shape[0] or scale.shape[0] != rope.shape[0]:
+            raise ValueError("inconsistent KvCache arrays")
+        if cap <= 0 or rope.shape[0] % cap != 0:
+            raise ValueError("rows must be a multiple of cap")
+        self.nope, self.rope, self.scale, self.cap = nope, rope, scale, int(cap)
+
+    @property
+    def d(self):
+        return self.nope.shape[1] + 64
+
+    @classmethod
+    def empty(cls, n_seq, cap, d, device="cuda"):
+        rows = n_seq * cap
+        return cls(torch.zeros(rows, d - 64, dtype=torch.uint8, device=device),
+                   torch.zeros(rows, 64, dtype=torch.bfloat16, device=device),
+                   torch.zeros(rows, dtype=torch.float32, device=device), cap)
+
+    def c(self):
+        return _Kv(self.nope.data_ptr(), self.rope.data_ptr(), self.scale.data_ptr(), self.cap)
+
+
+class IndexKeys:
+    """MXFP4 indexer keys: data uint8 [rows, d_i/2], scale uint8 [rows, d_i/32]; rows = n_seq*cap."""
+
+    def __init__(self, data, scale, cap):
+        _need(data, "keys.data", torch.uint8, 2)
+        _need(scale, "keys.scale", torch.uint8, 2)
+        if data.shape[0] != scale.shape[0] or data.shape[1] != scale.shape[1] * 16:
+            raise ValueError("inconsistent IndexKeys arrays")
+        self.data, self.scale, self.cap = data, scale, int(cap)
+
+    @property
+    def d_i(self):
+        return self.data.shape[1] * 2
+
+    def c(self):
+        return _IdxKeys(self.data.data_ptr(), self.scale.data_ptr(), self.cap)
+
+
+def csa_compress(kv, logits, tok0, m, seq, out, rope_base=10000.0):
+    """Compress tokens [tok0, tok0+n_tok) (kv bf16 [n_tok, d], logits fp32 [n_tok]) into `out` (KvCache)."""
+    _need(kv, "kv", torch.bfloat16, 2)
+    _need(logits, "logits", torch.float32, 1)
+    n_tok, d = kv.shape
+    if logits.shape[0] != n_tok or d != out.d:
+        raise ValueError("kv / logits / out shapes disagree")
+    _check(_lib.csa_compress(_ptr(kv), _ptr(logits), int(tok0), int(n_tok), int(m), int(d), float(rope_base),
+                             int(seq), out.c(), _stream()))
+    return out
+
+
+def csa_index_scores(q, q_scale, w, seq, pos, keys, m, n_cols, out=None):
+    """MXFP4 indexer scores: q uint8 [T, h_i, d_i/2], q_scale uint8 [T, h_i, d_i/32], w fp32 [T, h_i] -> fp32 [T, n_cols]."""
+    _need(q, "q", torch.uint8, 3)
+    _need(q_scale, "q_scale", torch.uint8, 3)
+    _need(w, "w", torch.float32, 2)
+    _need(seq, "seq", torch.int32, 1)
+    _need(pos, "pos", torch.int64, 1)
+    T, h_i, half = q.shape
+    d_i = half * 2
+    if d_i != keys.d_i or tuple(q_scale.shape) != (T, h_i, d_i // 32) or tuple(w.shape) != (T, h_i):
+        raise ValueError("indexer query shapes disagree")
+    if seq.shape[0] != T or pos.shape[0] != T:
+        raise ValueError("seq / pos must have T entries")
+    if out is None:
+        out = torch.empty(T, n_cols, dtype=torch.float32, device=q.device)
+    _need(out, "scores", torch.float32, 2)
+    if tuple(out.shape) != (T, n_cols):
+        raise ValueError("scores must be [T, n_cols]")
+    _check(_lib.csa_index_scores(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(seq), _ptr(pos), T, h_i, d_i, keys.c(), int(m),
+                                 int(n_cols), _ptr(out), _stream()))
+    return out
+
+
+def csa_topk_workspace(T, n_cols, k):
+    return int(_lib.csa_topk_workspace(int(T), int(n_cols), int(k)))
+
+
+def csa_topk(scores, pos, m, k, out=None, ws=None):
+    """Top-k per row (score desc, index asc) in ascending index order, -1 padded -> int32 [T, k]."""
+    _need(scores, "scores", torch.float32, 2)
+    _need(pos, "pos", torch.int64, 1)
+    T, n_cols = scores.shape
+    if out is None:
+        out = torch.empty(T, k, dtype=torch.int32, device=scores.device)
+    _need(out, "idx", torch.int32, 2)
+    need = csa_topk_workspace(T, n_cols, k)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    ws_bytes = ws.numel() if ws is not None else 0
+    _check(_lib.csa_topk(_ptr(scores), T, n_cols, _ptr(pos), int(m), int(k), _ptr(out), _ptr(ws), ws_bytes,
+                         _stream()))
+    return out
+
+
+def csa_mqa_workspace(T, H, d, max_keys):
+    return int(_lib.csa_mqa_workspace(int(T), int(H), int(d), int(max_keys)))
+
+
+def _mqa_outputs(q, out, lse):
+    T, H, d = q.shape
+    if out is None:
+        out = torch.empty(T, H, d, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty(T, H, dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, 3)
+    _need(lse, "lse", torch.float32, 2)
+    return out, lse
+
+
+def _win(win, comp):
+    return win.c() if win is not None else _Kv(None, None, None, 1)
+
+
+def csa_sparse_mqa(q, seq, pos, idx, m, comp, win, window, sm_scale, rope_base=10000.0, out=None, lse=None, ws=None):
+    """CSA attention over selected entries (idx int32 [T, k]) plus the window -> (out fp32 [T,H,d], lse fp32 [T,H])."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(seq, "seq", torch.int32, 1)
+    _need(pos, "pos", torch.int64, 1)
+    _need(idx, "idx", torch.int32, 2)
+    T, H, d = q.shape
+    k = idx.shape[1]
+    out, lse = _mqa_outputs(q, out, lse)
+    need = csa_mqa_workspace(T, H, d, k + window)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = ws.numel() if ws is not None else 0
+    _check(_lib.csa_sparse_mqa(_ptr(q), _ptr(seq), _ptr(pos), T, H, d, _ptr(idx), k, int(m), comp.c(), _win(win, comp),
+                               int(window), float(sm_scale), float(rope_base), _ptr(out), _ptr(lse), _ptr(ws),
+                               ws_bytes, _stream()))
+    return out, lse
+
+
+def hca_dense_mqa(q, seq, pos, m, max_vis, comp, win, window, sm_scale, rope_base=10000.0, out=None, lse=None,
+                  ws=None):
+    """HCA attention over every visible compressed entry plus the window -> (out, lse)."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(seq, "seq", torch.int32, 1)
+    _need(pos, "pos", torch.int64, 1)
+    T, H, d = q.shape
+    out, lse = _mqa_outputs(q, out, lse)
+    need = csa_mqa_workspace(T, H, d, max_vis + window)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = ws.numel() if ws is not None else 0
+    _check(_lib.hca_dense_mqa(_ptr(q), _ptr(seq), _ptr(pos), T, H, d, int(m), int(max_vis), comp.c(),
+                              _win(win, comp), int(window), float(sm_scale), float(rope_base), _ptr(out), _ptr(lse),
+                              _ptr(ws), ws_bytes, _stream()))
+    return out, lse

@@ -1,0 +1,172 @@
+// libcsa C ABI: argument validation, launch selection and error reporting.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/csa.h"
+#include "csa_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return CSA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(CSA_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_kv(const csa_kv_t& kv, int d, const char* what, const char* fn) {
+    if (!kv.nope || !kv.rope || !kv.scale) return fail(CSA_EINVAL, "%s: %s has a null array", fn, what);
+    if (kv.cap <= 0) return fail(CSA_EINVAL, "%s: %s.cap must be positive", fn, what);
+    if (!aligned16(kv.nope) || !aligned16(kv.rope))
+        return fail(CSA_EINVAL, "%s: %s.nope / %s.rope must be 16-byte aligned", fn, what, what);
+    if (((uintptr_t)kv.scale & 3u) != 0) return fail(CSA_EINVAL, "%s: %s.scale must be 4-byte aligned", fn, what);
+    (void)d;
+    return CSA_OK;
+}
+
+csa::KvView view(const csa_kv_t& kv) { return csa::KvView{kv.nope, kv.rope, kv.scale, kv.cap}; }
+
+int check_mqa_common(const char* fn, const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int32_t H,
+                     int32_t d, int32_t m, const csa_kv_t& comp, const csa_kv_t& win, int32_t window, float* out,
+                     float* lse) {
+    if (T < 0) return fail(CSA_EINVAL, "%s: T must be >= 0", fn);
+    if (T > 0 && (!q || !seq || !pos || !out || !lse)) return fail(CSA_EINVAL, "%s: null pointer argument", fn);
+    if (d != 128 && d != 512) return fail(CSA_EUNSUPPORTED, "%s: d=%d unsupported (128 or 512)", fn, d);
+    if (H != 16 && H != 32 && H != 64) return fail(CSA_EUNSUPPORTED, "%s: H=%d unsupported (16, 32, 64)", fn, H);
+    if (m < 1) return fail(CSA_EINVAL, "%s: m must be >= 1", fn);
+    if (window < 0 || window > 1024) return fail(CSA_EUNSUPPORTED, "%s: window=%d outside 0..1024", fn, window);
+    if (!aligned16(q) || !aligned16(out)) return fail(CSA_EINVAL, "%s: q and out must be 16-byte aligned", fn);
+    if (int rc = check_kv(comp, d, "comp", fn)) return rc;
+    if (window > 0) {
+        if (int rc = check_kv(win, d, "win", fn)) return rc;
+        if (win.cap < window) return fail(CSA_EINVAL, "%s: win.cap (%lld) < window (%d)", fn, (long long)win.cap, window);
+    }
+    return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa_last_error(void) { return g_err; }
+
+int csa_version(void) { return CSA_VERSION; }
+
+int csa_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t n_tok, int32_t m, int32_t d,
+                 float rope_base, int32_t seq, csa_kv_t out, csa_stream_t stream) {
+    const char* fn = "csa_compress";
+    if (m < 1 || m > 1024) return fail(CSA_EUNSUPPORTED, "%s: m=%d outside 1..1024", fn, m);
+    if (d != 128 && d != 512) return fail(CSA_EUNSUPPORTED, "%s: d=%d unsupported (128 or 512)", fn, d);
+    if (tok0 < 0 || n_tok < 0) return fail(CSA_EINVAL, "%s: tok0 and n_tok must be >= 0", fn);
+    if (tok0 % m != 0 || n_tok % m != 0)
+        return fail(CSA_EINVAL, "%s: tok0 (%lld) and n_tok (%lld) must be multiples of m (%d): only complete blocks "
+                    "are compressed", fn, (long long)tok0, (long long)n_tok, m);
+    if (seq < 0) return fail(CSA_EINVAL, "%s: seq must be >= 0", fn);
+    if (!(rope_base > 0.f)) return fail(CSA_EINVAL, "%s: rope_base must be positive", fn);
+    if (n_tok == 0) return ok();
+    if (!kv || !logits) return fail(CSA_EINVAL, "%s: null kv or logits", fn);
+    if (!aligned16(kv)) return fail(CSA_EINVAL, "%s: kv must be 16-byte aligned", fn);
+    if (int rc = check_kv(out, d, "out", fn)) return rc;
+    if (n_tok / m > out.cap)
+        return fail(CSA_EINVAL, "%s: %lld new entries exceed out.cap (%lld): slots would collide", fn,
+                    (long long)(n_tok / m), (long long)out.cap);
+    hipError_t e = csa::launch_compress(kv, logits, tok0, n_tok, m, d, (double)rope_base, (int64_t)seq * out.cap,
+                                        out.cap, out.nope, out.rope, out.scale, (hipStream_t)stream);
+    return hip_status(e, fn);
+}
+
+int csa_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
+                     const int64_t* pos, int64_t T, int32_t h_i, int32_t d_i, csa_index_keys_t keys, int32_t m,
+                     int64_t n_cols, float* scores, csa_stream_t stream) {
+    const char* fn = "csa_index_scores";
+    if (T < 0 || n_cols < 0) return fail(CSA_EINVAL, "%s: T and n_cols must be >= 0", fn);
+    if (h_i != 4 && h_i != 8) return fail(CSA_EUNSUPPORTED, "%s: h_i=%d unsupported (4 or 8)", fn, h_i);
+    if (d_i != 64 && d_i != 128) return fail(CSA_EUNSUPPORTED, "%s: d_i=%d unsupported (64 or 128)", fn, d_i);
+    if (m < 1) return fail(CSA_EINVAL, "%s: m must be >= 1", fn);
+    if (T == 0 || n_cols == 0) return ok();
+    if (!q || !q_scale || !w || !seq || !pos || !keys.data || !keys.scale || !scores)
+        return fail(CSA_EINVAL, "%s: null pointer argument", fn);
+    if (keys.cap < n_cols) return fail(CSA_EINVAL, "%s: n_cols (%lld) > keys.cap (%lld)", fn, (long long)n_cols,
+                                       (long long)keys.cap);
+    if (!aligned16(q) || !aligned16(keys.data)) return fail(CSA_EINVAL, "%s: q and keys.data must be 16-byte aligned", fn);
+    hipError_t e = csa::launch_index_scores(q, q_scale, w, seq, pos, T, h_i, d_i, keys.data, keys.scale, keys.cap, m,
+                                            n_cols, scores, (hipStream_t)stream);
+    return hip_status(e, fn);
+}
+
+size_t csa_topk_workspace(int64_t T, int64_t n_cols, int32_t k) { return csa::topk_workspace_bytes(T, n_cols, k); }
+
+int csa_topk(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos, int32_t m, int32_t k, int32_t* idx,
+             void* ws, size_t ws_bytes, csa_stream_t stream) {
+    const char* fn = "csa_topk";
+    if (T < 0 || n_cols < 0) return fail(CSA_EINVAL, "%s: T and n_cols must be >= 0", fn);
+    if (k < 1 || k > 2048) return fail(CSA_EUNSUPPORTED, "%s: k=%d outside 1..2048", fn, k);
+    if (n_cols >= ((int64_t)1 << 31)) return fail(CSA_EUNSUPPORTED, "%s: n_cols must be < 2^31", fn);
+    if (m < 1) return fail(CSA_EINVAL, "%s: m must be >= 1", fn);
+    if (T == 0) return ok();
+    if (!scores || !pos || !idx) return fail(CSA_EINVAL, "%s: null pointer argument", fn);
+    const size_t need = csa::topk_workspace_bytes(T, n_cols, k);
+    if (ws_bytes < need || (need > 0 && !ws))
+        return fail(CSA_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+    hipError_t e = csa::launch_topk(scores, T, n_cols, pos, m, k, idx, ws, (hipStream_t)stream);
+    return hip_status(e, fn);
+}
+
+size_t csa_mqa_workspace(int64_t T, int32_t H, int32_t d, int64_t max_keys) {
+    return csa::mqa_workspace_bytes(T, H, d, max_keys);
+}
+
+int csa_sparse_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int32_t H, int32_t d,
+                   const int32_t* idx, int32_t k, int32_t m, csa_kv_t comp, csa_kv_t win, int32_t window,
+                   float sm_scale, float rope_base, float* out, float* lse, void* ws, size_t ws_bytes,
+                   csa_stream_t stream) {
+    const char* fn = "csa_sparse_mqa";
+    if (int rc = check_mqa_common(fn, q, seq, pos, T, H, d, m, comp, win, window, out, lse)) return rc;
+    if (k < 1 || k > 2048) return fail(CSA_EUNSUPPORTED, "%s: k=%d outside 1..2048", fn, k);
+    if (T > 0 && !idx) return fail(CSA_EINVAL, "%s: null idx", fn);
+    if (!(rope_base > 0.f)) return fail(CSA_EINVAL, "%s: rope_base must be positive", fn);
+    if (T == 0) return ok();
+    const int64_t max_keys = (int64_t)k + window;
+    const size_t need = csa::mqa_workspace_bytes(T, H, d, max_keys);
+    if (ws_bytes < need || (need > 0 && !ws))
+        return fail(CSA_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+    if (need > 0 && !aligned16(ws)) return fail(CSA_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+    hipError_t e = csa::launch_mqa(q, seq, pos, T, H, d, idx, k, m, max_keys, view(comp), view(win), window, sm_scale,
+                                   (double)rope_base, out, lse, ws, (hipStream_t)stream);
+    return hip_status(e, fn);
+}
+
+int hca_dense_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int32_t H, int32_t d,
+                  int32_t m, int64_t max_vis, csa_kv_t comp, csa_kv_t win, int32_t window, float sm_scale,
+                  float rope_base, float* out, float* lse, void* ws, size_t ws_bytes, csa_stream_t stream) {
+    const char* fn = "hca_dense_mqa";
+    if (int rc = check_mqa_common(fn, q, seq, pos, T, H, d, m, comp, win, window, out, lse)) return rc;
+    if (max_vis < 1) return fail(CSA_EINVAL, "%s: max_vis must be >= 1", fn);
+    if (!(rope_base > 0.f)) return fail(CSA_EINVAL, "%s: rope_base must be positive", fn);
+    if (T == 0) return ok();
+    const int64_t max_keys = max_vis + window;
+    const size_t need = csa::mqa_workspace_bytes(T, H, d, max_keys);
+    if (ws_bytes < need || (need > 0 && !ws))
+        return fail(CSA_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+    if (need > 0 && !aligned16(ws)) return fail(CSA_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+    hipError_t e = csa::launch_mqa(q, seq, pos, T, H, d, nullptr, 0, m, max_keys, view(comp), view(win), window,
+                                   sm_scale, (double)rope_base, out, lse, ws, (hipStream_t)stream);
+    return hip_status(e, fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,155 @@
+// csa_compress kernel: weighted merge of m-token blocks into mixed-precision
+// entries.  One wave per entry; every lane owns D/64 consecutive dims, so a
+// token row is read as one coalesced 64-lane load (16 B per lane at D = 512).
+//
+// The merge, RoPE and scale run in fp64 and the FP8 / bf16 roundings are
+// taken from the fp64 values (round-to-odd into fp32, then the hardware
+// nearest-even conversion).  With bf16 tokens, value / (amax/448) lands on
+// an E4M3 rounding midpoint up to the last fp32 bit surprisingly often, so
+// an fp32 quotient would round those ties the wrong way.  The kernel is
+// bound by HBM traffic, so the fp64 arithmetic costs nothing measurable.
+#include "csa_device.hpp"
+#include "csa_internal.hpp"
+
+namespace csa {
+
+constexpr int kMaxM = 1024;
+
+// fp64 -> fp32 rounding to odd: a later round-to-nearest-even to any format
+// with at most 22 significant bits then equals rounding the fp64 value
+// directly (no double-rounding ties).
+__device__ __forceinline__ float f64_to_f32_odd(double d) {
+    float f = (float)d;
+    if ((double)f != d && f != 0.f) {
+        uint32_t b = __float_as_uint(f);
+        if ((b & 1u) == 0) b += fabs((double)f) < fabs(d) ? 1 : -1;
+        f = __uint_as_float(b);
+    }
+    return f;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ kv, const float* __restrict__ logits,
+                                                  int64_t tok0, int64_t n_blk, int m, double base, int64_t row0,
+                                                  int64_t cap, uint8_t* __restrict__ nope, uint16_t* __restrict__ rope,
+                                                  float* __restrict__ scale) {
+    constexpr int DN = D - 64;
+    constexpr int PER = D / 64;  // dims per lane (2 or 8)
+    __shared__ double wbuf[4][kMaxM];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t b = (int64_t)blockIdx.x * 4 + wv;
+    if (b >= n_blk) return;
+    const float* lg = logits + b * m;
+    const uint16_t* x = kv + b * m * (int64_t)D + lane * PER;
+    double* wb = wbuf[wv];
+
+    // block softmax weights in fp64: exp terms by lanes, their sum in token order
+    double mx = -INFINITY;
+    for (int i = 0; i < m; ++i) mx = fmax(mx, (double)lg[i]);
+    for (int i = lane; i < m; i += 64) wb[i] = exp((double)lg[i] - mx);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    double z = 0.0;
+    for (int i = 0; i < m; ++i) z = __dadd_rn(z, wb[i]);
+
+    // weighted merge in fp64, tokens in order, no fused multiply-add
+    double c[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) c[e] = 0.0;
+    constexpr int UN = 8;  // token rows in flight per lane
+    for (int i0 = 0; i0 < m; i0 += UN) {
+        uint16_t v[UN][PER];
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            if (i0 + u < m) {
+                if constexpr (PER == 8) {
+                    *(v4i*)v[u] = *(const v4i*)(x + (int64_t)(i0 + u) * D);
+                } else {
+                    uint32_t raw = *(const uint32_t*)(x + (int64_t)(i0 + u) * D);
+                    v[u][0] = (uint16_t)raw;
+                    v[u][1] = (uint16_t)(raw >> 16);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            if (i0 + u < m) {
+                const double wi = wb[i0 + u] / z;
+#pragma unroll
+                for (int e = 0; e < PER; ++e)
+                    c[e] = __dadd_rn(c[e], __dmul_rn(wi, (double)bf16_bits_to_f32(v[u][e])));
+            }
+        }
+    }
+
+    const int64_t J = tok0 / m + b;
+    const int dim0 = lane * PER;
+    const bool is_rope = dim0 >= DN;
+
+    // RoPE on the last 64 dims at the last covered token, fp64
+    if (is_rope) {
+        const double p = (double)((J + 1) * (int64_t)m - 1);
+#pragma unroll
+        for (int e = 0; e < PER; e += 2) {
+            const double theta = pow(base, -2.0 * (double)((dim0 - DN + e) >> 1) / 64.0);
+            const double a = __dmul_rn(p, theta);
+            const double cs = cos(a), sn = sin(a);
+            const double x0 = c[e], x1 = c[e + 1];
+            c[e] = __dsub_rn(__dmul_rn(x0, cs), __dmul_rn(x1, sn));
+            c[e + 1] = __dadd_rn(__dmul_rn(x0, sn), __dmul_rn(x1, cs));
+        }
+    }
+
+    // per-entry FP8 scale over the non-RoPE dims
+    double am = 0.0;
+    if (!is_rope) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) am = fmax(am, fabs(c[e]));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) am = fmax(am, __shfl_xor(am, o));
+    const float s = am > 0.0 ? (float)(am / 448.0) : 1.0f;
+
+    const int64_t row = row0 + (J % cap);
+    if (is_rope) {
+        uint16_t r[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) r[e] = f32_to_bf16_bits(f64_to_f32_odd(c[e]));
+        uint16_t* dst = rope + row * 64 + (dim0 - DN);
+        if constexpr (PER == 8) *(v4i*)dst = *(const v4i*)r;
+        else *(uint32_t*)dst = (uint32_t)r[0] | ((uint32_t)r[1] << 16);
+    } else {
+        uint16_t half[PER / 2];
+#pragma unroll
+        for (int e = 0; e < PER; e += 2) {
+            float a0 = fminf(fmaxf(f64_to_f32_odd(c[e] / (double)s), -448.f), 448.f);
+            float a1 = fminf(fmaxf(f64_to_f32_odd(c[e + 1] / (double)s), -448.f), 448.f);
+            half[e / 2] = (uint16_t)__builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+        }
+        uint8_t* dst = nope + row * DN + dim0;
+        if constexpr (PER == 8) {
+            *(uint2*)dst = make_uint2((uint32_t)half[0] | ((uint32_t)half[1] << 16),
+                                      (uint32_t)half[2] | ((uint32_t)half[3] << 16));
+        } else {
+            *(uint16_t*)dst = half[0];
+        }
+    }
+    if (lane == 0) scale[row] = s;
+}
+
+hipError_t launch_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t n_tok, int m, int d,
+                           double base, int64_t row0, int64_t cap, uint8_t* nope, uint16_t* rope, float* scale,
+                           hipStream_t st) {
+    const int64_t n_blk = n_tok / m;
+    if (n_blk == 0) return hipSuccess;
+    dim3 grid((unsigned)((n_blk + 3) / 4)), block(256);
+    if (d == 512)
+        hipLaunchKernelGGL(k_compress<512>, grid, block, 0, st, kv, logits, tok0, n_blk, m, base, row0, cap, nope,
+                           rope, scale);
+    else
+        hipLaunchKernelGGL(k_compress<128>, grid, block, 0, st, kv, logits, tok0, n_blk, m, base, row0, cap, nope,
+                           rope, scale);
+    return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,0 +1,289 @@
+// csa_index_scores kernels: lightning-indexer scores with MXFP4 scaled MFMA.
+//
+// score[t][j] = sum_h w[t][h] * max(0, <q[t][h], key_j>), -inf where j is not
+// yet visible to t.  Both operands are E2M1 with E8M0 block-32 scales, fed
+// straight to v_mfma_scale_f32_*_f8f6f4 (format 4 = E2M1 on both sides), so
+// the per-block scaling happens inside the matrix core.
+//
+// Two kernels:
+//   k_index_rows  few query rows (decode): MFMA rows = heads of one query,
+//                 columns = 16 keys per 16x16x128 MFMA; the run is bound by
+//                 streaming the MXFP4 keys from HBM (68 B per key at d_i=128).
+//   k_index_gemm  many query rows sharing a sequence (prefill): MFMA rows =
+//                 (query, head) pairs, 32 per 32x32x64 MFMA, 4 row tiles per
+//                 wave so each key fragment feeds 4-8 MFMAs.
+#include "csa_device.hpp"
+#include "csa_internal.hpp"
+
+namespace csa {
+
+__device__ __forceinline__ v8i frag16(const uint8_t* p) {
+    v4i x = *(const v4i*)p;
+    v8i r = {x[0], x[1], x[2], x[3], 0, 0, 0, 0};
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// decode: grid (key chunks, T), 4 waves; each wave streams tiles of 16 keys
+// ---------------------------------------------------------------------------
+template <int DI>
+__global__ __launch_bounds__(256) void k_index_rows(const uint8_t* __restrict__ q, const uint8_t* __restrict__ q_scale,
+                                                    const float* __restrict__ w, const int32_t* __restrict__ seq,
+                                                    const int64_t* __restrict__ pos, int h_i,
+                                                    const uint8_t* __restrict__ kdata,
+                                                    const uint8_t* __restrict__ kscale, int64_t kcap, int m,
+                                                    int64_t n_cols, int64_t chunk, float* __restrict__ scores) {
+    constexpr int KB = DI / 2;   // bytes per key
+    constexpr int NB = DI / 32;  // scale blocks per key
+    constexpr int U = 8;         // tiles in flight per wave
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t t = blockIdx.y;
+    const int r = lane & 15, g = lane >> 4;
+
+    v8i a = {0, 0, 0, 0, 0, 0, 0, 0};
+    int sa = 127;
+    if (r < h_i && g < NB) {
+        a = frag16(q + (t * h_i + r) * KB + g * 16);
+        sa = q_scale[(t * h_i + r) * NB + g];
+    }
+    float wr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int h = 4 * g + i;
+        wr[i] = h < h_i ? w[t * h_i + h] : 0.f;
+    }
+    int64_t nv = (pos[t] + 1) / m;
+    if (nv > n_cols) nv = n_cols;
+    const int64_t base = (int64_t)seq[t] * kcap;
+    const int64_t c0 = (int64_t)blockIdx.x * chunk;
+    const int64_t c1 = c0 + chunk < n_cols ? c0 + chunk : n_cols;
+    float* out = scores + t * n_cols;
+
+    for (int64_t j0 = c0 + (int64_t)wave * 16 * U; j0 < c1; j0 += 4 * 16 * U) {
+        v8i b[U];
+        int sb[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t j = j0 + u * 16 + r;
+            if (j < nv && g < NB) {
+                b[u] = frag16(kdata + (base + j) * KB + g * 16);
+                sb[u] = kscale[(base + j) * NB + g];
+            } else {
+                b[u] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+                sb[u] = 127;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            v4f acc = {0.f, 0.f, 0.f, 0.f};
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[u], acc, 4, 4, 0, sa, 0, sb[u]);
+            float p = wr[0] * fmaxf(acc[0], 0.f);
+            p = fmaf(wr[1], fmaxf(acc[1], 0.f), p);
+            p = fmaf(wr[2], fmaxf(acc[2], 0.f), p);
+            p = fmaf(wr[3], fmaxf(acc[3], 0.f), p);
+            p += __shfl_xor(p, 16);
+            p += __shfl_xor(p, 32);
+            const int64_t j = j0 + u * 16 + lane;
+            if (lane < 16 && j < c1) out[j] = j < nv ? p : -INFINITY;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// prefill: grid (key chunks, query tiles).  A row tile = 32 (query, head) rows
+// = 32/HI queries; each wave owns NA row tiles; keys stream 32 per step.
+// Rows of a wave that belong to different sequences are processed in one pass
+// per distinct sequence (a single pass when the batch is one sequence).
+// ---------------------------------------------------------------------------
+template <int DI, int HI>
+__global__ __launch_bounds__(256) void k_index_gemm(const uint8_t* __restrict__ q, const uint8_t* __restrict__ q_scale,
+                                                    const float* __restrict__ w, const int32_t* __restrict__ seq,
+                                                    const int64_t* __restrict__ pos, int64_t T,
+                                                    const uint8_t* __restrict__ kdata,
+                                                    const uint8_t* __restrict__ kscale, int64_t kcap, int m,
+                                                    int64_t n_cols, int64_t chunk, float* __restrict__ scores) {
+    constexpr int KB = DI / 2, NB = DI / 32;
+    constexpr int KS = DI / 64;       // 32x32x64 MFMA steps per score
+    constexpr int QA = 32 / HI;       // queries per row tile
+    constexpr int NA = 4;             // row tiles per wave
+    constexpr int QW = QA * NA;       // queries per wave (16 or 32)
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 31, g2 = lane >> 5;
+    const int64_t tq0 = ((int64_t)blockIdx.y * 4 + wave) * QW;  // first query of this wave
+    if (tq0 >= T) return;
+    const int64_t c0 = (int64_t)blockIdx.x * chunk;
+    const int64_t c1 = c0 + chunk < n_cols ? c0 + chunk : n_cols;
+
+    uint32_t todo = 0;
+    for (int i = 0; i < QW; ++i)
+        if (tq0 + i < T) todo |= 1u << i;
+
+    while (todo) {
+        const int first = __builtin_ctz(todo);
+        const int32_t s = seq[tq0 + first];
+        uint32_t mask = 0;
+        for (int i = 0; i < QW; ++i)
+            if (((todo >> i) & 1u) && seq[tq0 + i] == s) mask |= 1u << i;
+        todo &= ~mask;
+
+        // A fragments (rows of other sequences zeroed) and head weights
+        v8i a[NA][KS];
+        int sa[NA][KS];
+        float wt[NA][16];
+        int64_t nvq[NA][4];  // visible count per stored query slot
+        int64_t nv_max = 0, nv_min = INT64_MAX;
+#pragma unroll
+        for (int at = 0; at < NA; ++at) {
+            const int qi = at * QA + r / HI, h = r % HI;
+            const int64_t t = tq0 + qi;
+            const bool live = (mask >> qi) & 1u;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int blk = 2 * ks + g2;
+                if (live) {
+                    a[at][ks] = frag16(q + (t * HI + h) * KB + blk * 16);
+                    sa[at][ks] = q_scale[(t * HI + h) * NB + blk];
+                } else {
+                    a[at][ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+                    sa[at][ks] = 127;
+                }
+            }
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int row = 8 * (rr / 4) + 4 * g2 + (rr % 4);
+                const int qj = at * QA + row / HI;
+                wt[at][rr] = ((mask >> qj) & 1u) ? w[(tq0 + qj) * HI + row % HI] : 0.f;
+            }
+            for (int i = 0; i < 4; ++i) {
+                // stored query slots of this lane: HI=8 -> queries 2*g2+i' (i'<2 used), HI=4 -> 2*i+g2
+                const int qj = at * QA + (HI == 8 ? (i < 2 ? 2 * g2 + i : 0) : 2 * i + g2);
+                int64_t nv = -1;
+                if (((mask >> qj) & 1u) && (HI == 4 || i < 2)) {
+                    nv = (pos[tq0 + qj] + 1) / m;
+                    if (nv > n_cols) nv = n_cols;
+                }
+                nvq[at][i] = nv;
+            }
+        }
+        for (int i = 0; i < QW; ++i)
+            if ((mask >> i) & 1u) {
+                int64_t nv = (pos[tq0 + i] + 1) / m;
+                if (nv > n_cols) nv = n_cols;
+                nv_max = nv > nv_max ? nv : nv_max;
+                nv_min = nv < nv_min ? nv : nv_min;
+            }
+        const int64_t base = (int64_t)s * kcap;
+
+        for (int64_t j0 = c0; j0 < c1; j0 += 32) {
+            const int64_t j = j0 + r;
+            if (j0 >= nv_max) {
+                // nothing visible in this tile for any live query of the pass
+#pragma unroll
+                for (int at = 0; at < NA; ++at)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (nvq[at][i] >= 0 && j < c1) {
+                            const int qj = at * QA + (HI == 8 ? 2 * g2 + i : 2 * i + g2);
+                            scores[(tq0 + qj) * n_cols + j] = -INFINITY;
+                        }
+                continue;
+            }
+            v8i b[KS];
+            int sb[KS];
+            const bool kload = j < nv_max;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int blk = 2 * ks + g2;
+                if (kload) {
+                    b[ks] = frag16(kdata + (base + j) * KB + blk * 16);
+                    sb[ks] = kscale[(base + j) * NB + blk];
+                } else {
+                    b[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+                    sb[ks] = 127;
+                }
+            }
+#pragma unroll
+            for (int at = 0; at < NA; ++at) {
+                v16f acc = {};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[at][ks], b[ks], acc, 4, 4, 0, sa[at][ks], 0,
+                                                                          sb[ks]);
+                float part[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float p = wt[at][4 * i] * fmaxf(acc[4 * i], 0.f);
+                    p = fmaf(wt[at][4 * i + 1], fmaxf(acc[4 * i + 1], 0.f), p);
+                    p = fmaf(wt[at][4 * i + 2], fmaxf(acc[4 * i + 2], 0.f), p);
+                    p = fmaf(wt[at][4 * i + 3], fmaxf(acc[4 * i + 3], 0.f), p);
+                    part[i] = p;
+                }
+                if constexpr (HI == 8) {
+                    // query i of the tile = regs 4i..4i+3; heads split over lane halves
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) part[i] += __shfl_xor(part[i], 32);
+                    // lanes < 32 store queries 0,1; lanes >= 32 store queries 2,3
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const int64_t nv = nvq[at][i];
+                        const float v = g2 ? part[2 + i] : part[i];
+                        if (nv >= 0 && j < c1) {
+                            const int qj = at * QA + 2 * g2 + i;
+                            scores[(tq0 + qj) * n_cols + j] = j < nv ? v : -INFINITY;
+                        }
+                    }
+                } else {
+                    // query 2i+g2 complete in regs 4i..4i+3
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int64_t nv = nvq[at][i];
+                        if (nv >= 0 && j < c1) {
+                            const int qj = at * QA + 2 * i + g2;
+                            scores[(tq0 + qj) * n_cols + j] = j < nv ? part[i] : -INFINITY;
+                        }
+                    }
+                }
+            }
+        }
+        (void)nv_min;
+    }
+}
+
+hipError_t launch_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
+                               const int64_t* pos, int64_t T, int h_i, int d_i, const uint8_t* kdata,
+                               const uint8_t* kscale, int64_t kcap, int m, int64_t n_cols, float* scores,
+                               hipStream_t st) {
+    if (T == 0 || n_cols == 0) return hipSuccess;
+    if (T <= 64) {
+        // aim for >= 1024 workgroups; each wave handles 128 keys per step
+        int64_t chunk = (n_cols * T + 1023) / 1024;
+        chunk = ((chunk + 511) / 512) * 512;
+        if (chunk < 512) chunk = 512;
+        if (chunk > 16384) chunk = 16384;
+        dim3 grid((unsigned)((n_cols + chunk - 1) / chunk), (unsigned)T), block(256);
+        if (d_i == 128)
+            hipLaunchKernelGGL(k_index_rows<128>, grid, block, 0, st, q, q_scale, w, seq, pos, h_i, kdata, kscale,
+                               kcap, m, n_cols, chunk, scores);
+        else
+            hipLaunchKernelGGL(k_index_rows<64>, grid, block, 0, st, q, q_scale, w, seq, pos, h_i, kdata, kscale, kcap,
+                               m, n_cols, chunk, scores);
+        return hipGetLastError();
+    }
+    const int qwg = 4 * 4 * (32 / h_i);  // queries per workgroup
+    const int64_t qtiles = (T + qwg - 1) / qwg;
+    int64_t chunk = (n_cols * qtiles + 1023) / 1024;
+    chunk = ((chunk + 31) / 32) * 32;
+    if (chunk < 256) chunk = 256;
+    dim3 grid((unsigned)((n_cols + chunk - 1) / chunk), (unsigned)qtiles), block(256);
+#define CSA_GEMM(DI, HI)                                                                                          \
+    hipLaunchKernelGGL((k_index_gemm<DI, HI>), grid, block, 0, st, q, q_scale, w, seq, pos, T, kdata, kscale, kcap, \
+                       m, n_cols, chunk, scores)
+    if (d_i == 128 && h_i == 8) CSA_GEMM(128, 8);
+    else if (d_i == 128 && h_i == 4) CSA_GEMM(128, 4);
+    else if (d_i == 64 && h_i == 8) CSA_GEMM(64, 8);
+    else CSA_GEMM(64, 4);
+#undef CSA_GEMM
+    return hipGetLastError();
+}
+
+}  // namespace csa

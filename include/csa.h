@@ -1,0 +1,220 @@
+/*
+ * libcsa — Compressed Sparse Attention (CSA) and Heavily Compressed Attention
+ * (HCA) for AMD MI355X (gfx950), as a C ABI.
+ *
+ * The method (pages about DeepSeek-V4):
+ *   [xmsumi]    xmsumi.com DeepSeek-V4 article, § CSA (压缩稀疏注意力): the KV
+ *               entries of every m tokens merge by weighted compression into
+ *               one compressed entry; a lightning indexer picks the top-k
+ *               entries per query token; multi-query attention runs over the
+ *               selected entries plus a sliding-window branch.
+ *               § HCA (重度压缩注意力): compression ratio m' >> m, no selection,
+ *               dense attention over every compressed entry.
+ *               § 关键技术细节: RoPE only on the last 64 dims of queries and
+ *               entries with reverse compensation on the output; KV cache with
+ *               bf16 RoPE dims and FP8 for the rest; the indexer in FP4.
+ *   [hortopato] hortopato.cc wiki "DeepSeek-V4 — MoE nyelvmodellek milliós
+ *               kontextussal", CSA list: m = 4, k = 1024, window 128;
+ *               § Heavily Compressed Attention (HCA): m' = 128.
+ *   [zcldvi]    zcldvi.com V4 article: both attentions add a window branch.
+ *
+ * Conventions for every call
+ *   - Pointers are DEVICE pointers owned by the caller; the library never
+ *     allocates, frees or synchronises.  Work is enqueued on `stream` (a
+ *     hipStream_t; NULL is the null stream).  Inputs and outputs must not
+ *     alias.  Outputs are fully overwritten.
+ *   - Return value: CSA_OK, or a negative error code; the reason is available
+ *     from csa_last_error() on the calling thread.  Errors are detected on the
+ *     host before anything is enqueued.  Device-side faults surface at the
+ *     caller's next synchronisation.
+ *   - Shapes are validated on the host; values inside device arrays (seq,
+ *     pos, idx) are trusted except where a call documents a check.
+ *   - Results are deterministic: no floating-point atomics, fixed reduction
+ *     orders, no dependence on other rows of the batch.
+ *
+ * Storage formats
+ *   - Compressed KV entry (and window-ring entry), d = d_nope + 64:
+ *     nope[d_nope] FP8 E4M3FN codes, value = code * scale; rope[64] bf16;
+ *     scale fp32.  Structure-of-arrays, see csa_kv_t.
+ *   - Indexer vectors: MXFP4 (OCP MX): d_i E2M1 values packed two per byte
+ *     (element 2i in the low nibble) and one E8M0 scale (2^(b-127)) per 32
+ *     consecutive elements.
+ *
+ * Positions: a query row has absolute position t = pos[row].  Compressed entry
+ * j at ratio m covers tokens j*m .. j*m+m-1 and is visible to t iff
+ * (j+1)*m - 1 <= t, i.e. j < (t+1)/m (complete blocks only; the incomplete
+ * tail lives in the window ring).  Entries are roped at p_j = (j+1)*m - 1.
+ */
+#ifndef LIBCSA_CSA_H
+#define LIBCSA_CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_VERSION 100
+
+enum {
+    CSA_OK = 0,
+    CSA_EINVAL = -1,       /* null pointer, bad shape, bad alignment */
+    CSA_EUNSUPPORTED = -2, /* valid but not implemented (d, heads, k, ...) */
+    CSA_EHIP = -3,         /* the HIP runtime refused a launch */
+    CSA_EWORKSPACE = -4    /* workspace missing or too small */
+};
+
+/* A hipStream_t, passed through untouched. */
+typedef void* csa_stream_t;
+
+/*
+ * Mixed-precision entries for n_seq sequences, `cap` slots each.  Sequence s,
+ * slot i lives at row s*cap + i of every array:
+ *   nope  [n_seq*cap][d - 64]  FP8 E4M3FN codes
+ *   rope  [n_seq*cap][64]      bf16 bit patterns
+ *   scale [n_seq*cap]          fp32
+ * Compressed entry j lives at slot j % cap (cap >= entries kept).  A window
+ * ring holds raw tokens (m = 1 entries): token p at slot p % cap.
+ * Alignment: nope and rope rows must start on 16-byte boundaries
+ * ((d-64) % 16 == 0 and 16-byte aligned base pointers).
+ */
+typedef struct csa_kv {
+    uint8_t* nope;
+    uint16_t* rope;
+    float* scale;
+    int64_t cap;
+} csa_kv_t;
+
+/*
+ * MXFP4 indexer keys, one per compressed entry, n_seq*cap rows:
+ *   data  [n_seq*cap][d_i / 2]  packed E2M1
+ *   scale [n_seq*cap][d_i / 32] E8M0
+ * Key of entry j of sequence s is row s*cap + j.  16-byte aligned data.
+ */
+typedef struct csa_index_keys {
+    uint8_t* data;
+    uint8_t* scale;
+    int64_t cap;
+} csa_index_keys_t;
+
+/*
+ * csa_compress — token compression ([xmsumi] § CSA: the KV entries of every m
+ * tokens merge into one compressed entry by weighted compression; [hortopato]
+ * CSA list: m = 4; § HCA: m' = 128).
+ *
+ * For each complete block b of m tokens, b = 0 .. n_tok/m - 1:
+ *   w = softmax(logits[b*m .. b*m+m-1])        (one scalar logit per token)
+ *   c = sum_i w_i * kv[b*m + i]                 (fp64, tokens in order)
+ *   c[d-64:] rotated by RoPE at p = (J+1)*m - 1, J = tok0/m + b
+ *   scale = amax(|c[:d-64]|)/448 (1 if 0); nope = E4M3(c[:d-64]/scale), RNE,
+ *   saturating; rope = bf16(c[d-64:]), RNE; both roundings are taken from
+ *   the fp64 values (no intermediate fp32 rounding)
+ * and stores entry J at slot J % out.cap of sequence `seq`.  With m = 1 it
+ * writes raw tokens into a window ring (slot p % cap).
+ *
+ *   kv      [n_tok][d] bf16, tokens tok0 .. tok0+n_tok-1 of sequence seq
+ *   logits  [n_tok] fp32
+ *   tok0    multiple of m;  n_tok multiple of m, >= 0 (0 is a no-op);
+ *           n_tok/m <= out.cap (one call never writes a slot twice)
+ *   m       1 .. 1024;  d in {128, 512}
+ *   rope_base  RoPE base (10000 in the pages' setting)
+ * RoPE convention: pairs (2i, 2i+1) of the last 64 dims, theta_i =
+ * rope_base^(-2i/64), angle = pos * theta_i evaluated in fp64.
+ */
+int csa_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t n_tok, int32_t m, int32_t d,
+                 float rope_base, int32_t seq, csa_kv_t out, csa_stream_t stream);
+
+/*
+ * csa_index_scores — lightning-indexer scores ([xmsumi] § CSA: a lightweight
+ * indexer ranks compressed entries per query token; § 关键技术细节: FP4
+ * arithmetic inside the indexer; [zcldvi]: FP4 relevance of each query token
+ * to each compressed block).
+ *
+ *   score[t][j] = sum_h w[t][h] * max(0, <q[t][h], key_j>)   over MXFP4 values
+ *   score[t][j] = -inf for j >= (pos[t]+1)/m
+ *
+ *   q        [T][h_i][d_i/2] packed E2M1;  q_scale [T][h_i][d_i/32] E8M0
+ *   w        [T][h_i] fp32 head weights
+ *   seq      [T] int32 sequence of each row;  pos [T] int64 position
+ *   keys     index keys (key of entry j of seq s at row s*cap + j)
+ *   n_cols   columns written per row (<= keys.cap)
+ *   scores   [T][n_cols] fp32
+ * h_i in {4, 8}; d_i in {64, 128}.  With power-of-two head weights and block
+ * scales whose exponents span a few binades, every score is exact in fp32
+ * (each E2M1 product is a multiple of 1/4 below 36 in magnitude).
+ */
+int csa_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
+                     const int64_t* pos, int64_t T, int32_t h_i, int32_t d_i, csa_index_keys_t keys, int32_t m,
+                     int64_t n_cols, float* scores, csa_stream_t stream);
+
+/*
+ * csa_topk — top-k selection ([xmsumi] § CSA: the top-k compressed entries
+ * per query token; [hortopato] CSA list: k = 1024).
+ *
+ * For each row t, among columns j < min(n_cols, (pos[t]+1)/m), the
+ * min(k, visible) largest scores under the total order (score descending,
+ * index ascending; -0.0 equals +0.0), written in ascending index order,
+ * padded with -1.
+ *   scores [T][n_cols] fp32 (NaN not supported);  idx [T][k] int32
+ *   1 <= k <= 2048;  n_cols < 2^31
+ * Workspace: csa_topk_workspace(T, n_cols, k) bytes, 256-byte aligned,
+ * contents undefined on entry and exit (may be 0 bytes).
+ */
+size_t csa_topk_workspace(int64_t T, int64_t n_cols, int32_t k);
+int csa_topk(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos, int32_t m, int32_t k, int32_t* idx,
+             void* ws, size_t ws_bytes, csa_stream_t stream);
+
+/*
+ * csa_sparse_mqa — CSA attention: multi-query attention (one shared KV head;
+ * every entry is both key and value) over the selected compressed entries
+ * plus the sliding-window branch, merged in one softmax (what a log-sum-exp
+ * merge of the two branches gives) ([xmsumi] § CSA; [hortopato] CSA list:
+ * window 128; RoPE and reverse compensation per [xmsumi] § 关键技术细节).
+ *
+ * Row t, head h: key set U = { comp entry idx[t][a] : 0 <= idx < (t+1)/m }
+ * (entries outside that range are ignored) plus window tokens
+ * max(0, t-window+1) .. t (ring slot p % win.cap); duplicates kept.
+ *   q~ = q[t][h] with RoPE at t on its last 64 dims
+ *   s_u = sm_scale * <q~, e_u>;  lse = log sum exp s_u;  o = sum exp(s_u-lse) e_u
+ *   o[d-64:] rotated by RoPE at -t;  empty U gives o = 0, lse = -inf
+ *
+ *   q   [T][H][d] bf16 (before RoPE);  seq [T] int32;  pos [T] int64
+ *   idx [T][k] int32;  comp / win: compressed cache / window ring
+ *   out [T][H][d] fp32;  lse [T][H] fp32
+ * H in {16, 32, 64}; d in {128, 512}; 1 <= k <= 2048; 0 <= window <= 1024.
+ * The window ring must hold every token max(0, t-window+1) .. t of every row
+ * at slot p % win.cap (win.cap >= window).
+ * Workspace: csa_mqa_workspace(T, H, d, k + window) bytes (split-KV partials).
+ */
+size_t csa_mqa_workspace(int64_t T, int32_t H, int32_t d, int64_t max_keys);
+int csa_sparse_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int32_t H, int32_t d,
+                   const int32_t* idx, int32_t k, int32_t m, csa_kv_t comp, csa_kv_t win, int32_t window,
+                   float sm_scale, float rope_base, float* out, float* lse, void* ws, size_t ws_bytes,
+                   csa_stream_t stream);
+
+/*
+ * hca_dense_mqa — HCA attention ([xmsumi] § HCA: no selection, dense attention
+ * over every compressed entry; [hortopato] § HCA: m' = 128; [zcldvi]: window
+ * branch in both attentions).  Same as csa_sparse_mqa with the key set
+ * { every comp entry j < (t+1)/m } plus the window.
+ *   max_vis  an upper bound on (pos[t]+1)/m over the rows; it sizes the
+ *            split-KV launch only (results do not depend on it as long as it
+ *            is >= 1); the workspace is csa_mqa_workspace(T, H, d,
+ *            max_vis + window).
+ */
+int hca_dense_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int32_t H, int32_t d,
+                  int32_t m, int64_t max_vis, csa_kv_t comp, csa_kv_t win, int32_t window, float sm_scale,
+                  float rope_base, float* out, float* lse, void* ws, size_t ws_bytes, csa_stream_t stream);
+
+/* Text of the last error on the calling thread ("" if none). */
+const char* csa_last_error(void);
+
+/* CSA_VERSION of the built library. */
+int csa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBCSA_CSA_H */

@@ -1,0 +1,103 @@
+"""Host-only checks of the C ABI: every declared symbol is exported, and the
+argument validation rejects bad calls before anything reaches the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def csa():
+    import compressed_sparse_long_compress_amd as m
+
+    return m
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "csa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(csa):
+    names = declared_functions()
+    assert {"csa_compress", "csa_index_scores", "csa_topk", "csa_sparse_mqa", "hca_dense_mqa"} <= set(names)
+    lib = ctypes.CDLL(csa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/csa.h but not exported"
+    assert set(names) == set(csa.EXPORTS)
+
+
+def test_version(csa):
+    hdr = open(os.path.join(ROOT, "include", "csa.h")).read()
+    v = int(re.search(r"#define CSA_VERSION (\d+)", hdr).group(1))
+    assert csa.version() == v
+
+
+def _kv(csa, cap=16):
+    return csa._Kv(None, None, None, cap)
+
+
+def test_compress_validation(csa):
+    L = csa._lib
+    rc = L.csa_compress(None, None, 0, 8, 0, 512, 10000.0, 0, _kv(csa), None)
+    assert rc == csa.CSA_EUNSUPPORTED and b"m=0" in L.csa_last_error()
+    rc = L.csa_compress(None, None, 0, 8, 4, 256, 10000.0, 0, _kv(csa), None)
+    assert rc == csa.CSA_EUNSUPPORTED
+    rc = L.csa_compress(None, None, 2, 8, 4, 512, 10000.0, 0, _kv(csa), None)
+    assert rc == csa.CSA_EINVAL and b"complete blocks" in L.csa_last_error()
+    rc = L.csa_compress(None, None, 0, 0, 4, 512, 10000.0, 0, _kv(csa), None)
+    assert rc == csa.CSA_OK  # empty call is a no-op
+    rc = L.csa_compress(ctypes.c_void_p(16), ctypes.c_void_p(16), 0, 8, 4, 512, 10000.0, 0, _kv(csa), None)
+    assert rc == csa.CSA_EINVAL and b"null array" in L.csa_last_error()
+
+
+def test_index_topk_validation(csa):
+    L = csa._lib
+    keys = csa._IdxKeys(None, None, 16)
+    rc = L.csa_index_scores(None, None, None, None, None, 4, 16, 128, keys, 4, 16, None, None)
+    assert rc == csa.CSA_EUNSUPPORTED
+    rc = L.csa_index_scores(None, None, None, None, None, 4, 8, 96, keys, 4, 16, None, None)
+    assert rc == csa.CSA_EUNSUPPORTED
+    p = ctypes.c_void_p(256)
+    rc = L.csa_index_scores(p, p, p, p, p, 4, 8, 128, csa._IdxKeys(256, 256, 8), 4, 16, p, None)
+    assert rc == csa.CSA_EINVAL and b"keys.cap" in L.csa_last_error()
+    rc = L.csa_topk(None, 4, 100, None, 4, 0, None, None, 0, None)
+    assert rc == csa.CSA_EUNSUPPORTED
+    rc = L.csa_topk(None, 4, 100, None, 4, 4096, None, None, 0, None)
+    assert rc == csa.CSA_EUNSUPPORTED
+    rc = L.csa_topk(None, 0, 100, None, 4, 64, None, None, 0, None)
+    assert rc == csa.CSA_OK
+
+
+def test_mqa_validation(csa):
+    L = csa._lib
+    p = ctypes.c_void_p(256)
+    kv = csa._Kv(256, 256, 256, 256)
+    args = dict(T=2, H=64, d=512, k=64, m=4, window=128)
+
+    def sparse(**o):
+        a = dict(args, **o)
+        return L.csa_sparse_mqa(p, p, p, a["T"], a["H"], a["d"], p, a["k"], a["m"], kv, a.get("win", kv),
+                                a["window"], 0.04, 10000.0, p, p, None, 0, None)
+
+    assert sparse(H=48) == csa.CSA_EUNSUPPORTED
+    assert sparse(d=256) == csa.CSA_EUNSUPPORTED
+    assert sparse(k=4096) == csa.CSA_EUNSUPPORTED
+    assert sparse(window=2000) == csa.CSA_EUNSUPPORTED
+    assert sparse(win=csa._Kv(256, 256, 256, 16)) == csa.CSA_EINVAL  # ring smaller than the window
+    assert sparse(T=0) == csa.CSA_OK
+    rc = L.hca_dense_mqa(p, p, p, 2, 64, 512, 128, 0, kv, kv, 128, 0.04, 10000.0, p, p, None, 0, None)
+    assert rc == csa.CSA_EINVAL and b"max_vis" in L.csa_last_error()
+    rc = L.hca_dense_mqa(p, p, p, 2, 64, 512, 128, 8192, kv, kv, 128, 0.04, 10000.0, p, p, None, 0, None)
+    assert rc == csa.CSA_EWORKSPACE
+
+
+def test_workspace_sizes(csa):
+    assert csa.csa_topk_workspace(4, 262144, 1024) >= 0
+    # decode shapes split the key list; big batches do not
+    assert csa.csa_mqa_workspace(4, 64, 512, 1152) > 0
+    assert csa.csa_mqa_workspace(8192, 64, 512, 1152) == 0

@@ -1,0 +1,347 @@
+"""GPU parity: every libcsa call (through its C ABI) against the fp64 oracle.
+
+Bars: index scores and top-k indices bit-exact; attention outputs and lse
+within 2e-3 relative RMS and 1e-2 max-abs; compressed entries within one
+FP8 quantum / one bf16 ulp of the oracle (both round the same fp32/fp64
+value, so only values within rounding of a boundary may differ).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from gen import configs
+
+pytestmark = pytest.mark.gpu
+
+REL_RMS = 2e-3
+MAX_ABS = 1e-2
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import compressed_sparse_long_compress_amd as csa
+
+    return csa
+
+
+@pytest.fixture(scope="module")
+def dev(lib):
+    from gen import device
+
+    return device
+
+
+def rel_rms(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def assert_attn_close(out, lse, ref_out, ref_lse, what):
+    out = np.asarray(out, np.float64)
+    r = rel_rms(out, ref_out)
+    ma = float(np.max(np.abs(out - ref_out)))
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(lse), fin), f"{what}: lse finiteness differs"
+    rl = rel_rms(np.asarray(lse)[fin], ref_lse[fin]) if fin.any() else 0.0
+    ml = float(np.max(np.abs(np.asarray(lse)[fin] - ref_lse[fin]))) if fin.any() else 0.0
+    print(f"{what}: out rel-rms {r:.2e} max-abs {ma:.2e}; lse rel-rms {rl:.2e} max-abs {ml:.2e}", flush=True)
+    assert r <= REL_RMS and ma <= MAX_ABS, f"{what}: out rel-rms {r:.3e} max-abs {ma:.3e}"
+    assert rl <= REL_RMS and ml <= MAX_ABS, f"{what}: lse rel-rms {rl:.3e} max-abs {ml:.3e}"
+
+
+def compare_entries(orc, got, ref, what):
+    """got/ref: (nope u8, rope u16, scale f32) for the same entries."""
+    gn, gr, gs = got
+    rn, rr, rs = ref
+    # scale: both fp32 roundings of amax/448 (fp32 vs fp64 accumulation): within 2 ulp
+    assert np.all(np.abs(gs.astype(np.float64) - rs) <= np.abs(rs) * 2.0 ** -21), f"{what}: scale"
+    tab = orc.e4m3_table()
+    gv = tab[gn] * gs[:, None].astype(np.float64)
+    rv = tab[rn] * rs[:, None].astype(np.float64)
+    diff_codes = gn != rn
+    frac = diff_codes.mean()
+    # a differing code may move at most one FP8 step
+    q = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(rv) / rs[:, None], 2.0 ** -6))) - 3) * rs[:, None]
+    assert np.all(np.abs(gv - rv) <= 1.01 * q + 1e-30), f"{what}: nope value moved more than one FP8 step"
+    # both sides round the same fp64 value; only libm last-bit differences may flip a code
+    assert frac <= 1e-5, f"{what}: {frac:.2e} of FP8 codes differ"
+    g = orc.bf16_array_to_f64(gr)
+    r = orc.bf16_array_to_f64(rr)
+    assert np.all(np.abs(g - r) <= np.abs(r) * 2.0 ** -7 + 1e-30), f"{what}: rope beyond one bf16 ulp"
+    assert (gr != rr).mean() <= 1e-4, f"{what}: {(gr != rr).mean():.2e} of bf16 values differ"
+    print(f"{what}: {frac:.2e} FP8 codes differ, {(gr != rr).mean():.2e} bf16 differ", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# csa_compress
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("d,m,tok0,n_tok,cap", [
+    (128, 4, 0, 2048, 512),
+    (512, 4, 1024, 4096, 4096),
+    (512, 128, 0, 8192, 64),
+    (512, 1, 130944, 256, 8320),
+    (128, 1, 0, 300, 300),
+    (512, 4, 131072, 64, 40),    # slots wrap: entry J at J % cap
+])
+def test_compress(lib, dev, gen, orc, d, m, tok0, n_tok, cap):
+    import torch
+
+    _say(f"compress d={d} m={m} tok0={tok0} n_tok={n_tok} cap={cap}")
+    kv = gen.normal_bf16(201, 1, (n_tok, d))
+    logits = gen.normal_f32(201, 2, (n_tok,))
+    cache = lib.KvCache.empty(2, cap, d)
+    lib.csa_compress(dev.bf16(kv), dev.t(logits), tok0, m, 1, cache)
+    torch.cuda.synchronize()
+    got = dev.host_entries(cache)
+    ref = orc.compress(kv, logits, tok0, m)
+    n = n_tok // m
+    slots = cap + (tok0 // m + np.arange(n)) % cap  # sequence 1
+    compare_entries(orc, tuple(a[slots] for a in got), ref, f"compress d={d} m={m}")
+    # sequence 0 untouched
+    assert not got[0][:cap].any() and not got[2][:cap].any()
+
+
+def test_compress_rejects_partial_block(lib, dev, gen):
+    cache = lib.KvCache.empty(1, 16, 128)
+    kv = gen.normal_bf16(202, 1, (6, 128))
+    with pytest.raises(lib.CsaError) as e:
+        lib.csa_compress(dev.bf16(kv), dev.t(gen.normal_f32(202, 2, (6,))), 0, 4, 0, cache)
+    assert e.value.code == lib.CSA_EINVAL
+
+
+# ---------------------------------------------------------------------------
+# csa_index_scores
+# ---------------------------------------------------------------------------
+def _index_case(gen, seed, T, h_i, d_i, N, B, pos, seq, plant=0.0):
+    kd, ks, _ = gen.mxfp4(seed, 1, B * N, d_i, plant_frac=plant)
+    qd, qs, _ = gen.mxfp4(seed, 2, T * h_i, d_i)
+    w = gen.pow2_weights(seed, 3, (T, h_i))
+    return (qd.reshape(T, h_i, d_i // 2), qs.reshape(T, h_i, d_i // 32), w, np.asarray(seq, np.int32),
+            np.asarray(pos, np.int64), kd, ks)
+
+
+@pytest.mark.parametrize("T,h_i,d_i,N,B,m,n_cols,mode", [
+    (4, 8, 128, 5000, 4, 4, 5000, "decode"),        # ragged key chunk
+    (32, 8, 128, 16384, 32, 4, 16384, "decode"),
+    (3, 4, 64, 700, 2, 4, 650, "decode"),
+    (2048, 4, 64, 512, 1, 4, 512, "prefill"),       # small prefill
+    (200, 8, 128, 3000, 1, 4, 3000, "prefill"),     # ragged rows and columns
+    (130, 8, 128, 900, 3, 4, 900, "mixed"),          # several sequences inside one tile
+    (96, 4, 128, 400, 2, 2, 400, "mixed"),
+])
+def test_index_scores_bit_exact(lib, dev, gen, orc, T, h_i, d_i, N, B, m, n_cols, mode):
+    import torch
+
+    _say(f"index T={T} h_i={h_i} d_i={d_i} N={N} B={B} m={m} n_cols={n_cols} {mode}")
+    rng = np.random.default_rng(T + N)
+    if mode == "decode":
+        seq = np.arange(T) % B
+        pos = rng.integers(m * N // 2, m * N + 5, size=T)
+    elif mode == "prefill":
+        seq = np.zeros(T, np.int64)
+        pos = np.sort(rng.integers(0, m * N, size=T))
+    else:
+        seq = rng.integers(0, B, size=T)
+        pos = rng.integers(0, m * N, size=T)
+    qd, qs, w, seq, pos, kd, ks = _index_case(gen, 300 + T, T, h_i, d_i, N, B, pos, seq)
+    wit = orc.index_exact_witness(qd, qs, w, seq, pos, kd, ks, N, m, n_cols)
+    assert wit < 24, f"inputs break the fp32 exactness precondition ({wit:.1f} bits)"
+    ref = orc.index_scores(qd, qs, w, seq, pos, kd, ks, N, m, n_cols).astype(np.float32)
+    keys = dev.index_keys((kd, ks), N)
+    got = lib.csa_index_scores(dev.t(qd), dev.t(qs), dev.t(w), dev.t(seq), dev.t(pos), keys, m, n_cols)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    bad = got.view(np.uint32) != ref.view(np.uint32)
+    assert not bad.any(), f"{bad.sum()} scores differ; first at {np.argwhere(bad)[:3].tolist()}"
+
+
+# ---------------------------------------------------------------------------
+# csa_topk
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,n_cols,k,m,kind", [
+    (64, 512, 64, 4, "normal"),
+    (16, 40000, 1024, 4, "normal"),     # longer than the LDS cache
+    (32, 16384, 1024, 4, "ties"),
+    (8, 3000, 1024, 4, "short"),        # some rows see fewer than k columns
+    (5, 2048, 2048, 1, "normal"),
+    (4, 70000, 1024, 4, "allequal"),
+])
+def test_topk_bit_exact(lib, dev, orc, T, n_cols, k, m, kind):
+    import torch
+
+    _say(f"topk T={T} n_cols={n_cols} k={k} m={m} {kind}")
+    rng = np.random.default_rng(n_cols + k)
+    if kind == "ties":
+        scores = rng.integers(0, 50, size=(T, n_cols)).astype(np.float32)
+    elif kind == "allequal":
+        scores = np.zeros((T, n_cols), np.float32)
+        scores[:, ::7] = -0.0
+    else:
+        scores = np.abs(rng.standard_normal((T, n_cols))).astype(np.float32) * 10
+    if kind == "short":
+        pos = rng.integers(0, m * n_cols, size=T).astype(np.int64)
+        pos[0] = 5
+    else:
+        pos = np.full(T, m * n_cols - 1, np.int64)
+    ref = orc.topk(scores, pos, m, k)
+    got = lib.csa_topk(dev.t(scores), dev.t(pos), m, k)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    assert np.array_equal(got, ref), f"rows differ: {np.where((got != ref).any(axis=1))[0][:5].tolist()}"
+
+
+# ---------------------------------------------------------------------------
+# csa_sparse_mqa / hca_dense_mqa
+# ---------------------------------------------------------------------------
+def _attn_inputs(gen, seed, B, N, W, H, d, T, L, win_cap):
+    comp = gen.entries(seed, 20, B * N, d - 64)
+    win = gen.entries(seed, 21, B * win_cap, d - 64)
+    q = gen.normal_bf16(seed, 23, (T, H, d))
+    return comp, win, q
+
+
+@pytest.mark.parametrize("T,B,L,H,d,k,W,m,win_cap", [
+    (4, 4, 8192, 64, 512, 1024, 128, 4, 128),      # decode, split-KV
+    (32, 32, 4096, 64, 512, 1024, 128, 4, 128),
+    (3, 2, 600, 32, 512, 256, 128, 4, 128),        # fewer visible than k (-1 padding)
+    (6, 3, 2048, 16, 128, 64, 128, 4, 200),
+    (2, 2, 64, 64, 512, 64, 0, 4, 1),              # no window branch
+])
+def test_sparse_mqa_decode(lib, dev, gen, orc, T, B, L, H, d, k, W, m, win_cap):
+    import torch
+
+    _say(f"sparse_mqa T={T} B={B} L={L} H={H} d={d} k={k} W={W} m={m}")
+    N = L // m
+    comp, win, q = _attn_inputs(gen, 400 + T, B, N, W, H, d, T, L, win_cap)
+    seq = (np.arange(T) % B).astype(np.int32)
+    pos = np.full(T, L - 1, np.int64)
+    pos[-1] = L - 3  # a row whose last block is incomplete
+    nv = (pos + 1) // m
+    idx = gen.random_idx(401 + T, 1, nv, k)
+    sm = 1.0 / math.sqrt(d)
+    ref_o, ref_l = orc.attend(q, seq, pos, comp, N, win, win_cap, W, m, sm, idx=idx)
+    out, lse = lib.csa_sparse_mqa(dev.bf16(q), dev.t(seq), dev.t(pos), dev.t(idx), m, dev.kv_cache(comp, N),
+                                  dev.kv_cache(win, win_cap) if W > 0 else None, W, sm)
+    torch.cuda.synchronize()
+    assert_attn_close(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "sparse_mqa")
+
+
+def test_sparse_mqa_ignores_invalid_idx(lib, dev, gen, orc):
+    import torch
+
+    _say("sparse_mqa invalid idx entries")
+    B, N, H, d, k, W, m = 2, 256, 64, 512, 128, 128, 4
+    comp, win, q = _attn_inputs(gen, 450, B, N, W, H, d, 2, 1024, 128)
+    seq = np.array([0, 1], np.int32)
+    pos = np.array([1023, 500], np.int64)
+    idx = gen.random_idx(451, 1, np.array([256, 125]), k)
+    idx[1, 5] = 200  # not yet visible at t=500 (visible: j < 125)
+    idx[0, 7] = -1
+    sm = 1.0 / math.sqrt(d)
+    ref_o, ref_l = orc.attend(q, seq, pos, comp, N, win, 128, W, m, sm, idx=idx)
+    out, lse = lib.csa_sparse_mqa(dev.bf16(q), dev.t(seq), dev.t(pos), dev.t(idx), m, dev.kv_cache(comp, N),
+                                  dev.kv_cache(win, 128), W, sm)
+    torch.cuda.synchronize()
+    assert_attn_close(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "sparse_mqa invalid idx")
+
+
+@pytest.mark.parametrize("T,B,L,H,d,W,m", [
+    (8, 8, 131072, 64, 512, 128, 128),   # decode, 1024 entries
+    (3, 3, 20000, 32, 512, 128, 128),
+    (5, 1, 640, 16, 128, 64, 128),
+])
+def test_dense_mqa_decode(lib, dev, gen, orc, T, B, L, H, d, W, m):
+    import torch
+
+    _say(f"dense_mqa T={T} B={B} L={L} H={H} d={d} W={W} m={m}")
+    N = L // m
+    comp, win, q = _attn_inputs(gen, 500 + T, B, N, W, H, d, T, L, W)
+    seq = (np.arange(T) % B).astype(np.int32)
+    pos = np.full(T, L - 1, np.int64)
+    pos[0] = L - 200
+    sm = 1.0 / math.sqrt(d)
+    ref_o, ref_l = orc.attend(q, seq, pos, comp, N, win, W, W, m, sm)
+    out, lse = lib.hca_dense_mqa(dev.bf16(q), dev.t(seq), dev.t(pos), m, N, dev.kv_cache(comp, N),
+                                 dev.kv_cache(win, W), W, sm)
+    torch.cuda.synchronize()
+    assert_attn_close(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "dense_mqa")
+
+
+def test_sparse_all_selected_equals_dense(lib, dev, gen):
+    """k >= visible entries: CSA equals HCA at the same m (GPU against GPU, both checked against the oracle above)."""
+    import torch
+
+    _say("sparse(all) == dense")
+    B, N, H, d, W, m = 2, 300, 64, 512, 128, 4
+    comp, win, q = _attn_inputs(gen, 600, B, N, W, H, d, 2, 1200, 128)
+    seq = np.array([0, 1], np.int32)
+    pos = np.array([1199, 777], np.int64)
+    idx = np.full((2, 512), -1, np.int32)
+    for i in range(2):
+        nv = (pos[i] + 1) // m
+        idx[i, :nv] = np.arange(nv)
+    sm = 1.0 / math.sqrt(d)
+    a = lib.csa_sparse_mqa(dev.bf16(q), dev.t(seq), dev.t(pos), dev.t(idx), m, dev.kv_cache(comp, N),
+                           dev.kv_cache(win, 128), W, sm)
+    b = lib.hca_dense_mqa(dev.bf16(q), dev.t(seq), dev.t(pos), m, N, dev.kv_cache(comp, N), dev.kv_cache(win, 128), W,
+                          sm)
+    torch.cuda.synchronize()
+    # same key set, different split-KV partitioning: equal within the attention bar
+    assert rel_rms(a[0].cpu().numpy(), b[0].cpu().numpy()) < REL_RMS
+
+
+# ---------------------------------------------------------------------------
+# end to end: the small prefill workload through every call
+# ---------------------------------------------------------------------------
+def test_end_to_end_prefill_small(lib, dev, gen, orc):
+    import torch
+
+    _say("end-to-end prefill_small")
+    wl = configs.named("prefill_small")
+    T, d, m, k, W, H = wl["T"], wl["d"], wl["m"], wl["k"], wl["W"], wl["H"]
+    # GPU
+    comp = lib.KvCache.empty(1, wl["comp_cap"], d)
+    win = lib.KvCache.empty(1, wl["win_cap"], d)
+    hca = lib.KvCache.empty(1, wl["hca_cap"], d)
+    kv = dev.bf16(wl["kv"])
+    lg = dev.t(wl["logits"])
+    lib.csa_compress(kv, lg, 0, m, 0, comp)
+    lib.csa_compress(kv, lg, 0, 1, 0, win)
+    lib.csa_compress(kv, lg, 0, wl["m_hca"], 0, hca)
+    seq, pos = dev.t(wl["seq"]), dev.t(wl["pos"])
+    scores = lib.csa_index_scores(dev.t(wl["iq"][0]), dev.t(wl["iq"][1]), dev.t(wl["w"]), seq, pos,
+                                  dev.index_keys(wl["keys"], wl["N"]), m, wl["n_cols"])
+    idx = lib.csa_topk(scores, pos, m, k)
+    out, lse = lib.csa_sparse_mqa(dev.bf16(wl["q"]), seq, pos, idx, m, comp, win, W, wl["sm_scale"])
+    hout, hlse = lib.hca_dense_mqa(dev.bf16(wl["q"]), seq, pos, wl["m_hca"], wl["hca_cap"], hca, win, W,
+                                   wl["sm_scale"])
+    torch.cuda.synchronize()
+    # oracle, step by step from the same raw inputs
+    o_comp = orc.compress(wl["kv"], wl["logits"], 0, m)
+    o_win = orc.compress(wl["kv"], wl["logits"], 0, 1)
+    o_hca = orc.compress(wl["kv"], wl["logits"], 0, wl["m_hca"])
+    compare_entries(orc, dev.host_entries(comp), o_comp, "e2e compress m=4")
+    o_scores = orc.index_scores(wl["iq"][0], wl["iq"][1], wl["w"], wl["seq"], wl["pos"], wl["keys"][0],
+                                wl["keys"][1], wl["N"], m, wl["n_cols"]).astype(np.float32)
+    assert np.array_equal(scores.cpu().numpy().view(np.uint32), o_scores.view(np.uint32))
+    o_idx = orc.topk(o_scores, wl["pos"], m, k)
+    assert np.array_equal(idx.cpu().numpy(), o_idx)
+    # attention from the oracle's own caches (entries may differ in rare FP8 roundings)
+    ref_o, ref_l = orc.attend(wl["q"], wl["seq"], wl["pos"], o_comp, wl["comp_cap"], o_win, wl["T"], W, m,
+                              wl["sm_scale"], idx=o_idx)
+    assert_attn_close(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "e2e sparse")
+    ref_o, ref_l = orc.attend(wl["q"], wl["seq"], wl["pos"], o_hca, wl["hca_cap"], o_win, wl["T"], W, wl["m_hca"],
+                              wl["sm_scale"])
+    assert_attn_close(hout.cpu().numpy(), hlse.cpu().numpy(), ref_o, ref_l, "e2e dense")

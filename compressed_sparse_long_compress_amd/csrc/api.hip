@@ -1,4 +1,5 @@
 // libcsa C ABI: argument validation, launch selection and error reporting.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -61,6 +62,14 @@ int check_mqa_common(const char* fn, const uint16_t* q, const int32_t* seq, cons
 
 }  // namespace
 
+namespace csa {
+RopeTab rope_table(double base) {
+    RopeTab rt;
+    for (int i = 0; i < 32; ++i) rt.theta[i] = pow(base, -2.0 * (double)i / 64.0);
+    return rt;
+}
+}  // namespace csa
+
 extern "C" {
 
 const char* csa_last_error(void) { return g_err; }
@@ -85,7 +94,7 @@ int csa_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t 
     if (n_tok / m > out.cap)
         return fail(CSA_EINVAL, "%s: %lld new entries exceed out.cap (%lld): slots would collide", fn,
                     (long long)(n_tok / m), (long long)out.cap);
-    hipError_t e = csa::launch_compress(kv, logits, tok0, n_tok, m, d, (double)rope_base, (int64_t)seq * out.cap,
+    hipError_t e = csa::launch_compress(kv, logits, tok0, n_tok, m, d, csa::rope_table((double)rope_base), (int64_t)seq * out.cap,
                                         out.cap, out.nope, out.rope, out.scale, (hipStream_t)stream);
     return hip_status(e, fn);
 }
@@ -147,7 +156,7 @@ int csa_sparse_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos, in
         return fail(CSA_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
     if (need > 0 && !aligned16(ws)) return fail(CSA_EINVAL, "%s: workspace must be 16-byte aligned", fn);
     hipError_t e = csa::launch_mqa(q, seq, pos, T, H, d, idx, k, m, max_keys, view(comp), view(win), window, sm_scale,
-                                   (double)rope_base, out, lse, ws, (hipStream_t)stream);
+                                   csa::rope_table((double)rope_base), out, lse, ws, (hipStream_t)stream);
     return hip_status(e, fn);
 }
 
@@ -165,7 +174,7 @@ int hca_dense_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos, int
         return fail(CSA_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
     if (need > 0 && !aligned16(ws)) return fail(CSA_EINVAL, "%s: workspace must be 16-byte aligned", fn);
     hipError_t e = csa::launch_mqa(q, seq, pos, T, H, d, nullptr, 0, m, max_keys, view(comp), view(win), window,
-                                   sm_scale, (double)rope_base, out, lse, ws, (hipStream_t)stream);
+                                   sm_scale, csa::rope_table((double)rope_base), out, lse, ws, (hipStream_t)stream);
     return hip_status(e, fn);
 }
 

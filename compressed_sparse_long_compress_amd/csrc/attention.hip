@@ -4,18 +4,23 @@
 //
 // Grid: one workgroup per (row, split); a split is a contiguous range of the
 // row's key list.  Per tile of 32 keys the workgroup
-//   1. gathers the entries into LDS twice: a row-major bf16 copy (FP8 codes
+//   1. stages the entries into LDS twice: a row-major bf16 copy (FP8 codes
 //      and bf16 RoPE dims, both exact in bf16) for QK, and a transposed fp16
-//      copy scaled by scale_j / S (S = largest scale in the split) for PV;
-//   2. QK^T with bf16 MFMA 16x16x32: rows = keys, columns = heads; the query
-//      (RoPE applied at t in fp32) lives in registers; its 64 RoPE dims are
-//      split hi + lo in bf16 so they keep ~16 bits; the FP8 part's scale is
-//      applied per key to the fp32 accumulator;
+//      copy (codes exact in fp16) for PV; the next tile's entries are already
+//      in flight into registers while the current tile computes;
+//   2. S^T = K Q^T with bf16 MFMA 16x16x32: rows = keys, columns = heads; the
+//      query (RoPE applied at t in fp32) lives in registers, its 64 RoPE dims
+//      split hi + lo in bf16 so they keep ~16 bits; the FP8 part's per-entry
+//      scale multiplies the fp32 accumulator;
 //   3. online softmax in fp32 per head (running max / sum);
-//   4. P V with fp16 MFMA 16x16x32 into fp32 accumulators (dims x heads).
-// A single split writes the normalised output (with the inverse RoPE on the
-// last 64 dims); several splits write unnormalised partials plus (max, sum),
-// merged by k_mqa_combine in a fixed order (log-sum-exp merge).
+//   4. O^T += V^T P^T with fp16 MFMA 16x16x32 into fp32 accumulators
+//      (dims x heads).  For the FP8 dims P carries scale_j / S_tile (S_tile =
+//      largest scale of the tile, so P stays within [0, 1]); the accumulators
+//      are kept in units of the current S_tile and rescaled with the softmax
+//      correction when it changes.
+// A single split writes the normalised output (inverse RoPE on the last 64
+// dims); several splits write unnormalised partials plus (max, sum), merged by
+// k_mqa_combine in the fixed split order (a log-sum-exp merge).
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 
@@ -33,14 +38,15 @@ struct MqaSmem {
     __bf16 kr[KT * KR];
     _Float16 vt[D * VT];
     float s[KT * SS];
-    _Float16 p[H * PS];
+    _Float16 pn[H * PS];  // P * scale_j / S_tile (FP8 dims)
+    _Float16 pr[H * PS];  // P (RoPE dims)
     float alpha[H];
     float mrun[H];
     float lrun[H];
-    int64_t row[KT];
-    float scl[KT];
-    int valid[KT];
-    float red[8];
+    float cs[64];         // cos / sin of t * theta_i, i < 32
+    int64_t row[2][KT];   // resolved cache rows (double-buffered): >= 0 comp, <= -2 window, -1 masked
+    float scl[2][KT];
+    float sfac[2];        // ratio old S_tile / new S_tile for the FP8 accumulators
 };
 
 struct RowKeys {
@@ -59,24 +65,39 @@ __device__ __forceinline__ RowKeys row_keys(int64_t t, const int32_t* idx, int k
     return r;
 }
 
-// Resolve key-list position u of row t to a cache row (-1 when masked) and its scale.
+// Key-list position u of row t -> encoded cache row (comp >= 0, window <= -2, masked -1) and its scale.
 __device__ __forceinline__ int64_t resolve(int64_t u, int64_t t, int32_t sq, const RowKeys& rk, const int32_t* idx,
-                                           int k, const KvView& comp, const KvView& win, bool& is_win) {
+                                           int k, const KvView& comp, const KvView& win, float& scl) {
     if (u < rk.n_c) {
-        is_win = false;
-        int64_t j = idx ? (int64_t)idx[t * k + u] : u;
-        if (j < 0 || j >= rk.nv) return -1;
-        return (int64_t)sq * comp.cap + (j % comp.cap);
+        const int64_t j = idx ? (int64_t)idx[t * k + u] : u;
+        if (j < 0 || j >= rk.nv) {
+            scl = 0.f;
+            return -1;
+        }
+        const int64_t r = (int64_t)sq * comp.cap + (j % comp.cap);
+        scl = comp.scale[r];
+        return r;
     }
-    is_win = true;
     const int64_t p = rk.lo + (u - rk.n_c);
-    return (int64_t)sq * win.cap + (p % win.cap);
+    const int64_t r = (int64_t)sq * win.cap + (p % win.cap);
+    scl = win.scale[r];
+    return -(r + 2);
+}
+
+// cos / sin of pos * theta: fp64 product, fp64 reduction by 2*pi (two-part
+// constant), fp32 sincos of the reduced angle.
+__device__ __forceinline__ void angle_cs(double pos, double theta, float& c, float& s) {
+    const double a = pos * theta;
+    const double k = rint(a * 0.15915494309189533577);
+    double r = fma(-k, 6.28318530717958623200, a);
+    r = fma(-k, 2.44929359829470635445e-16, r);
+    sincosf((float)r, &s, &c);
 }
 
 template <int H, int D>
 __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, const int32_t* __restrict__ seq,
                                              const int64_t* __restrict__ pos, const int32_t* __restrict__ idx, int k,
-                                             int m, KvView comp, KvView win, int window, float sm_scale, double base,
+                                             int m, KvView comp, KvView win, int window, float sm_scale, RopeTab rt,
                                              int S, float* __restrict__ out, float* __restrict__ lse,
                                              float* __restrict__ part_o, float* __restrict__ part_ml) {
     using Sm = MqaSmem<H, D>;
@@ -90,6 +111,7 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
     constexpr int DW = D / 4;                   // dims per wave in PV
     constexpr int DT = DW / 16;                 // 16-dim tiles per wave in PV
     constexpr int CPK = DN / 16 + 8;            // 16-byte chunks per entry
+    constexpr int NCH = (KT * CPK + 255) / 256;  // chunks per thread per tile
 
     __shared__ Sm sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -101,19 +123,39 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
     const RowKeys rk = row_keys(tp, idx, k, m, window);
     const int64_t u0 = rk.n * s / S, u1 = rk.n * (s + 1) / S;
 
-    // ---- split-wide scale reference: largest entry scale of the split ----
-    float smax = 0.f;
-    for (int64_t u = u0 + tid; u < u1; u += 256) {
-        bool w;
-        int64_t r = resolve(u, t, sq, rk, idx, k, comp, win, w);
-        if (r >= 0) smax = fmaxf(smax, w ? win.scale[r] : comp.scale[r]);
+    // ---- first tile: resolve, then put its entries in flight ----
+    if (tid < KT) {
+        const int64_t u = u0 + tid;
+        float sc = 0.f;
+        sm.row[0][tid] = u < u1 ? resolve(u, t, sq, rk, idx, k, comp, win, sc) : -1;
+        sm.scl[0][tid] = sc;
+    } else if (tid >= 64 && tid < 96) {
+        float c, sn;
+        angle_cs((double)tp, rt.theta[tid - 64], c, sn);
+        sm.cs[2 * (tid - 64)] = c;
+        sm.cs[2 * (tid - 64) + 1] = sn;
     }
-    smax = wave_max(smax);
-    if (lane == 0) sm.red[wave] = smax;
     __syncthreads();
-    float sref = fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3]));
-    if (!(sref > 0.f)) sref = 1.f;
-    const float inv_sref = 1.f / sref;
+
+    v4i pre[NCH];
+    auto issue = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int c = tid + i * 256;
+            pre[i] = v4i{0, 0, 0, 0};
+            if (c < KT * CPK) {
+                const int key = c / CPK, part = c % CPK;
+                const int64_t code = sm.row[buf][key];
+                if (code != -1) {
+                    const bool w = code <= -2;
+                    const int64_t r = w ? -code - 2 : code;
+                    if (part < DN / 16) pre[i] = *(const v4i*)((w ? win.nope : comp.nope) + r * DN + part * 16);
+                    else pre[i] = *(const v4i*)((w ? win.rope : comp.rope) + r * 64 + (part - DN / 16) * 8);
+                }
+            }
+        }
+    };
+    issue(0);
 
     // ---- query fragments (B operand of S^T = K Q^T) with RoPE at tp ----
     const int hb = HT >= 4 ? wave : wave % HT;
@@ -135,8 +177,8 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
                 for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
-                    float cs, sn;
-                    rope_cs((double)tp, base, (d0 - DN + e) >> 1, cs, sn);
+                    const int pi = (d0 - DN + e) >> 1;
+                    const float cs = sm.cs[2 * pi], sn = sm.cs[2 * pi + 1];
                     const float x0 = x[e], x1 = x[e + 1];
                     x[e] = x0 * cs - x1 * sn;
                     x[e + 1] = x0 * sn + x1 * cs;
@@ -157,6 +199,7 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
     // running softmax stats live with the softmax threads (TPH per head)
     const int sh = tid / TPH, sk = tid % TPH;
     float m_run = -INFINITY, l_run = 0.f;
+    float s_ref = 0.f;  // S_tile the FP8 accumulators are expressed in (0: none yet)
 
     v4f acc[DT][HT];
 #pragma unroll
@@ -164,58 +207,53 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
 #pragma unroll
         for (int b = 0; b < HT; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t ut = u0; ut < u1; ut += KT) {
-        // ---- resolve the tile's keys ----
-        if (tid < KT) {
-            const int64_t u = ut + tid;
-            int64_t r = -1;
-            bool w = false;
-            if (u < u1) r = resolve(u, t, sq, rk, idx, k, comp, win, w);
-            sm.row[tid] = r >= 0 ? (w ? -(r + 2) : r) : -1;  // window rows encoded as -(r+2)
-            sm.valid[tid] = r >= 0;
-            sm.scl[tid] = r >= 0 ? (w ? win.scale[r] : comp.scale[r]) : 0.f;
-        }
-        __syncthreads();
-        // ---- gather into LDS ----
-        for (int c = tid; c < KT * CPK; c += 256) {
-            const int key = c / CPK, part = c % CPK;
-            const int64_t code = sm.row[key];
-            const bool w = code <= -2;
-            const int64_t r = w ? -code - 2 : code;
-            const uint8_t* nope = w ? win.nope : comp.nope;
-            const uint16_t* rope = w ? win.rope : comp.rope;
-            __bf16* kr = sm.kr + key * Sm::KR;
-            if (part < DN / 16) {
-                v4i raw = {0, 0, 0, 0};
-                if (code != -1) raw = *(const v4i*)(nope + r * DN + part * 16);
-                const float fs = sm.scl[key] * inv_sref;
-                v8bf b0, b1;
+    int buf = 0;
+    for (int64_t ut = u0; ut < u1; ut += KT, buf ^= 1) {
+        // ---- stage this tile from registers into LDS ----
 #pragma unroll
-                for (int wd = 0; wd < 4; ++wd) {
-                    v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[wd], false);
-                    v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[wd], true);
-                    float f[4] = {lo.x, lo.y, hi.x, hi.y};
+        for (int i = 0; i < NCH; ++i) {
+            const int c = tid + i * 256;
+            if (c < KT * CPK) {
+                const int key = c / CPK, part = c % CPK;
+                __bf16* kr = sm.kr + key * Sm::KR;
+                const v4i raw = pre[i];
+                if (part < DN / 16) {
+                    v8bf b0, b1;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int dd = part * 16 + wd * 4 + e;
-                        if (wd < 2) b0[wd * 4 + e] = (__bf16)f[e];
-                        else b1[(wd - 2) * 4 + e] = (__bf16)f[e];
-                        sm.vt[dd * Sm::VT + key] = (_Float16)(f[e] * fs);
+                    for (int wd = 0; wd < 4; ++wd) {
+                        const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[wd], false);
+                        const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[wd], true);
+                        const float f[4] = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if (wd < 2) b0[wd * 4 + e] = (__bf16)f[e];
+                            else b1[(wd - 2) * 4 + e] = (__bf16)f[e];
+                            sm.vt[(part * 16 + wd * 4 + e) * Sm::VT + key] = (_Float16)f[e];
+                        }
                     }
-                }
-                *(v8bf*)(kr + part * 16) = b0;
-                *(v8bf*)(kr + part * 16 + 8) = b1;
-            } else {
-                const int rp = part - DN / 16;  // 8 rope dims per chunk
-                v4i raw = {0, 0, 0, 0};
-                if (code != -1) raw = *(const v4i*)(rope + r * 64 + rp * 8);
-                *(v4i*)(kr + DN + rp * 8) = raw;
-                const uint16_t* hv = (const uint16_t*)&raw;
+                    *(v8bf*)(kr + part * 16) = b0;
+                    *(v8bf*)(kr + part * 16 + 8) = b1;
+                } else {
+                    const int rp = part - DN / 16;  // 8 rope dims per chunk
+                    *(v4i*)(kr + DN + rp * 8) = raw;
+                    const uint16_t* hv = (const uint16_t*)&raw;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) sm.vt[(DN + rp * 8 + e) * Sm::VT + key] = (_Float16)bf16_bits_to_f32(hv[e]);
+                    for (int e = 0; e < 8; ++e)
+                        sm.vt[(DN + rp * 8 + e) * Sm::VT + key] = (_Float16)bf16_bits_to_f32(hv[e]);
+                }
             }
         }
+        // ---- resolve the next tile and put it in flight ----
+        const bool more = ut + KT < u1;
+        if (more && tid < KT) {
+            const int64_t u = ut + KT + tid;
+            float sc = 0.f;
+            sm.row[buf ^ 1][tid] = u < u1 ? resolve(u, t, sq, rk, idx, k, comp, win, sc) : -1;
+            sm.scl[buf ^ 1][tid] = sc;
+        }
         __syncthreads();
+        if (more) issue(buf ^ 1);
+        const float* scl = sm.scl[buf];
         // ---- S^T = K Q^T ----
         if (qk_active) {
 #pragma unroll
@@ -236,14 +274,19 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int key = ksub * 16 + 4 * g4 + i;
-                    const float sc = sm_scale * fmaf(sm.scl[key], an[i], ar[i]);
-                    sm.s[key * Sm::SS + hb * 16 + l16] = sm.valid[key] ? sc : -INFINITY;
+                    const float sc = sm_scale * fmaf(scl[key], an[i], ar[i]);
+                    sm.s[key * Sm::SS + hb * 16 + l16] = sm.row[buf][key] != -1 ? sc : -INFINITY;
                 }
             }
         }
         __syncthreads();
         // ---- online softmax: TPH threads per head, KPT keys each ----
         {
+            float st_max = 0.f;
+#pragma unroll 8
+            for (int i = 0; i < KT; ++i) st_max = fmaxf(st_max, scl[i]);
+            const float s_new = st_max > 0.f ? st_max : (s_ref > 0.f ? s_ref : 1.f);
+            const float inv_s = 1.f / s_new;
             float sv[KPT];
             float mx = -INFINITY;
 #pragma unroll
@@ -257,9 +300,11 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
             float sum = 0.f;
 #pragma unroll
             for (int i = 0; i < KPT; ++i) {
+                const int key = sk * KPT + i;
                 const float p = m_new == -INFINITY ? 0.f : __expf(sv[i] - m_new);
                 sum += p;
-                sm.p[sh * Sm::PS + sk * KPT + i] = (_Float16)p;
+                sm.pr[sh * Sm::PS + key] = (_Float16)p;
+                sm.pn[sh * Sm::PS + key] = (_Float16)(p * (scl[key] * inv_s));
             }
 #pragma unroll
             for (int o = 1; o < TPH; o <<= 1) sum += __shfl_xor(sum, o);
@@ -267,24 +312,32 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
             l_run = l_run * alpha + sum;
             m_run = m_new;
             if (sk == 0) sm.alpha[sh] = alpha;
+            if (tid == 0) sm.sfac[buf] = s_ref > 0.f ? s_ref * inv_s : 1.f;
+            s_ref = s_new;
         }
         __syncthreads();
         // ---- O^T += V^T P^T over this wave's dims ----
         {
+            const float sf = sm.sfac[buf];
             float al[HT];
 #pragma unroll
             for (int b = 0; b < HT; ++b) al[b] = sm.alpha[b * 16 + l16];
-            v8h pf[HT];
+            v8h pfn[HT], pfr[HT];
 #pragma unroll
-            for (int b = 0; b < HT; ++b) pf[b] = *(const v8h*)(sm.p + (b * 16 + l16) * Sm::PS + 8 * g4);
+            for (int b = 0; b < HT; ++b) {
+                pfn[b] = *(const v8h*)(sm.pn + (b * 16 + l16) * Sm::PS + 8 * g4);
+                pfr[b] = *(const v8h*)(sm.pr + (b * 16 + l16) * Sm::PS + 8 * g4);
+            }
 #pragma unroll
             for (int a = 0; a < DT; ++a) {
-                const int dim = wave * DW + a * 16 + l16;
-                const v8h vf = *(const v8h*)(sm.vt + dim * Sm::VT + 8 * g4);
+                const int d0 = wave * DW + a * 16;
+                const v8h vf = *(const v8h*)(sm.vt + (d0 + l16) * Sm::VT + 8 * g4);
+                const bool nope_tile = d0 < DN;
 #pragma unroll
                 for (int b = 0; b < HT; ++b) {
-                    acc[a][b] *= al[b];
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[b], acc[a][b], 0, 0, 0);
+                    acc[a][b] *= nope_tile ? al[b] * sf : al[b];
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, nope_tile ? pfn[b] : pfr[b], acc[a][b], 0,
+                                                                       0, 0);
                 }
             }
         }
@@ -296,7 +349,9 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
         sm.mrun[sh] = m_run;
         sm.lrun[sh] = l_run;
     }
+    if (tid == 0) sm.sfac[0] = s_ref > 0.f ? s_ref : 1.f;
     __syncthreads();
+    const float sfin = sm.sfac[0];
     // lane holds dims wave*DW + a*16 + 4*g4 + i for head b*16 + l16
 #pragma unroll
     for (int b = 0; b < HT; ++b) {
@@ -306,7 +361,7 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
         for (int a = 0; a < DT; ++a) {
             const int d0 = wave * DW + a * 16 + 4 * g4;
             float o[4];
-            const float f = d0 < DN ? sref : 1.f;
+            const float f = d0 < DN ? sfin : 1.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = acc[a][b][i] * f;
             if (S == 1) {
@@ -316,8 +371,8 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
                 if (d0 >= DN) {
 #pragma unroll
                     for (int i = 0; i < 4; i += 2) {
-                        float cs, sn;
-                        rope_cs(-(double)tp, base, (d0 - DN + i) >> 1, cs, sn);
+                        const int pi = (d0 - DN + i) >> 1;
+                        const float cs = sm.cs[2 * pi], sn = -sm.cs[2 * pi + 1];  // rotation by -t
                         const float x0 = o[i], x1 = o[i + 1];
                         o[i] = x0 * cs - x1 * sn;
                         o[i + 1] = x0 * sn + x1 * cs;
@@ -338,40 +393,69 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
     }
 }
 
-// merge S split partials of one (row, head): fixed order s = 0 .. S-1
+// Merge the S split partials of one (row, head) in the fixed order s = 0 .. S-1.
 template <int D>
 __global__ __launch_bounds__(128) void k_mqa_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                                                     const int64_t* __restrict__ pos, int H, int S, double base,
+                                                     const int64_t* __restrict__ pos, int H, int S, RopeTab rt,
                                                      float* __restrict__ out, float* __restrict__ lse) {
     constexpr int DN = D - 64;
+    constexpr int SMAX = 64;
+    __shared__ float wgt[SMAX];
+    __shared__ float red[2];
     const int64_t th = blockIdx.x;  // t*H + h
     const int64_t t = th / H;
     const int h = (int)(th % H);
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, part_ml[((t * S + s) * H + h) * 2]);
-    float L = 0.f;
-    for (int s = 0; s < S; ++s) {
-        const float ms = part_ml[((t * S + s) * H + h) * 2], ls = part_ml[((t * S + s) * H + h) * 2 + 1];
-        L += ms == -INFINITY ? 0.f : ls * __expf(ms - M);
+    const int tid = threadIdx.x;
+    if (tid < 64) {
+        float ms = -INFINITY, ls = 0.f;
+        if (tid < S) {
+            ms = part_ml[((t * S + tid) * H + h) * 2];
+            ls = part_ml[((t * S + tid) * H + h) * 2 + 1];
+        }
+        const float M = wave_max(ms);
+        const float e = ms == -INFINITY ? 0.f : __expf(ms - M);
+        float L = ls * e;
+        // fixed-order sum over splits: lane 0 accumulates sequentially
+        float Lseq = 0.f;
+        for (int i = 0; i < S; ++i) Lseq += __shfl(L, i);
+        if (tid < S) wgt[tid] = Lseq > 0.f ? e / Lseq : 0.f;
+        if (tid == 0) {
+            red[0] = M;
+            red[1] = Lseq;
+        }
     }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    for (int d0 = threadIdx.x * 4; d0 < D; d0 += 128 * 4) {
+    __syncthreads();
+    for (int d0 = tid * 4; d0 < D; d0 += 128 * 4) {
         float o[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < S; ++s) {
-            const float ms = part_ml[((t * S + s) * H + h) * 2];
-            if (ms == -INFINITY) continue;
-            const float wgt = __expf(ms - M) * inv;
-            const float4 v = *(const float4*)(part_o + ((t * S + s) * H + h) * (int64_t)D + d0);
-            o[0] = fmaf(wgt, v.x, o[0]);
-            o[1] = fmaf(wgt, v.y, o[1]);
-            o[2] = fmaf(wgt, v.z, o[2]);
-            o[3] = fmaf(wgt, v.w, o[3]);
+        const float* base = part_o + (t * S * H + h) * (int64_t)D + d0;
+        int s = 0;
+        for (; s + 8 <= S; s += 8) {
+            float4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = *(const float4*)(base + (int64_t)(s + u) * H * D);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float wv = wgt[s + u];
+                o[0] = fmaf(wv, v[u].x, o[0]);
+                o[1] = fmaf(wv, v[u].y, o[1]);
+                o[2] = fmaf(wv, v[u].z, o[2]);
+                o[3] = fmaf(wv, v[u].w, o[3]);
+            }
+        }
+        for (; s < S; ++s) {
+            const float4 v = *(const float4*)(base + (int64_t)s * H * D);
+            const float wv = wgt[s];
+            o[0] = fmaf(wv, v.x, o[0]);
+            o[1] = fmaf(wv, v.y, o[1]);
+            o[2] = fmaf(wv, v.z, o[2]);
+            o[3] = fmaf(wv, v.w, o[3]);
         }
         if (d0 >= DN) {
             const double tp = (double)pos[t];
             for (int i = 0; i < 4; i += 2) {
                 float cs, sn;
-                rope_cs(-tp, base, (d0 - DN + i) >> 1, cs, sn);
+                angle_cs(tp, rt.theta[(d0 - DN + i) >> 1], cs, sn);
+                sn = -sn;  // rotation by -t
                 const float x0 = o[i], x1 = o[i + 1];
                 o[i] = x0 * cs - x1 * sn;
                 o[i + 1] = x0 * sn + x1 * cs;
@@ -379,7 +463,7 @@ __global__ __launch_bounds__(128) void k_mqa_combine(const float* __restrict__ p
         }
         *(float4*)(out + th * D + d0) = make_float4(o[0], o[1], o[2], o[3]);
     }
-    if (threadIdx.x == 0) lse[th] = L > 0.f ? M + __logf(L) : -INFINITY;
+    if (tid == 0) lse[th] = red[1] > 0.f ? red[0] + __logf(red[1]) : -INFINITY;
 }
 
 static int choose_splits(int64_t T, int64_t max_keys) {
@@ -399,18 +483,18 @@ size_t mqa_workspace_bytes(int64_t T, int H, int d, int64_t max_keys) {
 
 template <int H, int D>
 static void launch_mqa_t(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, const int32_t* idx,
-                         int k, int m, KvView comp, KvView win, int window, float sm_scale, double base, int S,
+                         int k, int m, KvView comp, KvView win, int window, float sm_scale, const RopeTab& rt, int S,
                          float* out, float* lse, float* po, float* pml, hipStream_t st) {
     hipLaunchKernelGGL((k_mqa<H, D>), dim3((unsigned)(T * S)), dim3(256), 0, st, q, seq, pos, idx, k, m, comp, win,
-                       window, sm_scale, base, S, out, lse, po, pml);
+                       window, sm_scale, rt, S, out, lse, po, pml);
     if (S > 1)
-        hipLaunchKernelGGL((k_mqa_combine<D>), dim3((unsigned)(T * H)), dim3(128), 0, st, po, pml, pos, H, S, base, out,
+        hipLaunchKernelGGL((k_mqa_combine<D>), dim3((unsigned)(T * H)), dim3(128), 0, st, po, pml, pos, H, S, rt, out,
                            lse);
 }
 
 hipError_t launch_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int H, int d,
                       const int32_t* idx, int k, int m, int64_t max_keys, KvView comp, KvView win, int window,
-                      float sm_scale, double base, float* out, float* lse, void* ws, hipStream_t st) {
+                      float sm_scale, const RopeTab& rt, float* out, float* lse, void* ws, hipStream_t st) {
     if (T == 0) return hipSuccess;
     const int S = choose_splits(T, max_keys);
     float* po = nullptr;
@@ -419,7 +503,8 @@ hipError_t launch_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos,
         po = (float*)ws;
         pml = po + (size_t)T * S * H * d;
     }
-#define CSA_MQA(HH, DD) launch_mqa_t<HH, DD>(q, seq, pos, T, idx, k, m, comp, win, window, sm_scale, base, S, out, lse, po, pml, st)
+#define CSA_MQA(HH, DD) \
+    launch_mqa_t<HH, DD>(q, seq, pos, T, idx, k, m, comp, win, window, sm_scale, rt, S, out, lse, po, pml, st)
     if (d == 512) {
         if (H == 64) CSA_MQA(64, 512);
         else if (H == 32) CSA_MQA(32, 512);

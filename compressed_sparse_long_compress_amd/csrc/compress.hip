@@ -30,7 +30,7 @@ __device__ __forceinline__ float f64_to_f32_odd(double d) {
 
 template <int D>
 __global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ kv, const float* __restrict__ logits,
-                                                  int64_t tok0, int64_t n_blk, int m, double base, int64_t row0,
+                                                  int64_t tok0, int64_t n_blk, int m, RopeTab rt, int64_t row0,
                                                   int64_t cap, uint8_t* __restrict__ nope, uint16_t* __restrict__ rope,
                                                   float* __restrict__ scale) {
     constexpr int DN = D - 64;
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ k
         const double p = (double)((J + 1) * (int64_t)m - 1);
 #pragma unroll
         for (int e = 0; e < PER; e += 2) {
-            const double theta = pow(base, -2.0 * (double)((dim0 - DN + e) >> 1) / 64.0);
+            const double theta = rt.theta[(dim0 - DN + e) >> 1];
             const double a = __dmul_rn(p, theta);
             const double cs = cos(a), sn = sin(a);
             const double x0 = c[e], x1 = c[e + 1];
@@ -138,16 +138,16 @@ __global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ k
 }
 
 hipError_t launch_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t n_tok, int m, int d,
-                           double base, int64_t row0, int64_t cap, uint8_t* nope, uint16_t* rope, float* scale,
+                           const RopeTab& rt, int64_t row0, int64_t cap, uint8_t* nope, uint16_t* rope, float* scale,
                            hipStream_t st) {
     const int64_t n_blk = n_tok / m;
     if (n_blk == 0) return hipSuccess;
     dim3 grid((unsigned)((n_blk + 3) / 4)), block(256);
     if (d == 512)
-        hipLaunchKernelGGL(k_compress<512>, grid, block, 0, st, kv, logits, tok0, n_blk, m, base, row0, cap, nope,
+        hipLaunchKernelGGL(k_compress<512>, grid, block, 0, st, kv, logits, tok0, n_blk, m, rt, row0, cap, nope,
                            rope, scale);
     else
-        hipLaunchKernelGGL(k_compress<128>, grid, block, 0, st, kv, logits, tok0, n_blk, m, base, row0, cap, nope,
+        hipLaunchKernelGGL(k_compress<128>, grid, block, 0, st, kv, logits, tok0, n_blk, m, rt, row0, cap, nope,
                            rope, scale);
     return hipGetLastError();
 }

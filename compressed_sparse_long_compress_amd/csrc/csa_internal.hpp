@@ -6,8 +6,14 @@
 
 namespace csa {
 
+// RoPE frequencies theta_i = base^(-2i/64), i < 32, evaluated once on the host in fp64.
+struct RopeTab {
+    double theta[32];
+};
+RopeTab rope_table(double base);
+
 hipError_t launch_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t n_tok, int m, int d,
-                           double base, int64_t row0, int64_t cap, uint8_t* nope, uint16_t* rope, float* scale,
+                           const RopeTab& rt, int64_t row0, int64_t cap, uint8_t* nope, uint16_t* rope, float* scale,
                            hipStream_t st);
 
 hipError_t launch_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
@@ -30,6 +36,6 @@ size_t mqa_workspace_bytes(int64_t T, int H, int d, int64_t max_keys);
 // idx == nullptr selects the dense (HCA) key set
 hipError_t launch_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int H, int d,
                       const int32_t* idx, int k, int m, int64_t max_keys, KvView comp, KvView win, int window,
-                      float sm_scale, double base, float* out, float* lse, void* ws, hipStream_t st);
+                      float sm_scale, const RopeTab& rt, float* out, float* lse, void* ws, hipStream_t st);
 
 }  // namespace csa

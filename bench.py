@@ -2,7 +2,8 @@
 
 One step = the CSA decode hot path for a batch of 4 sequences, each with a
 1,048,576-token context (262,144 compressed entries at m=4):
-    csa_index_scores (MXFP4 indexer over every entry)
+    csa_index_scores (MXFP4 indexer over every entry; it also builds the
+                      first radix histogram of the selection)
  -> csa_topk (k = 1024)
  -> csa_sparse_mqa (64 query heads over the 1024 selected entries + a
     128-token window, d = 512).
@@ -78,8 +79,7 @@ class DecodeSet:
         self.idx = torch.empty(T, wl["k"], dtype=torch.int32, device="cuda")
         self.out = torch.empty(T, wl["H"], wl["d"], dtype=torch.float32, device="cuda")
         self.lse = torch.empty(T, wl["H"], dtype=torch.float32, device="cuda")
-        tws = csa.csa_topk_workspace(T, wl["n_cols"], wl["k"])
-        self.tws = torch.empty(max(tws, 1), dtype=torch.uint8, device="cuda")
+        self.tws = csa.topk_workspace(T, wl["n_cols"], wl["k"])
         mws = csa.csa_mqa_workspace(T, wl["H"], wl["d"], wl["k"] + W)
         self.mws = torch.empty(max(mws, 1), dtype=torch.uint8, device="cuda")
         self.replicas = replicas
@@ -89,13 +89,13 @@ class DecodeSet:
 
         wl = self.wl
         csa.csa_index_scores(self.iq, self.iqs, self.w, self.seq, self.pos, self.keys[r], wl["m"], wl["n_cols"],
-                             out=self.scores)
+                             out=self.scores, topk_ws=self.tws)
 
     def topk(self, r):
         import compressed_sparse_long_compress_amd as csa
 
         wl = self.wl
-        csa.csa_topk(self.scores, self.pos, wl["m"], wl["k"], out=self.idx, ws=self.tws)
+        csa.csa_topk(self.scores, self.pos, wl["m"], wl["k"], out=self.idx, ws=self.tws, hist_ready=True)
 
     def attend(self, r):
         import compressed_sparse_long_compress_amd as csa

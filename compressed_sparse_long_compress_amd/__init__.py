@@ -36,10 +36,11 @@ class _IdxKeys(ctypes.Structure):
 
 _vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 _lib.csa_compress.argtypes = [_vp, _vp, _i64, _i64, _i32, _i32, _f32, _i32, _Kv, _vp]
-_lib.csa_index_scores.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _IdxKeys, _i32, _i64, _vp, _vp]
+_lib.csa_index_scores.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _IdxKeys, _i32, _i64, _vp, _vp, _sz, _vp]
 _lib.csa_topk_workspace.restype = _sz
 _lib.csa_topk_workspace.argtypes = [_i64, _i64, _i32]
-_lib.csa_topk.argtypes = [_vp, _i64, _i64, _vp, _i32, _i32, _vp, _vp, _sz, _vp]
+_lib.csa_topk.argtypes = [_vp, _i64, _i64, _vp, _i32, _i32, _vp, _vp, _sz, ctypes.c_uint32, _vp]
+CSA_TOPK_HIST_READY = 1
 _lib.csa_mqa_workspace.restype = _sz
 _lib.csa_mqa_workspace.argtypes = [_i64, _i32, _i32, _i64]
 _lib.csa_sparse_mqa.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _i32, _Kv, _Kv, _i32, _f32, _f32, _vp,
@@ -147,8 +148,11 @@ def csa_compress(kv, logits, tok0, m, seq, out, rope_base=10000.0):
     return out
 
 
-def csa_index_scores(q, q_scale, w, seq, pos, keys, m, n_cols, out=None):
-    """MXFP4 indexer scores: q uint8 [T, h_i, d_i/2], q_scale uint8 [T, h_i, d_i/32], w fp32 [T, h_i] -> fp32 [T, n_cols]."""
+def csa_index_scores(q, q_scale, w, seq, pos, keys, m, n_cols, out=None, topk_ws=None):
+    """MXFP4 indexer scores: q uint8 [T, h_i, d_i/2], q_scale uint8 [T, h_i, d_i/32], w fp32 [T, h_i] -> fp32 [T, n_cols].
+
+    topk_ws: the (zero-filled) workspace of the csa_topk call that follows; the
+    indexer then also builds its histogram, and that call passes hist_ready=True."""
     _need(q, "q", torch.uint8, 3)
     _need(q_scale, "q_scale", torch.uint8, 3)
     _need(w, "w", torch.float32, 2)
@@ -166,7 +170,8 @@ def csa_index_scores(q, q_scale, w, seq, pos, keys, m, n_cols, out=None):
     if tuple(out.shape) != (T, n_cols):
         raise ValueError("scores must be [T, n_cols]")
     _check(_lib.csa_index_scores(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(seq), _ptr(pos), T, h_i, d_i, keys.c(), int(m),
-                                 int(n_cols), _ptr(out), _stream()))
+                                 int(n_cols), _ptr(out), _ptr(topk_ws), topk_ws.numel() if topk_ws is not None else 0,
+                                 _stream()))
     return out
 
 
@@ -174,20 +179,26 @@ def csa_topk_workspace(T, n_cols, k):
     return int(_lib.csa_topk_workspace(int(T), int(n_cols), int(k)))
 
 
-def csa_topk(scores, pos, m, k, out=None, ws=None):
-    """Top-k per row (score desc, index asc) in ascending index order, -1 padded -> int32 [T, k]."""
+def topk_workspace(T, n_cols, k, device="cuda"):
+    """A zero-filled top-k workspace (the library leaves it zero-filled after every call)."""
+    need = csa_topk_workspace(T, n_cols, k)
+    return torch.zeros(max(need, 1), dtype=torch.uint8, device=device)
+
+
+def csa_topk(scores, pos, m, k, out=None, ws=None, hist_ready=False):
+    """Top-k per row (score desc, index asc) in ascending index order, -1 padded -> int32 [T, k].
+
+    ws: a zero-filled uint8 workspace of csa_topk_workspace(T, n_cols, k) bytes (allocated when None)."""
     _need(scores, "scores", torch.float32, 2)
     _need(pos, "pos", torch.int64, 1)
     T, n_cols = scores.shape
     if out is None:
         out = torch.empty(T, k, dtype=torch.int32, device=scores.device)
     _need(out, "idx", torch.int32, 2)
-    need = csa_topk_workspace(T, n_cols, k)
-    if ws is None and need > 0:
-        ws = torch.empty(need, dtype=torch.uint8, device=scores.device)
-    ws_bytes = ws.numel() if ws is not None else 0
-    _check(_lib.csa_topk(_ptr(scores), T, n_cols, _ptr(pos), int(m), int(k), _ptr(out), _ptr(ws), ws_bytes,
-                         _stream()))
+    if ws is None:
+        ws = topk_workspace(T, n_cols, k, scores.device)
+    _check(_lib.csa_topk(_ptr(scores), T, n_cols, _ptr(pos), int(m), int(k), _ptr(out), _ptr(ws), ws.numel(),
+                         CSA_TOPK_HIST_READY if hist_ready else 0, _stream()))
     return out
 
 

@@ -101,7 +101,7 @@ int csa_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t 
 
 int csa_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
                      const int64_t* pos, int64_t T, int32_t h_i, int32_t d_i, csa_index_keys_t keys, int32_t m,
-                     int64_t n_cols, float* scores, csa_stream_t stream) {
+                     int64_t n_cols, float* scores, void* topk_ws, size_t topk_ws_bytes, csa_stream_t stream) {
     const char* fn = "csa_index_scores";
     if (T < 0 || n_cols < 0) return fail(CSA_EINVAL, "%s: T and n_cols must be >= 0", fn);
     if (h_i != 4 && h_i != 8) return fail(CSA_EUNSUPPORTED, "%s: h_i=%d unsupported (4 or 8)", fn, h_i);
@@ -113,15 +113,23 @@ int csa_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, c
     if (keys.cap < n_cols) return fail(CSA_EINVAL, "%s: n_cols (%lld) > keys.cap (%lld)", fn, (long long)n_cols,
                                        (long long)keys.cap);
     if (!aligned16(q) || !aligned16(keys.data)) return fail(CSA_EINVAL, "%s: q and keys.data must be 16-byte aligned", fn);
+    void* hist = nullptr;
+    if (topk_ws && csa::topk_uses_hist(T, n_cols)) {
+        // the histogram lives in the first T row blocks of the top-k workspace
+        if (topk_ws_bytes < csa::topk_workspace_bytes(T, n_cols, 1))
+            return fail(CSA_EWORKSPACE, "%s: top-k workspace too small for the histogram", fn);
+        if (((uintptr_t)topk_ws & 255u) != 0) return fail(CSA_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+        hist = topk_ws;
+    }
     hipError_t e = csa::launch_index_scores(q, q_scale, w, seq, pos, T, h_i, d_i, keys.data, keys.scale, keys.cap, m,
-                                            n_cols, scores, (hipStream_t)stream);
+                                            n_cols, scores, hist, (hipStream_t)stream);
     return hip_status(e, fn);
 }
 
 size_t csa_topk_workspace(int64_t T, int64_t n_cols, int32_t k) { return csa::topk_workspace_bytes(T, n_cols, k); }
 
 int csa_topk(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos, int32_t m, int32_t k, int32_t* idx,
-             void* ws, size_t ws_bytes, csa_stream_t stream) {
+             void* ws, size_t ws_bytes, uint32_t flags, csa_stream_t stream) {
     const char* fn = "csa_topk";
     if (T < 0 || n_cols < 0) return fail(CSA_EINVAL, "%s: T and n_cols must be >= 0", fn);
     if (k < 1 || k > 2048) return fail(CSA_EUNSUPPORTED, "%s: k=%d outside 1..2048", fn, k);
@@ -132,7 +140,10 @@ int csa_topk(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos,
     const size_t need = csa::topk_workspace_bytes(T, n_cols, k);
     if (ws_bytes < need || (need > 0 && !ws))
         return fail(CSA_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
-    hipError_t e = csa::launch_topk(scores, T, n_cols, pos, m, k, idx, ws, (hipStream_t)stream);
+    if (need > 0 && ((uintptr_t)ws & 255u) != 0) return fail(CSA_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+    if (flags & ~(uint32_t)CSA_TOPK_HIST_READY) return fail(CSA_EINVAL, "%s: unknown flags 0x%x", fn, flags);
+    const bool ready = (flags & CSA_TOPK_HIST_READY) && csa::topk_uses_hist(T, n_cols);
+    hipError_t e = csa::launch_topk(scores, T, n_cols, pos, m, k, idx, ws, ready, (hipStream_t)stream);
     return hip_status(e, fn);
 }
 

@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
             const int c = tid + i * 256;
             pre[i] = v4i{0, 0, 0, 0};
             if (c < KT * CPK) {
-                const int key = c / CPK, part = c % CPK;
+                const int key = c % KT, part = c / KT;  // lanes of a wave: consecutive keys of one chunk column
                 const int64_t code = sm.row[buf][key];
                 if (code != -1) {
                     const bool w = code <= -2;
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
         for (int i = 0; i < NCH; ++i) {
             const int c = tid + i * 256;
             if (c < KT * CPK) {
-                const int key = c / CPK, part = c % CPK;
+                const int key = c % KT, part = c / KT;  // lanes of a wave: consecutive keys of one chunk column
                 __bf16* kr = sm.kr + key * Sm::KR;
                 const v4i raw = pre[i];
                 if (part < DN / 16) {

@@ -32,13 +32,19 @@ __global__ __launch_bounds__(256) void k_index_rows(const uint8_t* __restrict__ 
                                                     const int64_t* __restrict__ pos, int h_i,
                                                     const uint8_t* __restrict__ kdata,
                                                     const uint8_t* __restrict__ kscale, int64_t kcap, int m,
-                                                    int64_t n_cols, int64_t chunk, float* __restrict__ scores) {
+                                                    int64_t n_cols, int64_t chunk, float* __restrict__ scores,
+                                                    char* __restrict__ hist_ws) {
     constexpr int KB = DI / 2;   // bytes per key
     constexpr int NB = DI / 32;  // scale blocks per key
     constexpr int U = 8;         // tiles in flight per wave
+    __shared__ uint32_t hh[4096];  // top-12-bit key histogram of this chunk (when hist_ws)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t t = blockIdx.y;
     const int r = lane & 15, g = lane >> 4;
+    if (hist_ws) {
+        for (int i = threadIdx.x; i < 4096; i += 256) hh[i] = 0;
+        __syncthreads();
+    }
 
     v8i a = {0, 0, 0, 0, 0, 0, 0, 0};
     int sa = 127;
@@ -84,8 +90,17 @@ __global__ __launch_bounds__(256) void k_index_rows(const uint8_t* __restrict__ 
             p += __shfl_xor(p, 16);
             p += __shfl_xor(p, 32);
             const int64_t j = j0 + u * 16 + lane;
-            if (lane < 16 && j < c1) out[j] = j < nv ? p : -INFINITY;
+            if (lane < 16 && j < c1) {
+                out[j] = j < nv ? p : -INFINITY;
+                if (hist_ws && j < nv) atomicAdd(&hh[f32_order_key(p) >> 20], 1u);
+            }
         }
+    }
+    if (hist_ws) {
+        __syncthreads();
+        uint32_t* gh = (uint32_t*)(hist_ws + (size_t)t * kTopkRowBlock);
+        for (int i = threadIdx.x; i < 4096; i += 256)
+            if (hh[i]) atomicAdd(&gh[i], hh[i]);
     }
 }
 
@@ -252,9 +267,9 @@ __global__ __launch_bounds__(256) void k_index_gemm(const uint8_t* __restrict__ 
 hipError_t launch_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
                                const int64_t* pos, int64_t T, int h_i, int d_i, const uint8_t* kdata,
                                const uint8_t* kscale, int64_t kcap, int m, int64_t n_cols, float* scores,
-                               hipStream_t st) {
+                               void* hist_ws, hipStream_t st) {
     if (T == 0 || n_cols == 0) return hipSuccess;
-    if (T <= 64) {
+    if (T <= 64 || hist_ws) {
         // aim for >= 1024 workgroups; each wave handles 128 keys per step
         int64_t chunk = (n_cols * T + 1023) / 1024;
         chunk = ((chunk + 511) / 512) * 512;
@@ -263,10 +278,10 @@ hipError_t launch_index_scores(const uint8_t* q, const uint8_t* q_scale, const f
         dim3 grid((unsigned)((n_cols + chunk - 1) / chunk), (unsigned)T), block(256);
         if (d_i == 128)
             hipLaunchKernelGGL(k_index_rows<128>, grid, block, 0, st, q, q_scale, w, seq, pos, h_i, kdata, kscale,
-                               kcap, m, n_cols, chunk, scores);
+                               kcap, m, n_cols, chunk, scores, (char*)hist_ws);
         else
             hipLaunchKernelGGL(k_index_rows<64>, grid, block, 0, st, q, q_scale, w, seq, pos, h_i, kdata, kscale, kcap,
-                               m, n_cols, chunk, scores);
+                               m, n_cols, chunk, scores, (char*)hist_ws);
         return hipGetLastError();
     }
     const int qwg = 4 * 4 * (32 / h_i);  // queries per workgroup

@@ -163,47 +163,62 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_row(const float* __restri
 
 // ---------------------------------------------------------------------------
 // Few long rows (decode): the row is split over many workgroups.
-//   k_topkm_clear    zero the row's histogram and counters
 //   k_topkm_hist     per chunk, LDS histogram of the top 12 key bits, added
-//                    to the row's global histogram (integer atomics)
+//                    to the row's global histogram (integer atomics); the
+//                    indexer kernel can do the same while it writes scores
 //   k_topkm_collect  per chunk, every workgroup reads the row histogram,
 //                    finds the bin b1 holding the k-th largest key, appends
 //                    the indices of keys above b1 and the (key, index) pairs
-//                    inside b1; the last workgroup of the row (a counter
-//                    taken after a release fence) picks the remaining
-//                    need = k - #above among the candidates by radix select on
-//                    the composite (key, ~index), sorts the k indices and
-//                    writes the row.
+//                    inside b1 (one slot reservation per workgroup)
+//   k_topkm_final    one workgroup per row selects the remaining
+//                    need = k - #above candidates (radix select on the low
+//                    20 key bits, ties to the lower index), marks all k
+//                    indices in an LDS bitmap of the row and writes them in
+//                    ascending order; it then zeroes the row's histogram and
+//                    counters, so the workspace is left as it was found.
+// The hand-over between the two passes is a kernel boundary: a per-workgroup
+// agent-scope fence would write back the whole L2 (holding the freshly
+// written scores) once per workgroup.
+// Workspace: zero-filled before first use; every call leaves it zero-filled.
+// Layout: 128 row blocks of [4096 histogram bins + 16 counters] (the only
+// part that must start at zero), then T x k selected indices, then
+// T x n_cols candidates.
 // ---------------------------------------------------------------------------
 constexpr int kTmThreads = 256;
-constexpr int kCandLds = 12288;  // candidates held in LDS by the finalising workgroup
+constexpr int kTmE = 8;  // consecutive columns per thread in the collect pass
+constexpr int kBitmapWords = 16384;  // row bitmap of the finaliser: rows up to 524,288 columns
+constexpr int kCandLds = 4096;       // candidates the finaliser stages in LDS
+constexpr int kTieLds = 256;         // equal-key sets up to this size are ranked directly
+constexpr size_t kTmRowBlock = kTopkRowBlock;
 
 struct TmRow {
-    uint32_t* hist;  // [4096]
-    uint32_t* ctr;   // [0] appended above, [1] candidates, [2] finished chunks
+    uint32_t* hist;   // [4096] top 12 key bits of the row
+    uint32_t* hist2;  // [4096] bits 19..8 of the candidates (keys in bin b1)
+    uint32_t* ctr;    // [0] indices above b1, [1] candidates, [4] b1, [5] #keys above b1
     int32_t* sel;    // [k]
-    uint64_t* cand;  // [n_cols] composite (key << 32 | ~index)
+    uint64_t* cand;  // [n_cols] (key << 32 | ~index)
 };
 
-__device__ __forceinline__ TmRow tm_row(void* ws, int64_t t, int64_t n_cols, int k) {
-    const size_t per = 4096 * 4 + 64 + (((size_t)k * 4 + 255) / 256) * 256 + (size_t)n_cols * 8;
-    char* b = (char*)ws + (size_t)t * per;
+// The histogram / counter rows occupy a fixed region sized for the most rows
+// the multi-workgroup path accepts, so the selected-index and candidate
+// regions of any call never overlap a row block of a later call.
+constexpr int kTmMaxRows = 128;
+__host__ __device__ __forceinline__ size_t tm_sel_off(int64_t) {
+    return ((size_t)kTmMaxRows * kTmRowBlock + 255) & ~(size_t)255;
+}
+__host__ __device__ __forceinline__ size_t tm_cand_off(int64_t T, int k) {
+    return (tm_sel_off(T) + (size_t)T * k * 4 + 255) & ~(size_t)255;
+}
+
+__device__ __forceinline__ TmRow tm_row(void* ws, int64_t T, int64_t t, int64_t n_cols, int k) {
+    char* b = (char*)ws;
     TmRow r;
-    r.hist = (uint32_t*)b;
-    r.ctr = (uint32_t*)(b + 4096 * 4);
-    r.sel = (int32_t*)(b + 4096 * 4 + 64);
-    r.cand = (uint64_t*)(b + 4096 * 4 + 64 + (((size_t)k * 4 + 255) / 256) * 256);
+    r.hist = (uint32_t*)(b + (size_t)t * kTmRowBlock);
+    r.hist2 = r.hist + 4096;
+    r.ctr = r.hist2 + 4096;
+    r.sel = (int32_t*)(b + tm_sel_off(T)) + t * (int64_t)k;
+    r.cand = (uint64_t*)(b + tm_cand_off(T, k)) + t * n_cols;
     return r;
-}
-
-size_t topk_row_stride(int64_t n_cols, int k) {
-    return 4096 * 4 + 64 + (((size_t)k * 4 + 255) / 256) * 256 + (size_t)n_cols * 8;
-}
-
-__global__ __launch_bounds__(kTmThreads) void k_topkm_clear(void* ws, int64_t n_cols, int k) {
-    TmRow r = tm_row(ws, blockIdx.x, n_cols, k);
-    for (int i = threadIdx.x; i < 4096; i += kTmThreads) r.hist[i] = 0;
-    if (threadIdx.x < 16) r.ctr[threadIdx.x] = 0;
 }
 
 __device__ __forceinline__ int64_t row_visible(const int64_t* pos, int64_t t, int m, int64_t n_cols) {
@@ -213,7 +228,7 @@ __device__ __forceinline__ int64_t row_visible(const int64_t* pos, int64_t t, in
     return nv;
 }
 
-__global__ __launch_bounds__(kTmThreads) void k_topkm_hist(const float* __restrict__ scores, int64_t n_cols,
+__global__ __launch_bounds__(kTmThreads) void k_topkm_hist(const float* __restrict__ scores, int64_t T, int64_t n_cols,
                                                            const int64_t* __restrict__ pos, int m, int k, int64_t chunk,
                                                            void* ws) {
     __shared__ uint32_t h[4096];
@@ -238,9 +253,34 @@ __global__ __launch_bounds__(kTmThreads) void k_topkm_hist(const float* __restri
         }
     }
     __syncthreads();
-    TmRow r = tm_row(ws, t, n_cols, k);
+    TmRow r = tm_row(ws, T, t, n_cols, k);
     for (int i = threadIdx.x; i < 4096; i += kTmThreads)
         if (h[i]) atomicAdd(&r.hist[i], h[i]);
+}
+
+// Histograms handed to tm_find are stored "transposed": with PER = NB/256
+// bins per thread and bins ranked from the top (r = NB-1-bin), rank r sits
+// at position (r % PER) * 256 + r / PER.  Thread t then owns ranks
+// t*PER .. t*PER+PER-1 and reads them at positions i*256 + t: consecutive
+// threads, consecutive words, no LDS bank conflicts.
+template <int NB>
+__device__ __forceinline__ int tm_pos(uint32_t bin) {
+    constexpr int PER = NB / kTmThreads > 0 ? NB / kTmThreads : 1;
+    const int r = NB - 1 - (int)bin;
+    return (r % PER) * kTmThreads + r / PER;
+}
+
+// 4096-bin global histogram into the transposed LDS layout: thread t loads
+// its 16 consecutive bins (4 x 16 B, issued together) and scatters them.
+__device__ __forceinline__ void tm_load_hist(uint32_t* dst, const uint32_t* src) {
+    const int t = threadIdx.x;
+    uint4 v[4];
+    const uint4* p = (const uint4*)(src + 4096 - 16 * (t + 1));  // bins 4095-16t-15 .. 4095-16t
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = p[i];
+    const uint32_t* w = (const uint32_t*)v;  // w[q] = bin 4096-16(t+1)+q = rank 16t+15-q
+#pragma unroll
+    for (int q = 0; q < 16; ++q) dst[(15 - q) * kTmThreads + t] = w[q];
 }
 
 // exclusive scan over a 256-thread block
@@ -265,27 +305,31 @@ __device__ __forceinline__ int tm_scan(int v, int* wsum, int& total) {
     return off + x - v;
 }
 
-// bin (scanning from the top) where the running count reaches need; 256 threads
+// bin (scanning from the top) where the running count reaches need, on a
+// transposed histogram; 256 threads, one block scan.
 template <int NB>
 __device__ int tm_find(const uint32_t* hist, int need, int* wsum, int* bc, int& above) {
     constexpr int PER = NB / kTmThreads > 0 ? NB / kTmThreads : 1;
     const int tid = threadIdx.x;
+    uint32_t v[PER];
     int local = 0;
-    if (tid * PER < NB)
-        for (int i = 0; i < PER; ++i) local += (int)hist[NB - 1 - (tid * PER + i)];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        v[i] = tid * PER + i < NB ? hist[i * kTmThreads + tid] : 0u;
+        local += (int)v[i];
+    }
     int tot;
     const int before = tm_scan(local, wsum, tot);
-    if (tid * PER < NB && before < need && before + local >= need) {
+    if (before < need && before + local >= need) {
         int run = before;
+#pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int bin = NB - 1 - (tid * PER + i);
-            const int c = (int)hist[bin];
-            if (run + c >= need) {
-                bc[0] = bin;
+            if (run + (int)v[i] >= need) {
+                bc[0] = NB - 1 - (tid * PER + i);
                 bc[1] = run;
                 break;
             }
-            run += c;
+            run += (int)v[i];
         }
     }
     __syncthreads();
@@ -295,27 +339,14 @@ __device__ int tm_find(const uint32_t* hist, int need, int* wsum, int* bc, int& 
     return bin;
 }
 
-// wave-aggregated append: returns this lane's slot (valid when flag)
-__device__ __forceinline__ uint32_t tm_append(uint32_t* ctr, bool flag) {
-    const uint64_t mask = __ballot(flag);
-    const int lane = threadIdx.x & 63;
-    uint32_t base = 0;
-    const int leader = mask ? __builtin_ctzll(mask) : 0;
-    if (mask && lane == leader) base = atomicAdd(ctr, (uint32_t)__popcll(mask));
-    base = __shfl(base, leader);
-    return base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
-}
 
-__global__ __launch_bounds__(kTmThreads) void k_topkm_collect(const float* __restrict__ scores, int64_t n_cols,
-                                                              const int64_t* __restrict__ pos, int m, int k,
-                                                              int64_t chunk, int nchunk, void* ws,
+__global__ __launch_bounds__(kTmThreads) void k_topkm_collect(const float* __restrict__ scores, int64_t T,
+                                                              int64_t n_cols, const int64_t* __restrict__ pos, int m,
+                                                              int k, int64_t chunk, void* ws,
                                                               int32_t* __restrict__ idx) {
     __shared__ uint32_t h[4096];
-    __shared__ uint64_t cl[kCandLds];
-    __shared__ int32_t srt[2048];
     __shared__ int wsum[kTmThreads / 64];
     __shared__ int bc[4];
-    __shared__ int last;
     const int tid = threadIdx.x;
     const int64_t t = blockIdx.y;
     const int64_t nv = row_visible(pos, t, m, n_cols);
@@ -325,116 +356,285 @@ __global__ __launch_bounds__(kTmThreads) void k_topkm_collect(const float* __res
             for (int a = tid; a < k; a += kTmThreads) out[a] = a < nv ? a : -1;
         return;
     }
-    TmRow r = tm_row(ws, t, n_cols, k);
-    for (int i = tid; i < 4096; i += kTmThreads) h[i] = r.hist[i];
+    TmRow r = tm_row(ws, T, t, n_cols, k);
+    tm_load_hist(h, r.hist);
     __syncthreads();
     int above1;
     const uint32_t b1 = (uint32_t)tm_find<4096>(h, k, wsum, bc, above1);
 
+    // this chunk: E consecutive columns per thread, one slot reservation per workgroup
     const int64_t c0 = (int64_t)blockIdx.x * chunk;
     const int64_t c1 = c0 + chunk < nv ? c0 + chunk : nv;
     const float* row = scores + t * n_cols;
-    for (int64_t jb = c0; jb < c1; jb += kTmThreads) {
-        const int64_t j = jb + tid;
-        uint32_t key = 0;
-        if (j < c1) key = f32_order_key(row[j]);
-        const bool up = j < c1 && (key >> 20) > b1;
-        const bool eq = j < c1 && (key >> 20) == b1;
-        const uint32_t su = tm_append(&r.ctr[0], up);
-        if (up) r.sel[su] = (int32_t)j;
-        const uint32_t se = tm_append(&r.ctr[1], eq);
-        if (eq) r.cand[se] = ((uint64_t)key << 32) | (uint32_t)~(uint32_t)j;
+    for (int64_t jb = c0; jb < c1; jb += (int64_t)kTmThreads * kTmE) {
+        const int64_t j0 = jb + (int64_t)tid * kTmE;
+        uint32_t key[kTmE];
+        int n_up = 0, n_eq = 0;
+#pragma unroll
+        for (int e = 0; e < kTmE; ++e) {
+            const int64_t j = j0 + e;
+            key[e] = j < c1 ? f32_order_key(row[j]) : 0u;
+            n_up += (j < c1 && (key[e] >> 20) > b1) ? 1 : 0;
+            n_eq += (j < c1 && (key[e] >> 20) == b1) ? 1 : 0;
+        }
+        int tot;
+        const int pre = tm_scan(n_up | (n_eq << 16), wsum, tot);  // both counts < 2^16
+        if (tid == 0) {
+            const uint32_t tu = (uint32_t)tot & 0xFFFFu, te = (uint32_t)tot >> 16;
+            bc[2] = tu ? (int)atomicAdd(&r.ctr[0], tu) : 0;
+            bc[3] = te ? (int)atomicAdd(&r.ctr[1], te) : 0;
+        }
+        __syncthreads();
+        uint32_t su = (uint32_t)bc[2] + (uint32_t)(pre & 0xFFFF);
+        uint32_t se = (uint32_t)bc[3] + (uint32_t)(pre >> 16);
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < kTmE; ++e) {
+            const int64_t j = j0 + e;
+            if (j >= c1) continue;
+            const uint32_t bin = key[e] >> 20;
+            if (bin > b1) {
+                if (su < (uint32_t)k) r.sel[su] = (int32_t)j;
+                ++su;
+            } else if (bin == b1) {
+                r.cand[se++] = ((uint64_t)key[e] << 32) | (uint32_t)~(uint32_t)j;
+                atomicAdd(&r.hist2[(key[e] >> 8) & 0xFFF], 1u);
+            }
+        }
     }
-    // release this chunk's appends, count finished chunks
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) last = atomicAdd(&r.ctr[2], 1u) == (uint32_t)(nchunk - 1);
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
+    if (blockIdx.x == 0 && tid == 0) {
+        r.ctr[4] = b1;
+        r.ctr[5] = (uint32_t)above1;
+    }
+}
 
-    // ---- finalise the row: choose `need` candidates by (key desc, index asc) ----
-    const int n_up = (int)__atomic_load_n(&r.ctr[0], __ATOMIC_RELAXED);
-    const int n_cand = (int)__atomic_load_n(&r.ctr[1], __ATOMIC_RELAXED);
-    const int need = k - n_up;
-    const bool in_lds = n_cand <= kCandLds;
-    if (in_lds)
-        for (int i = tid; i < n_cand; i += kTmThreads) cl[i] = r.cand[i];
+// One workgroup per row: resolve the exact threshold from the candidate
+// histogram, mark every selected index in an LDS bitmap of the row (or sort
+// them when the row is too long for the bitmap), write the row in ascending
+// index order, and leave the row's histograms and counters zeroed.
+__global__ __launch_bounds__(kTmThreads) void k_topkm_final(int64_t T, int64_t n_cols, const int64_t* __restrict__ pos,
+                                                            int m, int k, void* ws, int32_t* __restrict__ idx) {
+    __shared__ uint32_t h[4096];
+    __shared__ uint32_t bm[kBitmapWords];  // row bitmap, or the index list to sort
+    __shared__ uint64_t cl[kCandLds];      // candidates
+    __shared__ uint32_t tie[kTieLds];      // indices of keys equal to the threshold
+    __shared__ int wsum[kTmThreads / 64];
+    __shared__ int bc[4];
+    __shared__ uint32_t lctr[3];
+    const int tid = threadIdx.x;
+    const int64_t t = blockIdx.x;
+    const int64_t nv = row_visible(pos, t, m, n_cols);
+    int32_t* out = idx + t * (int64_t)k;
+    if (nv <= k) return;  // written by the collect pass
+    TmRow r = tm_row(ws, T, t, n_cols, k);
+    const uint32_t b1 = r.ctr[4];
+    const int above1 = (int)r.ctr[5];
+    const int n_up = (int)r.ctr[0];
+    const int n_cand = (int)r.ctr[1];
+    const int64_t nwords = (nv + 31) / 32;
+    const bool use_bm = nwords <= kBitmapWords;  // kBitmapWords is a multiple of 256
+    tm_load_hist(h, r.hist2);
+    // bitmap word w belongs to thread w / perw and sits at (w % perw) * 256 + w / perw
+    const uint32_t perw = (uint32_t)((nwords + kTmThreads - 1) / kTmThreads);
+    if (use_bm)
+        for (uint32_t i = tid; i < perw * kTmThreads; i += kTmThreads) bm[i] = 0;
+    if (tid < 2) lctr[tid] = 0;
     __syncthreads();
-    auto cand_at = [&](int i) -> uint64_t { return in_lds ? cl[i] : r.cand[i]; };
-    // radix select over the 64-bit composite, 8 bits per pass, most significant first
-    uint64_t prefix = 0, pmask = 0;
-    int need_left = need;
-    for (int shift = 56; shift >= 0; shift -= 8) {
-        for (int i = tid; i < 256; i += kTmThreads) h[i] = 0;
+    int above2;
+    const int need = k - above1;
+    const uint32_t b2 = (uint32_t)tm_find<4096>(h, need, wsum, bc, above2);
+    auto mark = [&](uint32_t j) {
+        if (use_bm) {
+            if (j < (uint64_t)nv) {
+                const uint32_t wd = j >> 5;
+                atomicOr(&bm[(wd % perw) * kTmThreads + wd / perw], 1u << (j & 31));
+            }
+        } else {
+            const uint32_t o = atomicAdd(&lctr[1], 1u);
+            if (o < (uint32_t)k) bm[o] = j;
+        }
+    };
+    // candidates into LDS (batched loads), when they fit
+    const bool cand_lds = n_cand <= kCandLds;
+    if (cand_lds) {
+        for (int i0 = 0; i0 < n_cand; i0 += kTmThreads * 8) {
+            uint64_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * kTmThreads + tid;
+                v[u] = i < n_cand ? r.cand[i] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * kTmThreads + tid;
+                if (i < n_cand) cl[i] = v[u];
+            }
+        }
+    }
+    // keys above bin b1 (collected by the chunk pass), batched loads
+    {
+        const int nu = n_up < k ? n_up : k;
+        for (int a0 = 0; a0 < nu; a0 += kTmThreads * 8) {
+            int32_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int a = a0 + u * kTmThreads + tid;
+                v[u] = a < nu ? r.sel[a] : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (v[u] >= 0) mark((uint32_t)v[u]);
+        }
+    }
+    for (int i = tid; i < 256; i += kTmThreads) h[i] = 0;
+    __syncthreads();
+    auto cand_at = [&](int i) -> uint64_t { return cand_lds ? cl[i] : r.cand[i]; };
+    // candidates: mark those above b2, histogram the low 8 bits of those in b2
+    for (int i = tid; i < n_cand; i += kTmThreads) {
+        const uint64_t c = cand_at(i);
+        const uint32_t key = (uint32_t)(c >> 32), mid = (key >> 8) & 0xFFF;
+        if (mid > b2) mark(~(uint32_t)c);
+        else if (mid == b2) atomicAdd(&h[tm_pos<256>(key & 0xFF)], 1u);
+    }
+    __syncthreads();
+    int above3;
+    const uint32_t b3 = (uint32_t)tm_find<256>(h, need - above2, wsum, bc, above3);
+    const uint32_t thr = (b1 << 20) | (b2 << 8) | b3;
+    const int need_eq = need - above2 - above3;  // >= 1 keys equal to thr, lowest indices first
+    for (int i = tid; i < n_cand; i += kTmThreads) {
+        const uint64_t c = cand_at(i);
+        const uint32_t key = (uint32_t)(c >> 32);
+        if (((key >> 8) & 0xFFF) != b2) continue;
+        if (key > thr) mark(~(uint32_t)c);
+        else if (key == thr) atomicAdd(&lctr[0], 1u);
+    }
+    __syncthreads();
+    uint32_t idx_lim = 0xFFFFFFFFu;  // equal keys are taken up to this index
+    const int n_eq = (int)lctr[0];
+    if (n_eq > need_eq && n_eq <= kTieLds) {
+        // few equal keys: list them, rank each by index, keep the need_eq lowest
+        if (tid == 0) lctr[2] = 0;
         __syncthreads();
         for (int i = tid; i < n_cand; i += kTmThreads) {
             const uint64_t c = cand_at(i);
-            if ((c & pmask) == prefix) atomicAdd(&h[(c >> shift) & 0xFF], 1u);
+            if ((uint32_t)(c >> 32) == thr) tie[atomicAdd(&lctr[2], 1u)] = ~(uint32_t)c;
         }
         __syncthreads();
-        int above;
-        const uint32_t bin = (uint32_t)tm_find<256>(h, need_left, wsum, bc, above);
-        need_left -= above;
-        prefix |= (uint64_t)bin << shift;
-        pmask |= (uint64_t)0xFF << shift;
-    }
-    // composites are unique: select every candidate >= prefix (exactly `need` of them)
-    for (int i = tid; i < n_cand; i += kTmThreads) {
-        const uint64_t c = cand_at(i);
-        const bool take = c >= prefix;
-        const uint32_t s = tm_append(&r.ctr[0], take);
-        if (take) r.sel[s] = (int32_t)~(uint32_t)(c & 0xFFFFFFFFu);
-    }
-    __threadfence();
-    __syncthreads();
-    // ---- sort the k indices ascending (bitonic, padded to a power of two) ----
-    int np = 1;
-    while (np < k) np <<= 1;
-    for (int i = tid; i < np; i += kTmThreads) srt[i] = i < k ? r.sel[i] : INT32_MAX;
-    __syncthreads();
-    for (int size = 2; size <= np; size <<= 1)
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < np / 2; i += kTmThreads) {
-                const int lo = 2 * i - (i & (stride - 1));
-                const int hi = lo + stride;
-                const bool asc = (lo & size) == 0;
-                const int a = srt[lo], b = srt[hi];
-                if ((a > b) == asc) {
-                    srt[lo] = b;
-                    srt[hi] = a;
-                }
+        for (int i = tid; i < n_eq; i += kTmThreads) {
+            const uint32_t ji = tie[i];
+            int rank = 0;
+            for (int q = 0; q < n_eq; ++q) rank += tie[q] < ji ? 1 : 0;
+            if (rank == need_eq - 1) bc[2] = (int)ji;
+        }
+        __syncthreads();
+        idx_lim = (uint32_t)bc[2];
+        __syncthreads();
+    } else if (n_eq > need_eq) {
+        // the need_eq-th smallest index among equal keys (31-bit indices, 3 passes of 11 bits)
+        uint32_t pre = 0, pm = 0;
+        int nl = need_eq;
+        for (int sh = 22; sh >= 0; sh -= 11) {
+            for (int i = tid; i < 2048; i += kTmThreads) h[i] = 0;
+            __syncthreads();
+            for (int i = tid; i < n_cand; i += kTmThreads) {
+                const uint64_t c = cand_at(i);
+                if ((uint32_t)(c >> 32) != thr) continue;
+                const uint32_t jx = ~(uint32_t)c;
+                if ((jx & pm) == pre) atomicAdd(&h[tm_pos<2048>(2047 - ((jx >> sh) & 0x7FF))], 1u);  // smaller index, higher bin
             }
             __syncthreads();
+            int ab;
+            const uint32_t bn = 2047u - (uint32_t)tm_find<2048>(h, nl, wsum, bc, ab);
+            nl -= ab;
+            pre |= bn << sh;
+            pm |= 0x7FFu << sh;
         }
-    for (int a = tid; a < k; a += kTmThreads) out[a] = srt[a];
+        idx_lim = pre;
+    }
+    for (int i = tid; i < n_cand; i += kTmThreads) {
+        const uint64_t c = cand_at(i);
+        if ((uint32_t)(c >> 32) == thr && ~(uint32_t)c <= idx_lim) mark(~(uint32_t)c);
+    }
+    __syncthreads();
+    if (use_bm) {
+        // thread t owns words t*perw .. t*perw+perw-1 (reads free of bank conflicts)
+        int cnt = 0;
+        for (uint32_t i = 0; i < perw; ++i) cnt += __popc(bm[i * kTmThreads + tid]);
+        int tot;
+        int o = tm_scan(cnt, wsum, tot);
+        for (uint32_t i = 0; i < perw; ++i) {
+            uint32_t b = bm[i * kTmThreads + tid];
+            const int64_t wi = (int64_t)tid * perw + i;
+            while (b) {
+                const int bit = __builtin_ctz(b);
+                if (o < k) out[o] = (int32_t)(wi * 32 + bit);
+                ++o;
+                b &= b - 1;
+            }
+        }
+    } else {
+        // bitonic sort of the k marked indices
+        int np = 1;
+        while (np < k) np <<= 1;
+        for (int i = k + tid; i < np; i += kTmThreads) bm[i] = 0xFFFFFFFFu;
+        __syncthreads();
+        for (int size = 2; size <= np; size <<= 1)
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int i = tid; i < np / 2; i += kTmThreads) {
+                    const int lo = 2 * i - (i & (stride - 1));
+                    const int hi = lo + stride;
+                    const bool asc = (lo & size) == 0;
+                    const uint32_t a = bm[lo], b = bm[hi];
+                    if ((a > b) == asc) {
+                        bm[lo] = b;
+                        bm[hi] = a;
+                    }
+                }
+                __syncthreads();
+            }
+        for (int a = tid; a < k; a += kTmThreads) out[a] = (int32_t)bm[a];
+    }
+    // ---- leave the row's histograms and counters zero for the next call ----
+    for (int i = tid; i < 4096; i += kTmThreads) {
+        r.hist[i] = 0;
+        r.hist2[i] = 0;
+    }
+    if (tid < 16) r.ctr[tid] = 0;
 }
 
-static bool topk_multi(int64_t T, int64_t n_cols) { return T < 128 && n_cols > 4096; }
+static bool topk_multi(int64_t T, int64_t n_cols) { return T < kTmMaxRows && n_cols > 4096; }
 
 size_t topk_workspace_bytes(int64_t T, int64_t n_cols, int k) {
     if (!topk_multi(T, n_cols)) return 0;
-    return (size_t)T * topk_row_stride(n_cols, k) + 256;
+    return tm_cand_off(T, k) + (size_t)T * n_cols * 8;
+}
+
+int64_t topk_chunk(int64_t T, int64_t n_cols) {
+    int64_t chunk = (n_cols * T + 511) / 512;
+    chunk = ((chunk + 2047) / 2048) * 2048;
+    if (chunk < 2048) chunk = 2048;
+    if (chunk > 16384) chunk = 16384;
+    return chunk;
 }
 
 hipError_t launch_topk(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos, int m, int k, int32_t* idx,
-                       void* ws, hipStream_t st) {
+                       void* ws, bool hist_done, hipStream_t st) {
     if (T == 0) return hipSuccess;
     if (!topk_multi(T, n_cols)) {
         hipLaunchKernelGGL(k_topk_row, dim3((unsigned)T), dim3(kTopkThreads), 0, st, scores, n_cols, pos, m, k, idx);
         return hipGetLastError();
     }
-    int64_t chunk = (n_cols * T + 511) / 512;
-    chunk = ((chunk + 2047) / 2048) * 2048;
-    if (chunk < 2048) chunk = 2048;
-    if (chunk > 16384) chunk = 16384;
+    const int64_t chunk = topk_chunk(T, n_cols);
     const int nchunk = (int)((n_cols + chunk - 1) / chunk);
-    hipLaunchKernelGGL(k_topkm_clear, dim3((unsigned)T), dim3(kTmThreads), 0, st, ws, n_cols, k);
-    hipLaunchKernelGGL(k_topkm_hist, dim3((unsigned)nchunk, (unsigned)T), dim3(kTmThreads), 0, st, scores, n_cols, pos,
-                       m, k, chunk, ws);
-    hipLaunchKernelGGL(k_topkm_collect, dim3((unsigned)nchunk, (unsigned)T), dim3(kTmThreads), 0, st, scores, n_cols,
-                       pos, m, k, chunk, nchunk, ws, idx);
+    if (!hist_done)
+        hipLaunchKernelGGL(k_topkm_hist, dim3((unsigned)nchunk, (unsigned)T), dim3(kTmThreads), 0, st, scores, T, n_cols,
+                           pos, m, k, chunk, ws);
+    hipLaunchKernelGGL(k_topkm_collect, dim3((unsigned)nchunk, (unsigned)T), dim3(kTmThreads), 0, st, scores, T, n_cols,
+                       pos, m, k, chunk, ws, idx);
+    hipLaunchKernelGGL(k_topkm_final, dim3((unsigned)T), dim3(kTmThreads), 0, st, T, n_cols, pos, m, k, ws, idx);
     return hipGetLastError();
 }
+
+bool topk_uses_hist(int64_t T, int64_t n_cols) { return topk_multi(T, n_cols); }
 
 }  // namespace csa

@@ -140,13 +140,19 @@ int csa_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t 
  *   keys     index keys (key of entry j of seq s at row s*cap + j)
  *   n_cols   columns written per row (<= keys.cap)
  *   scores   [T][n_cols] fp32
+ *   topk_ws  optional (NULL, 0 to skip): the workspace of the csa_topk call
+ *            that will read these scores.  When given, the indexer also adds
+ *            each row's key histogram (the first radix pass of the selection)
+ *            into it, and that csa_topk call passes CSA_TOPK_HIST_READY so the
+ *            selection skips its own pass over the scores.  Results are the
+ *            same bit for bit either way.
  * h_i in {4, 8}; d_i in {64, 128}.  With power-of-two head weights and block
  * scales whose exponents span a few binades, every score is exact in fp32
  * (each E2M1 product is a multiple of 1/4 below 36 in magnitude).
  */
 int csa_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
                      const int64_t* pos, int64_t T, int32_t h_i, int32_t d_i, csa_index_keys_t keys, int32_t m,
-                     int64_t n_cols, float* scores, csa_stream_t stream);
+                     int64_t n_cols, float* scores, void* topk_ws, size_t topk_ws_bytes, csa_stream_t stream);
 
 /*
  * csa_topk — top-k selection ([xmsumi] § CSA: the top-k compressed entries
@@ -158,12 +164,17 @@ int csa_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, c
  * padded with -1.
  *   scores [T][n_cols] fp32 (NaN not supported);  idx [T][k] int32
  *   1 <= k <= 2048;  n_cols < 2^31
- * Workspace: csa_topk_workspace(T, n_cols, k) bytes, 256-byte aligned,
- * contents undefined on entry and exit (may be 0 bytes).
+ * Workspace: csa_topk_workspace(T, n_cols, k) bytes (may be 0), 256-byte
+ * aligned, ZERO-FILLED before its first use; every call leaves it
+ * zero-filled again, so one buffer serves any sequence of calls (any shapes)
+ * on one stream.  Calls that share a workspace must not run concurrently.
+ * flags: 0, or CSA_TOPK_HIST_READY when the preceding csa_index_scores call
+ * for these scores was given this workspace (it built the histogram).
  */
+#define CSA_TOPK_HIST_READY 1u
 size_t csa_topk_workspace(int64_t T, int64_t n_cols, int32_t k);
 int csa_topk(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos, int32_t m, int32_t k, int32_t* idx,
-             void* ws, size_t ws_bytes, csa_stream_t stream);
+             void* ws, size_t ws_bytes, uint32_t flags, csa_stream_t stream);
 
 /*
  * csa_sparse_mqa — CSA attention: multi-query attention (one shared KV head;

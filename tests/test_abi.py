@@ -58,19 +58,21 @@ def test_compress_validation(csa):
 def test_index_topk_validation(csa):
     L = csa._lib
     keys = csa._IdxKeys(None, None, 16)
-    rc = L.csa_index_scores(None, None, None, None, None, 4, 16, 128, keys, 4, 16, None, None)
+    rc = L.csa_index_scores(None, None, None, None, None, 4, 16, 128, keys, 4, 16, None, None, 0, None)
     assert rc == csa.CSA_EUNSUPPORTED
-    rc = L.csa_index_scores(None, None, None, None, None, 4, 8, 96, keys, 4, 16, None, None)
+    rc = L.csa_index_scores(None, None, None, None, None, 4, 8, 96, keys, 4, 16, None, None, 0, None)
     assert rc == csa.CSA_EUNSUPPORTED
     p = ctypes.c_void_p(256)
-    rc = L.csa_index_scores(p, p, p, p, p, 4, 8, 128, csa._IdxKeys(256, 256, 8), 4, 16, p, None)
+    rc = L.csa_index_scores(p, p, p, p, p, 4, 8, 128, csa._IdxKeys(256, 256, 8), 4, 16, p, None, 0, None)
     assert rc == csa.CSA_EINVAL and b"keys.cap" in L.csa_last_error()
-    rc = L.csa_topk(None, 4, 100, None, 4, 0, None, None, 0, None)
+    rc = L.csa_topk(None, 4, 100, None, 4, 0, None, None, 0, 0, None)
     assert rc == csa.CSA_EUNSUPPORTED
-    rc = L.csa_topk(None, 4, 100, None, 4, 4096, None, None, 0, None)
+    rc = L.csa_topk(None, 4, 100, None, 4, 4096, None, None, 0, 0, None)
     assert rc == csa.CSA_EUNSUPPORTED
-    rc = L.csa_topk(None, 0, 100, None, 4, 64, None, None, 0, None)
+    rc = L.csa_topk(None, 0, 100, None, 4, 64, None, None, 0, 0, None)
     assert rc == csa.CSA_OK
+    rc = L.csa_topk(p, 4, 100, p, 4, 64, p, None, 0, 8, None)
+    assert rc == csa.CSA_EINVAL and b"flags" in L.csa_last_error()
 
 
 def test_mqa_validation(csa):

@@ -26,7 +26,8 @@
 
 namespace csa {
 
-constexpr int KT = 32;  // keys per tile
+constexpr int KT = 32;   // keys per tile
+constexpr int RB = 256;  // key-list positions resolved per batch (8 tiles)
 
 template <int H, int D>
 struct MqaSmem {
@@ -44,8 +45,9 @@ struct MqaSmem {
     float mrun[H];
     float lrun[H];
     float cs[64];         // cos / sin of t * theta_i, i < 32
-    int64_t row[2][KT];   // resolved cache rows (double-buffered): >= 0 comp, <= -2 window, -1 masked
-    float scl[2][KT];
+    int64_t row[RB];      // cache rows of the current batch of key-list positions: >= 0 comp, <= -2 window, -1 masked
+    float scl[2][KT];     // entry scales of the tile (0 when masked)
+    int valid[2][KT];
     float sfac[2];        // ratio old S_tile / new S_tile for the FP8 accumulators
 };
 
@@ -65,23 +67,16 @@ __device__ __forceinline__ RowKeys row_keys(int64_t t, const int32_t* idx, int k
     return r;
 }
 
-// Key-list position u of row t -> encoded cache row (comp >= 0, window <= -2, masked -1) and its scale.
+// Key-list position u of row t -> encoded cache row (comp >= 0, window <= -2, masked -1).
 __device__ __forceinline__ int64_t resolve(int64_t u, int64_t t, int32_t sq, const RowKeys& rk, const int32_t* idx,
-                                           int k, const KvView& comp, const KvView& win, float& scl) {
+                                           int k, const KvView& comp, const KvView& win) {
     if (u < rk.n_c) {
         const int64_t j = idx ? (int64_t)idx[t * k + u] : u;
-        if (j < 0 || j >= rk.nv) {
-            scl = 0.f;
-            return -1;
-        }
-        const int64_t r = (int64_t)sq * comp.cap + (j % comp.cap);
-        scl = comp.scale[r];
-        return r;
+        if (j < 0 || j >= rk.nv) return -1;
+        return (int64_t)sq * comp.cap + (j % comp.cap);
     }
     const int64_t p = rk.lo + (u - rk.n_c);
-    const int64_t r = (int64_t)sq * win.cap + (p % win.cap);
-    scl = win.scale[r];
-    return -(r + 2);
+    return -((int64_t)sq * win.cap + (p % win.cap) + 2);
 }
 
 // cos / sin of pos * theta: fp64 product, fp64 reduction by 2*pi (two-part
@@ -123,35 +118,37 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
     const RowKeys rk = row_keys(tp, idx, k, m, window);
     const int64_t u0 = rk.n * s / S, u1 = rk.n * (s + 1) / S;
 
-    // ---- first tile: resolve, then put its entries in flight ----
-    if (tid < KT) {
-        const int64_t u = u0 + tid;
-        float sc = 0.f;
-        sm.row[0][tid] = u < u1 ? resolve(u, t, sq, rk, idx, k, comp, win, sc) : -1;
-        sm.scl[0][tid] = sc;
-    } else if (tid >= 64 && tid < 96) {
+    // ---- resolve the first batch of positions (one index load per thread), angles ----
+    static_assert(RB == 256 && RB % KT == 0, "one position per thread per batch");
+    sm.row[tid] = u0 + tid < u1 ? resolve(u0 + tid, t, sq, rk, idx, k, comp, win) : -1;
+    if (tid < 32) {
         float c, sn;
-        angle_cs((double)tp, rt.theta[tid - 64], c, sn);
-        sm.cs[2 * (tid - 64)] = c;
-        sm.cs[2 * (tid - 64) + 1] = sn;
+        angle_cs((double)tp, rt.theta[tid], c, sn);
+        sm.cs[2 * tid] = c;
+        sm.cs[2 * tid + 1] = sn;
     }
     __syncthreads();
 
+    // entries of a tile go to registers: 16-byte chunks, plus the scale for part 0
     v4i pre[NCH];
-    auto issue = [&](int buf) {
+    float pscl = 0.f;
+    int pval = 0;
+    auto issue = [&](int slot) {  // slot: first position of the tile inside the batch
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int c = tid + i * 256;
             pre[i] = v4i{0, 0, 0, 0};
             if (c < KT * CPK) {
                 const int key = c % KT, part = c / KT;  // lanes of a wave: consecutive keys of one chunk column
-                const int64_t code = sm.row[buf][key];
+                const int64_t code = sm.row[slot + key];
                 if (code != -1) {
                     const bool w = code <= -2;
                     const int64_t r = w ? -code - 2 : code;
                     if (part < DN / 16) pre[i] = *(const v4i*)((w ? win.nope : comp.nope) + r * DN + part * 16);
                     else pre[i] = *(const v4i*)((w ? win.rope : comp.rope) + r * 64 + (part - DN / 16) * 8);
+                    if (c < KT) pscl = (w ? win.scale : comp.scale)[r];
                 }
+                if (c < KT) pval = code != -1;
             }
         }
     };
@@ -207,8 +204,14 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
 #pragma unroll
         for (int b = 0; b < HT; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    int buf = 0;
-    for (int64_t ut = u0; ut < u1; ut += KT, buf ^= 1) {
+    int buf = 0, ti = 0;
+    for (int64_t ut = u0; ut < u1; ut += KT, buf ^= 1, ++ti) {
+        if (tid < KT) {
+            sm.scl[buf][tid] = pval ? pscl : 0.f;
+            sm.valid[buf][tid] = pval;
+            pscl = 0.f;
+            pval = 0;
+        }
         // ---- stage this tile from registers into LDS ----
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
@@ -243,16 +246,15 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
                 }
             }
         }
-        // ---- resolve the next tile and put it in flight ----
+        // ---- put the next tile in flight (resolving a new batch of positions first when needed) ----
         const bool more = ut + KT < u1;
-        if (more && tid < KT) {
+        const int nslot = ((ti + 1) % (RB / KT)) * KT;
+        if (more && nslot == 0) {
             const int64_t u = ut + KT + tid;
-            float sc = 0.f;
-            sm.row[buf ^ 1][tid] = u < u1 ? resolve(u, t, sq, rk, idx, k, comp, win, sc) : -1;
-            sm.scl[buf ^ 1][tid] = sc;
+            sm.row[tid] = u < u1 ? resolve(u, t, sq, rk, idx, k, comp, win) : -1;
         }
         __syncthreads();
-        if (more) issue(buf ^ 1);
+        if (more) issue(nslot);
         const float* scl = sm.scl[buf];
         // ---- S^T = K Q^T ----
         if (qk_active) {
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
                 for (int i = 0; i < 4; ++i) {
                     const int key = ksub * 16 + 4 * g4 + i;
                     const float sc = sm_scale * fmaf(scl[key], an[i], ar[i]);
-                    sm.s[key * Sm::SS + hb * 16 + l16] = sm.row[buf][key] != -1 ? sc : -INFINITY;
+                    sm.s[key * Sm::SS + hb * 16 + l16] = sm.valid[buf][key] ? sc : -INFINITY;
                 }
             }
         }

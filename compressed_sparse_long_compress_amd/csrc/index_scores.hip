@@ -26,7 +26,7 @@ __device__ __forceinline__ v8i frag16(const uint8_t* p) {
 // ---------------------------------------------------------------------------
 // decode: grid (key chunks, T), 4 waves; each wave streams tiles of 16 keys
 // ---------------------------------------------------------------------------
-template <int DI>
+template <int DI, int U>
 __global__ __launch_bounds__(256) void k_index_rows(const uint8_t* __restrict__ q, const uint8_t* __restrict__ q_scale,
                                                     const float* __restrict__ w, const int32_t* __restrict__ seq,
                                                     const int64_t* __restrict__ pos, int h_i,
@@ -36,7 +36,6 @@ __global__ __launch_bounds__(256) void k_index_rows(const uint8_t* __restrict__ 
                                                     char* __restrict__ hist_ws) {
     constexpr int KB = DI / 2;   // bytes per key
     constexpr int NB = DI / 32;  // scale blocks per key
-    constexpr int U = 8;         // tiles in flight per wave
     __shared__ uint32_t hh[4096];  // top-12-bit key histogram of this chunk (when hist_ws)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t t = blockIdx.y;
@@ -66,23 +65,24 @@ __global__ __launch_bounds__(256) void k_index_rows(const uint8_t* __restrict__ 
     float* out = scores + t * n_cols;
 
     for (int64_t j0 = c0 + (int64_t)wave * 16 * U; j0 < c1; j0 += 4 * 16 * U) {
-        v8i b[U];
+        v4i bk[U];
         int sb[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t j = j0 + u * 16 + r;
             if (j < nv && g < NB) {
-                b[u] = frag16(kdata + (base + j) * KB + g * 16);
+                bk[u] = *(const v4i*)(kdata + (base + j) * KB + g * 16);
                 sb[u] = kscale[(base + j) * NB + g];
             } else {
-                b[u] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+                bk[u] = v4i{0, 0, 0, 0};
                 sb[u] = 127;
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             v4f acc = {0.f, 0.f, 0.f, 0.f};
-            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[u], acc, 4, 4, 0, sa, 0, sb[u]);
+            const v8i bf = {bk[u][0], bk[u][1], bk[u][2], bk[u][3], 0, 0, 0, 0};
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bf, acc, 4, 4, 0, sa, 0, sb[u]);
             float p = wr[0] * fmaxf(acc[0], 0.f);
             p = fmaf(wr[1], fmaxf(acc[1], 0.f), p);
             p = fmaf(wr[2], fmaxf(acc[2], 0.f), p);
@@ -277,11 +277,11 @@ hipError_t launch_index_scores(const uint8_t* q, const uint8_t* q_scale, const f
         if (chunk > 16384) chunk = 16384;
         dim3 grid((unsigned)((n_cols + chunk - 1) / chunk), (unsigned)T), block(256);
         if (d_i == 128)
-            hipLaunchKernelGGL(k_index_rows<128>, grid, block, 0, st, q, q_scale, w, seq, pos, h_i, kdata, kscale,
+            hipLaunchKernelGGL((k_index_rows<128, 8>), grid, block, 0, st, q, q_scale, w, seq, pos, h_i, kdata, kscale,
                                kcap, m, n_cols, chunk, scores, (char*)hist_ws);
         else
-            hipLaunchKernelGGL(k_index_rows<64>, grid, block, 0, st, q, q_scale, w, seq, pos, h_i, kdata, kscale, kcap,
-                               m, n_cols, chunk, scores, (char*)hist_ws);
+            hipLaunchKernelGGL((k_index_rows<64, 8>), grid, block, 0, st, q, q_scale, w, seq, pos, h_i, kdata, kscale,
+                               kcap, m, n_cols, chunk, scores, (char*)hist_ws);
         return hipGetLastError();
     }
     const int qwg = 4 * 4 * (32 / h_i);  // queries per workgroup

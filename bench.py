@@ -29,9 +29,24 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 
+# HBM bytes per launch of the indexer kernel on the csa_decode_1m workload, from
+# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (scaled by a 256 MiB copy: fetch x2.0,
+# write x1.0; see profiles/csa_decode_1m_hbm_counters.md), valid for the kernel
+# source with this SHA-256 only.
+INDEX_TRAFFIC = {"sha256": "32de04b8deaf1c137d7e27e42ff49302b97ca64946013a6e6281a7695b9b74fa", "bytes": 75973205}
+
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def index_traffic():
+    """Counter-measured bytes per indexer launch, or None once the kernel source changed."""
+    import hashlib
+
+    src = os.path.join(ROOT, "compressed_sparse_long_compress_amd", "csrc", "index_scores.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    return INDEX_TRAFFIC["bytes"] if sha == INDEX_TRAFFIC["sha256"] else None
 
 
 def index_bytes_per_query(N, h_i, d_i):
@@ -111,6 +126,89 @@ class DecodeSet:
         self.attend(r)
 
 
+class PrefillSet:
+    """Device tensors of the chunked-prefill workload (8,192 new tokens after a
+    131,072-token context, one sequence, paired HCA layer).  One step compresses
+    the new chunk (CSA m=4, HCA m'=128, both window rings), scores every
+    (query, entry) pair, selects the top-1024 per query and runs both
+    attentions for all 8,192 queries.  The older context is compressed in set-up."""
+
+    def __init__(self, wl):
+        import torch
+
+        import compressed_sparse_long_compress_amd as csa
+        from gen import device as dev
+
+        self.wl = wl
+        T, L0, m, mh, d, W, k = (wl[x] for x in ("T", "L0", "m", "m_hca", "d", "W", "k"))
+        self.comp = csa.KvCache.empty(1, wl["comp_cap"], d)
+        self.hca = csa.KvCache.empty(1, wl["hca_cap"], d)
+        self.win = csa.KvCache.empty(1, wl["win_cap"], d)
+        self.win_h = csa.KvCache.empty(1, wl["win_cap"], d)
+        self.kv, self.lg = dev.bf16(wl["kv"]), dev.t(wl["logits"])
+        self.kvh, self.lgh = dev.bf16(wl["kv_hca"]), dev.t(wl["logits_hca"])
+        csa.csa_compress(self.kv[:L0], self.lg[:L0], 0, m, 0, self.comp)
+        csa.csa_compress(self.kvh[:L0], self.lgh[:L0], 0, mh, 0, self.hca)
+        csa.csa_compress(self.kv[L0 - W:L0], self.lg[L0 - W:L0], L0 - W, 1, 0, self.win)
+        csa.csa_compress(self.kvh[L0 - W:L0], self.lgh[L0 - W:L0], L0 - W, 1, 0, self.win_h)
+        self.seq, self.pos = dev.t(wl["seq"]), dev.t(wl["pos"])
+        self.iq, self.iqs, self.w = dev.t(wl["iq"][0]), dev.t(wl["iq"][1]), dev.t(wl["w"])
+        self.keys = dev.index_keys(wl["keys"], wl["N"])
+        self.q, self.qh = dev.bf16(wl["q"]), dev.bf16(wl["q_hca"])
+        self.scores = torch.empty(T, wl["n_cols"], dtype=torch.float32, device="cuda")
+        self.idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+        self.out = torch.empty(T, wl["H"], d, dtype=torch.float32, device="cuda")
+        self.lse = torch.empty(T, wl["H"], dtype=torch.float32, device="cuda")
+        self.hout, self.hlse = torch.empty_like(self.out), torch.empty_like(self.lse)
+        self.tws = csa.topk_workspace(T, wl["n_cols"], k)
+        self.replicas = 1
+
+    def step(self, i):
+        import compressed_sparse_long_compress_amd as csa
+
+        wl = self.wl
+        L0, m, mh, W, k = wl["L0"], wl["m"], wl["m_hca"], wl["W"], wl["k"]
+        csa.csa_compress(self.kv[L0:], self.lg[L0:], L0, m, 0, self.comp)
+        csa.csa_compress(self.kv[L0:], self.lg[L0:], L0, 1, 0, self.win)
+        csa.csa_compress(self.kvh[L0:], self.lgh[L0:], L0, mh, 0, self.hca)
+        csa.csa_compress(self.kvh[L0:], self.lgh[L0:], L0, 1, 0, self.win_h)
+        csa.csa_index_scores(self.iq, self.iqs, self.w, self.seq, self.pos, self.keys, m, wl["n_cols"], out=self.scores)
+        csa.csa_topk(self.scores, self.pos, m, k, out=self.idx, ws=self.tws)
+        csa.csa_sparse_mqa(self.q, self.seq, self.pos, self.idx, m, self.comp, self.win, W, wl["sm_scale"],
+                           out=self.out, lse=self.lse)
+        csa.hca_dense_mqa(self.qh, self.seq, self.pos, mh, wl["hca_cap"], self.hca, self.win_h, W, wl["sm_scale"],
+                          out=self.hout, lse=self.hlse)
+
+
+class HcaSet:
+    """HCA decode at 1M context: 8 sequences, 8,192 entries each (m'=128)."""
+
+    def __init__(self, wl, replicas):
+        import torch
+
+        import compressed_sparse_long_compress_amd as csa
+        from gen import device as dev
+
+        self.wl = wl
+        comp0 = dev.kv_cache(wl["comp"], wl["N"])
+        self.comp = [comp0] + [csa.KvCache(comp0.nope.clone(), comp0.rope.clone(), comp0.scale.clone(), wl["N"])
+                               for _ in range(replicas - 1)]
+        self.win = dev.kv_cache(wl["win"], wl["W"])
+        self.q, self.seq, self.pos = dev.bf16(wl["q"]), dev.t(wl["seq"]), dev.t(wl["pos"])
+        self.out = torch.empty(wl["T"], wl["H"], wl["d"], dtype=torch.float32, device="cuda")
+        self.lse = torch.empty(wl["T"], wl["H"], dtype=torch.float32, device="cuda")
+        n = csa.csa_mqa_workspace(wl["T"], wl["H"], wl["d"], wl["N"] + wl["W"])
+        self.ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+        self.replicas = replicas
+
+    def step(self, i):
+        import compressed_sparse_long_compress_amd as csa
+
+        wl = self.wl
+        csa.hca_dense_mqa(self.q, self.seq, self.pos, wl["m"], wl["N"], self.comp[i % self.replicas], self.win,
+                          wl["W"], wl["sm_scale"], wl["rope_base"], out=self.out, lse=self.lse, ws=self.ws)
+
+
 def time_steps(ds, steps, warmup):
     import torch
 
@@ -171,38 +269,31 @@ def cpu_baseline(wl):
             "sample": f"all {T} query rows of the batch (full 1M-context rows), {dt:.1f} s wall"}
 
 
-def secondary(steps, warmup):
-    """Other workloads (opt-in): 64K CSA decode, 1M HCA decode, chunked prefill."""
-    import torch
-
-    import compressed_sparse_long_compress_amd as csa
+def run_workload(name, steps, warmup):
+    """Time one named workload; returns (wl, dataset, seconds for `steps` steps)."""
     from gen import configs
-    from gen import device as dev
 
-    res = {}
-    wl = configs.named("csa_decode_64k")
-    ds = DecodeSet(wl, replicas=8)
+    wl = configs.named(name)
+    if name.startswith("csa_decode"):
+        ds = DecodeSet(wl, replicas=8)
+    elif name == "hca_decode_1m":
+        ds = HcaSet(wl, replicas=8)
+    else:
+        ds = PrefillSet(wl)
     sec, _ = time_steps(ds, steps, warmup)
-    res["csa_decode_64k"] = {"queries_per_s": wl["B"] * steps / sec, "ms_per_step": sec / steps * 1e3}
-    del ds
-    wl = configs.named("hca_decode_1m")
-    comp = [dev.kv_cache(wl["comp"], wl["N"]) for _ in range(8)]
-    win, q, seq, pos = dev.kv_cache(wl["win"], wl["W"]), dev.bf16(wl["q"]), dev.t(wl["seq"]), dev.t(wl["pos"])
-    ws = torch.empty(max(csa.csa_mqa_workspace(wl["T"], wl["H"], wl["d"], wl["N"] + wl["W"]), 1), dtype=torch.uint8,
-                     device="cuda")
+    return wl, ds, sec
 
-    def hstep(i):
-        csa.hca_dense_mqa(q, seq, pos, wl["m"], wl["N"], comp[i % 8], win, wl["W"], wl["sm_scale"], ws=ws)
 
-    for i in range(warmup):
-        hstep(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        hstep(i)
-    torch.cuda.synchronize()
-    sec = time.perf_counter() - t0
-    res["hca_decode_1m"] = {"queries_per_s": wl["B"] * steps / sec, "ms_per_step": sec / steps * 1e3}
+def secondary(steps, warmup):
+    """The other workloads (opt-in): 64K CSA decode, 1M HCA decode, chunked prefill."""
+    res = {}
+    for name in ("csa_decode_64k", "hca_decode_1m"):
+        wl, ds, sec = run_workload(name, steps, warmup)
+        res[name] = {"queries_per_s": wl["T"] * steps / sec, "ms_per_step": sec / steps * 1e3}
+        del ds
+    n = max(steps // 20, 3)
+    wl, ds, sec = run_workload("prefill_chunk", n, 2)
+    res["prefill_chunk"] = {"tokens_per_s": wl["T"] * n / sec, "ms_per_step": sec / n * 1e3}
     return res
 
 
@@ -211,8 +302,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--all", action="store_true", help="also time the other workloads")
+    ap.add_argument("--all", action="store_true", help="also time the other workloads (secondary object)")
+    ap.add_argument("--workload", default="csa_decode_1m",
+                    choices=["csa_decode_1m", "csa_decode_64k", "hca_decode_1m", "prefill_chunk"],
+                    help="time only this workload and print its line (profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run 5 device copies of 256 MiB (reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the CSA/HCA path here is built and timed on a single MI355X; "
@@ -225,6 +321,20 @@ def main():
     from gen import configs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": a.numel(), "copies": 5}))
+        return
+    if args.workload != "csa_decode_1m":
+        wl, ds, sec = run_workload(args.workload, args.steps, args.warmup)
+        unit = "tokens/s" if args.workload == "prefill_chunk" else "queries/s"
+        print(json.dumps({"workload": args.workload, "value": wl["T"] * args.steps / sec, "unit": unit,
+                          "ms_per_step": sec / args.steps * 1e3, "steps": args.steps}))
+        return
     t0 = time.perf_counter()
     wl = configs.named("csa_decode_1m")
     log(f"generated csa_decode_1m inputs in {time.perf_counter() - t0:.1f} s")
@@ -259,8 +369,8 @@ def main():
         "step_hbm_gbs": step_bytes * args.steps / sec / 1e9,
         "step_hbm_frac": step_bytes * args.steps / sec / 1e9 / HBM_PEAK_GBS,
         "per_call_us": {kk: v * 1e6 for kk, v in kern.items()},
-        "roofline": {"kernel": "k_index_rows<128>", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+        "roofline": {"kernel": "k_index_rows<128, 8>", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": index_traffic(),
                      "bytes_per_launch": idx_bytes},
     }
     if args.all:

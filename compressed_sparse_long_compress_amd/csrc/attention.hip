@@ -395,6 +395,285 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
     }
 }
 
+// ---------------------------------------------------------------------------
+// 64 query heads: each wave owns one 16-head tile end to end.  QK for its
+// heads over the tile's 32 keys, the online softmax in registers (a head's 32
+// scores sit in one lane group of 16 lanes x 8 registers), and PV over all d
+// dims for its heads with P taken straight from the QK accumulators.  Only
+// the staged K (row-major bf16) and V^T (fp16) tiles are shared through LDS.
+// MFMA 16x16x32 K-slot order for PV: lane group g holds keys 4g..4g+3 and
+// 16+4g..16+4g+3, exactly the keys its QK accumulators hold.
+// ---------------------------------------------------------------------------
+template <int D>
+struct MqaWSmem {
+    static constexpr int DN = D - 64;
+    static constexpr int KR = D + 8;
+    static constexpr int VT = KT + 8;
+    __bf16 kr[KT * KR];
+    _Float16 vt[D * VT];
+    float cs[64];
+    int64_t row[RB];
+    float scl[2][KT];
+    int valid[2][KT];
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void k_mqa_w(const uint16_t* __restrict__ q, const int32_t* __restrict__ seq,
+                                               const int64_t* __restrict__ pos, const int32_t* __restrict__ idx, int k,
+                                               int m, KvView comp, KvView win, int window, float sm_scale, RopeTab rt,
+                                               int S, float* __restrict__ out, float* __restrict__ lse,
+                                               float* __restrict__ part_o, float* __restrict__ part_ml) {
+    constexpr int H = 64;
+    using Sm = MqaWSmem<D>;
+    constexpr int DN = Sm::DN;
+    constexpr int DSTEP = D / 32;
+    constexpr int NSTEP = DN / 32;
+    constexpr int DT = D / 16;                   // 16-dim tiles, all owned by every wave
+    constexpr int CPK = DN / 16 + 8;
+    constexpr int NCH = (KT * CPK + 255) / 256;
+
+    __shared__ Sm sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int64_t t = blockIdx.x / S;
+    const int s = blockIdx.x % S;
+    const int64_t tp = pos[t];
+    const int32_t sq = seq[t];
+    const RowKeys rk = row_keys(tp, idx, k, m, window);
+    const int64_t u0 = rk.n * s / S, u1 = rk.n * (s + 1) / S;
+
+    sm.row[tid] = u0 + tid < u1 ? resolve(u0 + tid, t, sq, rk, idx, k, comp, win) : -1;
+    if (tid < 32) {
+        float c, sn;
+        angle_cs((double)tp, rt.theta[tid], c, sn);
+        sm.cs[2 * tid] = c;
+        sm.cs[2 * tid + 1] = sn;
+    }
+    __syncthreads();
+
+    v4i pre[NCH];
+    float pscl = 0.f;
+    int pval = 0;
+    auto issue = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int c = tid + i * 256;
+            pre[i] = v4i{0, 0, 0, 0};
+            if (c < KT * CPK) {
+                const int key = c % KT, part = c / KT;
+                const int64_t code = sm.row[slot + key];
+                if (code != -1) {
+                    const bool w = code <= -2;
+                    const int64_t r = w ? -code - 2 : code;
+                    if (part < DN / 16) pre[i] = *(const v4i*)((w ? win.nope : comp.nope) + r * DN + part * 16);
+                    else pre[i] = *(const v4i*)((w ? win.rope : comp.rope) + r * 64 + (part - DN / 16) * 8);
+                    if (c < KT) pscl = (w ? win.scale : comp.scale)[r];
+                }
+                if (c < KT) pval = code != -1;
+            }
+        }
+    };
+    issue(0);
+
+    // query fragments of this wave's 16 heads, RoPE at tp, RoPE dims split hi + lo
+    v8bf qf[DSTEP];
+    v8bf qlo[2];
+    {
+        const int h = wave * 16 + l16;
+        const uint16_t* qrow = q + (t * H + h) * (int64_t)D;
+#pragma unroll
+        for (int st = 0; st < DSTEP; ++st) {
+            const int d0 = 32 * st + 8 * g4;
+            v4i raw = *(const v4i*)(qrow + d0);
+            v8bf v = *(v8bf*)&raw;
+            if (st >= NSTEP) {
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const int pi = (d0 - DN + e) >> 1;
+                    const float cs = sm.cs[2 * pi], sn = sm.cs[2 * pi + 1];
+                    const float x0 = x[e], x1 = x[e + 1];
+                    x[e] = x0 * cs - x1 * sn;
+                    x[e + 1] = x0 * sn + x1 * cs;
+                }
+                v8bf hi, lo;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    hi[e] = (__bf16)x[e];
+                    lo[e] = (__bf16)(x[e] - (float)hi[e]);
+                }
+                v = hi;
+                qlo[st - NSTEP] = lo;
+            }
+            qf[st] = v;
+        }
+    }
+
+    float m_run = -INFINITY, l_run = 0.f, s_ref = 0.f;
+    v4f acc[DT];
+#pragma unroll
+    for (int a = 0; a < DT; ++a) acc[a] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    int buf = 0, ti = 0;
+    for (int64_t ut = u0; ut < u1; ut += KT, buf ^= 1, ++ti) {
+        if (tid < KT) {
+            sm.scl[buf][tid] = pval ? pscl : 0.f;
+            sm.valid[buf][tid] = pval;
+            pscl = 0.f;
+            pval = 0;
+        }
+        // ---- stage this tile into LDS ----
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int c = tid + i * 256;
+            if (c < KT * CPK) {
+                const int key = c % KT, part = c / KT;
+                __bf16* kr = sm.kr + key * Sm::KR;
+                const v4i raw = pre[i];
+                if (part < DN / 16) {
+                    v8bf b0, b1;
+#pragma unroll
+                    for (int wd = 0; wd < 4; ++wd) {
+                        const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[wd], false);
+                        const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[wd], true);
+                        const float f[4] = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if (wd < 2) b0[wd * 4 + e] = (__bf16)f[e];
+                            else b1[(wd - 2) * 4 + e] = (__bf16)f[e];
+                            sm.vt[(part * 16 + wd * 4 + e) * Sm::VT + key] = (_Float16)f[e];
+                        }
+                    }
+                    *(v8bf*)(kr + part * 16) = b0;
+                    *(v8bf*)(kr + part * 16 + 8) = b1;
+                } else {
+                    const int rp = part - DN / 16;
+                    *(v4i*)(kr + DN + rp * 8) = raw;
+                    const uint16_t* hv = (const uint16_t*)&raw;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        sm.vt[(DN + rp * 8 + e) * Sm::VT + key] = (_Float16)bf16_bits_to_f32(hv[e]);
+                }
+            }
+        }
+        const bool more = ut + KT < u1;
+        const int nslot = ((ti + 1) % (RB / KT)) * KT;
+        if (more && nslot == 0) {
+            const int64_t u = ut + KT + tid;
+            sm.row[tid] = u < u1 ? resolve(u, t, sq, rk, idx, k, comp, win) : -1;
+        }
+        __syncthreads();
+        if (more) issue(nslot);
+        const float* scl = sm.scl[buf];
+        const int* vld = sm.valid[buf];
+
+        // ---- scores: lane (head l16, group g4) holds keys 4*g4+i and 16+4*g4+i ----
+        float sv[8];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const __bf16* kb = sm.kr + (ks * 16 + l16) * Sm::KR + 8 * g4;
+            v4f an = {0.f, 0.f, 0.f, 0.f}, ar = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < NSTEP; ++st)
+                an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const v8bf*)(kb + 32 * st), qf[st], an, 0, 0, 0);
+#pragma unroll
+            for (int st = NSTEP; st < DSTEP; ++st) {
+                const v8bf kv = *(const v8bf*)(kb + 32 * st);
+                ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qf[st], ar, 0, 0, 0);
+                ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qlo[st - NSTEP], ar, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = ks * 16 + 4 * g4 + i;
+                sv[ks * 4 + i] = vld[key] ? sm_scale * fmaf(scl[key], an[i], ar[i]) : -INFINITY;
+            }
+        }
+        // ---- online softmax for head l16 (its 32 scores: 8 here, 24 in lanes l^16, l^32, l^48) ----
+        float mx = sv[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        float st_max = 0.f;
+#pragma unroll 8
+        for (int i = 0; i < KT; ++i) st_max = fmaxf(st_max, scl[i]);
+        const float s_new = st_max > 0.f ? st_max : (s_ref > 0.f ? s_ref : 1.f);
+        const float inv_s = 1.f / s_new;
+        v8h pn, pr;
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int key = (i >> 2) * 16 + 4 * g4 + (i & 3);
+            const float p = m_new == -INFINITY ? 0.f : __expf(sv[i] - m_new);
+            sum += p;
+            pr[i] = (_Float16)p;
+            pn[i] = (_Float16)(p * (scl[key] * inv_s));
+        }
+        sum += __shfl_xor(sum, 16);
+        sum += __shfl_xor(sum, 32);
+        const float alpha = m_new == -INFINITY ? 1.f : __expf(m_run - m_new);
+        const float sfac = s_ref > 0.f ? s_ref * inv_s : 1.f;
+        l_run = l_run * alpha + sum;
+        m_run = m_new;
+        s_ref = s_new;
+        // ---- O^T[dims x heads] += V^T P^T ----
+        const float an_f = alpha * sfac;
+#pragma unroll
+        for (int a = 0; a < DT; ++a) {
+            const int d0 = a * 16;
+            const _Float16* vr = sm.vt + (d0 + l16) * Sm::VT;
+            const uint2 v0 = *(const uint2*)(vr + 4 * g4);
+            const uint2 v1 = *(const uint2*)(vr + 16 + 4 * g4);
+            const uint4 vv = {v0.x, v0.y, v1.x, v1.y};
+            const v8h vf = *(const v8h*)&vv;
+            const bool nope_tile = d0 < DN;
+            acc[a] *= nope_tile ? an_f : alpha;
+            acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, nope_tile ? pn : pr, acc[a], 0, 0, 0);
+        }
+        __syncthreads();  // every wave is done with this tile's K / V before the next staging
+    }
+
+    // ---- epilogue: lane holds head wave*16+l16, dims a*16 + 4*g4 + i ----
+    const int h = wave * 16 + l16;
+    const float sfin = s_ref > 0.f ? s_ref : 1.f;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+    for (int a = 0; a < DT; ++a) {
+        const int d0 = a * 16 + 4 * g4;
+        float o[4];
+        const float f = d0 < DN ? sfin : 1.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = acc[a][i] * f;
+        if (S == 1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] *= inv;
+            if (d0 >= DN) {
+#pragma unroll
+                for (int i = 0; i < 4; i += 2) {
+                    const int pi = (d0 - DN + i) >> 1;
+                    const float cs = sm.cs[2 * pi], sn = -sm.cs[2 * pi + 1];
+                    const float x0 = o[i], x1 = o[i + 1];
+                    o[i] = x0 * cs - x1 * sn;
+                    o[i + 1] = x0 * sn + x1 * cs;
+                }
+            }
+            *(float4*)(out + (t * H + h) * (int64_t)D + d0) = make_float4(o[0], o[1], o[2], o[3]);
+        } else {
+            *(float4*)(part_o + ((t * S + s) * H + h) * (int64_t)D + d0) = make_float4(o[0], o[1], o[2], o[3]);
+        }
+    }
+    if (g4 == 0) {
+        if (S == 1) lse[t * H + h] = l_run > 0.f ? m_run + __logf(l_run) : -INFINITY;
+        else {
+            part_ml[((t * S + s) * H + h) * 2 + 0] = m_run;
+            part_ml[((t * S + s) * H + h) * 2 + 1] = l_run;
+        }
+    }
+}
+
 // Merge the S split partials of one (row, head) in the fixed order s = 0 .. S-1.
 template <int D>
 __global__ __launch_bounds__(128) void k_mqa_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
@@ -487,8 +766,12 @@ template <int H, int D>
 static void launch_mqa_t(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, const int32_t* idx,
                          int k, int m, KvView comp, KvView win, int window, float sm_scale, const RopeTab& rt, int S,
                          float* out, float* lse, float* po, float* pml, hipStream_t st) {
-    hipLaunchKernelGGL((k_mqa<H, D>), dim3((unsigned)(T * S)), dim3(256), 0, st, q, seq, pos, idx, k, m, comp, win,
-                       window, sm_scale, rt, S, out, lse, po, pml);
+    if constexpr (H == 64)
+        hipLaunchKernelGGL((k_mqa_w<D>), dim3((unsigned)(T * S)), dim3(256), 0, st, q, seq, pos, idx, k, m, comp, win,
+                           window, sm_scale, rt, S, out, lse, po, pml);
+    else
+        hipLaunchKernelGGL((k_mqa<H, D>), dim3((unsigned)(T * S)), dim3(256), 0, st, q, seq, pos, idx, k, m, comp,
+                           win, window, sm_scale, rt, S, out, lse, po, pml);
     if (S > 1)
         hipLaunchKernelGGL((k_mqa_combine<D>), dim3((unsigned)(T * H)), dim3(128), 0, st, po, pml, pos, H, S, rt, out,
                            lse);

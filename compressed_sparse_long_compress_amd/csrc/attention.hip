@@ -21,6 +21,8 @@
 // A single split writes the normalised output (inverse RoPE on the last 64
 // dims); several splits write unnormalised partials plus (max, sum), merged by
 // k_mqa_combine in the fixed split order (a log-sum-exp merge).
+#include <type_traits>
+
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 
@@ -396,44 +398,75 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
 }
 
 // ---------------------------------------------------------------------------
-// 64 query heads: each wave owns one 16-head tile end to end.  QK for its
-// heads over the tile's 32 keys, the online softmax in registers (a head's 32
-// scores sit in one lane group of 16 lanes x 8 registers), and PV over all d
-// dims for its heads with P taken straight from the QK accumulators.  Only
-// the staged K (row-major bf16) and V^T (fp16) tiles are shared through LDS.
-// MFMA 16x16x32 K-slot order for PV: lane group g holds keys 4g..4g+3 and
-// 16+4g..16+4g+3, exactly the keys its QK accumulators hold.
+// 64 query heads.  Each 32-key tile is staged once, as fp16 (FP8 codes and
+// bf16 RoPE dims both convert exactly), row-major with rows D + 16 halves
+// apart: that stride keeps the row-wise 16-byte reads of QK and the
+// transposed 8-byte reads of PV free of LDS bank conflicts.
+//   QK: wave w computes S^T = K Q^T for heads 16w..16w+15 over all dims.  The
+//       query lives in registers as fp16, scaled per head by a power of two
+//       (max |q| in [2^14, 2^15)) that is divided out of the scores exactly.
+//   softmax: in registers, a head's 32 scores in one 16-lane column of the
+//       accumulators.
+//   PV: wave w computes O for all 64 heads over the FP8 dims
+//       [w DN/4, (w+1) DN/4) and the RoPE dims [DN + 16w, DN + 16w + 16), so
+//       every wave has the same mix of the two.  P (fp16) comes through LDS,
+//       stored in the MFMA's K-slot order; V comes from the row-major tile
+//       through ds_read_b64_tr_b16 transposed loads.
+// K-slot order (both MFMAs): lane group g holds keys 4g..4g+3 and
+// 16+4g..16+4g+3, exactly the keys of its QK accumulator rows.
+//
+// Fixed references instead of a running rescale: each head's reference max
+// m_ref is the max of the first tile with visible keys, and S_ref (the FP8
+// part's scale reference) is that tile's largest entry scale.  P = exp(s -
+// m_ref) and P * scale_j / S_ref then stay below e^kLazy * kSRatio < 65504 as
+// long as no later tile's max exceeds m_ref + kLazy and no later scale
+// exceeds kSRatio * S_ref; a tile that breaks either bound restarts the
+// split with the references raised to everything seen so far (tiles already
+// seen can then never break them again).  The output accumulators are thus
+// only ever touched by MFMAs.
 // ---------------------------------------------------------------------------
-template <int D>
-struct MqaWSmem {
-    static constexpr int DN = D - 64;
-    static constexpr int KR = D + 8;
-    static constexpr int VT = KT + 8;
-    __bf16 kr[KT * KR];
-    _Float16 vt[D * VT];
-    float cs[64];
-    int64_t row[RB];
-    float scl[2][KT];
-    int valid[2][KT];
-};
+constexpr float kLazy = 8.f;     // e^8 ~ 2981
+constexpr float kSRatio = 16.f;  // 2981 * 16 < 65504
+
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 template <int D>
-__global__ __launch_bounds__(256) void k_mqa_w(const uint16_t* __restrict__ q, const int32_t* __restrict__ seq,
+struct __align__(16) Mqa64Smem {
+    static constexpr int KS = D + 16;  // fp16 row stride of a staged tile
+    _Float16 kv[2][KT * KS];
+    _Float16 pn[64 * KT];  // [head][K slot] P * scale_j / S_ref (FP8 dims)
+    _Float16 pr[64 * KT];  // [head][K slot] P (RoPE dims)
+    float lfin[64];
+    int64_t row[2][RB];    // two batches of resolved key-list positions
+    float scl[2][KT];      // entry scales (0 when masked)
+    int valid[2][KT];
+    float cs[64];
+    int restart;
+};
+
+__device__ __forceinline__ v4s lds_read_tr16(const _Float16* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, const int32_t* __restrict__ seq,
                                                const int64_t* __restrict__ pos, const int32_t* __restrict__ idx, int k,
                                                int m, KvView comp, KvView win, int window, float sm_scale, RopeTab rt,
                                                int S, float* __restrict__ out, float* __restrict__ lse,
                                                float* __restrict__ part_o, float* __restrict__ part_ml) {
     constexpr int H = 64;
-    using Sm = MqaWSmem<D>;
-    constexpr int DN = Sm::DN;
-    constexpr int DSTEP = D / 32;
-    constexpr int NSTEP = DN / 32;
-    constexpr int DT = D / 16;                   // 16-dim tiles, all owned by every wave
-    constexpr int CPK = DN / 16 + 8;
-    constexpr int NCH = (KT * CPK + 255) / 256;
+    using Sm = Mqa64Smem<D>;
+    constexpr int KS = Sm::KS;
+    constexpr int DN = D - 64;
+    constexpr int DSTEP = D / 32, NSTEP = DN / 32;  // QK steps of 32 dims
+    constexpr int NN = DN / 64, DT = NN + 1;        // PV 16-dim tiles per wave: NN FP8 tiles, then one RoPE tile
+    constexpr int CPE = DN / 16 + 8;                // 16-byte chunks per entry: FP8 part, then RoPE part
+    constexpr int NCH = (KT * CPE + 255) / 256;
+    constexpr int TPB = RB / KT;                    // tiles per batch of resolved positions
+    static_assert(RB == 256 && TPB >= 4, "one resolved position per thread, batch resolved 4+ tiles ahead");
 
     __shared__ Sm sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
     const int64_t t = blockIdx.x / S;
     const int s = blockIdx.x % S;
@@ -441,235 +474,340 @@ __global__ __launch_bounds__(256) void k_mqa_w(const uint16_t* __restrict__ q, c
     const int32_t sq = seq[t];
     const RowKeys rk = row_keys(tp, idx, k, m, window);
     const int64_t u0 = rk.n * s / S, u1 = rk.n * (s + 1) / S;
+    const int nt = (int)((u1 - u0 + KT - 1) / KT);
 
-    sm.row[tid] = u0 + tid < u1 ? resolve(u0 + tid, t, sq, rk, idx, k, comp, win) : -1;
+    // key-list position u -> cache row code, given the selected index j (read from idx beforehand)
+    auto fetch = [&](int64_t u) -> int64_t {
+        return (u < u1 && u < rk.n_c) ? (idx ? (int64_t)idx[t * k + u] : u) : 0;
+    };
+    auto code_of = [&](int64_t u, int64_t j) -> int64_t {
+        if (u >= u1) return -1;
+        if (u < rk.n_c) {
+            if (j < 0 || j >= rk.nv) return -1;
+            return (int64_t)sq * comp.cap + (j % comp.cap);
+        }
+        const int64_t p = rk.lo + (u - rk.n_c);
+        return -((int64_t)sq * win.cap + (p % win.cap) + 2);
+    };
+
     if (tid < 32) {
         float c, sn;
         angle_cs((double)tp, rt.theta[tid], c, sn);
         sm.cs[2 * tid] = c;
         sm.cs[2 * tid + 1] = sn;
     }
+    if (tid == 0) sm.restart = 0;
     __syncthreads();
 
+    // ---- tile loads (global -> registers) and staging (registers -> LDS) ----
+    // chunk c: entry c / CPE, part c % CPE (consecutive lanes read consecutive 16 bytes of an entry)
     v4i pre[NCH];
     float pscl = 0.f;
     int pval = 0;
-    auto issue = [&](int slot) {
+    auto issue = [&](int j) {
+        const int64_t* rows = sm.row[(j / TPB) & 1] + (j % TPB) * KT;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int c = tid + i * 256;
             pre[i] = v4i{0, 0, 0, 0};
-            if (c < KT * CPK) {
-                const int key = c % KT, part = c / KT;
-                const int64_t code = sm.row[slot + key];
+            if (c < KT * CPE) {
+                const int key = c / CPE, part = c % CPE;
+                const int64_t code = rows[key];
                 if (code != -1) {
                     const bool w = code <= -2;
                     const int64_t r = w ? -code - 2 : code;
                     if (part < DN / 16) pre[i] = *(const v4i*)((w ? win.nope : comp.nope) + r * DN + part * 16);
                     else pre[i] = *(const v4i*)((w ? win.rope : comp.rope) + r * 64 + (part - DN / 16) * 8);
-                    if (c < KT) pscl = (w ? win.scale : comp.scale)[r];
                 }
-                if (c < KT) pval = code != -1;
+            }
+        }
+        if (tid < KT) {
+            const int64_t code = rows[tid];
+            pval = code != -1;
+            pscl = 0.f;
+            if (pval) {
+                const bool w = code <= -2;
+                pscl = (w ? win.scale : comp.scale)[w ? -code - 2 : code];
             }
         }
     };
-    issue(0);
-
-    // query fragments of this wave's 16 heads, RoPE at tp, RoPE dims split hi + lo
-    v8bf qf[DSTEP];
-    v8bf qlo[2];
-    {
-        const int h = wave * 16 + l16;
-        const uint16_t* qrow = q + (t * H + h) * (int64_t)D;
-#pragma unroll
-        for (int st = 0; st < DSTEP; ++st) {
-            const int d0 = 32 * st + 8 * g4;
-            v4i raw = *(const v4i*)(qrow + d0);
-            v8bf v = *(v8bf*)&raw;
-            if (st >= NSTEP) {
-                float x[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const int pi = (d0 - DN + e) >> 1;
-                    const float cs = sm.cs[2 * pi], sn = sm.cs[2 * pi + 1];
-                    const float x0 = x[e], x1 = x[e + 1];
-                    x[e] = x0 * cs - x1 * sn;
-                    x[e + 1] = x0 * sn + x1 * cs;
-                }
-                v8bf hi, lo;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    hi[e] = (__bf16)x[e];
-                    lo[e] = (__bf16)(x[e] - (float)hi[e]);
-                }
-                v = hi;
-                qlo[st - NSTEP] = lo;
-            }
-            qf[st] = v;
-        }
-    }
-
-    float m_run = -INFINITY, l_run = 0.f, s_ref = 0.f;
-    v4f acc[DT];
-#pragma unroll
-    for (int a = 0; a < DT; ++a) acc[a] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    int buf = 0, ti = 0;
-    for (int64_t ut = u0; ut < u1; ut += KT, buf ^= 1, ++ti) {
-        if (tid < KT) {
-            sm.scl[buf][tid] = pval ? pscl : 0.f;
-            sm.valid[buf][tid] = pval;
-            pscl = 0.f;
-            pval = 0;
-        }
-        // ---- stage this tile into LDS ----
+    auto stage = [&](int j) {
+        _Float16* kv = sm.kv[j & 1];
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int c = tid + i * 256;
-            if (c < KT * CPK) {
-                const int key = c % KT, part = c / KT;
-                __bf16* kr = sm.kr + key * Sm::KR;
+            if (c < KT * CPE) {
+                const int key = c / CPE, part = c % CPE;
+                _Float16* dst = kv + key * KS;
                 const v4i raw = pre[i];
                 if (part < DN / 16) {
-                    v8bf b0, b1;
+                    v8h a, b;
+#pragma unroll
+                    for (int wd = 0; wd < 2; ++wd) {
+                        const v2h x0 = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[wd], 1.f, false));
+                        const v2h x1 = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[wd], 1.f, true));
+                        const v2h y0 = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[wd + 2], 1.f, false));
+                        const v2h y1 = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[wd + 2], 1.f, true));
+                        a[4 * wd] = x0[0];
+                        a[4 * wd + 1] = x0[1];
+                        a[4 * wd + 2] = x1[0];
+                        a[4 * wd + 3] = x1[1];
+                        b[4 * wd] = y0[0];
+                        b[4 * wd + 1] = y0[1];
+                        b[4 * wd + 2] = y1[0];
+                        b[4 * wd + 3] = y1[1];
+                    }
+                    *(v8h*)(dst + part * 16) = a;
+                    *(v8h*)(dst + part * 16 + 8) = b;
+                } else {
+                    v8h a;
 #pragma unroll
                     for (int wd = 0; wd < 4; ++wd) {
-                        const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[wd], false);
-                        const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[wd], true);
-                        const float f[4] = {lo.x, lo.y, hi.x, hi.y};
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            if (wd < 2) b0[wd * 4 + e] = (__bf16)f[e];
-                            else b1[(wd - 2) * 4 + e] = (__bf16)f[e];
-                            sm.vt[(part * 16 + wd * 4 + e) * Sm::VT + key] = (_Float16)f[e];
-                        }
+                        const uint32_t u = (uint32_t)raw[wd];
+                        const v2h x = __builtin_bit_cast(
+                            v2h, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(u << 16), __uint_as_float(u & 0xFFFF0000u)));
+                        a[2 * wd] = x[0];
+                        a[2 * wd + 1] = x[1];
                     }
-                    *(v8bf*)(kr + part * 16) = b0;
-                    *(v8bf*)(kr + part * 16 + 8) = b1;
-                } else {
-                    const int rp = part - DN / 16;
-                    *(v4i*)(kr + DN + rp * 8) = raw;
-                    const uint16_t* hv = (const uint16_t*)&raw;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        sm.vt[(DN + rp * 8 + e) * Sm::VT + key] = (_Float16)bf16_bits_to_f32(hv[e]);
+                    *(v8h*)(dst + DN + (part - DN / 16) * 8) = a;
                 }
             }
         }
-        const bool more = ut + KT < u1;
-        const int nslot = ((ti + 1) % (RB / KT)) * KT;
-        if (more && nslot == 0) {
-            const int64_t u = ut + KT + tid;
-            sm.row[tid] = u < u1 ? resolve(u, t, sq, rk, idx, k, comp, win) : -1;
+        if (tid < KT) {
+            sm.scl[j & 1][tid] = pscl;
+            sm.valid[j & 1][tid] = pval;
         }
+    };
+
+    // ---- query: lane holds head wave*16 + l16, dims 32 st + 8 g4 + e; RoPE at tp; fp16 with a per-head 2^e ----
+    const int hq = wave * 16 + l16;
+    v8h qf[DSTEP];
+    float sm_q;
+    {
+        const uint16_t* qrow = q + (t * H + hq) * (int64_t)D;
+        v4i raw[DSTEP];
+#pragma unroll
+        for (int st = 0; st < DSTEP; ++st) raw[st] = *(const v4i*)(qrow + 32 * st + 8 * g4);
+        float xr[DSTEP - NSTEP][8];
+        float mx = 0.f;
+#pragma unroll
+        for (int st = 0; st < DSTEP; ++st) {
+            const uint16_t* hv = (const uint16_t*)&raw[st];
+            if (st < NSTEP) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(bf16_bits_to_f32(hv[e])));
+            } else {
+                const int d0 = 32 * st + 8 * g4 - DN;
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const int pi = (d0 + e) >> 1;
+                    const float cs = sm.cs[2 * pi], sn = sm.cs[2 * pi + 1];
+                    const float x0 = bf16_bits_to_f32(hv[e]), x1 = bf16_bits_to_f32(hv[e + 1]);
+                    xr[st - NSTEP][e] = x0 * cs - x1 * sn;
+                    xr[st - NSTEP][e + 1] = x0 * sn + x1 * cs;
+                    mx = fmaxf(mx, fmaxf(fabsf(xr[st - NSTEP][e]), fabsf(xr[st - NSTEP][e + 1])));
+                }
+            }
+        }
+        mx = rows4_max(mx);
+        int ex = 0;
+        if (mx > 0.f) frexpf(mx, &ex);  // mx in [2^(ex-1), 2^ex)
+        int sh = mx > 0.f ? 15 - ex : 0;
+        sh = sh < -100 ? -100 : (sh > 100 ? 100 : sh);
+        const float qs = ldexpf(1.f, sh);
+        sm_q = sm_scale * ldexpf(1.f, -sh);
+#pragma unroll
+        for (int st = 0; st < DSTEP; ++st) {
+            const uint16_t* hv = (const uint16_t*)&raw[st];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                qf[st][e] = (_Float16)((st < NSTEP ? bf16_bits_to_f32(hv[e]) : xr[st - NSTEP][e]) * qs);
+        }
+    }
+
+    v4f acc[4][DT];
+    float m_ref = -INFINITY, l_run = 0.f, s_ref = 0.f;
+    float m_seen = -INFINITY, s_seen = 0.f;  // maxima over every tile seen (restart references)
+    for (;;) {
+        // ---- (re)start: batch 0 of the positions, tiles 0 and 1 in flight ----
+        sm.row[0][tid] = code_of(u0 + tid, fetch(u0 + tid));
         __syncthreads();
-        if (more) issue(nslot);
-        const float* scl = sm.scl[buf];
-        const int* vld = sm.valid[buf];
+        if (nt > 0) issue(0);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < DT; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+        m_ref = m_seen;
+        s_ref = s_seen;
+        l_run = 0.f;
+        if (nt > 0) stage(0);
+        if (nt > 1) issue(1);
+        __syncthreads();
+        int64_t nraw = 0;  // idx value of this thread's position in the next batch
+        bool again = false;
 
-        // ---- scores: lane (head l16, group g4) holds keys 4*g4+i and 16+4*g4+i ----
-        float sv[8];
+        for (int j = 0; j < nt; ++j) {
+            const int buf = j & 1;
+            const _Float16* kv = sm.kv[buf];
+            // ---- S^T (keys x heads) for this wave's 16 heads ----
+            v4f an[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+            v4f ar[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+            {
+                const _Float16* kb = kv + l16 * KS + 8 * g4;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const __bf16* kb = sm.kr + (ks * 16 + l16) * Sm::KR + 8 * g4;
-            v4f an = {0.f, 0.f, 0.f, 0.f}, ar = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int st = 0; st < NSTEP; ++st)
-                an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const v8bf*)(kb + 32 * st), qf[st], an, 0, 0, 0);
-#pragma unroll
-            for (int st = NSTEP; st < DSTEP; ++st) {
-                const v8bf kv = *(const v8bf*)(kb + 32 * st);
-                ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qf[st], ar, 0, 0, 0);
-                ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qlo[st - NSTEP], ar, 0, 0, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = ks * 16 + 4 * g4 + i;
-                sv[ks * 4 + i] = vld[key] ? sm_scale * fmaf(scl[key], an[i], ar[i]) : -INFINITY;
-            }
-        }
-        // ---- online softmax for head l16 (its 32 scores: 8 here, 24 in lanes l^16, l^32, l^48) ----
-        float mx = sv[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        float st_max = 0.f;
-#pragma unroll 8
-        for (int i = 0; i < KT; ++i) st_max = fmaxf(st_max, scl[i]);
-        const float s_new = st_max > 0.f ? st_max : (s_ref > 0.f ? s_ref : 1.f);
-        const float inv_s = 1.f / s_new;
-        v8h pn, pr;
-        float sum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int key = (i >> 2) * 16 + 4 * g4 + (i & 3);
-            const float p = m_new == -INFINITY ? 0.f : __expf(sv[i] - m_new);
-            sum += p;
-            pr[i] = (_Float16)p;
-            pn[i] = (_Float16)(p * (scl[key] * inv_s));
-        }
-        sum += __shfl_xor(sum, 16);
-        sum += __shfl_xor(sum, 32);
-        const float alpha = m_new == -INFINITY ? 1.f : __expf(m_run - m_new);
-        const float sfac = s_ref > 0.f ? s_ref * inv_s : 1.f;
-        l_run = l_run * alpha + sum;
-        m_run = m_new;
-        s_ref = s_new;
-        // ---- O^T[dims x heads] += V^T P^T ----
-        const float an_f = alpha * sfac;
-#pragma unroll
-        for (int a = 0; a < DT; ++a) {
-            const int d0 = a * 16;
-            const _Float16* vr = sm.vt + (d0 + l16) * Sm::VT;
-            const uint2 v0 = *(const uint2*)(vr + 4 * g4);
-            const uint2 v1 = *(const uint2*)(vr + 16 + 4 * g4);
-            const uint4 vv = {v0.x, v0.y, v1.x, v1.y};
-            const v8h vf = *(const v8h*)&vv;
-            const bool nope_tile = d0 < DN;
-            acc[a] *= nope_tile ? an_f : alpha;
-            acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, nope_tile ? pn : pr, acc[a], 0, 0, 0);
-        }
-        __syncthreads();  // every wave is done with this tile's K / V before the next staging
-    }
-
-    // ---- epilogue: lane holds head wave*16+l16, dims a*16 + 4*g4 + i ----
-    const int h = wave * 16 + l16;
-    const float sfin = s_ref > 0.f ? s_ref : 1.f;
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-#pragma unroll
-    for (int a = 0; a < DT; ++a) {
-        const int d0 = a * 16 + 4 * g4;
-        float o[4];
-        const float f = d0 < DN ? sfin : 1.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = acc[a][i] * f;
-        if (S == 1) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] *= inv;
-            if (d0 >= DN) {
-#pragma unroll
-                for (int i = 0; i < 4; i += 2) {
-                    const int pi = (d0 - DN + i) >> 1;
-                    const float cs = sm.cs[2 * pi], sn = -sm.cs[2 * pi + 1];
-                    const float x0 = o[i], x1 = o[i + 1];
-                    o[i] = x0 * cs - x1 * sn;
-                    o[i + 1] = x0 * sn + x1 * cs;
+                for (int st = 0; st < DSTEP; ++st) {
+                    const v8h k0 = *(const v8h*)(kb + 32 * st);
+                    const v8h k1 = *(const v8h*)(kb + 16 * KS + 32 * st);
+                    if (st < NSTEP) {
+                        an[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[st], an[0], 0, 0, 0);
+                        an[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[st], an[1], 0, 0, 0);
+                    } else {
+                        ar[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[st], ar[0], 0, 0, 0);
+                        ar[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[st], ar[1], 0, 0, 0);
+                    }
                 }
             }
-            *(float4*)(out + (t * H + h) * (int64_t)D + d0) = make_float4(o[0], o[1], o[2], o[3]);
-        } else {
-            *(float4*)(part_o + ((t * S + s) * H + h) * (int64_t)D + d0) = make_float4(o[0], o[1], o[2], o[3]);
+            // tile max of the entry scales (the same in every wave)
+            float st_max;
+            {
+                const float4 a = *(const float4*)(sm.scl[buf] + 4 * (lane & 7));
+                st_max = fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w));
+                st_max = fmaxf(st_max, __shfl_xor(st_max, 1));
+                st_max = fmaxf(st_max, __shfl_xor(st_max, 2));
+                st_max = fmaxf(st_max, __shfl_xor(st_max, 4));
+            }
+            // ---- scores of head hq: lane (l16, g4) holds keys 4 g4 + i and 16 + 4 g4 + i ----
+            float sv[8];
+            float kscl[8];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const float4 sc = *(const float4*)(sm.scl[buf] + ks * 16 + 4 * g4);
+                const int4 vl = *(const int4*)(sm.valid[buf] + ks * 16 + 4 * g4);
+                const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
+                const int vlv[4] = {vl.x, vl.y, vl.z, vl.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    kscl[ks * 4 + i] = scv[i];
+                    sv[ks * 4 + i] = vlv[i] ? sm_q * fmaf(scv[i], an[ks][i], ar[ks][i]) : -INFINITY;
+                }
+            }
+            float mx = sv[0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+            mx = rows4_max(mx);
+            m_seen = fmaxf(m_seen, mx);
+            s_seen = fmaxf(s_seen, st_max);
+            if (m_ref == -INFINITY) m_ref = mx;     // first tile with visible keys (accumulators still zero)
+            if (s_ref == 0.f) s_ref = st_max;
+            if (mx > m_ref + kLazy || st_max > kSRatio * s_ref) sm.restart = 1;
+            const float inv_s = s_ref > 0.f ? 1.f / s_ref : 0.f;
+            v8h pn, pr;
+            float sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float p = m_ref == -INFINITY ? 0.f : __expf(sv[i] - m_ref);
+                sum += p;
+                pr[i] = (_Float16)p;
+                pn[i] = (_Float16)(p * (kscl[i] * inv_s));
+            }
+            l_run += rows4_sum(sum);
+            *(v8h*)(sm.pn + hq * KT + 8 * g4) = pn;
+            *(v8h*)(sm.pr + hq * KT + 8 * g4) = pr;
+            __syncthreads();
+            // a restart finishes this iteration first (its output is discarded): leaving the
+            // loop from the middle of the body makes the compiler shuttle the accumulators
+            again = sm.restart != 0;
+
+            // ---- stage the next tile, resolve the next batch of positions, load the tile after ----
+            if (j + 1 < nt) stage(j + 1);
+            {
+                const int b1 = j / TPB + 1;  // next batch
+                const int64_t u = u0 + (int64_t)b1 * RB + tid;
+                if (j % TPB == 1 && b1 * TPB < nt) nraw = fetch(u);
+                if (j % TPB == 2 && b1 * TPB < nt) sm.row[b1 & 1][tid] = code_of(u, nraw);
+            }
+            if (j + 2 < nt) issue(j + 2);
+
+            // ---- O[heads x dims] += P V for all heads over this wave's dims ----
+            const _Float16* vb = kv + (4 * g4 + (l16 >> 2)) * KS + 4 * (l16 & 3);
+            v8h vf[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int d0 = dt < NN ? 16 * (NN * wave + dt) : DN + 16 * wave;
+                const v4s lo = lds_read_tr16(vb + d0);
+                const v4s hi = lds_read_tr16(vb + 16 * KS + d0);
+                const v8u16 c = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
+                                 (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
+                vf[dt] = __builtin_bit_cast(v8h, c);
+            }
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht) {
+                const int hr = 16 * ht + l16;
+                const v8h pnf = *(const v8h*)(sm.pn + hr * KT + 8 * g4);
+                const v8h prf = *(const v8h*)(sm.pr + hr * KT + 8 * g4);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+                    acc[ht][dt] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_f16(dt < NN ? pnf : prf, vf[dt], acc[ht][dt], 0, 0, 0);
+            }
+            __syncthreads();
+            if (again) break;
+        }
+        if (!again) break;
+        // every wave has read the flag (it broke out after the same barrier); clear it for the next attempt
+        m_seen = rows4_max(m_seen);
+        __syncthreads();
+        if (tid == 0) sm.restart = 0;
+    }
+
+    // ---- epilogue: lane holds heads 16 ht + 4 g4 + i at one dim of each of its dim tiles ----
+    if (g4 == 0) {
+        sm.lfin[hq] = l_run;
+        if (S == 1) lse[t * H + hq] = l_run > 0.f ? m_ref + __logf(l_run) : -INFINITY;
+        else {
+            part_ml[((t * S + s) * H + hq) * 2 + 0] = m_ref;
+            part_ml[((t * S + s) * H + hq) * 2 + 1] = l_run;
         }
     }
-    if (g4 == 0) {
-        if (S == 1) lse[t * H + h] = l_run > 0.f ? m_run + __logf(l_run) : -INFINITY;
-        else {
-            part_ml[((t * S + s) * H + h) * 2 + 0] = m_run;
-            part_ml[((t * S + s) * H + h) * 2 + 1] = l_run;
+    __syncthreads();
+    const float sfin = s_ref > 0.f ? s_ref : 1.f;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+        float inv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float l = sm.lfin[16 * ht + 4 * g4 + i];
+            inv[i] = l > 0.f ? 1.f / l : 0.f;
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const bool nope = dt < NN;
+            const int d = (nope ? 16 * (NN * wave + dt) : DN + 16 * wave) + l16;
+            float o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = acc[ht][dt][i] * (nope ? sfin : 1.f);
+            if (S == 1) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] *= inv[i];
+                if (!nope) {
+                    // inverse RoPE: pair (2p, 2p+1) lives in lanes l16 and l16 ^ 1
+                    const int pi = (d - DN) >> 1;
+                    const float cs = sm.cs[2 * pi], sn = -sm.cs[2 * pi + 1];
+                    const bool odd = d & 1;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float other = __shfl_xor(o[i], 1);
+                        const float x0 = odd ? other : o[i], x1 = odd ? o[i] : other;
+                        o[i] = odd ? x0 * sn + x1 * cs : x0 * cs - x1 * sn;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) out[(t * H + 16 * ht + 4 * g4 + i) * (int64_t)D + d] = o[i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    part_o[((t * S + s) * H + 16 * ht + 4 * g4 + i) * (int64_t)D + d] = o[i];
+            }
         }
     }
 }
@@ -767,7 +905,7 @@ static void launch_mqa_t(const uint16_t* q, const int32_t* seq, const int64_t* p
                          int k, int m, KvView comp, KvView win, int window, float sm_scale, const RopeTab& rt, int S,
                          float* out, float* lse, float* po, float* pml, hipStream_t st) {
     if constexpr (H == 64)
-        hipLaunchKernelGGL((k_mqa_w<D>), dim3((unsigned)(T * S)), dim3(256), 0, st, q, seq, pos, idx, k, m, comp, win,
+        hipLaunchKernelGGL((k_mqa64<D>), dim3((unsigned)(T * S)), dim3(256), 0, st, q, seq, pos, idx, k, m, comp, win,
                            window, sm_scale, rt, S, out, lse, po, pml);
     else
         hipLaunchKernelGGL((k_mqa<H, D>), dim3((unsigned)(T * S)), dim3(256), 0, st, q, seq, pos, idx, k, m, comp,

@@ -38,6 +38,22 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Max / sum over the four lanes l, l^16, l^32, l^48 (the same position in each
+// 16-lane row) with the gfx950 row-swap permutes; every one of the four lanes
+// gets the bitwise-identical result (each step adds or maxes one pair).
+__device__ __forceinline__ float rows4_max(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // RoPE on pair i (dims 2i, 2i+1 of the 64 rotary dims) at position pos:
 // theta_i = base^(-2i/64), angle = pos * theta_i, both in fp64.
 __device__ __forceinline__ void rope_cs(double pos, double base, int i, float& c, float& s) {

@@ -300,6 +300,88 @@ def test_dense_mqa_decode(lib, dev, gen, orc, T, B, L, H, d, W, m):
     assert_attn_close(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "dense_mqa")
 
 
+def _f64_to_bf16_bits(x):
+    """Round-to-nearest-even fp64 -> fp32 -> bf16 bits (test-side input shaping only)."""
+    b = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return b.astype(np.uint16)
+
+
+def _plant(orc, q, comp, cap, seq, rows, key_of_row, d, boost):
+    """Add to every head of each row's query a multiple of one entry's FP8 part,
+    so that entry's score rises by about ``boost`` (its value vector is unchanged)."""
+    dn = d - 64
+    tab = orc.e4m3_table()
+    qf = orc.bf16_array_to_f64(q).reshape(q.shape)
+    sm = 1.0 / math.sqrt(d)
+    for t in rows:
+        e = int(seq[t]) * cap + int(key_of_row[t])
+        kv = tab[comp[0][e]] * float(comp[2][e])
+        alpha = boost / (sm * float(kv @ kv))
+        qf[t, :, :dn] += alpha * kv[None, :]
+    return _f64_to_bf16_bits(qf)
+
+
+@pytest.mark.parametrize("kind,path,T", [
+    ("jump", "sparse", 512), ("jump", "sparse", 4), ("jump", "dense", 4),
+    ("scale", "sparse", 512), ("scale", "sparse", 4), ("scale", "dense", 4),
+])
+def test_attention_reference_restarts(lib, dev, gen, orc, kind, path, T):
+    """Inputs that break the per-split softmax references after the first tile:
+    'jump' plants, in a later tile of every row's key list, an entry whose score
+    is ~40 above the rest (reference max + 8 exceeded); 'scale' gives 1% of the
+    entries a 32x larger FP8 scale with tiny codes (scale reference x16
+    exceeded) while their values stay small.  T=512 runs one split per row
+    (many tiles), T=4 the split-KV path; rows are compared with the oracle."""
+    import torch
+
+    _say(f"attention restarts kind={kind} path={path} T={T}")
+    H, d, W = 64, 512, 128
+    dn = d - 64
+    if path == "sparse":
+        m, B, L, k = 4, 2, 16384, 1024
+    else:
+        m, B, L, k = 128, 2, 131072, 0
+    N = L // m
+    comp, win, q = _attn_inputs(gen, 700 + T, B, N, W, H, d, T, L, W)
+    seq = (np.arange(T) % B).astype(np.int32)
+    pos = np.full(T, L - 1, np.int64)
+    if path == "sparse":
+        idx = gen.random_idx(701 + T, 1, (pos + 1) // m, k)
+    else:
+        idx = None
+    if kind == "scale":
+        sel = np.random.default_rng(702).random(B * N) < 0.01
+        nope, rope, scale = comp
+        nope, scale = nope.copy(), scale.copy()
+        nope[sel] = 1  # smallest FP8 subnormal
+        scale[sel] *= 32.0
+        comp = (nope, rope, scale)
+    else:
+        # key-list position 64 * (2 + t % 9) + 37: a later tile of the row, and the
+        # second tile of its split when the key list is cut into splits of 64
+        u_star = 64 * (2 + np.arange(T) % 9) + 37
+        j_star = idx[np.arange(T), u_star] if idx is not None else u_star
+        q = _plant(orc, q, comp, N, seq, range(T), j_star, d, 40.0)
+    sm = 1.0 / math.sqrt(d)
+    qd = dev.bf16(q)
+    if path == "sparse":
+        out, lse = lib.csa_sparse_mqa(qd, dev.t(seq), dev.t(pos), dev.t(idx), m, dev.kv_cache(comp, N),
+                                      dev.kv_cache(win, W), W, sm)
+    else:
+        out, lse = lib.hca_dense_mqa(qd, dev.t(seq), dev.t(pos), m, N, dev.kv_cache(comp, N), dev.kv_cache(win, W),
+                                     W, sm)
+    torch.cuda.synchronize()
+    rows = np.arange(T) if T <= 8 else np.array([0, 1, 2, 77, 200, 301, 444, T - 1])
+    sub = lambda a: np.ascontiguousarray(a[rows])  # noqa: E731
+    ref_o, ref_l = orc.attend(sub(q), sub(seq), sub(pos), comp, N, win, W, W, m, sm,
+                              idx=sub(idx) if idx is not None else None)
+    if kind == "jump":
+        # the planted entry carries almost all the weight: the output is close to its value vector
+        assert np.all(ref_l[:, 0] > 20.0)
+    assert_attn_close(out.cpu().numpy()[rows], lse.cpu().numpy()[rows], ref_o, ref_l, f"restarts {kind} {path}")
+
+
 def test_sparse_all_selected_equals_dense(lib, dev, gen):
     """k >= visible entries: CSA equals HCA at the same m (GPU against GPU, both checked against the oracle above)."""
     import torch

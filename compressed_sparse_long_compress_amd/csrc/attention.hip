@@ -430,6 +430,10 @@ constexpr float kSRatio = 16.f;  // 2981 * 16 < 65504
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 
+// A masked key-list position (top-k padding, an entry not yet visible) reads
+// this all-zero entry, so the tile loads need no per-lane masking.
+__device__ __align__(16) uint8_t g_zero_entry[1024];
+
 template <int D>
 struct __align__(16) Mqa64Smem {
     static constexpr int KS = D + 16;  // fp16 row stride of a staged tile
@@ -437,9 +441,11 @@ struct __align__(16) Mqa64Smem {
     _Float16 pn[64 * KT];  // [head][K slot] P * scale_j / S_ref (FP8 dims)
     _Float16 pr[64 * KT];  // [head][K slot] P (RoPE dims)
     float lfin[64];
-    int64_t row[2][RB];    // two batches of resolved key-list positions
-    float scl[2][KT];      // entry scales (0 when masked)
-    int valid[2][KT];
+    // two batches of resolved key-list positions: FP8-row and RoPE-row
+    // addresses, entry scale (0 when masked) and visibility
+    const uint8_t* kaddr[2][RB][2];
+    float kscl[2][RB];
+    int kval[2][RB];
     float cs[64];
     int restart;
 };
@@ -460,10 +466,12 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
     constexpr int DN = D - 64;
     constexpr int DSTEP = D / 32, NSTEP = DN / 32;  // QK steps of 32 dims
     constexpr int NN = DN / 64, DT = NN + 1;        // PV 16-dim tiles per wave: NN FP8 tiles, then one RoPE tile
-    constexpr int CPE = DN / 16 + 8;                // 16-byte chunks per entry: FP8 part, then RoPE part
-    constexpr int NCH = (KT * CPE + 255) / 256;
+    constexpr int CPN = DN / 16;                    // 16-byte chunks of an entry's FP8 part (RoPE part: 8)
+    constexpr int NCN = KT * CPN;                   // FP8 chunks of a tile; its RoPE chunks follow
+    constexpr int NCH = (KT * (CPN + 8) + 255) / 256;
     constexpr int TPB = RB / KT;                    // tiles per batch of resolved positions
-    static_assert(RB == 256 && TPB >= 4, "one resolved position per thread, batch resolved 4+ tiles ahead");
+    static_assert(RB == 256 && TPB >= 6, "one resolved position per thread, a batch resolved 3+ tiles ahead");
+    static_assert(NCN % 64 == 0 && (KT * 8) % 64 == 0, "every wave load instruction is all FP8 or all RoPE chunks");
 
     __shared__ Sm sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -480,14 +488,30 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
     auto fetch = [&](int64_t u) -> int64_t {
         return (u < u1 && u < rk.n_c) ? (idx ? (int64_t)idx[t * k + u] : u) : 0;
     };
-    auto code_of = [&](int64_t u, int64_t j) -> int64_t {
-        if (u >= u1) return -1;
+    // position u (selected index j) -> FP8 / RoPE row addresses and scale pointer; false when masked
+    struct Res {
+        const uint8_t* an;
+        const uint8_t* ar;
+        const float* sp;
+        bool ok;
+    };
+    auto resolve_at = [&](int64_t u, int64_t j) -> Res {
+        Res r{g_zero_entry, g_zero_entry + DN, nullptr, false};
+        if (u >= u1) return r;
         if (u < rk.n_c) {
-            if (j < 0 || j >= rk.nv) return -1;
-            return (int64_t)sq * comp.cap + (j % comp.cap);
+            if (j < 0 || j >= rk.nv) return r;
+            const int64_t row = (int64_t)sq * comp.cap + (j % comp.cap);
+            return Res{comp.nope + row * DN, (const uint8_t*)(comp.rope + row * 64), comp.scale + row, true};
         }
         const int64_t p = rk.lo + (u - rk.n_c);
-        return -((int64_t)sq * win.cap + (p % win.cap) + 2);
+        const int64_t row = (int64_t)sq * win.cap + (p % win.cap);
+        return Res{win.nope + row * DN, (const uint8_t*)(win.rope + row * 64), win.scale + row, true};
+    };
+    auto publish = [&](int b, const Res& r, float sc) {
+        sm.kaddr[b][tid][0] = r.an;
+        sm.kaddr[b][tid][1] = r.ar;
+        sm.kscl[b][tid] = sc;
+        sm.kval[b][tid] = r.ok;
     };
 
     if (tid < 32) {
@@ -500,34 +524,19 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
     __syncthreads();
 
     // ---- tile loads (global -> registers) and staging (registers -> LDS) ----
-    // chunk c: entry c / CPE, part c % CPE (consecutive lanes read consecutive 16 bytes of an entry)
+    // chunk c < NCN: FP8 part of entry c / CPN, 16 bytes at (c % CPN) * 16; chunk c >= NCN:
+    // RoPE part of entry (c - NCN) / 8.  Consecutive lanes read consecutive 16 bytes of a row.
     v4i pre[NCH];
-    float pscl = 0.f;
-    int pval = 0;
     auto issue = [&](int j) {
-        const int64_t* rows = sm.row[(j / TPB) & 1] + (j % TPB) * KT;
+        const int b = (j / TPB) & 1, slot = (j % TPB) * KT;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int c = tid + i * 256;
-            pre[i] = v4i{0, 0, 0, 0};
-            if (c < KT * CPE) {
-                const int key = c / CPE, part = c % CPE;
-                const int64_t code = rows[key];
-                if (code != -1) {
-                    const bool w = code <= -2;
-                    const int64_t r = w ? -code - 2 : code;
-                    if (part < DN / 16) pre[i] = *(const v4i*)((w ? win.nope : comp.nope) + r * DN + part * 16);
-                    else pre[i] = *(const v4i*)((w ? win.rope : comp.rope) + r * 64 + (part - DN / 16) * 8);
-                }
-            }
-        }
-        if (tid < KT) {
-            const int64_t code = rows[tid];
-            pval = code != -1;
-            pscl = 0.f;
-            if (pval) {
-                const bool w = code <= -2;
-                pscl = (w ? win.scale : comp.scale)[w ? -code - 2 : code];
+            if (c < KT * (CPN + 8)) {
+                const bool np = c < NCN;
+                const int key = np ? c / CPN : (c - NCN) >> 3;
+                const int part = np ? c % CPN : (c - NCN) & 7;
+                pre[i] = *(const v4i*)(sm.kaddr[b][slot + key][np ? 0 : 1] + part * 16);
             }
         }
     };
@@ -536,46 +545,33 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int c = tid + i * 256;
-            if (c < KT * CPE) {
-                const int key = c / CPE, part = c % CPE;
-                _Float16* dst = kv + key * KS;
+            if (c < KT * (CPN + 8)) {
                 const v4i raw = pre[i];
-                if (part < DN / 16) {
-                    v8h a, b;
+                if (c < NCN) {
+                    const int key = c / CPN, part = c % CPN;
+                    uint32_t w[8];
 #pragma unroll
-                    for (int wd = 0; wd < 2; ++wd) {
-                        const v2h x0 = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[wd], 1.f, false));
-                        const v2h x1 = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[wd], 1.f, true));
-                        const v2h y0 = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[wd + 2], 1.f, false));
-                        const v2h y1 = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[wd + 2], 1.f, true));
-                        a[4 * wd] = x0[0];
-                        a[4 * wd + 1] = x0[1];
-                        a[4 * wd + 2] = x1[0];
-                        a[4 * wd + 3] = x1[1];
-                        b[4 * wd] = y0[0];
-                        b[4 * wd + 1] = y0[1];
-                        b[4 * wd + 2] = y1[0];
-                        b[4 * wd + 3] = y1[1];
+                    for (int wd = 0; wd < 4; ++wd) {
+                        w[2 * wd] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[wd], 1.f, false));
+                        w[2 * wd + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[wd], 1.f, true));
                     }
-                    *(v8h*)(dst + part * 16) = a;
-                    *(v8h*)(dst + part * 16 + 8) = b;
+                    // the two 16-byte halves in alternating order: lanes at 32-byte strides then cover all banks
+                    _Float16* dst = kv + key * KS + part * 16;
+                    const int h0 = (part & 1) * 8, h1 = 8 - h0;
+                    *(uint4*)(dst + h0) = h0 ? make_uint4(w[4], w[5], w[6], w[7]) : make_uint4(w[0], w[1], w[2], w[3]);
+                    *(uint4*)(dst + h1) = h0 ? make_uint4(w[0], w[1], w[2], w[3]) : make_uint4(w[4], w[5], w[6], w[7]);
                 } else {
-                    v8h a;
+                    const int key = (c - NCN) >> 3, part = (c - NCN) & 7;
+                    uint32_t w[4];
 #pragma unroll
                     for (int wd = 0; wd < 4; ++wd) {
                         const uint32_t u = (uint32_t)raw[wd];
-                        const v2h x = __builtin_bit_cast(
-                            v2h, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(u << 16), __uint_as_float(u & 0xFFFF0000u)));
-                        a[2 * wd] = x[0];
-                        a[2 * wd + 1] = x[1];
+                        w[wd] = __builtin_bit_cast(
+                            uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(u << 16), __uint_as_float(u & 0xFFFF0000u)));
                     }
-                    *(v8h*)(dst + DN + (part - DN / 16) * 8) = a;
+                    *(uint4*)(kv + key * KS + DN + part * 8) = make_uint4(w[0], w[1], w[2], w[3]);
                 }
             }
-        }
-        if (tid < KT) {
-            sm.scl[j & 1][tid] = pscl;
-            sm.valid[j & 1][tid] = pval;
         }
     };
 
@@ -630,7 +626,10 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
     float m_seen = -INFINITY, s_seen = 0.f;  // maxima over every tile seen (restart references)
     for (;;) {
         // ---- (re)start: batch 0 of the positions, tiles 0 and 1 in flight ----
-        sm.row[0][tid] = code_of(u0 + tid, fetch(u0 + tid));
+        {
+            const Res r = resolve_at(u0 + tid, fetch(u0 + tid));
+            publish(0, r, r.ok ? *r.sp : 0.f);
+        }
         __syncthreads();
         if (nt > 0) issue(0);
 #pragma unroll
@@ -643,7 +642,9 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
         if (nt > 0) stage(0);
         if (nt > 1) issue(1);
         __syncthreads();
-        int64_t nraw = 0;  // idx value of this thread's position in the next batch
+        int64_t nraw = 0;  // this thread's position in the next batch: selected index, then resolved
+        Res nres{g_zero_entry, g_zero_entry + DN, nullptr, false};
+        float nscl = 0.f;
         bool again = false;
 
         for (int j = 0; j < nt; ++j) {
@@ -667,10 +668,12 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
                     }
                 }
             }
+            const float* tscl = sm.kscl[(j / TPB) & 1] + (j % TPB) * KT;
+            const int* tval = sm.kval[(j / TPB) & 1] + (j % TPB) * KT;
             // tile max of the entry scales (the same in every wave)
             float st_max;
             {
-                const float4 a = *(const float4*)(sm.scl[buf] + 4 * (lane & 7));
+                const float4 a = *(const float4*)(tscl + 4 * (lane & 7));
                 st_max = fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w));
                 st_max = fmaxf(st_max, __shfl_xor(st_max, 1));
                 st_max = fmaxf(st_max, __shfl_xor(st_max, 2));
@@ -681,8 +684,8 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
             float kscl[8];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const float4 sc = *(const float4*)(sm.scl[buf] + ks * 16 + 4 * g4);
-                const int4 vl = *(const int4*)(sm.valid[buf] + ks * 16 + 4 * g4);
+                const float4 sc = *(const float4*)(tscl + ks * 16 + 4 * g4);
+                const int4 vl = *(const int4*)(tval + ks * 16 + 4 * g4);
                 const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
                 const int vlv[4] = {vl.x, vl.y, vl.z, vl.w};
 #pragma unroll
@@ -721,10 +724,17 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
             // ---- stage the next tile, resolve the next batch of positions, load the tile after ----
             if (j + 1 < nt) stage(j + 1);
             {
-                const int b1 = j / TPB + 1;  // next batch
+                // next batch: index load, then addresses and scale load, then publish (first used 3 tiles later)
+                const int b1 = j / TPB + 1;
                 const int64_t u = u0 + (int64_t)b1 * RB + tid;
-                if (j % TPB == 1 && b1 * TPB < nt) nraw = fetch(u);
-                if (j % TPB == 2 && b1 * TPB < nt) sm.row[b1 & 1][tid] = code_of(u, nraw);
+                if (b1 * TPB < nt) {
+                    if (j % TPB == 1) nraw = fetch(u);
+                    if (j % TPB == 2) {
+                        nres = resolve_at(u, nraw);
+                        nscl = nres.ok ? *nres.sp : 0.f;
+                    }
+                    if (j % TPB == 3) publish(b1 & 1, nres, nscl);
+                }
             }
             if (j + 2 < nt) issue(j + 2);
 

@@ -429,6 +429,7 @@ constexpr float kLazy = 8.f;     // e^8 ~ 2981
 constexpr float kSRatio = 16.f;  // 2981 * 16 < 65504
 
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 // A masked key-list position (top-k padding, an entry not yet visible) reads
 // this all-zero entry, so the tile loads need no per-lane masking.
@@ -437,9 +438,10 @@ __device__ __align__(16) uint8_t g_zero_entry[1024];
 template <int D>
 struct __align__(16) Mqa64Smem {
     static constexpr int KS = D + 16;  // fp16 row stride of a staged tile
-    _Float16 kv[2][KT * KS];
-    _Float16 pn[64 * KT];  // [head][K slot] P * scale_j / S_ref (FP8 dims)
-    _Float16 pr[64 * KT];  // [head][K slot] P (RoPE dims)
+    static constexpr int PS = KT + 8;  // fp16 row stride of P (80-byte rows: 16 lanes hit 16 distinct bank groups)
+    _Float16 kv[3][KT * KS];           // tile t in kv[t % 3]
+    _Float16 pn[64 * PS];  // [head][K slot] P * scale_j / S_ref (FP8 dims)
+    _Float16 pr[64 * PS];  // [head][K slot] P (RoPE dims)
     float lfin[64];
     // two batches of resolved key-list positions: FP8-row and RoPE-row
     // addresses, entry scale (0 when masked) and visibility
@@ -449,6 +451,13 @@ struct __align__(16) Mqa64Smem {
     float cs[64];
     int restart;
 };
+
+// Loads through addresses read back from LDS: tell the compiler they are global memory.
+typedef const __attribute__((address_space(1))) uint8_t* gptr_t;
+template <typename T>
+__device__ __forceinline__ T gload(const uint8_t* p) {
+    return *(const __attribute__((address_space(1))) T*)(gptr_t)p;
+}
 
 __device__ __forceinline__ v4s lds_read_tr16(const _Float16* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
@@ -467,11 +476,11 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
     constexpr int DSTEP = D / 32, NSTEP = DN / 32;  // QK steps of 32 dims
     constexpr int NN = DN / 64, DT = NN + 1;        // PV 16-dim tiles per wave: NN FP8 tiles, then one RoPE tile
     constexpr int CPN = DN / 16;                    // 16-byte chunks of an entry's FP8 part (RoPE part: 8)
-    constexpr int NCN = KT * CPN;                   // FP8 chunks of a tile; its RoPE chunks follow
-    constexpr int NCH = (KT * (CPN + 8) + 255) / 256;
+    constexpr int NCN = KT * CPN;                   // FP8 chunks of a tile
+    constexpr int NFULL = NCN / 256;                // whole FP8 chunks per thread; the other NCN % 256 go by halves
     constexpr int TPB = RB / KT;                    // tiles per batch of resolved positions
     static_assert(RB == 256 && TPB >= 6, "one resolved position per thread, a batch resolved 3+ tiles ahead");
-    static_assert(NCN % 64 == 0 && (KT * 8) % 64 == 0, "every wave load instruction is all FP8 or all RoPE chunks");
+    static_assert(KT * 8 == 256 && NCN % 256 == 128, "per thread: NFULL FP8 chunks, one RoPE chunk, one FP8 half chunk");
 
     __shared__ Sm sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -524,54 +533,54 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
     __syncthreads();
 
     // ---- tile loads (global -> registers) and staging (registers -> LDS) ----
-    // chunk c < NCN: FP8 part of entry c / CPN, 16 bytes at (c % CPN) * 16; chunk c >= NCN:
-    // RoPE part of entry (c - NCN) / 8.  Consecutive lanes read consecutive 16 bytes of a row.
-    v4i pre[NCH];
+    // Per thread and tile: FP8 chunks c = tid + 256 i (i < NFULL; entry c / CPN, bytes (c % CPN) * 16),
+    // the RoPE chunk of entry tid / 8 (bytes (tid % 8) * 16), and 8 bytes of FP8 chunk
+    // 256 NFULL + tid / 2.  Consecutive lanes read consecutive bytes of a row; no branches.
+    v4i pre[NFULL > 0 ? NFULL : 1];
+    v4i pre_r;
+    v2u pre_h;
     auto issue = [&](int j) {
         const int b = (j / TPB) & 1, slot = (j % TPB) * KT;
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
+        for (int i = 0; i < NFULL; ++i) {
             const int c = tid + i * 256;
-            if (c < KT * (CPN + 8)) {
-                const bool np = c < NCN;
-                const int key = np ? c / CPN : (c - NCN) >> 3;
-                const int part = np ? c % CPN : (c - NCN) & 7;
-                pre[i] = *(const v4i*)(sm.kaddr[b][slot + key][np ? 0 : 1] + part * 16);
-            }
+            pre[i] = gload<v4i>(sm.kaddr[b][slot + c / CPN][0] + (c % CPN) * 16);
         }
+        pre_r = gload<v4i>(sm.kaddr[b][slot + (tid >> 3)][1] + (tid & 7) * 16);
+        const int ch = 256 * NFULL + (tid >> 1);
+        pre_h = gload<v2u>(sm.kaddr[b][slot + ch / CPN][0] + (ch % CPN) * 16 + (tid & 1) * 8);
+    };
+    auto fp8x8_to_f16 = [](uint32_t lo, uint32_t hi) -> uint4 {
+        return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.f, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.f, true)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.f, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.f, true)));
     };
     auto stage = [&](int j) {
-        _Float16* kv = sm.kv[j & 1];
+        _Float16* kv = sm.kv[j % 3];
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
+        for (int i = 0; i < NFULL; ++i) {
             const int c = tid + i * 256;
-            if (c < KT * (CPN + 8)) {
-                const v4i raw = pre[i];
-                if (c < NCN) {
-                    const int key = c / CPN, part = c % CPN;
-                    uint32_t w[8];
+            const int part = c % CPN;
+            const uint4 lo = fp8x8_to_f16((uint32_t)pre[i][0], (uint32_t)pre[i][1]);
+            const uint4 hi = fp8x8_to_f16((uint32_t)pre[i][2], (uint32_t)pre[i][3]);
+            _Float16* dst = kv + (c / CPN) * KS + part * 16;
+            *(uint4*)dst = lo;
+            *(uint4*)(dst + 8) = hi;
+        }
+        {
+            uint32_t w[4];
 #pragma unroll
-                    for (int wd = 0; wd < 4; ++wd) {
-                        w[2 * wd] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[wd], 1.f, false));
-                        w[2 * wd + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[wd], 1.f, true));
-                    }
-                    // the two 16-byte halves in alternating order: lanes at 32-byte strides then cover all banks
-                    _Float16* dst = kv + key * KS + part * 16;
-                    const int h0 = (part & 1) * 8, h1 = 8 - h0;
-                    *(uint4*)(dst + h0) = h0 ? make_uint4(w[4], w[5], w[6], w[7]) : make_uint4(w[0], w[1], w[2], w[3]);
-                    *(uint4*)(dst + h1) = h0 ? make_uint4(w[0], w[1], w[2], w[3]) : make_uint4(w[4], w[5], w[6], w[7]);
-                } else {
-                    const int key = (c - NCN) >> 3, part = (c - NCN) & 7;
-                    uint32_t w[4];
-#pragma unroll
-                    for (int wd = 0; wd < 4; ++wd) {
-                        const uint32_t u = (uint32_t)raw[wd];
-                        w[wd] = __builtin_bit_cast(
-                            uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(u << 16), __uint_as_float(u & 0xFFFF0000u)));
-                    }
-                    *(uint4*)(kv + key * KS + DN + part * 8) = make_uint4(w[0], w[1], w[2], w[3]);
-                }
+            for (int wd = 0; wd < 4; ++wd) {
+                const uint32_t u = (uint32_t)pre_r[wd];
+                w[wd] = __builtin_bit_cast(
+                    uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(u << 16), __uint_as_float(u & 0xFFFF0000u)));
             }
+            *(uint4*)(kv + (tid >> 3) * KS + DN + (tid & 7) * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        {
+            const int ch = 256 * NFULL + (tid >> 1);
+            *(uint4*)(kv + (ch / CPN) * KS + (ch % CPN) * 16 + (tid & 1) * 8) = fp8x8_to_f16(pre_h[0], pre_h[1]);
         }
     };
 
@@ -624,8 +633,120 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
     v4f acc[4][DT];
     float m_ref = -INFINITY, l_run = 0.f, s_ref = 0.f;
     float m_seen = -INFINITY, s_seen = 0.f;  // maxima over every tile seen (restart references)
+    int64_t nraw = 0;  // this thread's position in the next batch: selected index, then resolved
+    Res nres{g_zero_entry, g_zero_entry + DN, nullptr, false};
+    float nscl = 0.f;
+
+    // S^T (keys x heads) of tile j for this wave's 16 heads: FP8-dim and RoPE-dim parts
+    auto qk = [&](int j, v4f (&an)[2], v4f (&ar)[2]) {
+        const _Float16* kb = sm.kv[j % 3] + l16 * KS + 8 * g4;
+        an[0] = an[1] = ar[0] = ar[1] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < DSTEP; ++st) {
+            const v8h k0 = *(const v8h*)(kb + 32 * st);
+            const v8h k1 = *(const v8h*)(kb + 16 * KS + 32 * st);
+            if (st < NSTEP) {
+                an[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[st], an[0], 0, 0, 0);
+                an[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[st], an[1], 0, 0, 0);
+            } else {
+                ar[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[st], ar[0], 0, 0, 0);
+                ar[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[st], ar[1], 0, 0, 0);
+            }
+        }
+    };
+    // scores and P of tile j for head hq; returns whether a reference is exceeded
+    auto softmax = [&](int j, const v4f (&an)[2], const v4f (&ar)[2]) -> bool {
+        const float* tscl = sm.kscl[(j / TPB) & 1] + (j % TPB) * KT;
+        const int* tval = sm.kval[(j / TPB) & 1] + (j % TPB) * KT;
+        // tile max of the entry scales (the same in every wave)
+        float st_max;
+        {
+            const float4 a = *(const float4*)(tscl + 4 * (lane & 7));
+            st_max = fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w));
+            st_max = fmaxf(st_max, __shfl_xor(st_max, 1));
+            st_max = fmaxf(st_max, __shfl_xor(st_max, 2));
+            st_max = fmaxf(st_max, __shfl_xor(st_max, 4));
+        }
+        // lane (l16, g4) holds keys 4 g4 + i and 16 + 4 g4 + i
+        float sv[8];
+        float kscl[8];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const float4 sc = *(const float4*)(tscl + ks * 16 + 4 * g4);
+            const int4 vl = *(const int4*)(tval + ks * 16 + 4 * g4);
+            const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
+            const int vlv[4] = {vl.x, vl.y, vl.z, vl.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                kscl[ks * 4 + i] = scv[i];
+                sv[ks * 4 + i] = vlv[i] ? sm_q * fmaf(scv[i], an[ks][i], ar[ks][i]) : -INFINITY;
+            }
+        }
+        float mx = sv[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+        mx = rows4_max(mx);
+        m_seen = fmaxf(m_seen, mx);
+        s_seen = fmaxf(s_seen, st_max);
+        m_ref = m_ref == -INFINITY ? mx : m_ref;  // first tile with visible keys (accumulators still zero)
+        s_ref = s_ref == 0.f ? st_max : s_ref;
+        const bool over = mx > m_ref + kLazy || st_max > kSRatio * s_ref;
+        const float inv_s = s_ref > 0.f ? 1.f / s_ref : 0.f;
+        v8h pn, pr;
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float p = m_ref == -INFINITY ? 0.f : __expf(sv[i] - m_ref);
+            sum += p;
+            pr[i] = (_Float16)p;
+            pn[i] = (_Float16)(p * (kscl[i] * inv_s));
+        }
+        l_run += rows4_sum(sum);
+        *(v8h*)(sm.pn + hq * Sm::PS + 8 * g4) = pn;
+        *(v8h*)(sm.pr + hq * Sm::PS + 8 * g4) = pr;
+        return over;
+    };
+    // O[heads x dims] += P V (tile j) for all heads over this wave's dims
+    auto pv = [&](int j) {
+        const _Float16* vb = sm.kv[j % 3] + (4 * g4 + (l16 >> 2)) * KS + 4 * (l16 & 3);
+        v8h vf[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int d0 = dt < NN ? 16 * (NN * wave + dt) : DN + 16 * wave;
+            const v4s lo = lds_read_tr16(vb + d0);
+            const v4s hi = lds_read_tr16(vb + 16 * KS + d0);
+            const v8u16 c = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
+                             (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
+            vf[dt] = __builtin_bit_cast(v8h, c);
+        }
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) {
+            const int hr = 16 * ht + l16;
+            const v8h pnf = *(const v8h*)(sm.pn + hr * Sm::PS + 8 * g4);
+            const v8h prf = *(const v8h*)(sm.pr + hr * Sm::PS + 8 * g4);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                acc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dt < NN ? pnf : prf, vf[dt], acc[ht][dt], 0, 0, 0);
+        }
+    };
+    // next batch of positions: index load, then addresses and scale load, then publish (first used 3 tiles later)
+    auto batch_step = [&](int j) {
+        const int b1 = j / TPB + 1;
+        const int64_t u = u0 + (int64_t)b1 * RB + tid;
+        if (b1 * TPB < nt) {
+            if (j % TPB == 1) nraw = fetch(u);
+            if (j % TPB == 2) {
+                nres = resolve_at(u, nraw);
+                nscl = nres.ok ? *nres.sp : 0.f;
+            }
+            if (j % TPB == 3) publish(b1 & 1, nres, nscl);
+        }
+    };
+
+    // Per tile, two barriers: [QK(j), softmax(j) -> P]  sync  [stage(j+1), load j+2, PV(j)]  sync.
+    // Tile t lives in kv[t % 3].
     for (;;) {
-        // ---- (re)start: batch 0 of the positions, tiles 0 and 1 in flight ----
+        // ---- (re)start: batch 0 of the positions, tile 0 staged, tile 1 in flight ----
         {
             const Res r = resolve_at(u0 + tid, fetch(u0 + tid));
             publish(0, r, r.ok ? *r.sp : 0.f);
@@ -642,124 +763,20 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
         if (nt > 0) stage(0);
         if (nt > 1) issue(1);
         __syncthreads();
-        int64_t nraw = 0;  // this thread's position in the next batch: selected index, then resolved
-        Res nres{g_zero_entry, g_zero_entry + DN, nullptr, false};
-        float nscl = 0.f;
         bool again = false;
 
         for (int j = 0; j < nt; ++j) {
-            const int buf = j & 1;
-            const _Float16* kv = sm.kv[buf];
-            // ---- S^T (keys x heads) for this wave's 16 heads ----
-            v4f an[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-            v4f ar[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-            {
-                const _Float16* kb = kv + l16 * KS + 8 * g4;
-#pragma unroll
-                for (int st = 0; st < DSTEP; ++st) {
-                    const v8h k0 = *(const v8h*)(kb + 32 * st);
-                    const v8h k1 = *(const v8h*)(kb + 16 * KS + 32 * st);
-                    if (st < NSTEP) {
-                        an[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[st], an[0], 0, 0, 0);
-                        an[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[st], an[1], 0, 0, 0);
-                    } else {
-                        ar[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[st], ar[0], 0, 0, 0);
-                        ar[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[st], ar[1], 0, 0, 0);
-                    }
-                }
-            }
-            const float* tscl = sm.kscl[(j / TPB) & 1] + (j % TPB) * KT;
-            const int* tval = sm.kval[(j / TPB) & 1] + (j % TPB) * KT;
-            // tile max of the entry scales (the same in every wave)
-            float st_max;
-            {
-                const float4 a = *(const float4*)(tscl + 4 * (lane & 7));
-                st_max = fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w));
-                st_max = fmaxf(st_max, __shfl_xor(st_max, 1));
-                st_max = fmaxf(st_max, __shfl_xor(st_max, 2));
-                st_max = fmaxf(st_max, __shfl_xor(st_max, 4));
-            }
-            // ---- scores of head hq: lane (l16, g4) holds keys 4 g4 + i and 16 + 4 g4 + i ----
-            float sv[8];
-            float kscl[8];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const float4 sc = *(const float4*)(tscl + ks * 16 + 4 * g4);
-                const int4 vl = *(const int4*)(tval + ks * 16 + 4 * g4);
-                const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
-                const int vlv[4] = {vl.x, vl.y, vl.z, vl.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    kscl[ks * 4 + i] = scv[i];
-                    sv[ks * 4 + i] = vlv[i] ? sm_q * fmaf(scv[i], an[ks][i], ar[ks][i]) : -INFINITY;
-                }
-            }
-            float mx = sv[0];
-#pragma unroll
-            for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-            mx = rows4_max(mx);
-            m_seen = fmaxf(m_seen, mx);
-            s_seen = fmaxf(s_seen, st_max);
-            if (m_ref == -INFINITY) m_ref = mx;     // first tile with visible keys (accumulators still zero)
-            if (s_ref == 0.f) s_ref = st_max;
-            if (mx > m_ref + kLazy || st_max > kSRatio * s_ref) sm.restart = 1;
-            const float inv_s = s_ref > 0.f ? 1.f / s_ref : 0.f;
-            v8h pn, pr;
-            float sum = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float p = m_ref == -INFINITY ? 0.f : __expf(sv[i] - m_ref);
-                sum += p;
-                pr[i] = (_Float16)p;
-                pn[i] = (_Float16)(p * (kscl[i] * inv_s));
-            }
-            l_run += rows4_sum(sum);
-            *(v8h*)(sm.pn + hq * KT + 8 * g4) = pn;
-            *(v8h*)(sm.pr + hq * KT + 8 * g4) = pr;
+            v4f sn[2], sr[2];
+            qk(j, sn, sr);
+            if (softmax(j, sn, sr)) sm.restart = 1;
             __syncthreads();
             // a restart finishes this iteration first (its output is discarded): leaving the
             // loop from the middle of the body makes the compiler shuttle the accumulators
             again = sm.restart != 0;
-
-            // ---- stage the next tile, resolve the next batch of positions, load the tile after ----
             if (j + 1 < nt) stage(j + 1);
-            {
-                // next batch: index load, then addresses and scale load, then publish (first used 3 tiles later)
-                const int b1 = j / TPB + 1;
-                const int64_t u = u0 + (int64_t)b1 * RB + tid;
-                if (b1 * TPB < nt) {
-                    if (j % TPB == 1) nraw = fetch(u);
-                    if (j % TPB == 2) {
-                        nres = resolve_at(u, nraw);
-                        nscl = nres.ok ? *nres.sp : 0.f;
-                    }
-                    if (j % TPB == 3) publish(b1 & 1, nres, nscl);
-                }
-            }
             if (j + 2 < nt) issue(j + 2);
-
-            // ---- O[heads x dims] += P V for all heads over this wave's dims ----
-            const _Float16* vb = kv + (4 * g4 + (l16 >> 2)) * KS + 4 * (l16 & 3);
-            v8h vf[DT];
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const int d0 = dt < NN ? 16 * (NN * wave + dt) : DN + 16 * wave;
-                const v4s lo = lds_read_tr16(vb + d0);
-                const v4s hi = lds_read_tr16(vb + 16 * KS + d0);
-                const v8u16 c = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
-                                 (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
-                vf[dt] = __builtin_bit_cast(v8h, c);
-            }
-#pragma unroll
-            for (int ht = 0; ht < 4; ++ht) {
-                const int hr = 16 * ht + l16;
-                const v8h pnf = *(const v8h*)(sm.pn + hr * KT + 8 * g4);
-                const v8h prf = *(const v8h*)(sm.pr + hr * KT + 8 * g4);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-                    acc[ht][dt] =
-                        __builtin_amdgcn_mfma_f32_16x16x32_f16(dt < NN ? pnf : prf, vf[dt], acc[ht][dt], 0, 0, 0);
-            }
+            pv(j);
+            batch_step(j);
             __syncthreads();
             if (again) break;
         }

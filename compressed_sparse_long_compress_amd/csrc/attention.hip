@@ -627,6 +627,9 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 qf[st][e] = (_Float16)((st < NSTEP ? bf16_bits_to_f32(hv[e]) : xr[st - NSTEP][e]) * qs);
+            // keep the query in AGPRs (MFMA reads its B operand from there): the VGPRs
+            // are left for K fragments in flight, softmax and the tile loads
+            asm volatile("" : "+a"(qf[st]));
         }
     }
 
@@ -638,20 +641,42 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
     float nscl = 0.f;
 
     // S^T (keys x heads) of tile j for this wave's 16 heads: FP8-dim and RoPE-dim parts
+    // K fragments go in groups of QG dim steps, the next group's loads issued before this
+    // group's MFMAs (the scheduler is not allowed to sink them: 2 QG loads in flight).
+    constexpr int QG = 4;
+    static_assert(DSTEP % QG == 0, "whole groups");
     auto qk = [&](int j, v4f (&an)[2], v4f (&ar)[2]) {
         const _Float16* kb = sm.kv[j % 3] + l16 * KS + 8 * g4;
         an[0] = an[1] = ar[0] = ar[1] = v4f{0.f, 0.f, 0.f, 0.f};
+        v8h kf[2][2 * QG];
 #pragma unroll
-        for (int st = 0; st < DSTEP; ++st) {
-            const v8h k0 = *(const v8h*)(kb + 32 * st);
-            const v8h k1 = *(const v8h*)(kb + 16 * KS + 32 * st);
-            if (st < NSTEP) {
-                an[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[st], an[0], 0, 0, 0);
-                an[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[st], an[1], 0, 0, 0);
-            } else {
-                ar[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[st], ar[0], 0, 0, 0);
-                ar[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[st], ar[1], 0, 0, 0);
+        for (int e = 0; e < QG; ++e) {
+            kf[0][2 * e] = *(const v8h*)(kb + 32 * e);
+            kf[0][2 * e + 1] = *(const v8h*)(kb + 16 * KS + 32 * e);
+        }
+#pragma unroll
+        for (int g = 0; g < DSTEP / QG; ++g) {
+            if (g + 1 < DSTEP / QG) {
+#pragma unroll
+                for (int e = 0; e < QG; ++e) {
+                    const int st = (g + 1) * QG + e;
+                    kf[(g + 1) & 1][2 * e] = *(const v8h*)(kb + 32 * st);
+                    kf[(g + 1) & 1][2 * e + 1] = *(const v8h*)(kb + 16 * KS + 32 * st);
+                }
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < QG; ++e) {
+                const int st = g * QG + e;
+                if (st < NSTEP) {
+                    an[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[g & 1][2 * e], qf[st], an[0], 0, 0, 0);
+                    an[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[g & 1][2 * e + 1], qf[st], an[1], 0, 0, 0);
+                } else {
+                    ar[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[g & 1][2 * e], qf[st], ar[0], 0, 0, 0);
+                    ar[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[g & 1][2 * e + 1], qf[st], ar[1], 0, 0, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
     // scores and P of tile j for head hq; returns whether a reference is exceeded

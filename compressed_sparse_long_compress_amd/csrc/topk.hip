@@ -12,7 +12,7 @@
 
 namespace csa {
 
-constexpr int kTopkThreads = 512;
+constexpr int kTopkThreads = 1024;
 constexpr int kTopkCache = 36608;  // keys cached in LDS (143 KB)
 
 // exclusive prefix sum over the block; returns the block total in `total`
@@ -74,10 +74,10 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_row(const float* __restri
                                                            const int64_t* __restrict__ pos, int m, int k,
                                                            int32_t* __restrict__ idx) {
     __shared__ uint32_t hist[4096];
-    __shared__ uint32_t cache[kTopkCache];
-    __shared__ int wsum[kTopkThreads / 64];
+    __shared__ __align__(16) uint32_t cache[kTopkCache];
+    __shared__ int wsum[2 * (kTopkThreads / 64)];
     __shared__ int bcast[4];
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t t = blockIdx.x;
     int64_t nv64 = (pos[t] + 1) / m;
     if (nv64 > n_cols) nv64 = n_cols;
@@ -91,25 +91,66 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_row(const float* __restri
         return;
     }
     const bool cached = nv <= kTopkCache;
-    if (cached)
-        for (int j = tid; j < nv; j += kTopkThreads) cache[j] = f32_order_key(row[j]);
     auto key_at = [&](int j) -> uint32_t { return cached ? cache[j] : f32_order_key(row[j]); };
-
-    // pass 1: top 12 bits
     for (int i = tid; i < 4096; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
-    for (int j = tid; j < nv; j += kTopkThreads) atomicAdd(&hist[key_at(j) >> 20], 1u);
+
+    // load the row into LDS (16-byte loads when aligned, several in flight) and histogram the top 12 bits
+    if (cached && (((uintptr_t)row & 15) == 0)) {
+        const int n4 = nv >> 2;
+#pragma unroll 4
+        for (int j4 = tid; j4 < n4; j4 += kTopkThreads) {
+            const float4 v = ((const float4*)row)[j4];
+            const uint4 kk = make_uint4(f32_order_key(v.x), f32_order_key(v.y), f32_order_key(v.z), f32_order_key(v.w));
+            *(uint4*)&cache[4 * j4] = kk;
+            atomicAdd(&hist[kk.x >> 20], 1u);
+            atomicAdd(&hist[kk.y >> 20], 1u);
+            atomicAdd(&hist[kk.z >> 20], 1u);
+            atomicAdd(&hist[kk.w >> 20], 1u);
+        }
+        for (int j = 4 * n4 + tid; j < nv; j += kTopkThreads) {
+            const uint32_t kk = f32_order_key(row[j]);
+            cache[j] = kk;
+            atomicAdd(&hist[kk >> 20], 1u);
+        }
+    } else {
+        for (int j = tid; j < nv; j += kTopkThreads) {
+            const uint32_t kk = f32_order_key(row[j]);
+            if (cached) cache[j] = kk;
+            atomicAdd(&hist[kk >> 20], 1u);
+        }
+    }
     __syncthreads();
     int above1;
     const uint32_t b1 = (uint32_t)find_bin<4096>(hist, k, wsum, bcast, above1);
 
+    // refinement passes over the keys whose prefix matches (LDS read 4 keys at a time)
+    auto refine = [&](auto match, auto bin) {
+        if (cached) {
+            const int n4 = nv >> 2;
+            for (int j4 = tid; j4 < n4; j4 += kTopkThreads) {
+                const uint4 kk = *(const uint4*)&cache[4 * j4];
+                if (match(kk.x)) atomicAdd(&hist[bin(kk.x)], 1u);
+                if (match(kk.y)) atomicAdd(&hist[bin(kk.y)], 1u);
+                if (match(kk.z)) atomicAdd(&hist[bin(kk.z)], 1u);
+                if (match(kk.w)) atomicAdd(&hist[bin(kk.w)], 1u);
+            }
+            for (int j = 4 * n4 + tid; j < nv; j += kTopkThreads) {
+                const uint32_t kk = cache[j];
+                if (match(kk)) atomicAdd(&hist[bin(kk)], 1u);
+            }
+        } else {
+            for (int j = tid; j < nv; j += kTopkThreads) {
+                const uint32_t kk = f32_order_key(row[j]);
+                if (match(kk)) atomicAdd(&hist[bin(kk)], 1u);
+            }
+        }
+    };
+
     // pass 2: middle 12 bits among keys with prefix b1
     for (int i = tid; i < 4096; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
-    for (int j = tid; j < nv; j += kTopkThreads) {
-        uint32_t key = key_at(j);
-        if ((key >> 20) == b1) atomicAdd(&hist[(key >> 8) & 0xFFF], 1u);
-    }
+    refine([&](uint32_t kk) { return (kk >> 20) == b1; }, [](uint32_t kk) { return (kk >> 8) & 0xFFFu; });
     __syncthreads();
     int above2;
     const uint32_t b2 = (uint32_t)find_bin<4096>(hist, k - above1, wsum, bcast, above2);
@@ -118,46 +159,48 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_row(const float* __restri
     // pass 3: low 8 bits among keys with prefix p2
     for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
-    for (int j = tid; j < nv; j += kTopkThreads) {
-        uint32_t key = key_at(j);
-        if ((key >> 8) == p2) atomicAdd(&hist[key & 0xFF], 1u);
-    }
+    refine([&](uint32_t kk) { return (kk >> 8) == p2; }, [](uint32_t kk) { return kk & 0xFFu; });
     __syncthreads();
     int above3;
     const uint32_t b3 = (uint32_t)find_bin<256>(hist, k - above1 - above2, wsum, bcast, above3);
     const uint32_t thr = (p2 << 8) | b3;
     const int need_eq = k - (above1 + above2 + above3);
 
-    // pass 4: ordered compaction, 4 consecutive columns per thread per tile
-    constexpr int E = 4;
-    int eq_run = 0, out_run = 0;
-    for (int j0 = 0; j0 < nv; j0 += kTopkThreads * E) {
-        const int jb = j0 + tid * E;
-        uint32_t kk[E];
-        int n_eq = 0;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            kk[e] = jb + e < nv ? key_at(jb + e) : 0u;
-            n_eq += (jb + e < nv && kk[e] == thr) ? 1 : 0;
-        }
-        int eq_tot;
-        int eq_before = block_excl_scan(n_eq, wsum, eq_tot) + eq_run;
-        int sel[E], n_sel = 0;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const bool in = jb + e < nv;
-            const bool eq = in && kk[e] == thr;
-            sel[e] = in && (kk[e] > thr || (eq && eq_before < need_eq));
-            eq_before += eq ? 1 : 0;
-            n_sel += sel[e];
-        }
-        int sel_tot;
-        int o = block_excl_scan(n_sel, wsum, sel_tot) + out_run;
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            if (sel[e]) out[o++] = jb + e;
-        eq_run += eq_tot;
-        out_run += sel_tot;
+    // ordered compaction: wave w owns the contiguous columns [w seg, (w+1) seg); ranks within a
+    // wave come from ballots, across waves from one exchange of (#greater, #equal) per wave
+    constexpr int NW = kTopkThreads / 64;
+    const int seg = (nv + NW * 64 - 1) / (NW * 64) * 64;
+    const int s0 = wave * seg < nv ? wave * seg : nv;
+    const int s1 = s0 + seg < nv ? s0 + seg : nv;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    int cgt = 0, ceq = 0;
+    for (int b = s0; b < s1; b += 64) {
+        const int j = b + lane;
+        const uint32_t kk = j < s1 ? key_at(j) : 0u;
+        cgt += __popcll(__ballot(j < s1 && kk > thr));
+        ceq += __popcll(__ballot(j < s1 && kk == thr));
+    }
+    if (lane == 0) {
+        wsum[2 * wave] = cgt;
+        wsum[2 * wave + 1] = ceq;
+    }
+    __syncthreads();
+    int gtb = 0, eqb = 0;
+    for (int w = 0; w < wave; ++w) {
+        gtb += wsum[2 * w];
+        eqb += wsum[2 * w + 1];
+    }
+    int eqrun = eqb, orun = gtb + (eqb < need_eq ? eqb : need_eq);
+    for (int b = s0; b < s1; b += 64) {
+        const int j = b + lane;
+        const uint32_t kk = j < s1 ? key_at(j) : 0u;
+        const bool eq = j < s1 && kk == thr;
+        const uint64_t eqm = __ballot(eq);
+        const bool sel = (j < s1 && kk > thr) || (eq && eqrun + __popcll(eqm & lt) < need_eq);
+        const uint64_t selm = __ballot(sel);
+        if (sel) out[orun + __popcll(selm & lt)] = j;
+        eqrun += __popcll(eqm);
+        orun += __popcll(selm);
     }
 }
 

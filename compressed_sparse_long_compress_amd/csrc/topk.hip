@@ -228,6 +228,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_row(const float* __restri
 // T x n_cols candidates.
 // ---------------------------------------------------------------------------
 constexpr int kTmThreads = 256;
+constexpr int kTfThreads = 1024;  // the per-row finaliser
 constexpr int kTmE = 8;  // consecutive columns per thread in the collect pass
 constexpr int kBitmapWords = 16384;  // row bitmap of the finaliser: rows up to 524,288 columns
 constexpr int kCandLds = 4096;       // candidates the finaliser stages in LDS
@@ -306,27 +307,31 @@ __global__ __launch_bounds__(kTmThreads) void k_topkm_hist(const float* __restri
 // at position (r % PER) * 256 + r / PER.  Thread t then owns ranks
 // t*PER .. t*PER+PER-1 and reads them at positions i*256 + t: consecutive
 // threads, consecutive words, no LDS bank conflicts.
-template <int NB>
+template <int NB, int NT = kTmThreads>
 __device__ __forceinline__ int tm_pos(uint32_t bin) {
-    constexpr int PER = NB / kTmThreads > 0 ? NB / kTmThreads : 1;
+    constexpr int PER = NB / NT > 0 ? NB / NT : 1;
     const int r = NB - 1 - (int)bin;
-    return (r % PER) * kTmThreads + r / PER;
+    return (r % PER) * NT + r / PER;
 }
 
 // 4096-bin global histogram into the transposed LDS layout: thread t loads
-// its 16 consecutive bins (4 x 16 B, issued together) and scatters them.
+// its PER = 4096/NT consecutive bins (16-byte loads, issued together) and
+// scatters them.
+template <int NT = kTmThreads>
 __device__ __forceinline__ void tm_load_hist(uint32_t* dst, const uint32_t* src) {
+    constexpr int PER = 4096 / NT, NV = PER / 4;
     const int t = threadIdx.x;
-    uint4 v[4];
-    const uint4* p = (const uint4*)(src + 4096 - 16 * (t + 1));  // bins 4095-16t-15 .. 4095-16t
+    uint4 v[NV];
+    const uint4* p = (const uint4*)(src + 4096 - PER * (t + 1));  // bins 4096-PER(t+1) .. 4095-PER t
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = p[i];
-    const uint32_t* w = (const uint32_t*)v;  // w[q] = bin 4096-16(t+1)+q = rank 16t+15-q
+    for (int i = 0; i < NV; ++i) v[i] = p[i];
+    const uint32_t* w = (const uint32_t*)v;  // w[q] = bin 4096-PER(t+1)+q = rank PER t+PER-1-q
 #pragma unroll
-    for (int q = 0; q < 16; ++q) dst[(15 - q) * kTmThreads + t] = w[q];
+    for (int q = 0; q < PER; ++q) dst[(PER - 1 - q) * NT + t] = w[q];
 }
 
-// exclusive scan over a 256-thread block
+// exclusive scan over an NT-thread block
+template <int NT = kTmThreads>
 __device__ __forceinline__ int tm_scan(int v, int* wsum, int& total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int x = v;
@@ -339,7 +344,7 @@ __device__ __forceinline__ int tm_scan(int v, int* wsum, int& total) {
     __syncthreads();
     int off = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < kTmThreads / 64; ++i) {
+    for (int i = 0; i < NT / 64; ++i) {
         off += i < wave ? wsum[i] : 0;
         tot += wsum[i];
     }
@@ -349,20 +354,20 @@ __device__ __forceinline__ int tm_scan(int v, int* wsum, int& total) {
 }
 
 // bin (scanning from the top) where the running count reaches need, on a
-// transposed histogram; 256 threads, one block scan.
-template <int NB>
+// transposed histogram; NT threads, one block scan.
+template <int NB, int NT = kTmThreads>
 __device__ int tm_find(const uint32_t* hist, int need, int* wsum, int* bc, int& above) {
-    constexpr int PER = NB / kTmThreads > 0 ? NB / kTmThreads : 1;
+    constexpr int PER = NB / NT > 0 ? NB / NT : 1;
     const int tid = threadIdx.x;
     uint32_t v[PER];
     int local = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        v[i] = tid * PER + i < NB ? hist[i * kTmThreads + tid] : 0u;
+        v[i] = tid * PER + i < NB ? hist[i * NT + tid] : 0u;
         local += (int)v[i];
     }
     int tot;
-    const int before = tm_scan(local, wsum, tot);
+    const int before = tm_scan<NT>(local, wsum, tot);
     if (before < need && before + local >= need) {
         int run = before;
 #pragma unroll
@@ -455,13 +460,14 @@ __global__ __launch_bounds__(kTmThreads) void k_topkm_collect(const float* __res
 // histogram, mark every selected index in an LDS bitmap of the row (or sort
 // them when the row is too long for the bitmap), write the row in ascending
 // index order, and leave the row's histograms and counters zeroed.
-__global__ __launch_bounds__(kTmThreads) void k_topkm_final(int64_t T, int64_t n_cols, const int64_t* __restrict__ pos,
+__global__ __launch_bounds__(kTfThreads) void k_topkm_final(int64_t T, int64_t n_cols, const int64_t* __restrict__ pos,
                                                             int m, int k, void* ws, int32_t* __restrict__ idx) {
+    constexpr int NT = kTfThreads;
     __shared__ uint32_t h[4096];
     __shared__ uint32_t bm[kBitmapWords];  // row bitmap, or the index list to sort
     __shared__ uint64_t cl[kCandLds];      // candidates
     __shared__ uint32_t tie[kTieLds];      // indices of keys equal to the threshold
-    __shared__ int wsum[kTmThreads / 64];
+    __shared__ int wsum[NT / 64];
     __shared__ int bc[4];
     __shared__ uint32_t lctr[3];
     const int tid = threadIdx.x;
@@ -475,22 +481,22 @@ __global__ __launch_bounds__(kTmThreads) void k_topkm_final(int64_t T, int64_t n
     const int n_up = (int)r.ctr[0];
     const int n_cand = (int)r.ctr[1];
     const int64_t nwords = (nv + 31) / 32;
-    const bool use_bm = nwords <= kBitmapWords;  // kBitmapWords is a multiple of 256
-    tm_load_hist(h, r.hist2);
-    // bitmap word w belongs to thread w / perw and sits at (w % perw) * 256 + w / perw
-    const uint32_t perw = (uint32_t)((nwords + kTmThreads - 1) / kTmThreads);
+    const bool use_bm = nwords <= kBitmapWords;  // kBitmapWords is a multiple of NT
+    tm_load_hist<NT>(h, r.hist2);
+    // bitmap word w belongs to thread w / perw and sits at (w % perw) * NT + w / perw
+    const uint32_t perw = (uint32_t)((nwords + NT - 1) / NT);
     if (use_bm)
-        for (uint32_t i = tid; i < perw * kTmThreads; i += kTmThreads) bm[i] = 0;
+        for (uint32_t i = tid; i < perw * NT; i += NT) bm[i] = 0;
     if (tid < 2) lctr[tid] = 0;
     __syncthreads();
     int above2;
     const int need = k - above1;
-    const uint32_t b2 = (uint32_t)tm_find<4096>(h, need, wsum, bc, above2);
+    const uint32_t b2 = (uint32_t)tm_find<4096, NT>(h, need, wsum, bc, above2);
     auto mark = [&](uint32_t j) {
         if (use_bm) {
             if (j < (uint64_t)nv) {
                 const uint32_t wd = j >> 5;
-                atomicOr(&bm[(wd % perw) * kTmThreads + wd / perw], 1u << (j & 31));
+                atomicOr(&bm[(wd % perw) * NT + wd / perw], 1u << (j & 31));
             }
         } else {
             const uint32_t o = atomicAdd(&lctr[1], 1u);
@@ -500,16 +506,16 @@ __global__ __launch_bounds__(kTmThreads) void k_topkm_final(int64_t T, int64_t n
     // candidates into LDS (batched loads), when they fit
     const bool cand_lds = n_cand <= kCandLds;
     if (cand_lds) {
-        for (int i0 = 0; i0 < n_cand; i0 += kTmThreads * 8) {
+        for (int i0 = 0; i0 < n_cand; i0 += NT * 8) {
             uint64_t v[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const int i = i0 + u * kTmThreads + tid;
+                const int i = i0 + u * NT + tid;
                 v[u] = i < n_cand ? r.cand[i] : 0;
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const int i = i0 + u * kTmThreads + tid;
+                const int i = i0 + u * NT + tid;
                 if (i < n_cand) cl[i] = v[u];
             }
         }
@@ -517,11 +523,11 @@ __global__ __launch_bounds__(kTmThreads) void k_topkm_final(int64_t T, int64_t n
     // keys above bin b1 (collected by the chunk pass), batched loads
     {
         const int nu = n_up < k ? n_up : k;
-        for (int a0 = 0; a0 < nu; a0 += kTmThreads * 8) {
+        for (int a0 = 0; a0 < nu; a0 += NT * 8) {
             int32_t v[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const int a = a0 + u * kTmThreads + tid;
+                const int a = a0 + u * NT + tid;
                 v[u] = a < nu ? r.sel[a] : -1;
             }
 #pragma unroll
@@ -529,22 +535,22 @@ __global__ __launch_bounds__(kTmThreads) void k_topkm_final(int64_t T, int64_t n
                 if (v[u] >= 0) mark((uint32_t)v[u]);
         }
     }
-    for (int i = tid; i < 256; i += kTmThreads) h[i] = 0;
+    for (int i = tid; i < 256; i += NT) h[i] = 0;
     __syncthreads();
     auto cand_at = [&](int i) -> uint64_t { return cand_lds ? cl[i] : r.cand[i]; };
     // candidates: mark those above b2, histogram the low 8 bits of those in b2
-    for (int i = tid; i < n_cand; i += kTmThreads) {
+    for (int i = tid; i < n_cand; i += NT) {
         const uint64_t c = cand_at(i);
         const uint32_t key = (uint32_t)(c >> 32), mid = (key >> 8) & 0xFFF;
         if (mid > b2) mark(~(uint32_t)c);
-        else if (mid == b2) atomicAdd(&h[tm_pos<256>(key & 0xFF)], 1u);
+        else if (mid == b2) atomicAdd(&h[tm_pos<256, NT>(key & 0xFF)], 1u);
     }
     __syncthreads();
     int above3;
-    const uint32_t b3 = (uint32_t)tm_find<256>(h, need - above2, wsum, bc, above3);
+    const uint32_t b3 = (uint32_t)tm_find<256, NT>(h, need - above2, wsum, bc, above3);
     const uint32_t thr = (b1 << 20) | (b2 << 8) | b3;
     const int need_eq = need - above2 - above3;  // >= 1 keys equal to thr, lowest indices first
-    for (int i = tid; i < n_cand; i += kTmThreads) {
+    for (int i = tid; i < n_cand; i += NT) {
         const uint64_t c = cand_at(i);
         const uint32_t key = (uint32_t)(c >> 32);
         if (((key >> 8) & 0xFFF) != b2) continue;
@@ -558,12 +564,12 @@ __global__ __launch_bounds__(kTmThreads) void k_topkm_final(int64_t T, int64_t n
         // few equal keys: list them, rank each by index, keep the need_eq lowest
         if (tid == 0) lctr[2] = 0;
         __syncthreads();
-        for (int i = tid; i < n_cand; i += kTmThreads) {
+        for (int i = tid; i < n_cand; i += NT) {
             const uint64_t c = cand_at(i);
             if ((uint32_t)(c >> 32) == thr) tie[atomicAdd(&lctr[2], 1u)] = ~(uint32_t)c;
         }
         __syncthreads();
-        for (int i = tid; i < n_eq; i += kTmThreads) {
+        for (int i = tid; i < n_eq; i += NT) {
             const uint32_t ji = tie[i];
             int rank = 0;
             for (int q = 0; q < n_eq; ++q) rank += tie[q] < ji ? 1 : 0;
@@ -577,24 +583,24 @@ __global__ __launch_bounds__(kTmThreads) void k_topkm_final(int64_t T, int64_t n
         uint32_t pre = 0, pm = 0;
         int nl = need_eq;
         for (int sh = 22; sh >= 0; sh -= 11) {
-            for (int i = tid; i < 2048; i += kTmThreads) h[i] = 0;
+            for (int i = tid; i < 2048; i += NT) h[i] = 0;
             __syncthreads();
-            for (int i = tid; i < n_cand; i += kTmThreads) {
+            for (int i = tid; i < n_cand; i += NT) {
                 const uint64_t c = cand_at(i);
                 if ((uint32_t)(c >> 32) != thr) continue;
                 const uint32_t jx = ~(uint32_t)c;
-                if ((jx & pm) == pre) atomicAdd(&h[tm_pos<2048>(2047 - ((jx >> sh) & 0x7FF))], 1u);  // smaller index, higher bin
+                if ((jx & pm) == pre) atomicAdd(&h[tm_pos<2048, NT>(2047 - ((jx >> sh) & 0x7FF))], 1u);  // smaller index, higher bin
             }
             __syncthreads();
             int ab;
-            const uint32_t bn = 2047u - (uint32_t)tm_find<2048>(h, nl, wsum, bc, ab);
+            const uint32_t bn = 2047u - (uint32_t)tm_find<2048, NT>(h, nl, wsum, bc, ab);
             nl -= ab;
             pre |= bn << sh;
             pm |= 0x7FFu << sh;
         }
         idx_lim = pre;
     }
-    for (int i = tid; i < n_cand; i += kTmThreads) {
+    for (int i = tid; i < n_cand; i += NT) {
         const uint64_t c = cand_at(i);
         if ((uint32_t)(c >> 32) == thr && ~(uint32_t)c <= idx_lim) mark(~(uint32_t)c);
     }
@@ -602,11 +608,11 @@ __global__ __launch_bounds__(kTmThreads) void k_topkm_final(int64_t T, int64_t n
     if (use_bm) {
         // thread t owns words t*perw .. t*perw+perw-1 (reads free of bank conflicts)
         int cnt = 0;
-        for (uint32_t i = 0; i < perw; ++i) cnt += __popc(bm[i * kTmThreads + tid]);
+        for (uint32_t i = 0; i < perw; ++i) cnt += __popc(bm[i * NT + tid]);
         int tot;
-        int o = tm_scan(cnt, wsum, tot);
+        int o = tm_scan<NT>(cnt, wsum, tot);
         for (uint32_t i = 0; i < perw; ++i) {
-            uint32_t b = bm[i * kTmThreads + tid];
+            uint32_t b = bm[i * NT + tid];
             const int64_t wi = (int64_t)tid * perw + i;
             while (b) {
                 const int bit = __builtin_ctz(b);
@@ -619,11 +625,11 @@ __global__ __launch_bounds__(kTmThreads) void k_topkm_final(int64_t T, int64_t n
         // bitonic sort of the k marked indices
         int np = 1;
         while (np < k) np <<= 1;
-        for (int i = k + tid; i < np; i += kTmThreads) bm[i] = 0xFFFFFFFFu;
+        for (int i = k + tid; i < np; i += NT) bm[i] = 0xFFFFFFFFu;
         __syncthreads();
         for (int size = 2; size <= np; size <<= 1)
             for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                for (int i = tid; i < np / 2; i += kTmThreads) {
+                for (int i = tid; i < np / 2; i += NT) {
                     const int lo = 2 * i - (i & (stride - 1));
                     const int hi = lo + stride;
                     const bool asc = (lo & size) == 0;
@@ -635,10 +641,10 @@ __global__ __launch_bounds__(kTmThreads) void k_topkm_final(int64_t T, int64_t n
                 }
                 __syncthreads();
             }
-        for (int a = tid; a < k; a += kTmThreads) out[a] = (int32_t)bm[a];
+        for (int a = tid; a < k; a += NT) out[a] = (int32_t)bm[a];
     }
     // ---- leave the row's histograms and counters zero for the next call ----
-    for (int i = tid; i < 4096; i += kTmThreads) {
+    for (int i = tid; i < 4096; i += NT) {
         r.hist[i] = 0;
         r.hist2[i] = 0;
     }
@@ -674,7 +680,7 @@ hipError_t launch_topk(const float* scores, int64_t T, int64_t n_cols, const int
                            pos, m, k, chunk, ws);
     hipLaunchKernelGGL(k_topkm_collect, dim3((unsigned)nchunk, (unsigned)T), dim3(kTmThreads), 0, st, scores, T, n_cols,
                        pos, m, k, chunk, ws, idx);
-    hipLaunchKernelGGL(k_topkm_final, dim3((unsigned)T), dim3(kTmThreads), 0, st, T, n_cols, pos, m, k, ws, idx);
+    hipLaunchKernelGGL(k_topkm_final, dim3((unsigned)T), dim3(kTfThreads), 0, st, T, n_cols, pos, m, k, ws, idx);
     return hipGetLastError();
 }
 

@@ -2,8 +2,9 @@
 
 One step = the CSA decode hot path for a batch of 4 sequences, each with a
 1,048,576-token context (262,144 compressed entries at m=4):
-    csa_index_scores (MXFP4 indexer over every entry; it also builds the
-                      first radix histogram of the selection)
+    csa_index_scores (MXFP4 indexer over every entry; it also writes the
+                      selection's row summary: the largest score of every
+                      128-column group)
  -> csa_topk (k = 1024)
  -> csa_sparse_mqa (64 query heads over the 1024 selected entries + a
     128-token window, d = 512).
@@ -110,7 +111,7 @@ class DecodeSet:
         import compressed_sparse_long_compress_amd as csa
 
         wl = self.wl
-        csa.csa_topk(self.scores, self.pos, wl["m"], wl["k"], out=self.idx, ws=self.tws, hist_ready=True)
+        csa.csa_topk(self.scores, self.pos, wl["m"], wl["k"], out=self.idx, ws=self.tws, prepared=True)
 
     def attend(self, r):
         import compressed_sparse_long_compress_amd as csa

@@ -40,7 +40,7 @@ _lib.csa_index_scores.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _Id
 _lib.csa_topk_workspace.restype = _sz
 _lib.csa_topk_workspace.argtypes = [_i64, _i64, _i32]
 _lib.csa_topk.argtypes = [_vp, _i64, _i64, _vp, _i32, _i32, _vp, _vp, _sz, ctypes.c_uint32, _vp]
-CSA_TOPK_HIST_READY = 1
+CSA_TOPK_PREPARED = 1
 _lib.csa_mqa_workspace.restype = _sz
 _lib.csa_mqa_workspace.argtypes = [_i64, _i32, _i32, _i64]
 _lib.csa_sparse_mqa.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _i32, _Kv, _Kv, _i32, _f32, _f32, _vp,
@@ -151,8 +151,9 @@ def csa_compress(kv, logits, tok0, m, seq, out, rope_base=10000.0):
 def csa_index_scores(q, q_scale, w, seq, pos, keys, m, n_cols, out=None, topk_ws=None):
     """MXFP4 indexer scores: q uint8 [T, h_i, d_i/2], q_scale uint8 [T, h_i, d_i/32], w fp32 [T, h_i] -> fp32 [T, n_cols].
 
-    topk_ws: the (zero-filled) workspace of the csa_topk call that follows; the
-    indexer then also builds its histogram, and that call passes hist_ready=True."""
+    topk_ws: the workspace of the csa_topk call that follows; the indexer then
+    also writes the selection's row summary into it, and that call passes
+    prepared=True."""
     _need(q, "q", torch.uint8, 3)
     _need(q_scale, "q_scale", torch.uint8, 3)
     _need(w, "w", torch.float32, 2)
@@ -185,7 +186,7 @@ def topk_workspace(T, n_cols, k, device="cuda"):
     return torch.zeros(max(need, 1), dtype=torch.uint8, device=device)
 
 
-def csa_topk(scores, pos, m, k, out=None, ws=None, hist_ready=False):
+def csa_topk(scores, pos, m, k, out=None, ws=None, prepared=False):
     """Top-k per row (score desc, index asc) in ascending index order, -1 padded -> int32 [T, k].
 
     ws: a zero-filled uint8 workspace of csa_topk_workspace(T, n_cols, k) bytes (allocated when None)."""
@@ -198,7 +199,7 @@ def csa_topk(scores, pos, m, k, out=None, ws=None, hist_ready=False):
     if ws is None:
         ws = topk_workspace(T, n_cols, k, scores.device)
     _check(_lib.csa_topk(_ptr(scores), T, n_cols, _ptr(pos), int(m), int(k), _ptr(out), _ptr(ws), ws.numel(),
-                         CSA_TOPK_HIST_READY if hist_ready else 0, _stream()))
+                         CSA_TOPK_PREPARED if prepared else 0, _stream()))
     return out
 
 

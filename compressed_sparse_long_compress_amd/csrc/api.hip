@@ -113,16 +113,16 @@ int csa_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, c
     if (keys.cap < n_cols) return fail(CSA_EINVAL, "%s: n_cols (%lld) > keys.cap (%lld)", fn, (long long)n_cols,
                                        (long long)keys.cap);
     if (!aligned16(q) || !aligned16(keys.data)) return fail(CSA_EINVAL, "%s: q and keys.data must be 16-byte aligned", fn);
-    void* hist = nullptr;
-    if (topk_ws && csa::topk_uses_hist(T, n_cols)) {
-        // the histogram lives in the first T row blocks of the top-k workspace
+    uint32_t* gmax = nullptr;
+    if (topk_ws && csa::topk_uses_summary(T, n_cols)) {
+        // the row summaries live in the top-k workspace, after its counters
         if (topk_ws_bytes < csa::topk_workspace_bytes(T, n_cols, 1))
-            return fail(CSA_EWORKSPACE, "%s: top-k workspace too small for the histogram", fn);
+            return fail(CSA_EWORKSPACE, "%s: top-k workspace too small for the row summaries", fn);
         if (((uintptr_t)topk_ws & 255u) != 0) return fail(CSA_EINVAL, "%s: workspace must be 256-byte aligned", fn);
-        hist = topk_ws;
+        gmax = (uint32_t*)((char*)topk_ws + csa::topk_ws_gmax_off());
     }
     hipError_t e = csa::launch_index_scores(q, q_scale, w, seq, pos, T, h_i, d_i, keys.data, keys.scale, keys.cap, m,
-                                            n_cols, scores, hist, (hipStream_t)stream);
+                                            n_cols, scores, gmax, (hipStream_t)stream);
     return hip_status(e, fn);
 }
 
@@ -141,8 +141,8 @@ int csa_topk(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos,
     if (ws_bytes < need || (need > 0 && !ws))
         return fail(CSA_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
     if (need > 0 && ((uintptr_t)ws & 255u) != 0) return fail(CSA_EINVAL, "%s: workspace must be 256-byte aligned", fn);
-    if (flags & ~(uint32_t)CSA_TOPK_HIST_READY) return fail(CSA_EINVAL, "%s: unknown flags 0x%x", fn, flags);
-    const bool ready = (flags & CSA_TOPK_HIST_READY) && csa::topk_uses_hist(T, n_cols);
+    if (flags & ~(uint32_t)CSA_TOPK_PREPARED) return fail(CSA_EINVAL, "%s: unknown flags 0x%x", fn, flags);
+    const bool ready = (flags & CSA_TOPK_PREPARED) && csa::topk_uses_summary(T, n_cols);
     hipError_t e = csa::launch_topk(scores, T, n_cols, pos, m, k, idx, ws, ready, (hipStream_t)stream);
     return hip_status(e, fn);
 }

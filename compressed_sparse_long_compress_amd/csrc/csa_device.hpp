@@ -38,6 +38,19 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts
+// (1, 2, 4, 8 within each 16-lane row; shifted-in lanes read 0) and the
+// row broadcasts of lanes 15 and 31 into the following rows.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+    return x;
+}
+
 // Max / sum over the four lanes l, l^16, l^32, l^48 (the same position in each
 // 16-lane row) with the gfx950 row-swap permutes; every one of the four lanes
 // gets the bitwise-identical result (each step adds or maxes one pair).

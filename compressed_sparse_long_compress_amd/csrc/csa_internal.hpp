@@ -12,28 +12,35 @@ struct RopeTab {
 };
 RopeTab rope_table(double base);
 
-// Top-k workspace row block for few-long-row batches: 4096 histogram bins of
-// the top 12 key bits, 4096 bins of the next 12 bits of the candidates, then
-// 16 counters.  Must start zero-filled.
-constexpr size_t kTopkRowBlock = 2 * 4096 * 4 + 64;
+// Top-k workspace of the few-long-rows path (T < kTopkMaxRows rows):
+// kTopkMaxRows x 16 counters (must start zero-filled; left zero-filled),
+// then the row summaries (per kTopkGroup-column group the largest order key
+// of its visible columns), then T x n_cols candidates.
+constexpr int kTopkMaxRows = 128;
+constexpr int kTopkGroup = 128;
+__host__ __device__ inline int64_t topk_groups(int64_t n_cols) { return (n_cols + kTopkGroup - 1) / kTopkGroup; }
+__host__ __device__ inline size_t topk_ws_gmax_off() { return (size_t)kTopkMaxRows * 64; }
+__host__ __device__ inline size_t topk_ws_cand_off(int64_t T, int64_t n_cols) {
+    return (topk_ws_gmax_off() + (size_t)T * topk_groups(n_cols) * 4 + 255) & ~(size_t)255;
+}
 
 hipError_t launch_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t n_tok, int m, int d,
                            const RopeTab& rt, int64_t row0, int64_t cap, uint8_t* nope, uint16_t* rope, float* scale,
                            hipStream_t st);
 
-// hist_ws != nullptr: also add each row's top-12-bit key histogram into the
-// top-k workspace (row blocks of kTmRowBlock bytes, histogram first)
+// gmax != nullptr: also write each row's summary (the largest order key of
+// the visible columns of every kTopkGroup-column group) to gmax[T][groups]
 hipError_t launch_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
                                const int64_t* pos, int64_t T, int h_i, int d_i, const uint8_t* kdata,
                                const uint8_t* kscale, int64_t kcap, int m, int64_t n_cols, float* scores,
-                               void* hist_ws, hipStream_t st);
+                               uint32_t* gmax, hipStream_t st);
 
 size_t topk_workspace_bytes(int64_t T, int64_t n_cols, int k);
-// true when the top-k for this shape uses the workspace histogram (few long rows)
-bool topk_uses_hist(int64_t T, int64_t n_cols);
-// hist_done: the row histograms were already accumulated by the indexer
+// true when the top-k for this shape uses the row summaries (few long rows)
+bool topk_uses_summary(int64_t T, int64_t n_cols);
+// prepared: the row summaries were already written by the indexer
 hipError_t launch_topk(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos, int m, int k, int32_t* idx,
-                       void* ws, bool hist_done, hipStream_t st);
+                       void* ws, bool prepared, hipStream_t st);
 
 struct KvView {
     const uint8_t* nope;

@@ -33,17 +33,13 @@ __global__ __launch_bounds__(256) void k_index_rows(const uint8_t* __restrict__ 
                                                     const uint8_t* __restrict__ kdata,
                                                     const uint8_t* __restrict__ kscale, int64_t kcap, int m,
                                                     int64_t n_cols, int64_t chunk, float* __restrict__ scores,
-                                                    char* __restrict__ hist_ws) {
+                                                    uint32_t* __restrict__ gmax) {
     constexpr int KB = DI / 2;   // bytes per key
     constexpr int NB = DI / 32;  // scale blocks per key
-    __shared__ uint32_t hh[4096];  // top-12-bit key histogram of this chunk (when hist_ws)
+    static_assert(16 * U == kTopkGroup, "one wave step = one summary group");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t t = blockIdx.y;
     const int r = lane & 15, g = lane >> 4;
-    if (hist_ws) {
-        for (int i = threadIdx.x; i < 4096; i += 256) hh[i] = 0;
-        __syncthreads();
-    }
 
     v8i a = {0, 0, 0, 0, 0, 0, 0, 0};
     int sa = 127;
@@ -65,6 +61,7 @@ __global__ __launch_bounds__(256) void k_index_rows(const uint8_t* __restrict__ 
     float* out = scores + t * n_cols;
 
     for (int64_t j0 = c0 + (int64_t)wave * 16 * U; j0 < c1; j0 += 4 * 16 * U) {
+        uint32_t gm = 0;  // largest order key of the visible scores of this group (lanes < 16)
         v4i bk[U];
         int sb[U];
 #pragma unroll
@@ -92,15 +89,14 @@ __global__ __launch_bounds__(256) void k_index_rows(const uint8_t* __restrict__ 
             const int64_t j = j0 + u * 16 + lane;
             if (lane < 16 && j < c1) {
                 out[j] = j < nv ? p : -INFINITY;
-                if (hist_ws && j < nv) atomicAdd(&hh[f32_order_key(p) >> 20], 1u);
+                if (j < nv) gm = max(gm, f32_order_key(p));
             }
         }
-    }
-    if (hist_ws) {
-        __syncthreads();
-        uint32_t* gh = (uint32_t*)(hist_ws + (size_t)t * kTopkRowBlock);
-        for (int i = threadIdx.x; i < 4096; i += 256)
-            if (hh[i]) atomicAdd(&gh[i], hh[i]);
+        if (gmax) {
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) gm = max(gm, (uint32_t)__shfl_xor((int)gm, o));
+            if (lane == 0) gmax[t * topk_groups(n_cols) + j0 / kTopkGroup] = gm;
+        }
     }
 }
 
@@ -267,9 +263,9 @@ __global__ __launch_bounds__(256) void k_index_gemm(const uint8_t* __restrict__ 
 hipError_t launch_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
                                const int64_t* pos, int64_t T, int h_i, int d_i, const uint8_t* kdata,
                                const uint8_t* kscale, int64_t kcap, int m, int64_t n_cols, float* scores,
-                               void* hist_ws, hipStream_t st) {
+                               uint32_t* gmax, hipStream_t st) {
     if (T == 0 || n_cols == 0) return hipSuccess;
-    if (T <= 64 || hist_ws) {
+    if (T <= 64 || gmax) {
         // aim for >= 1024 workgroups; each wave handles 128 keys per step
         int64_t chunk = (n_cols * T + 1023) / 1024;
         chunk = ((chunk + 511) / 512) * 512;
@@ -278,10 +274,10 @@ hipError_t launch_index_scores(const uint8_t* q, const uint8_t* q_scale, const f
         dim3 grid((unsigned)((n_cols + chunk - 1) / chunk), (unsigned)T), block(256);
         if (d_i == 128)
             hipLaunchKernelGGL((k_index_rows<128, 8>), grid, block, 0, st, q, q_scale, w, seq, pos, h_i, kdata, kscale,
-                               kcap, m, n_cols, chunk, scores, (char*)hist_ws);
+                               kcap, m, n_cols, chunk, scores, gmax);
         else
             hipLaunchKernelGGL((k_index_rows<64, 8>), grid, block, 0, st, q, q_scale, w, seq, pos, h_i, kdata, kscale,
-                               kcap, m, n_cols, chunk, scores, (char*)hist_ws);
+                               kcap, m, n_cols, chunk, scores, gmax);
         return hipGetLastError();
     }
     const int qwg = 4 * 4 * (32 / h_i);  // queries per workgroup

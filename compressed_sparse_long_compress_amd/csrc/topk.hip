@@ -18,12 +18,7 @@ constexpr int kTopkCache = 36608;  // keys cached in LDS (143 KB)
 // exclusive prefix sum over the block; returns the block total in `total`
 __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const int x = wave_incl_scan(v);
     if (lane == 63) wsum[wave] = x;
     __syncthreads();
     int off = 0, tot = 0;
@@ -206,62 +201,49 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_row(const float* __restri
 
 // ---------------------------------------------------------------------------
 // Few long rows (decode): the row is split over many workgroups.
-//   k_topkm_hist     per chunk, LDS histogram of the top 12 key bits, added
-//                    to the row's global histogram (integer atomics); the
-//                    indexer kernel can do the same while it writes scores
-//   k_topkm_collect  per chunk, every workgroup reads the row histogram,
-//                    finds the bin b1 holding the k-th largest key, appends
-//                    the indices of keys above b1 and the (key, index) pairs
-//                    inside b1 (one slot reservation per workgroup)
-//   k_topkm_final    one workgroup per row selects the remaining
-//                    need = k - #above candidates (radix select on the low
-//                    20 key bits, ties to the lower index), marks all k
-//                    indices in an LDS bitmap of the row and writes them in
-//                    ascending order; it then zeroes the row's histogram and
-//                    counters, so the workspace is left as it was found.
-// The hand-over between the two passes is a kernel boundary: a per-workgroup
-// agent-scope fence would write back the whole L2 (holding the freshly
-// written scores) once per workgroup.
-// Workspace: zero-filled before first use; every call leaves it zero-filled.
-// Layout: 128 row blocks of [4096 histogram bins + 16 counters] (the only
-// part that must start at zero), then T x k selected indices, then
+//   row summary      per kTopkGroup-column group, the largest order key of
+//                    its visible columns (0 for a group with none), written
+//                    by the indexer kernel next to the scores, or else by
+//                    k_topkm_gmax
+//   k_topkm_collect  per chunk.  tau = lower edge of the 12-bit key prefix
+//                    holding the k-th largest group maximum (0 when the row
+//                    has fewer than k groups).  The group maxima are keys of
+//                    distinct columns, so the row's k-th largest key is
+//                    >= tau and every column of the top-k (ties included)
+//                    has key >= tau.  Appends (key, ~index) of the chunk's
+//                    visible columns with key >= tau, one slot reservation
+//                    per workgroup.
+//   k_topkm_final    one workgroup per row: exact radix select over the
+//                    candidates (12 + 12 + 8 key bits, equal keys to the
+//                    lower index), marks the k winners in an LDS bitmap of
+//                    the row, writes them in ascending order and resets the
+//                    row's counters.
+// The hand-overs are kernel boundaries: a per-workgroup agent-scope fence
+// would write back the whole L2 (holding the freshly written scores).
+// Workspace (topk_ws_* in csa_internal.hpp): 128 rows x 16 counters
+// (zero-filled before first use, left zero-filled), the row summaries, then
 // T x n_cols candidates.
 // ---------------------------------------------------------------------------
 constexpr int kTmThreads = 256;
-constexpr int kTfThreads = 1024;  // the per-row finaliser
-constexpr int kTmE = 8;  // consecutive columns per thread in the collect pass
+constexpr int kTfThreads = 1024;     // the per-row finaliser
+constexpr int kTmE = 8;              // consecutive columns per thread in the collect pass
 constexpr int kBitmapWords = 16384;  // row bitmap of the finaliser: rows up to 524,288 columns
-constexpr int kCandLds = 4096;       // candidates the finaliser stages in LDS
+constexpr int kCandLds = 8192;       // candidates the finaliser stages in LDS
 constexpr int kTieLds = 256;         // equal-key sets up to this size are ranked directly
-constexpr size_t kTmRowBlock = kTopkRowBlock;
+static_assert(kTmThreads * kTmE % kTopkGroup == 0, "summary groups inside one collect step");
 
 struct TmRow {
-    uint32_t* hist;   // [4096] top 12 key bits of the row
-    uint32_t* hist2;  // [4096] bits 19..8 of the candidates (keys in bin b1)
-    uint32_t* ctr;    // [0] indices above b1, [1] candidates, [4] b1, [5] #keys above b1
-    int32_t* sel;    // [k]
+    uint32_t* ctr;   // [0] candidates
+    uint32_t* gmax;  // [topk_groups(n_cols)] group maxima
     uint64_t* cand;  // [n_cols] (key << 32 | ~index)
 };
 
-// The histogram / counter rows occupy a fixed region sized for the most rows
-// the multi-workgroup path accepts, so the selected-index and candidate
-// regions of any call never overlap a row block of a later call.
-constexpr int kTmMaxRows = 128;
-__host__ __device__ __forceinline__ size_t tm_sel_off(int64_t) {
-    return ((size_t)kTmMaxRows * kTmRowBlock + 255) & ~(size_t)255;
-}
-__host__ __device__ __forceinline__ size_t tm_cand_off(int64_t T, int k) {
-    return (tm_sel_off(T) + (size_t)T * k * 4 + 255) & ~(size_t)255;
-}
-
-__device__ __forceinline__ TmRow tm_row(void* ws, int64_t T, int64_t t, int64_t n_cols, int k) {
+__device__ __forceinline__ TmRow tm_row(void* ws, int64_t T, int64_t t, int64_t n_cols) {
     char* b = (char*)ws;
     TmRow r;
-    r.hist = (uint32_t*)(b + (size_t)t * kTmRowBlock);
-    r.hist2 = r.hist + 4096;
-    r.ctr = r.hist2 + 4096;
-    r.sel = (int32_t*)(b + tm_sel_off(T)) + t * (int64_t)k;
-    r.cand = (uint64_t*)(b + tm_cand_off(T, k)) + t * n_cols;
+    r.ctr = (uint32_t*)(b + (size_t)t * 64);
+    r.gmax = (uint32_t*)(b + topk_ws_gmax_off()) + t * topk_groups(n_cols);
+    r.cand = (uint64_t*)(b + topk_ws_cand_off(T, n_cols)) + t * n_cols;
     return r;
 }
 
@@ -272,34 +254,24 @@ __device__ __forceinline__ int64_t row_visible(const int64_t* pos, int64_t t, in
     return nv;
 }
 
-__global__ __launch_bounds__(kTmThreads) void k_topkm_hist(const float* __restrict__ scores, int64_t T, int64_t n_cols,
-                                                           const int64_t* __restrict__ pos, int m, int k, int64_t chunk,
-                                                           void* ws) {
-    __shared__ uint32_t h[4096];
+// Row summaries from the scores (when the indexer did not write them): 16
+// threads x 8 consecutive columns per group.
+__global__ __launch_bounds__(kTmThreads) void k_topkm_gmax(const float* __restrict__ scores, int64_t T,
+                                                           int64_t n_cols, const int64_t* __restrict__ pos, int m,
+                                                           int k, void* ws) {
+    const int tid = threadIdx.x;
     const int64_t t = blockIdx.y;
     const int64_t nv = row_visible(pos, t, m, n_cols);
     if (nv <= k) return;
-    const int64_t c0 = (int64_t)blockIdx.x * chunk;
-    if (c0 >= nv) return;
-    const int64_t c1 = c0 + chunk < nv ? c0 + chunk : nv;
-    for (int i = threadIdx.x; i < 4096; i += kTmThreads) h[i] = 0;
-    __syncthreads();
     const float* row = scores + t * n_cols;
-    for (int64_t j = c0 + threadIdx.x * 4; j < c1; j += kTmThreads * 4) {
-        if (j + 4 <= c1 && (((uintptr_t)(row + j) & 15) == 0)) {
-            float4 v = *(const float4*)(row + j);
-            atomicAdd(&h[f32_order_key(v.x) >> 20], 1u);
-            atomicAdd(&h[f32_order_key(v.y) >> 20], 1u);
-            atomicAdd(&h[f32_order_key(v.z) >> 20], 1u);
-            atomicAdd(&h[f32_order_key(v.w) >> 20], 1u);
-        } else {
-            for (int64_t jj = j; jj < c1 && jj < j + 4; ++jj) atomicAdd(&h[f32_order_key(row[jj]) >> 20], 1u);
-        }
-    }
-    __syncthreads();
-    TmRow r = tm_row(ws, T, t, n_cols, k);
-    for (int i = threadIdx.x; i < 4096; i += kTmThreads)
-        if (h[i]) atomicAdd(&r.hist[i], h[i]);
+    const int64_t j0 = (int64_t)blockIdx.x * (kTmThreads * 8) + tid * 8;
+    uint32_t g = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        if (j0 + e < nv) g = max(g, f32_order_key(row[j0 + e]));
+#pragma unroll
+    for (int o = 1; o < kTopkGroup / 8; o <<= 1) g = max(g, (uint32_t)__shfl_xor((int)g, o));
+    if ((tid & (kTopkGroup / 8 - 1)) == 0 && j0 < n_cols) tm_row(ws, T, t, n_cols).gmax[j0 / kTopkGroup] = g;
 }
 
 // Histograms handed to tm_find are stored "transposed": with PER = NB/256
@@ -334,12 +306,7 @@ __device__ __forceinline__ void tm_load_hist(uint32_t* dst, const uint32_t* src)
 template <int NT = kTmThreads>
 __device__ __forceinline__ int tm_scan(int v, int* wsum, int& total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const int x = wave_incl_scan(v);
     if (lane == 63) wsum[wave] = x;
     __syncthreads();
     int off = 0, tot = 0;
@@ -397,6 +364,27 @@ __global__ __launch_bounds__(kTmThreads) void k_topkm_collect(const float* __res
     __shared__ int bc[4];
     const int tid = threadIdx.x;
     const int64_t t = blockIdx.y;
+    TmRow r = tm_row(ws, T, t, n_cols);
+    // the row's group maxima (groups without visible columns hold 0) and this workgroup's first
+    // scores are requested before anything that depends on pos, and the histogram is cleared
+    // while they are in flight
+    constexpr int GPT = 16;  // group maxima per thread held in registers (rows up to 524,288 columns)
+    const int ng = (int)topk_groups(n_cols);
+    uint32_t gv[GPT];
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+        const int gi = i * kTmThreads + tid;
+        gv[i] = gi < ng ? r.gmax[gi] : 0u;
+    }
+    const int64_t c0 = (int64_t)blockIdx.x * chunk;
+    const float* row = scores + t * n_cols;
+    float pre[kTmE];
+    {
+        const int64_t j0 = c0 + (int64_t)tid * kTmE;
+#pragma unroll
+        for (int e = 0; e < kTmE; ++e) pre[e] = j0 + e < n_cols ? row[j0 + e] : 0.f;
+    }
+    for (int i = tid; i < 4096; i += kTmThreads) h[i] = 0;
     const int64_t nv = row_visible(pos, t, m, n_cols);
     int32_t* out = idx + t * (int64_t)k;
     if (nv <= k) {
@@ -404,62 +392,50 @@ __global__ __launch_bounds__(kTmThreads) void k_topkm_collect(const float* __res
             for (int a = tid; a < k; a += kTmThreads) out[a] = a < nv ? a : -1;
         return;
     }
-    TmRow r = tm_row(ws, T, t, n_cols, k);
-    tm_load_hist(h, r.hist);
-    __syncthreads();
-    int above1;
-    const uint32_t b1 = (uint32_t)tm_find<4096>(h, k, wsum, bc, above1);
-
-    // this chunk: E consecutive columns per thread, one slot reservation per workgroup
-    const int64_t c0 = (int64_t)blockIdx.x * chunk;
     const int64_t c1 = c0 + chunk < nv ? c0 + chunk : nv;
-    const float* row = scores + t * n_cols;
+
+    // ---- tau: the lower edge of the 12-bit key prefix holding the k-th largest group maximum
+    //      (0 when the row has fewer than k groups) ----
+    uint32_t tau = 0;
+    if (ng >= k) {
+        const bool more = ng > GPT * kTmThreads;  // longer rows re-read the rest from global memory
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < GPT; ++i)
+            if (i * kTmThreads + tid < ng) atomicAdd(&h[tm_pos<4096>(gv[i] >> 20)], 1u);
+        if (more)
+            for (int gi = GPT * kTmThreads + tid; gi < ng; gi += kTmThreads) atomicAdd(&h[tm_pos<4096>(r.gmax[gi] >> 20)], 1u);
+        __syncthreads();
+        int ab1;
+        const uint32_t g1 = (uint32_t)tm_find<4096>(h, k, wsum, bc, ab1);
+        tau = g1 << 20;
+    }
+
+    // ---- candidates of this chunk: E consecutive columns per thread, one slot reservation ----
     for (int64_t jb = c0; jb < c1; jb += (int64_t)kTmThreads * kTmE) {
         const int64_t j0 = jb + (int64_t)tid * kTmE;
         uint32_t key[kTmE];
-        int n_up = 0, n_eq = 0;
+        int n_c = 0;
 #pragma unroll
         for (int e = 0; e < kTmE; ++e) {
             const int64_t j = j0 + e;
-            key[e] = j < c1 ? f32_order_key(row[j]) : 0u;
-            n_up += (j < c1 && (key[e] >> 20) > b1) ? 1 : 0;
-            n_eq += (j < c1 && (key[e] >> 20) == b1) ? 1 : 0;
+            key[e] = j < c1 ? f32_order_key(jb == c0 ? pre[e] : row[j]) : 0u;
+            n_c += (j < c1 && key[e] >= tau) ? 1 : 0;
         }
         int tot;
-        const int pre = tm_scan(n_up | (n_eq << 16), wsum, tot);  // both counts < 2^16
-        if (tid == 0) {
-            const uint32_t tu = (uint32_t)tot & 0xFFFFu, te = (uint32_t)tot >> 16;
-            bc[2] = tu ? (int)atomicAdd(&r.ctr[0], tu) : 0;
-            bc[3] = te ? (int)atomicAdd(&r.ctr[1], te) : 0;
-        }
+        const int before = tm_scan(n_c, wsum, tot);
+        if (tid == 0) bc[2] = tot ? (int)atomicAdd(&r.ctr[0], (uint32_t)tot) : 0;
         __syncthreads();
-        uint32_t su = (uint32_t)bc[2] + (uint32_t)(pre & 0xFFFF);
-        uint32_t se = (uint32_t)bc[3] + (uint32_t)(pre >> 16);
+        uint32_t sc = (uint32_t)bc[2] + (uint32_t)before;
         __syncthreads();
 #pragma unroll
         for (int e = 0; e < kTmE; ++e) {
             const int64_t j = j0 + e;
-            if (j >= c1) continue;
-            const uint32_t bin = key[e] >> 20;
-            if (bin > b1) {
-                if (su < (uint32_t)k) r.sel[su] = (int32_t)j;
-                ++su;
-            } else if (bin == b1) {
-                r.cand[se++] = ((uint64_t)key[e] << 32) | (uint32_t)~(uint32_t)j;
-                atomicAdd(&r.hist2[(key[e] >> 8) & 0xFFF], 1u);
-            }
+            if (j < c1 && key[e] >= tau) r.cand[sc++] = ((uint64_t)key[e] << 32) | (uint32_t)~(uint32_t)j;
         }
-    }
-    if (blockIdx.x == 0 && tid == 0) {
-        r.ctr[4] = b1;
-        r.ctr[5] = (uint32_t)above1;
     }
 }
 
-// One workgroup per row: resolve the exact threshold from the candidate
-// histogram, mark every selected index in an LDS bitmap of the row (or sort
-// them when the row is too long for the bitmap), write the row in ascending
-// index order, and leave the row's histograms and counters zeroed.
 __global__ __launch_bounds__(kTfThreads) void k_topkm_final(int64_t T, int64_t n_cols, const int64_t* __restrict__ pos,
                                                             int m, int k, void* ws, int32_t* __restrict__ idx) {
     constexpr int NT = kTfThreads;
@@ -475,23 +451,16 @@ __global__ __launch_bounds__(kTfThreads) void k_topkm_final(int64_t T, int64_t n
     const int64_t nv = row_visible(pos, t, m, n_cols);
     int32_t* out = idx + t * (int64_t)k;
     if (nv <= k) return;  // written by the collect pass
-    TmRow r = tm_row(ws, T, t, n_cols, k);
-    const uint32_t b1 = r.ctr[4];
-    const int above1 = (int)r.ctr[5];
-    const int n_up = (int)r.ctr[0];
-    const int n_cand = (int)r.ctr[1];
+    TmRow r = tm_row(ws, T, t, n_cols);
+    const int n_cand = (int)r.ctr[0];
     const int64_t nwords = (nv + 31) / 32;
     const bool use_bm = nwords <= kBitmapWords;  // kBitmapWords is a multiple of NT
-    tm_load_hist<NT>(h, r.hist2);
     // bitmap word w belongs to thread w / perw and sits at (w % perw) * NT + w / perw
     const uint32_t perw = (uint32_t)((nwords + NT - 1) / NT);
     if (use_bm)
         for (uint32_t i = tid; i < perw * NT; i += NT) bm[i] = 0;
     if (tid < 2) lctr[tid] = 0;
-    __syncthreads();
-    int above2;
-    const int need = k - above1;
-    const uint32_t b2 = (uint32_t)tm_find<4096, NT>(h, need, wsum, bc, above2);
+    for (int i = tid; i < 4096; i += NT) h[i] = 0;
     auto mark = [&](uint32_t j) {
         if (use_bm) {
             if (j < (uint64_t)nv) {
@@ -506,54 +475,52 @@ __global__ __launch_bounds__(kTfThreads) void k_topkm_final(int64_t T, int64_t n
     // candidates into LDS (batched loads), when they fit
     const bool cand_lds = n_cand <= kCandLds;
     if (cand_lds) {
-        for (int i0 = 0; i0 < n_cand; i0 += NT * 8) {
-            uint64_t v[8];
+        for (int i0 = 0; i0 < n_cand; i0 += NT * 4) {
+            uint64_t v[4];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < 4; ++u) {
                 const int i = i0 + u * NT + tid;
                 v[u] = i < n_cand ? r.cand[i] : 0;
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < 4; ++u) {
                 const int i = i0 + u * NT + tid;
                 if (i < n_cand) cl[i] = v[u];
             }
         }
     }
-    // keys above bin b1 (collected by the chunk pass), batched loads
-    {
-        const int nu = n_up < k ? n_up : k;
-        for (int a0 = 0; a0 < nu; a0 += NT * 8) {
-            int32_t v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int a = a0 + u * NT + tid;
-                v[u] = a < nu ? r.sel[a] : -1;
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (v[u] >= 0) mark((uint32_t)v[u]);
-        }
-    }
-    for (int i = tid; i < 256; i += NT) h[i] = 0;
     __syncthreads();
     auto cand_at = [&](int i) -> uint64_t { return cand_lds ? cl[i] : r.cand[i]; };
-    // candidates: mark those above b2, histogram the low 8 bits of those in b2
+    // radix select of the k-th largest candidate key: 12, 12, 8 bits
+    for (int i = tid; i < n_cand; i += NT) atomicAdd(&h[tm_pos<4096, NT>((uint32_t)(cand_at(i) >> 52))], 1u);
+    __syncthreads();
+    int above1;
+    const uint32_t b1 = (uint32_t)tm_find<4096, NT>(h, k, wsum, bc, above1);
+    for (int i = tid; i < 4096; i += NT) h[i] = 0;
+    __syncthreads();
     for (int i = tid; i < n_cand; i += NT) {
-        const uint64_t c = cand_at(i);
-        const uint32_t key = (uint32_t)(c >> 32), mid = (key >> 8) & 0xFFF;
-        if (mid > b2) mark(~(uint32_t)c);
-        else if (mid == b2) atomicAdd(&h[tm_pos<256, NT>(key & 0xFF)], 1u);
+        const uint32_t key = (uint32_t)(cand_at(i) >> 32);
+        if ((key >> 20) == b1) atomicAdd(&h[tm_pos<4096, NT>((key >> 8) & 0xFFFu)], 1u);
+    }
+    __syncthreads();
+    int above2;
+    const int need = k - above1;
+    const uint32_t b2 = (uint32_t)tm_find<4096, NT>(h, need, wsum, bc, above2);
+    for (int i = tid; i < 256; i += NT) h[i] = 0;
+    __syncthreads();
+    const uint32_t p2 = (b1 << 12) | b2;
+    for (int i = tid; i < n_cand; i += NT) {
+        const uint32_t key = (uint32_t)(cand_at(i) >> 32);
+        if ((key >> 8) == p2) atomicAdd(&h[tm_pos<256, NT>(key & 0xFFu)], 1u);
     }
     __syncthreads();
     int above3;
     const uint32_t b3 = (uint32_t)tm_find<256, NT>(h, need - above2, wsum, bc, above3);
-    const uint32_t thr = (b1 << 20) | (b2 << 8) | b3;
+    const uint32_t thr = (p2 << 8) | b3;
     const int need_eq = need - above2 - above3;  // >= 1 keys equal to thr, lowest indices first
     for (int i = tid; i < n_cand; i += NT) {
         const uint64_t c = cand_at(i);
         const uint32_t key = (uint32_t)(c >> 32);
-        if (((key >> 8) & 0xFFF) != b2) continue;
         if (key > thr) mark(~(uint32_t)c);
         else if (key == thr) atomicAdd(&lctr[0], 1u);
     }
@@ -643,19 +610,15 @@ __global__ __launch_bounds__(kTfThreads) void k_topkm_final(int64_t T, int64_t n
             }
         for (int a = tid; a < k; a += NT) out[a] = (int32_t)bm[a];
     }
-    // ---- leave the row's histograms and counters zero for the next call ----
-    for (int i = tid; i < 4096; i += NT) {
-        r.hist[i] = 0;
-        r.hist2[i] = 0;
-    }
+    // ---- leave the row's counters zero for the next call ----
     if (tid < 16) r.ctr[tid] = 0;
 }
 
-static bool topk_multi(int64_t T, int64_t n_cols) { return T < kTmMaxRows && n_cols > 4096; }
+static bool topk_multi(int64_t T, int64_t n_cols) { return T < kTopkMaxRows && n_cols > 4096; }
 
-size_t topk_workspace_bytes(int64_t T, int64_t n_cols, int k) {
+size_t topk_workspace_bytes(int64_t T, int64_t n_cols, int) {
     if (!topk_multi(T, n_cols)) return 0;
-    return tm_cand_off(T, k) + (size_t)T * n_cols * 8;
+    return topk_ws_cand_off(T, n_cols) + (size_t)T * n_cols * 8;
 }
 
 int64_t topk_chunk(int64_t T, int64_t n_cols) {
@@ -667,7 +630,7 @@ int64_t topk_chunk(int64_t T, int64_t n_cols) {
 }
 
 hipError_t launch_topk(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos, int m, int k, int32_t* idx,
-                       void* ws, bool hist_done, hipStream_t st) {
+                       void* ws, bool prepared, hipStream_t st) {
     if (T == 0) return hipSuccess;
     if (!topk_multi(T, n_cols)) {
         hipLaunchKernelGGL(k_topk_row, dim3((unsigned)T), dim3(kTopkThreads), 0, st, scores, n_cols, pos, m, k, idx);
@@ -675,15 +638,15 @@ hipError_t launch_topk(const float* scores, int64_t T, int64_t n_cols, const int
     }
     const int64_t chunk = topk_chunk(T, n_cols);
     const int nchunk = (int)((n_cols + chunk - 1) / chunk);
-    if (!hist_done)
-        hipLaunchKernelGGL(k_topkm_hist, dim3((unsigned)nchunk, (unsigned)T), dim3(kTmThreads), 0, st, scores, T, n_cols,
-                           pos, m, k, chunk, ws);
+    if (!prepared)
+        hipLaunchKernelGGL(k_topkm_gmax, dim3((unsigned)((n_cols + kTmThreads * 8 - 1) / (kTmThreads * 8)), (unsigned)T),
+                           dim3(kTmThreads), 0, st, scores, T, n_cols, pos, m, k, ws);
     hipLaunchKernelGGL(k_topkm_collect, dim3((unsigned)nchunk, (unsigned)T), dim3(kTmThreads), 0, st, scores, T, n_cols,
                        pos, m, k, chunk, ws, idx);
     hipLaunchKernelGGL(k_topkm_final, dim3((unsigned)T), dim3(kTfThreads), 0, st, T, n_cols, pos, m, k, ws, idx);
     return hipGetLastError();
 }
 
-bool topk_uses_hist(int64_t T, int64_t n_cols) { return topk_multi(T, n_cols); }
+bool topk_uses_summary(int64_t T, int64_t n_cols) { return topk_multi(T, n_cols); }
 
 }  // namespace csa

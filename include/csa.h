@@ -141,9 +141,10 @@ int csa_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t 
  *   n_cols   columns written per row (<= keys.cap)
  *   scores   [T][n_cols] fp32
  *   topk_ws  optional (NULL, 0 to skip): the workspace of the csa_topk call
- *            that will read these scores.  When given, the indexer also adds
- *            each row's key histogram (the first radix pass of the selection)
- *            into it, and that csa_topk call passes CSA_TOPK_HIST_READY so the
+ *            that will read these scores.  When given, the indexer also
+ *            writes the selection's row summary into it (for shapes whose
+ *            selection uses one: the largest score of every 128-column
+ *            group), and that csa_topk call passes CSA_TOPK_PREPARED so the
  *            selection skips its own pass over the scores.  Results are the
  *            same bit for bit either way.
  * h_i in {4, 8}; d_i in {64, 128}.  With power-of-two head weights and block
@@ -168,10 +169,10 @@ int csa_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, c
  * aligned, ZERO-FILLED before its first use; every call leaves it
  * zero-filled again, so one buffer serves any sequence of calls (any shapes)
  * on one stream.  Calls that share a workspace must not run concurrently.
- * flags: 0, or CSA_TOPK_HIST_READY when the preceding csa_index_scores call
- * for these scores was given this workspace (it built the histogram).
+ * flags: 0, or CSA_TOPK_PREPARED when the preceding csa_index_scores call
+ * for these scores was given this workspace (it wrote the row summary).
  */
-#define CSA_TOPK_HIST_READY 1u
+#define CSA_TOPK_PREPARED 1u
 size_t csa_topk_workspace(int64_t T, int64_t n_cols, int32_t k);
 int csa_topk(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos, int32_t m, int32_t k, int32_t* idx,
              void* ws, size_t ws_bytes, uint32_t flags, csa_stream_t stream);

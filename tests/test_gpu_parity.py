@@ -202,12 +202,13 @@ def test_topk_bit_exact(lib, dev, orc, T, n_cols, k, m, kind):
     assert np.array_equal(got, ref), f"rows differ: {np.where((got != ref).any(axis=1))[0][:5].tolist()}"
 
 
-def test_fused_histogram_and_workspace_reuse(lib, dev, gen, orc):
-    """Indexer-built histogram + csa_topk(hist_ready) equals the plain path; one
-    zero-filled workspace serves calls of different shapes and is left zeroed."""
+def test_indexer_summary_and_workspace_reuse(lib, dev, gen, orc):
+    """Indexer-written row summary + csa_topk(prepared) equals the oracle, and so
+    does the plain path; one zero-filled workspace serves calls of different
+    shapes and its counters are left zeroed."""
     import torch
 
-    _say("fused histogram, workspace reuse")
+    _say("indexer row summary, workspace reuse")
     ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
     for (T, N, k, plant) in [(4, 70000, 1024, 0.05), (3, 9000, 512, 0.0), (8, 20000, 2048, 0.02), (4, 70000, 1024, 0.0)]:
         qd, qs, w, seq, pos, kd, ks = _index_case(gen, 700 + T + N, T, 8, 128, N, T, np.full(T, 4 * N - 1),
@@ -216,11 +217,14 @@ def test_fused_histogram_and_workspace_reuse(lib, dev, gen, orc):
         ref_i = orc.topk(ref, pos, 4, k)
         keys = dev.index_keys((kd, ks), N)
         sc = lib.csa_index_scores(dev.t(qd), dev.t(qs), dev.t(w), dev.t(seq), dev.t(pos), keys, 4, N, topk_ws=ws)
-        ix = lib.csa_topk(sc, dev.t(pos), 4, k, ws=ws, hist_ready=True)
+        ix = lib.csa_topk(sc, dev.t(pos), 4, k, ws=ws, prepared=True)
+        ix2 = lib.csa_topk(sc, dev.t(pos), 4, k, ws=ws)
         torch.cuda.synchronize()
         assert np.array_equal(sc.cpu().numpy().view(np.uint32), ref.view(np.uint32))
         assert np.array_equal(ix.cpu().numpy(), ref_i)
-        assert int(ws[: 128 * (2 * 4096 * 4 + 64)].count_nonzero()) == 0, "workspace histogram region not left zeroed"
+        assert np.array_equal(ix2.cpu().numpy(), ref_i)
+        # the per-row counters (128 rows x 64 bytes) must be left zero
+        assert int(ws[: 128 * 64].count_nonzero()) == 0, "workspace counters not left zeroed"
 
 
 # ---------------------------------------------------------------------------

@@ -84,8 +84,7 @@ __global__ __launch_bounds__(256) void k_index_rows(const uint8_t* __restrict__ 
             p = fmaf(wr[1], fmaxf(acc[1], 0.f), p);
             p = fmaf(wr[2], fmaxf(acc[2], 0.f), p);
             p = fmaf(wr[3], fmaxf(acc[3], 0.f), p);
-            p += __shfl_xor(p, 16);
-            p += __shfl_xor(p, 32);
+            p = rows4_sum(p);  // the four head groups (exact: every partial sum is representable)
             const int64_t j = j0 + u * 16 + lane;
             if (lane < 16 && j < c1) {
                 out[j] = j < nv ? p : -INFINITY;
@@ -93,9 +92,14 @@ __global__ __launch_bounds__(256) void k_index_rows(const uint8_t* __restrict__ 
             }
         }
         if (gmax) {
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) gm = max(gm, (uint32_t)__shfl_xor((int)gm, o));
-            if (lane == 0) gmax[t * topk_groups(n_cols) + j0 / kTopkGroup] = gm;
+            // unsigned max over lanes 0..15 by DPP row shifts (shifted-in lanes read 0, the identity):
+            // lane 15 holds it
+            uint32_t x = gm;
+            x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false));  // row_shr:1
+            x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false));  // row_shr:2
+            x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false));  // row_shr:4
+            x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false));  // row_shr:8
+            if (lane == 15) gmax[t * topk_groups(n_cols) + j0 / kTopkGroup] = x;
         }
     }
 }

@@ -216,10 +216,23 @@ def test_indexer_summary_and_workspace_reuse(lib, dev, gen, orc):
         ref = orc.index_scores(qd, qs, w, seq, pos, kd, ks, N, 4, N).astype(np.float32)
         ref_i = orc.topk(ref, pos, 4, k)
         keys = dev.index_keys((kd, ks), N)
+        # expected row summary: per 128-column group the largest order-preserving key of the scores
+        ng = -(-N // 128)
+        b = ref.view(np.uint32).astype(np.uint64)
+        b[b == 0x80000000] = 0
+        okey = np.where(b & 0x80000000, b ^ 0xFFFFFFFF, b | 0x80000000).astype(np.uint64)
+        pad = np.zeros((T, ng * 128), np.uint64)
+        pad[:, :N] = okey
+        want_g = pad.reshape(T, ng, 128).max(axis=2).astype(np.uint32)
+        gsum = lambda: ws[128 * 64: 128 * 64 + T * ng * 4].view(torch.int32).cpu().numpy().view(np.uint32).reshape(T, ng)  # noqa: E731
+
         sc = lib.csa_index_scores(dev.t(qd), dev.t(qs), dev.t(w), dev.t(seq), dev.t(pos), keys, 4, N, topk_ws=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(gsum(), want_g), "row summary written by the indexer"
         ix = lib.csa_topk(sc, dev.t(pos), 4, k, ws=ws, prepared=True)
         ix2 = lib.csa_topk(sc, dev.t(pos), 4, k, ws=ws)
         torch.cuda.synchronize()
+        assert np.array_equal(gsum(), want_g), "row summary written by the selection"
         assert np.array_equal(sc.cpu().numpy().view(np.uint32), ref.view(np.uint32))
         assert np.array_equal(ix.cpu().numpy(), ref_i)
         assert np.array_equal(ix2.cpu().numpy(), ref_i)

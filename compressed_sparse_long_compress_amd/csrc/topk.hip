@@ -614,6 +614,223 @@ __global__ __launch_bounds__(kTfThreads) void k_topkm_final(int64_t T, int64_t n
     if (tid < 16) r.ctr[tid] = 0;
 }
 
+// ---------------------------------------------------------------------------
+// Many rows of up to kTsMaxCols columns: one workgroup per row streams the
+// row twice instead of caching it (so several rows share a CU):
+//   pass A  histogram of the top 12 key bits -> bin b1 holding the k-th key
+//   pass B  keys above b1 go straight into an LDS bitmap of the row; keys in
+//           b1 (the boundary) go to an LDS list as (key << 32 | ~index)
+//   the boundary is resolved exactly on the list (12 + 8 key bits, then the
+//   lowest indices among equal keys), its winners are marked, and the
+//   bitmap is written out in ascending order.
+// A boundary bin larger than the list is resolved by further streamed
+// passes (12 + 8 key bits, index bits for ties) that mark the bitmap.
+// ---------------------------------------------------------------------------
+constexpr int kTsThreads = 512;
+constexpr int kTsMaxCols = 65536;  // bitmap of 2048 words
+constexpr int kTsCand = 4096;      // boundary keys held in LDS
+
+__global__ __launch_bounds__(kTsThreads) void k_topk_stream(const float* __restrict__ scores, int64_t n_cols,
+                                                            const int64_t* __restrict__ pos, int m, int k,
+                                                            int32_t* __restrict__ idx) {
+    constexpr int NT = kTsThreads;
+    __shared__ uint32_t h[4096];
+    __shared__ uint32_t bm[kTsMaxCols / 32];
+    __shared__ uint64_t cl[kTsCand];
+    __shared__ uint32_t tie[kTieLds];
+    __shared__ int wsum[NT / 64];
+    __shared__ int bc[4];
+    __shared__ uint32_t lctr[3];
+    const int tid = threadIdx.x;
+    const int64_t t = blockIdx.x;
+    const int64_t nv64 = row_visible(pos, t, m, n_cols);
+    const int nv = (int)nv64;
+    const float* row = scores + t * n_cols;
+    int32_t* out = idx + t * (int64_t)k;
+    if (nv <= k) {
+        for (int a = tid; a < k; a += NT) out[a] = a < nv ? a : -1;
+        return;
+    }
+    const int nwords = (nv + 31) / 32;
+    const int perw = (nwords + NT - 1) / NT;  // word w at (w % perw) * NT + w / perw (conflict-free emission)
+    for (int i = tid; i < perw * NT; i += NT) bm[i] = 0;
+    for (int i = tid; i < 4096; i += NT) h[i] = 0;
+    if (tid < 3) lctr[tid] = 0;
+    __syncthreads();
+    auto mark = [&](uint32_t j) {
+        const uint32_t wd = j >> 5;
+        atomicOr(&bm[(wd % perw) * NT + wd / perw], 1u << (j & 31));
+    };
+    // visible keys of the row, 16-byte loads (several in flight) when the row is aligned
+    const bool vec = (((uintptr_t)row & 15) == 0);
+    auto stream = [&](auto fn) {
+        int j0 = 0;
+        if (vec) {
+            const int n4 = nv >> 2;
+#pragma unroll 4
+            for (int j4 = tid; j4 < n4; j4 += NT) {
+                const float4 v = ((const float4*)row)[j4];
+                fn(f32_order_key(v.x), 4 * j4);
+                fn(f32_order_key(v.y), 4 * j4 + 1);
+                fn(f32_order_key(v.z), 4 * j4 + 2);
+                fn(f32_order_key(v.w), 4 * j4 + 3);
+            }
+            j0 = 4 * n4;
+        }
+        for (int j = j0 + tid; j < nv; j += NT) fn(f32_order_key(row[j]), j);
+    };
+
+    // ---- pass A ----
+    stream([&](uint32_t key, int) { atomicAdd(&h[tm_pos<4096, NT>(key >> 20)], 1u); });
+    __syncthreads();
+    int above1;
+    const uint32_t b1 = (uint32_t)tm_find<4096, NT>(h, k, wsum, bc, above1);
+    const int n_b1 = (int)h[tm_pos<4096, NT>(b1)];
+    const int need = k - above1;  // >= 1 keys of bin b1
+    __syncthreads();
+    for (int i = tid; i < 4096; i += NT) h[i] = 0;
+    __syncthreads();
+
+    if (n_b1 <= kTsCand) {
+        // ---- pass B: mark above b1, list b1 ----
+        stream([&](uint32_t key, int j) {
+            const uint32_t bin = key >> 20;
+            if (bin > b1) mark((uint32_t)j);
+            else if (bin == b1) cl[atomicAdd(&lctr[0], 1u)] = ((uint64_t)key << 32) | (uint32_t)~(uint32_t)j;
+        });
+        __syncthreads();
+        const int n_cand = n_b1;
+        for (int i = tid; i < n_cand; i += NT) {
+            const uint32_t key = (uint32_t)(cl[i] >> 32);
+            atomicAdd(&h[tm_pos<4096, NT>((key >> 8) & 0xFFFu)], 1u);
+        }
+        __syncthreads();
+        int above2;
+        const uint32_t b2 = (uint32_t)tm_find<4096, NT>(h, need, wsum, bc, above2);
+        for (int i = tid; i < 256; i += NT) h[i] = 0;
+        __syncthreads();
+        const uint32_t p2 = (b1 << 12) | b2;
+        for (int i = tid; i < n_cand; i += NT) {
+            const uint32_t key = (uint32_t)(cl[i] >> 32);
+            if ((key >> 8) == p2) atomicAdd(&h[tm_pos<256, NT>(key & 0xFFu)], 1u);
+        }
+        __syncthreads();
+        int above3;
+        const uint32_t b3 = (uint32_t)tm_find<256, NT>(h, need - above2, wsum, bc, above3);
+        const uint32_t thr = (p2 << 8) | b3;
+        const int need_eq = need - above2 - above3;
+        for (int i = tid; i < n_cand; i += NT) {
+            const uint64_t c = cl[i];
+            const uint32_t key = (uint32_t)(c >> 32);
+            if (key > thr) mark(~(uint32_t)c);
+            else if (key == thr) atomicAdd(&lctr[1], 1u);
+        }
+        __syncthreads();
+        uint32_t idx_lim = 0xFFFFFFFFu;  // equal keys are taken up to this index
+        const int n_eq = (int)lctr[1];
+        if (n_eq > need_eq && n_eq <= kTieLds) {
+            for (int i = tid; i < n_cand; i += NT) {
+                const uint64_t c = cl[i];
+                if ((uint32_t)(c >> 32) == thr) tie[atomicAdd(&lctr[2], 1u)] = ~(uint32_t)c;
+            }
+            __syncthreads();
+            for (int i = tid; i < n_eq; i += NT) {
+                const uint32_t ji = tie[i];
+                int rank = 0;
+                for (int q = 0; q < n_eq; ++q) rank += tie[q] < ji ? 1 : 0;
+                if (rank == need_eq - 1) bc[2] = (int)ji;
+            }
+            __syncthreads();
+            idx_lim = (uint32_t)bc[2];
+            __syncthreads();
+        } else if (n_eq > need_eq) {
+            uint32_t pre = 0, pm = 0;
+            int nl = need_eq;
+            for (int sh = 22; sh >= 0; sh -= 11) {
+                for (int i = tid; i < 2048; i += NT) h[i] = 0;
+                __syncthreads();
+                for (int i = tid; i < n_cand; i += NT) {
+                    const uint64_t c = cl[i];
+                    if ((uint32_t)(c >> 32) != thr) continue;
+                    const uint32_t jx = ~(uint32_t)c;
+                    if ((jx & pm) == pre) atomicAdd(&h[tm_pos<2048, NT>(2047 - ((jx >> sh) & 0x7FF))], 1u);
+                }
+                __syncthreads();
+                int ab;
+                const uint32_t bn = 2047u - (uint32_t)tm_find<2048, NT>(h, nl, wsum, bc, ab);
+                nl -= ab;
+                pre |= bn << sh;
+                pm |= 0x7FFu << sh;
+            }
+            idx_lim = pre;
+        }
+        for (int i = tid; i < n_cand; i += NT) {
+            const uint64_t c = cl[i];
+            if ((uint32_t)(c >> 32) == thr && ~(uint32_t)c <= idx_lim) mark(~(uint32_t)c);
+        }
+    } else {
+        // ---- large boundary bin: streamed refinement ----
+        stream([&](uint32_t key, int) {
+            if ((key >> 20) == b1) atomicAdd(&h[tm_pos<4096, NT>((key >> 8) & 0xFFFu)], 1u);
+        });
+        __syncthreads();
+        int above2;
+        const uint32_t b2 = (uint32_t)tm_find<4096, NT>(h, need, wsum, bc, above2);
+        for (int i = tid; i < 256; i += NT) h[i] = 0;
+        __syncthreads();
+        const uint32_t p2 = (b1 << 12) | b2;
+        stream([&](uint32_t key, int) {
+            if ((key >> 8) == p2) atomicAdd(&h[tm_pos<256, NT>(key & 0xFFu)], 1u);
+        });
+        __syncthreads();
+        int above3;
+        const uint32_t b3 = (uint32_t)tm_find<256, NT>(h, need - above2, wsum, bc, above3);
+        const uint32_t thr = (p2 << 8) | b3;
+        const int need_eq = need - above2 - above3;
+        const int n_eq = (int)h[tm_pos<256, NT>(b3)];
+        uint32_t idx_lim = 0xFFFFFFFFu;
+        if (n_eq > need_eq) {
+            uint32_t pre = 0, pm = 0;
+            int nl = need_eq;
+            for (int sh = 22; sh >= 0; sh -= 11) {
+                __syncthreads();
+                for (int i = tid; i < 2048; i += NT) h[i] = 0;
+                __syncthreads();
+                stream([&](uint32_t key, int j) {
+                    const uint32_t jx = (uint32_t)j;
+                    if (key == thr && (jx & pm) == pre) atomicAdd(&h[tm_pos<2048, NT>(2047 - ((jx >> sh) & 0x7FF))], 1u);
+                });
+                __syncthreads();
+                int ab;
+                const uint32_t bn = 2047u - (uint32_t)tm_find<2048, NT>(h, nl, wsum, bc, ab);
+                nl -= ab;
+                pre |= bn << sh;
+                pm |= 0x7FFu << sh;
+            }
+            idx_lim = pre;
+        }
+        stream([&](uint32_t key, int j) {
+            if (key > thr || (key == thr && (uint32_t)j <= idx_lim)) mark((uint32_t)j);
+        });
+    }
+    __syncthreads();
+    // ---- emit in ascending order: thread t owns words t*perw .. t*perw+perw-1 ----
+    int cnt = 0;
+    for (int i = 0; i < perw; ++i) cnt += __popc(bm[i * NT + tid]);
+    int tot;
+    int o = tm_scan<NT>(cnt, wsum, tot);
+    for (int i = 0; i < perw; ++i) {
+        uint32_t b = bm[i * NT + tid];
+        const int wi = tid * perw + i;
+        while (b) {
+            const int bit = __builtin_ctz(b);
+            if (o < k) out[o] = wi * 32 + bit;
+            ++o;
+            b &= b - 1;
+        }
+    }
+}
+
 static bool topk_multi(int64_t T, int64_t n_cols) { return T < kTopkMaxRows && n_cols > 4096; }
 
 size_t topk_workspace_bytes(int64_t T, int64_t n_cols, int) {
@@ -633,7 +850,10 @@ hipError_t launch_topk(const float* scores, int64_t T, int64_t n_cols, const int
                        void* ws, bool prepared, hipStream_t st) {
     if (T == 0) return hipSuccess;
     if (!topk_multi(T, n_cols)) {
-        hipLaunchKernelGGL(k_topk_row, dim3((unsigned)T), dim3(kTopkThreads), 0, st, scores, n_cols, pos, m, k, idx);
+        if (n_cols <= kTsMaxCols)
+            hipLaunchKernelGGL(k_topk_stream, dim3((unsigned)T), dim3(kTsThreads), 0, st, scores, n_cols, pos, m, k, idx);
+        else
+            hipLaunchKernelGGL(k_topk_row, dim3((unsigned)T), dim3(kTopkThreads), 0, st, scores, n_cols, pos, m, k, idx);
         return hipGetLastError();
     }
     const int64_t chunk = topk_chunk(T, n_cols);

@@ -177,6 +177,11 @@ def test_index_scores_bit_exact(lib, dev, gen, orc, T, h_i, d_i, N, B, m, n_cols
     (8, 3000, 1024, 4, "short"),        # some rows see fewer than k columns
     (5, 2048, 2048, 1, "normal"),
     (4, 70000, 1024, 4, "allequal"),
+    # many rows (one workgroup per row, row streamed from global memory)
+    (160, 16384, 512, 4, "ties"),       # equal keys beyond the direct-ranking limit
+    (128, 8192, 1024, 4, "allequal"),   # boundary bin larger than the LDS list
+    (136, 65536, 2048, 4, "normal"),    # longest rows of this path
+    (200, 20000, 1024, 4, "short"),
 ])
 def test_topk_bit_exact(lib, dev, orc, T, n_cols, k, m, kind):
     import torch

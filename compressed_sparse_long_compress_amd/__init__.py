@@ -181,15 +181,15 @@ def csa_topk_workspace(T, n_cols, k):
 
 
 def topk_workspace(T, n_cols, k, device="cuda"):
-    """A zero-filled top-k workspace (the library leaves it zero-filled after every call)."""
+    """A top-k workspace (its contents need no initialisation)."""
     need = csa_topk_workspace(T, n_cols, k)
-    return torch.zeros(max(need, 1), dtype=torch.uint8, device=device)
+    return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
 
 
 def csa_topk(scores, pos, m, k, out=None, ws=None, prepared=False):
     """Top-k per row (score desc, index asc) in ascending index order, -1 padded -> int32 [T, k].
 
-    ws: a zero-filled uint8 workspace of csa_topk_workspace(T, n_cols, k) bytes (allocated when None)."""
+    ws: a uint8 workspace of csa_topk_workspace(T, n_cols, k) bytes (allocated when None)."""
     _need(scores, "scores", torch.float32, 2)
     _need(pos, "pos", torch.int64, 1)
     T, n_cols = scores.shape

@@ -115,11 +115,11 @@ int csa_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, c
     if (!aligned16(q) || !aligned16(keys.data)) return fail(CSA_EINVAL, "%s: q and keys.data must be 16-byte aligned", fn);
     uint32_t* gmax = nullptr;
     if (topk_ws && csa::topk_uses_summary(T, n_cols)) {
-        // the row summaries live in the top-k workspace, after its counters
+        // the row summaries are the top-k workspace
         if (topk_ws_bytes < csa::topk_workspace_bytes(T, n_cols, 1))
             return fail(CSA_EWORKSPACE, "%s: top-k workspace too small for the row summaries", fn);
         if (((uintptr_t)topk_ws & 255u) != 0) return fail(CSA_EINVAL, "%s: workspace must be 256-byte aligned", fn);
-        gmax = (uint32_t*)((char*)topk_ws + csa::topk_ws_gmax_off());
+        gmax = (uint32_t*)topk_ws;
     }
     hipError_t e = csa::launch_index_scores(q, q_scale, w, seq, pos, T, h_i, d_i, keys.data, keys.scale, keys.cap, m,
                                             n_cols, scores, gmax, (hipStream_t)stream);

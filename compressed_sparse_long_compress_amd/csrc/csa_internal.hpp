@@ -12,17 +12,12 @@ struct RopeTab {
 };
 RopeTab rope_table(double base);
 
-// Top-k workspace of the few-long-rows path (T < kTopkMaxRows rows):
-// kTopkMaxRows x 16 counters (must start zero-filled; left zero-filled),
-// then the row summaries (per kTopkGroup-column group the largest order key
-// of its visible columns), then T x n_cols candidates.
+// Top-k workspace of the few-long-rows path (T < kTopkMaxRows rows): the
+// row summaries, summ[T][topk_groups(n_cols)], each the largest order key of
+// the visible columns of one kTopkGroup-column group (0 for none).
 constexpr int kTopkMaxRows = 128;
-constexpr int kTopkGroup = 128;
+constexpr int kTopkGroup = 32;
 __host__ __device__ inline int64_t topk_groups(int64_t n_cols) { return (n_cols + kTopkGroup - 1) / kTopkGroup; }
-__host__ __device__ inline size_t topk_ws_gmax_off() { return (size_t)kTopkMaxRows * 64; }
-__host__ __device__ inline size_t topk_ws_cand_off(int64_t T, int64_t n_cols) {
-    return (topk_ws_gmax_off() + (size_t)T * topk_groups(n_cols) * 4 + 255) & ~(size_t)255;
-}
 
 hipError_t launch_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t n_tok, int m, int d,
                            const RopeTab& rt, int64_t row0, int64_t cap, uint8_t* nope, uint16_t* rope, float* scale,

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void k_index_rows(const uint8_t* __restrict__ 
                                                     uint32_t* __restrict__ gmax) {
     constexpr int KB = DI / 2;   // bytes per key
     constexpr int NB = DI / 32;  // scale blocks per key
-    static_assert(16 * U == kTopkGroup, "one wave step = one summary group");
+    static_assert(16 * U == 4 * kTopkGroup, "one wave step = four summary groups");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t t = blockIdx.y;
     const int r = lane & 15, g = lane >> 4;
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void k_index_rows(const uint8_t* __restrict__ 
     float* out = scores + t * n_cols;
 
     for (int64_t j0 = c0 + (int64_t)wave * 16 * U; j0 < c1; j0 += 4 * 16 * U) {
-        uint32_t gm = 0;  // largest order key of the visible scores of this group (lanes < 16)
+        uint32_t gm[4] = {0u, 0u, 0u, 0u};  // per summary group of this step: largest visible order key (lanes < 16)
         v4i bk[U];
         int sb[U];
 #pragma unroll
@@ -88,18 +88,25 @@ __global__ __launch_bounds__(256) void k_index_rows(const uint8_t* __restrict__ 
             const int64_t j = j0 + u * 16 + lane;
             if (lane < 16 && j < c1) {
                 out[j] = j < nv ? p : -INFINITY;
-                if (j < nv) gm = max(gm, f32_order_key(p));
+                if (j < nv) gm[u / (U / 4)] = max(gm[u / (U / 4)], f32_order_key(p));
             }
         }
         if (gmax) {
-            // unsigned max over lanes 0..15 by DPP row shifts (shifted-in lanes read 0, the identity):
-            // lane 15 holds it
-            uint32_t x = gm;
-            x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false));  // row_shr:1
-            x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false));  // row_shr:2
-            x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false));  // row_shr:4
-            x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false));  // row_shr:8
-            if (lane == 15) gmax[t * topk_groups(n_cols) + j0 / kTopkGroup] = x;
+            // unsigned max over lanes 0..15 of four values, spread so that lanes 4G..4G+3 end with
+            // group G: exchange halves with the mirrored lane (l <-> 15-l), then with the mirrored
+            // lane within each half (l <-> 7-l), then reduce each quad (xor 1, xor 2)
+            const bool hi8 = (lane & 8) != 0, hi4 = (lane & 4) != 0;
+            const uint32_t s0 = hi8 ? gm[0] : gm[2], s1 = hi8 ? gm[1] : gm[3];
+            uint32_t k0 = hi8 ? gm[2] : gm[0], k1 = hi8 ? gm[3] : gm[1];
+            k0 = max(k0, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s0, 0x140, 0xf, 0xf, false));  // row_mirror
+            k1 = max(k1, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s1, 0x140, 0xf, 0xf, false));
+            const uint32_t s2 = hi4 ? k0 : k1;
+            uint32_t x = hi4 ? k1 : k0;
+            x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s2, 0x141, 0xf, 0xf, false));  // row_half_mirror
+            x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+            x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+            const int64_t gi = j0 / kTopkGroup + (lane >> 2);
+            if (lane < 16 && (lane & 3) == 0 && gi < topk_groups(n_cols)) gmax[t * topk_groups(n_cols) + gi] = x;
         }
     }
 }

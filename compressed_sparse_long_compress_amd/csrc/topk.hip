@@ -65,27 +65,14 @@ __device__ int find_bin(const uint32_t* hist, int need, int* wsum, int* bcast, i
     return bin;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void k_topk_row(const float* __restrict__ scores, int64_t n_cols,
-                                                           const int64_t* __restrict__ pos, int m, int k,
-                                                           int32_t* __restrict__ idx) {
-    __shared__ uint32_t hist[4096];
-    __shared__ __align__(16) uint32_t cache[kTopkCache];
-    __shared__ int wsum[2 * (kTopkThreads / 64)];
-    __shared__ int bcast[4];
+// Exact top-k of one row (nv > k visible columns) by one kTopkThreads-thread
+// workgroup.  The keys are cached in `cache` when the row fits (`cap` keys);
+// otherwise every pass re-reads global memory.  hist: 4096 words; wsum:
+// 2 * kTopkThreads / 64 ints; bcast: 4 ints.
+__device__ void row_select(const float* __restrict__ row, int nv, int k, int32_t* __restrict__ out, uint32_t* hist,
+                           uint32_t* cache, int cap, int* wsum, int* bcast) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t t = blockIdx.x;
-    int64_t nv64 = (pos[t] + 1) / m;
-    if (nv64 > n_cols) nv64 = n_cols;
-    if (nv64 < 0) nv64 = 0;
-    const int nv = (int)nv64;
-    const float* row = scores + t * n_cols;
-    int32_t* out = idx + t * (int64_t)k;
-
-    if (nv <= k) {
-        for (int a = tid; a < k; a += kTopkThreads) out[a] = a < nv ? a : -1;
-        return;
-    }
-    const bool cached = nv <= kTopkCache;
+    const bool cached = nv <= cap;
     auto key_at = [&](int j) -> uint32_t { return cached ? cache[j] : f32_order_key(row[j]); };
     for (int i = tid; i < 4096; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
@@ -199,53 +186,30 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_row(const float* __restri
     }
 }
 
-// ---------------------------------------------------------------------------
-// Few long rows (decode): the row is split over many workgroups.
-//   row summary      per kTopkGroup-column group, the largest order key of
-//                    its visible columns (0 for a group with none), written
-//                    by the indexer kernel next to the scores, or else by
-//                    k_topkm_gmax
-//   k_topkm_collect  per chunk.  tau = lower edge of the 12-bit key prefix
-//                    holding the k-th largest group maximum (0 when the row
-//                    has fewer than k groups).  The group maxima are keys of
-//                    distinct columns, so the row's k-th largest key is
-//                    >= tau and every column of the top-k (ties included)
-//                    has key >= tau.  Appends (key, ~index) of the chunk's
-//                    visible columns with key >= tau, one slot reservation
-//                    per workgroup.
-//   k_topkm_final    one workgroup per row: exact radix select over the
-//                    candidates (12 + 12 + 8 key bits, equal keys to the
-//                    lower index), marks the k winners in an LDS bitmap of
-//                    the row, writes them in ascending order and resets the
-//                    row's counters.
-// The hand-overs are kernel boundaries: a per-workgroup agent-scope fence
-// would write back the whole L2 (holding the freshly written scores).
-// Workspace (topk_ws_* in csa_internal.hpp): 128 rows x 16 counters
-// (zero-filled before first use, left zero-filled), the row summaries, then
-// T x n_cols candidates.
-// ---------------------------------------------------------------------------
-constexpr int kTmThreads = 256;
-constexpr int kTfThreads = 1024;     // the per-row finaliser
-constexpr int kTmE = 8;              // consecutive columns per thread in the collect pass
-constexpr int kBitmapWords = 16384;  // row bitmap of the finaliser: rows up to 524,288 columns
-constexpr int kCandLds = 8192;       // candidates the finaliser stages in LDS
-constexpr int kTieLds = 256;         // equal-key sets up to this size are ranked directly
-static_assert(kTmThreads * kTmE % kTopkGroup == 0, "summary groups inside one collect step");
-
-struct TmRow {
-    uint32_t* ctr;   // [0] candidates
-    uint32_t* gmax;  // [topk_groups(n_cols)] group maxima
-    uint64_t* cand;  // [n_cols] (key << 32 | ~index)
-};
-
-__device__ __forceinline__ TmRow tm_row(void* ws, int64_t T, int64_t t, int64_t n_cols) {
-    char* b = (char*)ws;
-    TmRow r;
-    r.ctr = (uint32_t*)(b + (size_t)t * 64);
-    r.gmax = (uint32_t*)(b + topk_ws_gmax_off()) + t * topk_groups(n_cols);
-    r.cand = (uint64_t*)(b + topk_ws_cand_off(T, n_cols)) + t * n_cols;
-    return r;
+__global__ __launch_bounds__(kTopkThreads) void k_topk_row(const float* __restrict__ scores, int64_t n_cols,
+                                                           const int64_t* __restrict__ pos, int m, int k,
+                                                           int32_t* __restrict__ idx) {
+    __shared__ uint32_t hist[4096];
+    __shared__ __align__(16) uint32_t cache[kTopkCache];
+    __shared__ int wsum[2 * (kTopkThreads / 64)];
+    __shared__ int bcast[4];
+    const int64_t t = blockIdx.x;
+    int64_t nv64 = (pos[t] + 1) / m;
+    if (nv64 > n_cols) nv64 = n_cols;
+    if (nv64 < 0) nv64 = 0;
+    const int nv = (int)nv64;
+    int32_t* out = idx + t * (int64_t)k;
+    if (nv <= k) {
+        for (int a = threadIdx.x; a < k; a += kTopkThreads) out[a] = a < nv ? a : -1;
+        return;
+    }
+    row_select(scores + t * n_cols, nv, k, out, hist, cache, kTopkCache, wsum, bcast);
 }
+
+// ---------------------------------------------------------------------------
+// Helpers of the histogram selections below.
+// ---------------------------------------------------------------------------
+constexpr int kTieLds = 256;  // equal-key sets up to this size are ranked directly
 
 __device__ __forceinline__ int64_t row_visible(const int64_t* pos, int64_t t, int m, int64_t n_cols) {
     int64_t nv = (pos[t] + 1) / m;
@@ -254,56 +218,20 @@ __device__ __forceinline__ int64_t row_visible(const int64_t* pos, int64_t t, in
     return nv;
 }
 
-// Row summaries from the scores (when the indexer did not write them): 16
-// threads x 8 consecutive columns per group.
-__global__ __launch_bounds__(kTmThreads) void k_topkm_gmax(const float* __restrict__ scores, int64_t T,
-                                                           int64_t n_cols, const int64_t* __restrict__ pos, int m,
-                                                           int k, void* ws) {
-    const int tid = threadIdx.x;
-    const int64_t t = blockIdx.y;
-    const int64_t nv = row_visible(pos, t, m, n_cols);
-    if (nv <= k) return;
-    const float* row = scores + t * n_cols;
-    const int64_t j0 = (int64_t)blockIdx.x * (kTmThreads * 8) + tid * 8;
-    uint32_t g = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        if (j0 + e < nv) g = max(g, f32_order_key(row[j0 + e]));
-#pragma unroll
-    for (int o = 1; o < kTopkGroup / 8; o <<= 1) g = max(g, (uint32_t)__shfl_xor((int)g, o));
-    if ((tid & (kTopkGroup / 8 - 1)) == 0 && j0 < n_cols) tm_row(ws, T, t, n_cols).gmax[j0 / kTopkGroup] = g;
-}
-
-// Histograms handed to tm_find are stored "transposed": with PER = NB/256
+// Histograms handed to tm_find are stored "transposed": with PER = NB/NT
 // bins per thread and bins ranked from the top (r = NB-1-bin), rank r sits
-// at position (r % PER) * 256 + r / PER.  Thread t then owns ranks
-// t*PER .. t*PER+PER-1 and reads them at positions i*256 + t: consecutive
+// at position (r % PER) * NT + r / PER.  Thread t then owns ranks
+// t*PER .. t*PER+PER-1 and reads them at positions i*NT + t: consecutive
 // threads, consecutive words, no LDS bank conflicts.
-template <int NB, int NT = kTmThreads>
+template <int NB, int NT>
 __device__ __forceinline__ int tm_pos(uint32_t bin) {
     constexpr int PER = NB / NT > 0 ? NB / NT : 1;
     const int r = NB - 1 - (int)bin;
     return (r % PER) * NT + r / PER;
 }
 
-// 4096-bin global histogram into the transposed LDS layout: thread t loads
-// its PER = 4096/NT consecutive bins (16-byte loads, issued together) and
-// scatters them.
-template <int NT = kTmThreads>
-__device__ __forceinline__ void tm_load_hist(uint32_t* dst, const uint32_t* src) {
-    constexpr int PER = 4096 / NT, NV = PER / 4;
-    const int t = threadIdx.x;
-    uint4 v[NV];
-    const uint4* p = (const uint4*)(src + 4096 - PER * (t + 1));  // bins 4096-PER(t+1) .. 4095-PER t
-#pragma unroll
-    for (int i = 0; i < NV; ++i) v[i] = p[i];
-    const uint32_t* w = (const uint32_t*)v;  // w[q] = bin 4096-PER(t+1)+q = rank PER t+PER-1-q
-#pragma unroll
-    for (int q = 0; q < PER; ++q) dst[(PER - 1 - q) * NT + t] = w[q];
-}
-
 // exclusive scan over an NT-thread block
-template <int NT = kTmThreads>
+template <int NT>
 __device__ __forceinline__ int tm_scan(int v, int* wsum, int& total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int x = wave_incl_scan(v);
@@ -322,7 +250,7 @@ __device__ __forceinline__ int tm_scan(int v, int* wsum, int& total) {
 
 // bin (scanning from the top) where the running count reaches need, on a
 // transposed histogram; NT threads, one block scan.
-template <int NB, int NT = kTmThreads>
+template <int NB, int NT>
 __device__ int tm_find(const uint32_t* hist, int need, int* wsum, int* bc, int& above) {
     constexpr int PER = NB / NT > 0 ? NB / NT : 1;
     const int tid = threadIdx.x;
@@ -354,209 +282,451 @@ __device__ int tm_find(const uint32_t* hist, int need, int* wsum, int* bc, int& 
     return bin;
 }
 
+// ---------------------------------------------------------------------------
+// Few long rows (decode): selection from the row summary, in two kernels.
+//   row summary    per kTopkGroup-column group, the largest order key of its
+//                  visible columns (0 for a group with none).  Written by the
+//                  indexer kernel next to the scores, or else by k_topk_gmax.
+//   k_topk_cand    grid (slices, rows).  Every workgroup derives the same
+//                  tau from the whole summary: the lower edge of a narrow key
+//                  window holding the k-th largest group maximum.  The group
+//                  maxima are keys of distinct columns, so the row's k-th
+//                  largest key is >= tau: every column of the top-k (ties
+//                  included) has key >= tau and lies in a group whose maximum
+//                  is >= tau.  The workgroup reads back only those groups of
+//                  its slice of the row (about k groups per row in all) and
+//                  writes their keys >= tau as (key << 32 | ~column) to its
+//                  slice of the candidate buffer, with the count, tau and the
+//                  row's largest key in its record.
+//   k_topk_pick    one workgroup per row: gathers the candidates into LDS,
+//                  finds the k-th largest by a histogram descent, ranks the
+//                  few keys of its window directly (equal keys to the lower
+//                  column), marks the winners in an LDS bitmap of the row and
+//                  writes them in ascending order.  When a slice overflowed
+//                  or the candidates exceed LDS (heavy ties), the row is
+//                  selected by row_select over the whole row instead.
+// The hand-overs are kernel boundaries: a per-workgroup agent-scope fence
+// would write back the whole L2 (holding the freshly written scores).
+// ---------------------------------------------------------------------------
+constexpr int kTgThreads = 256;      // k_topk_gmax: 8 consecutive columns per thread
+constexpr int kTcThreads = 1024;     // k_topk_cand
+constexpr int kTcChunks = 1;         // 8-group chunks per k_topk_cand thread held in registers
+constexpr int kTqCand = 8192;        // candidates k_topk_pick holds in LDS
+constexpr int kBitmapWords = 16384;  // k_topk_pick's row bitmap: rows up to 524,288 columns
 
-__global__ __launch_bounds__(kTmThreads) void k_topkm_collect(const float* __restrict__ scores, int64_t T,
-                                                              int64_t n_cols, const int64_t* __restrict__ pos, int m,
-                                                              int k, int64_t chunk, void* ws,
-                                                              int32_t* __restrict__ idx) {
-    __shared__ uint32_t h[4096];
-    __shared__ int wsum[kTmThreads / 64];
-    __shared__ int bc[4];
+__global__ __launch_bounds__(kTgThreads) void k_topk_gmax(const float* __restrict__ scores, int64_t n_cols,
+                                                          const int64_t* __restrict__ pos, int m, int k,
+                                                          uint32_t* __restrict__ summ) {
+    constexpr int TPG = kTopkGroup / 8;  // threads per group
     const int tid = threadIdx.x;
     const int64_t t = blockIdx.y;
-    TmRow r = tm_row(ws, T, t, n_cols);
-    // the row's group maxima (groups without visible columns hold 0) and this workgroup's first
-    // scores are requested before anything that depends on pos, and the histogram is cleared
-    // while they are in flight
-    constexpr int GPT = 16;  // group maxima per thread held in registers (rows up to 524,288 columns)
-    const int ng = (int)topk_groups(n_cols);
-    uint32_t gv[GPT];
-#pragma unroll
-    for (int i = 0; i < GPT; ++i) {
-        const int gi = i * kTmThreads + tid;
-        gv[i] = gi < ng ? r.gmax[gi] : 0u;
-    }
-    const int64_t c0 = (int64_t)blockIdx.x * chunk;
-    const float* row = scores + t * n_cols;
-    float pre[kTmE];
-    {
-        const int64_t j0 = c0 + (int64_t)tid * kTmE;
-#pragma unroll
-        for (int e = 0; e < kTmE; ++e) pre[e] = j0 + e < n_cols ? row[j0 + e] : 0.f;
-    }
-    for (int i = tid; i < 4096; i += kTmThreads) h[i] = 0;
     const int64_t nv = row_visible(pos, t, m, n_cols);
-    int32_t* out = idx + t * (int64_t)k;
-    if (nv <= k) {
-        if (blockIdx.x == 0)
-            for (int a = tid; a < k; a += kTmThreads) out[a] = a < nv ? a : -1;
-        return;
-    }
-    const int64_t c1 = c0 + chunk < nv ? c0 + chunk : nv;
+    if (nv <= k) return;
+    const float* row = scores + t * n_cols;
+    const int64_t j0 = (int64_t)blockIdx.x * (kTgThreads * 8) + tid * 8;
+    uint32_t g = 0;
+    for (int e = 0; e < 8; ++e)
+        if (j0 + e < nv) g = max(g, f32_order_key(row[j0 + e]));
+#pragma unroll
+    for (int o = 1; o < TPG; o <<= 1) g = max(g, (uint32_t)__shfl_xor((int)g, o));
+    if ((tid & (TPG - 1)) == 0 && j0 < n_cols) summ[t * topk_groups(n_cols) + j0 / kTopkGroup] = g;
+}
 
-    // ---- tau: the lower edge of the 12-bit key prefix holding the k-th largest group maximum
-    //      (0 when the row has fewer than k groups) ----
-    uint32_t tau = 0;
-    if (ng >= k) {
-        const bool more = ng > GPT * kTmThreads;  // longer rows re-read the rest from global memory
-        __syncthreads();
+// tm_find with two barriers: the caller must not write wsum or bc again before
+// its next barrier (and then only through another tm_find / tm_scan call).
+template <int NB, int NT>
+__device__ __forceinline__ int tm_find2(const uint32_t* hist, int need, int* wsum, int* bc, int& above) {
+    constexpr int PER = NB / NT > 0 ? NB / NT : 1;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t v[PER];
+    int local = 0;
 #pragma unroll
-        for (int i = 0; i < GPT; ++i)
-            if (i * kTmThreads + tid < ng) atomicAdd(&h[tm_pos<4096>(gv[i] >> 20)], 1u);
-        if (more)
-            for (int gi = GPT * kTmThreads + tid; gi < ng; gi += kTmThreads) atomicAdd(&h[tm_pos<4096>(r.gmax[gi] >> 20)], 1u);
-        __syncthreads();
-        int ab1;
-        const uint32_t g1 = (uint32_t)tm_find<4096>(h, k, wsum, bc, ab1);
-        tau = g1 << 20;
+    for (int i = 0; i < PER; ++i) {
+        v[i] = tid * PER + i < NB ? hist[i * NT + tid] : 0u;
+        local += (int)v[i];
     }
+    const int x = wave_incl_scan(local);
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int before = x - local;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) before += i < wave ? wsum[i] : 0;
+    if (before < need && before + local >= need) {
+        int run = before;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            if (run + (int)v[i] >= need) {
+                bc[0] = NB - 1 - (tid * PER + i);
+                bc[1] = run;
+                break;
+            }
+            run += (int)v[i];
+        }
+    }
+    __syncthreads();
+    above = bc[1];
+    return bc[0];
+}
 
-    // ---- candidates of this chunk: E consecutive columns per thread, one slot reservation ----
-    for (int64_t jb = c0; jb < c1; jb += (int64_t)kTmThreads * kTmE) {
-        const int64_t j0 = jb + (int64_t)tid * kTmE;
-        uint32_t key[kTmE];
-        int n_c = 0;
-#pragma unroll
-        for (int e = 0; e < kTmE; ++e) {
-            const int64_t j = j0 + e;
-            key[e] = j < c1 ? f32_order_key(jb == c0 ? pre[e] : row[j]) : 0u;
-            n_c += (j < c1 && key[e] >= tau) ? 1 : 0;
-        }
-        int tot;
-        const int before = tm_scan(n_c, wsum, tot);
-        if (tid == 0) bc[2] = tot ? (int)atomicAdd(&r.ctr[0], (uint32_t)tot) : 0;
+// Histogram descent over a set of keys (visited by for_each): finds a window
+// [base, base + 2^sh) holding the need-th largest key, with `above` keys
+// above the window and `inbin` keys inside it.  Each level histograms the
+// current window into 4096 bins and keeps the bin of the need-th largest,
+// until that bin holds at most `stop` keys or a single key value (sh == 0).
+// Requires lo <= the need-th largest key and every key <= hi; keys below lo
+// are ignored.  h: 4096 LDS words, zero on entry (and visible to all
+// threads); on return it holds the last level's counts, and the caller
+// passes a barrier before writing h, wsum or bc again.
+template <int NT, class ForEach>
+__device__ void hist_descend(ForEach for_each, uint32_t lo, uint32_t hi, int need, int stop, uint32_t* h, int* wsum,
+                             int* bc, uint32_t& base, int& sh, int& above, int& inbin) {
+    const int tid = threadIdx.x;
+    const uint64_t span = (uint64_t)hi - lo;
+    int s = 0;
+    while ((span >> s) >= 4096) ++s;
+    uint32_t b0 = lo;
+    int ab_tot = 0;
+    for (;;) {
+        const uint64_t top = (uint64_t)b0 + ((uint64_t)4096 << s);
+        const uint32_t wb = b0;
+        const int ws = s;
+        for_each([&](uint32_t key) {
+            if (key >= wb && (uint64_t)key < top) atomicAdd(&h[tm_pos<4096, NT>((key - wb) >> ws)], 1u);
+        });
         __syncthreads();
-        uint32_t sc = (uint32_t)bc[2] + (uint32_t)before;
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < kTmE; ++e) {
-            const int64_t j = j0 + e;
-            if (j < c1 && key[e] >= tau) r.cand[sc++] = ((uint64_t)key[e] << 32) | (uint32_t)~(uint32_t)j;
+        int ab;
+        const uint32_t b = (uint32_t)tm_find2<4096, NT>(h, need - ab_tot, wsum, bc, ab);
+        const int nb = (int)h[tm_pos<4096, NT>(b)];
+        ab_tot += ab;
+        b0 += b << s;
+        if (nb <= stop || s == 0) {
+            base = b0;
+            sh = s;
+            above = ab_tot;
+            inbin = nb;
+            break;
         }
+        s = s > 12 ? s - 12 : 0;
+        __syncthreads();  // h has been read before it is cleared
+        for (int i = tid; i < 4096; i += NT) h[i] = 0;
+        __syncthreads();
     }
 }
 
-__global__ __launch_bounds__(kTfThreads) void k_topkm_final(int64_t T, int64_t n_cols, const int64_t* __restrict__ pos,
-                                                            int m, int k, void* ws, int32_t* __restrict__ idx) {
-    constexpr int NT = kTfThreads;
+// j-th largest (1 <= j <= 8) of 8 values held in registers: the maximum, or a
+// descending sorting network (19 compare-exchanges) and a select
+__device__ __forceinline__ uint32_t jth_largest8(const uint32_t* v, int j) {
+    if (j == 1) {
+        uint32_t r = v[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) r = max(r, v[i]);
+        return r;
+    }
+    uint32_t a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = v[i];
+    constexpr int net[19][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}, {0, 4}, {1, 5}, {2, 6}, {3, 7}, {0, 1}, {2, 3},
+                                {4, 5}, {6, 7}, {2, 4}, {3, 5}, {1, 4}, {3, 6}, {1, 2}, {3, 4}, {5, 6}};
+#pragma unroll
+    for (int c = 0; c < 19; ++c) {
+        const uint32_t x = a[net[c][0]], y = a[net[c][1]];
+        a[net[c][0]] = max(x, y);
+        a[net[c][1]] = min(x, y);
+    }
+    uint32_t r = a[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) r = j == i + 1 ? a[i] : r;
+    return r;
+}
+
+struct TcRec {  // per (row, slice): candidates written (may exceed the slice), tau, the row's largest key
+    uint32_t n, tau, hi, pad;
+};
+
+__global__ __launch_bounds__(kTcThreads) void k_topk_cand(const float* __restrict__ scores, int64_t n_cols,
+                                                          const int64_t* __restrict__ pos, int m, int k,
+                                                          const uint32_t* __restrict__ summ, int S, int cap,
+                                                          TcRec* __restrict__ recs, uint64_t* __restrict__ cands) {
+    constexpr int NT = kTcThreads, NW = NT / 64, CH = kTcChunks, RC = NT * CH;  // RC chunks in registers
+    constexpr int GS = kTopkGroup;
     __shared__ uint32_t h[4096];
-    __shared__ uint32_t bm[kBitmapWords];  // row bitmap, or the index list to sort
-    __shared__ uint64_t cl[kCandLds];      // candidates
-    __shared__ uint32_t tie[kTieLds];      // indices of keys equal to the threshold
-    __shared__ int wsum[NT / 64];
+    __shared__ uint32_t glist[2048];
+    __shared__ int wsum[NW];
+    __shared__ uint32_t red[2 * NW];
     __shared__ int bc[4];
-    __shared__ uint32_t lctr[3];
-    const int tid = threadIdx.x;
-    const int64_t t = blockIdx.x;
-    const int64_t nv = row_visible(pos, t, m, n_cols);
-    int32_t* out = idx + t * (int64_t)k;
-    if (nv <= k) return;  // written by the collect pass
-    TmRow r = tm_row(ws, T, t, n_cols);
-    const int n_cand = (int)r.ctr[0];
-    const int64_t nwords = (nv + 31) / 32;
-    const bool use_bm = nwords <= kBitmapWords;  // kBitmapWords is a multiple of NT
-    // bitmap word w belongs to thread w / perw and sits at (w % perw) * NT + w / perw
-    const uint32_t perw = (uint32_t)((nwords + NT - 1) / NT);
-    if (use_bm)
-        for (uint32_t i = tid; i < perw * NT; i += NT) bm[i] = 0;
+    __shared__ uint32_t lctr[2];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t t = blockIdx.y;
+    const int s = blockIdx.x;
+    const float* row = scores + t * n_cols;
+    const int64_t ng_all = topk_groups(n_cols);
+    const uint32_t* gs = summ + t * ng_all;
+    // chunk c of thread tid = groups [8 (c NT + tid), +8); the first CH chunks are requested first
+    const bool gvec = (((uintptr_t)gs) & 15) == 0;
+    uint32_t gv[CH][8];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int64_t g0 = (int64_t)(c * NT + tid) * 8;
+        if (gvec && g0 + 8 <= ng_all) {
+            const uint4 a = ((const uint4*)(gs + g0))[0], b = ((const uint4*)(gs + g0))[1];
+            gv[c][0] = a.x, gv[c][1] = a.y, gv[c][2] = a.z, gv[c][3] = a.w;
+            gv[c][4] = b.x, gv[c][5] = b.y, gv[c][6] = b.z, gv[c][7] = b.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) gv[c][i] = g0 + i < ng_all ? gs[g0 + i] : 0u;
+        }
+    }
     if (tid < 2) lctr[tid] = 0;
     for (int i = tid; i < 4096; i += NT) h[i] = 0;
+    const int nv = (int)row_visible(pos, t, m, n_cols);
+    if (nv <= k) return;  // written by k_topk_pick
+    const int ngv = (nv + GS - 1) / GS;  // groups holding visible columns
+    const int nch = (ngv + 7) / 8;
+    // visit every visible group maximum: chunks held in registers, the rest re-read
+    auto for_groups = [&](auto fn) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int g0 = (c * NT + tid) * 8;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (g0 + i < ngv) fn(gv[c][i]);
+        }
+        for (int c = RC + tid; c < nch; c += NT)
+            for (int i = 0; i < 8; ++i)
+                if (c * 8 + i < ngv) fn(gs[c * 8 + i]);
+    };
+
+    // ---- hi = the row's largest key; lo <= the k-th largest group maximum: over the chunks
+    //      held in registers whose 8 groups are all visible, the smallest of each one's j-th
+    //      largest, j = ceil(k / #chunks) (those values come from >= k distinct groups) ----
+    uint32_t hi, lo;
+    {
+        uint32_t mx = 0;
+        for_groups([&](uint32_t x) { mx = max(mx, x); });
+        const int n_full = (ngv < RC * 8 ? ngv : RC * 8) / 8;
+        const int j = n_full > 0 ? (k + n_full - 1) / n_full : 9;
+        uint32_t mn = j > 8 ? 0u : 0xFFFFFFFFu;
+        if (j <= 8) {
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+                if (c * NT + tid < n_full) mn = min(mn, jth_largest8(gv[c], j));
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+            mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+        }
+        if (lane == 0) {
+            red[wave] = mx;
+            red[NW + wave] = mn;
+        }
+        __syncthreads();
+        hi = red[0];
+        lo = red[NW];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {
+            hi = max(hi, red[w]);
+            lo = min(lo, red[NW + w]);
+        }
+    }
+
+    // ---- tau (h was cleared before the barrier above) ----
+    uint32_t tau = 0;
+    if (ngv >= k) {
+        int sh, ab, nb;
+        hist_descend<NT>(for_groups, lo, hi, k, 64, h, wsum, bc, tau, sh, ab, nb);
+    }
+
+    // ---- this slice's groups whose maximum is >= tau (any order) ----
+    const int q0 = (int)((int64_t)ngv * s / S), q1 = (int)((int64_t)ngv * (s + 1) / S);
+    for (int q = q0 + tid; q < q1; q += NT) {
+        const uint32_t g = gs[q];
+        if (g >= tau) {
+            const uint32_t o = atomicAdd(&lctr[0], 1u);
+            if (o < 2048u) glist[o] = (uint32_t)q;
+        }
+    }
+    __syncthreads();
+    const int nq = (int)lctr[0];
+    uint64_t* out = cands + ((int64_t)t * S + s) * cap;
+    bool over = nq > 2048;
+    if (!over) {
+        // ---- keys >= tau of the listed groups, 8 lanes x 16 bytes per group ----
+        const bool vec = ((uintptr_t)row & 15) == 0;
+        constexpr int B = 4;
+        for (int u0 = 0; u0 < nq * 8; u0 += B * NT) {
+            uint32_t key[B][4];
+            int col[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const int u = u0 + b * NT + tid;
+                col[b] = u < nq * 8 ? (int)glist[u >> 3] * GS + (u & 7) * 4 : nv;
+                if (vec && col[b] + 4 <= nv) {
+                    const float4 x = *(const float4*)(row + col[b]);
+                    key[b][0] = f32_order_key(x.x);
+                    key[b][1] = f32_order_key(x.y);
+                    key[b][2] = f32_order_key(x.z);
+                    key[b][3] = f32_order_key(x.w);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) key[b][e] = col[b] + e < nv ? f32_order_key(row[col[b] + e]) : 0u;
+                }
+            }
+            int c = 0;
+#pragma unroll
+            for (int b = 0; b < B; ++b)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) c += (col[b] + e < nv && key[b][e] >= tau) ? 1 : 0;
+            const int x = wave_incl_scan(c);
+            uint32_t base = 0;
+            if (lane == 63) base = atomicAdd(&lctr[1], (uint32_t)x);
+            uint32_t slot = (uint32_t)__shfl((int)base, 63) + (uint32_t)(x - c);
+#pragma unroll
+            for (int b = 0; b < B; ++b)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (col[b] + e < nv && key[b][e] >= tau) {
+                        if (slot < (uint32_t)cap) out[slot] = ((uint64_t)key[b][e] << 32) | (uint32_t)~(uint32_t)(col[b] + e);
+                        ++slot;
+                    }
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        TcRec r;
+        r.n = over ? 0xFFFFFFFFu : lctr[1];
+        r.tau = tau;
+        r.hi = hi;
+        r.pad = 0;
+        recs[t * S + s] = r;
+    }
+}
+
+__global__ __launch_bounds__(kTopkThreads) void k_topk_pick(const float* __restrict__ scores, int64_t n_cols,
+                                                            const int64_t* __restrict__ pos, int m, int k, int S,
+                                                            int cap, const TcRec* __restrict__ recs,
+                                                            const uint64_t* __restrict__ cands,
+                                                            int32_t* __restrict__ idx) {
+    constexpr int NT = kTopkThreads, NW = NT / 64;
+    __shared__ uint32_t h[4096];
+    __shared__ __align__(16) uint32_t big[2 * kTqCand + kBitmapWords];  // candidates, then the row bitmap
+    __shared__ uint64_t tie[kTieLds];
+    __shared__ int wsum[2 * NW];
+    __shared__ int bc[4];
+    __shared__ uint32_t lctr[4];
+    __shared__ uint32_t scnt[2 * NW];
+    uint64_t* cl = (uint64_t*)big;
+    uint32_t* bm = big + 2 * kTqCand;  // row bitmap, or the list of winners to sort
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t t = blockIdx.x;
+    const float* row = scores + t * n_cols;
+    const int nv = (int)row_visible(pos, t, m, n_cols);
+    int32_t* out = idx + t * (int64_t)k;
+    if (nv <= k) {
+        for (int a = tid; a < k; a += NT) out[a] = a < nv ? a : -1;
+        return;
+    }
+    // slice records and the first 128 candidates of each slice are requested together
+    // (wave w: slices w and w + NW; S <= 2 NW, kSliceCap >= 128)
+    uint64_t pre[2][2];
+    uint32_t rn[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int s = wave + i * NW;
+        rn[i] = 0;
+        pre[i][0] = pre[i][1] = 0;
+        if (s < S) {
+            const uint64_t* src = cands + ((int64_t)t * S + s) * cap;
+            const TcRec r = recs[t * S + s];
+            pre[i][0] = src[lane];
+            pre[i][1] = src[64 + lane];
+            rn[i] = r.n;
+            if (lane == 0) scnt[s] = r.n;
+            if (s == 0 && lane == 0) {
+                lctr[2] = r.tau;
+                lctr[3] = r.hi;
+            }
+        }
+    }
+    const int nwords = (nv + 31) / 32;
+    const bool use_bm = nwords <= kBitmapWords;  // kBitmapWords is a multiple of NT
+    // bitmap word w belongs to thread w / perw and sits at (w % perw) * NT + w / perw
+    const int perw = (nwords + NT - 1) / NT;
+    if (use_bm)
+        for (int i = tid; i < perw * NT; i += NT) bm[i] = 0;
+    for (int i = tid; i < 4096; i += NT) h[i] = 0;
+    if (tid < 2) lctr[tid] = 0;
+    __syncthreads();
+    // offsets of the slices: one wave-wide scan of the counts (S <= 64)
+    const uint32_t sn = lane < S ? scnt[lane] : 0u;
+    const bool sbad = sn > (uint32_t)cap;
+    const int sx = wave_incl_scan(sbad ? 0 : (int)sn);
+    const int n_cand = __shfl(sx, 63);
+    int off[2];
+    off[0] = __shfl(sx - (int)sn, wave & 63);
+    off[1] = __shfl(sx - (int)sn, (wave + NW) & 63);
+    if (__ballot(sbad) != 0 || n_cand > kTqCand) {
+        row_select(row, nv, k, out, h, big, 2 * kTqCand + kBitmapWords, wsum, bc);
+        return;
+    }
+    const uint32_t tau = lctr[2], hi = lctr[3];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int s = wave + i * NW;
+        if (s >= S) continue;
+        const int n = (int)rn[i];
+        if (lane < n) cl[off[i] + lane] = pre[i][0];
+        if (64 + lane < n) cl[off[i] + 64 + lane] = pre[i][1];
+        const uint64_t* src = cands + ((int64_t)t * S + s) * cap;
+        for (int j = 128 + lane; j < n; j += 64) cl[off[i] + j] = src[j];
+    }
     auto mark = [&](uint32_t j) {
         if (use_bm) {
-            if (j < (uint64_t)nv) {
-                const uint32_t wd = j >> 5;
-                atomicOr(&bm[(wd % perw) * NT + wd / perw], 1u << (j & 31));
-            }
+            const uint32_t wd = j >> 5;
+            atomicOr(&bm[(wd % perw) * NT + wd / perw], 1u << (j & 31));
         } else {
             const uint32_t o = atomicAdd(&lctr[1], 1u);
             if (o < (uint32_t)k) bm[o] = j;
         }
     };
-    // candidates into LDS (batched loads), when they fit
-    const bool cand_lds = n_cand <= kCandLds;
-    if (cand_lds) {
-        for (int i0 = 0; i0 < n_cand; i0 += NT * 4) {
-            uint64_t v[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i = i0 + u * NT + tid;
-                v[u] = i < n_cand ? r.cand[i] : 0;
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i = i0 + u * NT + tid;
-                if (i < n_cand) cl[i] = v[u];
-            }
-        }
-    }
     __syncthreads();
-    auto cand_at = [&](int i) -> uint64_t { return cand_lds ? cl[i] : r.cand[i]; };
-    // radix select of the k-th largest candidate key: 12, 12, 8 bits
-    for (int i = tid; i < n_cand; i += NT) atomicAdd(&h[tm_pos<4096, NT>((uint32_t)(cand_at(i) >> 52))], 1u);
-    __syncthreads();
-    int above1;
-    const uint32_t b1 = (uint32_t)tm_find<4096, NT>(h, k, wsum, bc, above1);
-    for (int i = tid; i < 4096; i += NT) h[i] = 0;
-    __syncthreads();
+
+    // ---- the k-th largest candidate: a window holding it, then rank inside the window ----
+    uint32_t wbase;
+    int wsh, above, nb;
+    hist_descend<NT>([&](auto fn) { for (int i = tid; i < n_cand; i += NT) fn((uint32_t)(cl[i] >> 32)); }, tau, hi, k,
+                     kTieLds, h, wsum, bc, wbase, wsh, above, nb);
+    const uint64_t wtop = (uint64_t)wbase + ((uint64_t)1 << wsh);
+    const int need = k - above;  // >= 1 winners inside the window
     for (int i = tid; i < n_cand; i += NT) {
-        const uint32_t key = (uint32_t)(cand_at(i) >> 32);
-        if ((key >> 20) == b1) atomicAdd(&h[tm_pos<4096, NT>((key >> 8) & 0xFFFu)], 1u);
-    }
-    __syncthreads();
-    int above2;
-    const int need = k - above1;
-    const uint32_t b2 = (uint32_t)tm_find<4096, NT>(h, need, wsum, bc, above2);
-    for (int i = tid; i < 256; i += NT) h[i] = 0;
-    __syncthreads();
-    const uint32_t p2 = (b1 << 12) | b2;
-    for (int i = tid; i < n_cand; i += NT) {
-        const uint32_t key = (uint32_t)(cand_at(i) >> 32);
-        if ((key >> 8) == p2) atomicAdd(&h[tm_pos<256, NT>(key & 0xFFu)], 1u);
-    }
-    __syncthreads();
-    int above3;
-    const uint32_t b3 = (uint32_t)tm_find<256, NT>(h, need - above2, wsum, bc, above3);
-    const uint32_t thr = (p2 << 8) | b3;
-    const int need_eq = need - above2 - above3;  // >= 1 keys equal to thr, lowest indices first
-    for (int i = tid; i < n_cand; i += NT) {
-        const uint64_t c = cand_at(i);
+        const uint64_t c = cl[i];
         const uint32_t key = (uint32_t)(c >> 32);
-        if (key > thr) mark(~(uint32_t)c);
-        else if (key == thr) atomicAdd(&lctr[0], 1u);
+        if ((uint64_t)key >= wtop) mark(~(uint32_t)c);
+        else if (key >= wbase && nb <= kTieLds) tie[atomicAdd(&lctr[0], 1u)] = c;
     }
     __syncthreads();
-    uint32_t idx_lim = 0xFFFFFFFFu;  // equal keys are taken up to this index
-    const int n_eq = (int)lctr[0];
-    if (n_eq > need_eq && n_eq <= kTieLds) {
-        // few equal keys: list them, rank each by index, keep the need_eq lowest
-        if (tid == 0) lctr[2] = 0;
-        __syncthreads();
-        for (int i = tid; i < n_cand; i += NT) {
-            const uint64_t c = cand_at(i);
-            if ((uint32_t)(c >> 32) == thr) tie[atomicAdd(&lctr[2], 1u)] = ~(uint32_t)c;
-        }
-        __syncthreads();
-        for (int i = tid; i < n_eq; i += NT) {
-            const uint32_t ji = tie[i];
+    if (nb <= kTieLds) {
+        // (key desc, column asc) is (key << 32 | ~column) desc: rank each window entry directly
+        for (int i = tid; i < nb; i += NT) {
+            const uint64_t e = tie[i];
             int rank = 0;
-            for (int q = 0; q < n_eq; ++q) rank += tie[q] < ji ? 1 : 0;
-            if (rank == need_eq - 1) bc[2] = (int)ji;
+            for (int q = 0; q < nb; ++q) rank += tie[q] > e ? 1 : 0;
+            if (rank < need) mark(~(uint32_t)e);
         }
-        __syncthreads();
-        idx_lim = (uint32_t)bc[2];
-        __syncthreads();
-    } else if (n_eq > need_eq) {
-        // the need_eq-th smallest index among equal keys (31-bit indices, 3 passes of 11 bits)
+    } else {
+        // a single key value (wbase) held by more than kTieLds candidates: the need lowest
+        // columns among them (3 passes of 11 bits)
+        const uint32_t thr = wbase;
         uint32_t pre = 0, pm = 0;
-        int nl = need_eq;
+        int nl = need;
         for (int sh = 22; sh >= 0; sh -= 11) {
             for (int i = tid; i < 2048; i += NT) h[i] = 0;
             __syncthreads();
             for (int i = tid; i < n_cand; i += NT) {
-                const uint64_t c = cand_at(i);
+                const uint64_t c = cl[i];
                 if ((uint32_t)(c >> 32) != thr) continue;
                 const uint32_t jx = ~(uint32_t)c;
-                if ((jx & pm) == pre) atomicAdd(&h[tm_pos<2048, NT>(2047 - ((jx >> sh) & 0x7FF))], 1u);  // smaller index, higher bin
+                if ((jx & pm) == pre) atomicAdd(&h[tm_pos<2048, NT>(2047 - ((jx >> sh) & 0x7FF))], 1u);  // lower, higher bin
             }
             __syncthreads();
             int ab;
@@ -565,31 +735,31 @@ __global__ __launch_bounds__(kTfThreads) void k_topkm_final(int64_t T, int64_t n
             pre |= bn << sh;
             pm |= 0x7FFu << sh;
         }
-        idx_lim = pre;
-    }
-    for (int i = tid; i < n_cand; i += NT) {
-        const uint64_t c = cand_at(i);
-        if ((uint32_t)(c >> 32) == thr && ~(uint32_t)c <= idx_lim) mark(~(uint32_t)c);
+        for (int i = tid; i < n_cand; i += NT) {
+            const uint64_t c = cl[i];
+            if ((uint32_t)(c >> 32) == thr && ~(uint32_t)c <= pre) mark(~(uint32_t)c);
+        }
     }
     __syncthreads();
+
     if (use_bm) {
         // thread t owns words t*perw .. t*perw+perw-1 (reads free of bank conflicts)
         int cnt = 0;
-        for (uint32_t i = 0; i < perw; ++i) cnt += __popc(bm[i * NT + tid]);
+        for (int i = 0; i < perw; ++i) cnt += __popc(bm[i * NT + tid]);
         int tot;
         int o = tm_scan<NT>(cnt, wsum, tot);
-        for (uint32_t i = 0; i < perw; ++i) {
+        for (int i = 0; i < perw; ++i) {
             uint32_t b = bm[i * NT + tid];
-            const int64_t wi = (int64_t)tid * perw + i;
+            const int wi = tid * perw + i;
             while (b) {
                 const int bit = __builtin_ctz(b);
-                if (o < k) out[o] = (int32_t)(wi * 32 + bit);
+                if (o < k) out[o] = wi * 32 + bit;
                 ++o;
                 b &= b - 1;
             }
         }
     } else {
-        // bitonic sort of the k marked indices
+        // bitonic sort of the k marked columns
         int np = 1;
         while (np < k) np <<= 1;
         for (int i = k + tid; i < np; i += NT) bm[i] = 0xFFFFFFFFu;
@@ -597,21 +767,19 @@ __global__ __launch_bounds__(kTfThreads) void k_topkm_final(int64_t T, int64_t n
         for (int size = 2; size <= np; size <<= 1)
             for (int stride = size >> 1; stride > 0; stride >>= 1) {
                 for (int i = tid; i < np / 2; i += NT) {
-                    const int lo = 2 * i - (i & (stride - 1));
-                    const int hi = lo + stride;
-                    const bool asc = (lo & size) == 0;
-                    const uint32_t a = bm[lo], b = bm[hi];
+                    const int lo2 = 2 * i - (i & (stride - 1));
+                    const int hi2 = lo2 + stride;
+                    const bool asc = (lo2 & size) == 0;
+                    const uint32_t a = bm[lo2], b = bm[hi2];
                     if ((a > b) == asc) {
-                        bm[lo] = b;
-                        bm[hi] = a;
+                        bm[lo2] = b;
+                        bm[hi2] = a;
                     }
                 }
                 __syncthreads();
             }
         for (int a = tid; a < k; a += NT) out[a] = (int32_t)bm[a];
     }
-    // ---- leave the row's counters zero for the next call ----
-    if (tid < 16) r.ctr[tid] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -831,42 +999,47 @@ __global__ __launch_bounds__(kTsThreads) void k_topk_stream(const float* __restr
     }
 }
 
-static bool topk_multi(int64_t T, int64_t n_cols) { return T < kTopkMaxRows && n_cols > 4096; }
+// few rows longer than k_topk_stream takes: selection from the row summary
+// few rows longer than k_topk_stream takes: selection from the row summary
+static bool topk_summ(int64_t T, int64_t n_cols) { return T < kTopkMaxRows && n_cols > kTsMaxCols; }
+// k_topk_cand workgroups per row (about 256 in all) and candidates each may write
+static int topk_slices(int64_t T) { return T >= 256 ? 1 : (int)(256 / T < 32 ? 256 / T : 32); }  // <= 32
+constexpr int kSliceCap = 4096;  // >= 128
 
-size_t topk_workspace_bytes(int64_t T, int64_t n_cols, int) {
-    if (!topk_multi(T, n_cols)) return 0;
-    return topk_ws_cand_off(T, n_cols) + (size_t)T * n_cols * 8;
+// workspace: summaries [T][groups], slice records [T][S], candidates [T][S][kSliceCap]
+static size_t ws_recs_off(int64_t T, int64_t n_cols) { return ((size_t)T * topk_groups(n_cols) * 4 + 255) & ~(size_t)255; }
+static size_t ws_cands_off(int64_t T, int64_t n_cols) {
+    return (ws_recs_off(T, n_cols) + (size_t)T * topk_slices(T) * sizeof(TcRec) + 255) & ~(size_t)255;
 }
 
-int64_t topk_chunk(int64_t T, int64_t n_cols) {
-    int64_t chunk = (n_cols * T + 511) / 512;
-    chunk = ((chunk + 2047) / 2048) * 2048;
-    if (chunk < 2048) chunk = 2048;
-    if (chunk > 16384) chunk = 16384;
-    return chunk;
+size_t topk_workspace_bytes(int64_t T, int64_t n_cols, int) {
+    if (!topk_summ(T, n_cols)) return 0;
+    return ws_cands_off(T, n_cols) + (size_t)T * topk_slices(T) * kSliceCap * 8;
 }
 
 hipError_t launch_topk(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos, int m, int k, int32_t* idx,
                        void* ws, bool prepared, hipStream_t st) {
     if (T == 0) return hipSuccess;
-    if (!topk_multi(T, n_cols)) {
-        if (n_cols <= kTsMaxCols)
-            hipLaunchKernelGGL(k_topk_stream, dim3((unsigned)T), dim3(kTsThreads), 0, st, scores, n_cols, pos, m, k, idx);
-        else
-            hipLaunchKernelGGL(k_topk_row, dim3((unsigned)T), dim3(kTopkThreads), 0, st, scores, n_cols, pos, m, k, idx);
-        return hipGetLastError();
+    if (topk_summ(T, n_cols)) {
+        uint32_t* summ = (uint32_t*)ws;
+        TcRec* recs = (TcRec*)((char*)ws + ws_recs_off(T, n_cols));
+        uint64_t* cands = (uint64_t*)((char*)ws + ws_cands_off(T, n_cols));
+        const int S = topk_slices(T);
+        if (!prepared)
+            hipLaunchKernelGGL(k_topk_gmax, dim3((unsigned)((n_cols + kTgThreads * 8 - 1) / (kTgThreads * 8)), (unsigned)T),
+                               dim3(kTgThreads), 0, st, scores, n_cols, pos, m, k, summ);
+        hipLaunchKernelGGL(k_topk_cand, dim3((unsigned)S, (unsigned)T), dim3(kTcThreads), 0, st, scores, n_cols, pos, m, k,
+                           summ, S, kSliceCap, recs, cands);
+        hipLaunchKernelGGL(k_topk_pick, dim3((unsigned)T), dim3(kTopkThreads), 0, st, scores, n_cols, pos, m, k, S,
+                           kSliceCap, recs, cands, idx);
+    } else if (n_cols <= kTsMaxCols) {
+        hipLaunchKernelGGL(k_topk_stream, dim3((unsigned)T), dim3(kTsThreads), 0, st, scores, n_cols, pos, m, k, idx);
+    } else {
+        hipLaunchKernelGGL(k_topk_row, dim3((unsigned)T), dim3(kTopkThreads), 0, st, scores, n_cols, pos, m, k, idx);
     }
-    const int64_t chunk = topk_chunk(T, n_cols);
-    const int nchunk = (int)((n_cols + chunk - 1) / chunk);
-    if (!prepared)
-        hipLaunchKernelGGL(k_topkm_gmax, dim3((unsigned)((n_cols + kTmThreads * 8 - 1) / (kTmThreads * 8)), (unsigned)T),
-                           dim3(kTmThreads), 0, st, scores, T, n_cols, pos, m, k, ws);
-    hipLaunchKernelGGL(k_topkm_collect, dim3((unsigned)nchunk, (unsigned)T), dim3(kTmThreads), 0, st, scores, T, n_cols,
-                       pos, m, k, chunk, ws, idx);
-    hipLaunchKernelGGL(k_topkm_final, dim3((unsigned)T), dim3(kTfThreads), 0, st, T, n_cols, pos, m, k, ws, idx);
     return hipGetLastError();
 }
 
-bool topk_uses_summary(int64_t T, int64_t n_cols) { return topk_multi(T, n_cols); }
+bool topk_uses_summary(int64_t T, int64_t n_cols) { return topk_summ(T, n_cols); }
 
 }  // namespace csa

@@ -143,7 +143,7 @@ int csa_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t 
  *   topk_ws  optional (NULL, 0 to skip): the workspace of the csa_topk call
  *            that will read these scores.  When given, the indexer also
  *            writes the selection's row summary into it (for shapes whose
- *            selection uses one: the largest score of every 128-column
+ *            selection uses one: the largest score of every 32-column
  *            group), and that csa_topk call passes CSA_TOPK_PREPARED so the
  *            selection skips its own pass over the scores.  Results are the
  *            same bit for bit either way.
@@ -166,9 +166,9 @@ int csa_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, c
  *   scores [T][n_cols] fp32 (NaN not supported);  idx [T][k] int32
  *   1 <= k <= 2048;  n_cols < 2^31
  * Workspace: csa_topk_workspace(T, n_cols, k) bytes (may be 0), 256-byte
- * aligned, ZERO-FILLED before its first use; every call leaves it
- * zero-filled again, so one buffer serves any sequence of calls (any shapes)
- * on one stream.  Calls that share a workspace must not run concurrently.
+ * aligned; its contents need no initialisation, and one buffer serves any
+ * sequence of calls (any shapes) on one stream.  Calls that share a
+ * workspace must not run concurrently.
  * flags: 0, or CSA_TOPK_PREPARED when the preceding csa_index_scores call
  * for these scores was given this workspace (it wrote the row summary).
  */

@@ -4,7 +4,7 @@ One step = the CSA decode hot path for a batch of 4 sequences, each with a
 1,048,576-token context (262,144 compressed entries at m=4):
     csa_index_scores (MXFP4 indexer over every entry; it also writes the
                       selection's row summary: the largest score of every
-                      128-column group)
+                      32-column group)
  -> csa_topk (k = 1024)
  -> csa_sparse_mqa (64 query heads over the 1024 selected entries + a
     128-token window, d = 512).
@@ -34,7 +34,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (scaled by a 256 MiB copy: fetch x2.0,
 # write x1.0; see profiles/csa_decode_1m_hbm_counters.md), valid for the kernel
 # source with this SHA-256 only.
-INDEX_TRAFFIC = {"sha256": "2b06a218d792963db7c9247984bf7082998aceea6e6a5999b9422d55f8e1bce5", "bytes": 75654667}
+INDEX_TRAFFIC = {"sha256": "acf9b0f6d8f9e6d8c27dfccaa6eb35806443b1d731ae2b762ec7c288ace6f076", "bytes": 75736058}
 
 
 def log(msg):
@@ -54,18 +54,19 @@ def index_bytes_per_query(N, h_i, d_i):
     """Algorithmic HBM bytes of csa_index_scores per query row: every MXFP4 key
     (d_i/2 data + d_i/32 scale bytes), the query (h_i keys' worth + fp32
     weights), the fp32 score row written and the selection's row summary (one
-    4-byte key per 128 columns)."""
+    4-byte key per 32 columns)."""
     key = d_i // 2 + d_i // 32
-    return N * key + h_i * key + h_i * 4 + N * 4 + (N + 127) // 128 * 4
+    return N * key + h_i * key + h_i * 4 + N * 4 + (N + 31) // 32 * 4
 
 
 def step_bytes_per_query(N, h_i, d_i, k, W, H, d):
     """Algorithmic HBM bytes of the whole decode step per query: indexer bytes,
-    the score row read back by top-k, k indices, the gathered entries
+    what the summary-based selection reads back (the row summary and k
+    32-column groups of scores), k indices, the gathered entries
     (k + W) x (d-64 + 128 + 4) B, the bf16 query and fp32 output + lse."""
     entry = (d - 64) + 64 * 2 + 4
-    return (index_bytes_per_query(N, h_i, d_i) + N * 4 + k * 4 * 2 + (k + W) * entry + H * d * 2 + H * d * 4
-            + H * 4)
+    return (index_bytes_per_query(N, h_i, d_i) + (N + 31) // 32 * 4 + k * 32 * 4 + k * 4 * 2 + (k + W) * entry
+            + H * d * 2 + H * d * 4 + H * 4)
 
 
 class DecodeSet:

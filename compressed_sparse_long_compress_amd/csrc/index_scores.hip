@@ -277,8 +277,9 @@ hipError_t launch_index_scores(const uint8_t* q, const uint8_t* q_scale, const f
                                uint32_t* gmax, hipStream_t st) {
     if (T == 0 || n_cols == 0) return hipSuccess;
     if (T <= 64 || gmax) {
-        // aim for >= 1024 workgroups; each wave handles 128 keys per step
-        int64_t chunk = (n_cols * T + 1023) / 1024;
+        // aim for >= 2048 workgroups (one 128-key step per wave at the 1M-context decode shape);
+        // each wave handles 128 keys per step
+        int64_t chunk = (n_cols * T + 2047) / 2048;
         chunk = ((chunk + 511) / 512) * 512;
         if (chunk < 512) chunk = 512;
         if (chunk > 16384) chunk = 16384;

@@ -420,10 +420,11 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
 // part's scale reference) is that tile's largest entry scale.  P = exp(s -
 // m_ref) and P * scale_j / S_ref then stay below e^kLazy * kSRatio < 65504 as
 // long as no later tile's max exceeds m_ref + kLazy and no later scale
-// exceeds kSRatio * S_ref; a tile that breaks either bound restarts the
-// split with the references raised to everything seen so far (tiles already
-// seen can then never break them again).  The output accumulators are thus
-// only ever touched by MFMAs.
+// exceeds kSRatio * S_ref.  A tile that breaks either bound sets a flag; the
+// pass still runs to its end (its output is then discarded), collecting the
+// maxima of every tile, and a second pass with those as the references
+// (which no tile can break) produces the output.  The output accumulators
+// are thus only ever touched by MFMAs.
 // ---------------------------------------------------------------------------
 constexpr float kLazy = 8.f;     // e^8 ~ 2981
 constexpr float kSRatio = 16.f;  // 2981 * 16 < 65504
@@ -635,7 +636,7 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
 
     v4f acc[4][DT];
     float m_ref = -INFINITY, l_run = 0.f, s_ref = 0.f;
-    float m_seen = -INFINITY, s_seen = 0.f;  // maxima over every tile seen (restart references)
+    float m_seen = -INFINITY, s_seen = 0.f;  // maxima over every tile seen (second-pass references)
     int64_t nraw = 0;  // this thread's position in the next batch: selected index, then resolved
     Res nres{g_zero_entry, g_zero_entry + DN, nullptr, false};
     float nscl = 0.f;
@@ -768,10 +769,11 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
         }
     };
 
-    // Per tile, two barriers: [QK(j), softmax(j) -> P]  sync  [stage(j+1), load j+2, PV(j)]  sync.
-    // Tile t lives in kv[t % 3].
-    for (;;) {
-        // ---- (re)start: batch 0 of the positions, tile 0 staged, tile 1 in flight ----
+    // One pass over the split.  Per tile, two barriers: [QK(j), softmax(j) -> P]  sync
+    // [stage(j+1), load j+2, PV(j)]  sync.  Tile t lives in kv[t % 3].  Returns whether a tile
+    // broke the references (the pass's output is then discarded).  The loop has a single exit,
+    // so the output accumulators keep their registers and every PV MFMA runs in place.
+    auto run_pass = [&]() -> bool {
         {
             const Res r = resolve_at(u0 + tid, fetch(u0 + tid));
             publish(0, r, r.ok ? *r.sp : 0.f);
@@ -788,28 +790,26 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
         if (nt > 0) stage(0);
         if (nt > 1) issue(1);
         __syncthreads();
-        bool again = false;
-
         for (int j = 0; j < nt; ++j) {
             v4f sn[2], sr[2];
             qk(j, sn, sr);
             if (softmax(j, sn, sr)) sm.restart = 1;
             __syncthreads();
-            // a restart finishes this iteration first (its output is discarded): leaving the
-            // loop from the middle of the body makes the compiler shuttle the accumulators
-            again = sm.restart != 0;
             if (j + 1 < nt) stage(j + 1);
             if (j + 2 < nt) issue(j + 2);
             pv(j);
             batch_step(j);
             __syncthreads();
-            if (again) break;
         }
-        if (!again) break;
-        // every wave has read the flag (it broke out after the same barrier); clear it for the next attempt
+        return sm.restart != 0;
+    };
+    if (run_pass()) {
+        // a tile broke the references: run the split again with the maxima of every tile as the
+        // references (no tile can break them); every wave has read the flag before the last barrier
         m_seen = rows4_max(m_seen);
         __syncthreads();
         if (tid == 0) sm.restart = 0;
+        run_pass();
     }
 
     // ---- epilogue: lane holds heads 16 ht + 4 g4 + i at one dim of each of its dim tiles ----

@@ -447,8 +447,7 @@ struct __align__(16) Mqa64Smem {
     // two batches of resolved key-list positions: FP8-row and RoPE-row
     // addresses, entry scale (0 when masked) and visibility
     const uint8_t* kaddr[2][RB][2];
-    float kscl[2][RB];
-    int kval[2][RB];
+    float kscl[2][RB];  // entry scale, -1 for a masked position
     float cs[64];
     int restart;
 };
@@ -459,6 +458,13 @@ template <typename T>
 __device__ __forceinline__ T gload(const uint8_t* p) {
     return *(const __attribute__((address_space(1))) T*)(gptr_t)p;
 }
+
+// Workgroup barrier for hand-overs through LDS only: waits for this wave's LDS
+// operations but not for its global loads in flight (the fences of
+// __syncthreads would wait for those too, cutting short the prefetch of the
+// next tiles).  The memory clobber keeps the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ v4s lds_read_tr16(const _Float16* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
@@ -520,8 +526,7 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
     auto publish = [&](int b, const Res& r, float sc) {
         sm.kaddr[b][tid][0] = r.an;
         sm.kaddr[b][tid][1] = r.ar;
-        sm.kscl[b][tid] = sc;
-        sm.kval[b][tid] = r.ok;
+        sm.kscl[b][tid] = r.ok ? sc : -1.f;
     };
 
     if (tid < 32) {
@@ -680,34 +685,23 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // scores and P of tile j for head hq; returns whether a reference is exceeded
-    auto softmax = [&](int j, const v4f (&an)[2], const v4f (&ar)[2]) -> bool {
+    // entry scales of tile j: lane (l16, g4) holds keys 4 g4 + i and 16 + 4 g4 + i (read before QK)
+    auto tile_scales = [&](int j, float4& s0, float4& s1) {
         const float* tscl = sm.kscl[(j / TPB) & 1] + (j % TPB) * KT;
-        const int* tval = sm.kval[(j / TPB) & 1] + (j % TPB) * KT;
-        // tile max of the entry scales (the same in every wave)
-        float st_max;
-        {
-            const float4 a = *(const float4*)(tscl + 4 * (lane & 7));
-            st_max = fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w));
-            st_max = fmaxf(st_max, __shfl_xor(st_max, 1));
-            st_max = fmaxf(st_max, __shfl_xor(st_max, 2));
-            st_max = fmaxf(st_max, __shfl_xor(st_max, 4));
-        }
-        // lane (l16, g4) holds keys 4 g4 + i and 16 + 4 g4 + i
+        s0 = *(const float4*)(tscl + 4 * g4);
+        s1 = *(const float4*)(tscl + 16 + 4 * g4);
+    };
+    // scores and P of tile j for head hq; returns whether a reference is exceeded
+    auto softmax = [&](const float4& s0, const float4& s1, const v4f (&an)[2], const v4f (&ar)[2]) -> bool {
+        const float kscl[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
         float sv[8];
-        float kscl[8];
+        float st_max = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const float4 sc = *(const float4*)(tscl + ks * 16 + 4 * g4);
-            const int4 vl = *(const int4*)(tval + ks * 16 + 4 * g4);
-            const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
-            const int vlv[4] = {vl.x, vl.y, vl.z, vl.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                kscl[ks * 4 + i] = scv[i];
-                sv[ks * 4 + i] = vlv[i] ? sm_q * fmaf(scv[i], an[ks][i], ar[ks][i]) : -INFINITY;
-            }
+        for (int i = 0; i < 8; ++i) {
+            sv[i] = kscl[i] >= 0.f ? sm_q * fmaf(kscl[i], an[i >> 2][i & 3], ar[i >> 2][i & 3]) : -INFINITY;
+            st_max = fmaxf(st_max, kscl[i]);
         }
+        st_max = rows4_max(st_max);  // over the tile's 32 keys: the same in every lane and wave
         float mx = sv[0];
 #pragma unroll
         for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
@@ -755,17 +749,25 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
                 acc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dt < NN ? pnf : prf, vf[dt], acc[ht][dt], 0, 0, 0);
         }
     };
-    // next batch of positions: index load, then addresses and scale load, then publish (first used 3 tiles later)
-    auto batch_step = [&](int j) {
+    // Next batch of positions, one step per tile: index load (tile j % TPB == 1), row addresses
+    // (end of that tile), scale load (tile 2), publish (end of tile 2; first used 5 tiles later).
+    // Every load is issued at the start of a tile and consumed at its end, so no load but the
+    // tile prefetch is in flight across the loop's back edge (a pending load there makes the
+    // next tile wait for all of them before its first LDS read).
+    auto batch_begin = [&](int j) {
         const int b1 = j / TPB + 1;
         const int64_t u = u0 + (int64_t)b1 * RB + tid;
         if (b1 * TPB < nt) {
             if (j % TPB == 1) nraw = fetch(u);
-            if (j % TPB == 2) {
-                nres = resolve_at(u, nraw);
-                nscl = nres.ok ? *nres.sp : 0.f;
-            }
-            if (j % TPB == 3) publish(b1 & 1, nres, nscl);
+            if (j % TPB == 2) nscl = nres.ok ? gload<float>((const uint8_t*)nres.sp) : 0.f;  // global, not flat
+        }
+    };
+    auto batch_end = [&](int j) {
+        const int b1 = j / TPB + 1;
+        const int64_t u = u0 + (int64_t)b1 * RB + tid;
+        if (b1 * TPB < nt) {
+            if (j % TPB == 1) nres = resolve_at(u, nraw);
+            if (j % TPB == 2) publish(b1 & 1, nres, nscl);
         }
     };
 
@@ -773,10 +775,14 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
     // [stage(j+1), load j+2, PV(j)]  sync.  Tile t lives in kv[t % 3].  Returns whether a tile
     // broke the references (the pass's output is then discarded).  The loop has a single exit,
     // so the output accumulators keep their registers and every PV MFMA runs in place.
+    // One pass over the split.  Per tile, two barriers: [QK(j), softmax(j) -> P]  sync
+    // [stage(j+1), load j+2, PV(j)]  sync.  Tile t lives in kv[t % 3].  Returns whether a tile
+    // broke the references (the pass's output is then discarded).  The loop has a single exit,
+    // so the output accumulators keep their registers and every PV MFMA runs in place.
     auto run_pass = [&]() -> bool {
         {
             const Res r = resolve_at(u0 + tid, fetch(u0 + tid));
-            publish(0, r, r.ok ? *r.sp : 0.f);
+            publish(0, r, r.ok ? gload<float>((const uint8_t*)r.sp) : 0.f);
         }
         __syncthreads();
         if (nt > 0) issue(0);
@@ -792,14 +798,17 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
         __syncthreads();
         for (int j = 0; j < nt; ++j) {
             v4f sn[2], sr[2];
+            batch_begin(j);
+            float4 s0, s1;
+            tile_scales(j, s0, s1);
             qk(j, sn, sr);
-            if (softmax(j, sn, sr)) sm.restart = 1;
-            __syncthreads();
+            if (softmax(s0, s1, sn, sr)) sm.restart = 1;
+            lds_barrier();
             if (j + 1 < nt) stage(j + 1);
             if (j + 2 < nt) issue(j + 2);
             pv(j);
-            batch_step(j);
-            __syncthreads();
+            batch_end(j);
+            lds_barrier();
         }
         return sm.restart != 0;
     };

@@ -873,6 +873,438 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
     }
 }
 
+// ---------------------------------------------------------------------------
+// 64 query heads, d = 512, eight waves in two roles that run one tile apart
+// (two waves per SIMD, one of each role), so that the softmax and the LDS
+// reads of one role overlap the MFMAs of the other:
+//   waves 0-3 (scores): wave w computes S^T for heads 16w..16w+15 over all
+//       dims (query fp16 in AGPRs), then the softmax of tile i against the
+//       lazy references into P buffer i & 1;
+//   waves 4-7 (values): gather and stage tile i+1 (and issue tile i+2),
+//       then O += P V for tile i-1 over the FP8 dims [112 (w-4), +112) and
+//       the RoPE dims [448 + 16 (w-4), +16), reading P buffer (i-1) & 1.
+// One barrier per step; tiles, references and the second pass are those of
+// k_mqa64.  Each role's loop is its own branch, so the query registers of
+// one and the output accumulators of the other can share the register file.
+// ---------------------------------------------------------------------------
+template <int D>
+struct __align__(16) MqaWsSmem {
+    static constexpr int KS = D + 16;  // fp16 row stride of a staged tile
+    static constexpr int PS = KT + 8;  // fp16 row stride of P
+    _Float16 kv[3][KT * KS];           // tile t in kv[t % 3]
+    _Float16 pn[2][64 * PS];           // [tile & 1][head][K slot] P * scale_j / S_ref (FP8 dims)
+    _Float16 pr[2][64 * PS];           // [tile & 1][head][K slot] P (RoPE dims)
+    float mfin[64];                    // per head: reference max and sum of the pass (scores -> values)
+    float lfin[64];
+    float sfin;
+    const uint8_t* kaddr[2][RB][2];
+    float kscl[2][RB];  // entry scale, -1 for a masked position
+    float cs[64];
+    int restart;
+};
+
+template <int D>
+__global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q, const int32_t* __restrict__ seq,
+                                                 const int64_t* __restrict__ pos, const int32_t* __restrict__ idx,
+                                                 int k, int m, KvView comp, KvView win, int window, float sm_scale,
+                                                 RopeTab rt, int S, float* __restrict__ out, float* __restrict__ lse,
+                                                 float* __restrict__ part_o, float* __restrict__ part_ml) {
+    static_assert(D == 512, "the 64-head shape of the pages");
+    constexpr int H = 64;
+    using Sm = MqaWsSmem<D>;
+    constexpr int KS = Sm::KS;
+    constexpr int DN = D - 64;
+    constexpr int DSTEP = D / 32, NSTEP = DN / 32;  // QK steps of 32 dims
+    constexpr int NN = DN / 64, DT = NN + 1;        // PV 16-dim tiles per wave: NN FP8 tiles, then one RoPE tile
+    constexpr int CPN = DN / 16;                    // 16-byte chunks of an entry's FP8 part (RoPE part: 8)
+    constexpr int NCN = KT * CPN;                   // FP8 chunks of a tile
+    constexpr int NFULL = NCN / 256;                // whole FP8 chunks per value thread; the other NCN % 256 go by halves
+    constexpr int TPB = RB / KT;                    // tiles per batch of resolved positions
+    static_assert(RB == 256 && TPB >= 6, "one resolved position per value thread, a batch resolved 3+ tiles ahead");
+    static_assert(KT * 8 == 256 && NCN % 256 == 128, "per thread: NFULL FP8 chunks, one RoPE chunk, one FP8 half chunk");
+
+    __shared__ Sm sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool scores_role = wave < 4;
+    const int rw = wave & 3;      // wave index within the role
+    const int vt = tid & 255;     // thread index within the role
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int64_t t = blockIdx.x / S;
+    const int s = blockIdx.x % S;
+    const int64_t tp = pos[t];
+    const int32_t sq = seq[t];
+    const RowKeys rk = row_keys(tp, idx, k, m, window);
+    const int64_t u0 = rk.n * s / S, u1 = rk.n * (s + 1) / S;
+    const int nt = (int)((u1 - u0 + KT - 1) / KT);
+
+    auto fetch = [&](int64_t u) -> int64_t {
+        return (u < u1 && u < rk.n_c) ? (idx ? (int64_t)idx[t * k + u] : u) : 0;
+    };
+    struct Res {
+        const uint8_t* an;
+        const uint8_t* ar;
+        const float* sp;
+        bool ok;
+    };
+    auto resolve_at = [&](int64_t u, int64_t j) -> Res {
+        Res r{g_zero_entry, g_zero_entry + DN, nullptr, false};
+        if (u >= u1) return r;
+        if (u < rk.n_c) {
+            if (j < 0 || j >= rk.nv) return r;
+            const int64_t row = (int64_t)sq * comp.cap + (j % comp.cap);
+            return Res{comp.nope + row * DN, (const uint8_t*)(comp.rope + row * 64), comp.scale + row, true};
+        }
+        const int64_t p = rk.lo + (u - rk.n_c);
+        const int64_t row = (int64_t)sq * win.cap + (p % win.cap);
+        return Res{win.nope + row * DN, (const uint8_t*)(win.rope + row * 64), win.scale + row, true};
+    };
+    auto publish = [&](int b, const Res& r, float sc) {
+        sm.kaddr[b][vt][0] = r.an;
+        sm.kaddr[b][vt][1] = r.ar;
+        sm.kscl[b][vt] = r.ok ? sc : -1.f;
+    };
+
+    if (tid < 32) {
+        float c, sn;
+        angle_cs((double)tp, rt.theta[tid], c, sn);
+        sm.cs[2 * tid] = c;
+        sm.cs[2 * tid + 1] = sn;
+    }
+    if (tid == 0) sm.restart = 0;
+    __syncthreads();
+
+    float m_seen = -INFINITY, s_seen = 0.f;  // scores role: maxima over every tile seen (second-pass references)
+
+    // ---- values role: tile loads (global -> registers) and staging (registers -> LDS), as in k_mqa64 ----
+    v4i pre[NFULL > 0 ? NFULL : 1];
+    v4i pre_r;
+    v2u pre_h;
+    auto issue = [&](int j) {
+        const int b = (j / TPB) & 1, slot = (j % TPB) * KT;
+#pragma unroll
+        for (int i = 0; i < NFULL; ++i) {
+            const int c = vt + i * 256;
+            pre[i] = gload<v4i>(sm.kaddr[b][slot + c / CPN][0] + (c % CPN) * 16);
+        }
+        pre_r = gload<v4i>(sm.kaddr[b][slot + (vt >> 3)][1] + (vt & 7) * 16);
+        const int ch = 256 * NFULL + (vt >> 1);
+        pre_h = gload<v2u>(sm.kaddr[b][slot + ch / CPN][0] + (ch % CPN) * 16 + (vt & 1) * 8);
+    };
+    auto fp8x8_to_f16 = [](uint32_t lo, uint32_t hi) -> uint4 {
+        return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.f, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.f, true)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.f, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.f, true)));
+    };
+    auto stage = [&](int j) {
+        _Float16* kv = sm.kv[j % 3];
+#pragma unroll
+        for (int i = 0; i < NFULL; ++i) {
+            const int c = vt + i * 256;
+            const int part = c % CPN;
+            const uint4 lo = fp8x8_to_f16((uint32_t)pre[i][0], (uint32_t)pre[i][1]);
+            const uint4 hi = fp8x8_to_f16((uint32_t)pre[i][2], (uint32_t)pre[i][3]);
+            _Float16* dst = kv + (c / CPN) * KS + part * 16;
+            *(uint4*)dst = lo;
+            *(uint4*)(dst + 8) = hi;
+        }
+        {
+            uint32_t w[4];
+#pragma unroll
+            for (int wd = 0; wd < 4; ++wd) {
+                const uint32_t u = (uint32_t)pre_r[wd];
+                w[wd] = __builtin_bit_cast(
+                    uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(u << 16), __uint_as_float(u & 0xFFFF0000u)));
+            }
+            *(uint4*)(kv + (vt >> 3) * KS + DN + (vt & 7) * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        {
+            const int ch = 256 * NFULL + (vt >> 1);
+            *(uint4*)(kv + (ch / CPN) * KS + (ch % CPN) * 16 + (vt & 1) * 8) = fp8x8_to_f16(pre_h[0], pre_h[1]);
+        }
+    };
+    int64_t nraw = 0;  // this thread's position in the next batch: selected index, then resolved
+    Res nres{g_zero_entry, g_zero_entry + DN, nullptr, false};
+    float nscl = 0.f;
+    // next batch, one step per tile: each load is issued at the start of a tile and consumed at
+    // its end (no load but the tile prefetch in flight across the loop's back edge)
+    auto batch_begin = [&](int j) {
+        const int b1 = j / TPB + 1;
+        const int64_t u = u0 + (int64_t)b1 * RB + vt;
+        if (b1 * TPB < nt) {
+            if (j % TPB == 1) nraw = fetch(u);
+            if (j % TPB == 2) nscl = nres.ok ? gload<float>((const uint8_t*)nres.sp) : 0.f;
+        }
+    };
+    auto batch_end = [&](int j) {
+        const int b1 = j / TPB + 1;
+        const int64_t u = u0 + (int64_t)b1 * RB + vt;
+        if (b1 * TPB < nt) {
+            if (j % TPB == 1) nres = resolve_at(u, nraw);
+            if (j % TPB == 2) publish(b1 & 1, nres, nscl);
+        }
+    };
+
+    // One pass over the split (both roles); writes the output unless a tile broke the references
+    // in a first pass, which it returns.
+    auto run_pass = [&](bool second) -> bool {
+        // batch 0 of the positions, tile 0 staged, tile 1 in flight
+        if (!scores_role) {
+            const Res r = resolve_at(u0 + vt, fetch(u0 + vt));
+            publish(0, r, r.ok ? gload<float>((const uint8_t*)r.sp) : 0.f);
+        }
+        __syncthreads();
+        if (!scores_role) {
+            if (nt > 0) issue(0);
+            if (nt > 0) stage(0);
+            if (nt > 1) issue(1);
+        }
+        __syncthreads();
+        if (scores_role) {
+            // ---- query: lane holds head 16 rw + l16, dims 32 st + 8 g4 + e; RoPE at tp; fp16 with a per-head 2^e ----
+            const int hq = rw * 16 + l16;
+            v8h qf[DSTEP];
+            float sm_q;
+            {
+                const uint16_t* qrow = q + (t * H + hq) * (int64_t)D;
+                v4i raw[DSTEP];
+#pragma unroll
+                for (int st = 0; st < DSTEP; ++st) raw[st] = *(const v4i*)(qrow + 32 * st + 8 * g4);
+                float xr[DSTEP - NSTEP][8];
+                float mx = 0.f;
+#pragma unroll
+                for (int st = 0; st < DSTEP; ++st) {
+                    const uint16_t* hv = (const uint16_t*)&raw[st];
+                    if (st < NSTEP) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(bf16_bits_to_f32(hv[e])));
+                    } else {
+                        const int d0 = 32 * st + 8 * g4 - DN;
+#pragma unroll
+                        for (int e = 0; e < 8; e += 2) {
+                            const int pi = (d0 + e) >> 1;
+                            const float cs = sm.cs[2 * pi], sn = sm.cs[2 * pi + 1];
+                            const float x0 = bf16_bits_to_f32(hv[e]), x1 = bf16_bits_to_f32(hv[e + 1]);
+                            xr[st - NSTEP][e] = x0 * cs - x1 * sn;
+                            xr[st - NSTEP][e + 1] = x0 * sn + x1 * cs;
+                            mx = fmaxf(mx, fmaxf(fabsf(xr[st - NSTEP][e]), fabsf(xr[st - NSTEP][e + 1])));
+                        }
+                    }
+                }
+                mx = rows4_max(mx);
+                int ex = 0;
+                if (mx > 0.f) frexpf(mx, &ex);  // mx in [2^(ex-1), 2^ex)
+                int shq = mx > 0.f ? 15 - ex : 0;
+                shq = shq < -100 ? -100 : (shq > 100 ? 100 : shq);
+                const float qs = ldexpf(1.f, shq);
+                sm_q = sm_scale * ldexpf(1.f, -shq);
+#pragma unroll
+                for (int st = 0; st < DSTEP; ++st) {
+                    const uint16_t* hv = (const uint16_t*)&raw[st];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        qf[st][e] = (_Float16)((st < NSTEP ? bf16_bits_to_f32(hv[e]) : xr[st - NSTEP][e]) * qs);
+                    asm volatile("" : "+a"(qf[st]));
+                }
+            }
+            float m_ref = m_seen, s_ref = s_seen, l_run = 0.f;
+            constexpr int QG = 2;
+            static_assert(DSTEP % QG == 0, "whole groups");
+            for (int it = 0; it <= nt; ++it) {
+                if (it < nt) {
+                    const int j = it;
+                    const float* tscl = sm.kscl[(j / TPB) & 1] + (j % TPB) * KT;
+                    const float4 s0 = *(const float4*)(tscl + 4 * g4), s1 = *(const float4*)(tscl + 16 + 4 * g4);
+                    // S^T (keys x heads) of tile j for this wave's 16 heads: FP8-dim and RoPE-dim parts
+                    v4f an[2], ar[2];
+                    {
+                        const _Float16* kb = sm.kv[j % 3] + l16 * KS + 8 * g4;
+                        an[0] = an[1] = ar[0] = ar[1] = v4f{0.f, 0.f, 0.f, 0.f};
+                        v8h kf[2][2 * QG];
+#pragma unroll
+                        for (int e = 0; e < QG; ++e) {
+                            kf[0][2 * e] = *(const v8h*)(kb + 32 * e);
+                            kf[0][2 * e + 1] = *(const v8h*)(kb + 16 * KS + 32 * e);
+                        }
+#pragma unroll
+                        for (int g = 0; g < DSTEP / QG; ++g) {
+                            if (g + 1 < DSTEP / QG) {
+#pragma unroll
+                                for (int e = 0; e < QG; ++e) {
+                                    const int st = (g + 1) * QG + e;
+                                    kf[(g + 1) & 1][2 * e] = *(const v8h*)(kb + 32 * st);
+                                    kf[(g + 1) & 1][2 * e + 1] = *(const v8h*)(kb + 16 * KS + 32 * st);
+                                }
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                            for (int e = 0; e < QG; ++e) {
+                                const int st = g * QG + e;
+                                if (st < NSTEP) {
+                                    an[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[g & 1][2 * e], qf[st], an[0], 0, 0, 0);
+                                    an[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[g & 1][2 * e + 1], qf[st], an[1], 0, 0, 0);
+                                } else {
+                                    ar[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[g & 1][2 * e], qf[st], ar[0], 0, 0, 0);
+                                    ar[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[g & 1][2 * e + 1], qf[st], ar[1], 0, 0, 0);
+                                }
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
+                    // scores and P of tile j for head hq: lane (l16, g4) holds keys 4 g4 + i and 16 + 4 g4 + i
+                    const float kscl[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+                    float sv[8];
+                    float st_max = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        sv[i] = kscl[i] >= 0.f ? sm_q * fmaf(kscl[i], an[i >> 2][i & 3], ar[i >> 2][i & 3]) : -INFINITY;
+                        st_max = fmaxf(st_max, kscl[i]);
+                    }
+                    st_max = rows4_max(st_max);  // over the tile's 32 keys
+                    float mx = sv[0];
+#pragma unroll
+                    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+                    mx = rows4_max(mx);
+                    m_seen = fmaxf(m_seen, mx);
+                    s_seen = fmaxf(s_seen, st_max);
+                    m_ref = m_ref == -INFINITY ? mx : m_ref;  // first tile with visible keys (accumulators still zero)
+                    s_ref = s_ref == 0.f ? st_max : s_ref;
+                    if (mx > m_ref + kLazy || st_max > kSRatio * s_ref) sm.restart = 1;
+                    const float inv_s = s_ref > 0.f ? 1.f / s_ref : 0.f;
+                    v8h pn, pr;
+                    float sum = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float p = m_ref == -INFINITY ? 0.f : __expf(sv[i] - m_ref);
+                        sum += p;
+                        pr[i] = (_Float16)p;
+                        pn[i] = (_Float16)(p * (kscl[i] * inv_s));
+                    }
+                    l_run += rows4_sum(sum);
+                    *(v8h*)(sm.pn[j & 1] + hq * Sm::PS + 8 * g4) = pn;
+                    *(v8h*)(sm.pr[j & 1] + hq * Sm::PS + 8 * g4) = pr;
+                }
+                lds_barrier();
+            }
+            // hand the head's references and sum to the values role; lse / partial statistics
+            if (g4 == 0) {
+                sm.mfin[hq] = m_ref;
+                sm.lfin[hq] = l_run;
+            }
+            if (tid == 0) sm.sfin = s_ref > 0.f ? s_ref : 1.f;
+            const bool redo = !second && sm.restart != 0;
+            if (!redo && g4 == 0) {
+                if (S == 1) lse[t * H + hq] = l_run > 0.f ? m_ref + __logf(l_run) : -INFINITY;
+                else {
+                    part_ml[((t * S + s) * H + hq) * 2 + 0] = m_ref;
+                    part_ml[((t * S + s) * H + hq) * 2 + 1] = l_run;
+                }
+            }
+            __syncthreads();
+        } else {
+            v4f acc[4][DT];
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < DT; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+            for (int it = 0; it <= nt; ++it) {
+                batch_begin(it);
+                if (it + 1 < nt) stage(it + 1);
+                if (it + 2 < nt) issue(it + 2);
+                if (it >= 1) {
+                    // O[heads x dims] += P V (tile it - 1) for all heads over this wave's dims
+                    const int j = it - 1;
+                    const _Float16* vb = sm.kv[j % 3] + (4 * g4 + (l16 >> 2)) * KS + 4 * (l16 & 3);
+                    auto vfrag = [&](int dt) -> v8h {
+                        const int d0 = dt < NN ? 16 * (NN * rw + dt) : DN + 16 * rw;
+                        const v4s lo = lds_read_tr16(vb + d0);
+                        const v4s hi = lds_read_tr16(vb + 16 * KS + d0);
+                        const v8u16 c = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
+                                         (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
+                        return __builtin_bit_cast(v8h, c);
+                    };
+                    // P of every head group, then one V fragment at a time (fewer registers live)
+                    v8h pf[4];
+#pragma unroll
+                    for (int ht = 0; ht < 4; ++ht) pf[ht] = *(const v8h*)(sm.pn[j & 1] + (16 * ht + l16) * Sm::PS + 8 * g4);
+#pragma unroll
+                    for (int dt = 0; dt < NN; ++dt) {
+                        const v8h vf = vfrag(dt);
+#pragma unroll
+                        for (int ht = 0; ht < 4; ++ht)
+                            acc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[ht], vf, acc[ht][dt], 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int ht = 0; ht < 4; ++ht) pf[ht] = *(const v8h*)(sm.pr[j & 1] + (16 * ht + l16) * Sm::PS + 8 * g4);
+                    {
+                        const v8h vf = vfrag(NN);
+#pragma unroll
+                        for (int ht = 0; ht < 4; ++ht)
+                            acc[ht][NN] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[ht], vf, acc[ht][NN], 0, 0, 0);
+                    }
+                }
+                batch_end(it);
+                lds_barrier();
+            }
+            __syncthreads();  // the scores role's per-head statistics
+            const bool redo = !second && sm.restart != 0;
+            if (!redo) {
+                // ---- output: lane holds heads 16 ht + 4 g4 + i at one dim of each of its dim tiles ----
+                const float sfin = sm.sfin;
+#pragma unroll
+                for (int ht = 0; ht < 4; ++ht) {
+                    float inv[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float l = sm.lfin[16 * ht + 4 * g4 + i];
+                        inv[i] = l > 0.f ? 1.f / l : 0.f;
+                    }
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) {
+                        const bool nope = dt < NN;
+                        const int d = (nope ? 16 * (NN * rw + dt) : DN + 16 * rw) + l16;
+                        float o[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) o[i] = acc[ht][dt][i] * (nope ? sfin : 1.f);
+                        if (S == 1) {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) o[i] *= inv[i];
+                            if (!nope) {
+                                // inverse RoPE: pair (2p, 2p+1) lives in lanes l16 and l16 ^ 1
+                                const int pi = (d - DN) >> 1;
+                                const float cs = sm.cs[2 * pi], sn = -sm.cs[2 * pi + 1];
+                                const bool odd = d & 1;
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) {
+                                    const float other = __shfl_xor(o[i], 1);
+                                    const float x0 = odd ? other : o[i], x1 = odd ? o[i] : other;
+                                    o[i] = odd ? x0 * sn + x1 * cs : x0 * cs - x1 * sn;
+                                }
+                            }
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) out[(t * H + 16 * ht + 4 * g4 + i) * (int64_t)D + d] = o[i];
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                part_o[((t * S + s) * H + 16 * ht + 4 * g4 + i) * (int64_t)D + d] = o[i];
+                        }
+                    }
+                }
+            }
+        }
+        const bool redo = !second && sm.restart != 0;
+        __syncthreads();  // every wave has read the flag
+        return redo;
+    };
+
+    if (run_pass(false)) {
+        // a tile broke the references: again, with the maxima of every tile as the references
+        // (no tile can break them)
+        if (tid == 0) sm.restart = 0;
+        run_pass(true);
+    }
+}
+
 // Merge the S split partials of one (row, head) in the fixed order s = 0 .. S-1.
 template <int D>
 __global__ __launch_bounds__(128) void k_mqa_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
@@ -964,8 +1396,13 @@ size_t mqa_workspace_bytes(int64_t T, int H, int d, int64_t max_keys) {
 template <int H, int D>
 static void launch_mqa_t(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, const int32_t* idx,
                          int k, int m, KvView comp, KvView win, int window, float sm_scale, const RopeTab& rt, int S,
-                         float* out, float* lse, float* po, float* pml, hipStream_t st) {
-    if constexpr (H == 64)
+                         int64_t max_keys, float* out, float* lse, float* po, float* pml, hipStream_t st) {
+    // splits of more than a few tiles: the two-role kernel (its pipeline costs a step at either end)
+    const bool long_splits = (max_keys + S - 1) / S > 4 * KT;
+    if (H == 64 && D == 512 && long_splits)
+        hipLaunchKernelGGL((k_mqa64ws<512>), dim3((unsigned)(T * S)), dim3(512), 0, st, q, seq, pos, idx, k, m, comp,
+                           win, window, sm_scale, rt, S, out, lse, po, pml);
+    else if constexpr (H == 64)
         hipLaunchKernelGGL((k_mqa64<D>), dim3((unsigned)(T * S)), dim3(256), 0, st, q, seq, pos, idx, k, m, comp, win,
                            window, sm_scale, rt, S, out, lse, po, pml);
     else
@@ -988,7 +1425,7 @@ hipError_t launch_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos,
         pml = po + (size_t)T * S * H * d;
     }
 #define CSA_MQA(HH, DD) \
-    launch_mqa_t<HH, DD>(q, seq, pos, T, idx, k, m, comp, win, window, sm_scale, rt, S, out, lse, po, pml, st)
+    launch_mqa_t<HH, DD>(q, seq, pos, T, idx, k, m, comp, win, window, sm_scale, rt, S, max_keys, out, lse, po, pml, st)
     if (d == 512) {
         if (H == 64) CSA_MQA(64, 512);
         else if (H == 32) CSA_MQA(32, 512);

@@ -272,6 +272,7 @@ def _attn_inputs(gen, seed, B, N, W, H, d, T, L, win_cap):
     (3, 2, 600, 32, 512, 256, 128, 4, 128),        # fewer visible than k (-1 padding)
     (6, 3, 2048, 16, 128, 64, 128, 4, 200),
     (2, 2, 64, 64, 512, 64, 0, 4, 1),              # no window branch
+    (64, 4, 8192, 64, 512, 1024, 128, 4, 128),     # 8 splits of 144 keys: the two-role 64-head kernel
 ])
 def test_sparse_mqa_decode(lib, dev, gen, orc, T, B, L, H, d, k, W, m, win_cap):
     import torch
@@ -315,6 +316,7 @@ def test_sparse_mqa_ignores_invalid_idx(lib, dev, gen, orc):
     (8, 8, 131072, 64, 512, 128, 128),   # decode, 1024 entries
     (3, 3, 20000, 32, 512, 128, 128),
     (5, 1, 640, 16, 128, 64, 128),
+    (128, 8, 131072, 64, 512, 128, 128),  # 4 splits of 288 keys: the two-role 64-head kernel
 ])
 def test_dense_mqa_decode(lib, dev, gen, orc, T, B, L, H, d, W, m):
     import torch

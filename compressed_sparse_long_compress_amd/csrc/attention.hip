@@ -975,20 +975,26 @@ __global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q,
 
     float m_seen = -INFINITY, s_seen = 0.f;  // scores role: maxima over every tile seen (second-pass references)
 
-    // ---- values role: tile loads (global -> registers) and staging (registers -> LDS), as in k_mqa64 ----
-    v4i pre[NFULL > 0 ? NFULL : 1];
-    v4i pre_r;
+    // ---- tile loads (global -> registers) and staging (registers -> LDS), shared by the roles.
+    // Thread vt of the values role: FP8 chunks c = vt and vt + 256 (entry c / CPN, bytes (c % CPN) * 16).
+    // Thread vt of the scores role: FP8 chunk vt + 512, the RoPE chunk of entry vt / 8 (bytes
+    // (vt % 8) * 16) and 8 bytes of FP8 chunk 768 + vt / 2.  Consecutive lanes read consecutive bytes.
+    static_assert(NFULL == 3, "two whole FP8 chunks per values thread, one per scores thread");
+    v4i pre_a, pre_b;
     v2u pre_h;
     auto issue = [&](int j) {
         const int b = (j / TPB) & 1, slot = (j % TPB) * KT;
-#pragma unroll
-        for (int i = 0; i < NFULL; ++i) {
-            const int c = vt + i * 256;
-            pre[i] = gload<v4i>(sm.kaddr[b][slot + c / CPN][0] + (c % CPN) * 16);
+        if (!scores_role) {
+            pre_a = gload<v4i>(sm.kaddr[b][slot + vt / CPN][0] + (vt % CPN) * 16);
+            const int c = vt + 256;
+            pre_b = gload<v4i>(sm.kaddr[b][slot + c / CPN][0] + (c % CPN) * 16);
+        } else {
+            const int c = vt + 512;
+            pre_a = gload<v4i>(sm.kaddr[b][slot + c / CPN][0] + (c % CPN) * 16);
+            pre_b = gload<v4i>(sm.kaddr[b][slot + (vt >> 3)][1] + (vt & 7) * 16);
+            const int ch = 768 + (vt >> 1);
+            pre_h = gload<v2u>(sm.kaddr[b][slot + ch / CPN][0] + (ch % CPN) * 16 + (vt & 1) * 8);
         }
-        pre_r = gload<v4i>(sm.kaddr[b][slot + (vt >> 3)][1] + (vt & 7) * 16);
-        const int ch = 256 * NFULL + (vt >> 1);
-        pre_h = gload<v2u>(sm.kaddr[b][slot + ch / CPN][0] + (ch % CPN) * 16 + (vt & 1) * 8);
     };
     auto fp8x8_to_f16 = [](uint32_t lo, uint32_t hi) -> uint4 {
         return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.f, false)),
@@ -996,30 +1002,27 @@ __global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q,
                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.f, false)),
                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.f, true)));
     };
+    auto stage_chunk = [&](_Float16* kv, int c, const v4i& x) {
+        _Float16* dst = kv + (c / CPN) * KS + (c % CPN) * 16;
+        *(uint4*)dst = fp8x8_to_f16((uint32_t)x[0], (uint32_t)x[1]);
+        *(uint4*)(dst + 8) = fp8x8_to_f16((uint32_t)x[2], (uint32_t)x[3]);
+    };
     auto stage = [&](int j) {
         _Float16* kv = sm.kv[j % 3];
-#pragma unroll
-        for (int i = 0; i < NFULL; ++i) {
-            const int c = vt + i * 256;
-            const int part = c % CPN;
-            const uint4 lo = fp8x8_to_f16((uint32_t)pre[i][0], (uint32_t)pre[i][1]);
-            const uint4 hi = fp8x8_to_f16((uint32_t)pre[i][2], (uint32_t)pre[i][3]);
-            _Float16* dst = kv + (c / CPN) * KS + part * 16;
-            *(uint4*)dst = lo;
-            *(uint4*)(dst + 8) = hi;
-        }
-        {
+        if (!scores_role) {
+            stage_chunk(kv, vt, pre_a);
+            stage_chunk(kv, vt + 256, pre_b);
+        } else {
+            stage_chunk(kv, vt + 512, pre_a);
             uint32_t w[4];
 #pragma unroll
             for (int wd = 0; wd < 4; ++wd) {
-                const uint32_t u = (uint32_t)pre_r[wd];
+                const uint32_t u = (uint32_t)pre_b[wd];
                 w[wd] = __builtin_bit_cast(
                     uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(u << 16), __uint_as_float(u & 0xFFFF0000u)));
             }
             *(uint4*)(kv + (vt >> 3) * KS + DN + (vt & 7) * 8) = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-        {
-            const int ch = 256 * NFULL + (vt >> 1);
+            const int ch = 768 + (vt >> 1);
             *(uint4*)(kv + (ch / CPN) * KS + (ch % CPN) * 16 + (vt & 1) * 8) = fp8x8_to_f16(pre_h[0], pre_h[1]);
         }
     };
@@ -1054,11 +1057,9 @@ __global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q,
             publish(0, r, r.ok ? gload<float>((const uint8_t*)r.sp) : 0.f);
         }
         __syncthreads();
-        if (!scores_role) {
-            if (nt > 0) issue(0);
-            if (nt > 0) stage(0);
-            if (nt > 1) issue(1);
-        }
+        if (nt > 0) issue(0);
+        if (nt > 0) stage(0);
+        if (nt > 1) issue(1);
         __syncthreads();
         if (scores_role) {
             // ---- query: lane holds head 16 rw + l16, dims 32 st + 8 g4 + e; RoPE at tp; fp16 with a per-head 2^e ----
@@ -1111,6 +1112,8 @@ __global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q,
             constexpr int QG = 2;
             static_assert(DSTEP % QG == 0, "whole groups");
             for (int it = 0; it <= nt; ++it) {
+                if (it + 1 < nt) stage(it + 1);
+                if (it + 2 < nt) issue(it + 2);
                 if (it < nt) {
                     const int j = it;
                     const float* tscl = sm.kscl[(j / TPB) & 1] + (j % TPB) * KT;

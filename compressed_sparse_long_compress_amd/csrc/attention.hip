@@ -470,6 +470,48 @@ __device__ __forceinline__ v4s lds_read_tr16(const _Float16* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
 }
 
+// The output of 64 heads leaves in two halves of 32 heads, staged in LDS as fp32 rows of
+// D + 4 floats (the lanes' 4 head groups then fall on distinct banks) and written in 16-byte
+// stores: one lane per element would issue 8x the store instructions.
+template <int D>
+constexpr int kOutStride = D + 4;
+
+// Lane (l16, g4) puts its normalised head values 16 hh + 4 g4 + i at dim d into the staging rows.
+__device__ __forceinline__ void stage_out(float* ob, int os, int hh, int g4, int d, const float (&o)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ob[(16 * hh + 4 * g4 + i) * os + d] = o[i];
+}
+
+// Rows [h0, h0 + 32) of the staging to the row's output (S == 1; inverse RoPE on the last 64
+// dims) or to the split's fp16 partial (S > 1; each head normalised by its own sum).
+template <int D, int NTH>
+__device__ __forceinline__ void store_out(const float* ob, const float* cs, int h0, int tid, int64_t t, int s, int S,
+                                          float* __restrict__ out, _Float16* __restrict__ po) {
+    constexpr int OS = kOutStride<D>, DN = D - 64, H = 64;
+    if (S == 1) {
+#pragma unroll
+        for (int c = tid; c < 32 * D / 4; c += NTH) {
+            const int r = c / (D / 4), d = (c % (D / 4)) * 4;
+            float4 v = *(const float4*)(ob + r * OS + d);
+            if (d >= DN) {
+                const int p = (d - DN) >> 1;
+                const float c0 = cs[2 * p], s0 = -cs[2 * p + 1], c1 = cs[2 * p + 2], s1 = -cs[2 * p + 3];
+                v = make_float4(v.x * c0 - v.y * s0, v.x * s0 + v.y * c0, v.z * c1 - v.w * s1, v.z * s1 + v.w * c1);
+            }
+            *(float4*)(out + (t * H + h0 + r) * (int64_t)D + d) = v;
+        }
+    } else {
+#pragma unroll
+        for (int c = tid; c < 32 * D / 8; c += NTH) {
+            const int r = c / (D / 8), d = (c % (D / 8)) * 8;
+            const float4 a = *(const float4*)(ob + r * OS + d), b = *(const float4*)(ob + r * OS + d + 4);
+            const v8h hv = {(_Float16)a.x, (_Float16)a.y, (_Float16)a.z, (_Float16)a.w,
+                            (_Float16)b.x, (_Float16)b.y, (_Float16)b.z, (_Float16)b.w};
+            *(v8h*)(po + ((t * S + s) * H + h0 + r) * (int64_t)D + d) = hv;
+        }
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, const int32_t* __restrict__ seq,
                                                const int64_t* __restrict__ pos, const int32_t* __restrict__ idx, int k,
@@ -494,6 +536,14 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
     const int l16 = lane & 15, g4 = lane >> 4;
     const int64_t t = blockIdx.x / S;
     const int s = blockIdx.x % S;
+    // the query's loads go first: they depend on nothing but the row
+    const int hq = wave * 16 + l16;
+    v4i qraw[DSTEP];
+    {
+        const uint16_t* qrow = q + (t * H + hq) * (int64_t)D;
+#pragma unroll
+        for (int st = 0; st < DSTEP; ++st) qraw[st] = *(const v4i*)(qrow + 32 * st + 8 * g4);
+    }
     const int64_t tp = pos[t];
     const int32_t sq = seq[t];
     const RowKeys rk = row_keys(tp, idx, k, m, window);
@@ -511,24 +561,39 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
         const float* sp;
         bool ok;
     };
+    // (the views' fields as scalars: a choice between the two views as objects would put both
+    // in scratch memory)
+    const uint8_t* const c_nope = comp.nope;
+    const uint8_t* const w_nope = win.nope;
+    const uint16_t* const c_rope = comp.rope;
+    const uint16_t* const w_rope = win.rope;
+    const float* const c_scale = comp.scale;
+    const float* const w_scale = win.scale;
+    const int64_t c_cap = comp.cap, w_cap = win.cap;
     auto resolve_at = [&](int64_t u, int64_t j) -> Res {
-        Res r{g_zero_entry, g_zero_entry + DN, nullptr, false};
-        if (u >= u1) return r;
-        if (u < rk.n_c) {
-            if (j < 0 || j >= rk.nv) return r;
-            const int64_t row = (int64_t)sq * comp.cap + (j % comp.cap);
-            return Res{comp.nope + row * DN, (const uint8_t*)(comp.rope + row * 64), comp.scale + row, true};
-        }
-        const int64_t p = rk.lo + (u - rk.n_c);
-        const int64_t row = (int64_t)sq * win.cap + (p % win.cap);
-        return Res{win.nope + row * DN, (const uint8_t*)(win.rope + row * 64), win.scale + row, true};
+        const bool inw = u >= rk.n_c;
+        if (u >= u1 || (!inw && (j < 0 || j >= rk.nv))) return Res{g_zero_entry, g_zero_entry + DN, nullptr, false};
+        const int64_t x = inw ? rk.lo + (u - rk.n_c) : j;
+        const int64_t cap = inw ? w_cap : c_cap;
+        const uint8_t* nb = inw ? w_nope : c_nope;
+        const uint16_t* rb = inw ? w_rope : c_rope;
+        const float* sb = inw ? w_scale : c_scale;
+        const int64_t row = (int64_t)sq * cap + (x % cap);
+        return Res{nb + row * DN, (const uint8_t*)(rb + row * 64), sb + row, true};
     };
-    auto publish = [&](int b, const Res& r, float sc) {
+    auto publish_addr = [&](int b, const Res& r) {
         sm.kaddr[b][tid][0] = r.an;
         sm.kaddr[b][tid][1] = r.ar;
-        sm.kscl[b][tid] = r.ok ? sc : -1.f;
+    };
+    auto publish_scale = [&](int b, const Res& r, float sc) { sm.kscl[b][tid] = r.ok ? sc : -1.f; };
+    auto publish = [&](int b, const Res& r, float sc) {
+        publish_addr(b, r);
+        publish_scale(b, r, sc);
     };
 
+    // batch 0 of the positions: row addresses now (the first tile's loads need them), the
+    // entry scales in flight until the query is converted
+    const Res r0 = resolve_at(u0 + tid, fetch(u0 + tid));
     if (tid < 32) {
         float c, sn;
         angle_cs((double)tp, rt.theta[tid], c, sn);
@@ -536,7 +601,9 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
         sm.cs[2 * tid + 1] = sn;
     }
     if (tid == 0) sm.restart = 0;
-    __syncthreads();
+    publish_addr(0, r0);
+    const float sc0 = r0.ok ? gload<float>((const uint8_t*)r0.sp) : 0.f;
+    lds_barrier();
 
     // ---- tile loads (global -> registers) and staging (registers -> LDS) ----
     // Per thread and tile: FP8 chunks c = tid + 256 i (i < NFULL; entry c / CPN, bytes (c % CPN) * 16),
@@ -591,14 +658,10 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
     };
 
     // ---- query: lane holds head wave*16 + l16, dims 32 st + 8 g4 + e; RoPE at tp; fp16 with a per-head 2^e ----
-    const int hq = wave * 16 + l16;
     v8h qf[DSTEP];
-    float sm_q;
-    {
-        const uint16_t* qrow = q + (t * H + hq) * (int64_t)D;
-        v4i raw[DSTEP];
-#pragma unroll
-        for (int st = 0; st < DSTEP; ++st) raw[st] = *(const v4i*)(qrow + 32 * st + 8 * g4);
+    float sm_q = 0.f;
+    auto convert_q = [&]() {
+        const v4i (&raw)[DSTEP] = qraw;
         float xr[DSTEP - NSTEP][8];
         float mx = 0.f;
 #pragma unroll
@@ -637,7 +700,7 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
             // are left for K fragments in flight, softmax and the tile loads
             asm volatile("" : "+a"(qf[st]));
         }
-    }
+    };
 
     v4f acc[4][DT];
     float m_ref = -INFINITY, l_run = 0.f, s_ref = 0.f;
@@ -779,13 +842,18 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
     // [stage(j+1), load j+2, PV(j)]  sync.  Tile t lives in kv[t % 3].  Returns whether a tile
     // broke the references (the pass's output is then discarded).  The loop has a single exit,
     // so the output accumulators keep their registers and every PV MFMA runs in place.
-    auto run_pass = [&]() -> bool {
-        {
+    auto run_pass = [&](bool first) -> bool {
+        if (first) {
+            // batch 0's addresses are published; convert the query while tile 0 is in flight
+            if (nt > 0) issue(0);
+            convert_q();
+            publish_scale(0, r0, sc0);
+        } else {
             const Res r = resolve_at(u0 + tid, fetch(u0 + tid));
             publish(0, r, r.ok ? gload<float>((const uint8_t*)r.sp) : 0.f);
+            lds_barrier();
+            if (nt > 0) issue(0);
         }
-        __syncthreads();
-        if (nt > 0) issue(0);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -795,7 +863,7 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
         l_run = 0.f;
         if (nt > 0) stage(0);
         if (nt > 1) issue(1);
-        __syncthreads();
+        lds_barrier();
         for (int j = 0; j < nt; ++j) {
             v4f sn[2], sr[2];
             batch_begin(j);
@@ -812,13 +880,13 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
         }
         return sm.restart != 0;
     };
-    if (run_pass()) {
+    if (run_pass(true)) {
         // a tile broke the references: run the split again with the maxima of every tile as the
         // references (no tile can break them); every wave has read the flag before the last barrier
         m_seen = rows4_max(m_seen);
-        __syncthreads();
+        lds_barrier();
         if (tid == 0) sm.restart = 0;
-        run_pass();
+        run_pass(false);
     }
 
     // ---- epilogue: lane holds heads 16 ht + 4 g4 + i at one dim of each of its dim tiles ----
@@ -830,46 +898,34 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
             part_ml[((t * S + s) * H + hq) * 2 + 1] = l_run;
         }
     }
-    __syncthreads();
+    lds_barrier();
     const float sfin = s_ref > 0.f ? s_ref : 1.f;
+    float* ob = (float*)&sm.kv[0][0];  // the tiles are no longer read
+    static_assert(32 * kOutStride<D> * sizeof(float) <= sizeof(sm.kv), "32 staged output rows fit the tile buffers");
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-        float inv[4];
+    for (int half = 0; half < 2; ++half) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float l = sm.lfin[16 * ht + 4 * g4 + i];
-            inv[i] = l > 0.f ? 1.f / l : 0.f;
-        }
+        for (int hh = 0; hh < 2; ++hh) {
+            const int ht = 2 * half + hh;
+            float inv[4];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const bool nope = dt < NN;
-            const int d = (nope ? 16 * (NN * wave + dt) : DN + 16 * wave) + l16;
-            float o[4];
+            for (int i = 0; i < 4; ++i) {
+                const float l = sm.lfin[16 * ht + 4 * g4 + i];
+                inv[i] = l > 0.f ? 1.f / l : 0.f;
+            }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = acc[ht][dt][i] * (nope ? sfin : 1.f);
-            if (S == 1) {
+            for (int dt = 0; dt < DT; ++dt) {
+                const bool nope = dt < NN;
+                const int d = (nope ? 16 * (NN * wave + dt) : DN + 16 * wave) + l16;
+                float o[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] *= inv[i];
-                if (!nope) {
-                    // inverse RoPE: pair (2p, 2p+1) lives in lanes l16 and l16 ^ 1
-                    const int pi = (d - DN) >> 1;
-                    const float cs = sm.cs[2 * pi], sn = -sm.cs[2 * pi + 1];
-                    const bool odd = d & 1;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float other = __shfl_xor(o[i], 1);
-                        const float x0 = odd ? other : o[i], x1 = odd ? o[i] : other;
-                        o[i] = odd ? x0 * sn + x1 * cs : x0 * cs - x1 * sn;
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) out[(t * H + 16 * ht + 4 * g4 + i) * (int64_t)D + d] = o[i];
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    part_o[((t * S + s) * H + 16 * ht + 4 * g4 + i) * (int64_t)D + d] = o[i];
+                for (int i = 0; i < 4; ++i) o[i] = acc[ht][dt][i] * (nope ? sfin : 1.f) * inv[i];
+                stage_out(ob, kOutStride<D>, hh, g4, d, o);
             }
         }
+        lds_barrier();
+        store_out<D, 256>(ob, sm.cs, 32 * half, tid, t, s, S, out, (_Float16*)part_o);
+        if (half == 0) lds_barrier();
     }
 }
 
@@ -946,17 +1002,25 @@ __global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q,
         const float* sp;
         bool ok;
     };
+    // (the views' fields as scalars: a choice between the two views as objects would put both
+    // in scratch memory)
+    const uint8_t* const c_nope = comp.nope;
+    const uint8_t* const w_nope = win.nope;
+    const uint16_t* const c_rope = comp.rope;
+    const uint16_t* const w_rope = win.rope;
+    const float* const c_scale = comp.scale;
+    const float* const w_scale = win.scale;
+    const int64_t c_cap = comp.cap, w_cap = win.cap;
     auto resolve_at = [&](int64_t u, int64_t j) -> Res {
-        Res r{g_zero_entry, g_zero_entry + DN, nullptr, false};
-        if (u >= u1) return r;
-        if (u < rk.n_c) {
-            if (j < 0 || j >= rk.nv) return r;
-            const int64_t row = (int64_t)sq * comp.cap + (j % comp.cap);
-            return Res{comp.nope + row * DN, (const uint8_t*)(comp.rope + row * 64), comp.scale + row, true};
-        }
-        const int64_t p = rk.lo + (u - rk.n_c);
-        const int64_t row = (int64_t)sq * win.cap + (p % win.cap);
-        return Res{win.nope + row * DN, (const uint8_t*)(win.rope + row * 64), win.scale + row, true};
+        const bool inw = u >= rk.n_c;
+        if (u >= u1 || (!inw && (j < 0 || j >= rk.nv))) return Res{g_zero_entry, g_zero_entry + DN, nullptr, false};
+        const int64_t x = inw ? rk.lo + (u - rk.n_c) : j;
+        const int64_t cap = inw ? w_cap : c_cap;
+        const uint8_t* nb = inw ? w_nope : c_nope;
+        const uint16_t* rb = inw ? w_rope : c_rope;
+        const float* sb = inw ? w_scale : c_scale;
+        const int64_t row = (int64_t)sq * cap + (x % cap);
+        return Res{nb + row * DN, (const uint8_t*)(rb + row * 64), sb + row, true};
     };
     auto publish = [&](int b, const Res& r, float sc) {
         sm.kaddr[b][vt][0] = r.an;
@@ -1050,17 +1114,19 @@ __global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q,
 
     // One pass over the split (both roles); writes the output unless a tile broke the references
     // in a first pass, which it returns.
+    float* ob = (float*)&sm.kv[0][0];  // output staging, once the tiles are no longer read
+    static_assert(32 * kOutStride<D> * sizeof(float) <= sizeof(sm.kv), "32 staged output rows fit the tile buffers");
     auto run_pass = [&](bool second) -> bool {
         // batch 0 of the positions, tile 0 staged, tile 1 in flight
         if (!scores_role) {
             const Res r = resolve_at(u0 + vt, fetch(u0 + vt));
             publish(0, r, r.ok ? gload<float>((const uint8_t*)r.sp) : 0.f);
         }
-        __syncthreads();
+        lds_barrier();
         if (nt > 0) issue(0);
         if (nt > 0) stage(0);
         if (nt > 1) issue(1);
-        __syncthreads();
+        lds_barrier();
         if (scores_role) {
             // ---- query: lane holds head 16 rw + l16, dims 32 st + 8 g4 + e; RoPE at tp; fp16 with a per-head 2^e ----
             const int hq = rw * 16 + l16;
@@ -1203,7 +1269,16 @@ __global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q,
                     part_ml[((t * S + s) * H + hq) * 2 + 1] = l_run;
                 }
             }
-            __syncthreads();
+            lds_barrier();
+            if (!redo) {
+                // the values role stages the output half by half; both roles store it
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    lds_barrier();
+                    store_out<D, 512>(ob, sm.cs, 32 * half, tid, t, s, S, out, (_Float16*)part_o);
+                    lds_barrier();
+                }
+            }
         } else {
             v4f acc[4][DT];
 #pragma unroll
@@ -1249,54 +1324,40 @@ __global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q,
                 batch_end(it);
                 lds_barrier();
             }
-            __syncthreads();  // the scores role's per-head statistics
+            lds_barrier();  // the scores role's per-head statistics
             const bool redo = !second && sm.restart != 0;
             if (!redo) {
                 // ---- output: lane holds heads 16 ht + 4 g4 + i at one dim of each of its dim tiles ----
                 const float sfin = sm.sfin;
 #pragma unroll
-                for (int ht = 0; ht < 4; ++ht) {
-                    float inv[4];
+                for (int half = 0; half < 2; ++half) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float l = sm.lfin[16 * ht + 4 * g4 + i];
-                        inv[i] = l > 0.f ? 1.f / l : 0.f;
-                    }
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int ht = 2 * half + hh;
+                        float inv[4];
 #pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) {
-                        const bool nope = dt < NN;
-                        const int d = (nope ? 16 * (NN * rw + dt) : DN + 16 * rw) + l16;
-                        float o[4];
+                        for (int i = 0; i < 4; ++i) {
+                            const float l = sm.lfin[16 * ht + 4 * g4 + i];
+                            inv[i] = l > 0.f ? 1.f / l : 0.f;
+                        }
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) o[i] = acc[ht][dt][i] * (nope ? sfin : 1.f);
-                        if (S == 1) {
+                        for (int dt = 0; dt < DT; ++dt) {
+                            const bool nope = dt < NN;
+                            const int d = (nope ? 16 * (NN * rw + dt) : DN + 16 * rw) + l16;
+                            float o[4];
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) o[i] *= inv[i];
-                            if (!nope) {
-                                // inverse RoPE: pair (2p, 2p+1) lives in lanes l16 and l16 ^ 1
-                                const int pi = (d - DN) >> 1;
-                                const float cs = sm.cs[2 * pi], sn = -sm.cs[2 * pi + 1];
-                                const bool odd = d & 1;
-#pragma unroll
-                                for (int i = 0; i < 4; ++i) {
-                                    const float other = __shfl_xor(o[i], 1);
-                                    const float x0 = odd ? other : o[i], x1 = odd ? o[i] : other;
-                                    o[i] = odd ? x0 * sn + x1 * cs : x0 * cs - x1 * sn;
-                                }
-                            }
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) out[(t * H + 16 * ht + 4 * g4 + i) * (int64_t)D + d] = o[i];
-                        } else {
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                part_o[((t * S + s) * H + 16 * ht + 4 * g4 + i) * (int64_t)D + d] = o[i];
+                            for (int i = 0; i < 4; ++i) o[i] = acc[ht][dt][i] * (nope ? sfin : 1.f) * inv[i];
+                            stage_out(ob, kOutStride<D>, hh, g4, d, o);
                         }
                     }
+                    lds_barrier();
+                    store_out<D, 512>(ob, sm.cs, 32 * half, tid, t, s, S, out, (_Float16*)part_o);
+                    lds_barrier();
                 }
             }
         }
         const bool redo = !second && sm.restart != 0;
-        __syncthreads();  // every wave has read the flag
+        lds_barrier();  // every wave has read the flag
         return redo;
     };
 
@@ -1381,6 +1442,83 @@ __global__ __launch_bounds__(128) void k_mqa_combine(const float* __restrict__ p
     if (tid == 0) lse[th] = red[1] > 0.f ? red[0] + __logf(red[1]) : -INFINITY;
 }
 
+// Merge of the 64-head kernels' split partials: fp16, each normalised by its own sum l_s,
+// weighted by exp(m_s - M) l_s / L in the fixed order s = 0 .. S-1.
+template <int D>
+__global__ __launch_bounds__(128) void k_mqa_combine16(const _Float16* __restrict__ part_o,
+                                                       const float* __restrict__ part_ml, const int64_t* __restrict__ pos,
+                                                       int H, int S, RopeTab rt, float* __restrict__ out,
+                                                       float* __restrict__ lse) {
+    constexpr int DN = D - 64;
+    constexpr int SMAX = 64;
+    __shared__ float wgt[SMAX];
+    __shared__ float red[2];
+    const int64_t th = blockIdx.x;  // t*H + h
+    const int64_t t = th / H;
+    const int h = (int)(th % H);
+    const int tid = threadIdx.x;
+    if (tid < 64) {
+        float ms = -INFINITY, ls = 0.f;
+        if (tid < S) {
+            ms = part_ml[((t * S + tid) * H + h) * 2];
+            ls = part_ml[((t * S + tid) * H + h) * 2 + 1];
+        }
+        const float M = wave_max(ms);
+        const float e = ms == -INFINITY ? 0.f : __expf(ms - M);
+        const float L = ls * e;
+        // fixed-order sum over splits
+        float Lseq = 0.f;
+        for (int i = 0; i < S; ++i) Lseq += __shfl(L, i);
+        if (tid < S) wgt[tid] = Lseq > 0.f ? L / Lseq : 0.f;
+        if (tid == 0) {
+            red[0] = M;
+            red[1] = Lseq;
+        }
+    }
+    __syncthreads();
+    for (int d0 = tid * 4; d0 < D; d0 += 128 * 4) {
+        float o[4] = {0.f, 0.f, 0.f, 0.f};
+        const _Float16* base = part_o + (t * S * H + h) * (int64_t)D + d0;
+        int s = 0;
+        for (; s + 8 <= S; s += 8) {
+            uint2 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = *(const uint2*)(base + (int64_t)(s + u) * H * D);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float wv = wgt[s + u];
+                const v2h a = __builtin_bit_cast(v2h, v[u].x), b = __builtin_bit_cast(v2h, v[u].y);
+                o[0] = fmaf(wv, (float)a[0], o[0]);
+                o[1] = fmaf(wv, (float)a[1], o[1]);
+                o[2] = fmaf(wv, (float)b[0], o[2]);
+                o[3] = fmaf(wv, (float)b[1], o[3]);
+            }
+        }
+        for (; s < S; ++s) {
+            const uint2 v = *(const uint2*)(base + (int64_t)s * H * D);
+            const float wv = wgt[s];
+            const v2h a = __builtin_bit_cast(v2h, v.x), b = __builtin_bit_cast(v2h, v.y);
+            o[0] = fmaf(wv, (float)a[0], o[0]);
+            o[1] = fmaf(wv, (float)a[1], o[1]);
+            o[2] = fmaf(wv, (float)b[0], o[2]);
+            o[3] = fmaf(wv, (float)b[1], o[3]);
+        }
+        if (d0 >= DN) {
+            const double tp = (double)pos[t];
+            for (int i = 0; i < 4; i += 2) {
+                float cs, sn;
+                angle_cs(tp, rt.theta[(d0 - DN + i) >> 1], cs, sn);
+                sn = -sn;  // rotation by -t
+                const float x0 = o[i], x1 = o[i + 1];
+                o[i] = x0 * cs - x1 * sn;
+                o[i + 1] = x0 * sn + x1 * cs;
+            }
+        }
+        *(float4*)(out + th * D + d0) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+    if (tid == 0) lse[th] = red[1] > 0.f ? red[0] + __logf(red[1]) : -INFINITY;
+}
+
 static int choose_splits(int64_t T, int64_t max_keys) {
     int64_t s = (512 + T - 1) / T;
     int64_t by_keys = (max_keys + 63) / 64;
@@ -1412,6 +1550,10 @@ static void launch_mqa_t(const uint16_t* q, const int32_t* seq, const int64_t* p
         hipLaunchKernelGGL((k_mqa<H, D>), dim3((unsigned)(T * S)), dim3(256), 0, st, q, seq, pos, idx, k, m, comp,
                            win, window, sm_scale, rt, S, out, lse, po, pml);
     if (S > 1)
+        if constexpr (H == 64)
+            hipLaunchKernelGGL((k_mqa_combine16<D>), dim3((unsigned)(T * H)), dim3(128), 0, st, (const _Float16*)po, pml,
+                               pos, H, S, rt, out, lse);
+        else
         hipLaunchKernelGGL((k_mqa_combine<D>), dim3((unsigned)(T * H)), dim3(128), 0, st, po, pml, pos, H, S, rt, out,
                            lse);
 }

@@ -68,13 +68,15 @@ __global__ __launch_bounds__(256) void k_index_rows(const uint8_t* __restrict__ 
         for (int u = 0; u < U; ++u) {
             const int64_t j = j0 + u * 16 + r;
             if (j < nv && g < NB) {
-                bk[u] = *(const v4i*)(kdata + (base + j) * KB + g * 16);
+                // streamed once: nontemporal, so the keys do not displace cached lines
+                bk[u] = __builtin_nontemporal_load((const v4i*)(kdata + (base + j) * KB + g * 16));
                 sb[u] = kscale[(base + j) * NB + g];
             } else {
                 bk[u] = v4i{0, 0, 0, 0};
                 sb[u] = 127;
             }
         }
+        float pv[U];  // score of key j0 + 16 u + r (every lane, after the head-group sum)
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             v4f acc = {0.f, 0.f, 0.f, 0.f};
@@ -85,11 +87,19 @@ __global__ __launch_bounds__(256) void k_index_rows(const uint8_t* __restrict__ 
             p = fmaf(wr[2], fmaxf(acc[2], 0.f), p);
             p = fmaf(wr[3], fmaxf(acc[3], 0.f), p);
             p = rows4_sum(p);  // the four head groups (exact: every partial sum is representable)
-            const int64_t j = j0 + u * 16 + lane;
-            if (lane < 16 && j < c1) {
-                out[j] = j < nv ? p : -INFINITY;
-                if (j < nv) gm[u / (U / 4)] = max(gm[u / (U / 4)], f32_order_key(p));
-            }
+            const int64_t j = j0 + u * 16 + r;
+            pv[u] = j < nv ? p : -INFINITY;
+            if (lane < 16 && j < c1 && j < nv) gm[u / (U / 4)] = max(gm[u / (U / 4)], f32_order_key(p));
+        }
+        {
+            // the step's 128 scores in two full-wave stores: lane (r, g) writes keys j0 + 16 g + r
+            // and j0 + 64 + 16 g + r (a quarter-wave store per tile would issue four times as many)
+            static_assert(U == 8, "two stores of 64 keys");
+            const float v0 = g == 0 ? pv[0] : g == 1 ? pv[1] : g == 2 ? pv[2] : pv[3];
+            const float v1 = g == 0 ? pv[4] : g == 1 ? pv[5] : g == 2 ? pv[6] : pv[7];
+            const int64_t ja = j0 + lane, jb = j0 + 64 + lane;
+            if (ja < c1) out[ja] = v0;
+            if (jb < c1) out[jb] = v1;
         }
         if (gmax) {
             // unsigned max over lanes 0..15 of four values, spread so that lanes 4G..4G+3 end with

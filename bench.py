@@ -34,7 +34,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (scaled by a 256 MiB copy: fetch x2.0,
 # write x1.0; see profiles/csa_decode_1m_hbm_counters.md), valid for the kernel
 # source with this SHA-256 only.
-INDEX_TRAFFIC = {"sha256": "acf9b0f6d8f9e6d8c27dfccaa6eb35806443b1d731ae2b762ec7c288ace6f076", "bytes": 75736058}
+INDEX_TRAFFIC = {"sha256": "a5a3c886293fa9cf848b04ff3c60013ad7b442b98bea38786542ca1080eb42f4", "bytes": 75730032}
 
 
 def log(msg):

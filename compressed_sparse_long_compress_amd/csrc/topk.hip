@@ -999,7 +999,259 @@ __global__ __launch_bounds__(kTsThreads) void k_topk_stream(const float* __restr
     }
 }
 
-// few rows longer than k_topk_stream takes: selection from the row summary
+// ---------------------------------------------------------------------------
+// Many rows of up to kTrMaxCols columns (e.g. prefill): one workgroup per row
+// holds the row's visible keys in registers (NV4 float4 slots per thread), so
+// the row is read once.  A lower bound lo of the k-th largest key: each thread
+// keeps its two largest keys; the smallest j-th of them over the threads
+// holding >= j keys, j = ceil(k / NT), bounds the k-th largest of those pairs
+// (distinct columns) from below, and one histogram level over the pairs
+// brings lo up to the lower edge of the bin holding their k-th largest, which
+// never exceeds the row's k-th largest key.  One pass then lists the
+// keys >= lo (a few k of the row) in LDS as (key << 32 | ~column), placed by a
+// block scan, and the selection runs on that list: a histogram descent with
+// bins scaled to [lo, hi] down to a window of at most kTieLds keys (ranked
+// directly, key desc and column asc) or a single key value (its lowest columns
+// by two 11-bit passes over the column index).  A list that would not fit LDS
+// (heavy ties at lo) is handled the same way over the registers.  Winners go
+// to an LDS bitmap of the row, written in ascending column order.
+// ---------------------------------------------------------------------------
+constexpr int kTrThreads = 1024;
+constexpr int kTrMaxV4 = 9;                            // float4 slots per thread at most
+constexpr int kTrMaxCols = kTrThreads * kTrMaxV4 * 4;  // 36,864 columns
+constexpr int kTrList = 8192;                          // keys >= lo held in LDS
+
+template <int NV4>
+__global__ __launch_bounds__(kTrThreads) void k_topk_reg(const float* __restrict__ scores, int64_t n_cols,
+                                                            const int64_t* __restrict__ pos, int m, int k,
+                                                            int32_t* __restrict__ idx) {
+    constexpr int NT = kTrThreads, NW = NT / 64;
+    constexpr int NCOL = NV4 * NT * 4;
+    static_assert(NCOL < (1 << 22), "columns fit two 11-bit passes");
+    constexpr int BMW = (NCOL / 32 + NT - 1) / NT * NT;  // bitmap words, whole per-thread runs
+    __shared__ uint32_t h[4096];
+    __shared__ uint32_t bm[BMW];
+    __shared__ uint64_t cl[kTrList];
+    __shared__ uint64_t tie[kTieLds];
+    __shared__ int wsum[NW];
+    __shared__ uint32_t red[3 * NW];
+    __shared__ int bc[4];
+    __shared__ uint32_t lctr[1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t t = blockIdx.x;
+    const int nv = (int)row_visible(pos, t, m, n_cols);
+    int32_t* out = idx + t * (int64_t)k;
+    if (nv <= k) {
+        for (int a = tid; a < k; a += NT) out[a] = a < nv ? a : -1;
+        return;
+    }
+    const float* row = scores + t * n_cols;
+
+    // ---- the row in registers: slot i holds columns 4 (i NT + tid) .. +3; key 0 = not visible ----
+    // (every load is issued before any is used: a conversion next to its load would make
+    // each slot wait for the previous one)
+    uint32_t key[NV4][4];
+    {
+        v4f raw[NV4];
+        if (((uintptr_t)row & 15) == 0) {
+#pragma unroll
+            for (int i = 0; i < NV4; ++i) {
+                const int c = 4 * (i * NT + tid);
+                raw[i] = c + 4 <= nv ? __builtin_nontemporal_load((const v4f*)(row + c)) : v4f{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int i = 0; i < NV4; ++i) {
+                const int c = 4 * (i * NT + tid);
+                if (c < nv && c + 4 > nv)  // the slot holding the row's last visible columns
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) raw[i][e] = c + e < nv ? row[c + e] : 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NV4; ++i) {
+                const int c = 4 * (i * NT + tid);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) raw[i][e] = c + e < nv ? row[c + e] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NV4; ++i) {
+            const int c = 4 * (i * NT + tid);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) key[i][e] = c + e < nv ? f32_order_key(raw[i][e]) : 0u;
+        }
+    }
+    for (int i = tid; i < BMW; i += NT) bm[i] = 0;
+    for (int i = tid; i < 4096; i += NT) h[i] = 0;
+    if (tid == 0) lctr[0] = 0;
+    auto for_cols = [&](auto fn) {
+#pragma unroll
+        for (int i = 0; i < NV4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) fn(key[i][e], (uint32_t)(4 * (i * NT + tid) + e));
+    };
+    auto for_keys = [&](auto fn) { for_cols([&](uint32_t x, uint32_t) { fn(x); }); };
+
+    // ---- hi = the row's largest key; lo = the smallest j-th largest key of the threads holding >= j ----
+    static_assert(2 * NT >= 2048, "j <= 2 for k <= 2048");
+    const int j = (k + NT - 1) / NT;          // 1 or 2
+    uint32_t t1 = 0, t2 = 0;                  // this thread's two largest keys
+    int nk = 0;
+    for_keys([&](uint32_t x) {
+        t2 = max(t2, min(t1, x));
+        t1 = max(t1, x);
+        nk += x != 0u;
+    });
+    uint32_t lo, hi;
+    bool tight;
+    {
+        const bool part = nk >= j;
+        uint32_t mx = t1, mn = part ? (j == 1 ? t1 : t2) : 0xFFFFFFFFu;
+        const uint32_t np = (uint32_t)__popcll(__ballot(part));
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+            mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+        }
+        if (lane == 0) {
+            red[wave] = mx;
+            red[NW + wave] = mn;
+            red[2 * NW + wave] = np;
+        }
+        __syncthreads();
+        hi = red[0];
+        lo = red[NW];
+        uint32_t npart = red[2 * NW];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {
+            hi = max(hi, red[w]);
+            lo = min(lo, red[NW + w]);
+            npart += red[2 * NW + w];
+        }
+        tight = (int64_t)npart * j >= k;
+        if (!tight) lo = 1;  // too few full threads: every visible key (all > 0)
+    }
+    if (tight) {
+        // the k-th largest of the threads' pairs (t1, t2), >= lo, is <= the row's k-th largest key:
+        // 256 bins scaled to [lo, hi] over those 2 NT keys, scanned from the top by wave 0, and lo
+        // moves up to the lower edge of the bin holding that k-th largest
+        int s = 0;
+        while ((((uint64_t)hi - lo) >> s) >= 256) ++s;
+        if (t1 >= lo) atomicAdd(&h[255 - ((t1 - lo) >> s)], 1u);
+        if (t2 >= lo) atomicAdd(&h[255 - ((t2 - lo) >> s)], 1u);
+        __syncthreads();
+        if (wave == 0) {
+            // lane l holds ranks 4l .. 4l+3 from the top (bins 255-4l .. 252-4l)
+            const uint4 c = *(const uint4*)&h[4 * lane];
+            const int sum4 = (int)(c.x + c.y + c.z + c.w);
+            const int incl = wave_incl_scan(sum4);
+            const int before = incl - sum4;
+            if (before < k && incl >= k) {
+                int run = before, r = 4 * lane;
+                const int cc[4] = {(int)c.x, (int)c.y, (int)c.z, (int)c.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (run < k) {
+                        run += cc[q];
+                        r = 4 * lane + q;
+                    }
+                bc[0] = 255 - r;  // the bin whose running count from the top reaches k
+            }
+        }
+        __syncthreads();
+        lo = lo + ((uint32_t)bc[0] << s);
+        if (tid < 256) h[tid] = 0;  // read by wave 0 only, before the barrier above
+    }
+
+    // ---- list the keys >= lo (block scan; no atomics) when they fit ----
+    int cnt = 0;
+    for_keys([&](uint32_t x) { cnt += x >= lo; });
+    int n_c;
+    int off = tm_scan<NT>(cnt, wsum, n_c);
+    const bool listed = n_c <= kTrList;
+    if (listed)
+        for_cols([&](uint32_t x, uint32_t col) {
+            if (x >= lo) cl[off++] = ((uint64_t)x << 32) | (uint32_t)~col;
+        });
+    __syncthreads();
+    // visit the candidates: the list, or every key in registers
+    auto for_cand = [&](auto fn) {
+        if (listed) {
+            for (int i = tid; i < n_c; i += NT) {
+                const uint64_t c = cl[i];
+                fn((uint32_t)(c >> 32), ~(uint32_t)c);
+            }
+        } else {
+            for_cols(fn);
+        }
+    };
+
+    // ---- the window holding the k-th largest key ----
+    uint32_t wbase;
+    int wsh, above, nb;
+    hist_descend<NT>([&](auto fn) { for_cand([&](uint32_t x, uint32_t) { fn(x); }); }, lo, hi, k, kTieLds, h, wsum,
+                     bc, wbase, wsh, above, nb);
+    const uint64_t wtop = (uint64_t)wbase + ((uint64_t)1 << wsh);
+    const int need = k - above;  // >= 1 winners inside the window
+    const int nwords = (nv + 31) / 32;
+    const int perw = (nwords + NT - 1) / NT;  // word w at (w % perw) * NT + w / perw (conflict-free emission)
+    auto mark = [&](uint32_t col) {
+        const uint32_t wd = col >> 5;
+        atomicOr(&bm[(wd % perw) * NT + wd / perw], 1u << (col & 31));
+    };
+    for_cand([&](uint32_t x, uint32_t col) {
+        if ((uint64_t)x >= wtop) mark(col);
+        else if (nb <= kTieLds && x >= wbase) tie[atomicAdd(&lctr[0], 1u)] = ((uint64_t)x << 32) | (uint32_t)~col;
+    });
+    __syncthreads();
+    if (nb <= kTieLds) {
+        // (key desc, column asc) is (key << 32 | ~column) desc: rank each window entry directly
+        for (int q = tid; q < nb; q += NT) {
+            const uint64_t e = tie[q];
+            int rank = 0;
+            for (int r = 0; r < nb; ++r) rank += tie[r] > e ? 1 : 0;
+            if (rank < need) mark(~(uint32_t)e);
+        }
+    } else {
+        // one key value (wbase) held by more than kTieLds keys: the need lowest columns among them
+        const uint32_t thr = wbase;
+        uint32_t pre = 0, pm = 0;
+        int nl = need;
+        for (int sh = 11; sh >= 0; sh -= 11) {
+            for (int i = tid; i < 2048; i += NT) h[i] = 0;
+            __syncthreads();
+            for_cand([&](uint32_t x, uint32_t col) {
+                if (x == thr && (col & pm) == pre) atomicAdd(&h[tm_pos<2048, NT>(2047 - ((col >> sh) & 0x7FF))], 1u);
+            });
+            __syncthreads();
+            int ab;
+            const uint32_t bn = 2047u - (uint32_t)tm_find<2048, NT>(h, nl, wsum, bc, ab);
+            nl -= ab;
+            pre |= bn << sh;
+            pm |= 0x7FFu << sh;
+        }
+        for_cand([&](uint32_t x, uint32_t col) {
+            if (x == thr && col <= pre) mark(col);
+        });
+    }
+    __syncthreads();
+    // ---- emit in ascending order: thread t owns words t*perw .. t*perw+perw-1 ----
+    int nm = 0;
+    for (int i = 0; i < perw; ++i) nm += __popc(bm[i * NT + tid]);
+    int tot;
+    int o = tm_scan<NT>(nm, wsum, tot);
+    for (int i = 0; i < perw; ++i) {
+        uint32_t b = bm[i * NT + tid];
+        const int wi = tid * perw + i;
+        while (b) {
+            const int bit = __builtin_ctz(b);
+            if (o < k) out[o] = wi * 32 + bit;
+            ++o;
+            b &= b - 1;
+        }
+    }
+}
+
 // few rows longer than k_topk_stream takes: selection from the row summary
 static bool topk_summ(int64_t T, int64_t n_cols) { return T < kTopkMaxRows && n_cols > kTsMaxCols; }
 // k_topk_cand workgroups per row (about 256 in all) and candidates each may write
@@ -1032,6 +1284,16 @@ hipError_t launch_topk(const float* scores, int64_t T, int64_t n_cols, const int
                            summ, S, kSliceCap, recs, cands);
         hipLaunchKernelGGL(k_topk_pick, dim3((unsigned)T), dim3(kTopkThreads), 0, st, scores, n_cols, pos, m, k, S,
                            kSliceCap, recs, cands, idx);
+    } else if (n_cols <= kTrMaxCols) {
+        const dim3 g((unsigned)T), b(kTrThreads);
+        if (n_cols <= kTrThreads * 4)
+            hipLaunchKernelGGL(k_topk_reg<1>, g, b, 0, st, scores, n_cols, pos, m, k, idx);
+        else if (n_cols <= kTrThreads * 8)
+            hipLaunchKernelGGL(k_topk_reg<2>, g, b, 0, st, scores, n_cols, pos, m, k, idx);
+        else if (n_cols <= kTrThreads * 16)
+            hipLaunchKernelGGL(k_topk_reg<4>, g, b, 0, st, scores, n_cols, pos, m, k, idx);
+        else
+            hipLaunchKernelGGL(k_topk_reg<kTrMaxV4>, g, b, 0, st, scores, n_cols, pos, m, k, idx);
     } else if (n_cols <= kTsMaxCols) {
         hipLaunchKernelGGL(k_topk_stream, dim3((unsigned)T), dim3(kTsThreads), 0, st, scores, n_cols, pos, m, k, idx);
     } else {

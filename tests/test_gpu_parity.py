@@ -177,11 +177,18 @@ def test_index_scores_bit_exact(lib, dev, gen, orc, T, h_i, d_i, N, B, m, n_cols
     (8, 3000, 1024, 4, "short"),        # some rows see fewer than k columns
     (5, 2048, 2048, 1, "normal"),
     (4, 70000, 1024, 4, "allequal"),
-    # many rows (one workgroup per row, row streamed from global memory)
+    # many rows of up to 36,864 columns (one workgroup per row, the row held in registers)
     (160, 16384, 512, 4, "ties"),       # equal keys beyond the direct-ranking limit
-    (128, 8192, 1024, 4, "allequal"),   # boundary bin larger than the LDS list
-    (136, 65536, 2048, 4, "normal"),    # longest rows of this path
+    (128, 8192, 1024, 4, "allequal"),   # one key value: the lowest columns by column passes
     (200, 20000, 1024, 4, "short"),
+    (144, 36864, 2048, 4, "normal"),    # widest rows of this path; 4th largest key per thread
+    (130, 36863, 1500, 4, "signed"),    # odd length: unaligned rows load by element; 3rd largest
+    (129, 4097, 1024, 4, "ties"),
+    (150, 18433, 513, 4, "short"),
+    (140, 3000, 1, 1, "normal"),
+    # many rows, longer (one workgroup per row, row streamed from global memory)
+    (136, 65536, 2048, 4, "normal"),    # longest rows of this path
+    (128, 40000, 1024, 4, "ties"),
     # few long rows (selection from the row summary)
     (4, 262144, 1024, 4, "normal"),
     (8, 100000, 2048, 4, "ties"),       # candidates overflow LDS: whole-row selection
@@ -199,6 +206,8 @@ def test_topk_bit_exact(lib, dev, orc, T, n_cols, k, m, kind):
     elif kind == "allequal":
         scores = np.zeros((T, n_cols), np.float32)
         scores[:, ::7] = -0.0
+    elif kind == "signed":
+        scores = rng.standard_normal((T, n_cols)).astype(np.float32) * 10
     else:
         scores = np.abs(rng.standard_normal((T, n_cols))).astype(np.float32) * 10
     if kind == "short":

@@ -106,8 +106,13 @@ class DecodeSet:
         import compressed_sparse_long_compress_amd as csa
 
         wl = self.wl
-        csa.csa_index_scores(self.iq, self.iqs, self.w, self.seq, self.pos, self.keys[r], wl["m"], wl["n_cols"],
-                             out=self.scores, topk_ws=self.tws)
+        if wl.get("tokens", 1) > 1:
+            # rows of a sequence adjacent: each sequence's keys streamed once for all its rows
+            csa.csa_index_scores_grouped(self.iq, self.iqs, self.w, self.seq, self.pos, self.keys[r], wl["m"],
+                                         wl["n_cols"], wl["tokens"], out=self.scores, topk_ws=self.tws)
+        else:
+            csa.csa_index_scores(self.iq, self.iqs, self.w, self.seq, self.pos, self.keys[r], wl["m"], wl["n_cols"],
+                                 out=self.scores, topk_ws=self.tws)
 
     def topk(self, r):
         import compressed_sparse_long_compress_amd as csa
@@ -310,9 +315,10 @@ def run_workload(name, steps, warmup):
 
 
 def secondary(steps, warmup):
-    """The other workloads (opt-in): 64K CSA decode, 1M HCA decode, chunked prefill."""
+    """The other workloads (opt-in): 1M CSA decode with two query rows per sequence, 64K CSA
+    decode, 1M HCA decode, chunked prefill."""
     res = {}
-    for name in ("csa_decode_64k", "hca_decode_1m"):
+    for name in ("csa_decode_1m_mtp2", "csa_decode_64k", "hca_decode_1m"):
         wl, ds, sec = run_workload(name, steps, warmup)
         res[name] = {"queries_per_s": wl["T"] * steps / sec, "ms_per_step": sec / steps * 1e3}
         del ds
@@ -329,7 +335,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--all", action="store_true", help="also time the other workloads (secondary object)")
     ap.add_argument("--workload", default="csa_decode_1m",
-                    choices=["csa_decode_1m", "csa_decode_64k", "hca_decode_1m", "prefill_chunk"],
+                    choices=["csa_decode_1m", "csa_decode_1m_mtp2", "csa_decode_64k", "hca_decode_1m",
+                             "prefill_chunk"],
                     help="time only this workload and print its line (profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true",

@@ -37,6 +37,8 @@ class _IdxKeys(ctypes.Structure):
 _vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 _lib.csa_compress.argtypes = [_vp, _vp, _i64, _i64, _i32, _i32, _f32, _i32, _Kv, _vp]
 _lib.csa_index_scores.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _IdxKeys, _i32, _i64, _vp, _vp, _sz, _vp]
+_lib.csa_index_scores_grouped.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _IdxKeys, _i32, _i64, _i32, _vp,
+                                          _vp, _sz, _vp]
 _lib.csa_topk_workspace.restype = _sz
 _lib.csa_topk_workspace.argtypes = [_i64, _i64, _i32]
 _lib.csa_topk.argtypes = [_vp, _i64, _i64, _vp, _i32, _i32, _vp, _vp, _sz, ctypes.c_uint32, _vp]
@@ -50,7 +52,7 @@ _lib.hca_dense_mqa.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _Kv,
 _lib.csa_last_error.restype = ctypes.c_char_p
 _lib.csa_version.restype = ctypes.c_int
 
-EXPORTS = ["csa_compress", "csa_index_scores", "csa_topk_workspace", "csa_topk", "csa_mqa_workspace",
+EXPORTS = ["csa_compress", "csa_index_scores", "csa_index_scores_grouped", "csa_topk_workspace", "csa_topk", "csa_mqa_workspace",
            "csa_sparse_mqa", "hca_dense_mqa", "csa_last_error", "csa_version"]
 
 
@@ -173,6 +175,32 @@ def csa_index_scores(q, q_scale, w, seq, pos, keys, m, n_cols, out=None, topk_ws
     _check(_lib.csa_index_scores(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(seq), _ptr(pos), T, h_i, d_i, keys.c(), int(m),
                                  int(n_cols), _ptr(out), _ptr(topk_ws), topk_ws.numel() if topk_ws is not None else 0,
                                  _stream()))
+    return out
+
+
+def csa_index_scores_grouped(q, q_scale, w, seq, pos, keys, m, n_cols, group, out=None, topk_ws=None):
+    """csa_index_scores for rows in groups of `group` (1, 2 or 4) that share a sequence
+    (multi-token decode): each group streams its keys once.  Same result as
+    csa_index_scores for any seq / pos."""
+    _need(q, "q", torch.uint8, 3)
+    _need(q_scale, "q_scale", torch.uint8, 3)
+    _need(w, "w", torch.float32, 2)
+    _need(seq, "seq", torch.int32, 1)
+    _need(pos, "pos", torch.int64, 1)
+    T, h_i, half = q.shape
+    d_i = half * 2
+    if d_i != keys.d_i or tuple(q_scale.shape) != (T, h_i, d_i // 32) or tuple(w.shape) != (T, h_i):
+        raise ValueError("indexer query shapes disagree")
+    if seq.shape[0] != T or pos.shape[0] != T:
+        raise ValueError("seq / pos must have T entries")
+    if out is None:
+        out = torch.empty(T, n_cols, dtype=torch.float32, device=q.device)
+    _need(out, "scores", torch.float32, 2)
+    if tuple(out.shape) != (T, n_cols):
+        raise ValueError("scores must be [T, n_cols]")
+    _check(_lib.csa_index_scores_grouped(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(seq), _ptr(pos), T, h_i, d_i, keys.c(),
+                                         int(m), int(n_cols), int(group), _ptr(out), _ptr(topk_ws),
+                                         topk_ws.numel() if topk_ws is not None else 0, _stream()))
     return out
 
 

@@ -99,30 +99,65 @@ int csa_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t 
     return hip_status(e, fn);
 }
 
-int csa_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
-                     const int64_t* pos, int64_t T, int32_t h_i, int32_t d_i, csa_index_keys_t keys, int32_t m,
-                     int64_t n_cols, float* scores, void* topk_ws, size_t topk_ws_bytes, csa_stream_t stream) {
-    const char* fn = "csa_index_scores";
+// shared by the two indexer entry points: argument checks and the row-summary destination
+static int index_args(const char* fn, const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
+                      const int64_t* pos, int64_t T, int32_t h_i, int32_t d_i, const csa_index_keys_t& keys, int32_t m,
+                      int64_t n_cols, const float* scores, void* topk_ws, size_t topk_ws_bytes, uint32_t** gmax,
+                      bool* nothing) {
+    *gmax = nullptr;
+    *nothing = false;
     if (T < 0 || n_cols < 0) return fail(CSA_EINVAL, "%s: T and n_cols must be >= 0", fn);
     if (h_i != 4 && h_i != 8) return fail(CSA_EUNSUPPORTED, "%s: h_i=%d unsupported (4 or 8)", fn, h_i);
     if (d_i != 64 && d_i != 128) return fail(CSA_EUNSUPPORTED, "%s: d_i=%d unsupported (64 or 128)", fn, d_i);
     if (m < 1) return fail(CSA_EINVAL, "%s: m must be >= 1", fn);
-    if (T == 0 || n_cols == 0) return ok();
+    if (T == 0 || n_cols == 0) {
+        *nothing = true;
+        return ok();
+    }
     if (!q || !q_scale || !w || !seq || !pos || !keys.data || !keys.scale || !scores)
         return fail(CSA_EINVAL, "%s: null pointer argument", fn);
     if (keys.cap < n_cols) return fail(CSA_EINVAL, "%s: n_cols (%lld) > keys.cap (%lld)", fn, (long long)n_cols,
                                        (long long)keys.cap);
     if (!aligned16(q) || !aligned16(keys.data)) return fail(CSA_EINVAL, "%s: q and keys.data must be 16-byte aligned", fn);
-    uint32_t* gmax = nullptr;
     if (topk_ws && csa::topk_uses_summary(T, n_cols)) {
         // the row summaries are the top-k workspace
         if (topk_ws_bytes < csa::topk_workspace_bytes(T, n_cols, 1))
             return fail(CSA_EWORKSPACE, "%s: top-k workspace too small for the row summaries", fn);
         if (((uintptr_t)topk_ws & 255u) != 0) return fail(CSA_EINVAL, "%s: workspace must be 256-byte aligned", fn);
-        gmax = (uint32_t*)topk_ws;
+        *gmax = (uint32_t*)topk_ws;
     }
+    return ok();
+}
+
+int csa_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
+                     const int64_t* pos, int64_t T, int32_t h_i, int32_t d_i, csa_index_keys_t keys, int32_t m,
+                     int64_t n_cols, float* scores, void* topk_ws, size_t topk_ws_bytes, csa_stream_t stream) {
+    const char* fn = "csa_index_scores";
+    uint32_t* gmax;
+    bool nothing;
+    const int rc = index_args(fn, q, q_scale, w, seq, pos, T, h_i, d_i, keys, m, n_cols, scores, topk_ws,
+                              topk_ws_bytes, &gmax, &nothing);
+    if (rc != CSA_OK || nothing) return rc;
     hipError_t e = csa::launch_index_scores(q, q_scale, w, seq, pos, T, h_i, d_i, keys.data, keys.scale, keys.cap, m,
                                             n_cols, scores, gmax, (hipStream_t)stream);
+    return hip_status(e, fn);
+}
+
+int csa_index_scores_grouped(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
+                             const int64_t* pos, int64_t T, int32_t h_i, int32_t d_i, csa_index_keys_t keys,
+                             int32_t m, int64_t n_cols, int32_t group, float* scores, void* topk_ws,
+                             size_t topk_ws_bytes, csa_stream_t stream) {
+    const char* fn = "csa_index_scores_grouped";
+    if (group != 1 && group != 2 && group != 4)
+        return fail(CSA_EUNSUPPORTED, "%s: group=%d unsupported (1, 2 or 4)", fn, group);
+    if (T > 0 && T % group != 0) return fail(CSA_EINVAL, "%s: T (%lld) must be a multiple of group", fn, (long long)T);
+    uint32_t* gmax;
+    bool nothing;
+    const int rc = index_args(fn, q, q_scale, w, seq, pos, T, h_i, d_i, keys, m, n_cols, scores, topk_ws,
+                              topk_ws_bytes, &gmax, &nothing);
+    if (rc != CSA_OK || nothing) return rc;
+    hipError_t e = csa::launch_index_scores_grouped(q, q_scale, w, seq, pos, T, h_i, d_i, keys.data, keys.scale,
+                                                    keys.cap, m, n_cols, group, scores, gmax, (hipStream_t)stream);
     return hip_status(e, fn);
 }
 

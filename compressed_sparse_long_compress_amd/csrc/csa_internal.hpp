@@ -29,6 +29,11 @@ hipError_t launch_index_scores(const uint8_t* q, const uint8_t* q_scale, const f
                                const int64_t* pos, int64_t T, int h_i, int d_i, const uint8_t* kdata,
                                const uint8_t* kscale, int64_t kcap, int m, int64_t n_cols, float* scores,
                                uint32_t* gmax, hipStream_t st);
+// rows g*group .. g*group+group-1 share each key stream (group 1, 2 or 4; T % group == 0)
+hipError_t launch_index_scores_grouped(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
+                                       const int64_t* pos, int64_t T, int h_i, int d_i, const uint8_t* kdata,
+                                       const uint8_t* kscale, int64_t kcap, int m, int64_t n_cols, int group,
+                                       float* scores, uint32_t* gmax, hipStream_t st);
 
 size_t topk_workspace_bytes(int64_t T, int64_t n_cols, int k);
 // true when the top-k for this shape uses the row summaries (few long rows)

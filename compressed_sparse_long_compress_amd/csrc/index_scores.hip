@@ -122,6 +122,158 @@ __global__ __launch_bounds__(256) void k_index_rows(const uint8_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// grouped decode (several query rows of one sequence per step, e.g. the draft
+// tokens of multi-token prediction): grid (key chunks, T / R).  The R rows of
+// a group share every key fragment: MFMA rows = (row, head) pairs, 16 per
+// 16x16x128 tile, NA = ceil(R HI / 16) tiles per key tile, so the keys are
+// streamed once per group.  Lane group g of tile a holds MFMA rows
+// 16a + 4g .. +3: four heads of one row; with HI = 8 a row spans two lane
+// groups, summed by a row swap.  Rows of a group on another sequence than
+// its first row are handled in a pass of their own (their A rows zeroed in
+// the other passes), so every layout gives the plain kernel's scores.
+// ---------------------------------------------------------------------------
+template <int DI, int R, int HI>
+__global__ __launch_bounds__(256) void k_index_rows_grp(const uint8_t* __restrict__ q,
+                                                        const uint8_t* __restrict__ q_scale,
+                                                        const float* __restrict__ w, const int32_t* __restrict__ seq,
+                                                        const int64_t* __restrict__ pos,
+                                                        const uint8_t* __restrict__ kdata,
+                                                        const uint8_t* __restrict__ kscale, int64_t kcap, int m,
+                                                        int64_t n_cols, int64_t chunk, float* __restrict__ scores,
+                                                        uint32_t* __restrict__ gmax) {
+    constexpr int KB = DI / 2;            // bytes per key
+    constexpr int NB = DI / 32;           // scale blocks per key
+    constexpr int U = 8;                  // key tiles of 16 per wave step
+    constexpr int NA = (R * HI + 15) / 16;
+    constexpr int GPQ = HI / 4;           // lane groups per row in a tile
+    static_assert(16 * U == 4 * kTopkGroup, "one wave step = four summary groups");
+    static_assert(R * HI <= 32 && (HI == 4 || HI == 8), "at most two tiles of (row, head) pairs");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t t0 = (int64_t)blockIdx.y * R;
+    const int64_t c0 = (int64_t)blockIdx.x * chunk;
+    const int64_t c1 = c0 + chunk < n_cols ? c0 + chunk : n_cols;
+    const int64_t ng = topk_groups(n_cols);
+
+    int64_t nvr[R];
+    int32_t sr[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        nvr[i] = (pos[t0 + i] + 1) / m;
+        if (nvr[i] > n_cols) nvr[i] = n_cols;
+        sr[i] = seq[t0 + i];
+    }
+    uint32_t todo = (1u << R) - 1;
+    while (todo) {
+        const int first = __builtin_ctz(todo);
+        int32_t s = sr[0];
+#pragma unroll
+        for (int i = 1; i < R; ++i) s = i == first ? sr[i] : s;
+        uint32_t mask = 0;
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+            if (((todo >> i) & 1u) && sr[i] == s) mask |= 1u << i;
+        todo &= ~mask;
+
+        // A of tile a: lane (r, g) = MFMA row 16a + r = (row qa, head ha), block g of its query vector
+        v8i a[NA];
+        int sa[NA];
+        // this lane group's row in tile a (-1: none in this pass), its head weights, visible count, output
+        int qrow[NA];
+        float wr[NA][4];
+        int64_t nvl[NA];
+        float* orow[NA];
+        int64_t nv_max = 0;
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+            if ((mask >> i) & 1u) nv_max = nvr[i] > nv_max ? nvr[i] : nv_max;
+#pragma unroll
+        for (int at = 0; at < NA; ++at) {
+            const int qa = (16 * at + r) / HI, ha = (16 * at + r) % HI;
+            a[at] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+            sa[at] = 127;
+            if (qa < R && ((mask >> qa) & 1u) && g < NB) {
+                a[at] = frag16(q + ((t0 + qa) * HI + ha) * KB + g * 16);
+                sa[at] = q_scale[((t0 + qa) * HI + ha) * NB + g];
+            }
+            const int qg = (16 * at + 4 * g) / HI, hb = (16 * at + 4 * g) % HI;
+            const bool live = qg < R && ((mask >> qg) & 1u);
+            qrow[at] = live ? qg : -1;
+            int64_t nv = 0;
+#pragma unroll
+            for (int i = 0; i < R; ++i) nv = i == qg ? nvr[i] : nv;
+            nvl[at] = live ? nv : 0;
+            orow[at] = scores + (t0 + (live ? qg : 0)) * n_cols;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wr[at][i] = live ? w[(t0 + qg) * HI + hb + i] : 0.f;
+        }
+        const int64_t base = (int64_t)s * kcap;
+
+        for (int64_t j0 = c0 + (int64_t)wave * 16 * U; j0 < c1; j0 += 4 * 16 * U) {
+            uint32_t gm[NA][4];  // per tile and summary group of this step: the lane group's largest visible key
+#pragma unroll
+            for (int at = 0; at < NA; ++at) gm[at][0] = gm[at][1] = gm[at][2] = gm[at][3] = 0u;
+            v4i bk[U];
+            int sb[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t j = j0 + u * 16 + r;
+                if (j < nv_max && g < NB) {
+                    bk[u] = __builtin_nontemporal_load((const v4i*)(kdata + (base + j) * KB + g * 16));
+                    sb[u] = kscale[(base + j) * NB + g];
+                } else {
+                    bk[u] = v4i{0, 0, 0, 0};
+                    sb[u] = 127;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const v8i bf = {bk[u][0], bk[u][1], bk[u][2], bk[u][3], 0, 0, 0, 0};
+                const int64_t j = j0 + u * 16 + r;
+#pragma unroll
+                for (int at = 0; at < NA; ++at) {
+                    v4f acc = {0.f, 0.f, 0.f, 0.f};
+                    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[at], bf, acc, 4, 4, 0, sa[at], 0, sb[u]);
+                    float p = wr[at][0] * fmaxf(acc[0], 0.f);
+                    p = fmaf(wr[at][1], fmaxf(acc[1], 0.f), p);
+                    p = fmaf(wr[at][2], fmaxf(acc[2], 0.f), p);
+                    p = fmaf(wr[at][3], fmaxf(acc[3], 0.f), p);
+                    if (GPQ == 2) {
+                        // the row's two lane groups (exact: every partial sum is representable)
+                        const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+                        p = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+                    }
+                    if (qrow[at] >= 0 && (g % GPQ) == 0 && j < c1) {
+                        orow[at][j] = j < nvl[at] ? p : -INFINITY;
+                        if (j < nvl[at]) gm[at][u / (U / 4)] = max(gm[at][u / (U / 4)], f32_order_key(p));
+                    }
+                }
+            }
+            if (gmax) {
+                // per lane group: unsigned max over its 16 lanes of four values, lanes 4G..4G+3 ending with
+                // group G (mirror exchanges within the 16-lane row, then quad reductions)
+                const bool hi8 = (lane & 8) != 0, hi4 = (lane & 4) != 0;
+#pragma unroll
+                for (int at = 0; at < NA; ++at) {
+                    const uint32_t s0 = hi8 ? gm[at][0] : gm[at][2], s1 = hi8 ? gm[at][1] : gm[at][3];
+                    uint32_t k0 = hi8 ? gm[at][2] : gm[at][0], k1 = hi8 ? gm[at][3] : gm[at][1];
+                    k0 = max(k0, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s0, 0x140, 0xf, 0xf, false));  // row_mirror
+                    k1 = max(k1, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s1, 0x140, 0xf, 0xf, false));
+                    const uint32_t s2 = hi4 ? k0 : k1;
+                    uint32_t x = hi4 ? k1 : k0;
+                    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s2, 0x141, 0xf, 0xf, false));  // row_half_mirror
+                    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+                    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+                    const int64_t gi = j0 / kTopkGroup + (r >> 2);
+                    if (qrow[at] >= 0 && (g % GPQ) == 0 && (r & 3) == 0 && gi < ng)
+                        gmax[(t0 + qrow[at]) * ng + gi] = x;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // prefill: grid (key chunks, query tiles).  A row tile = 32 (query, head) rows
 // = 32/HI queries; each wave owns NA row tiles; keys stream 32 per step.
 // Rows of a wave that belong to different sequences are processed in one pass
@@ -318,5 +470,45 @@ hipError_t launch_index_scores(const uint8_t* q, const uint8_t* q_scale, const f
 #undef CSA_GEMM
     return hipGetLastError();
 }
+
+hipError_t launch_index_scores_grouped(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
+                                       const int64_t* pos, int64_t T, int h_i, int d_i, const uint8_t* kdata,
+                                       const uint8_t* kscale, int64_t kcap, int m, int64_t n_cols, int group,
+                                       float* scores, uint32_t* gmax, hipStream_t st) {
+    if (group == 1)
+        return launch_index_scores(q, q_scale, w, seq, pos, T, h_i, d_i, kdata, kscale, kcap, m, n_cols, scores, gmax,
+                                   st);
+    if (T == 0 || n_cols == 0) return hipSuccess;
+    const int64_t G = T / group;
+    // about 2048 workgroups, one 128-key step per wave at the 1M-context shape
+    int64_t chunk = (n_cols * G + 2047) / 2048;
+    chunk = ((chunk + 511) / 512) * 512;
+    if (chunk < 512) chunk = 512;
+    if (chunk > 16384) chunk = 16384;
+    const dim3 grid((unsigned)((n_cols + chunk - 1) / chunk), (unsigned)G), block(256);
+#define CSA_GRP(DI, R, HI)                                                                                         \
+    hipLaunchKernelGGL((k_index_rows_grp<DI, R, HI>), grid, block, 0, st, q, q_scale, w, seq, pos, kdata, kscale, \
+                       kcap, m, n_cols, chunk, scores, gmax)
+    if (d_i == 128) {
+        if (h_i == 8) {
+            if (group == 2) CSA_GRP(128, 2, 8);
+            else CSA_GRP(128, 4, 8);
+        } else {
+            if (group == 2) CSA_GRP(128, 2, 4);
+            else CSA_GRP(128, 4, 4);
+        }
+    } else {
+        if (h_i == 8) {
+            if (group == 2) CSA_GRP(64, 2, 8);
+            else CSA_GRP(64, 4, 8);
+        } else {
+            if (group == 2) CSA_GRP(64, 2, 4);
+            else CSA_GRP(64, 4, 4);
+        }
+    }
+#undef CSA_GRP
+    return hipGetLastError();
+}
+
 
 }  // namespace csa

@@ -13,6 +13,7 @@ Named workloads (seeds 101..105):
   csa_decode_64k B=32, L=65,536 (16,384 entries), 64 heads, d=512, k=1024
   hca_decode_1m  B=8,  L=1,048,576 at m'=128 (8,192 entries)
   csa_decode_1m  B=4,  L=1,048,576 (262,144 entries), 5% planted index keys
+  csa_decode_1m_mtp2  the same cache, two query rows per sequence (positions L-2, L-1)
   prefill_chunk  8,192 new tokens after a 131,072-token context (CSA + HCA)
 """
 import math
@@ -24,24 +25,28 @@ from . import entries, mxfp4, normal_bf16, normal_f32, pow2_weights
 ROPE_BASE = 10000.0
 
 
-def csa_decode(B, L, m=4, H=64, d=512, h_i=8, d_i=128, k=1024, W=128, plant_frac=0.0, seed=102, n_cols=None):
-    """One decode query per sequence at position L-1 over a pre-built cache."""
+def csa_decode(B, L, m=4, H=64, d=512, h_i=8, d_i=128, k=1024, W=128, plant_frac=0.0, seed=102, n_cols=None,
+               tokens=1):
+    """Decode over a pre-built cache: `tokens` query rows per sequence at the
+    positions L-tokens .. L-1 (tokens > 1: a multi-token step, e.g. the target
+    pass over draft tokens, rows of a sequence adjacent), T = B * tokens."""
     N = L // m
     dn = d - 64
+    T = B * tokens
     wl = dict(kind="csa_decode", B=B, L=L, m=m, H=H, d=d, h_i=h_i, d_i=d_i, k=k, W=W, N=N, seed=seed,
-              rope_base=ROPE_BASE, sm_scale=1.0 / math.sqrt(d), T=B, n_cols=N if n_cols is None else n_cols,
-              comp_cap=N, win_cap=W)
-    wl["pos"] = np.full(B, L - 1, dtype=np.int64)
-    wl["seq"] = np.arange(B, dtype=np.int32)
+              rope_base=ROPE_BASE, sm_scale=1.0 / math.sqrt(d), T=T, n_cols=N if n_cols is None else n_cols,
+              comp_cap=N, win_cap=W, tokens=tokens)
+    wl["pos"] = np.tile(np.arange(L - tokens, L, dtype=np.int64), B)
+    wl["seq"] = np.repeat(np.arange(B, dtype=np.int32), tokens)
     wl["comp"] = entries(seed, 20, B * N, dn)
     wl["win"] = entries(seed, 21, B * W, dn)
     kd, ks, planted = mxfp4(seed, 22, B * N, d_i, plant_frac=plant_frac)
     wl["keys"] = (kd, ks)
     wl["planted"] = planted
-    wl["q"] = normal_bf16(seed, 23, (B, H, d))
-    qd, qs, _ = mxfp4(seed, 24, B * h_i, d_i)
-    wl["iq"] = (qd.reshape(B, h_i, d_i // 2), qs.reshape(B, h_i, d_i // 32))
-    wl["w"] = pow2_weights(seed, 25, (B, h_i))
+    wl["q"] = normal_bf16(seed, 23, (T, H, d))
+    qd, qs, _ = mxfp4(seed, 24, T * h_i, d_i)
+    wl["iq"] = (qd.reshape(T, h_i, d_i // 2), qs.reshape(T, h_i, d_i // 32))
+    wl["w"] = pow2_weights(seed, 25, (T, h_i))
     return wl
 
 
@@ -107,6 +112,10 @@ def named(name, **over):
         return hca_decode(**kw)
     if name == "csa_decode_1m":
         kw = dict(B=4, L=1 << 20, plant_frac=0.05, seed=104)
+        kw.update(over)
+        return csa_decode(**kw)
+    if name == "csa_decode_1m_mtp2":
+        kw = dict(B=4, L=1 << 20, plant_frac=0.05, seed=104, tokens=2)
         kw.update(over)
         return csa_decode(**kw)
     if name == "prefill_chunk":

@@ -156,6 +156,26 @@ int csa_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, c
                      int64_t n_cols, float* scores, void* topk_ws, size_t topk_ws_bytes, csa_stream_t stream);
 
 /*
+ * csa_index_scores_grouped — csa_index_scores for query rows that come in
+ * groups of one sequence, as in multi-token decode (the pages keep
+ * multi-token prediction from V3: [xmsumi] § 四大架构创新; its draft tokens
+ * are extra query rows of the same sequence at the next positions).
+ *
+ * Rows g*group .. g*group+group-1 are expected to belong to one sequence; each
+ * group then streams its keys once for all its rows (group x h_i rows of the
+ * MXFP4 matrix product instead of h_i).  A row of a group whose sequence
+ * differs from the group's first row is handled in a separate pass, so the
+ * scores (and the row summary) equal those of csa_index_scores bit for bit
+ * for any seq / pos.
+ *   group  1, 2 or 4 (1 is csa_index_scores);  T % group == 0
+ * Every other argument, layout and workspace rule as csa_index_scores.
+ */
+int csa_index_scores_grouped(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
+                             const int64_t* pos, int64_t T, int32_t h_i, int32_t d_i, csa_index_keys_t keys,
+                             int32_t m, int64_t n_cols, int32_t group, float* scores, void* topk_ws,
+                             size_t topk_ws_bytes, csa_stream_t stream);
+
+/*
  * csa_topk — top-k selection ([xmsumi] § CSA: the top-k compressed entries
  * per query token; [hortopato] CSA list: k = 1024).
  *

@@ -65,6 +65,14 @@ def test_index_topk_validation(csa):
     p = ctypes.c_void_p(256)
     rc = L.csa_index_scores(p, p, p, p, p, 4, 8, 128, csa._IdxKeys(256, 256, 8), 4, 16, p, None, 0, None)
     assert rc == csa.CSA_EINVAL and b"keys.cap" in L.csa_last_error()
+    rc = L.csa_index_scores_grouped(p, p, p, p, p, 4, 8, 128, csa._IdxKeys(256, 256, 16), 4, 16, 3, p, None, 0, None)
+    assert rc == csa.CSA_EUNSUPPORTED and b"group=3" in L.csa_last_error()
+    rc = L.csa_index_scores_grouped(p, p, p, p, p, 6, 8, 128, csa._IdxKeys(256, 256, 16), 4, 16, 4, p, None, 0, None)
+    assert rc == csa.CSA_EINVAL and b"multiple of group" in L.csa_last_error()
+    rc = L.csa_index_scores_grouped(p, p, p, p, p, 4, 8, 128, csa._IdxKeys(256, 256, 8), 4, 16, 2, p, None, 0, None)
+    assert rc == csa.CSA_EINVAL and b"keys.cap" in L.csa_last_error()
+    rc = L.csa_index_scores_grouped(None, None, None, None, None, 0, 8, 128, keys, 4, 16, 2, None, None, 0, None)
+    assert rc == csa.CSA_OK  # empty call is a no-op
     rc = L.csa_topk(None, 4, 100, None, 4, 0, None, None, 0, 0, None)
     assert rc == csa.CSA_EUNSUPPORTED
     rc = L.csa_topk(None, 4, 100, None, 4, 4096, None, None, 0, 0, None)

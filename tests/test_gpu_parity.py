@@ -167,6 +167,72 @@ def test_index_scores_bit_exact(lib, dev, gen, orc, T, h_i, d_i, N, B, m, n_cols
     assert not bad.any(), f"{bad.sum()} scores differ; first at {np.argwhere(bad)[:3].tolist()}"
 
 
+@pytest.mark.parametrize("G,group,h_i,d_i,N,B,m,n_cols,layout", [
+    (4, 2, 8, 128, 5000, 4, 4, 5000, "mtp"),       # 4 sequences x 2 tokens at consecutive positions
+    (3, 4, 8, 128, 9000, 3, 4, 8990, "mtp"),       # 4 tokens: two matrix tiles per key tile; ragged columns
+    (5, 2, 4, 64, 700, 2, 4, 650, "mtp"),
+    (2, 4, 4, 128, 3000, 2, 2, 3000, "mtp"),       # h_i = 4: four rows in one tile
+    (6, 2, 8, 128, 4000, 3, 4, 4000, "mixed"),     # rows of a group on different sequences
+    (3, 4, 8, 64, 2500, 4, 4, 2500, "mixed"),
+])
+def test_index_scores_grouped_bit_exact(lib, dev, gen, orc, G, group, h_i, d_i, N, B, m, n_cols, layout):
+    """Multi-token decode: rows in groups of one sequence stream its keys once;
+    the scores equal the oracle's and the plain kernel's bit for bit, also when
+    a group's rows belong to different sequences."""
+    import torch
+
+    T = G * group
+    _say(f"grouped index G={G} group={group} h_i={h_i} d_i={d_i} N={N} n_cols={n_cols} {layout}")
+    rng = np.random.default_rng(T + N + group)
+    if layout == "mtp":
+        seq = np.repeat(np.arange(G) % B, group)
+        p0 = rng.integers(m * N // 2, m * N - group, size=G)
+        p0[0] = m * 37 - 1 - group // 2  # a group whose rows straddle a block boundary
+        pos = (p0[:, None] + np.arange(group)[None, :]).reshape(-1)
+    else:
+        seq = rng.integers(0, B, size=T)
+        pos = rng.integers(0, m * N, size=T)
+    qd, qs, w, seq, pos, kd, ks = _index_case(gen, 500 + T, T, h_i, d_i, N, B, pos, seq)
+    wit = orc.index_exact_witness(qd, qs, w, seq, pos, kd, ks, N, m, n_cols)
+    assert wit < 24, f"inputs break the fp32 exactness precondition ({wit:.1f} bits)"
+    ref = orc.index_scores(qd, qs, w, seq, pos, kd, ks, N, m, n_cols).astype(np.float32)
+    keys = dev.index_keys((kd, ks), N)
+    args = (dev.t(qd), dev.t(qs), dev.t(w), dev.t(seq), dev.t(pos), keys, m, n_cols)
+    got = lib.csa_index_scores_grouped(*args, group)
+    plain = lib.csa_index_scores(*args)
+    torch.cuda.synchronize()
+    got, plain = got.cpu().numpy(), plain.cpu().numpy()
+    bad = got.view(np.uint32) != ref.view(np.uint32)
+    assert not bad.any(), f"{bad.sum()} scores differ; first at {np.argwhere(bad)[:3].tolist()}"
+    assert np.array_equal(got.view(np.uint32), plain.view(np.uint32))
+
+
+def test_index_scores_grouped_summary_topk(lib, dev, gen, orc):
+    """Grouped indexer writing the row summary of long rows + csa_topk(prepared)
+    equals the oracle's selection."""
+    import torch
+
+    for (G, group, N, k, plant) in [(2, 2, 70000, 1024, 0.05), (2, 4, 100000, 2048, 0.02)]:
+        T = G * group
+        _say(f"grouped index + summary top-k G={G} group={group} N={N} k={k}")
+        seq = np.repeat(np.arange(G), group)
+        pos = np.repeat(np.full(G, 4 * N - group), group) + np.tile(np.arange(group), G)
+        pos = np.minimum(pos, 4 * N - 1)
+        qd, qs, w, seq, pos, kd, ks = _index_case(gen, 900 + T + N, T, 8, 128, N, G, pos, seq, plant=plant)
+        ref = orc.index_scores(qd, qs, w, seq, pos, kd, ks, N, 4, N).astype(np.float32)
+        ref_i = orc.topk(ref, pos, 4, k)
+        keys = dev.index_keys((kd, ks), N)
+        ws = torch.full((lib.csa_topk_workspace(T, N, k) + 256,), 0x5A, dtype=torch.uint8, device="cuda")
+        ws = ws[: lib.csa_topk_workspace(T, N, k)]
+        sc = lib.csa_index_scores_grouped(dev.t(qd), dev.t(qs), dev.t(w), dev.t(seq), dev.t(pos), keys, 4, N, group,
+                                          topk_ws=ws)
+        idx = lib.csa_topk(sc, dev.t(pos), 4, k, ws=ws, prepared=True)
+        torch.cuda.synchronize()
+        got = sc.cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+        assert np.array_equal(idx.cpu().numpy(), ref_i)
+
+
 # ---------------------------------------------------------------------------
 # csa_topk
 # ---------------------------------------------------------------------------

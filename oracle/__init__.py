@@ -47,6 +47,13 @@ def _load():
     lib.orc_rope64.argtypes = [vp, f64, f64, ctypes.c_int]
     lib.orc_compress.restype = ctypes.c_int
     lib.orc_compress.argtypes = [vp, vp, i64, i64, i32, i32, f64, i64, vp, vp, vp]
+    lib.orc_compress_channel.restype = ctypes.c_int
+    lib.orc_compress_channel.argtypes = [vp, vp, i64, i64, i32, i32, f64, i64, vp, vp, vp]
+    lib.orc_f64_to_e2m1.restype = ctypes.c_uint8
+    lib.orc_f64_to_e2m1.argtypes = [f64]
+    lib.orc_mxfp4_block.argtypes = [vp, ctypes.c_int, vp, vp]
+    lib.orc_compress_index_keys.restype = ctypes.c_int
+    lib.orc_compress_index_keys.argtypes = [vp, vp, i64, i64, i32, i32, i64, vp, vp]
     lib.orc_index_scores.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, vp, vp, i64, i32, i64, vp]
     lib.orc_topk.argtypes = [vp, i64, i64, vp, i32, i32, vp]
     lib.orc_attend.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32, i32, vp, vp, vp, i64, vp, vp, vp, i64, i32,
@@ -132,6 +139,51 @@ def compress(kv, logits, tok0, m, rope_base=10000.0):
     # entry J = tok0/m + b sits at slot J % nblk; put them back in order
     order = (tok0 // m + np.arange(nblk)) % nblk
     return nope[order], rope[order], scale[order]
+
+
+def compress_channel(kv, logits, tok0, m, rope_base=10000.0):
+    """Per-channel weights: kv [n_tok, d] bf16 bits, logits [n_tok, d] -> (nope, rope, scale), in order."""
+    kv = _c(kv, np.uint16)
+    logits = _c(logits, np.float32)
+    n_tok, d = kv.shape
+    assert logits.shape == (n_tok, d) and tok0 % m == 0 and n_tok % m == 0 and n_tok > 0
+    nblk = n_tok // m
+    nope = np.zeros((nblk, d - 64), np.uint8)
+    rope = np.zeros((nblk, 64), np.uint16)
+    scale = np.zeros(nblk, np.float32)
+    rc = _load().orc_compress_channel(_p(kv), _p(logits), tok0, n_tok, m, d, rope_base, nblk, _p(nope), _p(rope),
+                                      _p(scale))
+    assert rc == 0
+    order = (tok0 // m + np.arange(nblk)) % nblk
+    return nope[order], rope[order], scale[order]
+
+
+def f64_to_e2m1(x):
+    return int(_load().orc_f64_to_e2m1(float(x)))
+
+
+def mxfp4_block(c):
+    """32 values -> (codes [32] nibbles, E8M0 scale byte)."""
+    c = _c(c, np.float64)
+    codes = np.zeros(c.shape[0], np.uint8)
+    sb = np.zeros(1, np.uint8)
+    _load().orc_mxfp4_block(_p(c), c.shape[0], _p(codes), _p(sb))
+    return codes, int(sb[0])
+
+
+def compress_index_keys(k, logits, tok0, m):
+    """k [n_tok, d_i] bf16 bits, logits [n_tok] -> (data [n, d_i/2] packed E2M1, scale [n, d_i/32] E8M0), in order."""
+    k = _c(k, np.uint16)
+    logits = _c(logits, np.float32)
+    n_tok, d_i = k.shape
+    assert tok0 % m == 0 and n_tok % m == 0 and n_tok > 0
+    nblk = n_tok // m
+    data = np.zeros((nblk, d_i // 2), np.uint8)
+    scale = np.zeros((nblk, d_i // 32), np.uint8)
+    rc = _load().orc_compress_index_keys(_p(k), _p(logits), tok0, n_tok, m, d_i, nblk, _p(data), _p(scale))
+    assert rc == 0
+    order = (tok0 // m + np.arange(nblk)) % nblk
+    return data[order], scale[order]
 
 
 def compress_into(kv, logits, tok0, m, rope_base, nope, rope, scale):

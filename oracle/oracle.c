@@ -187,6 +187,122 @@ int orc_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t 
     return 0;
 }
 
+/* Per-channel compression weights (a variant of the reading above, where the
+   pages leave the shape of the weights open): logits is n_tok x d, and
+   channel e of block b merges its m tokens with weights softmax over
+   logits[bm+i][e], i < m.  Everything else as orc_compress. */
+int orc_compress_channel(const uint16_t* kv, const float* logits, int64_t tok0, int64_t n_tok, int32_t m, int32_t d,
+                         double rope_base, int64_t cap, uint8_t* nope, uint16_t* rope, float* scale) {
+    if (m <= 0 || tok0 % m != 0 || n_tok % m != 0 || d < 64 || cap <= 0) return -1;
+    const int dn = d - 64;
+    const int64_t nblk = n_tok / m;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t b = 0; b < nblk; ++b) {
+        double* c = (double*)calloc((size_t)d, sizeof(double));
+        for (int e = 0; e < d; ++e) {
+            /* softmax over the block's logits of channel e, then that channel's merge */
+            double mx = -INFINITY;
+            for (int i = 0; i < m; ++i) mx = fmax(mx, (double)logits[(b * m + i) * (int64_t)d + e]);
+            double z = 0.0;
+            for (int i = 0; i < m; ++i) z += exp((double)logits[(b * m + i) * (int64_t)d + e] - mx);
+            for (int i = 0; i < m; ++i) {
+                const double wi = exp((double)logits[(b * m + i) * (int64_t)d + e] - mx) / z;
+                c[e] += wi * orc_bf16_to_f64(kv[(b * m + i) * (int64_t)d + e]);
+            }
+        }
+        int64_t J = tok0 / m + b;
+        double pj = (double)((J + 1) * (int64_t)m - 1);
+        orc_rope64(c + dn, pj, rope_base, 0);
+        double amax = 0.0;
+        for (int e = 0; e < dn; ++e) amax = fmax(amax, fabs(c[e]));
+        float s = amax > 0.0 ? (float)(amax / 448.0) : 1.0f;
+        int64_t slot = J % cap;
+        scale[slot] = s;
+        for (int e = 0; e < dn; ++e) nope[slot * dn + e] = orc_f64_to_e4m3(c[e] / (double)s);
+        for (int e = 0; e < 64; ++e) rope[slot * 64 + e] = orc_f64_to_bf16(c[dn + e]);
+        free(c);
+    }
+    return 0;
+}
+
+/* x -> OCP E2M1 nibble: the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 to |x|
+   (ties to the even mantissa bit), saturating at 6; the sign bit is set for
+   x < 0 unless the magnitude code is 0 (zero is stored as +0). */
+uint8_t orc_f64_to_e2m1(double x) {
+    static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    const double a = fabs(x);
+    int best = 7;
+    if (a < 6.0) {
+        /* a lies in [mag[i], mag[i+1]) for one i; pick the nearer end, the even code on a tie */
+        int i = 0;
+        while (!(a < mag[i + 1])) ++i;
+        const double dl = a - mag[i], du = mag[i + 1] - a;
+        if (dl < du) best = i;
+        else if (du < dl) best = i + 1;
+        else best = (i & 1) ? i + 1 : i;
+    }
+    return (uint8_t)((x < 0.0 && best != 0 ? 8 : 0) | best);
+}
+
+/* One 32-element MXFP4 block ([zcldvi]: FP4 relevance scores; the format is
+   the OCP MX one): shared scale 2^(floor(log2 amax) - 2), the exponent of the
+   largest E2M1 value (6 = 1.5 x 2^2) subtracted, as the E8M0 byte (clamped
+   to 0..254); elements c / scale to E2M1.  An all-zero block gets byte 127
+   (scale 1) and zero codes.  codes: n nibbles, one per byte. */
+void orc_mxfp4_block(const double* c, int n, uint8_t* codes, uint8_t* scale_byte) {
+    double amax = 0.0;
+    for (int i = 0; i < n; ++i) amax = fmax(amax, fabs(c[i]));
+    if (amax == 0.0) {
+        *scale_byte = 127;
+        for (int i = 0; i < n; ++i) codes[i] = 0;
+        return;
+    }
+    int ex;
+    frexp(amax, &ex);  /* amax = f 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1 */
+    int b = (ex - 1) - 2 + 127;
+    if (b < 0) b = 0;
+    if (b > 254) b = 254;
+    *scale_byte = (uint8_t)b;
+    const double s = ldexp(1.0, b - 127);
+    for (int i = 0; i < n; ++i) codes[i] = orc_f64_to_e2m1(c[i] / s);
+}
+
+/* Index-key compression (the pages leave it open how the indexer's keys are
+   formed; reading: the same softmax-weighted merge of every m tokens as the
+   KV entries, no RoPE, then MXFP4 with one scale per 32 elements).
+   k: n_tok x d_i bf16; logits: n_tok.  Entry J = tok0/m + b goes to slot
+   J % cap: data[slot][d_i/2] (element 2i in the low nibble), scale[slot][d_i/32].
+   Returns 0, or -1 for a bad shape. */
+int orc_compress_index_keys(const uint16_t* k, const float* logits, int64_t tok0, int64_t n_tok, int32_t m,
+                            int32_t d_i, int64_t cap, uint8_t* data, uint8_t* scale) {
+    if (m <= 0 || tok0 % m != 0 || n_tok % m != 0 || d_i % 32 != 0 || d_i <= 0 || cap <= 0) return -1;
+    const int64_t nblk = n_tok / m;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t b = 0; b < nblk; ++b) {
+        double* w = (double*)malloc(sizeof(double) * (size_t)m);
+        double* c = (double*)calloc((size_t)d_i, sizeof(double));
+        uint8_t codes[32];
+        double mx = -INFINITY;
+        for (int i = 0; i < m; ++i) mx = fmax(mx, (double)logits[b * m + i]);
+        double z = 0.0;
+        for (int i = 0; i < m; ++i) { w[i] = exp((double)logits[b * m + i] - mx); z += w[i]; }
+        for (int i = 0; i < m; ++i) w[i] /= z;
+        for (int i = 0; i < m; ++i) {
+            const uint16_t* x = k + (b * m + i) * (int64_t)d_i;
+            for (int e = 0; e < d_i; ++e) c[e] += w[i] * orc_bf16_to_f64(x[e]);
+        }
+        const int64_t slot = (tok0 / m + b) % cap;
+        for (int blk = 0; blk < d_i / 32; ++blk) {
+            orc_mxfp4_block(c + 32 * blk, 32, codes, scale + slot * (d_i / 32) + blk);
+            for (int i = 0; i < 32; i += 2)
+                data[slot * (d_i / 2) + 16 * blk + i / 2] = (uint8_t)(codes[i] | (codes[i + 1] << 4));
+        }
+        free(w);
+        free(c);
+    }
+    return 0;
+}
+
 /* Dequantise one stored entry (slot) into d doubles. */
 static void entry_f64(const uint8_t* nope, const uint16_t* rope, const float* scale, int dn, int64_t slot,
                       double* out) {

@@ -461,3 +461,126 @@ def test_window_branch_is_last_W_tokens(orc, gen):
         o = p @ K
         o[:, 64:] = rot(o[:, 64:], -t)
         assert np.allclose(out[i], o, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# compression variants: per-channel weights, index-key compression to MXFP4
+# ---------------------------------------------------------------------------
+def test_compress_channel_equal_logits_is_scalar(orc, gen):
+    """Per-channel logits that repeat the token's logit on every channel give the
+    scalar-weight routine's bytes exactly."""
+    m, d = 4, 256
+    kv = gen.normal_bf16(31, 1, (32, d))
+    logits = gen.normal_f32(31, 2, (32,))
+    a = orc.compress(kv, logits, 8, m)
+    b = orc.compress_channel(kv, np.repeat(logits[:, None], d, axis=1), 8, m)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_compress_channel_selects_per_channel(orc, gen):
+    """Channel e with one logit 0 and the others -1000 (weights exactly 1 and 0)
+    takes that token's value: the entry equals the m=1 entry of the token built
+    channel by channel, at the block's RoPE position."""
+    m, d = 4, 128
+    nblk = 3
+    kv = gen.normal_bf16(32, 1, (nblk * m, d))
+    rng = np.random.default_rng(7)
+    pick = rng.integers(0, m, size=(nblk, d))
+    logits = np.full((nblk * m, d), -1000.0, np.float32)
+    sel = np.zeros((nblk, d), np.uint16)
+    for b in range(nblk):
+        for e in range(d):
+            logits[b * m + pick[b, e], e] = 0.0
+            sel[b, e] = kv[b * m + pick[b, e], e]
+    got = orc.compress_channel(kv, logits, 0, m)
+    for b in range(nblk):
+        p = (b + 1) * m - 1  # the block's entry is roped at its last token
+        want = orc.compress(sel[b:b + 1], np.zeros(1, np.float32), p, 1)
+        for x, y in zip(got, want):
+            assert np.array_equal(x[b:b + 1], y)
+
+
+def test_compress_channel_uniform_logits_is_mean(orc, gen):
+    m, d = 2, 128
+    kv = gen.normal_bf16(33, 1, (8, d))
+    x = orc.bf16_array_to_f64(kv)
+    rng = np.random.default_rng(3)
+    logits = np.repeat(rng.standard_normal((4, 1, d)).astype(np.float32), m, axis=1).reshape(8, d)
+    ent = orc.compress_channel(kv, logits, 0, m)
+    deq = _dq(orc, ent)
+    for b in range(4):
+        mean = x[b * m:(b + 1) * m].mean(axis=0)
+        s = float(ent[2][b])
+        assert np.all(np.abs(deq[b, :64] - mean[:64]) <= 0.5 * _e4m3_quantum(mean[:64] / s) * s + 1e-15)
+
+
+def _e2m1_brute(orc, v):
+    """Nearest E2M1 code by search over all 16 codes (ties: even mantissa bit; +0 for zero)."""
+    best, bd = 0, None
+    for c in range(16):
+        dc = abs(orc.e2m1_to_f64(c) - v)
+        if bd is None or dc < bd or (dc == bd and (c & 1) == 0 and (best & 1) == 1):
+            best, bd = c, dc
+    mag = best & 7
+    return (8 if (v < 0 and mag != 0) else 0) | mag
+
+
+def test_e2m1_encoder_brute_force(orc):
+    grid = [i / 8.0 for i in range(-64, 65)] + [0.24, 0.26, 0.749, 0.751, 4.99, 5.01, 5.5, 6.5, 7.0, 1e3, -1e3, -0.0]
+    for v in grid:
+        assert orc.f64_to_e2m1(v) == _e2m1_brute(orc, v), v
+
+
+def test_mxfp4_scale_rule_and_zero_block(orc):
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        c = rng.standard_normal(32) * 2.0 ** rng.integers(-20, 20)
+        codes, sb = orc.mxfp4_block(c)
+        amax = np.max(np.abs(c))
+        assert 4.0 <= amax / 2.0 ** (sb - 127) < 8.0
+        s = 2.0 ** (sb - 127)
+        for x, k in zip(c, codes):
+            assert k == _e2m1_brute(orc, x / s)
+    codes, sb = orc.mxfp4_block(np.zeros(32))
+    assert sb == 127 and not codes.any()
+
+
+def test_compress_index_keys_m1_and_representable(orc, gen):
+    """m=1: each token quantised alone (brute-force check); tokens made of E2M1 values
+    times a power of two, block maximum 4 or 6, come back exactly."""
+    d_i = 128
+    k = gen.normal_bf16(34, 1, (6, d_i))
+    data, scale = orc.compress_index_keys(k, np.zeros(6, np.float32), 0, 1)
+    x = orc.bf16_array_to_f64(k)
+    for t in range(6):
+        for blk in range(d_i // 32):
+            codes, sb = orc.mxfp4_block(x[t, 32 * blk:32 * blk + 32])
+            assert scale[t, blk] == sb
+            packed = data[t, 16 * blk:16 * blk + 16]
+            assert np.array_equal(packed & 15, codes[0::2]) and np.array_equal(packed >> 4, codes[1::2])
+    rng = np.random.default_rng(5)
+    vals = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    for e in (-3, 0, 7):
+        v = rng.choice(vals, size=(2, d_i)) * rng.choice([-1, 1], size=(2, d_i))
+        v[:, ::32] = 6.0  # every block's maximum is 6: scale exactly 2^e
+        tok = np.array([orc.f64_to_bf16(a) for a in (v * 2.0 ** e).ravel()], np.uint16).reshape(2, d_i)
+        data, scale = orc.compress_index_keys(tok, np.zeros(2, np.float32), 0, 1)
+        assert np.all(scale == 127 + e)
+        dec = np.array([[orc.e2m1_to_f64(int(b) & 15), orc.e2m1_to_f64(int(b) >> 4)] for b in data.ravel()]).reshape(2, d_i)
+        assert np.array_equal(dec * 2.0 ** e, v * 2.0 ** e)
+
+
+def test_compress_index_keys_uniform_logits_mean(orc):
+    """Two tokens, equal logits: the entry is their mean (chosen exactly representable)."""
+    d_i = 64
+    a = np.full(d_i, 4.0)
+    b = np.full(d_i, 2.0)
+    a[1::2], b[1::2] = -3.0, -1.0  # means 3 and -2
+    tok = np.array([orc.f64_to_bf16(x) for x in np.concatenate([a, b])], np.uint16).reshape(2, d_i)
+    data, scale = orc.compress_index_keys(tok, np.zeros(2, np.float32), 0, 2)
+    dec = np.array([[orc.e2m1_to_f64(int(x) & 15), orc.e2m1_to_f64(int(x) >> 4)] for x in data[0]]).reshape(-1)
+    # block maximum 3: scale 2^(floor(log2 3) - 2) = 1/2 (byte 126); 3 and -2 are 6 and -4 in E2M1
+    assert np.all(scale[0] == 126)
+    want = np.where(np.arange(d_i) % 2 == 0, 3.0, -2.0)
+    assert np.array_equal(dec * 0.5, want)

@@ -217,6 +217,73 @@ class HcaSet:
                           wl["W"], wl["sm_scale"], wl["rope_base"], out=self.out, lse=self.lse, ws=self.ws)
 
 
+class CompressSet:
+    """One chunk's compression: entries with per-token weights, with per-channel weights,
+    and MXFP4 index keys, each from 8,192 raw tokens (m=4)."""
+
+    CALLS = ("compress", "compress_channel", "compress_index_keys")
+
+    def __init__(self, wl):
+        import torch
+
+        import compressed_sparse_long_compress_amd as csa
+        from gen import device as dev
+
+        self.wl = wl
+        T, d, d_i, m = wl["T"], wl["d"], wl["d_i"], wl["m"]
+        self.kv, self.lg, self.lgc, self.ik = (dev.bf16(wl["kv"]), dev.t(wl["logits"]), dev.t(wl["logits_ch"]),
+                                               dev.bf16(wl["ik"]))
+        self.c1 = csa.KvCache.empty(1, T // m, d)
+        self.c2 = csa.KvCache.empty(1, T // m, d)
+        self.keys = csa.IndexKeys(torch.zeros(T // m, d_i // 2, dtype=torch.uint8, device="cuda"),
+                                  torch.zeros(T // m, d_i // 32, dtype=torch.uint8, device="cuda"), T // m)
+        self.replicas = 1
+
+    def call(self, name):
+        import compressed_sparse_long_compress_amd as csa
+
+        m = self.wl["m"]
+        if name == "compress":
+            csa.csa_compress(self.kv, self.lg, 0, m, 0, self.c1)
+        elif name == "compress_channel":
+            csa.csa_compress_channel(self.kv, self.lgc, 0, m, 0, self.c2)
+        else:
+            csa.csa_compress_index_keys(self.ik, self.lg, 0, m, 0, self.keys)
+
+    def step(self, i):
+        for name in self.CALLS:
+            self.call(name)
+
+    def bytes_per_call(self):
+        """Algorithmic HBM bytes of each call: inputs read once, outputs written once."""
+        T, d, d_i, m = (self.wl[x] for x in ("T", "d", "d_i", "m"))
+        n = T // m
+        entry = (d - 64) + 64 * 2 + 4
+        return {"compress": T * (2 * d + 4) + n * entry,
+                "compress_channel": T * (2 * d + 4 * d) + n * entry,
+                "compress_index_keys": T * (2 * d_i + 4) + n * (d_i // 2 + d_i // 32)}
+
+
+def time_calls(ds, n):
+    """Average duration of each call of a CompressSet: n back-to-back launches between one pair of events."""
+    import torch
+
+    res = {}
+    for name in ds.CALLS:
+        for _ in range(3):
+            ds.call(name)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            ds.call(name)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / n / 1e3
+    return res
+
+
 def time_steps(ds, steps, warmup):
     import torch
 
@@ -306,6 +373,8 @@ def run_workload(name, steps, warmup):
     wl = configs.named(name)
     if name.startswith("csa_decode"):
         ds = DecodeSet(wl, replicas=8)
+    elif name == "compress_chunk":
+        ds = CompressSet(wl)
     elif name == "hca_decode_1m":
         ds = HcaSet(wl, replicas=8)
     else:
@@ -336,7 +405,7 @@ def main():
     ap.add_argument("--all", action="store_true", help="also time the other workloads (secondary object)")
     ap.add_argument("--workload", default="csa_decode_1m",
                     choices=["csa_decode_1m", "csa_decode_1m_mtp2", "csa_decode_64k", "hca_decode_1m",
-                             "prefill_chunk"],
+                             "prefill_chunk", "compress_chunk"],
                     help="time only this workload and print its line (profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -360,6 +429,15 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": a.numel(), "copies": 5}))
+        return
+    if args.workload == "compress_chunk":
+        wl, ds, sec = run_workload(args.workload, args.steps, args.warmup)
+        calls = time_calls(ds, args.steps)
+        by = ds.bytes_per_call()
+        print(json.dumps({"workload": args.workload, "value": wl["T"] * args.steps / sec, "unit": "tokens/s",
+                          "ms_per_step": sec / args.steps * 1e3, "steps": args.steps,
+                          "per_call_us": {k: v * 1e6 for k, v in calls.items()},
+                          "hbm_gbs": {k: by[k] / calls[k] / 1e9 for k in calls}}))
         return
     if args.workload != "csa_decode_1m":
         wl, ds, sec = run_workload(args.workload, args.steps, args.warmup)

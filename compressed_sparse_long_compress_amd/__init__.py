@@ -36,6 +36,8 @@ class _IdxKeys(ctypes.Structure):
 
 _vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 _lib.csa_compress.argtypes = [_vp, _vp, _i64, _i64, _i32, _i32, _f32, _i32, _Kv, _vp]
+_lib.csa_compress_channel.argtypes = [_vp, _vp, _i64, _i64, _i32, _i32, _f32, _i32, _Kv, _vp]
+_lib.csa_compress_index_keys.argtypes = [_vp, _vp, _i64, _i64, _i32, _i32, _i32, _IdxKeys, _vp]
 _lib.csa_index_scores.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _IdxKeys, _i32, _i64, _vp, _vp, _sz, _vp]
 _lib.csa_index_scores_grouped.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _IdxKeys, _i32, _i64, _i32, _vp,
                                           _vp, _sz, _vp]
@@ -52,7 +54,7 @@ _lib.hca_dense_mqa.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _Kv,
 _lib.csa_last_error.restype = ctypes.c_char_p
 _lib.csa_version.restype = ctypes.c_int
 
-EXPORTS = ["csa_compress", "csa_index_scores", "csa_index_scores_grouped", "csa_topk_workspace", "csa_topk", "csa_mqa_workspace",
+EXPORTS = ["csa_compress", "csa_compress_channel", "csa_compress_index_keys", "csa_index_scores", "csa_index_scores_grouped", "csa_topk_workspace", "csa_topk", "csa_mqa_workspace",
            "csa_sparse_mqa", "hca_dense_mqa", "csa_last_error", "csa_version"]
 
 
@@ -147,6 +149,30 @@ def csa_compress(kv, logits, tok0, m, seq, out, rope_base=10000.0):
         raise ValueError("kv / logits / out shapes disagree")
     _check(_lib.csa_compress(_ptr(kv), _ptr(logits), int(tok0), int(n_tok), int(m), int(d), float(rope_base),
                              int(seq), out.c(), _stream()))
+    return out
+
+
+def csa_compress_channel(kv, logits, tok0, m, seq, out, rope_base=10000.0):
+    """csa_compress with per-channel weights: logits fp32 [n_tok, d]."""
+    _need(kv, "kv", torch.bfloat16, 2)
+    _need(logits, "logits", torch.float32, 2)
+    n_tok, d = kv.shape
+    if tuple(logits.shape) != (n_tok, d) or d != out.d:
+        raise ValueError("kv / logits / out shapes disagree")
+    _check(_lib.csa_compress_channel(_ptr(kv), _ptr(logits), int(tok0), int(n_tok), int(m), int(d), float(rope_base),
+                                     int(seq), out.c(), _stream()))
+    return out
+
+
+def csa_compress_index_keys(k, logits, tok0, m, seq, out):
+    """Raw index-key tokens (bf16 [n_tok, d_i], logits fp32 [n_tok]) -> MXFP4 rows of `out` (IndexKeys)."""
+    _need(k, "k", torch.bfloat16, 2)
+    _need(logits, "logits", torch.float32, 1)
+    n_tok, d_i = k.shape
+    if logits.shape[0] != n_tok or d_i != out.d_i:
+        raise ValueError("k / logits / out shapes disagree")
+    _check(_lib.csa_compress_index_keys(_ptr(k), _ptr(logits), int(tok0), int(n_tok), int(m), int(d_i), int(seq),
+                                        out.c(), _stream()))
     return out
 
 

@@ -99,6 +99,52 @@ int csa_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t 
     return hip_status(e, fn);
 }
 
+int csa_compress_channel(const uint16_t* kv, const float* logits, int64_t tok0, int64_t n_tok, int32_t m, int32_t d,
+                         float rope_base, int32_t seq, csa_kv_t out, csa_stream_t stream) {
+    const char* fn = "csa_compress_channel";
+    if (m < 1 || m > 1024) return fail(CSA_EUNSUPPORTED, "%s: m=%d outside 1..1024", fn, m);
+    if (d != 128 && d != 512) return fail(CSA_EUNSUPPORTED, "%s: d=%d unsupported (128 or 512)", fn, d);
+    if (tok0 < 0 || n_tok < 0) return fail(CSA_EINVAL, "%s: tok0 and n_tok must be >= 0", fn);
+    if (tok0 % m != 0 || n_tok % m != 0)
+        return fail(CSA_EINVAL, "%s: tok0 (%lld) and n_tok (%lld) must be multiples of m (%d): only complete blocks "
+                    "are compressed", fn, (long long)tok0, (long long)n_tok, m);
+    if (seq < 0) return fail(CSA_EINVAL, "%s: seq must be >= 0", fn);
+    if (!(rope_base > 0.f)) return fail(CSA_EINVAL, "%s: rope_base must be positive", fn);
+    if (n_tok == 0) return ok();
+    if (!kv || !logits) return fail(CSA_EINVAL, "%s: null kv or logits", fn);
+    if (!aligned16(kv) || !aligned16(logits)) return fail(CSA_EINVAL, "%s: kv and logits must be 16-byte aligned", fn);
+    if (int rc = check_kv(out, d, "out", fn)) return rc;
+    if (n_tok / m > out.cap)
+        return fail(CSA_EINVAL, "%s: %lld new entries exceed out.cap (%lld): slots would collide", fn,
+                    (long long)(n_tok / m), (long long)out.cap);
+    hipError_t e = csa::launch_compress_channel(kv, logits, tok0, n_tok, m, d, csa::rope_table((double)rope_base),
+                                                (int64_t)seq * out.cap, out.cap, out.nope, out.rope, out.scale,
+                                                (hipStream_t)stream);
+    return hip_status(e, fn);
+}
+
+int csa_compress_index_keys(const uint16_t* k, const float* logits, int64_t tok0, int64_t n_tok, int32_t m,
+                            int32_t d_i, int32_t seq, csa_index_keys_t out, csa_stream_t stream) {
+    const char* fn = "csa_compress_index_keys";
+    if (m < 1 || m > 1024) return fail(CSA_EUNSUPPORTED, "%s: m=%d outside 1..1024", fn, m);
+    if (d_i != 64 && d_i != 128) return fail(CSA_EUNSUPPORTED, "%s: d_i=%d unsupported (64 or 128)", fn, d_i);
+    if (tok0 < 0 || n_tok < 0) return fail(CSA_EINVAL, "%s: tok0 and n_tok must be >= 0", fn);
+    if (tok0 % m != 0 || n_tok % m != 0)
+        return fail(CSA_EINVAL, "%s: tok0 (%lld) and n_tok (%lld) must be multiples of m (%d): only complete blocks "
+                    "are compressed", fn, (long long)tok0, (long long)n_tok, m);
+    if (seq < 0) return fail(CSA_EINVAL, "%s: seq must be >= 0", fn);
+    if (n_tok == 0) return ok();
+    if (!k || !logits || !out.data || !out.scale) return fail(CSA_EINVAL, "%s: null array", fn);
+    if (((uintptr_t)k & 3u) != 0) return fail(CSA_EINVAL, "%s: k must be 4-byte aligned", fn);
+    if (out.cap < 1) return fail(CSA_EINVAL, "%s: out.cap must be >= 1", fn);
+    if (n_tok / m > out.cap)
+        return fail(CSA_EINVAL, "%s: %lld new entries exceed out.cap (%lld): slots would collide", fn,
+                    (long long)(n_tok / m), (long long)out.cap);
+    hipError_t e = csa::launch_compress_index_keys(k, logits, tok0, n_tok, m, d_i, (int64_t)seq * out.cap, out.cap,
+                                                   out.data, out.scale, (hipStream_t)stream);
+    return hip_status(e, fn);
+}
+
 // shared by the two indexer entry points: argument checks and the row-summary destination
 static int index_args(const char* fn, const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
                       const int64_t* pos, int64_t T, int32_t h_i, int32_t d_i, const csa_index_keys_t& keys, int32_t m,

@@ -137,6 +137,186 @@ __global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ k
     if (lane == 0) scale[row] = s;
 }
 
+// ---------------------------------------------------------------------------
+// Per-channel weights: channel e of block b merges its m tokens with weights
+// softmax over logits[bm+i][e].  Same layout, RoPE and storage as
+// k_compress; per dim three passes over the block's logits (max, the sum of
+// exponentials in token order, the weighted merge), all in fp64.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void k_compress_ch(const uint16_t* __restrict__ kv, const float* __restrict__ logits,
+                                                     int64_t tok0, int64_t n_blk, int m, RopeTab rt, int64_t row0,
+                                                     int64_t cap, uint8_t* __restrict__ nope,
+                                                     uint16_t* __restrict__ rope, float* __restrict__ scale) {
+    constexpr int DN = D - 64;
+    constexpr int PER = D / 64;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t b = (int64_t)blockIdx.x * 4 + wv;
+    if (b >= n_blk) return;
+    const int dim0 = lane * PER;
+    const float* lg = logits + b * m * (int64_t)D + dim0;
+    const uint16_t* x = kv + b * m * (int64_t)D + dim0;
+
+    double mx[PER], z[PER], c[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        mx[e] = -INFINITY;
+        z[e] = 0.0;
+        c[e] = 0.0;
+    }
+    for (int i = 0; i < m; ++i)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) mx[e] = fmax(mx[e], (double)lg[(int64_t)i * D + e]);
+    for (int i = 0; i < m; ++i)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) z[e] = __dadd_rn(z[e], exp((double)lg[(int64_t)i * D + e] - mx[e]));
+    for (int i = 0; i < m; ++i) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const double wi = exp((double)lg[(int64_t)i * D + e] - mx[e]) / z[e];
+            c[e] = __dadd_rn(c[e], __dmul_rn(wi, (double)bf16_bits_to_f32(x[(int64_t)i * D + e])));
+        }
+    }
+
+    const int64_t J = tok0 / m + b;
+    const bool is_rope = dim0 >= DN;
+    if (is_rope) {
+        const double p = (double)((J + 1) * (int64_t)m - 1);
+#pragma unroll
+        for (int e = 0; e < PER; e += 2) {
+            const double theta = rt.theta[(dim0 - DN + e) >> 1];
+            const double a = __dmul_rn(p, theta);
+            const double cs = cos(a), sn = sin(a);
+            const double x0 = c[e], x1 = c[e + 1];
+            c[e] = __dsub_rn(__dmul_rn(x0, cs), __dmul_rn(x1, sn));
+            c[e + 1] = __dadd_rn(__dmul_rn(x0, sn), __dmul_rn(x1, cs));
+        }
+    }
+    double am = 0.0;
+    if (!is_rope) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) am = fmax(am, fabs(c[e]));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) am = fmax(am, __shfl_xor(am, o));
+    const float s = am > 0.0 ? (float)(am / 448.0) : 1.0f;
+    const int64_t row = row0 + (J % cap);
+    if (is_rope) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) rope[row * 64 + (dim0 - DN) + e] = f32_to_bf16_bits(f64_to_f32_odd(c[e]));
+    } else {
+#pragma unroll
+        for (int e = 0; e < PER; e += 2) {
+            const float a0 = fminf(fmaxf(f64_to_f32_odd(c[e] / (double)s), -448.f), 448.f);
+            const float a1 = fminf(fmaxf(f64_to_f32_odd(c[e + 1] / (double)s), -448.f), 448.f);
+            *(uint16_t*)(nope + row * DN + dim0 + e) = (uint16_t)__builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+        }
+    }
+    if (lane == 0) scale[row] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Index keys: the softmax-weighted merge of every m raw key tokens (fp64, no
+// RoPE), then MXFP4: per 32 elements the E8M0 scale 2^(floor(log2 amax) - 2)
+// and E2M1 codes of value / scale, nearest with ties to the even mantissa,
+// saturating at 6, zero stored as +0.  One wave per entry, lane l holds
+// elements 2l, 2l+1 (its packed byte); a block is 16 lanes.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e2m1_code(double v) {
+    // magnitude code = midpoints of the E2M1 grid (0 .5 1 1.5 2 3 4 6) passed by |v|;
+    // at a midpoint itself, toward the even code
+    const double a = fabs(v);
+    uint32_t c = 0;
+    c += a > 0.25;
+    c += a >= 0.75;
+    c += a > 1.25;
+    c += a >= 1.75;
+    c += a > 2.5;
+    c += a >= 3.5;
+    c += a > 5.0;
+    return (v < 0.0 && c != 0 ? 8u : 0u) | c;
+}
+
+template <int DI>
+__global__ __launch_bounds__(256) void k_compress_ikey(const uint16_t* __restrict__ k, const float* __restrict__ logits,
+                                                       int64_t tok0, int64_t n_blk, int m, int64_t row0, int64_t cap,
+                                                       uint8_t* __restrict__ data, uint8_t* __restrict__ kscale) {
+    static_assert(DI == 64 || DI == 128, "two elements per lane");
+    __shared__ double wbuf[4][kMaxM];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t b = (int64_t)blockIdx.x * 4 + wv;
+    if (b >= n_blk) return;
+    const float* lg = logits + b * m;
+    double* wb = wbuf[wv];
+    double mx = -INFINITY;
+    for (int i = 0; i < m; ++i) mx = fmax(mx, (double)lg[i]);
+    for (int i = lane; i < m; i += 64) wb[i] = exp((double)lg[i] - mx);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    double z = 0.0;
+    for (int i = 0; i < m; ++i) z = __dadd_rn(z, wb[i]);
+
+    const bool live = 2 * lane < DI;
+    double c0 = 0.0, c1 = 0.0;
+    if (live) {
+        const uint16_t* x = k + b * m * (int64_t)DI + 2 * lane;
+        for (int i = 0; i < m; ++i) {
+            const uint32_t raw = *(const uint32_t*)(x + (int64_t)i * DI);
+            const double wi = wb[i] / z;
+            c0 = __dadd_rn(c0, __dmul_rn(wi, (double)bf16_bits_to_f32((uint16_t)raw)));
+            c1 = __dadd_rn(c1, __dmul_rn(wi, (double)bf16_bits_to_f32((uint16_t)(raw >> 16))));
+        }
+    }
+    // block amax over its 16 lanes
+    double am = fmax(fabs(c0), fabs(c1));
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) am = fmax(am, __shfl_xor(am, o));
+    int sb = 127;
+    if (am > 0.0) {
+        int ex;
+        frexp(am, &ex);  // am in [2^(ex-1), 2^ex)
+        sb = ex - 1 - 2 + 127;
+        sb = sb < 0 ? 0 : (sb > 254 ? 254 : sb);
+    }
+    const double inv = ldexp(1.0, 127 - sb);  // exact power of two
+    const int64_t row = row0 + ((tok0 / m + b) % cap);
+    if (live) {
+        const uint32_t lo = am > 0.0 ? e2m1_code(c0 * inv) : 0u, hi = am > 0.0 ? e2m1_code(c1 * inv) : 0u;
+        data[row * (DI / 2) + lane] = (uint8_t)(lo | (hi << 4));
+        if ((lane & 15) == 0) kscale[row * (DI / 32) + (lane >> 4)] = (uint8_t)sb;
+    }
+}
+
+hipError_t launch_compress_channel(const uint16_t* kv, const float* logits, int64_t tok0, int64_t n_tok, int m, int d,
+                                   const RopeTab& rt, int64_t row0, int64_t cap, uint8_t* nope, uint16_t* rope,
+                                   float* scale, hipStream_t st) {
+    const int64_t n_blk = n_tok / m;
+    if (n_blk == 0) return hipSuccess;
+    dim3 grid((unsigned)((n_blk + 3) / 4)), block(256);
+    if (d == 512)
+        hipLaunchKernelGGL(k_compress_ch<512>, grid, block, 0, st, kv, logits, tok0, n_blk, m, rt, row0, cap, nope,
+                           rope, scale);
+    else
+        hipLaunchKernelGGL(k_compress_ch<128>, grid, block, 0, st, kv, logits, tok0, n_blk, m, rt, row0, cap, nope,
+                           rope, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_compress_index_keys(const uint16_t* k, const float* logits, int64_t tok0, int64_t n_tok, int m,
+                                      int d_i, int64_t row0, int64_t cap, uint8_t* data, uint8_t* kscale,
+                                      hipStream_t st) {
+    const int64_t n_blk = n_tok / m;
+    if (n_blk == 0) return hipSuccess;
+    dim3 grid((unsigned)((n_blk + 3) / 4)), block(256);
+    if (d_i == 128)
+        hipLaunchKernelGGL(k_compress_ikey<128>, grid, block, 0, st, k, logits, tok0, n_blk, m, row0, cap, data,
+                           kscale);
+    else
+        hipLaunchKernelGGL(k_compress_ikey<64>, grid, block, 0, st, k, logits, tok0, n_blk, m, row0, cap, data,
+                           kscale);
+    return hipGetLastError();
+}
+
 hipError_t launch_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t n_tok, int m, int d,
                            const RopeTab& rt, int64_t row0, int64_t cap, uint8_t* nope, uint16_t* rope, float* scale,
                            hipStream_t st) {

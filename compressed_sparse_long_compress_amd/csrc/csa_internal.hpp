@@ -22,6 +22,14 @@ __host__ __device__ inline int64_t topk_groups(int64_t n_cols) { return (n_cols 
 hipError_t launch_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t n_tok, int m, int d,
                            const RopeTab& rt, int64_t row0, int64_t cap, uint8_t* nope, uint16_t* rope, float* scale,
                            hipStream_t st);
+// logits [n_tok][d]: per-channel weights
+hipError_t launch_compress_channel(const uint16_t* kv, const float* logits, int64_t tok0, int64_t n_tok, int m, int d,
+                                   const RopeTab& rt, int64_t row0, int64_t cap, uint8_t* nope, uint16_t* rope,
+                                   float* scale, hipStream_t st);
+// raw bf16 index keys -> MXFP4 rows
+hipError_t launch_compress_index_keys(const uint16_t* k, const float* logits, int64_t tok0, int64_t n_tok, int m,
+                                      int d_i, int64_t row0, int64_t cap, uint8_t* data, uint8_t* kscale,
+                                      hipStream_t st);
 
 // gmax != nullptr: also write each row's summary (the largest order key of
 // the visible columns of every kTopkGroup-column group) to gmax[T][groups]

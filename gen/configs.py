@@ -15,6 +15,7 @@ Named workloads (seeds 101..105):
   csa_decode_1m  B=4,  L=1,048,576 (262,144 entries), 5% planted index keys
   csa_decode_1m_mtp2  the same cache, two query rows per sequence (positions L-2, L-1)
   prefill_chunk  8,192 new tokens after a 131,072-token context (CSA + HCA)
+  compress_chunk 8,192 raw tokens (d=512) and index-key tokens (d_i=128), seed 106
 """
 import math
 
@@ -96,6 +97,17 @@ def prefill(T, L0=0, m=4, m_hca=128, H=64, d=512, h_i=8, d_i=128, k=1024, W=128,
     return wl
 
 
+def compress_chunk(T=8192, d=512, d_i=128, m=4, seed=106):
+    """Raw inputs of one chunk's compression: bf16 tokens, one logit per token and one
+    per (token, channel), and raw bf16 index-key tokens."""
+    wl = dict(kind="compress", T=T, d=d, d_i=d_i, m=m, seed=seed, rope_base=ROPE_BASE)
+    wl["kv"] = normal_bf16(seed, 1, (T, d))
+    wl["logits"] = normal_f32(seed, 2, (T,))
+    wl["logits_ch"] = normal_f32(seed, 3, (T, d))
+    wl["ik"] = normal_bf16(seed, 4, (T, d_i))
+    return wl
+
+
 def named(name, **over):
     """The five named workloads at full size (keyword overrides allowed)."""
     if name == "prefill_small":
@@ -114,6 +126,8 @@ def named(name, **over):
         kw = dict(B=4, L=1 << 20, plant_frac=0.05, seed=104)
         kw.update(over)
         return csa_decode(**kw)
+    if name == "compress_chunk":
+        return compress_chunk(**over)
     if name == "csa_decode_1m_mtp2":
         kw = dict(B=4, L=1 << 20, plant_frac=0.05, seed=104, tokens=2)
         kw.update(over)

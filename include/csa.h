@@ -126,6 +126,34 @@ int csa_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t 
                  float rope_base, int32_t seq, csa_kv_t out, csa_stream_t stream);
 
 /*
+ * csa_compress_channel — csa_compress with one logit per token and channel
+ * (the pages call the merge a weighted compression without fixing the
+ * weights' shape: [xmsumi] § CSA).  Channel e of block b merges its m tokens
+ * with weights softmax_i(logits[bm+i][e]); RoPE, storage and slot rules as
+ * csa_compress.  With logits equal across channels it equals csa_compress.
+ *   logits [n_tok][d] fp32 (16-byte aligned)
+ */
+int csa_compress_channel(const uint16_t* kv, const float* logits, int64_t tok0, int64_t n_tok, int32_t m, int32_t d,
+                         float rope_base, int32_t seq, csa_kv_t out, csa_stream_t stream);
+
+/*
+ * csa_compress_index_keys — the indexer's key for each compressed entry from
+ * raw key tokens: the same weighted merge of every m tokens as csa_compress
+ * ([xmsumi] § CSA; how the indexer's keys are formed is not on the pages,
+ * this is the reading taken), no RoPE (the indexer has none), then MXFP4
+ * ([xmsumi] § 关键技术细节: the indexer runs in FP4): per 32 elements the E8M0
+ * scale 2^(floor(log2 amax) - 2) (byte 127 for an all-zero block, clamped to
+ * 0..254) and E2M1 codes of value / scale, nearest with ties to the even
+ * mantissa bit, saturating at 6, zero stored as +0.  Merge in fp64.
+ *   k      [n_tok][d_i] bf16 raw key tokens tok0 .. tok0+n_tok-1 of sequence seq
+ *   logits [n_tok] fp32 (one per token, as csa_compress)
+ *   out    entry J = tok0/m + b at row seq*out.cap + J % out.cap
+ * d_i in {64, 128}; 1 <= m <= 1024; tok0 and n_tok multiples of m.
+ */
+int csa_compress_index_keys(const uint16_t* k, const float* logits, int64_t tok0, int64_t n_tok, int32_t m,
+                            int32_t d_i, int32_t seq, csa_index_keys_t out, csa_stream_t stream);
+
+/*
  * csa_index_scores — lightning-indexer scores ([xmsumi] § CSA: a lightweight
  * indexer ranks compressed entries per query token; § 关键技术细节: FP4
  * arithmetic inside the indexer; [zcldvi]: FP4 relevance of each query token

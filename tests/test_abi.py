@@ -55,6 +55,26 @@ def test_compress_validation(csa):
     assert rc == csa.CSA_EINVAL and b"null array" in L.csa_last_error()
 
 
+def test_compress_variants_validation(csa):
+    L = csa._lib
+    p = ctypes.c_void_p(256)
+    rc = L.csa_compress_channel(None, None, 0, 8, 0, 512, 10000.0, 0, _kv(csa), None)
+    assert rc == csa.CSA_EUNSUPPORTED and b"m=0" in L.csa_last_error()
+    rc = L.csa_compress_channel(p, p, 2, 8, 4, 512, 10000.0, 0, _kv(csa), None)
+    assert rc == csa.CSA_EINVAL and b"complete blocks" in L.csa_last_error()
+    rc = L.csa_compress_channel(None, None, 0, 0, 4, 512, 10000.0, 0, _kv(csa), None)
+    assert rc == csa.CSA_OK  # empty call is a no-op
+    keys = csa._IdxKeys(256, 256, 16)
+    rc = L.csa_compress_index_keys(p, p, 0, 8, 4, 96, 0, keys, None)
+    assert rc == csa.CSA_EUNSUPPORTED and b"d_i=96" in L.csa_last_error()
+    rc = L.csa_compress_index_keys(p, p, 0, 6, 4, 128, 0, keys, None)
+    assert rc == csa.CSA_EINVAL and b"complete blocks" in L.csa_last_error()
+    rc = L.csa_compress_index_keys(p, p, 0, 128, 4, 128, 0, keys, None)
+    assert rc == csa.CSA_EINVAL and b"out.cap" in L.csa_last_error()
+    rc = L.csa_compress_index_keys(None, None, 0, 8, 4, 128, 0, csa._IdxKeys(None, None, 16), None)
+    assert rc == csa.CSA_EINVAL and b"null" in L.csa_last_error()
+
+
 def test_index_topk_validation(csa):
     L = csa._lib
     keys = csa._IdxKeys(None, None, 16)

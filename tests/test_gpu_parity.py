@@ -113,6 +113,61 @@ def test_compress(lib, dev, gen, orc, d, m, tok0, n_tok, cap):
     assert not got[0][:cap].any() and not got[2][:cap].any()
 
 
+@pytest.mark.parametrize("d,m,tok0,n_tok,cap", [
+    (512, 4, 8, 64, 40),
+    (128, 128, 0, 256, 4),      # HCA ratio
+    (512, 1, 3, 17, 32),        # window ring, wrap-around
+])
+def test_compress_channel(lib, dev, gen, orc, d, m, tok0, n_tok, cap):
+    """Per-channel compression weights against the oracle (same bar as csa_compress)."""
+    import torch
+
+    _say(f"compress_channel d={d} m={m} tok0={tok0} n_tok={n_tok} cap={cap}")
+    kv = gen.normal_bf16(211, 1, (n_tok, d))
+    logits = gen.normal_f32(211, 2, (n_tok, d))
+    cache = lib.KvCache.empty(2, cap, d)
+    lib.csa_compress_channel(dev.bf16(kv), dev.t(logits), tok0, m, 1, cache)
+    torch.cuda.synchronize()
+    got = dev.host_entries(cache)
+    ref = orc.compress_channel(kv, logits, tok0, m)
+    n = n_tok // m
+    slots = cap + (tok0 // m + np.arange(n)) % cap
+    compare_entries(orc, tuple(a[slots] for a in got), ref, f"compress_channel d={d} m={m}")
+    assert not got[0][:cap].any() and not got[2][:cap].any()
+
+
+@pytest.mark.parametrize("d_i,m,tok0,n_tok,cap", [
+    (128, 4, 0, 4096, 1024),
+    (64, 4, 12, 400, 200),
+    (128, 1, 5, 77, 100),
+    (128, 128, 0, 1024, 8),
+])
+def test_compress_index_keys(lib, dev, gen, orc, d_i, m, tok0, n_tok, cap):
+    """Raw key tokens -> MXFP4 index keys: codes and scales equal the oracle's bit for bit
+    (an all-zero block and a wide-magnitude block included)."""
+    import torch
+
+    _say(f"compress_index_keys d_i={d_i} m={m} tok0={tok0} n_tok={n_tok} cap={cap}")
+    k = gen.normal_bf16(221, 1, (n_tok, d_i))
+    k[:m] = 0  # first entry: all-zero blocks (scale byte 127)
+    if n_tok >= 2 * m:
+        big = np.array([orc.f64_to_bf16(v) for v in np.geomspace(1e-6, 1e6, d_i)], np.uint16)
+        k[m:2 * m] = big  # second entry: saturation and underflow to zero inside a block
+    logits = gen.normal_f32(221, 2, (n_tok,))
+    out = lib.IndexKeys(torch.zeros(2 * cap, d_i // 2, dtype=torch.uint8, device="cuda"),
+                        torch.zeros(2 * cap, d_i // 32, dtype=torch.uint8, device="cuda"), cap)
+    lib.csa_compress_index_keys(dev.bf16(k), dev.t(logits), tok0, m, 1, out)
+    torch.cuda.synchronize()
+    data, scale = out.data.cpu().numpy(), out.scale.cpu().numpy()
+    ref_d, ref_s = orc.compress_index_keys(k, logits, tok0, m)
+    n = n_tok // m
+    slots = cap + (tok0 // m + np.arange(n)) % cap
+    assert np.array_equal(scale[slots], ref_s), "E8M0 scales differ"
+    bad = data[slots] != ref_d
+    assert not bad.any(), f"{bad.sum()} packed code bytes differ; first at {np.argwhere(bad)[:3].tolist()}"
+    assert not data[:cap].any() and not scale[:cap].any()  # sequence 0 untouched
+
+
 def test_compress_rejects_partial_block(lib, dev, gen):
     cache = lib.KvCache.empty(1, 16, 128)
     kv = gen.normal_bf16(202, 1, (6, 128))

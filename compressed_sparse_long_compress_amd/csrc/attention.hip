@@ -1443,80 +1443,72 @@ __global__ __launch_bounds__(128) void k_mqa_combine(const float* __restrict__ p
 }
 
 // Merge of the 64-head kernels' split partials: fp16, each normalised by its own sum l_s,
-// weighted by exp(m_s - M) l_s / L in the fixed order s = 0 .. S-1.
+// weighted by e^(m_s - M) l_s / L, L summed in the fixed order s = 0 .. S-1.  The partial
+// loads are issued first (up to kC16Reg splits held in registers), beside the splits'
+// statistics, so the merge waits for one round of global loads.
+constexpr int kC16Reg = 24;
 template <int D>
 __global__ __launch_bounds__(128) void k_mqa_combine16(const _Float16* __restrict__ part_o,
                                                        const float* __restrict__ part_ml, const int64_t* __restrict__ pos,
                                                        int H, int S, RopeTab rt, float* __restrict__ out,
                                                        float* __restrict__ lse) {
+    static_assert(D <= 4 * 128, "one pass of 128 threads x 4 dims");
     constexpr int DN = D - 64;
     constexpr int SMAX = 64;
-    __shared__ float wgt[SMAX];
-    __shared__ float red[2];
+    __shared__ float ms[SMAX], ll[SMAX];
     const int64_t th = blockIdx.x;  // t*H + h
     const int64_t t = th / H;
     const int h = (int)(th % H);
     const int tid = threadIdx.x;
-    if (tid < 64) {
-        float ms = -INFINITY, ls = 0.f;
-        if (tid < S) {
-            ms = part_ml[((t * S + tid) * H + h) * 2];
-            ls = part_ml[((t * S + tid) * H + h) * 2 + 1];
-        }
-        const float M = wave_max(ms);
-        const float e = ms == -INFINITY ? 0.f : __expf(ms - M);
-        const float L = ls * e;
-        // fixed-order sum over splits
-        float Lseq = 0.f;
-        for (int i = 0; i < S; ++i) Lseq += __shfl(L, i);
-        if (tid < S) wgt[tid] = Lseq > 0.f ? L / Lseq : 0.f;
-        if (tid == 0) {
-            red[0] = M;
-            red[1] = Lseq;
-        }
+    const int d0 = tid * 4;
+    const bool live = d0 < D;  // D = 128: 32 threads carry dims
+    const _Float16* base = part_o + (t * S * H + h) * (int64_t)D + (live ? d0 : 0);
+    uint2 v[kC16Reg];
+#pragma unroll
+    for (int s = 0; s < kC16Reg; ++s)
+        if (s < S && live) v[s] = *(const uint2*)(base + (int64_t)s * H * D);
+    if (tid < S) {
+        ms[tid] = part_ml[((t * S + tid) * H + h) * 2];
+        ll[tid] = part_ml[((t * S + tid) * H + h) * 2 + 1];
     }
     __syncthreads();
-    for (int d0 = tid * 4; d0 < D; d0 += 128 * 4) {
-        float o[4] = {0.f, 0.f, 0.f, 0.f};
-        const _Float16* base = part_o + (t * S * H + h) * (int64_t)D + d0;
-        int s = 0;
-        for (; s + 8 <= S; s += 8) {
-            uint2 v[8];
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, ms[s]);
+    float Ls = 0.f;
+    if (tid < S) Ls = ms[tid] == -INFINITY ? 0.f : ll[tid] * __expf(ms[tid] - M);
+    __syncthreads();  // every thread has read ms and ll
+    if (tid < S) ll[tid] = Ls;
+    __syncthreads();
+    float L = 0.f;
+    for (int s = 0; s < S; ++s) L += ll[s];  // fixed order
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+    auto acc = [&](const uint2 x, float wv) {
+        const v2h a = __builtin_bit_cast(v2h, x.x), b = __builtin_bit_cast(v2h, x.y);
+        o[0] = fmaf(wv, (float)a[0], o[0]);
+        o[1] = fmaf(wv, (float)a[1], o[1]);
+        o[2] = fmaf(wv, (float)b[0], o[2]);
+        o[3] = fmaf(wv, (float)b[1], o[3]);
+    };
+    if (live) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = *(const uint2*)(base + (int64_t)(s + u) * H * D);
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float wv = wgt[s + u];
-                const v2h a = __builtin_bit_cast(v2h, v[u].x), b = __builtin_bit_cast(v2h, v[u].y);
-                o[0] = fmaf(wv, (float)a[0], o[0]);
-                o[1] = fmaf(wv, (float)a[1], o[1]);
-                o[2] = fmaf(wv, (float)b[0], o[2]);
-                o[3] = fmaf(wv, (float)b[1], o[3]);
-            }
-        }
-        for (; s < S; ++s) {
-            const uint2 v = *(const uint2*)(base + (int64_t)s * H * D);
-            const float wv = wgt[s];
-            const v2h a = __builtin_bit_cast(v2h, v.x), b = __builtin_bit_cast(v2h, v.y);
-            o[0] = fmaf(wv, (float)a[0], o[0]);
-            o[1] = fmaf(wv, (float)a[1], o[1]);
-            o[2] = fmaf(wv, (float)b[0], o[2]);
-            o[3] = fmaf(wv, (float)b[1], o[3]);
-        }
-        if (d0 >= DN) {
-            const double tp = (double)pos[t];
-            for (int i = 0; i < 4; i += 2) {
-                float cs, sn;
-                angle_cs(tp, rt.theta[(d0 - DN + i) >> 1], cs, sn);
-                sn = -sn;  // rotation by -t
-                const float x0 = o[i], x1 = o[i + 1];
-                o[i] = x0 * cs - x1 * sn;
-                o[i + 1] = x0 * sn + x1 * cs;
-            }
-        }
-        *(float4*)(out + th * D + d0) = make_float4(o[0], o[1], o[2], o[3]);
+        for (int s = 0; s < kC16Reg; ++s)
+            if (s < S) acc(v[s], ll[s] * inv);
+        for (int s = kC16Reg; s < S; ++s) acc(*(const uint2*)(base + (int64_t)s * H * D), ll[s] * inv);
     }
-    if (tid == 0) lse[th] = red[1] > 0.f ? red[0] + __logf(red[1]) : -INFINITY;
+    if (live && d0 >= DN) {
+        const double tp = (double)pos[t];
+        for (int i = 0; i < 4; i += 2) {
+            float cs, sn;
+            angle_cs(tp, rt.theta[(d0 - DN + i) >> 1], cs, sn);
+            sn = -sn;  // rotation by -t
+            const float x0 = o[i], x1 = o[i + 1];
+            o[i] = x0 * cs - x1 * sn;
+            o[i + 1] = x0 * sn + x1 * cs;
+        }
+    }
+    if (live) *(float4*)(out + th * D + d0) = make_float4(o[0], o[1], o[2], o[3]);
+    if (tid == 0) lse[th] = L > 0.f ? M + __logf(L) : -INFINITY;
 }
 
 static int choose_splits(int64_t T, int64_t max_keys) {

@@ -1511,8 +1511,11 @@ __global__ __launch_bounds__(128) void k_mqa_combine16(const _Float16* __restric
     if (tid == 0) lse[th] = L > 0.f ? M + __logf(L) : -INFINITY;
 }
 
+// Splits per row: about one workgroup per CU in all (the 64-head kernels hold most of a
+// CU's LDS, so a second round of workgroups would run after the first), at least 64 keys
+// per split, at most 64 splits.
 static int choose_splits(int64_t T, int64_t max_keys) {
-    int64_t s = (512 + T - 1) / T;
+    int64_t s = (256 + T - 1) / T;
     int64_t by_keys = (max_keys + 63) / 64;
     if (s > by_keys) s = by_keys;
     if (s > 64) s = 64;
@@ -1531,7 +1534,7 @@ static void launch_mqa_t(const uint16_t* q, const int32_t* seq, const int64_t* p
                          int k, int m, KvView comp, KvView win, int window, float sm_scale, const RopeTab& rt, int S,
                          int64_t max_keys, float* out, float* lse, float* po, float* pml, hipStream_t st) {
     // splits of more than a few tiles: the two-role kernel (its pipeline costs a step at either end)
-    const bool long_splits = (max_keys + S - 1) / S > 4 * KT;
+    const bool long_splits = (max_keys + S - 1) / S > 12 * KT;
     if (H == 64 && D == 512 && long_splits)
         hipLaunchKernelGGL((k_mqa64ws<512>), dim3((unsigned)(T * S)), dim3(512), 0, st, q, seq, pos, idx, k, m, comp,
                            win, window, sm_scale, rt, S, out, lse, po, pml);

@@ -34,7 +34,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (scaled by a 256 MiB copy: fetch x2.0,
 # write x1.0; see profiles/csa_decode_1m_hbm_counters.md), valid for the kernel
 # source with this SHA-256 only.
-INDEX_TRAFFIC = {"sha256": "a5a3c886293fa9cf848b04ff3c60013ad7b442b98bea38786542ca1080eb42f4", "bytes": 75730032}
+INDEX_TRAFFIC = {"sha256": "980df2241730cd3587bdaeb5eb0fed177402d1296f473bae0aa8db8bb13c9afe", "bytes": 75732059}
 
 
 def log(msg):

@@ -838,10 +838,6 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
     // [stage(j+1), load j+2, PV(j)]  sync.  Tile t lives in kv[t % 3].  Returns whether a tile
     // broke the references (the pass's output is then discarded).  The loop has a single exit,
     // so the output accumulators keep their registers and every PV MFMA runs in place.
-    // One pass over the split.  Per tile, two barriers: [QK(j), softmax(j) -> P]  sync
-    // [stage(j+1), load j+2, PV(j)]  sync.  Tile t lives in kv[t % 3].  Returns whether a tile
-    // broke the references (the pass's output is then discarded).  The loop has a single exit,
-    // so the output accumulators keep their registers and every PV MFMA runs in place.
     auto run_pass = [&](bool first) -> bool {
         if (first) {
             // batch 0's addresses are published; convert the query while tile 0 is in flight

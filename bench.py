@@ -354,16 +354,20 @@ def cpu_baseline(wl):
     import oracle
 
     T = wl["T"]
+    reps = 0
     t0 = time.perf_counter()
-    sc = oracle.index_scores(wl["iq"][0], wl["iq"][1], wl["w"], wl["seq"], wl["pos"], wl["keys"][0], wl["keys"][1],
-                             wl["N"], wl["m"], wl["n_cols"]).astype(np.float32)
-    idx = oracle.topk(sc, wl["pos"], wl["m"], wl["k"])
-    oracle.attend(wl["q"], wl["seq"], wl["pos"], wl["comp"], wl["N"], wl["win"], wl["W"], wl["W"], wl["m"],
-                  wl["sm_scale"], wl["rope_base"], idx=idx)
+    # the whole batch, repeated until about 10 s of work (at most 30 passes)
+    while reps < 30 and (reps == 0 or time.perf_counter() - t0 < 10.0):
+        sc = oracle.index_scores(wl["iq"][0], wl["iq"][1], wl["w"], wl["seq"], wl["pos"], wl["keys"][0],
+                                 wl["keys"][1], wl["N"], wl["m"], wl["n_cols"]).astype(np.float32)
+        idx = oracle.topk(sc, wl["pos"], wl["m"], wl["k"])
+        oracle.attend(wl["q"], wl["seq"], wl["pos"], wl["comp"], wl["N"], wl["win"], wl["W"], wl["W"], wl["m"],
+                      wl["sm_scale"], wl["rope_base"], idx=idx)
+        reps += 1
     dt = time.perf_counter() - t0
     cores = min(T, os.cpu_count() or 1)  # the oracle parallelises over query rows
-    return {"value": T / dt, "unit": "queries/s", "cores": cores, "kind": "oracle",
-            "sample": f"all {T} query rows of the batch (full 1M-context rows), {dt:.1f} s wall"}
+    return {"value": T * reps / dt, "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "sample": f"all {T} query rows of the batch (full 1M-context rows), {reps} passes, {dt:.1f} s wall"}
 
 
 def run_workload(name, steps, warmup):

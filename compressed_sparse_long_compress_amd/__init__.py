@@ -27,7 +27,7 @@ CSA_OK, CSA_EINVAL, CSA_EUNSUPPORTED, CSA_EHIP, CSA_EWORKSPACE = 0, -1, -2, -3, 
 
 class _Kv(ctypes.Structure):
     _fields_ = [("nope", ctypes.c_void_p), ("rope", ctypes.c_void_p), ("scale", ctypes.c_void_p),
-                ("cap", ctypes.c_int64)]
+                ("cap", ctypes.c_int64), ("pages", ctypes.c_void_p), ("page", ctypes.c_int32)]
 
 
 class _IdxKeys(ctypes.Structure):
@@ -95,17 +95,29 @@ def version():
 
 
 class KvCache:
-    """Mixed-precision entries: nope uint8 [rows, d-64], rope bf16 [rows, 64], scale fp32 [rows]; rows = n_seq*cap."""
+    """Mixed-precision entries: nope uint8 [rows, d-64], rope bf16 [rows, 64], scale fp32 [rows].
 
-    def __init__(self, nope, rope, scale, cap):
+    Contiguous: rows = n_seq*cap, slot i of sequence s at row s*cap + i.  Paged
+    (pages int32 [n_seq, cap // page], page a power of two): slot i of sequence s
+    at row pages[s, i // page] * page + i % page; sequences may share pages."""
+
+    def __init__(self, nope, rope, scale, cap, pages=None, page=0):
         _need(nope, "nope", torch.uint8, 2)
         _need(rope, "rope", torch.bfloat16, 2)
         _need(scale, "scale", torch.float32, 1)
         if rope.shape[1] != 64 or nope.shape[0] != rope.shape[0] or scale.shape[0] != rope.shape[0]:
             raise ValueError("inconsistent KvCache arrays")
-        if cap <= 0 or rope.shape[0] % cap != 0:
-            raise ValueError("rows must be a multiple of cap")
+        if pages is None:
+            if cap <= 0 or rope.shape[0] % cap != 0:
+                raise ValueError("rows must be a multiple of cap")
+        else:
+            _need(pages, "pages", torch.int32, 2)
+            if page <= 0 or page & (page - 1) or cap % page or pages.shape[1] != cap // page:
+                raise ValueError("page must be a power of two dividing cap; pages [n_seq, cap // page]")
+            if rope.shape[0] % page:
+                raise ValueError("rows must be whole pages")
         self.nope, self.rope, self.scale, self.cap = nope, rope, scale, int(cap)
+        self.pages, self.page = pages, int(page) if pages is not None else 0
 
     @property
     def d(self):
@@ -119,7 +131,8 @@ class KvCache:
                    torch.zeros(rows, dtype=torch.float32, device=device), cap)
 
     def c(self):
-        return _Kv(self.nope.data_ptr(), self.rope.data_ptr(), self.scale.data_ptr(), self.cap)
+        return _Kv(self.nope.data_ptr(), self.rope.data_ptr(), self.scale.data_ptr(), self.cap,
+                   self.pages.data_ptr() if self.pages is not None else None, self.page)
 
 
 class IndexKeys:

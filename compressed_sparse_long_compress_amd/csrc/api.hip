@@ -36,11 +36,23 @@ int check_kv(const csa_kv_t& kv, int d, const char* what, const char* fn) {
     if (!aligned16(kv.nope) || !aligned16(kv.rope))
         return fail(CSA_EINVAL, "%s: %s.nope / %s.rope must be 16-byte aligned", fn, what, what);
     if (((uintptr_t)kv.scale & 3u) != 0) return fail(CSA_EINVAL, "%s: %s.scale must be 4-byte aligned", fn, what);
+    if (kv.pages) {
+        if (kv.page < 1 || (kv.page & (kv.page - 1)) != 0)
+            return fail(CSA_EINVAL, "%s: %s.page (%d) must be a power of two", fn, what, kv.page);
+        if (kv.cap % kv.page != 0)
+            return fail(CSA_EINVAL, "%s: %s.page (%d) must divide %s.cap (%lld)", fn, what, kv.page, what,
+                        (long long)kv.cap);
+    }
     (void)d;
     return CSA_OK;
 }
 
-csa::KvView view(const csa_kv_t& kv) { return csa::KvView{kv.nope, kv.rope, kv.scale, kv.cap}; }
+csa::KvView view(const csa_kv_t& kv) {
+    int sh = 0;
+    if (kv.pages)
+        while ((1 << sh) < kv.page) ++sh;
+    return csa::KvView{kv.nope, kv.rope, kv.scale, kv.cap, kv.pages, sh};
+}
 
 int check_mqa_common(const char* fn, const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int32_t H,
                      int32_t d, int32_t m, const csa_kv_t& comp, const csa_kv_t& win, int32_t window, float* out,
@@ -94,8 +106,8 @@ int csa_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t 
     if (n_tok / m > out.cap)
         return fail(CSA_EINVAL, "%s: %lld new entries exceed out.cap (%lld): slots would collide", fn,
                     (long long)(n_tok / m), (long long)out.cap);
-    hipError_t e = csa::launch_compress(kv, logits, tok0, n_tok, m, d, csa::rope_table((double)rope_base), (int64_t)seq * out.cap,
-                                        out.cap, out.nope, out.rope, out.scale, (hipStream_t)stream);
+    hipError_t e = csa::launch_compress(kv, logits, tok0, n_tok, m, d, csa::rope_table((double)rope_base), seq,
+                                        view(out), out.nope, out.rope, out.scale, (hipStream_t)stream);
     return hip_status(e, fn);
 }
 
@@ -118,8 +130,7 @@ int csa_compress_channel(const uint16_t* kv, const float* logits, int64_t tok0, 
         return fail(CSA_EINVAL, "%s: %lld new entries exceed out.cap (%lld): slots would collide", fn,
                     (long long)(n_tok / m), (long long)out.cap);
     hipError_t e = csa::launch_compress_channel(kv, logits, tok0, n_tok, m, d, csa::rope_table((double)rope_base),
-                                                (int64_t)seq * out.cap, out.cap, out.nope, out.rope, out.scale,
-                                                (hipStream_t)stream);
+                                                seq, view(out), out.nope, out.rope, out.scale, (hipStream_t)stream);
     return hip_status(e, fn);
 }
 

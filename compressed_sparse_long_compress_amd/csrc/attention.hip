@@ -75,10 +75,10 @@ __device__ __forceinline__ int64_t resolve(int64_t u, int64_t t, int32_t sq, con
     if (u < rk.n_c) {
         const int64_t j = idx ? (int64_t)idx[t * k + u] : u;
         if (j < 0 || j >= rk.nv) return -1;
-        return (int64_t)sq * comp.cap + (j % comp.cap);
+        return kv_row(comp.pages, comp.pshift, comp.cap, sq, j % comp.cap);
     }
     const int64_t p = rk.lo + (u - rk.n_c);
-    return -((int64_t)sq * win.cap + (p % win.cap) + 2);
+    return -(kv_row(win.pages, win.pshift, win.cap, sq, p % win.cap) + 2);
 }
 
 // cos / sin of pos * theta: fp64 product, fp64 reduction by 2*pi (two-part
@@ -512,7 +512,7 @@ __device__ __forceinline__ void store_out(const float* ob, const float* cs, int 
     }
 }
 
-template <int D>
+template <int D, bool PG>  // PG: a view is paged
 __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, const int32_t* __restrict__ seq,
                                                const int64_t* __restrict__ pos, const int32_t* __restrict__ idx, int k,
                                                int m, KvView comp, KvView win, int window, float sm_scale, RopeTab rt,
@@ -570,15 +570,25 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
     const float* const c_scale = comp.scale;
     const float* const w_scale = win.scale;
     const int64_t c_cap = comp.cap, w_cap = win.cap;
+    const int32_t* const c_pages = comp.pages;
+    const int32_t* const w_pages = win.pages;
+    const int c_psh = comp.pshift, w_psh = win.pshift;
     auto resolve_at = [&](int64_t u, int64_t j) -> Res {
         const bool inw = u >= rk.n_c;
         if (u >= u1 || (!inw && (j < 0 || j >= rk.nv))) return Res{g_zero_entry, g_zero_entry + DN, nullptr, false};
-        const int64_t x = inw ? rk.lo + (u - rk.n_c) : j;
-        const int64_t cap = inw ? w_cap : c_cap;
         const uint8_t* nb = inw ? w_nope : c_nope;
         const uint16_t* rb = inw ? w_rope : c_rope;
         const float* sb = inw ? w_scale : c_scale;
-        const int64_t row = (int64_t)sq * cap + (x % cap);
+        const int64_t x = inw ? rk.lo + (u - rk.n_c) : j;
+        int64_t row;
+        if constexpr (!PG) {
+            const int64_t cap = inw ? w_cap : c_cap;
+            row = (int64_t)sq * cap + (x % cap);
+        } else if (inw) {  // a branch, not selects: selects of this many view fields went to scratch memory
+            row = kv_row(w_pages, w_psh, w_cap, sq, x % w_cap);
+        } else {
+            row = kv_row(c_pages, c_psh, c_cap, sq, x % c_cap);
+        }
         return Res{nb + row * DN, (const uint8_t*)(rb + row * 64), sb + row, true};
     };
     auto publish_addr = [&](int b, const Res& r) {
@@ -955,7 +965,7 @@ struct __align__(16) MqaWsSmem {
     int restart;
 };
 
-template <int D>
+template <int D, bool PG>  // PG: a view is paged
 __global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q, const int32_t* __restrict__ seq,
                                                  const int64_t* __restrict__ pos, const int32_t* __restrict__ idx,
                                                  int k, int m, KvView comp, KvView win, int window, float sm_scale,
@@ -1007,15 +1017,25 @@ __global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q,
     const float* const c_scale = comp.scale;
     const float* const w_scale = win.scale;
     const int64_t c_cap = comp.cap, w_cap = win.cap;
+    const int32_t* const c_pages = comp.pages;
+    const int32_t* const w_pages = win.pages;
+    const int c_psh = comp.pshift, w_psh = win.pshift;
     auto resolve_at = [&](int64_t u, int64_t j) -> Res {
         const bool inw = u >= rk.n_c;
         if (u >= u1 || (!inw && (j < 0 || j >= rk.nv))) return Res{g_zero_entry, g_zero_entry + DN, nullptr, false};
-        const int64_t x = inw ? rk.lo + (u - rk.n_c) : j;
-        const int64_t cap = inw ? w_cap : c_cap;
         const uint8_t* nb = inw ? w_nope : c_nope;
         const uint16_t* rb = inw ? w_rope : c_rope;
         const float* sb = inw ? w_scale : c_scale;
-        const int64_t row = (int64_t)sq * cap + (x % cap);
+        const int64_t x = inw ? rk.lo + (u - rk.n_c) : j;
+        int64_t row;
+        if constexpr (!PG) {
+            const int64_t cap = inw ? w_cap : c_cap;
+            row = (int64_t)sq * cap + (x % cap);
+        } else if (inw) {  // a branch, not selects: selects of this many view fields went to scratch memory
+            row = kv_row(w_pages, w_psh, w_cap, sq, x % w_cap);
+        } else {
+            row = kv_row(c_pages, c_psh, c_cap, sq, x % c_cap);
+        }
         return Res{nb + row * DN, (const uint8_t*)(rb + row * 64), sb + row, true};
     };
     auto publish = [&](int b, const Res& r, float sc) {
@@ -1531,15 +1551,20 @@ static void launch_mqa_t(const uint16_t* q, const int32_t* seq, const int64_t* p
                          int64_t max_keys, float* out, float* lse, float* po, float* pml, hipStream_t st) {
     // splits of more than a few tiles: the two-role kernel (its pipeline costs a step at either end)
     const bool long_splits = (max_keys + S - 1) / S > 12 * KT;
-    if (H == 64 && D == 512 && long_splits)
-        hipLaunchKernelGGL((k_mqa64ws<512>), dim3((unsigned)(T * S)), dim3(512), 0, st, q, seq, pos, idx, k, m, comp,
-                           win, window, sm_scale, rt, S, out, lse, po, pml);
-    else if constexpr (H == 64)
-        hipLaunchKernelGGL((k_mqa64<D>), dim3((unsigned)(T * S)), dim3(256), 0, st, q, seq, pos, idx, k, m, comp, win,
-                           window, sm_scale, rt, S, out, lse, po, pml);
-    else
-        hipLaunchKernelGGL((k_mqa<H, D>), dim3((unsigned)(T * S)), dim3(256), 0, st, q, seq, pos, idx, k, m, comp,
-                           win, window, sm_scale, rt, S, out, lse, po, pml);
+    const bool paged = comp.pages || win.pages;  // paged views: their own instantiation
+#define CSA_MQA_LAUNCH(KERN, NTH)                                                                                  \
+    hipLaunchKernelGGL((KERN), dim3((unsigned)(T * S)), dim3(NTH), 0, st, q, seq, pos, idx, k, m, comp, win, window, \
+                       sm_scale, rt, S, out, lse, po, pml)
+    if (H == 64 && D == 512 && long_splits) {
+        if (paged) CSA_MQA_LAUNCH((k_mqa64ws<512, true>), 512);
+        else CSA_MQA_LAUNCH((k_mqa64ws<512, false>), 512);
+    } else if constexpr (H == 64) {
+        if (paged) CSA_MQA_LAUNCH((k_mqa64<D, true>), 256);
+        else CSA_MQA_LAUNCH((k_mqa64<D, false>), 256);
+    } else {
+        CSA_MQA_LAUNCH((k_mqa<H, D>), 256);
+    }
+#undef CSA_MQA_LAUNCH
     if (S > 1)
         if constexpr (H == 64)
             hipLaunchKernelGGL((k_mqa_combine16<D>), dim3((unsigned)(T * H)), dim3(128), 0, st, (const _Float16*)po, pml,

@@ -30,8 +30,9 @@ __device__ __forceinline__ float f64_to_f32_odd(double d) {
 
 template <int D>
 __global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ kv, const float* __restrict__ logits,
-                                                  int64_t tok0, int64_t n_blk, int m, RopeTab rt, int64_t row0,
-                                                  int64_t cap, uint8_t* __restrict__ nope, uint16_t* __restrict__ rope,
+                                                  int64_t tok0, int64_t n_blk, int m, RopeTab rt, int64_t seq,
+                                                  int64_t cap, const int32_t* __restrict__ pages, int pshift,
+                                                  uint8_t* __restrict__ nope, uint16_t* __restrict__ rope,
                                                   float* __restrict__ scale) {
     constexpr int DN = D - 64;
     constexpr int PER = D / 64;  // dims per lane (2 or 8)
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ k
     for (int o = 32; o > 0; o >>= 1) am = fmax(am, __shfl_xor(am, o));
     const float s = am > 0.0 ? (float)(am / 448.0) : 1.0f;
 
-    const int64_t row = row0 + (J % cap);
+    const int64_t row = kv_row(pages, pshift, cap, seq, J % cap);
     if (is_rope) {
         uint16_t r[PER];
 #pragma unroll
@@ -145,9 +146,10 @@ __global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ k
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void k_compress_ch(const uint16_t* __restrict__ kv, const float* __restrict__ logits,
-                                                     int64_t tok0, int64_t n_blk, int m, RopeTab rt, int64_t row0,
-                                                     int64_t cap, uint8_t* __restrict__ nope,
-                                                     uint16_t* __restrict__ rope, float* __restrict__ scale) {
+                                                     int64_t tok0, int64_t n_blk, int m, RopeTab rt, int64_t seq,
+                                                     int64_t cap, const int32_t* __restrict__ pages, int pshift,
+                                                     uint8_t* __restrict__ nope, uint16_t* __restrict__ rope,
+                                                     float* __restrict__ scale) {
     constexpr int DN = D - 64;
     constexpr int PER = D / 64;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(256) void k_compress_ch(const uint16_t* __restrict_
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) am = fmax(am, __shfl_xor(am, o));
     const float s = am > 0.0 ? (float)(am / 448.0) : 1.0f;
-    const int64_t row = row0 + (J % cap);
+    const int64_t row = kv_row(pages, pshift, cap, seq, J % cap);
     if (is_rope) {
 #pragma unroll
         for (int e = 0; e < PER; ++e) rope[row * 64 + (dim0 - DN) + e] = f32_to_bf16_bits(f64_to_f32_odd(c[e]));
@@ -288,16 +290,16 @@ __global__ __launch_bounds__(256) void k_compress_ikey(const uint16_t* __restric
 }
 
 hipError_t launch_compress_channel(const uint16_t* kv, const float* logits, int64_t tok0, int64_t n_tok, int m, int d,
-                                   const RopeTab& rt, int64_t row0, int64_t cap, uint8_t* nope, uint16_t* rope,
+                                   const RopeTab& rt, int64_t seq, const KvView& out, uint8_t* nope, uint16_t* rope,
                                    float* scale, hipStream_t st) {
     const int64_t n_blk = n_tok / m;
     if (n_blk == 0) return hipSuccess;
     dim3 grid((unsigned)((n_blk + 3) / 4)), block(256);
     if (d == 512)
-        hipLaunchKernelGGL(k_compress_ch<512>, grid, block, 0, st, kv, logits, tok0, n_blk, m, rt, row0, cap, nope,
+        hipLaunchKernelGGL(k_compress_ch<512>, grid, block, 0, st, kv, logits, tok0, n_blk, m, rt, seq, out.cap, out.pages, out.pshift, nope,
                            rope, scale);
     else
-        hipLaunchKernelGGL(k_compress_ch<128>, grid, block, 0, st, kv, logits, tok0, n_blk, m, rt, row0, cap, nope,
+        hipLaunchKernelGGL(k_compress_ch<128>, grid, block, 0, st, kv, logits, tok0, n_blk, m, rt, seq, out.cap, out.pages, out.pshift, nope,
                            rope, scale);
     return hipGetLastError();
 }
@@ -318,16 +320,16 @@ hipError_t launch_compress_index_keys(const uint16_t* k, const float* logits, in
 }
 
 hipError_t launch_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t n_tok, int m, int d,
-                           const RopeTab& rt, int64_t row0, int64_t cap, uint8_t* nope, uint16_t* rope, float* scale,
-                           hipStream_t st) {
+                           const RopeTab& rt, int64_t seq, const KvView& out, uint8_t* nope, uint16_t* rope,
+                           float* scale, hipStream_t st) {
     const int64_t n_blk = n_tok / m;
     if (n_blk == 0) return hipSuccess;
     dim3 grid((unsigned)((n_blk + 3) / 4)), block(256);
     if (d == 512)
-        hipLaunchKernelGGL(k_compress<512>, grid, block, 0, st, kv, logits, tok0, n_blk, m, rt, row0, cap, nope,
+        hipLaunchKernelGGL(k_compress<512>, grid, block, 0, st, kv, logits, tok0, n_blk, m, rt, seq, out.cap, out.pages, out.pshift, nope,
                            rope, scale);
     else
-        hipLaunchKernelGGL(k_compress<128>, grid, block, 0, st, kv, logits, tok0, n_blk, m, rt, row0, cap, nope,
+        hipLaunchKernelGGL(k_compress<128>, grid, block, 0, st, kv, logits, tok0, n_blk, m, rt, seq, out.cap, out.pages, out.pshift, nope,
                            rope, scale);
     return hipGetLastError();
 }

@@ -12,6 +12,23 @@ struct RopeTab {
 };
 RopeTab rope_table(double base);
 
+struct KvView {
+    const uint8_t* nope;
+    const uint16_t* rope;
+    const float* scale;
+    int64_t cap;
+    const int32_t* pages;  // nullptr: contiguous rows seq*cap + slot
+    int pshift;            // log2(slots per page) when paged
+};
+
+// Row of slot `slot` (< cap) of sequence `seq`: contiguous, or through the page table.
+__host__ __device__ __forceinline__ int64_t kv_row(const int32_t* pages, int pshift, int64_t cap, int64_t seq,
+                                                   int64_t slot) {
+    if (!pages) return seq * cap + slot;
+    const int64_t npp = cap >> pshift;
+    return ((int64_t)pages[seq * npp + (slot >> pshift)] << pshift) | (slot & ((1LL << pshift) - 1));
+}
+
 // Top-k workspace of the few-long-rows path (T < kTopkMaxRows rows): the
 // row summaries, summ[T][topk_groups(n_cols)], each the largest order key of
 // the visible columns of one kTopkGroup-column group (0 for none).
@@ -20,11 +37,11 @@ constexpr int kTopkGroup = 32;
 __host__ __device__ inline int64_t topk_groups(int64_t n_cols) { return (n_cols + kTopkGroup - 1) / kTopkGroup; }
 
 hipError_t launch_compress(const uint16_t* kv, const float* logits, int64_t tok0, int64_t n_tok, int m, int d,
-                           const RopeTab& rt, int64_t row0, int64_t cap, uint8_t* nope, uint16_t* rope, float* scale,
-                           hipStream_t st);
+                           const RopeTab& rt, int64_t seq, const KvView& out, uint8_t* nope, uint16_t* rope,
+                           float* scale, hipStream_t st);
 // logits [n_tok][d]: per-channel weights
 hipError_t launch_compress_channel(const uint16_t* kv, const float* logits, int64_t tok0, int64_t n_tok, int m, int d,
-                                   const RopeTab& rt, int64_t row0, int64_t cap, uint8_t* nope, uint16_t* rope,
+                                   const RopeTab& rt, int64_t seq, const KvView& out, uint8_t* nope, uint16_t* rope,
                                    float* scale, hipStream_t st);
 // raw bf16 index keys -> MXFP4 rows
 hipError_t launch_compress_index_keys(const uint16_t* k, const float* logits, int64_t tok0, int64_t n_tok, int m,
@@ -50,12 +67,7 @@ bool topk_uses_summary(int64_t T, int64_t n_cols);
 hipError_t launch_topk(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos, int m, int k, int32_t* idx,
                        void* ws, bool prepared, hipStream_t st);
 
-struct KvView {
-    const uint8_t* nope;
-    const uint16_t* rope;
-    const float* scale;
-    int64_t cap;
-};
+
 
 size_t mqa_workspace_bytes(int64_t T, int H, int d, int64_t max_keys);
 // idx == nullptr selects the dense (HCA) key set

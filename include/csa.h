@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CSA_VERSION 100
+#define CSA_VERSION 101
 
 enum {
     CSA_OK = 0,
@@ -71,19 +71,30 @@ typedef void* csa_stream_t;
 /*
  * Mixed-precision entries for n_seq sequences, `cap` slots each.  Sequence s,
  * slot i lives at row s*cap + i of every array:
- *   nope  [n_seq*cap][d - 64]  FP8 E4M3FN codes
- *   rope  [n_seq*cap][64]      bf16 bit patterns
- *   scale [n_seq*cap]          fp32
+ *   nope  [rows][d - 64]  FP8 E4M3FN codes
+ *   rope  [rows][64]      bf16 bit patterns
+ *   scale [rows]          fp32
  * Compressed entry j lives at slot j % cap (cap >= entries kept).  A window
  * ring holds raw tokens (m = 1 entries): token p at slot p % cap.
  * Alignment: nope and rope rows must start on 16-byte boundaries
  * ((d-64) % 16 == 0 and 16-byte aligned base pointers).
+ *
+ * Paged layout (the pages' compressed-entry cache of a two-level KV cache
+ * whose entries can be shared by sequences with a common prefix: [xmsumi]
+ * § 百万Token 长上下文真实表现): with `pages` non-NULL, slot i of sequence s
+ * lives at row pages[s * (cap / page) + i / page] * page + i % page.  page is
+ * a power of two dividing cap; the table holds physical page numbers, and
+ * sequences may share pages (a common prefix stored once; a page written by
+ * csa_compress must not be shared with a sequence that reads it in the same
+ * call).  pages == NULL (page ignored) is the contiguous layout above.
  */
 typedef struct csa_kv {
     uint8_t* nope;
     uint16_t* rope;
     float* scale;
     int64_t cap;
+    const int32_t* pages; /* NULL: contiguous rows */
+    int32_t page;         /* slots per page when paged */
 } csa_kv_t;
 
 /*

@@ -75,6 +75,17 @@ def test_compress_variants_validation(csa):
     assert rc == csa.CSA_EINVAL and b"null" in L.csa_last_error()
 
 
+def test_paged_cache_validation(csa):
+    L = csa._lib
+    p = ctypes.c_void_p(256)
+    bad = csa._Kv(256, 256, 256, 96, 256, 24)  # page not a power of two
+    rc = L.csa_compress(p, p, 0, 8, 4, 512, 10000.0, 0, bad, None)
+    assert rc == csa.CSA_EINVAL and b"power of two" in L.csa_last_error()
+    bad = csa._Kv(256, 256, 256, 96, 256, 64)  # page does not divide cap
+    rc = L.csa_compress(p, p, 0, 8, 4, 512, 10000.0, 0, bad, None)
+    assert rc == csa.CSA_EINVAL and b"divide" in L.csa_last_error()
+
+
 def test_index_topk_validation(csa):
     L = csa._lib
     keys = csa._IdxKeys(None, None, 16)

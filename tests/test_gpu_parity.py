@@ -613,3 +613,84 @@ def test_end_to_end_prefill_small(lib, dev, gen, orc):
     ref_o, ref_l = orc.attend(wl["q"], wl["seq"], wl["pos"], o_hca, wl["hca_cap"], o_win, wl["T"], W, wl["m_hca"],
                               wl["sm_scale"])
     assert_attn_close(hout.cpu().numpy(), hlse.cpu().numpy(), ref_o, ref_l, "e2e dense")
+
+
+# ---------------------------------------------------------------------------
+# paged compressed cache (and window ring): same results as the contiguous layout
+# ---------------------------------------------------------------------------
+def _paged_like(lib, torch, n_seq, cap, d, page, perm, extra):
+    """An empty paged cache: n_seq sequences of cap slots, physical pages perm[s * npp + i] (+ extra spare pages)."""
+    npp = cap // page
+    rows = (n_seq * npp + extra) * page
+    pages = torch.tensor(np.asarray(perm, np.int32).reshape(n_seq, npp), device="cuda")
+    return lib.KvCache(torch.zeros(rows, d - 64, dtype=torch.uint8, device="cuda"),
+                       torch.zeros(rows, 64, dtype=torch.bfloat16, device="cuda"),
+                       torch.zeros(rows, dtype=torch.float32, device="cuda"), cap, pages=pages, page=page)
+
+
+def _slot_rows(cache, s, cap):
+    if cache.pages is None:
+        return s * cap + np.arange(cap)
+    pg = cache.pages.cpu().numpy()[s]
+    i = np.arange(cap)
+    return pg[i // cache.page] * cache.page + i % cache.page
+
+
+@pytest.mark.parametrize("share", [False, True])
+def test_paged_cache_matches_contiguous(lib, dev, gen, share):
+    """Compression into a paged cache (pages in a shuffled order, a spare page unused), then
+    CSA and HCA attention with paged entries and a paged window ring, equal the contiguous
+    layout bit for bit.  share: sequence 1 reuses sequence 0's first four physical pages (a
+    common prefix compressed once), against a contiguous cache holding copies."""
+    import torch
+
+    _say(f"paged cache, shared prefix {share}")
+    B, m, d, cap, page, W, wpage = 3, 4, 512, 128, 16, 128, 32
+    L = m * cap
+    npp = cap // page
+    kv = [gen.normal_bf16(700 + b, 1, (L, d)) for b in range(B)]
+    lg = [gen.normal_f32(700 + b, 2, (L,)) for b in range(B)]
+    P = 4  # shared pages (P * page entries = P * page * m tokens)
+    if share:
+        kv[1][: P * page * m] = kv[0][: P * page * m]
+        lg[1][: P * page * m] = lg[0][: P * page * m]
+    rng = np.random.default_rng(11)
+    perm = rng.permutation(B * npp + 1)[: B * npp]
+    if share:
+        perm = perm.reshape(B, npp)
+        perm[1, :P] = perm[0, :P]
+        perm = perm.reshape(-1)
+    contig = lib.KvCache.empty(B, cap, d)
+    paged = _paged_like(lib, torch, B, cap, d, page, perm, 1)
+    wperm = rng.permutation(B * (W // wpage))
+    wc = lib.KvCache.empty(B, W, d)
+    wp = _paged_like(lib, torch, B, W, d, wpage, wperm, 0)
+    for b in range(B):
+        for cache in (contig, paged):
+            if share and b == 1 and cache is paged:
+                # the shared prefix is already in place: compress only this sequence's own blocks
+                lib.csa_compress(dev.bf16(kv[b][P * page * m:]), dev.t(lg[b][P * page * m:]), P * page * m, m, b, cache)
+            else:
+                lib.csa_compress(dev.bf16(kv[b]), dev.t(lg[b]), 0, m, b, cache)
+        for cache in (wc, wp):
+            lib.csa_compress(dev.bf16(kv[b][L - W:]), dev.t(lg[b][L - W:]), L - W, 1, b, cache)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for (a, c) in ((contig, paged), (wc, wp)):
+            ra, rc = _slot_rows(a, b, a.cap), _slot_rows(c, b, c.cap)
+            for x, y in ((a.nope, c.nope), (a.rope, c.rope), (a.scale, c.scale)):
+                assert torch.equal(x[torch.tensor(ra, device="cuda")], y[torch.tensor(rc, device="cuda")])
+    # attention over both layouts
+    T, H, k = 2 * B, 64, 96
+    seq = np.repeat(np.arange(B), 2).astype(np.int32)
+    pos = np.tile(np.array([L - 1, L - 37]), B).astype(np.int64)
+    q = gen.normal_bf16(799, 3, (T, H, d))
+    idx = np.stack([np.sort(rng.choice((int(p) + 1) // m, size=k, replace=False)) for p in pos]).astype(np.int32)
+    args = dict(seq=dev.t(seq), pos=dev.t(pos), m=m, window=W, sm_scale=1.0 / np.sqrt(d))
+    o1, l1 = lib.csa_sparse_mqa(dev.bf16(q), idx=dev.t(idx), comp=contig, win=wc, **args)
+    o2, l2 = lib.csa_sparse_mqa(dev.bf16(q), idx=dev.t(idx), comp=paged, win=wp, **args)
+    h1, hl1 = lib.hca_dense_mqa(dev.bf16(q), max_vis=cap, comp=contig, win=wc, **args)
+    h2, hl2 = lib.hca_dense_mqa(dev.bf16(q), max_vis=cap, comp=paged, win=wp, **args)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(h1, h2) and torch.equal(hl1, hl2)

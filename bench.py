@@ -82,9 +82,22 @@ class DecodeSet:
         B, N, W = wl["B"], wl["N"], wl["W"]
         keys0 = dev.index_keys(wl["keys"], N)
         comp0 = dev.kv_cache(wl["comp"], N)
+        if wl.get("page"):
+            # paged layout: the same entries in pages placed in a seeded shuffled order
+            import numpy as np
+
+            pg = wl["page"]
+            npp = N // pg
+            perm = np.random.default_rng(wl["seed"]).permutation(B * npp).astype(np.int32)
+            src = torch.arange(B * N, device="cuda")
+            dst = (torch.tensor(perm, device="cuda").view(B, npp).repeat_interleave(pg, dim=1) * pg
+                   + torch.arange(N, device="cuda").remainder(pg)).view(-1)
+            nope, rope, scale = (torch.empty_like(a) for a in (comp0.nope, comp0.rope, comp0.scale))
+            nope[dst], rope[dst], scale[dst] = comp0.nope[src], comp0.rope[src], comp0.scale[src]
+            comp0 = csa.KvCache(nope, rope, scale, N, pages=torch.tensor(perm, device="cuda").view(B, npp), page=pg)
         self.keys = [keys0] + [csa.IndexKeys(keys0.data.clone(), keys0.scale.clone(), N) for _ in range(replicas - 1)]
-        self.comp = [comp0] + [csa.KvCache(comp0.nope.clone(), comp0.rope.clone(), comp0.scale.clone(), N)
-                               for _ in range(replicas - 1)]
+        self.comp = [comp0] + [csa.KvCache(comp0.nope.clone(), comp0.rope.clone(), comp0.scale.clone(), N,
+                                           pages=comp0.pages, page=comp0.page) for _ in range(replicas - 1)]
         self.win = dev.kv_cache(wl["win"], W)
         self.q = dev.bf16(wl["q"])
         self.iq = dev.t(wl["iq"][0])
@@ -408,8 +421,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--all", action="store_true", help="also time the other workloads (secondary object)")
     ap.add_argument("--workload", default="csa_decode_1m",
-                    choices=["csa_decode_1m", "csa_decode_1m_mtp2", "csa_decode_64k", "hca_decode_1m",
-                             "prefill_chunk", "compress_chunk"],
+                    choices=["csa_decode_1m", "csa_decode_1m_mtp2", "csa_decode_1m_paged", "csa_decode_64k",
+                             "hca_decode_1m", "prefill_chunk", "compress_chunk"],
                     help="time only this workload and print its line (profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true",

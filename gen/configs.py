@@ -14,6 +14,7 @@ Named workloads (seeds 101..105):
   hca_decode_1m  B=8,  L=1,048,576 at m'=128 (8,192 entries)
   csa_decode_1m  B=4,  L=1,048,576 (262,144 entries), 5% planted index keys
   csa_decode_1m_mtp2  the same cache, two query rows per sequence (positions L-2, L-1)
+  csa_decode_1m_paged the same workload with the compressed cache in shuffled 1,024-entry pages
   prefill_chunk  8,192 new tokens after a 131,072-token context (CSA + HCA)
   compress_chunk 8,192 raw tokens (d=512) and index-key tokens (d_i=128), seed 106
 """
@@ -128,6 +129,12 @@ def named(name, **over):
         return csa_decode(**kw)
     if name == "compress_chunk":
         return compress_chunk(**over)
+    if name == "csa_decode_1m_paged":
+        kw = dict(B=4, L=1 << 20, plant_frac=0.05, seed=104)
+        kw.update(over)
+        wl = csa_decode(**kw)
+        wl["page"] = 1024  # compressed entries per page; pages in a seeded shuffled order
+        return wl
     if name == "csa_decode_1m_mtp2":
         kw = dict(B=4, L=1 << 20, plant_frac=0.05, seed=104, tokens=2)
         kw.update(over)

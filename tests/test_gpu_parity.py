@@ -636,21 +636,21 @@ def _slot_rows(cache, s, cap):
     return pg[i // cache.page] * cache.page + i % cache.page
 
 
-@pytest.mark.parametrize("share", [False, True])
-def test_paged_cache_matches_contiguous(lib, dev, gen, share):
+@pytest.mark.parametrize("share,page,wpage", [(False, 16, 32), (True, 16, 32), (False, 128, 128), (True, 1, 1)])
+def test_paged_cache_matches_contiguous(lib, dev, gen, share, page, wpage):
     """Compression into a paged cache (pages in a shuffled order, a spare page unused), then
     CSA and HCA attention with paged entries and a paged window ring, equal the contiguous
     layout bit for bit.  share: sequence 1 reuses sequence 0's first four physical pages (a
     common prefix compressed once), against a contiguous cache holding copies."""
     import torch
 
-    _say(f"paged cache, shared prefix {share}")
-    B, m, d, cap, page, W, wpage = 3, 4, 512, 128, 16, 128, 32
+    _say(f"paged cache, shared prefix {share}, page {page}, window page {wpage}")
+    B, m, d, cap, W = 3, 4, 512, 128, 128
     L = m * cap
     npp = cap // page
     kv = [gen.normal_bf16(700 + b, 1, (L, d)) for b in range(B)]
     lg = [gen.normal_f32(700 + b, 2, (L,)) for b in range(B)]
-    P = 4  # shared pages (P * page entries = P * page * m tokens)
+    P = max(1, 64 // page) if page < cap else 0  # shared pages (P * page entries = P * page * m tokens)
     if share:
         kv[1][: P * page * m] = kv[0][: P * page * m]
         lg[1][: P * page * m] = lg[0][: P * page * m]

@@ -584,3 +584,132 @@ def test_compress_index_keys_uniform_logits_mean(orc):
     assert np.all(scale[0] == 126)
     want = np.where(np.arange(d_i) % 2 == 0, 3.0, -2.0)
     assert np.array_equal(dec * 0.5, want)
+
+
+# --------------------------------------------------------------------------
+# attention gradient (oracle/backward.py)
+# --------------------------------------------------------------------------
+def _bw():
+    from oracle import backward
+    return backward
+
+
+def _rotated(g, tp, d):
+    gr = np.array(g, dtype=np.float64)
+    gr[..., d - 64:] = _bw().rope_rows(gr[..., d - 64:], tp)
+    return gr
+
+
+def test_bwd_forward_core_matches_oracle_attend(orc, gen):
+    """The fp64 forward the gradient is taken of is the oracle's attention step."""
+    bw = _bw()
+    m, H, d, W, N = 4, 4, 128, 8, 64
+    comp = _cache(gen, 51, N, d - 64)
+    win = gen.entries(51, 41, 16, d - 64)
+    q = gen.normal_bf16(51, 42, (3, H, d))
+    pos = np.array([255, 130, 9], np.int64)
+    seq = np.zeros(3, np.int32)
+    rng = np.random.default_rng(51)
+    idx = rng.integers(-3, 70, size=(3, 12)).astype(np.int32)  # masked, out-of-range and valid picks
+    sm = 1 / math.sqrt(d)
+    out, lse = orc.attend(q, seq, pos, comp, N, win, 16, W, m, sm, idx=idx)
+    qf = orc.bf16_array_to_f64(q)
+    ce, we = orc.dequant_entries(*comp), orc.dequant_entries(*win)
+    for t in range(3):
+        rows = bw.key_rows(t, seq, pos, m, N, 16, W, idx)
+        keys = np.stack([(ce if kd == "c" else we)[r] for kd, r in rows])
+        o, l = bw.attend_core(qf[t], keys, int(pos[t]), sm)
+        assert np.allclose(o, out[t], rtol=0, atol=1e-12) and np.allclose(l, lse[t], rtol=0, atol=1e-12)
+
+
+def test_bwd_matches_central_differences():
+    """Every element of dq and de against a central difference of the fp64 forward."""
+    bw = _bw()
+    rng = np.random.default_rng(52)
+    H, d, n, tp, sm = 3, 128, 7, 1234, 0.09
+    qh = rng.standard_normal((H, d))
+    keys = rng.standard_normal((n, d)) * 1.5
+    g = rng.standard_normal((H, d))
+    dq, dk = bw.attend_core_bwd(qh, keys, tp, sm, g)
+
+    def loss(qq, kk):
+        return float((g * bw.attend_core(qq, kk, tp, sm)[0]).sum())
+
+    h = 1e-6
+    num_q = np.zeros_like(qh)
+    for i in range(H):
+        for e in range(d):
+            a, b = qh.copy(), qh.copy()
+            a[i, e] += h
+            b[i, e] -= h
+            num_q[i, e] = (loss(a, keys) - loss(b, keys)) / (2 * h)
+    num_k = np.zeros_like(keys)
+    for u in range(n):
+        for e in range(d):
+            a, b = keys.copy(), keys.copy()
+            a[u, e] += h
+            b[u, e] -= h
+            num_k[u, e] = (loss(qh, a) - loss(qh, b)) / (2 * h)
+    assert np.allclose(dq, num_q, rtol=1e-6, atol=1e-7)
+    assert np.allclose(dk, num_k, rtol=1e-6, atol=1e-7)
+
+
+def test_bwd_shift_of_all_entries_closed_form():
+    """Shifting every entry by c leaves the softmax unchanged and moves each output by R(-tp) c,
+    so the entry gradients sum to the rotated output gradients summed over heads."""
+    bw = _bw()
+    rng = np.random.default_rng(53)
+    H, d, n, tp = 5, 128, 11, 777
+    qh, keys, g = rng.standard_normal((H, d)), rng.standard_normal((n, d)), rng.standard_normal((H, d))
+    _, dk = bw.attend_core_bwd(qh, keys, tp, 0.1, g)
+    assert np.allclose(dk.sum(axis=0), _rotated(g, tp, d).sum(axis=0), rtol=1e-12, atol=1e-12)
+
+
+def test_bwd_single_key():
+    """One key: the softmax is constant (dq = 0) and the output is the key (de = sum_h g~_h)."""
+    bw = _bw()
+    rng = np.random.default_rng(54)
+    H, d, tp = 4, 128, 41
+    qh, key, g = rng.standard_normal((H, d)), rng.standard_normal((1, d)), rng.standard_normal((H, d))
+    dq, dk = bw.attend_core_bwd(qh, key, tp, 0.2, g)
+    assert np.abs(dq).max() < 1e-13
+    assert np.allclose(dk[0], _rotated(g, tp, d).sum(axis=0), rtol=0, atol=1e-12)
+
+
+def test_bwd_batch_accumulates_every_row(orc, gen):
+    """Rows sharing entries: the accumulated entry gradients of the whole batch sum to the rotated
+    output gradients of every row with keys; a row without keys has dq = 0."""
+    bw = _bw()
+    m, H, d, W, N = 4, 3, 128, 6, 48
+    comp = _cache(gen, 55, 2 * N, d - 64)
+    win = gen.entries(55, 41, 2 * 8, d - 64)
+    T = 5
+    q = gen.normal_bf16(55, 42, (T, H, d))
+    pos = np.array([150, 151, 150, 2, 40], np.int64)
+    seq = np.array([0, 0, 1, 1, 0], np.int32)
+    rng = np.random.default_rng(55)
+    idx = rng.integers(0, 30, size=(T, 10)).astype(np.int32)
+    idx[3] = -1  # row 3 (position 2): no visible entry is selected; window 0 leaves it empty
+    g = rng.standard_normal((T, H, d))
+    W0 = np.array([W, W, W, 0, W])
+    dq = np.zeros((T, H, d))
+    tot = np.zeros(d)
+    for t in range(T):  # rows with their own window sizes, one call each, summed
+        dqt, dc, dw = bw.attend_bwd(q[t:t + 1], seq[t:t + 1], pos[t:t + 1], comp, N, win, 8, int(W0[t]), m,
+                                    0.1, g[t:t + 1], idx=idx[t:t + 1])
+        dq[t] = dqt[0]
+        tot += dc.sum(axis=0) + dw.sum(axis=0)
+    want = sum(_rotated(g[t], pos[t], d).sum(axis=0) for t in range(T) if t != 3)
+    assert np.allclose(tot, want, rtol=1e-11, atol=1e-11)
+    assert np.abs(dq[3]).max() == 0.0
+    # the batch call accumulates the same entry gradients as the per-row calls
+    keep = [0, 1, 2, 4]
+    dqb, dcb, dwb = bw.attend_bwd(q[keep], seq[keep], pos[keep], comp, N, win, 8, W, m, 0.1, g[keep], idx=idx[keep])
+    acc_c, acc_w = np.zeros_like(dcb), np.zeros_like(dwb)
+    for t in keep:
+        _, dc, dw = bw.attend_bwd(q[t:t + 1], seq[t:t + 1], pos[t:t + 1], comp, N, win, 8, W, m, 0.1, g[t:t + 1],
+                                  idx=idx[t:t + 1])
+        acc_c += dc
+        acc_w += dw
+    assert np.allclose(dcb, acc_c, rtol=1e-12, atol=1e-12) and np.allclose(dwb, acc_w, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(dqb, dq[keep])

@@ -51,11 +51,13 @@ _lib.csa_sparse_mqa.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _i32
                                 _vp, _vp, _sz, _vp]
 _lib.hca_dense_mqa.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _Kv, _Kv, _i32, _f32, _f32, _vp, _vp,
                                _vp, _sz, _vp]
+_lib.csa_mqa_bwd.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _i32, _Kv, _Kv, _i32, _f32, _f32, _vp, _vp,
+                             _vp, _vp, _vp, _vp, _vp]
 _lib.csa_last_error.restype = ctypes.c_char_p
 _lib.csa_version.restype = ctypes.c_int
 
 EXPORTS = ["csa_compress", "csa_compress_channel", "csa_compress_index_keys", "csa_index_scores", "csa_index_scores_grouped", "csa_topk_workspace", "csa_topk", "csa_mqa_workspace",
-           "csa_sparse_mqa", "hca_dense_mqa", "csa_last_error", "csa_version"]
+           "csa_sparse_mqa", "hca_dense_mqa", "csa_mqa_bwd", "csa_last_error", "csa_version"]
 
 
 class CsaError(RuntimeError):
@@ -324,3 +326,32 @@ def hca_dense_mqa(q, seq, pos, m, max_vis, comp, win, window, sm_scale, rope_bas
                               _win(win, comp), int(window), float(sm_scale), float(rope_base), _ptr(out), _ptr(lse),
                               _ptr(ws), ws_bytes, _stream()))
     return out, lse
+
+
+def csa_mqa_bwd(q, seq, pos, idx, m, comp, win, window, sm_scale, out, lse, dout, rope_base=10000.0, dq=None,
+                dcomp=None, dwin=None):
+    """Gradient of the attention step -> (dq fp32 [T,H,d], dcomp fp32 [comp rows, d], dwin fp32 [win rows, d]).
+
+    idx int32 [T, k] (the selected entries) or None (every visible entry); out / lse are the forward's.
+    dcomp / dwin are accumulated into (fresh zeros when not given; dwin None when window is 0)."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(seq, "seq", torch.int32, 1)
+    _need(pos, "pos", torch.int64, 1)
+    _need(out, "out", torch.float32, 3)
+    _need(lse, "lse", torch.float32, 2)
+    _need(dout, "dout", torch.float32, 3)
+    k = 0
+    if idx is not None:
+        _need(idx, "idx", torch.int32, 2)
+        k = idx.shape[1]
+    T, H, d = q.shape
+    if dq is None:
+        dq = torch.empty(T, H, d, dtype=torch.float32, device=q.device)
+    if dcomp is None:
+        dcomp = torch.zeros(comp.nope.shape[0], d, dtype=torch.float32, device=q.device)
+    if dwin is None and window > 0:
+        dwin = torch.zeros(win.nope.shape[0], d, dtype=torch.float32, device=q.device)
+    _check(_lib.csa_mqa_bwd(_ptr(q), _ptr(seq), _ptr(pos), T, H, d, _ptr(idx), k, int(m), comp.c(), _win(win, comp),
+                            int(window), float(sm_scale), float(rope_base), _ptr(out), _ptr(lse), _ptr(dout),
+                            _ptr(dq), _ptr(dcomp), _ptr(dwin), _stream()))
+    return dq, dcomp, dwin

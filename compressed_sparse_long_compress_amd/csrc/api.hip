@@ -263,6 +263,25 @@ int csa_sparse_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos, in
     return hip_status(e, fn);
 }
 
+int csa_mqa_bwd(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int32_t H, int32_t d,
+                const int32_t* idx, int32_t k, int32_t m, csa_kv_t comp, csa_kv_t win, int32_t window, float sm_scale,
+                float rope_base, const float* out, const float* lse, const float* dout, float* dq, float* dcomp,
+                float* dwin, csa_stream_t stream) {
+    const char* fn = "csa_mqa_bwd";
+    if (int rc = check_mqa_common(fn, q, seq, pos, T, H, d, m, comp, win, window, dq, (float*)lse)) return rc;
+    if (d != 512) return fail(CSA_EUNSUPPORTED, "%s: d=%d unsupported (512)", fn, d);
+    if (T > 0 && (!out || !dout || !dcomp || (window > 0 && !dwin)))
+        return fail(CSA_EINVAL, "%s: null pointer argument", fn);
+    if (T > 0 && (!aligned16(out) || !aligned16(dout))) return fail(CSA_EINVAL, "%s: out and dout must be 16-byte aligned", fn);
+    if (idx && (k < 1 || k > 2048)) return fail(CSA_EUNSUPPORTED, "%s: k=%d outside 1..2048", fn, k);
+    if (!(rope_base > 0.f)) return fail(CSA_EINVAL, "%s: rope_base must be positive", fn);
+    if (T == 0) return ok();
+    hipError_t e = csa::launch_mqa_bwd(q, seq, pos, T, H, idx, idx ? k : 0, m, view(comp), view(win), window, sm_scale,
+                                       csa::rope_table((double)rope_base), out, lse, dout, dq, dcomp, dwin,
+                                       (hipStream_t)stream);
+    return hip_status(e, fn);
+}
+
 int hca_dense_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int32_t H, int32_t d,
                   int32_t m, int64_t max_vis, csa_kv_t comp, csa_kv_t win, int32_t window, float sm_scale,
                   float rope_base, float* out, float* lse, void* ws, size_t ws_bytes, csa_stream_t stream) {

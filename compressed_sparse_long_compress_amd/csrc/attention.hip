@@ -430,6 +430,7 @@ constexpr float kLazy = 8.f;     // e^8 ~ 2981
 constexpr float kSRatio = 16.f;  // 2981 * 16 < 65504
 
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 // A masked key-list position (top-k padding, an entry not yet visible) reads
@@ -1597,6 +1598,336 @@ hipError_t launch_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos,
         else CSA_MQA(16, 128);
     }
 #undef CSA_MQA
+    return hipGetLastError();
+}
+
+
+// ---------------------------------------------------------------------------
+// Backward of the attention step (training side): the gradient of sum(g * out)
+// with respect to the pre-RoPE query and to the dequantised entries, for the
+// forward above (keys and values are the same entry, RoPE on the last 64 dims,
+// reverse RoPE on the output).  With q~ = R(tp) q, g~ = R(tp) g, the forward's
+// lse and out, D = <g, out>:
+//   p_u = exp(c <q~, e_u> - lse),  ds_u = p_u (<g~, e_u> - D)
+//   dq  = R(-tp) (c sum_u ds_u e_u),  de_u += c ds_u q~ + p_u g~.
+// One workgroup per (query row, group of 16 heads) walks the row's whole key
+// list in tiles of 64 entries: wave w takes key block w of a tile for the scores
+// (S and dP as keys x heads, MFMA 16x16x32 f16), then dims [128 w, 128 w + 128)
+// for dq (accumulated in registers) and for the entry gradients, which leave
+// through fp32 atomics (an entry is shared by many rows and heads).  g is
+// scaled by a power of two per workgroup (|g~ s_g| <= 1 per head) so that it and
+// ds fit fp16 whatever the loss scale; the scale is divided out exactly.
+// ---------------------------------------------------------------------------
+constexpr int kBwdKT = 64;  // keys per tile
+
+struct __align__(16) MqaBwdSmem {
+    static constexpr int QS = 512 + 8;  // fp16 row stride of the [head][dim] copies
+    static constexpr int KS = 512 + 16;
+    static constexpr int PS = kBwdKT + 8;
+    _Float16 qs[16 * QS];      // c * q~, [head][dim]
+    _Float16 gs[16 * QS];      // s_g * g~
+    _Float16 kt[kBwdKT * KS];  // the tile: FP8 dims as decoded (scale apart), RoPE dims
+    _Float16 dsn[16 * PS];     // [head][slot] ds * s_g * entry scale (dq over FP8 dims)
+    _Float16 dsr[16 * PS];     // [head][slot] ds * s_g
+    _Float16 pp[16 * PS];      // [head][slot] p
+    int64_t krow[2][kBwdKT];   // resolved row code per key of tile j in [j & 1] (-1 masked)
+    float kscl[2][kBwdKT];     // entry scale, -1 for a masked key
+    float cs[64];
+    float red[4][16];
+};
+
+// slot of the [head][slot] arrays -> key of the tile: within each half of 32 keys, slot
+// 8 g + 4 e + i holds key 16 e + 4 g + i (the order the MFMA operands read them in)
+__device__ __forceinline__ int bwd_slot_key(int slot) {
+    const int r = slot & 31;
+    return (slot & 32) + 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
+}
+
+__global__ __launch_bounds__(256) void k_mqa_bwd(const uint16_t* __restrict__ q, const int32_t* __restrict__ seq,
+                                                 const int64_t* __restrict__ pos, int64_t T, int H,
+                                                 const int32_t* __restrict__ idx, int k, int m, KvView comp,
+                                                 KvView win, int window, float sm_scale, RopeTab rt,
+                                                 const float* __restrict__ out, const float* __restrict__ lse,
+                                                 const float* __restrict__ dout, float* __restrict__ dq,
+                                                 float* __restrict__ dcomp, float* __restrict__ dwin) {
+    constexpr int D = 512, DN = 448;
+    using Sm = MqaBwdSmem;
+    __shared__ Sm sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g4 = lane >> 4;
+    // the 4 head groups of a row run on one XCD (workgroups b, b + 8, b + 16, b + 24)
+    const int b = blockIdx.x, HG = H / 16;
+    const int hg = (b >> 3) % HG;
+    const int64_t t = (int64_t)(b / (8 * HG)) * 8 + (b & 7);
+    if (t >= T) return;
+    const int64_t tp = pos[t];
+    const int32_t sq = seq[t];
+    const RowKeys rk = row_keys(tp, idx, k, m, window);
+    const int64_t hrow = t * H + 16 * hg + l16;  // this lane's head (row of q, g, out)
+
+    if (tid < 32) {
+        float c, sn;
+        angle_cs((double)tp, rt.theta[tid], c, sn);
+        sm.cs[2 * tid] = c;
+        sm.cs[2 * tid + 1] = sn;
+    }
+    // ---- D = <g, out> and |g|^2 per head (rotation-free), then the power-of-two scale ----
+    float dsum = 0.f, g2 = 0.f;
+    {
+        const float* gr = dout + hrow * D + 8 * g4;
+        const float* orow = out + hrow * D + 8 * g4;
+#pragma unroll 4
+        for (int st = 0; st < D / 32; ++st) {
+            const v4f a0 = *(const v4f*)(gr + 32 * st), a1 = *(const v4f*)(gr + 32 * st + 4);
+            const v4f o0 = *(const v4f*)(orow + 32 * st), o1 = *(const v4f*)(orow + 32 * st + 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dsum = fmaf(a0[i], o0[i], fmaf(a1[i], o1[i], dsum));
+                g2 = fmaf(a0[i], a0[i], fmaf(a1[i], a1[i], g2));
+            }
+        }
+    }
+    dsum += __shfl_xor(dsum, 16);
+    dsum += __shfl_xor(dsum, 32);
+    g2 += __shfl_xor(g2, 16);
+    g2 += __shfl_xor(g2, 32);
+    float g2max = g2;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) g2max = fmaxf(g2max, __shfl_xor(g2max, o));
+    int ex = 0;
+    if (g2max > 0.f) (void)frexpf(sqrtf(g2max), &ex);  // |g_h| < 2^ex for every head
+    ex = ex < -120 ? -120 : (ex > 120 ? 120 : ex);
+    const float sg = ldexpf(1.f, -ex), inv_sg = ldexpf(1.f, ex);
+    const float dh = dsum * sg;  // D * s_g of head l16
+    const float lse_h = lse[hrow];
+    __syncthreads();  // cs
+
+    // ---- q~ and s_g g~ in fp16: B operands of S / dP in registers, [head][dim] copies in LDS ----
+    v8h qf[D / 32], gf[D / 32];
+    {
+        const uint16_t* qr = q + hrow * D + 8 * g4;
+        const float* gr = dout + hrow * D + 8 * g4;
+#pragma unroll
+        for (int st = 0; st < D / 32; ++st) {
+            const v4i raw = *(const v4i*)(qr + 32 * st);
+            const v4f a0 = *(const v4f*)(gr + 32 * st), a1 = *(const v4f*)(gr + 32 * st + 4);
+            float xq[8], xg[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                xq[2 * i] = __uint_as_float((uint32_t)raw[i] << 16);
+                xq[2 * i + 1] = __uint_as_float((uint32_t)raw[i] & 0xFFFF0000u);
+                xg[i] = a0[i] * sg;
+                xg[4 + i] = a1[i] * sg;
+            }
+            if (32 * st >= DN) {  // RoPE pairs (2p, 2p + 1) of the last 64 dims, at +tp
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int pr = (32 * st + 8 * g4 - DN) / 2 + i;
+                    const float c = sm.cs[2 * pr], sn = sm.cs[2 * pr + 1];
+                    const float q0 = xq[2 * i], q1 = xq[2 * i + 1], a = xg[2 * i], bb = xg[2 * i + 1];
+                    xq[2 * i] = q0 * c - q1 * sn;
+                    xq[2 * i + 1] = q0 * sn + q1 * c;
+                    xg[2 * i] = a * c - bb * sn;
+                    xg[2 * i + 1] = a * sn + bb * c;
+                }
+            }
+            v8h hq, hgv, hqs;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                hq[i] = (_Float16)xq[i];
+                hgv[i] = (_Float16)xg[i];
+                hqs[i] = (_Float16)(xq[i] * sm_scale);
+            }
+            qf[st] = hq;
+            gf[st] = hgv;
+            if ((st >> 2) == wave) {  // each wave writes a quarter of the copies
+                *(v8h*)(sm.qs + l16 * Sm::QS + 32 * st + 8 * g4) = hqs;
+                *(v8h*)(sm.gs + l16 * Sm::QS + 32 * st + 8 * g4) = hgv;
+            }
+        }
+    }
+    __syncthreads();
+
+    // B operands of the entry gradient (k = 4 heads of c q~, 4 heads of s_g g~ per lane group;
+    // columns = dims) stay in registers for the whole row
+    v8h bq[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+        const int d0 = 128 * wave + 16 * dt;
+        const int off = (4 * g4 + (l16 >> 2)) * Sm::QS + 4 * (l16 & 3) + d0;
+        const v4s lo = lds_read_tr16(sm.qs + off), hi = lds_read_tr16(sm.gs + off);
+        const v8u16 c = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
+                         (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
+        bq[dt] = __builtin_bit_cast(v8h, c);
+    }
+
+    v4f accq[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) accq[dt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t n = rk.n;
+    for (int64_t u0 = 0; u0 < n; u0 += kBwdKT) {
+        // ---- resolve the tile's keys (double-buffered: other waves may still read the last tile's) ----
+        const int pb = (int)((u0 / kBwdKT) & 1);
+        int64_t* const krow = sm.krow[pb];
+        float* const kscl = sm.kscl[pb];
+        if (tid < kBwdKT) {
+            const int64_t u = u0 + tid;
+            const int64_t code = u < n ? resolve(u, t, sq, rk, idx, k, comp, win) : -1;
+            krow[tid] = code;
+            kscl[tid] = code == -1 ? -1.f : (code >= 0 ? comp.scale[code] : win.scale[-code - 2]);
+        }
+        lds_barrier();  // (also: every wave is done with the last tile's staged keys and ds)
+        // ---- stage: 64 keys x (28 FP8 chunks + 8 RoPE chunks of 16 bytes), 9 chunks per thread ----
+        {
+            v4i raw[9];
+#pragma unroll
+            for (int i = 0; i < 9; ++i) {
+                const int c = tid + 256 * i, kk = c / 36, part = c % 36;
+                const int64_t code = krow[kk];
+                const uint8_t* src;
+                if (code == -1) src = g_zero_entry;
+                else if (part < 28) src = (code >= 0 ? comp.nope + code * DN : win.nope + (-code - 2) * DN) + 16 * part;
+                else src = (const uint8_t*)(code >= 0 ? comp.rope + code * 64 : win.rope + (-code - 2) * 64) + 16 * (part - 28);
+                raw[i] = gload<v4i>(src);
+            }
+#pragma unroll
+            for (int i = 0; i < 9; ++i) {
+                const int c = tid + 256 * i, kk = c / 36, part = c % 36;
+                _Float16* dst = sm.kt + kk * Sm::KS;
+                if (part < 28) {
+                    v8h lo8, hi8;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)raw[i][w], 1.f, false);
+                        const v2h bb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)raw[i][w], 1.f, true);
+                        if (w < 2) {
+                            lo8[4 * w] = a[0], lo8[4 * w + 1] = a[1], lo8[4 * w + 2] = bb[0], lo8[4 * w + 3] = bb[1];
+                        } else {
+                            hi8[4 * w - 8] = a[0], hi8[4 * w - 7] = a[1], hi8[4 * w - 6] = bb[0], hi8[4 * w - 5] = bb[1];
+                        }
+                    }
+                    *(v8h*)(dst + 16 * part) = lo8;
+                    *(v8h*)(dst + 16 * part + 8) = hi8;
+                } else {
+                    v8h r8;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        r8[2 * w] = (_Float16)__uint_as_float((uint32_t)raw[i][w] << 16);
+                        r8[2 * w + 1] = (_Float16)__uint_as_float((uint32_t)raw[i][w] & 0xFFFF0000u);
+                    }
+                    *(v8h*)(dst + DN + 8 * (part - 28)) = r8;
+                }
+            }
+        }
+        lds_barrier();
+
+        // ---- S and dP for key block `wave` (keys x heads), then p and ds to LDS ----
+        {
+            v4f an = {0.f, 0.f, 0.f, 0.f}, ar = an, gn = an, gr = an;
+            const _Float16* kb = sm.kt + (16 * wave + l16) * Sm::KS + 8 * g4;
+#pragma unroll
+            for (int st = 0; st < D / 32; ++st) {
+                const v8h kv = *(const v8h*)(kb + 32 * st);
+                if (32 * st < DN) {
+                    an = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qf[st], an, 0, 0, 0);
+                    gn = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, gf[st], gn, 0, 0, 0);
+                } else {
+                    ar = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qf[st], ar, 0, 0, 0);
+                    gr = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, gf[st], gr, 0, 0, 0);
+                }
+            }
+            v4h hn, hr, hp;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float sc = kscl[16 * wave + 4 * g4 + i];
+                const bool ok = sc >= 0.f;
+                const float sv = sm_scale * fmaf(sc, an[i], ar[i]);
+                const float p = ok ? __expf(sv - lse_h) : 0.f;
+                const float ds = ok ? p * (fmaf(sc, gn[i], gr[i]) - dh) : 0.f;
+                hn[i] = (_Float16)(ds * sc);
+                hr[i] = (_Float16)ds;
+                hp[i] = (_Float16)p;
+            }
+            const int slot = 32 * (wave >> 1) + 8 * g4 + 4 * (wave & 1);
+            *(v4h*)(sm.dsn + l16 * Sm::PS + slot) = hn;
+            *(v4h*)(sm.dsr + l16 * Sm::PS + slot) = hr;
+            *(v4h*)(sm.pp + l16 * Sm::PS + slot) = hp;
+        }
+        lds_barrier();
+
+        // ---- dq[heads x this wave's dims] += ds K ----
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const v8h an = *(const v8h*)(sm.dsn + l16 * Sm::PS + 32 * h + 8 * g4);
+            const v8h ar = *(const v8h*)(sm.dsr + l16 * Sm::PS + 32 * h + 8 * g4);
+            const _Float16* vb = sm.kt + (32 * h + 4 * g4 + (l16 >> 2)) * Sm::KS + 4 * (l16 & 3);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const int d0 = 128 * wave + 16 * dt;
+                const v4s lo = lds_read_tr16(vb + d0), hi = lds_read_tr16(vb + 16 * Sm::KS + d0);
+                const v8u16 c = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
+                                 (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
+                accq[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(d0 < DN ? an : ar, __builtin_bit_cast(v8h, c),
+                                                                  accq[dt], 0, 0, 0);
+            }
+        }
+
+        // ---- entry gradients [keys x this wave's dims] = [ds | p] [c q~ ; s_g g~], atomically added ----
+#pragma unroll
+        for (int kb = 0; kb < kBwdKT / 16; ++kb) {
+            const int off = (4 * g4 + (l16 >> 2)) * Sm::PS + 4 * (l16 & 3) + 16 * kb;
+            const v4s lo = lds_read_tr16(sm.dsr + off), hi = lds_read_tr16(sm.pp + off);
+            const v8u16 c = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
+                             (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
+            const v8h a = __builtin_bit_cast(v8h, c);
+            float* dst[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t code = krow[bwd_slot_key(16 * kb + 4 * g4 + i)];
+                dst[i] = code == -1 ? nullptr : (code >= 0 ? dcomp + code * D : dwin + (-code - 2) * D);
+            }
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const v4f e = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[dt], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                const int dcol = 128 * wave + 16 * dt + l16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (dst[i]) unsafeAtomicAdd(dst[i] + dcol, e[i] * inv_sg);
+            }
+        }
+    }
+
+    // ---- dq = R(-tp) (c / s_g) acc: lane holds heads 4 g4 + i at dim 128 wave + 16 dt + l16 ----
+    const float fq = sm_scale * inv_sg;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+        const int dim = 128 * wave + 16 * dt + l16;
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = accq[dt][i] * fq;
+        if (128 * wave + 16 * dt >= DN) {  // RoPE dims (wave 3, dt >= 4)
+            const int pr = (dim - DN) >> 1;
+            const float c = sm.cs[2 * pr], sn = sm.cs[2 * pr + 1];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float other = __shfl_xor(v[i], 1);
+                v[i] = (l16 & 1) ? fmaf(-other, sn, v[i] * c) : fmaf(other, sn, v[i] * c);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dq[(t * H + 16 * hg + 4 * g4 + i) * D + dim] = v[i];
+    }
+}
+
+hipError_t launch_mqa_bwd(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int H,
+                          const int32_t* idx, int k, int m, KvView comp, KvView win, int window, float sm_scale,
+                          const RopeTab& rt, const float* out, const float* lse, const float* dout, float* dq,
+                          float* dcomp, float* dwin, hipStream_t st) {
+    if (T == 0) return hipSuccess;
+    const int64_t blocks = (T + 7) / 8 * 8 * (H / 16);
+    hipLaunchKernelGGL(k_mqa_bwd, dim3((unsigned)blocks), dim3(256), 0, st, q, seq, pos, T, H, idx, k, m, comp, win,
+                       window, sm_scale, rt, out, lse, dout, dq, dcomp, dwin);
     return hipGetLastError();
 }
 

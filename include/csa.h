@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CSA_VERSION 101
+#define CSA_VERSION 102
 
 enum {
     CSA_OK = 0,
@@ -277,6 +277,38 @@ int csa_sparse_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos, in
 int hca_dense_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int32_t H, int32_t d,
                   int32_t m, int64_t max_vis, csa_kv_t comp, csa_kv_t win, int32_t window, float sm_scale,
                   float rope_base, float* out, float* lse, void* ws, size_t ws_bytes, csa_stream_t stream);
+
+/*
+ * csa_mqa_bwd — gradient of the attention step (training side: the pages
+ * train with the sparse attention in place, [xmsumi] § 预训练, after an
+ * indexer warm-up; no page gives the gradient, so this is the exact
+ * derivative of csa_sparse_mqa / hca_dense_mqa).  With q~ = q[t][h] roped at
+ * pos[t], g = dout[t][h], g~ = g roped at pos[t] on its last 64 dims, and the
+ * forward's out and lse:
+ *   p_u = exp(sm_scale <q~, e_u> - lse);  ds_u = p_u (<g~, e_u> - <g, out>)
+ *   dq[t][h] = sm_scale * sum_u ds_u e_u, rotated back by RoPE at -pos[t]
+ *   dcomp / dwin row of entry u += sm_scale ds_u q~ + p_u g~
+ * over the same key set U as the forward (idx non-null: the selected entries
+ * as csa_sparse_mqa; idx null: every visible entry as hca_dense_mqa, k ignored),
+ * gradients taken with respect to the dequantised entries (FP8 * scale, BF16).
+ *
+ *   q [T][H][d] bf16, out [T][H][d] fp32, lse [T][H] fp32: the forward's
+ *   inputs and outputs; dout [T][H][d] fp32;  dq [T][H][d] fp32 (written)
+ *   dcomp [comp rows][d], dwin [win rows][d] fp32: indexed by the same cache
+ *            row as the entries (seq * cap + slot, or through the page
+ *            table); ACCUMULATED into (the caller clears them).  dwin may be
+ *            null when window == 0.
+ * H in {16, 32, 64}; d = 512 only; 16-byte aligned q, out, dout, dq.
+ * Entries shared by rows and heads are summed with fp32 atomics, so the
+ * summation order (and the last bits of dcomp / dwin) varies between runs.
+ * The output gradient is scaled by a power of two per (row, 16 heads) inside;
+ * entries with |e|_2 above ~3e4 may overflow the fp16 products.
+ * No workspace.
+ */
+int csa_mqa_bwd(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int32_t H, int32_t d,
+                const int32_t* idx, int32_t k, int32_t m, csa_kv_t comp, csa_kv_t win, int32_t window, float sm_scale,
+                float rope_base, const float* out, const float* lse, const float* dout, float* dq, float* dcomp,
+                float* dwin, csa_stream_t stream);
 
 /* Text of the last error on the calling thread ("" if none). */
 const char* csa_last_error(void);

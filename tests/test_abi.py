@@ -137,6 +137,26 @@ def test_mqa_validation(csa):
     assert rc == csa.CSA_EWORKSPACE
 
 
+def test_mqa_bwd_validation(csa):
+    L = csa._lib
+    p = ctypes.c_void_p(256)
+    kv = csa._Kv(256, 256, 256, 256)
+    args = dict(T=2, H=64, d=512, k=64, m=4, window=128)
+
+    def bwd(**o):
+        a = dict(args, **o)
+        return L.csa_mqa_bwd(p, p, p, a["T"], a["H"], a["d"], a.get("idx", p), a["k"], a["m"], kv, kv, a["window"],
+                             0.04, 10000.0, a.get("out", p), p, p, p, p, a.get("dwin", p), None)
+
+    assert bwd(d=128) == csa.CSA_EUNSUPPORTED and b"d=128" in L.csa_last_error()
+    assert bwd(H=48) == csa.CSA_EUNSUPPORTED
+    assert bwd(k=4096) == csa.CSA_EUNSUPPORTED
+    assert bwd(out=None) == csa.CSA_EINVAL
+    assert bwd(dwin=None) == csa.CSA_EINVAL  # window > 0 needs the window gradient
+    assert bwd(out=ctypes.c_void_p(264)) == csa.CSA_EINVAL and b"aligned" in L.csa_last_error()
+    assert bwd(T=0) == csa.CSA_OK
+
+
 def test_workspace_sizes(csa):
     assert csa.csa_topk_workspace(4, 262144, 1024) >= 0
     # decode shapes split the key list; big batches do not

@@ -694,3 +694,58 @@ def test_paged_cache_matches_contiguous(lib, dev, gen, share, page, wpage):
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.equal(h1, h2) and torch.equal(hl1, hl2)
+
+
+# --------------------------------------------------------------------------
+# attention backward (csa_mqa_bwd) against the fp64 gradient of the oracle
+# --------------------------------------------------------------------------
+def assert_grad_close(got, ref, what):
+    got = np.asarray(got, np.float64)
+    r = rel_rms(got, ref)
+    scale = max(float(np.max(np.abs(ref))), 1e-30)
+    ma = float(np.max(np.abs(got - ref))) / scale
+    print(f"{what}: rel-rms {r:.2e} max-abs/max {ma:.2e}", flush=True)
+    assert r <= REL_RMS and ma <= MAX_ABS, f"{what}: rel-rms {r:.3e} max-abs/max {ma:.3e}"
+
+
+@pytest.mark.parametrize("T,B,L,H,k,W,m,win_cap,sel,same_seq", [
+    (6, 3, 4096, 64, 200, 128, 4, 128, True, False),    # 5 tiles + a ragged one; -1 padding in one row
+    (16, 1, 2048, 32, 96, 64, 4, 96, True, True),       # 16 rows of one sequence: shared entries and window
+    (5, 2, 512, 16, 0, 16, 4, 16, False, False),        # every visible entry (no selection), small window
+    (3, 3, 256, 64, 64, 0, 4, 1, True, False),          # no window branch
+])
+def test_mqa_bwd(lib, dev, gen, orc, T, B, L, H, k, W, m, win_cap, sel, same_seq):
+    import torch
+
+    from oracle import backward as obw
+
+    d = 512
+    _say(f"mqa_bwd T={T} B={B} L={L} H={H} k={k} W={W} m={m} sel={sel}")
+    N = L // m
+    comp, win, q = _attn_inputs(gen, 700 + T, B, N, W, H, d, T, L, win_cap)
+    seq = (np.zeros(T) if same_seq else np.arange(T) % B).astype(np.int32)
+    pos = (L - 1 - np.arange(T) * (3 if same_seq else 37)).astype(np.int64)
+    pos[-1] = min(pos[-1], 70)  # a short row: partial window, fewer visible entries than k
+    nv = (pos + 1) // m
+    idx = gen.random_idx(701 + T, 1, nv, k) if sel else None
+    dout = gen.normal_f32(702 + T, 1, (T, H, d)) * 0.01
+    sm = 1.0 / math.sqrt(d)
+    kvc = dev.kv_cache(comp, N)
+    kvw = dev.kv_cache(win, win_cap) if W > 0 else None
+    tq, tseq, tpos = dev.bf16(q), dev.t(seq), dev.t(pos)
+    tidx = dev.t(idx) if sel else None
+    if sel:
+        out, lse = lib.csa_sparse_mqa(tq, tseq, tpos, tidx, m, kvc, kvw, W, sm)
+    else:
+        out, lse = lib.hca_dense_mqa(tq, tseq, tpos, m, int(nv.max()), kvc, kvw, W, sm)
+    dq, dcomp, dwin = lib.csa_mqa_bwd(tq, tseq, tpos, tidx, m, kvc, kvw, W, sm, out, lse, dev.t(dout))
+    torch.cuda.synchronize()
+    rq, rc, rw = obw.attend_bwd(q, seq, pos, comp, N, win, win_cap, W, m, sm, dout, idx=idx)
+    assert_grad_close(dq.cpu().numpy(), rq, "dq")
+    got_c = dcomp.cpu().numpy()
+    assert np.array_equal(got_c != 0, rc != 0) or np.all(got_c[rc == 0] == 0), "dcomp rows outside the key sets"
+    assert_grad_close(got_c, rc, "dcomp")
+    if W > 0:
+        got_w = dwin.cpu().numpy()
+        assert np.all(got_w[rw == 0] == 0), "dwin rows outside the windows"
+        assert_grad_close(got_w, rw, "dwin")

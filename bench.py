@@ -201,6 +201,66 @@ class PrefillSet:
                           out=self.hout, lse=self.hlse)
 
 
+class PrefillBwdSet(PrefillSet):
+    """Gradient of both attention layers of the chunked-prefill step (training side): the
+    forward runs once in set-up (its indices, out and lse are the backward's inputs), the
+    output gradient is seeded N(0, 0.01^2).  One step clears the entry-gradient buffers and
+    runs csa_mqa_bwd for the CSA layer (selected entries + window) and the HCA layer (every
+    visible entry + window)."""
+
+    def __init__(self, wl):
+        import torch
+
+        super().__init__(wl)
+        self.step_fwd = super().step
+        self.step_fwd(0)
+        T, H, d = wl["T"], wl["H"], wl["d"]
+        g = torch.Generator(device="cuda")
+        g.manual_seed(107)
+        self.dout = torch.randn(T, H, d, generator=g, device="cuda") * 0.01
+        self.douth = torch.randn(T, H, d, generator=g, device="cuda") * 0.01
+        self.dq = torch.empty(T, H, d, dtype=torch.float32, device="cuda")
+        self.dqh = torch.empty_like(self.dq)
+        self.dc = torch.zeros(self.comp.nope.shape[0], d, dtype=torch.float32, device="cuda")
+        self.dw = torch.zeros(self.win.nope.shape[0], d, dtype=torch.float32, device="cuda")
+        self.dch = torch.zeros(self.hca.nope.shape[0], d, dtype=torch.float32, device="cuda")
+        self.dwh = torch.zeros(self.win_h.nope.shape[0], d, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+
+    def bwd(self, layer):
+        import compressed_sparse_long_compress_amd as csa
+
+        wl = self.wl
+        if layer == "csa":
+            self.dc.zero_()
+            self.dw.zero_()
+            csa.csa_mqa_bwd(self.q, self.seq, self.pos, self.idx, wl["m"], self.comp, self.win, wl["W"],
+                            wl["sm_scale"], self.out, self.lse, self.dout, dq=self.dq, dcomp=self.dc, dwin=self.dw)
+        else:
+            self.dch.zero_()
+            self.dwh.zero_()
+            csa.csa_mqa_bwd(self.qh, self.seq, self.pos, None, wl["m_hca"], self.hca, self.win_h, wl["W"],
+                            wl["sm_scale"], self.hout, self.hlse, self.douth, dq=self.dqh, dcomp=self.dch,
+                            dwin=self.dwh)
+
+    def step(self, i):
+        self.bwd("csa")
+        self.bwd("hca")
+
+    def flops(self):
+        """MFMA work of each layer: per (row, head, key) 2d each for S, dP, dq and 4d for the
+        entry gradient (two products), 10 d in all."""
+        import numpy as np
+
+        wl = self.wl
+        pos = np.asarray(wl["pos"], np.int64)
+        win = np.minimum(pos + 1, wl["W"])
+        keys_c = np.minimum(wl["k"], (pos + 1) // wl["m"]) + win
+        keys_h = (pos + 1) // wl["m_hca"] + win
+        per = wl["H"] * 10 * wl["d"]
+        return {"csa": float(keys_c.sum()) * per, "hca": float(keys_h.sum()) * per}
+
+
 class HcaSet:
     """HCA decode at 1M context: 8 sequences, 8,192 entries each (m'=128)."""
 
@@ -387,13 +447,15 @@ def run_workload(name, steps, warmup):
     """Time one named workload; returns (wl, dataset, seconds for `steps` steps)."""
     from gen import configs
 
-    wl = configs.named(name)
+    wl = configs.named("prefill_chunk" if name == "prefill_chunk_bwd" else name)
     if name.startswith("csa_decode"):
         ds = DecodeSet(wl, replicas=8)
     elif name == "compress_chunk":
         ds = CompressSet(wl)
     elif name == "hca_decode_1m":
         ds = HcaSet(wl, replicas=8)
+    elif name == "prefill_chunk_bwd":
+        ds = PrefillBwdSet(wl)
     else:
         ds = PrefillSet(wl)
     sec, _ = time_steps(ds, steps, warmup)
@@ -422,6 +484,7 @@ def main():
     ap.add_argument("--all", action="store_true", help="also time the other workloads (secondary object)")
     ap.add_argument("--workload", default="csa_decode_1m",
                     choices=["csa_decode_1m", "csa_decode_1m_mtp2", "csa_decode_1m_paged", "csa_decode_64k",
+                             "prefill_chunk_bwd",
                              "hca_decode_1m", "prefill_chunk", "compress_chunk"],
                     help="time only this workload and print its line (profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -455,6 +518,26 @@ def main():
                           "ms_per_step": sec / args.steps * 1e3, "steps": args.steps,
                           "per_call_us": {k: v * 1e6 for k, v in calls.items()},
                           "hbm_gbs": {k: by[k] / calls[k] / 1e9 for k in calls}}))
+        return
+    if args.workload == "prefill_chunk_bwd":
+        wl, ds, sec = run_workload(args.workload, args.steps, args.warmup)
+        fl = ds.flops()
+        per = {}
+        for layer in ("csa", "hca"):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                ds.bwd(layer)
+            e1.record()
+            torch.cuda.synchronize()
+            per[layer] = e0.elapsed_time(e1) / args.steps / 1e3
+        tot = sum(fl.values())
+        print(json.dumps({"workload": args.workload, "value": wl["T"] * args.steps / sec, "unit": "tokens/s",
+                          "ms_per_step": sec / args.steps * 1e3, "steps": args.steps, "dtype": "f16 mfma, fp32 atomics",
+                          "per_layer_ms": {k: v * 1e3 for k, v in per.items()},
+                          "tflops": {k: fl[k] / per[k] / 1e12 for k in per},
+                          "mfma": {"achieved": tot / (sec / args.steps) / 1e12, "peak": 2500.0, "unit": "TFLOP/s",
+                                   "frac": tot / (sec / args.steps) / 1e12 / 2500.0}}))
         return
     if args.workload != "csa_decode_1m":
         wl, ds, sec = run_workload(args.workload, args.steps, args.warmup)

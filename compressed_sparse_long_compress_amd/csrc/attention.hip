@@ -1610,60 +1610,63 @@ hipError_t launch_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos,
 // lse and out, D = <g, out>:
 //   p_u = exp(c <q~, e_u> - lse),  ds_u = p_u (<g~, e_u> - D)
 //   dq  = R(-tp) (c sum_u ds_u e_u),  de_u += c ds_u q~ + p_u g~.
-// One workgroup per (query row, group of 16 heads) walks the row's whole key
-// list in tiles of 64 entries: wave w takes key block w of a tile for the scores
-// (S and dP as keys x heads, MFMA 16x16x32 f16), then dims [128 w, 128 w + 128)
-// for dq (accumulated in registers) and for the entry gradients, which leave
-// through fp32 atomics (an entry is shared by many rows and heads).  g is
-// scaled by a power of two per workgroup (|g~ s_g| <= 1 per head) so that it and
-// ds fit fp16 whatever the loss scale; the scale is divided out exactly.
+// One workgroup per query row, one wave per 16 heads, the row's key list in
+// tiles of 16 entries (the next tile's loads in flight during this one):
+//   S, dP    per wave: keys x its heads (MFMA 16x16x32 f16) on the entries as
+//            staged, dequantised to fp16 (the entry scale folded in keeps ds and
+//            the keys clear of fp16's subnormal range)
+//   dq      per wave: its heads x 512 dims += ds K, the ds values straight from
+//            the S layout as the A operand of 16x16x16 MFMAs; kept in registers
+//   de      per wave: the tile's keys x its share of the dims, summed over all
+//            heads in the MFMA ([ds | p] x [c q~ ; g~] from the LDS copies),
+//            then one fp32 atomic per (key, dim): an entry is shared by many
+//            rows, so the summation order varies.
+// g is scaled by a power of two per row (|g~ s_g| <= 1 for every head) so that
+// it and ds fit fp16 whatever the loss scale; the scale is divided out exactly.
 // ---------------------------------------------------------------------------
-constexpr int kBwdKT = 64;  // keys per tile
+constexpr int kBwdKT = 16;   // keys per tile
+constexpr int kBwdRB = 256;  // keys resolved per batch (one per thread of a 4-wave workgroup)
 
+template <int NW>
 struct __align__(16) MqaBwdSmem {
     static constexpr int QS = 512 + 8;  // fp16 row stride of the [head][dim] copies
     static constexpr int KS = 512 + 16;
     static constexpr int PS = kBwdKT + 8;
-    _Float16 qs[16 * QS];      // c * q~, [head][dim]
-    _Float16 gs[16 * QS];      // s_g * g~
-    _Float16 kt[kBwdKT * KS];  // the tile: FP8 dims as decoded (scale apart), RoPE dims
-    _Float16 dsn[16 * PS];     // [head][slot] ds * s_g * entry scale (dq over FP8 dims)
-    _Float16 dsr[16 * PS];     // [head][slot] ds * s_g
-    _Float16 pp[16 * PS];      // [head][slot] p
-    int64_t krow[2][kBwdKT];   // resolved row code per key of tile j in [j & 1] (-1 masked)
-    float kscl[2][kBwdKT];     // entry scale, -1 for a masked key
+    _Float16 qs[16 * NW * QS];   // c * q~, [head][dim]
+    _Float16 gs[16 * NW * QS];   // s_g * g~
+    _Float16 kt[kBwdKT * KS];    // the tile, dequantised: FP8 dims * entry scale, RoPE dims
+    _Float16 dsr[16 * NW * PS];  // [head][key] ds * s_g
+    _Float16 pp[16 * NW * PS];   // [head][key] p
+    int64_t krow[2][kBwdKT];     // resolved row code per key of tile j in [j & 1] (-1 masked)
+    float kscl[2][kBwdKT];       // entry scale, -1 for a masked key
     float cs[64];
-    float red[4][16];
+    float g2w[NW];
 };
 
-// slot of the [head][slot] arrays -> key of the tile: within each half of 32 keys, slot
-// 8 g + 4 e + i holds key 16 e + 4 g + i (the order the MFMA operands read them in)
-__device__ __forceinline__ int bwd_slot_key(int slot) {
-    const int r = slot & 31;
-    return (slot & 32) + 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
-}
-
-__global__ __launch_bounds__(256) void k_mqa_bwd(const uint16_t* __restrict__ q, const int32_t* __restrict__ seq,
-                                                 const int64_t* __restrict__ pos, int64_t T, int H,
-                                                 const int32_t* __restrict__ idx, int k, int m, KvView comp,
-                                                 KvView win, int window, float sm_scale, RopeTab rt,
-                                                 const float* __restrict__ out, const float* __restrict__ lse,
-                                                 const float* __restrict__ dout, float* __restrict__ dq,
-                                                 float* __restrict__ dcomp, float* __restrict__ dwin) {
-    constexpr int D = 512, DN = 448;
-    using Sm = MqaBwdSmem;
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void k_mqa_bwd(const uint16_t* __restrict__ q, const int32_t* __restrict__ seq,
+                                                     const int64_t* __restrict__ pos, const int32_t* __restrict__ idx,
+                                                     int k, int m, KvView comp, KvView win, int window,
+                                                     float sm_scale, RopeTab rt, const float* __restrict__ out,
+                                                     const float* __restrict__ lse, const float* __restrict__ dout,
+                                                     float* __restrict__ dq, float* __restrict__ dcomp,
+                                                     float* __restrict__ dwin) {
+    constexpr int D = 512, DN = 448, NT = 64 * NW, H = 16 * NW;
+    constexpr int DTW = D / NW / 16;                           // 16-dim tiles of de per wave
+    constexpr int NCH = (kBwdKT * 36 + NT - 1) / NT;           // staged 16-byte chunks per thread
+    constexpr int TPB = kBwdRB / kBwdKT;                       // tiles per resolved batch
+    static_assert(NT <= kBwdRB && kBwdRB % NT == 0, "threads resolve whole batches");
+    constexpr int RPT = kBwdRB / NT;                           // keys resolved per thread and batch
+    using Sm = MqaBwdSmem<NW>;
     __shared__ Sm sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
-    // the 4 head groups of a row run on one XCD (workgroups b, b + 8, b + 16, b + 24)
-    const int b = blockIdx.x, HG = H / 16;
-    const int hg = (b >> 3) % HG;
-    const int64_t t = (int64_t)(b / (8 * HG)) * 8 + (b & 7);
-    if (t >= T) return;
+    const int64_t t = blockIdx.x;
     const int64_t tp = pos[t];
     const int32_t sq = seq[t];
     const RowKeys rk = row_keys(tp, idx, k, m, window);
-    const int64_t hrow = t * H + 16 * hg + l16;  // this lane's head (row of q, g, out)
+    const int64_t n = rk.n;
+    const int64_t hrow = t * H + 16 * wave + l16;  // this lane's head (row of q, g, out)
 
     if (tid < 32) {
         float c, sn;
@@ -1671,7 +1674,7 @@ __global__ __launch_bounds__(256) void k_mqa_bwd(const uint16_t* __restrict__ q,
         sm.cs[2 * tid] = c;
         sm.cs[2 * tid + 1] = sn;
     }
-    // ---- D = <g, out> and |g|^2 per head (rotation-free), then the power-of-two scale ----
+    // ---- D = <g, out> and |g|^2 per head (rotation-free), then one power-of-two scale per row ----
     float dsum = 0.f, g2 = 0.f;
     {
         const float* gr = dout + hrow * D + 8 * g4;
@@ -1694,19 +1697,24 @@ __global__ __launch_bounds__(256) void k_mqa_bwd(const uint16_t* __restrict__ q,
     float g2max = g2;
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) g2max = fmaxf(g2max, __shfl_xor(g2max, o));
+    if (lane == 0) sm.g2w[wave] = g2max;
+    __syncthreads();  // cs, g2w
+#pragma unroll
+    for (int w = 0; w < NW; ++w) g2max = fmaxf(g2max, sm.g2w[w]);
     int ex = 0;
-    if (g2max > 0.f) (void)frexpf(sqrtf(g2max), &ex);  // |g_h| < 2^ex for every head
+    if (g2max > 0.f) (void)frexpf(sqrtf(g2max), &ex);  // |g_h| < 2^ex for every head of the row
     ex = ex < -120 ? -120 : (ex > 120 ? 120 : ex);
     const float sg = ldexpf(1.f, -ex), inv_sg = ldexpf(1.f, ex);
     const float dh = dsum * sg;  // D * s_g of head l16
     const float lse_h = lse[hrow];
-    __syncthreads();  // cs
 
     // ---- q~ and s_g g~ in fp16: B operands of S / dP in registers, [head][dim] copies in LDS ----
     v8h qf[D / 32], gf[D / 32];
     {
         const uint16_t* qr = q + hrow * D + 8 * g4;
         const float* gr = dout + hrow * D + 8 * g4;
+        _Float16* qrow = sm.qs + (16 * wave + l16) * Sm::QS + 8 * g4;
+        _Float16* grow = sm.gs + (16 * wave + l16) * Sm::QS + 8 * g4;
 #pragma unroll
         for (int st = 0; st < D / 32; ++st) {
             const v4i raw = *(const v4i*)(qr + 32 * st);
@@ -1740,71 +1748,72 @@ __global__ __launch_bounds__(256) void k_mqa_bwd(const uint16_t* __restrict__ q,
             }
             qf[st] = hq;
             gf[st] = hgv;
-            if ((st >> 2) == wave) {  // each wave writes a quarter of the copies
-                *(v8h*)(sm.qs + l16 * Sm::QS + 32 * st + 8 * g4) = hqs;
-                *(v8h*)(sm.gs + l16 * Sm::QS + 32 * st + 8 * g4) = hgv;
+            *(v8h*)(qrow + 32 * st) = hqs;
+            *(v8h*)(grow + 32 * st) = hgv;
+        }
+    }
+
+    // ---- the key list: resolved a batch of 256 keys ahead (RPT keys per thread, in registers),
+    //      handed to LDS one tile ahead, staged one tile ahead ----
+    int64_t cur_code[RPT], nxt_code[RPT];
+    float cur_scl[RPT], nxt_scl[RPT];
+    auto resolve_batch = [&](int64_t bt, int64_t (&code)[RPT], float (&scl)[RPT]) {
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const int64_t u = bt * kBwdRB + r * NT + tid;
+            code[r] = u < n ? resolve(u, t, sq, rk, idx, k, comp, win) : -1;
+            scl[r] = code[r] == -1 ? -1.f : (code[r] >= 0 ? comp.scale[code[r]] : win.scale[-code[r] - 2]);
+        }
+    };
+    // tile j's keys are keys 16 (j % 16) .. + 15 of batch j / 16: held by threads (and slots r) whose
+    // batch index r NT + tid falls there
+    auto publish = [&](int64_t j) {
+        const int first = (int)(j % TPB) * kBwdKT;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const int bi = r * NT + tid;
+            if (bi >= first && bi < first + kBwdKT) {
+                sm.krow[j & 1][bi - first] = cur_code[r];
+                sm.kscl[j & 1][bi - first] = cur_scl[r];
             }
         }
-    }
-    __syncthreads();
-
-    // B operands of the entry gradient (k = 4 heads of c q~, 4 heads of s_g g~ per lane group;
-    // columns = dims) stay in registers for the whole row
-    v8h bq[8];
+    };
+    v4i raw[NCH];
+    auto issue = [&](int b) {
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-        const int d0 = 128 * wave + 16 * dt;
-        const int off = (4 * g4 + (l16 >> 2)) * Sm::QS + 4 * (l16 & 3) + d0;
-        const v4s lo = lds_read_tr16(sm.qs + off), hi = lds_read_tr16(sm.gs + off);
-        const v8u16 c = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
-                         (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
-        bq[dt] = __builtin_bit_cast(v8h, c);
-    }
-
-    v4f accq[8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) accq[dt] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    const int64_t n = rk.n;
-    for (int64_t u0 = 0; u0 < n; u0 += kBwdKT) {
-        // ---- resolve the tile's keys (double-buffered: other waves may still read the last tile's) ----
-        const int pb = (int)((u0 / kBwdKT) & 1);
-        int64_t* const krow = sm.krow[pb];
-        float* const kscl = sm.kscl[pb];
-        if (tid < kBwdKT) {
-            const int64_t u = u0 + tid;
-            const int64_t code = u < n ? resolve(u, t, sq, rk, idx, k, comp, win) : -1;
-            krow[tid] = code;
-            kscl[tid] = code == -1 ? -1.f : (code >= 0 ? comp.scale[code] : win.scale[-code - 2]);
-        }
-        lds_barrier();  // (also: every wave is done with the last tile's staged keys and ds)
-        // ---- stage: 64 keys x (28 FP8 chunks + 8 RoPE chunks of 16 bytes), 9 chunks per thread ----
-        {
-            v4i raw[9];
-#pragma unroll
-            for (int i = 0; i < 9; ++i) {
-                const int c = tid + 256 * i, kk = c / 36, part = c % 36;
-                const int64_t code = krow[kk];
+        for (int i = 0; i < NCH; ++i) {
+            const int c = tid + NT * i;
+            if (c < kBwdKT * 36) {
+                const int kk = c / 36, part = c % 36;
+                const int64_t code = sm.krow[b][kk];
                 const uint8_t* src;
                 if (code == -1) src = g_zero_entry;
                 else if (part < 28) src = (code >= 0 ? comp.nope + code * DN : win.nope + (-code - 2) * DN) + 16 * part;
                 else src = (const uint8_t*)(code >= 0 ? comp.rope + code * 64 : win.rope + (-code - 2) * 64) + 16 * (part - 28);
                 raw[i] = gload<v4i>(src);
             }
+        }
+    };
+    auto stage = [&](int b) {
 #pragma unroll
-            for (int i = 0; i < 9; ++i) {
-                const int c = tid + 256 * i, kk = c / 36, part = c % 36;
+        for (int i = 0; i < NCH; ++i) {
+            const int c = tid + NT * i;
+            if (c < kBwdKT * 36) {
+                const int kk = c / 36, part = c % 36;
                 _Float16* dst = sm.kt + kk * Sm::KS;
                 if (part < 28) {
+                    const float sc = sm.kscl[b][kk] > 0.f ? sm.kscl[b][kk] : 0.f;
                     v8h lo8, hi8;
 #pragma unroll
                     for (int w = 0; w < 4; ++w) {
                         const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)raw[i][w], 1.f, false);
                         const v2h bb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)raw[i][w], 1.f, true);
+                        const _Float16 x0 = (_Float16)((float)a[0] * sc), x1 = (_Float16)((float)a[1] * sc);
+                        const _Float16 x2 = (_Float16)((float)bb[0] * sc), x3 = (_Float16)((float)bb[1] * sc);
                         if (w < 2) {
-                            lo8[4 * w] = a[0], lo8[4 * w + 1] = a[1], lo8[4 * w + 2] = bb[0], lo8[4 * w + 3] = bb[1];
+                            lo8[4 * w] = x0, lo8[4 * w + 1] = x1, lo8[4 * w + 2] = x2, lo8[4 * w + 3] = x3;
                         } else {
-                            hi8[4 * w - 8] = a[0], hi8[4 * w - 7] = a[1], hi8[4 * w - 6] = bb[0], hi8[4 * w - 5] = bb[1];
+                            hi8[4 * w - 8] = x0, hi8[4 * w - 7] = x1, hi8[4 * w - 6] = x2, hi8[4 * w - 5] = x3;
                         }
                     }
                     *(v8h*)(dst + 16 * part) = lo8;
@@ -1820,93 +1829,114 @@ __global__ __launch_bounds__(256) void k_mqa_bwd(const uint16_t* __restrict__ q,
                 }
             }
         }
-        lds_barrier();
+    };
 
-        // ---- S and dP for key block `wave` (keys x heads), then p and ds to LDS ----
+    v4f accq[D / 16];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) accq[dt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t ntile = (n + kBwdKT - 1) / kBwdKT;
+    if (ntile > 0) {
+        resolve_batch(0, cur_code, cur_scl);
+        resolve_batch(1, nxt_code, nxt_scl);
+        publish(0);
+    }
+    __syncthreads();  // the [head][dim] copies, tile 0's keys
+    if (ntile > 0) issue(0);
+    for (int64_t j = 0; j < ntile; ++j) {
+        const int b = (int)(j & 1);
+        if (j > 0) lds_barrier();  // every wave is done with tile j - 1 (kt, dsr, pp, krow[b ^ 1])
+        stage(b);
+        if (j + 1 < ntile) {
+            if ((j + 1) % TPB == 0) {  // the next tile opens a new batch
+#pragma unroll
+                for (int r = 0; r < RPT; ++r) cur_code[r] = nxt_code[r], cur_scl[r] = nxt_scl[r];
+                resolve_batch((j + 1) / TPB + 1, nxt_code, nxt_scl);
+            }
+            publish(j + 1);
+        }
+        lds_barrier();  // kt and tile j + 1's keys
+        if (j + 1 < ntile) issue(b ^ 1);
+
+        // ---- S and dP: keys x this wave's heads ----
+        v4f sa = {0.f, 0.f, 0.f, 0.f}, ga = sa;
         {
-            v4f an = {0.f, 0.f, 0.f, 0.f}, ar = an, gn = an, gr = an;
-            const _Float16* kb = sm.kt + (16 * wave + l16) * Sm::KS + 8 * g4;
+            const _Float16* kb = sm.kt + l16 * Sm::KS + 8 * g4;
 #pragma unroll
             for (int st = 0; st < D / 32; ++st) {
                 const v8h kv = *(const v8h*)(kb + 32 * st);
-                if (32 * st < DN) {
-                    an = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qf[st], an, 0, 0, 0);
-                    gn = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, gf[st], gn, 0, 0, 0);
-                } else {
-                    ar = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qf[st], ar, 0, 0, 0);
-                    gr = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, gf[st], gr, 0, 0, 0);
-                }
+                sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qf[st], sa, 0, 0, 0);
+                ga = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, gf[st], ga, 0, 0, 0);
             }
-            v4h hn, hr, hp;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float sc = kscl[16 * wave + 4 * g4 + i];
-                const bool ok = sc >= 0.f;
-                const float sv = sm_scale * fmaf(sc, an[i], ar[i]);
-                const float p = ok ? __expf(sv - lse_h) : 0.f;
-                const float ds = ok ? p * (fmaf(sc, gn[i], gr[i]) - dh) : 0.f;
-                hn[i] = (_Float16)(ds * sc);
-                hr[i] = (_Float16)ds;
-                hp[i] = (_Float16)p;
-            }
-            const int slot = 32 * (wave >> 1) + 8 * g4 + 4 * (wave & 1);
-            *(v4h*)(sm.dsn + l16 * Sm::PS + slot) = hn;
-            *(v4h*)(sm.dsr + l16 * Sm::PS + slot) = hr;
-            *(v4h*)(sm.pp + l16 * Sm::PS + slot) = hp;
         }
-        lds_barrier();
+        v4h hr, hp;  // lane: keys 4 g4 + i of head l16
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = sm.kscl[b][4 * g4 + i] >= 0.f;
+            const float p = ok ? __expf(sm_scale * sa[i] - lse_h) : 0.f;
+            const float ds = ok ? p * (ga[i] - dh) : 0.f;
+            hr[i] = (_Float16)ds;
+            hp[i] = (_Float16)p;
+        }
+        *(v4h*)(sm.dsr + (16 * wave + l16) * Sm::PS + 4 * g4) = hr;
+        *(v4h*)(sm.pp + (16 * wave + l16) * Sm::PS + 4 * g4) = hp;
 
-        // ---- dq[heads x this wave's dims] += ds K ----
+        // ---- dq[its heads x 512 dims] += ds K: the S layout is the A operand of 16x16x16 ----
+        {
+            const _Float16* vb = sm.kt + (4 * g4 + (l16 >> 2)) * Sm::KS + 4 * (l16 & 3);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const v8h an = *(const v8h*)(sm.dsn + l16 * Sm::PS + 32 * h + 8 * g4);
-            const v8h ar = *(const v8h*)(sm.dsr + l16 * Sm::PS + 32 * h + 8 * g4);
-            const _Float16* vb = sm.kt + (32 * h + 4 * g4 + (l16 >> 2)) * Sm::KS + 4 * (l16 & 3);
+            for (int dt = 0; dt < D / 16; ++dt) {
+                const v4s kv = lds_read_tr16(vb + 16 * dt);  // keys 4 g4 + i at dim 16 dt + l16
+                accq[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(hr, __builtin_bit_cast(v4h, kv), accq[dt], 0, 0, 0);
+            }
+        }
+        lds_barrier();  // every head's ds and p
+
+        // ---- de[keys x this wave's dims] = sum over heads of [ds | p] x [c q~ ; s_g g~] ----
+        {
+            v8h a[NW];  // k step hb: 4 heads 16 hb + 4 g4 + i of ds, then of p, at key l16
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const int d0 = 128 * wave + 16 * dt;
-                const v4s lo = lds_read_tr16(vb + d0), hi = lds_read_tr16(vb + 16 * Sm::KS + d0);
+            for (int hb = 0; hb < NW; ++hb) {
+                const int off = (16 * hb + 4 * g4 + (l16 >> 2)) * Sm::PS + 4 * (l16 & 3);
+                const v4s lo = lds_read_tr16(sm.dsr + off), hi = lds_read_tr16(sm.pp + off);
                 const v8u16 c = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
                                  (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
-                accq[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(d0 < DN ? an : ar, __builtin_bit_cast(v8h, c),
-                                                                  accq[dt], 0, 0, 0);
+                a[hb] = __builtin_bit_cast(v8h, c);
             }
-        }
-
-        // ---- entry gradients [keys x this wave's dims] = [ds | p] [c q~ ; s_g g~], atomically added ----
-#pragma unroll
-        for (int kb = 0; kb < kBwdKT / 16; ++kb) {
-            const int off = (4 * g4 + (l16 >> 2)) * Sm::PS + 4 * (l16 & 3) + 16 * kb;
-            const v4s lo = lds_read_tr16(sm.dsr + off), hi = lds_read_tr16(sm.pp + off);
-            const v8u16 c = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
-                             (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
-            const v8h a = __builtin_bit_cast(v8h, c);
             float* dst[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int64_t code = krow[bwd_slot_key(16 * kb + 4 * g4 + i)];
+                const int64_t code = sm.krow[b][4 * g4 + i];
                 dst[i] = code == -1 ? nullptr : (code >= 0 ? dcomp + code * D : dwin + (-code - 2) * D);
             }
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const v4f e = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[dt], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                const int dcol = 128 * wave + 16 * dt + l16;
+            for (int dt = 0; dt < DTW; ++dt) {
+                const int d0 = (D / NW) * wave + 16 * dt;
+                v4f e = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int hb = 0; hb < NW; ++hb) {
+                    const int off = (16 * hb + 4 * g4 + (l16 >> 2)) * Sm::QS + 4 * (l16 & 3) + d0;
+                    const v4s lo = lds_read_tr16(sm.qs + off), hi = lds_read_tr16(sm.gs + off);
+                    const v8u16 c = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
+                                     (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
+                    e = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[hb], __builtin_bit_cast(v8h, c), e, 0, 0, 0);
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (dst[i]) unsafeAtomicAdd(dst[i] + dcol, e[i] * inv_sg);
+                    if (dst[i]) unsafeAtomicAdd(dst[i] + d0 + l16, e[i] * inv_sg);
             }
         }
     }
 
-    // ---- dq = R(-tp) (c / s_g) acc: lane holds heads 4 g4 + i at dim 128 wave + 16 dt + l16 ----
+    // ---- dq = R(-tp) (c / s_g) acc: lane holds heads 16 wave + 4 g4 + i at dim 16 dt + l16 ----
     const float fq = sm_scale * inv_sg;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-        const int dim = 128 * wave + 16 * dt + l16;
+    for (int dt = 0; dt < D / 16; ++dt) {
+        const int dim = 16 * dt + l16;
         float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = accq[dt][i] * fq;
-        if (128 * wave + 16 * dt >= DN) {  // RoPE dims (wave 3, dt >= 4)
+        if (16 * dt >= DN) {  // RoPE dims: the pair's other dim is in lane l16 ^ 1
             const int pr = (dim - DN) >> 1;
             const float c = sm.cs[2 * pr], sn = sm.cs[2 * pr + 1];
 #pragma unroll
@@ -1916,7 +1946,7 @@ __global__ __launch_bounds__(256) void k_mqa_bwd(const uint16_t* __restrict__ q,
             }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dq[(t * H + 16 * hg + 4 * g4 + i) * D + dim] = v[i];
+        for (int i = 0; i < 4; ++i) dq[(t * H + 16 * wave + 4 * g4 + i) * D + dim] = v[i];
     }
 }
 
@@ -1925,9 +1955,13 @@ hipError_t launch_mqa_bwd(const uint16_t* q, const int32_t* seq, const int64_t* 
                           const RopeTab& rt, const float* out, const float* lse, const float* dout, float* dq,
                           float* dcomp, float* dwin, hipStream_t st) {
     if (T == 0) return hipSuccess;
-    const int64_t blocks = (T + 7) / 8 * 8 * (H / 16);
-    hipLaunchKernelGGL(k_mqa_bwd, dim3((unsigned)blocks), dim3(256), 0, st, q, seq, pos, T, H, idx, k, m, comp, win,
-                       window, sm_scale, rt, out, lse, dout, dq, dcomp, dwin);
+#define CSA_BWD(NW)                                                                                                    \
+    hipLaunchKernelGGL(k_mqa_bwd<NW>, dim3((unsigned)T), dim3(64 * (NW)), 0, st, q, seq, pos, idx, k, m, comp, win,  \
+                       window, sm_scale, rt, out, lse, dout, dq, dcomp, dwin)
+    if (H == 64) CSA_BWD(4);
+    else if (H == 32) CSA_BWD(2);
+    else CSA_BWD(1);
+#undef CSA_BWD
     return hipGetLastError();
 }
 

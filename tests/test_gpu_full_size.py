@@ -153,3 +153,38 @@ def test_prefill_chunk_sampled(lib, orc):
     ref_o, ref_l = orc.attend(sub(wl["q_hca"]), sub(wl["seq"]), sub(wl["pos"]), o_hca, wl["hca_cap"], o_winh, wcap, W,
                               mh, wl["sm_scale"], wl["rope_base"])
     _close(hout.cpu().numpy()[rows], hlse.cpu().numpy()[rows], ref_o, ref_l, "prefill dense")
+
+    # ---- gradient of the sparse layer at full size: dq on the sampled rows against the oracle;
+    #      the entry gradients through properties that hold at any size ----
+    import gen as gen_mod
+    from oracle import backward as obw
+
+    _say("prefill_chunk backward")
+    H = wl["H"]
+    dout = gen_mod.normal_f32(108, 1, (T, H, d), sigma=0.01)
+    dq, dcomp, dwin = lib.csa_mqa_bwd(dev.bf16(wl["q"]), seq, pos, idx, m, comp, win, W, wl["sm_scale"], out, lse,
+                                      dev.t(dout))
+    torch.cuda.synchronize()
+    rq, _, _ = obw.attend_bwd(sub(wl["q"]), sub(wl["seq"]), sub(wl["pos"]), o_comp, wl["comp_cap"], o_win, wcap, W,
+                              m, wl["sm_scale"], sub(dout), rope_base=wl["rope_base"], idx=ref_i)
+    r = float(np.linalg.norm(dq.cpu().numpy()[rows] - rq) / np.linalg.norm(rq))
+    print(f"prefill backward dq (48 rows): rel-rms {r:.2e}", flush=True)
+    assert r <= 2e-3
+    # entries no row selected get no gradient
+    picked = np.zeros(wl["comp_cap"], bool)
+    iv = idx.cpu().numpy()
+    picked[iv[iv >= 0]] = True
+    dc = dcomp.cpu().numpy()
+    assert np.all(dc[~picked] == 0), "gradient on entries no row selected"
+    # shifting every key by c moves every output by R(-t) c: the entry gradients of the whole
+    # batch sum to the output gradients rotated by RoPE at each row's position
+    want = np.zeros(d)
+    p64 = np.asarray(wl["pos"], np.int64)
+    for t in range(T):
+        g = dout[t].astype(np.float64).sum(axis=0)
+        g[d - 64:] = obw.rope_rows(g[d - 64:], int(p64[t]), wl["rope_base"])
+        want += g
+    got = dcomp.double().sum(dim=0).cpu().numpy() + dwin.double().sum(dim=0).cpu().numpy()
+    r = float(np.linalg.norm(got - want) / np.linalg.norm(want))
+    print(f"prefill backward: sum of entry gradients rel-rms {r:.2e}", flush=True)
+    assert r <= 2e-3

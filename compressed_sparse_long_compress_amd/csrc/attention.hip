@@ -1637,8 +1637,8 @@ struct __align__(16) MqaBwdSmem {
     _Float16 kt[kBwdKT * KS];    // the tile, dequantised: FP8 dims * entry scale, RoPE dims
     _Float16 dsr[16 * NW * PS];  // [head][key] ds * s_g
     _Float16 pp[16 * NW * PS];   // [head][key] p
-    int64_t krow[2][kBwdKT];     // resolved row code per key of tile j in [j & 1] (-1 masked)
-    float kscl[2][kBwdKT];       // entry scale, -1 for a masked key
+    int64_t krow[3][kBwdKT];     // resolved row code per key of tile j in [j % 3] (-1 masked)
+    float kscl[3][kBwdKT];       // entry scale, -1 for a masked key
     float cs[64];
     float g2w[NW];
 };
@@ -1773,25 +1773,26 @@ __global__ __launch_bounds__(64 * NW) void k_mqa_bwd(const uint16_t* __restrict_
         for (int r = 0; r < RPT; ++r) {
             const int bi = r * NT + tid;
             if (bi >= first && bi < first + kBwdKT) {
-                sm.krow[j & 1][bi - first] = cur_code[r];
-                sm.kscl[j & 1][bi - first] = cur_scl[r];
+                sm.krow[j % 3][bi - first] = cur_code[r];
+                sm.kscl[j % 3][bi - first] = cur_scl[r];
             }
         }
     };
+    // Every thread issues NCH loads and every lane of the tile loop one atomic per (key, dim), masked
+    // or not: with a fixed count of memory operations in flight, the wait for a tile's loads can
+    // leave the previous tile's atomics in flight (a variable count makes the compiler wait for all).
     v4i raw[NCH];
     auto issue = [&](int b) {
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
-            const int c = tid + NT * i;
-            if (c < kBwdKT * 36) {
-                const int kk = c / 36, part = c % 36;
-                const int64_t code = sm.krow[b][kk];
-                const uint8_t* src;
-                if (code == -1) src = g_zero_entry;
-                else if (part < 28) src = (code >= 0 ? comp.nope + code * DN : win.nope + (-code - 2) * DN) + 16 * part;
-                else src = (const uint8_t*)(code >= 0 ? comp.rope + code * 64 : win.rope + (-code - 2) * 64) + 16 * (part - 28);
-                raw[i] = gload<v4i>(src);
-            }
+            const int c = (tid + NT * i) % (kBwdKT * 36);  // (the overhang re-reads a chunk; not staged)
+            const int kk = c / 36, part = c % 36;
+            const int64_t code = sm.krow[b][kk];
+            const uint8_t* src;
+            if (code == -1) src = g_zero_entry;
+            else if (part < 28) src = (code >= 0 ? comp.nope + code * DN : win.nope + (-code - 2) * DN) + 16 * part;
+            else src = (const uint8_t*)(code >= 0 ? comp.rope + code * 64 : win.rope + (-code - 2) * 64) + 16 * (part - 28);
+            raw[i] = gload<v4i>(src);
         }
     };
     auto stage = [&](int b) {
@@ -1835,28 +1836,35 @@ __global__ __launch_bounds__(64 * NW) void k_mqa_bwd(const uint16_t* __restrict_
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) accq[dt] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    // Tile j: its keys published (LDS ring slot j % 3) at the end of tile j - 2, its loads issued
+    // at the start of tile j - 1 and staged at that tile's end, after its atomics: loads, then
+    // atomics, then the wait for the loads, on one path, so the wait leaves the atomics in flight.
+    // Past the last tile the keys resolve to masked ones: the extra tile's loads read the zero
+    // entry and its staging is never read.
     const int64_t ntile = (n + kBwdKT - 1) / kBwdKT;
+    auto next_keys = [&](int64_t jn) {  // publish tile jn's keys (batch switch on its first tile)
+        if (jn % TPB == 0 && jn > 0) {
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) cur_code[r] = nxt_code[r], cur_scl[r] = nxt_scl[r];
+            resolve_batch(jn / TPB + 1, nxt_code, nxt_scl);
+        }
+        publish(jn);
+    };
     if (ntile > 0) {
         resolve_batch(0, cur_code, cur_scl);
         resolve_batch(1, nxt_code, nxt_scl);
         publish(0);
+        publish(1);
     }
-    __syncthreads();  // the [head][dim] copies, tile 0's keys
-    if (ntile > 0) issue(0);
+    __syncthreads();  // the [head][dim] copies, the keys of tiles 0 and 1
+    if (ntile > 0) {
+        issue(0);
+        stage(0);
+    }
     for (int64_t j = 0; j < ntile; ++j) {
-        const int b = (int)(j & 1);
-        if (j > 0) lds_barrier();  // every wave is done with tile j - 1 (kt, dsr, pp, krow[b ^ 1])
-        stage(b);
-        if (j + 1 < ntile) {
-            if ((j + 1) % TPB == 0) {  // the next tile opens a new batch
-#pragma unroll
-                for (int r = 0; r < RPT; ++r) cur_code[r] = nxt_code[r], cur_scl[r] = nxt_scl[r];
-                resolve_batch((j + 1) / TPB + 1, nxt_code, nxt_scl);
-            }
-            publish(j + 1);
-        }
-        lds_barrier();  // kt and tile j + 1's keys
-        if (j + 1 < ntile) issue(b ^ 1);
+        const int b = (int)(j % 3);
+        lds_barrier();  // tile j staged by every thread, tile j + 1's keys published
+        issue((b + 1) % 3);
 
         // ---- S and dP: keys x this wave's heads ----
         v4f sa = {0.f, 0.f, 0.f, 0.f}, ga = sa;
@@ -1893,7 +1901,8 @@ __global__ __launch_bounds__(64 * NW) void k_mqa_bwd(const uint16_t* __restrict_
         lds_barrier();  // every head's ds and p
 
         // ---- de[keys x this wave's dims] = sum over heads of [ds | p] x [c q~ ; s_g g~] ----
-        {
+        auto de_phase = [&](auto last_t) {
+            constexpr bool last = decltype(last_t)::value;
             v8h a[NW];  // k step hb: 4 heads 16 hb + 4 g4 + i of ds, then of p, at key l16
 #pragma unroll
             for (int hb = 0; hb < NW; ++hb) {
@@ -1903,12 +1912,21 @@ __global__ __launch_bounds__(64 * NW) void k_mqa_bwd(const uint16_t* __restrict_
                                  (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
                 a[hb] = __builtin_bit_cast(v8h, c);
             }
+            // A masked key adds zero to the row of a valid key of the same lane (else row 0), so
+            // every lane issues its atomics without sending many rows' zeros to one hot row; the
+            // last tile (ragged; no wait follows it) skips them instead.
             float* dst[4];
+            float mul[4];
+            float* alt = dcomp;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 3; i >= 0; --i) {
                 const int64_t code = sm.krow[b][4 * g4 + i];
                 dst[i] = code == -1 ? nullptr : (code >= 0 ? dcomp + code * D : dwin + (-code - 2) * D);
+                mul[i] = code == -1 ? 0.f : inv_sg;
+                if (dst[i]) alt = dst[i];
             }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[i] = dst[i] ? dst[i] : alt;
 #pragma unroll
             for (int dt = 0; dt < DTW; ++dt) {
                 const int d0 = (D / NW) * wave + 16 * dt;
@@ -1921,10 +1939,24 @@ __global__ __launch_bounds__(64 * NW) void k_mqa_bwd(const uint16_t* __restrict_
                                      (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
                     e = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[hb], __builtin_bit_cast(v8h, c), e, 0, 0, 0);
                 }
+                if constexpr (!last) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (dst[i]) unsafeAtomicAdd(dst[i] + d0 + l16, e[i] * inv_sg);
+                    for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst[i] + d0 + l16, e[i] * mul[i]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (mul[i] != 0.f) unsafeAtomicAdd(dst[i] + d0 + l16, e[i] * mul[i]);
+                }
             }
+        };
+        // the path into the next tile's staging runs straight from this tile's loads through its
+        // atomics (the wait then leaves them in flight); the last tile needs no staging
+        if (j + 1 < ntile) {
+            de_phase(std::false_type{});
+            stage((b + 1) % 3);  // tile j + 1 (every wave is past this tile's reads of kt)
+            next_keys(j + 2);     // slot (j + 2) % 3 held tile j - 1, which every wave finished before this tile
+        } else {
+            de_phase(std::true_type{});
         }
     }
 

@@ -629,25 +629,20 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_pick(const float* __restr
     // slice records and the first 128 candidates of each slice are requested together
     // (wave w: slices w and w + NW; S <= 2 NW, kSliceCap >= 128)
     uint64_t pre[2][2];
-    uint32_t rn[2];
+    TcRec rr[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int s = wave + i * NW;
-        rn[i] = 0;
+        rr[i] = TcRec{0, 0, 0, 0};
         pre[i][0] = pre[i][1] = 0;
         if (s < S) {
             const uint64_t* src = cands + ((int64_t)t * S + s) * cap;
-            const TcRec r = recs[t * S + s];
+            rr[i] = recs[t * S + s];
             pre[i][0] = src[lane];
             pre[i][1] = src[64 + lane];
-            rn[i] = r.n;
-            if (lane == 0) scnt[s] = r.n;
-            if (s == 0 && lane == 0) {
-                lctr[2] = r.tau;
-                lctr[3] = r.hi;
-            }
         }
     }
+    // the LDS set-up runs while those loads are in flight
     const int nwords = (nv + 31) / 32;
     const bool use_bm = nwords <= kBitmapWords;  // kBitmapWords is a multiple of NT
     // bitmap word w belongs to thread w / perw and sits at (w % perw) * NT + w / perw
@@ -656,6 +651,17 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_pick(const float* __restr
         for (int i = tid; i < perw * NT; i += NT) bm[i] = 0;
     for (int i = tid; i < 4096; i += NT) h[i] = 0;
     if (tid < 2) lctr[tid] = 0;
+    uint32_t rn[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int s = wave + i * NW;
+        rn[i] = rr[i].n;
+        if (s < S && lane == 0) scnt[s] = rn[i];
+        if (s == 0 && lane == 0) {
+            lctr[2] = rr[i].tau;
+            lctr[3] = rr[i].hi;
+        }
+    }
     __syncthreads();
     // offsets of the slices: one wave-wide scan of the counts (S <= 64)
     const uint32_t sn = lane < S ? scnt[lane] : 0u;

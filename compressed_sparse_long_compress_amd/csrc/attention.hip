@@ -1676,12 +1676,15 @@ __global__ __launch_bounds__(64 * NW) void k_mqa_bwd(const uint16_t* __restrict_
     }
     // ---- D = <g, out> and |g|^2 per head (rotation-free), then one power-of-two scale per row ----
     float dsum = 0.f, g2 = 0.f;
+    v4f gk[D / 16];  // this lane's 128 elements of g, read once
     {
         const float* gr = dout + hrow * D + 8 * g4;
         const float* orow = out + hrow * D + 8 * g4;
-#pragma unroll 4
+#pragma unroll
         for (int st = 0; st < D / 32; ++st) {
-            const v4f a0 = *(const v4f*)(gr + 32 * st), a1 = *(const v4f*)(gr + 32 * st + 4);
+            gk[2 * st] = *(const v4f*)(gr + 32 * st);
+            gk[2 * st + 1] = *(const v4f*)(gr + 32 * st + 4);
+            const v4f a0 = gk[2 * st], a1 = gk[2 * st + 1];
             const v4f o0 = *(const v4f*)(orow + 32 * st), o1 = *(const v4f*)(orow + 32 * st + 4);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1712,13 +1715,12 @@ __global__ __launch_bounds__(64 * NW) void k_mqa_bwd(const uint16_t* __restrict_
     v8h qf[D / 32], gf[D / 32];
     {
         const uint16_t* qr = q + hrow * D + 8 * g4;
-        const float* gr = dout + hrow * D + 8 * g4;
         _Float16* qrow = sm.qs + (16 * wave + l16) * Sm::QS + 8 * g4;
         _Float16* grow = sm.gs + (16 * wave + l16) * Sm::QS + 8 * g4;
 #pragma unroll
         for (int st = 0; st < D / 32; ++st) {
             const v4i raw = *(const v4i*)(qr + 32 * st);
-            const v4f a0 = *(const v4f*)(gr + 32 * st), a1 = *(const v4f*)(gr + 32 * st + 4);
+            const v4f a0 = gk[2 * st], a1 = gk[2 * st + 1];
             float xq[8], xg[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {

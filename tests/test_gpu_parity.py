@@ -694,6 +694,29 @@ def test_paged_cache_matches_contiguous(lib, dev, gen, share, page, wpage):
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.equal(h1, h2) and torch.equal(hl1, hl2)
+    # the gradient through both layouts: dq identical; entry gradients land in the physical rows
+    # (a shared page sums its sequences' gradients), equal up to the atomics' summation order
+    dout = dev.t(gen.normal_f32(798, 4, (T, H, d), sigma=0.01))
+    for sel in (True, False):
+        if sel:
+            fa = (o1, l1, contig, wc, dev.t(idx))
+            fb = (o2, l2, paged, wp, dev.t(idx))
+        else:
+            fa = (h1, hl1, contig, wc, None)
+            fb = (h2, hl2, paged, wp, None)
+        g1 = lib.csa_mqa_bwd(dev.bf16(q), args["seq"], args["pos"], fa[4], m, fa[2], fa[3], W, args["sm_scale"],
+                             fa[0], fa[1], dout)
+        g2 = lib.csa_mqa_bwd(dev.bf16(q), args["seq"], args["pos"], fb[4], m, fb[2], fb[3], W, args["sm_scale"],
+                             fb[0], fb[1], dout)
+        torch.cuda.synchronize()
+        assert torch.equal(g1[0], g2[0]), "dq differs between layouts"
+        for got, ref, ca, cb in ((g2[1], g1[1], contig, paged), (g2[2], g1[2], wc, wp)):
+            want = torch.zeros_like(got)
+            for b in range(B):
+                want.index_add_(0, torch.tensor(_slot_rows(cb, b, cb.cap), device="cuda", dtype=torch.int64),
+                                ref[torch.tensor(_slot_rows(ca, b, ca.cap), device="cuda")])
+            r = rel_rms(got.cpu().numpy(), want.cpu().numpy())
+            assert r <= 1e-5, f"paged entry gradients differ (rel-rms {r:.2e}, selection {sel})"
 
 
 # --------------------------------------------------------------------------
@@ -749,26 +772,3 @@ def test_mqa_bwd(lib, dev, gen, orc, T, B, L, H, k, W, m, win_cap, sel, same_seq
         got_w = dwin.cpu().numpy()
         assert np.all(got_w[rw == 0] == 0), "dwin rows outside the windows"
         assert_grad_close(got_w, rw, "dwin")
-    # the gradient through both layouts: dq identical; entry gradients land in the physical rows
-    # (a shared page sums its sequences' gradients), equal up to the atomics' summation order
-    dout = dev.t(gen.normal_f32(798, 4, (T, H, d), sigma=0.01))
-    for sel in (True, False):
-        if sel:
-            fa = (o1, l1, contig, wc, dev.t(idx))
-            fb = (o2, l2, paged, wp, dev.t(idx))
-        else:
-            fa = (h1, hl1, contig, wc, None)
-            fb = (h2, hl2, paged, wp, None)
-        g1 = lib.csa_mqa_bwd(dev.bf16(q), args["seq"], args["pos"], fa[4], m, fa[2], fa[3], W, args["sm_scale"],
-                             fa[0], fa[1], dout)
-        g2 = lib.csa_mqa_bwd(dev.bf16(q), args["seq"], args["pos"], fb[4], m, fb[2], fb[3], W, args["sm_scale"],
-                             fb[0], fb[1], dout)
-        torch.cuda.synchronize()
-        assert torch.equal(g1[0], g2[0]), "dq differs between layouts"
-        for got, ref, ca, cb in ((g2[1], g1[1], contig, paged), (g2[2], g1[2], wc, wp)):
-            want = torch.zeros_like(got)
-            for b in range(B):
-                want.index_add_(0, torch.tensor(_slot_rows(cb, b, cb.cap), device="cuda", dtype=torch.int64),
-                                ref[torch.tensor(_slot_rows(ca, b, ca.cap), device="cuda")])
-            r = rel_rms(got.cpu().numpy(), want.cpu().numpy())
-            assert r <= 1e-5, f"paged entry gradients differ (rel-rms {r:.2e}, selection {sel})"

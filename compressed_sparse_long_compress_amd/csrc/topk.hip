@@ -373,6 +373,10 @@ __device__ __forceinline__ int tm_find2(const uint32_t* hist, int need, int* wsu
 // above the window and `inbin` keys inside it.  Each level histograms the
 // current window into 4096 bins and keeps the bin of the need-th largest,
 // until that bin holds at most `stop` keys or a single key value (sh == 0).
+// A level's window never reaches past the bin the previous level kept: when
+// the shift drops from s < 12 to 0, 4096 unit bins would cover more than that
+// 2^s-wide bin, and keys above it (already counted in `above`) would be
+// counted a second time.
 // Requires lo <= the need-th largest key and every key <= hi; keys below lo
 // are ignored.  h: 4096 LDS words, zero on entry (and visible to all
 // threads); on return it holds the last level's counts, and the caller
@@ -386,8 +390,10 @@ __device__ void hist_descend(ForEach for_each, uint32_t lo, uint32_t hi, int nee
     while ((span >> s) >= 4096) ++s;
     uint32_t b0 = lo;
     int ab_tot = 0;
+    uint64_t ptop = (uint64_t)lo + ((uint64_t)4096 << s);  // end of the bin kept by the previous level
     for (;;) {
-        const uint64_t top = (uint64_t)b0 + ((uint64_t)4096 << s);
+        uint64_t top = (uint64_t)b0 + ((uint64_t)4096 << s);
+        if (top > ptop) top = ptop;
         const uint32_t wb = b0;
         const int ws = s;
         for_each([&](uint32_t key) {
@@ -399,6 +405,7 @@ __device__ void hist_descend(ForEach for_each, uint32_t lo, uint32_t hi, int nee
         const int nb = (int)h[tm_pos<4096, NT>(b)];
         ab_tot += ab;
         b0 += b << s;
+        ptop = (uint64_t)b0 + ((uint64_t)1 << s);
         if (nb <= stop || s == 0) {
             base = b0;
             sh = s;

@@ -339,15 +339,22 @@ static double mx_elem(const uint8_t* data, const uint8_t* scl, int64_t row, int 
 void orc_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
                       const int64_t* pos, int64_t T, int32_t h_i, int32_t d_i, const uint8_t* kdata,
                       const uint8_t* kscale, int64_t cap, int32_t m, int64_t n_cols, double* scores) {
+    /* work items are (row, chunk of columns), so a few long rows still spread over
+       every core; each score is computed by the same expression either way */
+    const int64_t chunk = 4096;
+    const int64_t n_chunks = (n_cols + chunk - 1) / chunk;
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t t = 0; t < T; ++t) {
+    for (int64_t u = 0; u < T * n_chunks; ++u) {
+        const int64_t t = u / n_chunks;
+        const int64_t j0 = (u % n_chunks) * chunk;
+        const int64_t j1 = j0 + chunk < n_cols ? j0 + chunk : n_cols;
         double* qd = (double*)malloc(sizeof(double) * (size_t)h_i * d_i);
         for (int h = 0; h < h_i; ++h)
             for (int c = 0; c < d_i; ++c) qd[h * d_i + c] = mx_elem(q, q_scale, t * h_i + h, d_i, c);
         double* kd = (double*)malloc(sizeof(double) * (size_t)d_i);
         int64_t nv = n_visible(pos[t], m);
         int64_t base = (int64_t)seq[t] * cap;
-        for (int64_t j = 0; j < n_cols; ++j) {
+        for (int64_t j = j0; j < j1; ++j) {
             if (j >= nv) { scores[t * n_cols + j] = -INFINITY; continue; }
             for (int c = 0; c < d_i; ++c) kd[c] = mx_elem(kdata, kscale, base + j, d_i, c);
             double acc = 0.0;

@@ -1,7 +1,7 @@
 """GPU parity at the full sizes of the named workloads, in the launch
 configuration bench.py times.  Indices and scores are compared in full; the
 oracle computes attention for every row of the decode batches and for a seeded
-sample of rows of the prefill chunk."""
+sample of rows of the prefill chunk, whose top-k is checked on every row."""
 import math
 import sys
 
@@ -146,7 +146,14 @@ def test_prefill_chunk_sampled(lib, orc):
     got_s = scores.cpu().numpy()[rows]
     assert np.array_equal(got_s.view(np.uint32), ref_s.view(np.uint32)), "scores differ"
     ref_i = orc.topk(ref_s, sub(wl["pos"]), m, k)
-    assert np.array_equal(idx.cpu().numpy()[rows], ref_i), "top-k differs"
+    got_idx = idx.cpu().numpy()
+    assert np.array_equal(got_idx[rows], ref_i), "top-k differs"
+    # every row's selection: the oracle's sort of the GPU's score matrix (bit-exact on the rows
+    # checked above) against the GPU's indices, on all 8,192 rows
+    all_i = orc.topk(scores.cpu().numpy(), wl["pos"], m, k)
+    bad = np.where((all_i != got_idx).any(axis=1))[0]
+    assert bad.size == 0, f"top-k differs on {bad.size} rows, first {bad[:5].tolist()}"
+    del all_i
     ref_o, ref_l = orc.attend(sub(wl["q"]), sub(wl["seq"]), sub(wl["pos"]), o_comp, wl["comp_cap"], o_win, wcap, W, m,
                               wl["sm_scale"], wl["rope_base"], idx=ref_i)
     _close(out.cpu().numpy()[rows], lse.cpu().numpy()[rows], ref_o, ref_l, "prefill sparse")

@@ -193,6 +193,8 @@ def _index_case(gen, seed, T, h_i, d_i, N, B, pos, seq, plant=0.0):
     (3, 4, 64, 700, 2, 4, 650, "decode"),
     (2048, 4, 64, 512, 1, 4, 512, "prefill"),       # small prefill
     (200, 8, 128, 3000, 1, 4, 3000, "prefill"),     # ragged rows and columns
+    (300, 8, 64, 2000, 1, 4, 1999, "prefill"),      # d_i = 64 with 8 heads
+    (150, 4, 128, 1500, 1, 4, 1500, "prefill"),     # d_i = 128 with 4 heads
     (130, 8, 128, 900, 3, 4, 900, "mixed"),          # several sequences inside one tile
     (96, 4, 128, 400, 2, 2, 400, "mixed"),
 ])
@@ -291,6 +293,29 @@ def test_index_scores_grouped_summary_topk(lib, dev, gen, orc):
 # ---------------------------------------------------------------------------
 # csa_topk
 # ---------------------------------------------------------------------------
+def _cluster_scores(rng, T, n, k):
+    """Rows whose k-th largest score lies in a dense cluster: a set of equal scores (X = 10.0,
+    often more of them than a histogram descent stops at or ranks directly) and distinct
+    scores 8 .. 3005 ulps above X, over a background below 7; some rows also hold a few
+    scores in [20, 40), which widen the key span so the descent takes several levels.  Odd
+    rows put the k-th largest among the equal scores, even rows among the distinct ones."""
+    s = np.abs(rng.standard_normal((T, n))).astype(np.float32)
+    x = np.float32(10.0).view(np.uint32)
+    for t in range(T):
+        n_hi = 0 if t % 3 == 0 else int(rng.integers(1, k // 4 + 1))
+        c1 = int(rng.integers(65, 600))
+        if t % 2:
+            c2 = int(rng.integers(max(1, k - n_hi - c1), k - n_hi))
+        else:
+            c2 = int(rng.integers(k - n_hi, k - n_hi + min(2000, n // 4)))
+        cols = rng.choice(n, size=min(n, n_hi + c1 + c2), replace=False)
+        a, b = n_hi, n_hi + c1
+        s[t, cols[:a]] = rng.uniform(20, 40, a).astype(np.float32)
+        s[t, cols[a:b]] = x.view(np.float32)
+        s[t, cols[b:]] = (x + rng.integers(8, 3006, len(cols) - b).astype(np.uint32)).view(np.float32)
+    return s
+
+
 @pytest.mark.parametrize("T,n_cols,k,m,kind", [
     (64, 512, 64, 4, "normal"),
     (16, 40000, 1024, 4, "normal"),     # longer than the LDS cache
@@ -316,13 +341,32 @@ def test_index_scores_grouped_summary_topk(lib, dev, gen, orc):
     (6, 300000, 1024, 4, "short"),
     (3, 70000, 1, 4, "normal"),
     (2, 1048576, 2048, 4, "normal"),    # summary longer than one pass of registers
+    # many rows longer than 65,536 columns (one workgroup per row, radix select; rows of at most
+    # 36,608 visible columns are cached in LDS)
+    (160, 70000, 1024, 4, "normal"),
+    (160, 70000, 1024, 4, "ties"),
+    (160, 70000, 1024, 4, "short"),
+    (128, 70001, 2048, 4, "signed"),
+    # dense clusters of near-equal keys (a tie cluster larger than the descents' stop counts, and
+    # distinct keys a few thousand order-key units above it) on every selection path
+    (130, 20000, 1050, 4, "cluster"),   # registers
+    (130, 36864, 2048, 4, "cluster"),
+    (130, 3000, 700, 4, "cluster"),
+    (130, 50000, 1050, 4, "cluster"),   # streamed
+    (160, 70000, 1050, 4, "cluster"),   # radix select
+    (4, 200000, 1050, 4, "cluster"),    # row summary
+    (8, 100000, 1024, 4, "cluster"),
+    (3, 70000, 2048, 4, "cluster"),
+    (64, 262144, 1024, 4, "cluster"),
 ])
 def test_topk_bit_exact(lib, dev, orc, T, n_cols, k, m, kind):
     import torch
 
     _say(f"topk T={T} n_cols={n_cols} k={k} m={m} {kind}")
     rng = np.random.default_rng(n_cols + k)
-    if kind == "ties":
+    if kind == "cluster":
+        scores = _cluster_scores(rng, T, n_cols, k)
+    elif kind == "ties":
         scores = rng.integers(0, 50, size=(T, n_cols)).astype(np.float32)
     elif kind == "allequal":
         scores = np.zeros((T, n_cols), np.float32)
@@ -402,7 +446,11 @@ def _attn_inputs(gen, seed, B, N, W, H, d, T, L, win_cap):
     (3, 2, 600, 32, 512, 256, 128, 4, 128),        # fewer visible than k (-1 padding)
     (6, 3, 2048, 16, 128, 64, 128, 4, 200),
     (2, 2, 64, 64, 512, 64, 0, 4, 1),              # no window branch
-    (64, 4, 8192, 64, 512, 1024, 128, 4, 128),     # 8 splits of 144 keys: the two-role 64-head kernel
+    (64, 4, 8192, 64, 512, 1024, 128, 4, 128),     # 4 splits of 288 keys
+    (128, 4, 8192, 64, 512, 1024, 128, 4, 128),    # 2 splits of 576 keys: the two-role 64-head kernel
+    (4, 4, 8192, 64, 128, 1024, 128, 4, 128),      # 64 heads with d = 128, split-KV
+    (40, 2, 4096, 64, 128, 512, 128, 4, 130),      # 64 heads with d = 128, longer splits
+    (2, 2, 4096, 32, 128, 2048, 64, 4, 64),        # k = 2048, 32 heads
 ])
 def test_sparse_mqa_decode(lib, dev, gen, orc, T, B, L, H, d, k, W, m, win_cap):
     import torch
@@ -717,6 +765,57 @@ def test_paged_cache_matches_contiguous(lib, dev, gen, share, page, wpage):
                                 ref[torch.tensor(_slot_rows(ca, b, ca.cap), device="cuda")])
             r = rel_rms(got.cpu().numpy(), want.cpu().numpy())
             assert r <= 1e-5, f"paged entry gradients differ (rel-rms {r:.2e}, selection {sel})"
+
+
+def _paged_from_host(lib, torch, dev, ent, n_seq, cap, page, rng, extra=1):
+    """Host entries indexed seq*cap + slot, placed on the device in pages of `page` slots at
+    seeded shuffled physical pages (plus `extra` unused pages)."""
+    npp = cap // page
+    perm = rng.permutation(n_seq * npp + extra)[: n_seq * npp].astype(np.int32)
+    rows = (perm.reshape(n_seq, npp)[:, :, None] * page + np.arange(page)[None, None, :]).reshape(-1)
+    n_rows = (n_seq * npp + extra) * page
+    arrs = []
+    for a in ent:
+        b = np.zeros((n_rows,) + a.shape[1:], a.dtype)
+        b[rows] = a
+        arrs.append(b)
+    return lib.KvCache(dev.t(arrs[0]), dev.bf16(arrs[1]), dev.t(arrs[2]), cap,
+                       pages=torch.tensor(perm.reshape(n_seq, npp), device="cuda"), page=page)
+
+
+@pytest.mark.parametrize("path,T,B,L,H,d,k,W,m,page,wpage", [
+    ("sparse", 128, 4, 8192, 64, 512, 1024, 128, 4, 64, 32),    # two-role kernel, paged
+    ("sparse", 4, 4, 8192, 64, 512, 1024, 128, 4, 16, 128),     # split-KV 64-head kernel, paged
+    ("sparse", 4, 2, 8192, 64, 128, 1024, 128, 4, 256, 8),      # 64 heads, d = 128, paged
+    ("sparse", 6, 3, 2048, 16, 128, 64, 128, 4, 32, 1),         # 16 heads, paged
+    ("dense", 128, 8, 131072, 64, 512, 0, 128, 128, 128, 64),   # HCA, two-role kernel, paged
+    ("dense", 8, 8, 131072, 64, 512, 0, 128, 128, 1024, 128),   # HCA decode, paged
+])
+def test_paged_attention_against_oracle(lib, dev, gen, orc, path, T, B, L, H, d, k, W, m, page, wpage):
+    """Attention reading a paged compressed cache and a paged window ring (pages in a shuffled
+    physical order) against the oracle on the logical entries (seq * cap + slot)."""
+    import torch
+
+    _say(f"paged attention {path} T={T} B={B} L={L} H={H} d={d} k={k} page={page} wpage={wpage}")
+    N = L // m
+    comp, win, q = _attn_inputs(gen, 800 + T + d, B, N, W, H, d, T, L, W)
+    rng = np.random.default_rng(T + page)
+    seq = (np.arange(T) % B).astype(np.int32)
+    pos = np.full(T, L - 1, np.int64)
+    pos[0] = L - 7
+    pos[-1] = L // 2 + 1
+    sm = 1.0 / math.sqrt(d)
+    pc = _paged_from_host(lib, torch, dev, comp, B, N, page, rng)
+    pw = _paged_from_host(lib, torch, dev, win, B, W, wpage, rng, extra=0)
+    if path == "sparse":
+        idx = gen.random_idx(801 + T, 1, (pos + 1) // m, k)
+        ref_o, ref_l = orc.attend(q, seq, pos, comp, N, win, W, W, m, sm, idx=idx)
+        out, lse = lib.csa_sparse_mqa(dev.bf16(q), dev.t(seq), dev.t(pos), dev.t(idx), m, pc, pw, W, sm)
+    else:
+        ref_o, ref_l = orc.attend(q, seq, pos, comp, N, win, W, W, m, sm)
+        out, lse = lib.hca_dense_mqa(dev.bf16(q), dev.t(seq), dev.t(pos), m, N, pc, pw, W, sm)
+    torch.cuda.synchronize()
+    assert_attn_close(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, f"paged {path}")
 
 
 # --------------------------------------------------------------------------

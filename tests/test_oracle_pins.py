@@ -278,6 +278,47 @@ def test_index_negated_query_zeroes_relu(orc, gen):
     assert np.any(a > 0) and np.any(b > 0)
 
 
+def test_index_exact_witness_closed_forms(orc, gen):
+    """The fp32-exactness witness: log2 of (sum of |product terms|) over the finest
+    quantum a term can carry (1/4 x q scale x key scale x head weight), worst visible
+    (row, column); +inf for a head weight that is not a power of two."""
+    d_i, N, m = 128, 4, 4
+    ones = np.full((N, d_i // 2), 0x22, np.uint8)  # every element E2M1 1.0
+    unit = np.full((N, d_i // 32), 127, np.uint8)
+    q1 = np.full((1, d_i // 2), 0x22, np.uint8)
+    qs1 = np.full((1, d_i // 32), 127, np.uint8)
+    seq, pos = np.zeros(1, np.int32), np.full(1, 4 * N - 1, np.int64)
+    # one head, unit weight: 128 terms of 1 against a quantum of 1/4 -> log2(512) = 9
+    w = np.ones((1, 1), np.float32)
+    assert orc.index_exact_witness(q1, qs1, w, seq, pos, ones, unit, N, m, N) == 9.0
+    # two heads, weights 1 and 1/2: (128 + 64) / (1/4 * 1/2) = 1536
+    q2 = np.repeat(q1, 2, axis=0)
+    qs2 = np.repeat(qs1, 2, axis=0)
+    w2 = np.array([[1.0, 0.5]], np.float32)
+    assert orc.index_exact_witness(q2, qs2, w2, seq, pos, ones, unit, N, m, N) == math.log2(1536.0)
+    # a key block scale 2^-30 beside unit blocks: the quantum falls by 2^30, the sum barely moves
+    ks = unit.copy()
+    ks[:, 1] = 127 - 30
+    got = orc.index_exact_witness(q1, qs1, w, seq, pos, ones, ks, N, m, N)
+    assert got >= 24 and got == math.log2((96 + 32 * 2.0 ** -30) / (0.25 * 2.0 ** -30))
+    # a head weight that is not a power of two
+    w3 = np.array([[0.75]], np.float32)
+    assert orc.index_exact_witness(q1, qs1, w3, seq, pos, ones, unit, N, m, N) == math.inf
+    # no visible column: nothing to check
+    assert orc.index_exact_witness(q1, qs1, w, seq, np.full(1, 2, np.int64), ones, unit, N, m, N) == -math.inf
+    # only visible columns count: a wide-span key beyond the row's position is ignored
+    ks2 = unit.copy()
+    ks2[N - 1, 1] = 127 - 30
+    pos2 = np.full(1, 4 * (N - 1) - 1, np.int64)  # entries 0 .. N-2 visible
+    assert orc.index_exact_witness(q1, qs1, w, seq, pos2, ones, ks2, N, m, N) == 9.0
+    # the generator's N(0,1) data keeps a wide margin below 24 bits
+    kd, kss, _ = gen.mxfp4(24, 1, 64, d_i)
+    qd, qss, _ = gen.mxfp4(24, 2, 8, d_i)
+    wg = gen.pow2_weights(24, 3, (1, 8))
+    wit = orc.index_exact_witness(qd, qss, wg, seq, np.full(1, 255, np.int64), kd, kss, 64, m, 64)
+    assert 9.0 < wit < 20.0
+
+
 # --------------------------------------------------------------------------
 # top-k
 # --------------------------------------------------------------------------

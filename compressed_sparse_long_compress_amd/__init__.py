@@ -45,6 +45,7 @@ _lib.csa_topk_workspace.restype = _sz
 _lib.csa_topk_workspace.argtypes = [_i64, _i64, _i32]
 _lib.csa_topk.argtypes = [_vp, _i64, _i64, _vp, _i32, _i32, _vp, _vp, _sz, ctypes.c_uint32, _vp]
 CSA_TOPK_PREPARED = 1
+_lib.csa_topk_noalloc.argtypes = [_vp, _i64, _i64, _vp, _i32, _i32, _vp, _vp]
 _lib.csa_mqa_workspace.restype = _sz
 _lib.csa_mqa_workspace.argtypes = [_i64, _i32, _i32, _i64]
 _lib.csa_sparse_mqa.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _i32, _Kv, _Kv, _i32, _f32, _f32, _vp,
@@ -56,7 +57,7 @@ _lib.csa_mqa_bwd.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _i32, _
 _lib.csa_last_error.restype = ctypes.c_char_p
 _lib.csa_version.restype = ctypes.c_int
 
-EXPORTS = ["csa_compress", "csa_compress_channel", "csa_compress_index_keys", "csa_index_scores", "csa_index_scores_grouped", "csa_topk_workspace", "csa_topk", "csa_mqa_workspace",
+EXPORTS = ["csa_compress", "csa_compress_channel", "csa_compress_index_keys", "csa_index_scores", "csa_index_scores_grouped", "csa_topk_workspace", "csa_topk", "csa_topk_noalloc", "csa_mqa_workspace",
            "csa_sparse_mqa", "hca_dense_mqa", "csa_mqa_bwd", "csa_last_error", "csa_version"]
 
 
@@ -269,6 +270,18 @@ def csa_topk(scores, pos, m, k, out=None, ws=None, prepared=False):
         ws = topk_workspace(T, n_cols, k, scores.device)
     _check(_lib.csa_topk(_ptr(scores), T, n_cols, _ptr(pos), int(m), int(k), _ptr(out), _ptr(ws), ws.numel(),
                          CSA_TOPK_PREPARED if prepared else 0, _stream()))
+    return out
+
+
+def csa_topk_noalloc(scores, pos, m, k, out=None):
+    """csa_topk through the entry point that allocates nothing (the library's own scratch array)."""
+    _need(scores, "scores", torch.float32, 2)
+    _need(pos, "pos", torch.int64, 1)
+    T, n_cols = scores.shape
+    if out is None:
+        out = torch.empty(T, k, dtype=torch.int32, device=scores.device)
+    _need(out, "idx", torch.int32, 2)
+    _check(_lib.csa_topk_noalloc(_ptr(scores), T, n_cols, _ptr(pos), int(m), int(k), _ptr(out), _stream()))
     return out
 
 

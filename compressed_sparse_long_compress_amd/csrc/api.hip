@@ -239,6 +239,24 @@ int csa_topk(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos,
     return hip_status(e, fn);
 }
 
+int csa_topk_noalloc(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos, int32_t m, int32_t k,
+                     int32_t* idx, csa_stream_t stream) {
+    const char* fn = "csa_topk_noalloc";
+    if (T < 0 || n_cols < 0) return fail(CSA_EINVAL, "%s: T and n_cols must be >= 0", fn);
+    if (k < 1 || k > 2048) return fail(CSA_EUNSUPPORTED, "%s: k=%d outside 1..2048", fn, k);
+    if (n_cols >= ((int64_t)1 << 31)) return fail(CSA_EUNSUPPORTED, "%s: n_cols must be < 2^31", fn);
+    if (m < 1) return fail(CSA_EINVAL, "%s: m must be >= 1", fn);
+    if (T == 0) return ok();
+    if (!scores || !pos || !idx) return fail(CSA_EINVAL, "%s: null pointer argument", fn);
+    const size_t need = csa::topk_workspace_bytes(T, n_cols, k);
+    if (need > csa::topk_scratch_bytes())
+        return fail(CSA_EUNSUPPORTED, "%s: T=%lld x n_cols=%lld needs %zu bytes of scratch, more than the library's "
+                    "%zu-byte array; call csa_topk with a workspace", fn, (long long)T, (long long)n_cols, need,
+                    csa::topk_scratch_bytes());
+    hipError_t e = csa::launch_topk_noalloc(scores, T, n_cols, pos, m, k, idx, (hipStream_t)stream);
+    return hip_status(e, fn);
+}
+
 size_t csa_mqa_workspace(int64_t T, int32_t H, int32_t d, int64_t max_keys) {
     return csa::mqa_workspace_bytes(T, H, d, max_keys);
 }

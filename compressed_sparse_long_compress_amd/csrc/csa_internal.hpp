@@ -66,6 +66,11 @@ bool topk_uses_summary(int64_t T, int64_t n_cols);
 // prepared: the row summaries were already written by the indexer
 hipError_t launch_topk(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos, int m, int k, int32_t* idx,
                        void* ws, bool prepared, hipStream_t st);
+// the same selection with the library's own scratch array in place of a workspace
+// (shapes needing more than topk_scratch_bytes() of it are refused by the caller)
+size_t topk_scratch_bytes();
+hipError_t launch_topk_noalloc(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos, int m, int k,
+                               int32_t* idx, hipStream_t st);
 
 
 

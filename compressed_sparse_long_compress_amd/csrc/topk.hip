@@ -7,6 +7,9 @@
 // order (score desc, index asc) the selection is defined by.  Rows that fit
 // in LDS (<= 36608 columns) are cached there; longer rows re-read global
 // memory each pass.
+#include <atomic>
+#include <mutex>
+
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 
@@ -1316,5 +1319,55 @@ hipError_t launch_topk(const float* scores, int64_t T, int64_t n_cols, const int
 }
 
 bool topk_uses_summary(int64_t T, int64_t n_cols) { return topk_summ(T, n_cols); }
+
+// ---------------------------------------------------------------------------
+// Selection without a caller workspace: for shapes that select from the row
+// summary, the summaries, slice records and candidates live in `scratch`, a
+// device array of the library (each GPU holds its own copy, at its own
+// address, until the process ends).  Host code never passes the array's name
+// to a kernel: its device address is looked up once per device, with that
+// device current, and kept.  Nothing in it needs to start at zero; calls that
+// overlap on one GPU share it and race.
+// ---------------------------------------------------------------------------
+constexpr size_t kTopkScratchBytes = (size_t)12 << 20;
+static __device__ __align__(256) uint8_t scratch[kTopkScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_addr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+static hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+size_t topk_scratch_bytes() { return kTopkScratchBytes; }
+
+hipError_t launch_topk_noalloc(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos, int m, int k,
+                               int32_t* idx, hipStream_t st) {
+    if (T == 0) return hipSuccess;
+    void* ws = nullptr;
+    if (topk_summ(T, n_cols)) {
+        if (topk_workspace_bytes(T, n_cols, k) > kTopkScratchBytes) return hipErrorInvalidValue;
+        const hipError_t e = scratch_address(&ws);
+        if (e != hipSuccess) return e;
+    }
+    return launch_topk(scores, T, n_cols, pos, m, k, idx, ws, false, st);
+}
 
 }  // namespace csa

@@ -237,6 +237,21 @@ int csa_topk(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos,
              void* ws, size_t ws_bytes, uint32_t flags, csa_stream_t stream);
 
 /*
+ * csa_topk_noalloc — csa_topk for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same selection, arguments and results as csa_topk with flags 0;
+ * instead of a caller workspace it uses a 12 MiB scratch array of the library
+ * (one per GPU, held until the process ends).  It allocates nothing.
+ *   Limit: shapes whose csa_topk_workspace(T, n_cols, k) exceeds 12 MiB
+ *   (few rows of very many columns, e.g. T x n_cols beyond ~32 M for T < 128)
+ *   are refused with CSA_EUNSUPPORTED; other shapes need no scratch.
+ * Every call on one GPU shares that array: calls that overlap on one GPU
+ * (concurrent streams, threads) race and must be serialised by the caller.
+ */
+int csa_topk_noalloc(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos, int32_t m, int32_t k,
+                     int32_t* idx, csa_stream_t stream);
+
+/*
  * csa_sparse_mqa — CSA attention: multi-query attention (one shared KV head;
  * every entry is both key and value) over the selected compressed entries
  * plus the sliding-window branch, merged in one softmax (what a log-sum-exp

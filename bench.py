@@ -11,10 +11,15 @@ One step = the CSA decode hot path for a batch of 4 sequences, each with a
 Inputs are seeded synthetic tensors resident in HBM before timing starts;
 8 replica sets of the keys and the compressed cache (~5.5 GB) rotate step by
 step so the 256 MB Infinity Cache cannot serve a step from the previous one.
+The timed steps are captured as one HIP graph (replica sets rotating as in
+the eager loop) and replayed once; its outputs are checked against the eager
+step.
 
 Prints ONE JSON line: queries/s for the batch, a roofline object for the
-dominant kernel (the indexer, bound by HBM), and the fp64 CPU oracle timed
-on the same batch as a reported baseline.
+dominant kernel (the indexer, bound by HBM), the chunked prefill (8,192 new
+tokens after 131,072: tokens/s and its MFMA-bound kernels against their
+peaks), and the fp64 CPU oracle timed on the same decode batch as a reported
+baseline.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--all]
 """
@@ -52,21 +57,24 @@ def index_traffic():
 
 def index_bytes_per_query(N, h_i, d_i):
     """Algorithmic HBM bytes of csa_index_scores per query row: every MXFP4 key
-    (d_i/2 data + d_i/32 scale bytes), the query (h_i keys' worth + fp32
-    weights), the fp32 score row written and the selection's row summary (one
-    4-byte key per 32 columns)."""
+    (d_i/2 data + d_i/32 scale bytes) and the query (h_i MXFP4 vectors and their
+    fp32 head weights).  17,826,368 B per row at 1M context."""
     key = d_i // 2 + d_i // 32
-    return N * key + h_i * key + h_i * 4 + N * 4 + (N + 31) // 32 * 4
+    return N * key + h_i * key + h_i * 4
+
+
+def index_excess_bytes_per_query(N):
+    """Bytes the indexer writes beyond the algorithmic ones: the fp32 score row and
+    the selection's row summary (one 4-byte key per 32 columns)."""
+    return N * 4 + (N + 31) // 32 * 4
 
 
 def step_bytes_per_query(N, h_i, d_i, k, W, H, d):
-    """Algorithmic HBM bytes of the whole decode step per query: indexer bytes,
-    what the summary-based selection reads back (the row summary and k
-    32-column groups of scores), k indices, the gathered entries
-    (k + W) x (d-64 + 128 + 4) B, the bf16 query and fp32 output + lse."""
+    """Algorithmic HBM bytes of the whole decode step per query: the indexer's
+    keys and query, the gathered entries (k + W) x (d-64 + 128 + 4) B, the bf16
+    query and the fp32 output (18,691,136 B per query at 1M context)."""
     entry = (d - 64) + 64 * 2 + 4
-    return (index_bytes_per_query(N, h_i, d_i) + (N + 31) // 32 * 4 + k * 32 * 4 + k * 4 * 2 + (k + W) * entry
-            + H * d * 2 + H * d * 4 + H * 4)
+    return index_bytes_per_query(N, h_i, d_i) + (k + W) * entry + H * d * 2 + H * d * 4
 
 
 class DecodeSet:
@@ -145,6 +153,36 @@ class DecodeSet:
         self.index(r)
         self.topk(r)
         self.attend(r)
+
+    def capture(self, n_steps):
+        """One HIP graph holding n_steps whole steps, replica sets rotating as in the eager
+        loop (the library issues kernels only: no memset, no allocation).  Returns the
+        eager step's (indices, out, lse), which every replay must reproduce."""
+        import torch
+
+        self.step(0)
+        torch.cuda.synchronize()
+        want = (self.idx.clone(), self.out.clone(), self.lse.clone())
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for r in range(self.replicas):
+                self.step(r)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            for i in range(n_steps):
+                self.step(i)
+        torch.cuda.synchronize()
+        return want
+
+    def check(self, want, what):
+        import torch
+
+        torch.cuda.synchronize()
+        assert torch.equal(self.idx, want[0]) and torch.equal(self.out, want[1]) and torch.equal(self.lse, want[2]), \
+            f"{what}: differs from the eager step"
 
 
 class PrefillSet:
@@ -357,17 +395,18 @@ def time_calls(ds, n):
     return res
 
 
-def time_steps(ds, steps, warmup):
+def time_steps(ds, steps, warmup, fn=None):
     import torch
 
+    fn = fn or ds.step
     for i in range(warmup):
-        ds.step(i)
+        fn(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     t0 = time.perf_counter()
     for i in range(steps):
-        ds.step(i)
+        fn(i)
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -419,9 +458,23 @@ def time_index_launches(ds, n):
     return e0.elapsed_time(e1) / n / 1e3
 
 
+def cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(wl):
     """The fp64 oracle (as written, untuned) on the same batch: index scores,
-    top-k and sparse attention for every query row of the workload."""
+    top-k and sparse attention for every query row of the workload, repeated
+    for about 10 s.  The oracle's OpenMP loops run over (row, column chunk) for
+    the scores and over rows elsewhere, with every host core."""
     import numpy as np
 
     import oracle
@@ -429,8 +482,7 @@ def cpu_baseline(wl):
     T = wl["T"]
     reps = 0
     t0 = time.perf_counter()
-    # the whole batch, repeated until about 10 s of work (at most 30 passes)
-    while reps < 30 and (reps == 0 or time.perf_counter() - t0 < 10.0):
+    while reps < 200 and (reps == 0 or time.perf_counter() - t0 < 10.0):
         sc = oracle.index_scores(wl["iq"][0], wl["iq"][1], wl["w"], wl["seq"], wl["pos"], wl["keys"][0],
                                  wl["keys"][1], wl["N"], wl["m"], wl["n_cols"]).astype(np.float32)
         idx = oracle.topk(sc, wl["pos"], wl["m"], wl["k"])
@@ -438,9 +490,82 @@ def cpu_baseline(wl):
                       wl["sm_scale"], wl["rope_base"], idx=idx)
         reps += 1
     dt = time.perf_counter() - t0
-    cores = min(T, os.cpu_count() or 1)  # the oracle parallelises over query rows
-    return {"value": T * reps / dt, "unit": "queries/s", "cores": cores, "kind": "oracle",
-            "sample": f"all {T} query rows of the batch (full 1M-context rows), {reps} passes, {dt:.1f} s wall"}
+    ncpu = os.cpu_count() or 1
+    threads = int(os.environ.get("OMP_NUM_THREADS", ncpu))
+    return {"value": T * reps / dt, "unit": "queries/s", "cores": min(threads, ncpu), "host_cpus": ncpu,
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": f"all {T} query rows of the batch (full 1M-context rows), {reps} passes, {dt:.1f} s wall; "
+                      f"OpenMP threads {min(threads, ncpu)} of {ncpu} host CPUs"}
+
+
+def time_back_to_back(fn, n):
+    """Average duration of n launches of fn queued back to back between one pair of events."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n / 1e3
+
+
+MXFP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 (fp4) MFMA
+FP16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 / bf16 MFMA
+
+
+def prefill_flops(wl):
+    """Algorithmic work of the chunked prefill: indexer 2 h_i d_i flop per visible
+    (query, entry) pair; attention 4 d flop per (row, head, key) (QK and PV) over
+    each row's key set (selected entries + window; HCA: every visible entry + window)."""
+    import numpy as np
+
+    pos = np.asarray(wl["pos"], np.int64)
+    nv = np.minimum((pos + 1) // wl["m"], wl["n_cols"])
+    win = np.minimum(pos + 1, wl["W"])
+    per_key = wl["H"] * 4 * wl["d"]
+    return {"index": float(nv.sum()) * 2 * wl["h_i"] * wl["d_i"],
+            "sparse_mqa": float((np.minimum(wl["k"], nv) + win).sum()) * per_key,
+            "hca_mqa": float(((pos + 1) // wl["m_hca"] + win).sum()) * per_key}
+
+
+def prefill_measure(steps):
+    """The chunked-prefill workload: whole steps (compress the chunk, index, top-k, both
+    attentions) and, for the MFMA-bound kernels, back-to-back launches of each call."""
+    import compressed_sparse_long_compress_amd as csa
+    from gen import configs
+
+    wl = configs.named("prefill_chunk")
+    ds = PrefillSet(wl)
+    n = max(steps, 3)
+    sec, _ = time_steps(ds, n, 2)
+    m, k, W = wl["m"], wl["k"], wl["W"]
+    t_index = time_back_to_back(lambda: csa.csa_index_scores(ds.iq, ds.iqs, ds.w, ds.seq, ds.pos, ds.keys, m,
+                                                              wl["n_cols"], out=ds.scores), n)
+    t_topk = time_back_to_back(lambda: csa.csa_topk(ds.scores, ds.pos, m, k, out=ds.idx, ws=ds.tws), n)
+    t_sparse = time_back_to_back(lambda: csa.csa_sparse_mqa(ds.q, ds.seq, ds.pos, ds.idx, m, ds.comp, ds.win, W,
+                                                            wl["sm_scale"], out=ds.out, lse=ds.lse), n)
+    t_hca = time_back_to_back(lambda: csa.hca_dense_mqa(ds.qh, ds.seq, ds.pos, wl["m_hca"], wl["hca_cap"], ds.hca,
+                                                        ds.win_h, W, wl["sm_scale"], out=ds.hout, lse=ds.hlse), n)
+    fl = prefill_flops(wl)
+    res = {"workload": "prefill_chunk", "tokens": wl["T"], "context": wl["total"],
+           "tokens_per_s": wl["T"] * n / sec, "ms_per_step": sec / n * 1e3, "steps": n,
+           "per_call_ms": {"index": t_index * 1e3, "topk": t_topk * 1e3, "sparse_mqa": t_sparse * 1e3,
+                           "hca_mqa": t_hca * 1e3},
+           "index": {"kernel": "k_index_gemm<128, 8>", "bound": "mfma", "flops": fl["index"],
+                     "achieved": fl["index"] / t_index / 1e12, "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": fl["index"] / t_index / 1e12 / MXFP4_PEAK_TFLOPS},
+           "sparse_mqa": {"kernel": "k_mqa64ws<512, false>", "bound": "mfma", "flops": fl["sparse_mqa"],
+                          "achieved": fl["sparse_mqa"] / t_sparse / 1e12, "peak": FP16_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": fl["sparse_mqa"] / t_sparse / 1e12 / FP16_PEAK_TFLOPS},
+           "hca_mqa": {"kernel": "k_mqa64ws<512, false>", "bound": "mfma", "flops": fl["hca_mqa"],
+                       "achieved": fl["hca_mqa"] / t_hca / 1e12, "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                       "frac": fl["hca_mqa"] / t_hca / 1e12 / FP16_PEAK_TFLOPS}}
+    del ds
+    return res
 
 
 def run_workload(name, steps, warmup):
@@ -463,16 +588,13 @@ def run_workload(name, steps, warmup):
 
 
 def secondary(steps, warmup):
-    """The other workloads (opt-in): 1M CSA decode with two query rows per sequence, 64K CSA
-    decode, 1M HCA decode, chunked prefill."""
+    """The other decode workloads (opt-in): 1M CSA decode with two query rows per sequence,
+    64K CSA decode, 1M HCA decode."""
     res = {}
     for name in ("csa_decode_1m_mtp2", "csa_decode_64k", "hca_decode_1m"):
         wl, ds, sec = run_workload(name, steps, warmup)
         res[name] = {"queries_per_s": wl["T"] * steps / sec, "ms_per_step": sec / steps * 1e3}
         del ds
-    n = max(steps // 20, 3)
-    wl, ds, sec = run_workload("prefill_chunk", n, 2)
-    res["prefill_chunk"] = {"tokens_per_s": wl["T"] * n / sec, "ms_per_step": sec / n * 1e3}
     return res
 
 
@@ -488,6 +610,7 @@ def main():
                              "hca_decode_1m", "prefill_chunk", "compress_chunk"],
                     help="time only this workload and print its line (profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill object")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 5 device copies of 256 MiB (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -550,8 +673,26 @@ def main():
     log(f"generated csa_decode_1m inputs in {time.perf_counter() - t0:.1f} s")
     ds = DecodeSet(wl, replicas=8)
     log("uploaded 8 replica sets")
-    sec, wall = time_steps(ds, args.steps, args.warmup)
-    log(f"timed {args.steps} steps: {sec * 1e3 / args.steps:.3f} ms/step (wall {wall:.3f} s)")
+    want = ds.capture(args.steps)
+    log(f"captured the {args.steps} timed steps as one HIP graph")
+    eager_sec, _ = time_steps(ds, args.steps, args.warmup)
+    ds.check(want, "eager steps")
+    for i in range(args.warmup):
+        ds.step(i)
+    ds.idx.fill_(-3)
+    ds.out.zero_()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    ds.graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sec = e0.elapsed_time(e1) / 1e3
+    ds.check(want, "graph replay")
+    log(f"timed {args.steps} steps as one graph replay: {sec * 1e3 / args.steps:.4f} ms/step "
+        f"(eager {eager_sec * 1e3 / args.steps:.4f}, host wall {wall:.4f} s); the replay's outputs equal the eager step")
     kern = time_kernels(ds, args.steps)
     log("per-call ms: " + ", ".join(f"{k} {v * 1e3:.4f}" for k, v in kern.items()))
     idx_sec = time_index_launches(ds, args.steps)
@@ -573,18 +714,26 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4+bf16",
+        "dtype": "mxfp4+fp16",
         "data": "synthetic (seeded N(0,1) before quantisation, 5% planted index keys)",
         "config": {"workload": "csa_decode_1m", "batch": B, "context": wl["L"], "entries_per_seq": N, "m": wl["m"],
                    "k": k, "window": W, "heads": H, "head_dim": d, "indexer": f"{h_i}x{d_i} mxfp4",
-                   "replicas": ds.replicas},
+                   "replicas": ds.replicas, "timing": "the timed steps replayed as one HIP graph (replica sets rotated)"},
+        "eager_ms_per_step": eager_sec / args.steps * 1e3,
+        "step_bytes": step_bytes,
         "step_hbm_gbs": step_bytes * args.steps / sec / 1e9,
         "step_hbm_frac": step_bytes * args.steps / sec / 1e9 / HBM_PEAK_GBS,
         "per_call_us": {kk: v * 1e6 for kk, v in kern.items()},
         "roofline": {"kernel": "k_index_rows<128, 8>", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": index_traffic(),
-                     "bytes_per_launch": idx_bytes, "kernel_us": idx_sec * 1e6},
+                     "bytes_per_launch": idx_bytes, "excess_bytes_per_launch": B * index_excess_bytes_per_query(N),
+                     "kernel_us": idx_sec * 1e6},
     }
+    del ds
+    if not args.no_prefill:
+        log("timing the chunked prefill (8,192 tokens after 131,072)")
+        result["prefill"] = prefill_measure(max(args.steps // 4, 3))
+        log(f"prefill: {result['prefill']['tokens_per_s']:.4g} tokens/s")
     if args.all:
         result["secondary"] = secondary(max(args.steps // 2, 20), args.warmup)
     if not args.no_cpu:

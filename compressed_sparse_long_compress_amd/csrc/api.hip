@@ -2,6 +2,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include "../../include/csa.h"
 #include "csa_internal.hpp"
@@ -69,6 +70,32 @@ int check_mqa_common(const char* fn, const uint16_t* q, const int32_t* seq, cons
         if (int rc = check_kv(win, d, "win", fn)) return rc;
         if (win.cap < window) return fail(CSA_EINVAL, "%s: win.cap (%lld) < window (%d)", fn, (long long)win.cap, window);
     }
+    return CSA_OK;
+}
+
+// Debug checks (environment variable CSA_DEBUG_CHECKS set and not "0"): the attention calls
+// first scan the entries they will read for RoPE dims outside the fp16 range and fail with
+// CSA_EINVAL.  The check synchronises the caller's stream (not for graph capture).
+static __device__ int g_rope_bad;
+
+bool debug_checks() {
+    const char* e = getenv("CSA_DEBUG_CHECKS");
+    return e && e[0] && !(e[0] == '0' && e[1] == 0);
+}
+
+int check_rope_range(const char* fn, const int32_t* seq, const int64_t* pos, int64_t T, const int32_t* idx, int k,
+                     int m, const csa::KvView& comp, const csa::KvView& win, int window, hipStream_t st) {
+    void* flag = nullptr;
+    hipError_t e = hipGetSymbolAddress(&flag, HIP_SYMBOL(g_rope_bad));
+    if (e == hipSuccess) e = hipMemsetAsync(flag, 0, sizeof(int), st);
+    if (e == hipSuccess) e = csa::launch_check_rope(seq, pos, T, idx, k, m, comp, win, window, (int*)flag, st);
+    int bad = 0;
+    if (e == hipSuccess) e = hipMemcpyAsync(&bad, flag, sizeof(int), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(CSA_EHIP, "%s: debug range check failed: %s", fn, hipGetErrorString(e));
+    if (bad)
+        return fail(CSA_EINVAL, "%s: an entry read by this call has a RoPE dim of magnitude above 65504 (or not "
+                    "finite); the attention kernels stage those dims in fp16", fn);
     return CSA_OK;
 }
 
@@ -276,6 +303,9 @@ int csa_sparse_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos, in
     if (ws_bytes < need || (need > 0 && !ws))
         return fail(CSA_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
     if (need > 0 && !aligned16(ws)) return fail(CSA_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+    if (debug_checks())
+        if (int rc = check_rope_range(fn, seq, pos, T, idx, k, m, view(comp), view(win), window, (hipStream_t)stream))
+            return rc;
     hipError_t e = csa::launch_mqa(q, seq, pos, T, H, d, idx, k, m, max_keys, view(comp), view(win), window, sm_scale,
                                    csa::rope_table((double)rope_base), out, lse, ws, (hipStream_t)stream);
     return hip_status(e, fn);
@@ -313,6 +343,10 @@ int hca_dense_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos, int
     if (ws_bytes < need || (need > 0 && !ws))
         return fail(CSA_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
     if (need > 0 && !aligned16(ws)) return fail(CSA_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+    if (debug_checks())
+        if (int rc = check_rope_range(fn, seq, pos, T, nullptr, 0, m, view(comp), view(win), window,
+                                      (hipStream_t)stream))
+            return rc;
     hipError_t e = csa::launch_mqa(q, seq, pos, T, H, d, nullptr, 0, m, max_keys, view(comp), view(win), window,
                                    sm_scale, csa::rope_table((double)rope_base), out, lse, ws, (hipStream_t)stream);
     return hip_status(e, fn);

@@ -1528,6 +1528,36 @@ __global__ __launch_bounds__(128) void k_mqa_combine16(const _Float16* __restric
     if (tid == 0) lse[th] = L > 0.f ? M + __logf(L) : -INFINITY;
 }
 
+// Range check of the entries a call reads (debug builds of a caller's pipeline): the
+// 64-head kernels stage the bf16 RoPE dims as fp16 with truncation, so a value of magnitude
+// above 65504 (or a NaN / infinity) would be clamped.  One workgroup per row walks the row's
+// key list like the attention kernels and sets *bad when any referenced entry holds one.
+__global__ __launch_bounds__(256) void k_check_rope(const int32_t* __restrict__ seq, const int64_t* __restrict__ pos,
+                                                    const int32_t* __restrict__ idx, int k, int m, KvView comp,
+                                                    KvView win, int window, int* __restrict__ bad) {
+    const int64_t t = blockIdx.x;
+    const RowKeys rk = row_keys(pos[t], idx, k, m, window);
+    const int32_t sq = seq[t];
+    int found = 0;
+    for (int64_t u = threadIdx.x; u < rk.n; u += 256) {
+        const int64_t r = resolve(u, t, sq, rk, idx, k, comp, win);
+        if (r == -1) continue;
+        const uint16_t* rp = r >= 0 ? comp.rope + r * 64 : win.rope + (-r - 2) * 64;
+        for (int e = 0; e < 64; ++e) {
+            const uint32_t b = (uint32_t)rp[e] & 0x7FFFu;
+            found |= b > 0x477Fu;  // |x| > 65504 in bf16 (0x477F = 65280; the next value 65536 is beyond)
+        }
+    }
+    if (found) atomicOr(bad, 1);
+}
+
+hipError_t launch_check_rope(const int32_t* seq, const int64_t* pos, int64_t T, const int32_t* idx, int k, int m,
+                             KvView comp, KvView win, int window, int* bad, hipStream_t st) {
+    if (T == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_check_rope, dim3((unsigned)T), dim3(256), 0, st, seq, pos, idx, k, m, comp, win, window, bad);
+    return hipGetLastError();
+}
+
 // Splits per row: about one workgroup per CU in all (the 64-head kernels hold most of a
 // CU's LDS, so a second round of workgroups would run after the first), at least 64 keys
 // per split, at most 64 splits.

@@ -79,6 +79,10 @@ size_t mqa_workspace_bytes(int64_t T, int H, int d, int64_t max_keys);
 hipError_t launch_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int H, int d,
                       const int32_t* idx, int k, int m, int64_t max_keys, KvView comp, KvView win, int window,
                       float sm_scale, const RopeTab& rt, float* out, float* lse, void* ws, hipStream_t st);
+// sets *bad (device int) when an entry the attention would read for these rows holds a
+// bf16 RoPE dim outside the fp16 range (64-head kernels stage those dims as fp16)
+hipError_t launch_check_rope(const int32_t* seq, const int64_t* pos, int64_t T, const int32_t* idx, int k, int m,
+                             KvView comp, KvView win, int window, int* bad, hipStream_t st);
 hipError_t launch_mqa_bwd(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int H,
                           const int32_t* idx, int k, int m, KvView comp, KvView win, int window, float sm_scale,
                           const RopeTab& rt, const float* out, const float* lse, const float* dout, float* dq,

@@ -29,8 +29,23 @@
  *     caller's next synchronisation.
  *   - Shapes are validated on the host; values inside device arrays (seq,
  *     pos, idx) are trusted except where a call documents a check.
- *   - Results are deterministic: no floating-point atomics, fixed reduction
- *     orders, no dependence on other rows of the batch.
+ *   - Determinism.  Every forward call is run-to-run deterministic: no
+ *     floating-point atomics, fixed reduction orders.  csa_mqa_bwd documents
+ *     its own rule.
+ *   - Batch invariance.  csa_compress* and csa_topk give each row (entry)
+ *     the same bits whatever the other rows of the call and T.  So does
+ *     csa_index_scores* under its exactness precondition (every score exact
+ *     in fp32; the kernel chosen for a shape then cannot change a bit).  The
+ *     attention calls never read another row's inputs, but each row's key
+ *     list is cut into S split-KV ranges, range s = positions
+ *     [n*s/S, n*(s+1)/S) of the row's n keys, with
+ *       S = min(ceil(256 / T), ceil(bound / 64), 64),
+ *       bound = k + window (csa_sparse_mqa) or max_vis + window (hca_dense_mqa),
+ *     and the partial results are merged in split order.  A row's out and lse
+ *     are bit-identical across calls that give the same S (e.g. any T <= 15 at
+ *     k = 1024, window = 128); with another S the fp16 partials round
+ *     differently and the results agree to about 3e-4 relative RMS (each
+ *     meets the 2e-3 relative-RMS bar against the fp64 reference).
  *
  * Storage formats
  *   - Compressed KV entry (and window-ring entry), d = d_nope + 64:
@@ -55,7 +70,7 @@
 extern "C" {
 #endif
 
-#define CSA_VERSION 102
+#define CSA_VERSION 103
 
 enum {
     CSA_OK = 0,
@@ -271,6 +286,12 @@ int csa_topk_noalloc(const float* scores, int64_t T, int64_t n_cols, const int64
  * H in {16, 32, 64}; d in {128, 512}; 1 <= k <= 2048; 0 <= window <= 1024.
  * The window ring must hold every token max(0, t-window+1) .. t of every row
  * at slot p % win.cap (win.cap >= window).
+ * Range: the kernels stage the entries' bf16 RoPE dims as fp16, so every
+ * entry read must have |rope value| <= 65504 (larger values are clamped or
+ * overflow; entries written by csa_compress from data of that magnitude
+ * qualify).  With the environment variable CSA_DEBUG_CHECKS=1 this call and
+ * hca_dense_mqa first scan the entries they will read and return CSA_EINVAL
+ * on a violation (the scan synchronises the stream; not for graph capture).
  * Workspace: csa_mqa_workspace(T, H, d, k + window) bytes (split-KV partials).
  */
 size_t csa_mqa_workspace(int64_t T, int32_t H, int32_t d, int64_t max_keys);
@@ -284,10 +305,11 @@ int csa_sparse_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos, in
  * over every compressed entry; [hortopato] § HCA: m' = 128; [zcldvi]: window
  * branch in both attentions).  Same as csa_sparse_mqa with the key set
  * { every comp entry j < (t+1)/m } plus the window.
- *   max_vis  an upper bound on (pos[t]+1)/m over the rows; it sizes the
- *            split-KV launch only (results do not depend on it as long as it
- *            is >= 1); the workspace is csa_mqa_workspace(T, H, d,
- *            max_vis + window).
+ *   max_vis  an upper bound on (pos[t]+1)/m over the rows, >= 1; with T it
+ *            sets the split-KV partition (see the batch-invariance rule at the
+ *            top: results are bit-identical for equal partitions and agree
+ *            to rounding level otherwise); the workspace is
+ *            csa_mqa_workspace(T, H, d, max_vis + window).
  */
 int hca_dense_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int32_t H, int32_t d,
                   int32_t m, int64_t max_vis, csa_kv_t comp, csa_kv_t win, int32_t window, float sm_scale,

@@ -188,9 +188,10 @@ class DecodeSet:
 class PrefillSet:
     """Device tensors of the chunked-prefill workload (8,192 new tokens after a
     131,072-token context, one sequence, paired HCA layer).  One step compresses
-    the new chunk (CSA m=4, HCA m'=128, both window rings), scores every
-    (query, entry) pair, selects the top-1024 per query and runs both
-    attentions for all 8,192 queries.  The older context is compressed in set-up."""
+    the new chunk (CSA m=4, HCA m'=128, both window rings), selects the top-1024
+    entries per query with the fused indexer + top-k (every (query, entry) pair
+    scored, no score rows written) and runs both attentions for all 8,192
+    queries.  The older context is compressed in set-up."""
 
     def __init__(self, wl):
         import torch
@@ -220,6 +221,8 @@ class PrefillSet:
         self.lse = torch.empty(T, wl["H"], dtype=torch.float32, device="cuda")
         self.hout, self.hlse = torch.empty_like(self.out), torch.empty_like(self.lse)
         self.tws = csa.topk_workspace(T, wl["n_cols"], k)
+        self.itk_ws = torch.empty(csa.csa_index_topk_workspace(T, wl["n_cols"], k, wl["h_i"]), dtype=torch.uint8,
+                                  device="cuda")
         self.replicas = 1
 
     def step(self, i):
@@ -231,8 +234,9 @@ class PrefillSet:
         csa.csa_compress(self.kv[L0:], self.lg[L0:], L0, 1, 0, self.win)
         csa.csa_compress(self.kvh[L0:], self.lgh[L0:], L0, mh, 0, self.hca)
         csa.csa_compress(self.kvh[L0:], self.lgh[L0:], L0, 1, 0, self.win_h)
-        csa.csa_index_scores(self.iq, self.iqs, self.w, self.seq, self.pos, self.keys, m, wl["n_cols"], out=self.scores)
-        csa.csa_topk(self.scores, self.pos, m, k, out=self.idx, ws=self.tws)
+        # indexer and top-k fused: no score rows are written
+        csa.csa_index_topk(self.iq, self.iqs, self.w, self.seq, self.pos, self.keys, m, wl["n_cols"], k, out=self.idx,
+                           ws=self.itk_ws)
         csa.csa_sparse_mqa(self.q, self.seq, self.pos, self.idx, m, self.comp, self.win, W, wl["sm_scale"],
                            out=self.out, lse=self.lse)
         csa.hca_dense_mqa(self.qh, self.seq, self.pos, mh, wl["hca_cap"], self.hca, self.win_h, W, wl["sm_scale"],
@@ -533,8 +537,12 @@ def prefill_flops(wl):
 
 
 def prefill_measure(steps):
-    """The chunked-prefill workload: whole steps (compress the chunk, index, top-k, both
-    attentions) and, for the MFMA-bound kernels, back-to-back launches of each call."""
+    """The chunked-prefill workload: whole steps (compress the chunk, fused index + top-k, both
+    attentions) and back-to-back launches of each call: the fused selection, the indexer alone
+    (score rows written, against the MXFP4 peak), the top-k on those rows, both attentions
+    (against the fp16 peak)."""
+    import torch
+
     import compressed_sparse_long_compress_amd as csa
     from gen import configs
 
@@ -546,6 +554,8 @@ def prefill_measure(steps):
     t_index = time_back_to_back(lambda: csa.csa_index_scores(ds.iq, ds.iqs, ds.w, ds.seq, ds.pos, ds.keys, m,
                                                               wl["n_cols"], out=ds.scores), n)
     t_topk = time_back_to_back(lambda: csa.csa_topk(ds.scores, ds.pos, m, k, out=ds.idx, ws=ds.tws), n)
+    t_fused = time_back_to_back(lambda: csa.csa_index_topk(ds.iq, ds.iqs, ds.w, ds.seq, ds.pos, ds.keys, m,
+                                                           wl["n_cols"], k, out=ds.idx, ws=ds.itk_ws), n)
     t_sparse = time_back_to_back(lambda: csa.csa_sparse_mqa(ds.q, ds.seq, ds.pos, ds.idx, m, ds.comp, ds.win, W,
                                                             wl["sm_scale"], out=ds.out, lse=ds.lse), n)
     t_hca = time_back_to_back(lambda: csa.hca_dense_mqa(ds.qh, ds.seq, ds.pos, wl["m_hca"], wl["hca_cap"], ds.hca,
@@ -553,8 +563,11 @@ def prefill_measure(steps):
     fl = prefill_flops(wl)
     res = {"workload": "prefill_chunk", "tokens": wl["T"], "context": wl["total"],
            "tokens_per_s": wl["T"] * n / sec, "ms_per_step": sec / n * 1e3, "steps": n,
-           "per_call_ms": {"index": t_index * 1e3, "topk": t_topk * 1e3, "sparse_mqa": t_sparse * 1e3,
-                           "hca_mqa": t_hca * 1e3},
+           "per_call_ms": {"index_topk_fused": t_fused * 1e3, "index": t_index * 1e3, "topk": t_topk * 1e3,
+                           "sparse_mqa": t_sparse * 1e3, "hca_mqa": t_hca * 1e3},
+           "index_topk_fused": {"calls": "csa_index_topk (sample, threshold, emit, pick)",
+                                "ms": t_fused * 1e3, "split_ms": (t_index + t_topk) * 1e3,
+                                "mxfp4_tflops": fl["index"] / t_fused / 1e12},
            "index": {"kernel": "k_index_gemm<128, 8>", "bound": "mfma", "flops": fl["index"],
                      "achieved": fl["index"] / t_index / 1e12, "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": fl["index"] / t_index / 1e12 / MXFP4_PEAK_TFLOPS},

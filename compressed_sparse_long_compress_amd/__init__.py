@@ -41,6 +41,10 @@ _lib.csa_compress_index_keys.argtypes = [_vp, _vp, _i64, _i64, _i32, _i32, _i32,
 _lib.csa_index_scores.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _IdxKeys, _i32, _i64, _vp, _vp, _sz, _vp]
 _lib.csa_index_scores_grouped.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _IdxKeys, _i32, _i64, _i32, _vp,
                                           _vp, _sz, _vp]
+_lib.csa_index_topk_workspace.restype = _sz
+_lib.csa_index_topk_workspace.argtypes = [_i64, _i64, _i32, _i32]
+_lib.csa_index_topk.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _IdxKeys, _i32, _i64, _i32, _vp, _vp, _sz,
+                                _vp]
 _lib.csa_topk_workspace.restype = _sz
 _lib.csa_topk_workspace.argtypes = [_i64, _i64, _i32]
 _lib.csa_topk.argtypes = [_vp, _i64, _i64, _vp, _i32, _i32, _vp, _vp, _sz, ctypes.c_uint32, _vp]
@@ -57,7 +61,7 @@ _lib.csa_mqa_bwd.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _i32, _
 _lib.csa_last_error.restype = ctypes.c_char_p
 _lib.csa_version.restype = ctypes.c_int
 
-EXPORTS = ["csa_compress", "csa_compress_channel", "csa_compress_index_keys", "csa_index_scores", "csa_index_scores_grouped", "csa_topk_workspace", "csa_topk", "csa_topk_noalloc", "csa_mqa_workspace",
+EXPORTS = ["csa_compress", "csa_compress_channel", "csa_compress_index_keys", "csa_index_scores", "csa_index_scores_grouped", "csa_index_topk_workspace", "csa_index_topk", "csa_topk_workspace", "csa_topk", "csa_topk_noalloc", "csa_mqa_workspace",
            "csa_sparse_mqa", "hca_dense_mqa", "csa_mqa_bwd", "csa_last_error", "csa_version"]
 
 
@@ -243,6 +247,37 @@ def csa_index_scores_grouped(q, q_scale, w, seq, pos, keys, m, n_cols, group, ou
     _check(_lib.csa_index_scores_grouped(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(seq), _ptr(pos), T, h_i, d_i, keys.c(),
                                          int(m), int(n_cols), int(group), _ptr(out), _ptr(topk_ws),
                                          topk_ws.numel() if topk_ws is not None else 0, _stream()))
+    return out
+
+
+def csa_index_topk_workspace(T, n_cols, k, h_i):
+    return int(_lib.csa_index_topk_workspace(int(T), int(n_cols), int(k), int(h_i)))
+
+
+def csa_index_topk(q, q_scale, w, seq, pos, keys, m, n_cols, k, out=None, ws=None):
+    """Indexer + top-k without score rows -> int32 [T, k] (what csa_index_scores + csa_topk give).
+
+    ws: a uint8 workspace of csa_index_topk_workspace(T, n_cols, k, h_i) bytes (allocated when None)."""
+    _need(q, "q", torch.uint8, 3)
+    _need(q_scale, "q_scale", torch.uint8, 3)
+    _need(w, "w", torch.float32, 2)
+    _need(seq, "seq", torch.int32, 1)
+    _need(pos, "pos", torch.int64, 1)
+    T, h_i, half = q.shape
+    d_i = half * 2
+    if d_i != keys.d_i or tuple(q_scale.shape) != (T, h_i, d_i // 32) or tuple(w.shape) != (T, h_i):
+        raise ValueError("indexer query shapes disagree")
+    if seq.shape[0] != T or pos.shape[0] != T:
+        raise ValueError("seq / pos must have T entries")
+    if out is None:
+        out = torch.empty(T, k, dtype=torch.int32, device=q.device)
+    _need(out, "idx", torch.int32, 2)
+    if tuple(out.shape) != (T, k):
+        raise ValueError("idx must be [T, k]")
+    if ws is None:
+        ws = torch.empty(max(csa_index_topk_workspace(T, n_cols, k, h_i), 1), dtype=torch.uint8, device=q.device)
+    _check(_lib.csa_index_topk(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(seq), _ptr(pos), T, h_i, d_i, keys.c(),
+                               int(m), int(n_cols), int(k), _ptr(out), _ptr(ws), ws.numel(), _stream()))
     return out
 
 

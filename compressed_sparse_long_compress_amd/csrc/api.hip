@@ -245,6 +245,38 @@ int csa_index_scores_grouped(const uint8_t* q, const uint8_t* q_scale, const flo
     return hip_status(e, fn);
 }
 
+size_t csa_index_topk_workspace(int64_t T, int64_t n_cols, int32_t k, int32_t h_i) {
+    if (T <= 0 || n_cols <= 0 || k < 1 || k > 2048 || (h_i != 4 && h_i != 8)) return 0;
+    return csa::index_topk_workspace_bytes(T, n_cols, k, h_i);
+}
+
+int csa_index_topk(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq, const int64_t* pos,
+                   int64_t T, int32_t h_i, int32_t d_i, csa_index_keys_t keys, int32_t m, int64_t n_cols, int32_t k,
+                   int32_t* idx, void* ws, size_t ws_bytes, csa_stream_t stream) {
+    const char* fn = "csa_index_topk";
+    uint32_t* gmax;
+    bool nothing;
+    if (k < 1 || k > 2048) return fail(CSA_EUNSUPPORTED, "%s: k=%d outside 1..2048", fn, k);
+    if (n_cols >= ((int64_t)1 << 31)) return fail(CSA_EUNSUPPORTED, "%s: n_cols must be < 2^31", fn);
+    // same argument rules as csa_index_scores (no score row: a non-null dummy stands for it)
+    const int rc = index_args(fn, q, q_scale, w, seq, pos, T, h_i, d_i, keys, m, n_cols, (const float*)idx, nullptr, 0,
+                              &gmax, &nothing);
+    if (rc != CSA_OK) return rc;
+    if (T == 0) return ok();
+    if (!idx) return fail(CSA_EINVAL, "%s: null idx", fn);
+    if (n_cols == 0) {
+        // nothing visible: every row is padding (a tiny launch of the selection does it)
+        return fail(CSA_EINVAL, "%s: n_cols must be >= 1", fn);
+    }
+    const size_t need = csa::index_topk_workspace_bytes(T, n_cols, k, h_i);
+    if (ws_bytes < need || !ws)
+        return fail(CSA_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+    if (((uintptr_t)ws & 255u) != 0) return fail(CSA_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+    hipError_t e = csa::launch_index_topk(q, q_scale, w, seq, pos, T, h_i, d_i, keys.data, keys.scale, keys.cap, m,
+                                          n_cols, k, idx, ws, (hipStream_t)stream);
+    return hip_status(e, fn);
+}
+
 size_t csa_topk_workspace(int64_t T, int64_t n_cols, int32_t k) { return csa::topk_workspace_bytes(T, n_cols, k); }
 
 int csa_topk(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos, int32_t m, int32_t k, int32_t* idx,

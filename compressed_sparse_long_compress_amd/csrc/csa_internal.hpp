@@ -60,6 +60,13 @@ hipError_t launch_index_scores_grouped(const uint8_t* q, const uint8_t* q_scale,
                                        const uint8_t* kscale, int64_t kcap, int m, int64_t n_cols, int group,
                                        float* scores, uint32_t* gmax, hipStream_t st);
 
+// fused indexer + top-k (no score row written): workspace and launch
+size_t index_topk_workspace_bytes(int64_t T, int64_t n_cols, int k, int h_i);
+hipError_t launch_index_topk(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
+                             const int64_t* pos, int64_t T, int h_i, int d_i, const uint8_t* kdata,
+                             const uint8_t* kscale, int64_t kcap, int m, int64_t n_cols, int k, int32_t* idx, void* ws,
+                             hipStream_t st);
+
 size_t topk_workspace_bytes(int64_t T, int64_t n_cols, int k);
 // true when the top-k for this shape uses the row summaries (few long rows)
 bool topk_uses_summary(int64_t T, int64_t n_cols);

@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define CSA_VERSION 103
+#define CSA_VERSION 104
 
 enum {
     CSA_OK = 0,
@@ -228,6 +228,33 @@ int csa_index_scores_grouped(const uint8_t* q, const uint8_t* q_scale, const flo
                              const int64_t* pos, int64_t T, int32_t h_i, int32_t d_i, csa_index_keys_t keys,
                              int32_t m, int64_t n_cols, int32_t group, float* scores, void* topk_ws,
                              size_t topk_ws_bytes, csa_stream_t stream);
+
+/*
+ * csa_index_topk — the indexer and the top-k selection fused, without
+ * writing the score rows ([xmsumi] § CSA: the indexer ranks the compressed
+ * entries per query token and only the top-k are kept; [hortopato] CSA list:
+ * k = 1024).  idx receives what csa_index_scores followed by csa_topk would
+ * give (same arguments, same order rule and padding), bit for bit under the
+ * indexer's exactness precondition.
+ *
+ * How: the indexer scores a sample of each row (all of its first
+ * max(2048, 2k) columns, then one 32-column group in 16) and a per-row
+ * threshold is set where the sample predicts about 2k columns above it; a
+ * second indexer pass emits only the columns whose score reaches the
+ * threshold, and the exact top-k is taken among them.  The count is verified:
+ * a row with fewer than k such columns, or more than its candidate space, is
+ * scored again on its own and selected over the whole row (correct, slower).
+ *   idx        [T][k] int32 (written)
+ *   1 <= k <= 2048;  n_cols >= 1;  h_i in {4, 8};  d_i in {64, 128}
+ * Workspace: csa_index_topk_workspace(T, n_cols, k, h_i) bytes, 256-byte
+ * aligned, contents need no initialisation; calls sharing it must not run
+ * concurrently.  It holds the sample keys, the candidates (a few times k per
+ * row) and 16 scratch rows of n_cols floats for re-scored rows.
+ */
+size_t csa_index_topk_workspace(int64_t T, int64_t n_cols, int32_t k, int32_t h_i);
+int csa_index_topk(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq, const int64_t* pos,
+                   int64_t T, int32_t h_i, int32_t d_i, csa_index_keys_t keys, int32_t m, int64_t n_cols, int32_t k,
+                   int32_t* idx, void* ws, size_t ws_bytes, csa_stream_t stream);
 
 /*
  * csa_topk — top-k selection ([xmsumi] § CSA: the top-k compressed entries

@@ -62,6 +62,10 @@ def test_csa_decode_full(lib, orc, name):
     ref_i = orc.topk(ref_s, wl["pos"], wl["m"], wl["k"])
     got_i = ds.idx.cpu().numpy()
     assert np.array_equal(got_i, ref_i), "top-k differs"
+    # the fused indexer + top-k (no score rows) on the same batch
+    fused = lib.csa_index_topk(ds.iq, ds.iqs, ds.w, ds.seq, ds.pos, ds.keys[0], wl["m"], wl["n_cols"], wl["k"])
+    torch.cuda.synchronize()
+    assert np.array_equal(fused.cpu().numpy(), ref_i), "fused index + top-k differs"
     if name == "csa_decode_1m":
         # the planted 5% dominate the selection (the structure makes top-k non-uniform)
         planted = wl["planted"].reshape(wl["B"], wl["N"])
@@ -154,6 +158,12 @@ def test_prefill_chunk_sampled(lib, orc):
     bad = np.where((all_i != got_idx).any(axis=1))[0]
     assert bad.size == 0, f"top-k differs on {bad.size} rows, first {bad[:5].tolist()}"
     del all_i
+    # the fused indexer + top-k (no score rows): the same indices on every row
+    fused = lib.csa_index_topk(dev.t(wl["iq"][0]), dev.t(wl["iq"][1]), dev.t(wl["w"]), seq, pos,
+                               dev.index_keys(wl["keys"], wl["N"]), m, wl["n_cols"], k)
+    torch.cuda.synchronize()
+    bad = np.where((fused.cpu().numpy() != got_idx).any(axis=1))[0]
+    assert bad.size == 0, f"fused index + top-k differs on {bad.size} rows, first {bad[:5].tolist()}"
     ref_o, ref_l = orc.attend(sub(wl["q"]), sub(wl["seq"]), sub(wl["pos"]), o_comp, wl["comp_cap"], o_win, wcap, W, m,
                               wl["sm_scale"], wl["rope_base"], idx=ref_i)
     _close(out.cpu().numpy()[rows], lse.cpu().numpy()[rows], ref_o, ref_l, "prefill sparse")

@@ -981,3 +981,107 @@ def test_debug_check_rejects_rope_beyond_fp16(lib, dev, gen, orc, monkeypatch):
     monkeypatch.setenv("CSA_DEBUG_CHECKS", "0")
     lib.csa_sparse_mqa(dev.bf16(q), dev.t(seq), dev.t(pos), dev.t(with_5), m, kvc, kvw, W, sm)  # not checked
     torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------
+# csa_index_topk: indexer + top-k fused, no score rows written
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("T,h_i,d_i,N,B,m,n_cols,k,mode,plant", [
+    (4, 8, 128, 70000, 4, 4, 70000, 1024, "decode", 0.05),     # rows kernel, long rows
+    (4, 8, 128, 262144, 4, 4, 262144, 1024, "decode", 0.05),   # the 1M-context decode shape
+    (3, 8, 128, 5000, 3, 4, 4990, 512, "decode", 0.0),
+    (8, 8, 128, 100000, 8, 4, 100000, 2048, "decode", 0.02),
+    (5, 4, 64, 3000, 2, 4, 3000, 1, "decode", 0.0),
+    (6, 8, 128, 20000, 3, 4, 20000, 64, "short", 0.0),        # some rows see fewer than k columns
+    (2048, 4, 64, 512, 1, 4, 512, 64, "prefill", 0.0),        # the small prefill shape (matrix-core GEMM)
+    (300, 8, 128, 3000, 1, 4, 3000, 1024, "prefill", 0.0),
+    (200, 8, 128, 9000, 3, 4, 9000, 256, "mixed", 0.0),       # several sequences in a tile
+    (130, 8, 128, 40000, 1, 4, 40000, 1024, "prefill", 0.05),
+    (100, 8, 64, 5000, 1, 4, 5000, 2048, "prefill", 0.0),
+])
+def test_index_topk_bit_exact(lib, dev, gen, orc, T, h_i, d_i, N, B, m, n_cols, k, mode, plant):
+    import torch
+
+    _say(f"index_topk T={T} h_i={h_i} d_i={d_i} N={N} k={k} {mode}")
+    rng = np.random.default_rng(T + N + k)
+    if mode == "decode":
+        seq = np.arange(T) % B
+        pos = np.full(T, m * N - 1, np.int64)
+        pos[-1] = m * N - 5
+    elif mode == "short":
+        seq = np.arange(T) % B
+        pos = rng.integers(0, m * N, size=T)
+        pos[0] = m * 100 + 3
+    elif mode == "prefill":
+        seq = np.zeros(T, np.int64)
+        pos = np.sort(rng.integers(0, m * N, size=T))
+        pos[-1] = m * N - 1
+    else:
+        seq = rng.integers(0, B, size=T)
+        pos = rng.integers(0, m * N, size=T)
+    qd, qs, w, seq, pos, kd, ks = _index_case(gen, 950 + T + k, T, h_i, d_i, N, B, pos, seq, plant=plant)
+    wit = orc.index_exact_witness(qd, qs, w, seq, pos, kd, ks, N, m, n_cols)
+    assert wit < 24, f"inputs break the fp32 exactness precondition ({wit:.1f} bits)"
+    ref = orc.topk(orc.index_scores(qd, qs, w, seq, pos, kd, ks, N, m, n_cols).astype(np.float32), pos, m, k)
+    keys = dev.index_keys((kd, ks), N)
+    args = (dev.t(qd), dev.t(qs), dev.t(w), dev.t(seq), dev.t(pos), keys, m, n_cols)
+    ws = torch.full((lib.csa_index_topk_workspace(T, n_cols, k, h_i),), 0x5A, dtype=torch.uint8, device="cuda")
+    got = lib.csa_index_topk(*args, k, ws=ws)
+    again = lib.csa_index_topk(*args, k, ws=ws)  # the workspace needs no initialisation between calls
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    bad = np.where((got != ref).any(axis=1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first {bad[:5].tolist()}"
+    assert np.array_equal(again.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("T,N,B,k,layout", [
+    (3, 20000, 3, 1024, "decode"),
+    (100, 6000, 1, 512, "prefill"),
+])
+def test_index_topk_fallback_equal_scores(lib, dev, gen, orc, T, N, B, k, layout):
+    """Every key identical: each row's scores are all equal, so every visible column reaches
+    the threshold, the candidate space overflows and each row is scored again and selected
+    over the whole row: the k lowest visible columns."""
+    import torch
+
+    _say(f"index_topk fallback, equal scores T={T} N={N} k={k} {layout}")
+    m, h_i, d_i = 4, 8, 128
+    rng = np.random.default_rng(31)
+    seq = (np.arange(T) % B).astype(np.int32)
+    pos = rng.integers(m * 2000, m * N, size=T).astype(np.int64) if layout == "prefill" else \
+        np.full(T, m * N - 1, np.int64)
+    qd, qs, w, seq, pos, _, _ = _index_case(gen, 960, T, h_i, d_i, N, B, pos, seq)
+    kd = np.full((B * N, d_i // 2), 0x22, np.uint8)
+    ks = np.full((B * N, d_i // 32), 127, np.uint8)
+    ref = orc.topk(orc.index_scores(qd, qs, w, seq, pos, kd, ks, N, m, N).astype(np.float32), pos, m, k)
+    got = lib.csa_index_topk(dev.t(qd), dev.t(qs), dev.t(w), dev.t(seq), dev.t(pos), dev.index_keys((kd, ks), N), m,
+                             N, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+def test_index_topk_fallback_too_few(lib, dev, gen, orc):
+    """High scores planted only in sampled column groups after the sampled prefix (the prefix
+    is 2,048 columns at k <= 1024, then one 32-column group in 16): the sample predicts far more
+    high columns than there are, fewer than k columns reach the threshold, and the rows are
+    scored again and selected over the whole row."""
+    import torch
+
+    _say("index_topk fallback, too few candidates")
+    T, B, N, m, k, h_i, d_i = 2, 2, 70000, 4, 1024, 8, 128
+    seq = np.arange(T, dtype=np.int32)
+    pos = np.full(T, m * N - 1, np.int64)
+    qd, qs, w, seq, pos, kd, ks = _index_case(gen, 970, T, h_i, d_i, N, B, pos, seq)
+    kd, ks = kd.copy(), ks.copy()
+    cols = np.concatenate([2048 + 512 * g + np.arange(32) for g in range(8)])  # 8 sampled groups
+    for b in range(B):
+        kd[b * N + cols] = qd[b, 0]   # aligned with head 0 of the row's query: large scores
+        ks[b * N + cols] = qs[b, 0]
+    sc = orc.index_scores(qd, qs, w, seq, pos, kd, ks, N, m, N)
+    assert np.all(np.sort(sc, axis=1)[:, -256] > np.sort(sc, axis=1)[:, -257])  # the planted 256 lead each row
+    ref = orc.topk(sc.astype(np.float32), pos, m, k)
+    got = lib.csa_index_topk(dev.t(qd), dev.t(qs), dev.t(w), dev.t(seq), dev.t(pos), dev.index_keys((kd, ks), N), m,
+                             N, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), ref)

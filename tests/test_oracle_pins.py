@@ -754,3 +754,111 @@ def test_bwd_batch_accumulates_every_row(orc, gen):
         acc_w += dw
     assert np.allclose(dcb, acc_c, rtol=1e-12, atol=1e-12) and np.allclose(dwb, acc_w, rtol=1e-12, atol=1e-12)
     assert np.array_equal(dqb, dq[keep])
+
+
+# --------------------------------------------------------------------------
+# indexer backward (oracle/index_backward.py)
+# --------------------------------------------------------------------------
+def _ibw():
+    from oracle import index_backward
+
+    return index_backward
+
+
+def test_index_bwd_forward_core_matches_oracle(orc, gen):
+    """The fp64 forward on dequantised values equals oracle.index_scores on the MXFP4 inputs."""
+    ib = _ibw()
+    T, h_i, d_i, N, B, m = 5, 8, 128, 300, 2, 4
+    kd, ks, _ = gen.mxfp4(41, 1, B * N, d_i)
+    qd, qs, _ = gen.mxfp4(41, 2, T * h_i, d_i)
+    w = gen.pow2_weights(41, 3, (T, h_i))
+    seq = np.array([0, 1, 0, 1, 1], np.int32)
+    pos = np.array([1199, 700, 4, 1000, 3], np.int64)
+    ref = orc.index_scores(qd.reshape(T, h_i, -1), qs.reshape(T, h_i, -1), w, seq, pos, kd, ks, N, m, N)
+    qv = ib.dequant_mxfp4(qd, qs).reshape(T, h_i, d_i)
+    got = ib.index_scores_f64(qv, w, ib.dequant_mxfp4(kd, ks), seq, pos, N, m, N)
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    fin = np.isfinite(ref)
+    assert np.max(np.abs(got[fin] - ref[fin])) <= 1e-12 * np.max(np.abs(ref[fin]))
+
+
+def test_index_bwd_matches_central_differences():
+    """Every gradient element against central differences of L = sum G * score[idx] (continuous
+    fp64 inputs; entries whose dot products sit within 1e-3 of the ReLU kink are excluded)."""
+    ib = _ibw()
+    rng = np.random.default_rng(42)
+    T, h, d, N, B, m, k = 3, 4, 32, 12, 2, 1, 5
+    qv = rng.standard_normal((T, h, d))
+    kv = rng.standard_normal((B * N, d))
+    w = rng.uniform(0.5, 2.0, (T, h))
+    seq = np.array([0, 1, 0], np.int32)
+    pos = np.array([N - 1, N - 1, 6], np.int64)
+    idx = np.stack([rng.choice(N, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    idx[2, 0] = 9          # not visible at pos 6: ignored
+    idx[1, 3] = -1         # padding: ignored
+    G = rng.standard_normal((T, k))
+
+    def loss(qv_, w_, kv_):
+        s = ib.index_scores_f64(qv_, w_, kv_, seq, pos, N, m, N)
+        tot = 0.0
+        for t in range(T):
+            for a in range(k):
+                j = idx[t, a]
+                if 0 <= j < (pos[t] + 1) // m:
+                    tot += G[t, a] * s[t, j]
+        return tot
+
+    for t in range(T):  # keep every used dot product away from the kink
+        for a in range(k):
+            j = idx[t, a]
+            if 0 <= j < (pos[t] + 1) // m:
+                dots = qv[t] @ kv[seq[t] * N + j]
+                assert np.all(np.abs(dots) > 1e-3)
+    dq, dw, dk = ib.index_bwd_f64(qv, w, kv, seq, pos, N, m, idx, G)
+    eps = 1e-6
+    for arr, grad in ((qv, dq), (w, dw), (kv, dk)):
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            old = arr[i]
+            arr[i] = old + eps
+            lp = loss(qv, w, kv)
+            arr[i] = old - eps
+            lm = loss(qv, w, kv)
+            arr[i] = old
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - grad[i]) <= 1e-6 * max(1.0, abs(fd)), f"{i}: {fd} vs {grad[i]}"
+
+
+def test_index_bwd_closed_forms():
+    """One head, unit weight, one selected key: with <q, k> > 0, dq = G k, dk = G q and
+    dw = G <q, k>; with <q, k> < 0 every gradient is zero; scaling w scales dq and dk."""
+    ib = _ibw()
+    q = np.array([[[1.0, 2.0, -0.5, 0.25]]])
+    kv = np.array([[0.5, 1.0, 1.0, -2.0]])  # <q, k> = 0.5 + 2 - 0.5 - 0.5 = 1.5
+    seq, pos = np.zeros(1, np.int32), np.zeros(1, np.int64)
+    idx, G = np.zeros((1, 1), np.int32), np.array([[3.0]])
+    dq, dw, dk = ib.index_bwd_f64(q, np.ones((1, 1)), kv, seq, pos, 1, 1, idx, G)
+    assert np.array_equal(dq[0, 0], 3.0 * kv[0]) and np.array_equal(dk[0], 3.0 * q[0, 0]) and dw[0, 0] == 4.5
+    dq2, dw2, dk2 = ib.index_bwd_f64(q, np.full((1, 1), 0.25), kv, seq, pos, 1, 1, idx, G)
+    assert np.array_equal(dq2, 0.25 * dq) and np.array_equal(dk2, 0.25 * dk) and dw2[0, 0] == dw[0, 0]
+    dq3, dw3, dk3 = ib.index_bwd_f64(-q, np.ones((1, 1)), kv, seq, pos, 1, 1, idx, G)
+    assert not dq3.any() and not dw3.any() and not dk3.any()
+
+
+def test_index_bwd_rows_accumulate(gen):
+    """Rows selecting the same key: its gradient is the sum of each row's alone."""
+    ib = _ibw()
+    rng = np.random.default_rng(43)
+    T, h, d, N = 4, 8, 64, 20
+    qv = rng.standard_normal((T, h, d))
+    kv = rng.standard_normal((N, d))
+    w = rng.uniform(0.1, 1.0, (T, h))
+    seq, pos = np.zeros(T, np.int32), np.full(T, N - 1, np.int64)
+    idx = np.tile(np.array([[3, 7, 11]], np.int32), (T, 1))
+    G = rng.standard_normal((T, 3))
+    _, _, dk = ib.index_bwd_f64(qv, w, kv, seq, pos, N, 1, idx, G)
+    want = sum(ib.index_bwd_f64(qv[t:t + 1], w[t:t + 1], kv, seq[:1], pos[:1], N, 1, idx[:1], G[t:t + 1])[2]
+               for t in range(T))
+    assert np.allclose(dk, want, rtol=1e-13, atol=1e-13)
+    assert not dk[[0, 1, 2, 4, 19]].any()

@@ -45,6 +45,10 @@ _lib.csa_index_topk_workspace.restype = _sz
 _lib.csa_index_topk_workspace.argtypes = [_i64, _i64, _i32, _i32]
 _lib.csa_index_topk.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _IdxKeys, _i32, _i64, _i32, _vp, _vp, _sz,
                                 _vp]
+_lib.csa_index_bwd_workspace.restype = _sz
+_lib.csa_index_bwd_workspace.argtypes = [_i64, _i32]
+_lib.csa_index_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _IdxKeys, _i32, _vp, _vp, _i32, _vp, _vp, _vp,
+                               _i64, _vp, _sz, _vp]
 _lib.csa_topk_workspace.restype = _sz
 _lib.csa_topk_workspace.argtypes = [_i64, _i64, _i32]
 _lib.csa_topk.argtypes = [_vp, _i64, _i64, _vp, _i32, _i32, _vp, _vp, _sz, ctypes.c_uint32, _vp]
@@ -61,7 +65,8 @@ _lib.csa_mqa_bwd.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _i32, _
 _lib.csa_last_error.restype = ctypes.c_char_p
 _lib.csa_version.restype = ctypes.c_int
 
-EXPORTS = ["csa_compress", "csa_compress_channel", "csa_compress_index_keys", "csa_index_scores", "csa_index_scores_grouped", "csa_index_topk_workspace", "csa_index_topk", "csa_topk_workspace", "csa_topk", "csa_topk_noalloc", "csa_mqa_workspace",
+EXPORTS = ["csa_compress", "csa_compress_channel", "csa_compress_index_keys", "csa_index_scores", "csa_index_scores_grouped", "csa_index_topk_workspace", "csa_index_topk", "csa_index_bwd_workspace",
+           "csa_index_bwd", "csa_topk_workspace", "csa_topk", "csa_topk_noalloc", "csa_mqa_workspace",
            "csa_sparse_mqa", "hca_dense_mqa", "csa_mqa_bwd", "csa_last_error", "csa_version"]
 
 
@@ -279,6 +284,44 @@ def csa_index_topk(q, q_scale, w, seq, pos, keys, m, n_cols, k, out=None, ws=Non
     _check(_lib.csa_index_topk(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(seq), _ptr(pos), T, h_i, d_i, keys.c(),
                                int(m), int(n_cols), int(k), _ptr(out), _ptr(ws), ws.numel(), _stream()))
     return out
+
+
+def csa_index_bwd(q, q_scale, w, seq, pos, keys, m, idx, g, key_rows=None, dkeys=None, ws=None):
+    """Gradient of the indexer scores at the selected columns idx [T, n_sel] given g = dL/dscore there
+    -> (dq fp32 [T, h_i, d_i], dw fp32 [T, h_i], dkeys fp32 [key_rows, d_i]); dkeys is accumulated into
+    when given (zeros otherwise)."""
+    _need(q, "q", torch.uint8, 3)
+    _need(q_scale, "q_scale", torch.uint8, 3)
+    _need(w, "w", torch.float32, 2)
+    _need(seq, "seq", torch.int32, 1)
+    _need(pos, "pos", torch.int64, 1)
+    _need(idx, "idx", torch.int32, 2)
+    _need(g, "g", torch.float32, 2)
+    T, h_i, half = q.shape
+    d_i = half * 2
+    if d_i != keys.d_i or tuple(q_scale.shape) != (T, h_i, d_i // 32) or tuple(w.shape) != (T, h_i):
+        raise ValueError("indexer query shapes disagree")
+    if idx.shape[0] != T or tuple(g.shape) != tuple(idx.shape):
+        raise ValueError("idx and g must be [T, n_sel]")
+    if key_rows is None:
+        key_rows = keys.data.shape[0]
+    dq = torch.empty(T, h_i, d_i, dtype=torch.float32, device=q.device)
+    dw = torch.empty(T, h_i, dtype=torch.float32, device=q.device)
+    if dkeys is None:
+        dkeys = torch.zeros(key_rows, d_i, dtype=torch.float32, device=q.device)
+    _need(dkeys, "dkeys", torch.float32, 2)
+    if tuple(dkeys.shape) != (key_rows, d_i):
+        raise ValueError("dkeys must be [key_rows, d_i]")
+    if ws is None:
+        ws = torch.empty(csa_index_bwd_workspace(key_rows, d_i), dtype=torch.uint8, device=q.device)
+    _check(_lib.csa_index_bwd(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(seq), _ptr(pos), T, h_i, d_i, keys.c(), int(m),
+                              _ptr(idx), _ptr(g), int(idx.shape[1]), _ptr(dq), _ptr(dw), _ptr(dkeys), int(key_rows),
+                              _ptr(ws), ws.numel(), _stream()))
+    return dq, dw, dkeys
+
+
+def csa_index_bwd_workspace(key_rows, d_i):
+    return int(_lib.csa_index_bwd_workspace(int(key_rows), int(d_i)))
 
 
 def csa_topk_workspace(T, n_cols, k):

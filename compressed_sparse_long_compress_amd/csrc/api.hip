@@ -277,6 +277,35 @@ int csa_index_topk(const uint8_t* q, const uint8_t* q_scale, const float* w, con
     return hip_status(e, fn);
 }
 
+size_t csa_index_bwd_workspace(int64_t key_rows, int32_t d_i) {
+    if (key_rows <= 0 || (d_i != 64 && d_i != 128)) return 0;
+    return (size_t)key_rows * d_i * 8;
+}
+
+int csa_index_bwd(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq, const int64_t* pos,
+                  int64_t T, int32_t h_i, int32_t d_i, csa_index_keys_t keys, int32_t m, const int32_t* idx,
+                  const float* g, int32_t n_sel, float* dq, float* dw, float* dkeys, int64_t key_rows, void* ws,
+                  size_t ws_bytes, csa_stream_t stream) {
+    const char* fn = "csa_index_bwd";
+    if (T < 0) return fail(CSA_EINVAL, "%s: T must be >= 0", fn);
+    if (h_i != 4 && h_i != 8) return fail(CSA_EUNSUPPORTED, "%s: h_i=%d unsupported (4 or 8)", fn, h_i);
+    if (d_i != 64 && d_i != 128) return fail(CSA_EUNSUPPORTED, "%s: d_i=%d unsupported (64 or 128)", fn, d_i);
+    if (m < 1) return fail(CSA_EINVAL, "%s: m must be >= 1", fn);
+    if (n_sel < 1) return fail(CSA_EINVAL, "%s: n_sel must be >= 1", fn);
+    if (key_rows < 1) return fail(CSA_EINVAL, "%s: key_rows must be >= 1", fn);
+    if (T == 0) return ok();
+    if (!q || !q_scale || !w || !seq || !pos || !keys.data || !keys.scale || !idx || !g || !dq || !dw || !dkeys)
+        return fail(CSA_EINVAL, "%s: null pointer argument", fn);
+    if (keys.cap < 1) return fail(CSA_EINVAL, "%s: keys.cap must be >= 1", fn);
+    const size_t need = csa_index_bwd_workspace(key_rows, d_i);
+    if (ws_bytes < need || !ws)
+        return fail(CSA_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+    if (((uintptr_t)ws & 7u) != 0) return fail(CSA_EINVAL, "%s: workspace must be 8-byte aligned", fn);
+    hipError_t e = csa::launch_index_bwd(q, q_scale, w, seq, pos, T, h_i, d_i, keys.data, keys.scale, keys.cap, m, idx,
+                                         g, n_sel, dq, dw, dkeys, key_rows, ws, (hipStream_t)stream);
+    return hip_status(e, fn);
+}
+
 size_t csa_topk_workspace(int64_t T, int64_t n_cols, int32_t k) { return csa::topk_workspace_bytes(T, n_cols, k); }
 
 int csa_topk(const float* scores, int64_t T, int64_t n_cols, const int64_t* pos, int32_t m, int32_t k, int32_t* idx,

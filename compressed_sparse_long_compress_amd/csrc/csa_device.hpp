@@ -77,6 +77,15 @@ __device__ __forceinline__ void rope_cs(double pos, double base, int i, float& c
     s = (float)sn;
 }
 
+// Gradient sums that must not depend on the order of their terms (several rows or heads adding
+// into one entry's gradient) accumulate in 64-bit fixed point: units of 2^-40, range +-2^23.
+// Each term is rounded once to the nearest unit; integer addition is associative, so the sum
+// is the same bits whatever order the atomics land in.
+constexpr double kFxUnit = 1099511627776.0;  // 2^40 units per 1.0
+__device__ __forceinline__ void fx_add(unsigned long long* p, float v) {
+    atomicAdd(p, (unsigned long long)__double2ll_rn((double)v * kFxUnit));
+}
+
 // Order-preserving map float -> u32 (larger float, larger key); -0 maps like +0.
 __device__ __forceinline__ uint32_t f32_order_key(float f) {
     uint32_t b = __float_as_uint(f);

@@ -81,6 +81,16 @@ hipError_t launch_topk_noalloc(const float* scores, int64_t T, int64_t n_cols, c
 
 
 
+// 64-bit fixed-point gradient buffers (fx_add): clear n words; dst[i] += src[i] * 2^-40
+hipError_t launch_fx_zero(unsigned long long* p, int64_t n, hipStream_t st);
+hipError_t launch_fx_flush(const unsigned long long* src, float* dst, int64_t n, hipStream_t st);
+
+// gradient of the indexer scores at the selected columns; ws: key_rows x d_i x 8 bytes
+hipError_t launch_index_bwd(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
+                            const int64_t* pos, int64_t T, int h_i, int d_i, const uint8_t* kdata,
+                            const uint8_t* kscale, int64_t kcap, int m, const int32_t* idx, const float* g, int n_sel,
+                            float* dq, float* dw, float* dkeys, int64_t key_rows, void* ws, hipStream_t st);
+
 size_t mqa_workspace_bytes(int64_t T, int H, int d, int64_t max_keys);
 // idx == nullptr selects the dense (HCA) key set
 hipError_t launch_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int H, int d,

@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define CSA_VERSION 104
+#define CSA_VERSION 105
 
 enum {
     CSA_OK = 0,
@@ -255,6 +255,38 @@ size_t csa_index_topk_workspace(int64_t T, int64_t n_cols, int32_t k, int32_t h_
 int csa_index_topk(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq, const int64_t* pos,
                    int64_t T, int32_t h_i, int32_t d_i, csa_index_keys_t keys, int32_t m, int64_t n_cols, int32_t k,
                    int32_t* idx, void* ws, size_t ws_bytes, csa_stream_t stream);
+
+/*
+ * csa_index_bwd — gradient of the lightning-indexer scores (training side:
+ * the pages warm the indexer up and train its QK path in FP4, [xmsumi]
+ * § 预训练：32T Token 炼就基座 and [hortopato]'s training section; no page
+ * gives the gradient, so this is the exact derivative of csa_index_scores).
+ * Given G = dL/dscore at the selected columns j = idx[t][a] (entries with
+ * j < 0 or j >= (pos[t]+1)/m are ignored), with dot_h = <q[t][h], key_j> and
+ * the ReLU's derivative taken as 0 at 0:
+ *   dq[t][h]  = sum_a G[t][a] w[t][h] [dot_h > 0] key_j
+ *   dw[t][h]  = sum_a G[t][a] max(0, dot_h)
+ *   dkeys[row of key_j] += sum_t sum_a G[t][a] sum_h w[t][h] [dot_h > 0] q[t][h]
+ * with respect to the dequantised MXFP4 values (quantisation passes the
+ * gradient straight through).
+ *   idx, g     [T][n_sel] int32 / fp32 (e.g. csa_topk's indices and the loss's
+ *              gradient at them; any n_sel >= 1)
+ *   dq         [T][h_i][d_i] fp32, dw [T][h_i] fp32: written
+ *   dkeys      [key_rows][d_i] fp32, indexed like the keys (seq * keys.cap + j):
+ *              ACCUMULATED into; every referenced row must be < key_rows
+ * The key gradients are summed in 64-bit fixed point (each term rounded to a
+ * multiple of 2^-40; |partial sums| < 2^23), so dkeys does not depend on the
+ * order the rows' terms arrive in: repeated calls give the same bits.  dq and
+ * dw are summed in a fixed order per row.  The dot products are exact under
+ * csa_index_scores' precondition, so the ReLU decisions match its scores.
+ * Workspace: csa_index_bwd_workspace(key_rows, d_i) bytes, 8-byte aligned
+ * (cleared by the call).  h_i in {4, 8}; d_i in {64, 128}.
+ */
+size_t csa_index_bwd_workspace(int64_t key_rows, int32_t d_i);
+int csa_index_bwd(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq, const int64_t* pos,
+                  int64_t T, int32_t h_i, int32_t d_i, csa_index_keys_t keys, int32_t m, const int32_t* idx,
+                  const float* g, int32_t n_sel, float* dq, float* dw, float* dkeys, int64_t key_rows, void* ws,
+                  size_t ws_bytes, csa_stream_t stream);
 
 /*
  * csa_topk — top-k selection ([xmsumi] § CSA: the top-k compressed entries

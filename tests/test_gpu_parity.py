@@ -1085,3 +1085,53 @@ def test_index_topk_fallback_too_few(lib, dev, gen, orc):
                              N, k)
     torch.cuda.synchronize()
     assert np.array_equal(got.cpu().numpy(), ref)
+
+
+# --------------------------------------------------------------------------
+# csa_index_bwd: gradient of the indexer scores against the fp64 oracle
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("T,h_i,d_i,N,B,m,n_sel,layout", [
+    (6, 8, 128, 3000, 2, 4, 1024, "decode"),     # selected by the library's own top-k
+    (64, 4, 64, 500, 1, 4, 64, "prefill"),       # causal rows of one sequence: keys shared by many rows
+    (3, 8, 128, 5000, 3, 4, 2500, "random"),     # more selected columns than one chunk; -1 and invisible entries
+    (40, 8, 64, 800, 2, 2, 300, "random"),
+])
+def test_index_bwd(lib, dev, gen, orc, T, h_i, d_i, N, B, m, n_sel, layout):
+    import torch
+
+    from oracle import index_backward as ib
+
+    _say(f"index_bwd T={T} h_i={h_i} d_i={d_i} N={N} n_sel={n_sel} {layout}")
+    rng = np.random.default_rng(T + N + n_sel)
+    if layout == "prefill":
+        seq = np.zeros(T, np.int64)
+        pos = np.sort(rng.integers(m * 4, m * N, size=T))
+    else:
+        seq = np.arange(T) % B
+        pos = rng.integers(m * N // 2, m * N, size=T)
+    qd, qs, w, seq, pos, kd, ks = _index_case(gen, 980 + T, T, h_i, d_i, N, B, pos, seq)
+    keys = dev.index_keys((kd, ks), N)
+    tq, tqs, tw, tseq, tpos = dev.t(qd), dev.t(qs), dev.t(w), dev.t(seq), dev.t(pos)
+    if layout in ("decode", "prefill"):
+        idx = lib.csa_topk(lib.csa_index_scores(tq, tqs, tw, tseq, tpos, keys, m, N), tpos, m, n_sel).cpu().numpy()
+    else:
+        idx = rng.integers(-1, N, size=(T, n_sel)).astype(np.int32)
+    G = gen.normal_f32(981 + T, 1, (T, n_sel))
+    rq, rw, rk = ib.index_bwd(qd, qs, w, seq, pos, kd, ks, N, m, idx, G)
+    dq, dw, dk = lib.csa_index_bwd(tq, tqs, tw, tseq, tpos, keys, m, dev.t(idx), dev.t(G))
+    dk2 = lib.csa_index_bwd(tq, tqs, tw, tseq, tpos, keys, m, dev.t(idx), dev.t(G))[2]
+    torch.cuda.synchronize()
+    assert torch.equal(dk, dk2), "key gradients differ between two runs"
+    for got, ref, name in ((dq, rq, "dq"), (dw, rw, "dw"), (dk, rk, "dkeys")):
+        got = got.cpu().numpy().astype(np.float64).reshape(ref.shape)
+        r = rel_rms(got, ref)
+        ma = float(np.max(np.abs(got - ref))) / max(float(np.max(np.abs(ref))), 1e-30)
+        print(f"index_bwd {name}: rel-rms {r:.2e} max-abs/max {ma:.2e}", flush=True)
+        assert r <= 1e-5 and ma <= 1e-5, f"{name}: rel-rms {r:.3e} max-abs/max {ma:.3e}"
+    # key rows no row selected (validly) get no gradient
+    nv = (pos + 1) // m
+    used = np.zeros(B * N, bool)
+    for t in range(T):
+        v = idx[t][(idx[t] >= 0) & (idx[t] < nv[t])]
+        used[seq[t] * N + v] = True
+    assert not dk.cpu().numpy()[~used].any(), "gradient on key rows no row selected"

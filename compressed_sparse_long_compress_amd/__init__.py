@@ -60,14 +60,16 @@ _lib.csa_sparse_mqa.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _i32
                                 _vp, _vp, _sz, _vp]
 _lib.hca_dense_mqa.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _Kv, _Kv, _i32, _f32, _f32, _vp, _vp,
                                _vp, _sz, _vp]
+_lib.csa_mqa_bwd_workspace.restype = _sz
+_lib.csa_mqa_bwd_workspace.argtypes = [_i64, _i64, _i32]
 _lib.csa_mqa_bwd.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _i32, _Kv, _Kv, _i32, _f32, _f32, _vp, _vp,
-                             _vp, _vp, _vp, _vp, _vp]
+                             _vp, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp]
 _lib.csa_last_error.restype = ctypes.c_char_p
 _lib.csa_version.restype = ctypes.c_int
 
 EXPORTS = ["csa_compress", "csa_compress_channel", "csa_compress_index_keys", "csa_index_scores", "csa_index_scores_grouped", "csa_index_topk_workspace", "csa_index_topk", "csa_index_bwd_workspace",
            "csa_index_bwd", "csa_topk_workspace", "csa_topk", "csa_topk_noalloc", "csa_mqa_workspace",
-           "csa_sparse_mqa", "hca_dense_mqa", "csa_mqa_bwd", "csa_last_error", "csa_version"]
+           "csa_sparse_mqa", "hca_dense_mqa", "csa_mqa_bwd_workspace", "csa_mqa_bwd", "csa_last_error", "csa_version"]
 
 
 class CsaError(RuntimeError):
@@ -419,12 +421,17 @@ def hca_dense_mqa(q, seq, pos, m, max_vis, comp, win, window, sm_scale, rope_bas
     return out, lse
 
 
+def csa_mqa_bwd_workspace(comp_rows, win_rows, d):
+    return int(_lib.csa_mqa_bwd_workspace(int(comp_rows), int(win_rows), int(d)))
+
+
 def csa_mqa_bwd(q, seq, pos, idx, m, comp, win, window, sm_scale, out, lse, dout, rope_base=10000.0, dq=None,
-                dcomp=None, dwin=None):
+                dcomp=None, dwin=None, ws=None):
     """Gradient of the attention step -> (dq fp32 [T,H,d], dcomp fp32 [comp rows, d], dwin fp32 [win rows, d]).
 
     idx int32 [T, k] (the selected entries) or None (every visible entry); out / lse are the forward's.
-    dcomp / dwin are accumulated into (fresh zeros when not given; dwin None when window is 0)."""
+    dcomp / dwin are accumulated into (fresh zeros when not given; dwin None when window is 0); their
+    row counts bound the cache rows.  ws: csa_mqa_bwd_workspace bytes (allocated when None)."""
     _need(q, "q", torch.bfloat16, 3)
     _need(seq, "seq", torch.int32, 1)
     _need(pos, "pos", torch.int64, 1)
@@ -442,7 +449,11 @@ def csa_mqa_bwd(q, seq, pos, idx, m, comp, win, window, sm_scale, out, lse, dout
         dcomp = torch.zeros(comp.nope.shape[0], d, dtype=torch.float32, device=q.device)
     if dwin is None and window > 0:
         dwin = torch.zeros(win.nope.shape[0], d, dtype=torch.float32, device=q.device)
+    comp_rows = dcomp.shape[0]
+    win_rows = dwin.shape[0] if (dwin is not None and window > 0) else 0
+    if ws is None:
+        ws = torch.empty(csa_mqa_bwd_workspace(comp_rows, win_rows, d), dtype=torch.uint8, device=q.device)
     _check(_lib.csa_mqa_bwd(_ptr(q), _ptr(seq), _ptr(pos), T, H, d, _ptr(idx), k, int(m), comp.c(), _win(win, comp),
                             int(window), float(sm_scale), float(rope_base), _ptr(out), _ptr(lse), _ptr(dout),
-                            _ptr(dq), _ptr(dcomp), _ptr(dwin), _stream()))
+                            _ptr(dq), _ptr(dcomp), comp_rows, _ptr(dwin), win_rows, _ptr(ws), ws.numel(), _stream()))
     return dq, dcomp, dwin

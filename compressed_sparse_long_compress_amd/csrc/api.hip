@@ -372,10 +372,15 @@ int csa_sparse_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos, in
     return hip_status(e, fn);
 }
 
+size_t csa_mqa_bwd_workspace(int64_t comp_rows, int64_t win_rows, int32_t d) {
+    if (comp_rows < 0 || win_rows < 0 || d != 512) return 0;
+    return (size_t)(comp_rows + win_rows) * d * 8;
+}
+
 int csa_mqa_bwd(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int32_t H, int32_t d,
                 const int32_t* idx, int32_t k, int32_t m, csa_kv_t comp, csa_kv_t win, int32_t window, float sm_scale,
                 float rope_base, const float* out, const float* lse, const float* dout, float* dq, float* dcomp,
-                float* dwin, csa_stream_t stream) {
+                int64_t comp_rows, float* dwin, int64_t win_rows, void* ws, size_t ws_bytes, csa_stream_t stream) {
     const char* fn = "csa_mqa_bwd";
     if (int rc = check_mqa_common(fn, q, seq, pos, T, H, d, m, comp, win, window, dq, (float*)lse)) return rc;
     if (d != 512) return fail(CSA_EUNSUPPORTED, "%s: d=%d unsupported (512)", fn, d);
@@ -384,10 +389,17 @@ int csa_mqa_bwd(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64
     if (T > 0 && (!aligned16(out) || !aligned16(dout))) return fail(CSA_EINVAL, "%s: out and dout must be 16-byte aligned", fn);
     if (idx && (k < 1 || k > 2048)) return fail(CSA_EUNSUPPORTED, "%s: k=%d outside 1..2048", fn, k);
     if (!(rope_base > 0.f)) return fail(CSA_EINVAL, "%s: rope_base must be positive", fn);
+    if (comp_rows < 1 || (window > 0 && win_rows < 1))
+        return fail(CSA_EINVAL, "%s: comp_rows (and win_rows when window > 0) must be >= 1", fn);
     if (T == 0) return ok();
+    const int64_t wr = window > 0 ? win_rows : 0;
+    const size_t need = csa_mqa_bwd_workspace(comp_rows, wr, d);
+    if (ws_bytes < need || !ws)
+        return fail(CSA_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+    if (((uintptr_t)ws & 7u) != 0) return fail(CSA_EINVAL, "%s: workspace must be 8-byte aligned", fn);
     hipError_t e = csa::launch_mqa_bwd(q, seq, pos, T, H, idx, idx ? k : 0, m, view(comp), view(win), window, sm_scale,
-                                       csa::rope_table((double)rope_base), out, lse, dout, dq, dcomp, dwin,
-                                       (hipStream_t)stream);
+                                       csa::rope_table((double)rope_base), out, lse, dout, dq, dcomp, comp_rows, dwin,
+                                       wr, ws, (hipStream_t)stream);
     return hip_status(e, fn);
 }
 

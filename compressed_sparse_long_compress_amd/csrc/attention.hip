@@ -1679,8 +1679,8 @@ __global__ __launch_bounds__(64 * NW) void k_mqa_bwd(const uint16_t* __restrict_
                                                      int k, int m, KvView comp, KvView win, int window,
                                                      float sm_scale, RopeTab rt, const float* __restrict__ out,
                                                      const float* __restrict__ lse, const float* __restrict__ dout,
-                                                     float* __restrict__ dq, float* __restrict__ dcomp,
-                                                     float* __restrict__ dwin) {
+                                                     float* __restrict__ dq, unsigned long long* __restrict__ dcomp,
+                                                     unsigned long long* __restrict__ dwin) {
     constexpr int D = 512, DN = 448, NT = 64 * NW, H = 16 * NW;
     constexpr int DTW = D / NW / 16;                           // 16-dim tiles of de per wave
     constexpr int NCH = (kBwdKT * 36 + NT - 1) / NT;           // staged 16-byte chunks per thread
@@ -1947,9 +1947,9 @@ __global__ __launch_bounds__(64 * NW) void k_mqa_bwd(const uint16_t* __restrict_
             // A masked key adds zero to the row of a valid key of the same lane (else row 0), so
             // every lane issues its atomics without sending many rows' zeros to one hot row; the
             // last tile (ragged; no wait follows it) skips them instead.
-            float* dst[4];
+            unsigned long long* dst[4];
             float mul[4];
-            float* alt = dcomp;
+            unsigned long long* alt = dcomp;
 #pragma unroll
             for (int i = 3; i >= 0; --i) {
                 const int64_t code = sm.krow[b][4 * g4 + i];
@@ -1973,11 +1973,11 @@ __global__ __launch_bounds__(64 * NW) void k_mqa_bwd(const uint16_t* __restrict_
                 }
                 if constexpr (!last) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst[i] + d0 + l16, e[i] * mul[i]);
+                    for (int i = 0; i < 4; ++i) fx_add(dst[i] + d0 + l16, e[i] * mul[i]);
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (mul[i] != 0.f) unsafeAtomicAdd(dst[i] + d0 + l16, e[i] * mul[i]);
+                        if (mul[i] != 0.f) fx_add(dst[i] + d0 + l16, e[i] * mul[i]);
                 }
             }
         };
@@ -2017,16 +2017,27 @@ __global__ __launch_bounds__(64 * NW) void k_mqa_bwd(const uint16_t* __restrict_
 hipError_t launch_mqa_bwd(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int H,
                           const int32_t* idx, int k, int m, KvView comp, KvView win, int window, float sm_scale,
                           const RopeTab& rt, const float* out, const float* lse, const float* dout, float* dq,
-                          float* dcomp, float* dwin, hipStream_t st) {
+                          float* dcomp, int64_t comp_rows, float* dwin, int64_t win_rows, void* ws, hipStream_t st) {
     if (T == 0) return hipSuccess;
+    // entry gradients in 64-bit fixed point (order-independent sums), then added to dcomp / dwin
+    constexpr int D = 512;
+    unsigned long long* fc = (unsigned long long*)ws;
+    unsigned long long* fw = fc + comp_rows * D;
+    const int64_t nw = window > 0 ? win_rows * D : 0;
+    hipError_t e = launch_fx_zero(fc, comp_rows * D, st);
+    if (e == hipSuccess) e = launch_fx_zero(fw, nw, st);
+    if (e != hipSuccess) return e;
 #define CSA_BWD(NW)                                                                                                    \
     hipLaunchKernelGGL(k_mqa_bwd<NW>, dim3((unsigned)T), dim3(64 * (NW)), 0, st, q, seq, pos, idx, k, m, comp, win,  \
-                       window, sm_scale, rt, out, lse, dout, dq, dcomp, dwin)
+                       window, sm_scale, rt, out, lse, dout, dq, fc, fw)
     if (H == 64) CSA_BWD(4);
     else if (H == 32) CSA_BWD(2);
     else CSA_BWD(1);
 #undef CSA_BWD
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (e == hipSuccess) e = launch_fx_flush(fc, dcomp, comp_rows * D, st);
+    if (e == hipSuccess && nw > 0) e = launch_fx_flush(fw, dwin, nw, st);
+    return e;
 }
 
 }  // namespace csa

@@ -79,11 +79,23 @@ __device__ __forceinline__ void rope_cs(double pos, double base, int i, float& c
 
 // Gradient sums that must not depend on the order of their terms (several rows or heads adding
 // into one entry's gradient) accumulate in 64-bit fixed point: units of 2^-40, range +-2^23.
-// Each term is rounded once to the nearest unit; integer addition is associative, so the sum
-// is the same bits whatever order the atomics land in.
+// Each term is rounded once to the nearest unit (ties away from zero); integer addition is
+// associative, so the sum is the same bits whatever order the atomics land in.
 constexpr double kFxUnit = 1099511627776.0;  // 2^40 units per 1.0
+__device__ __forceinline__ long long f32_to_fx(float v) {
+    // v = mant * 2^(ex - 150) for a normal float; times 2^40: mant * 2^(ex - 110), by integer shifts
+    const uint32_t b = __float_as_uint(v);
+    const int ex = (int)((b >> 23) & 0xFFu);
+    const long long mant = (long long)((b & 0x7FFFFFu) | 0x800000u);
+    const int sh = ex - 110;
+    long long r;
+    if (sh >= 0) r = mant << (sh < 39 ? sh : 39);                                   // |v| < 2^23 assumed
+    else r = sh > -25 ? (mant + (1ll << (-sh - 1))) >> (-sh) : 0ll;               // below 2^-41: 0
+    if (ex == 0) r = 0;                                                            // zero, subnormals
+    return (b >> 31) ? -r : r;
+}
 __device__ __forceinline__ void fx_add(unsigned long long* p, float v) {
-    atomicAdd(p, (unsigned long long)__double2ll_rn((double)v * kFxUnit));
+    atomicAdd(p, (unsigned long long)f32_to_fx(v));
 }
 
 // Order-preserving map float -> u32 (larger float, larger key); -0 maps like +0.

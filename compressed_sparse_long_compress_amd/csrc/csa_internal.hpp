@@ -100,9 +100,10 @@ hipError_t launch_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos,
 // bf16 RoPE dim outside the fp16 range (64-head kernels stage those dims as fp16)
 hipError_t launch_check_rope(const int32_t* seq, const int64_t* pos, int64_t T, const int32_t* idx, int k, int m,
                              KvView comp, KvView win, int window, int* bad, hipStream_t st);
+// ws: (comp_rows + win_rows) x 512 x 8 bytes of fixed-point entry gradients
 hipError_t launch_mqa_bwd(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int H,
                           const int32_t* idx, int k, int m, KvView comp, KvView win, int window, float sm_scale,
                           const RopeTab& rt, const float* out, const float* lse, const float* dout, float* dq,
-                          float* dcomp, float* dwin, hipStream_t st);
+                          float* dcomp, int64_t comp_rows, float* dwin, int64_t win_rows, void* ws, hipStream_t st);
 
 }  // namespace csa

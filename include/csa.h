@@ -29,9 +29,9 @@
  *     caller's next synchronisation.
  *   - Shapes are validated on the host; values inside device arrays (seq,
  *     pos, idx) are trusted except where a call documents a check.
- *   - Determinism.  Every forward call is run-to-run deterministic: no
- *     floating-point atomics, fixed reduction orders.  csa_mqa_bwd documents
- *     its own rule.
+ *   - Determinism.  Every call is run-to-run deterministic: no floating-point
+ *     atomics, fixed reduction orders; the backward calls sum shared
+ *     gradients in 64-bit fixed point (order-independent integer sums).
  *   - Batch invariance.  csa_compress* and csa_topk give each row (entry)
  *     the same bits whatever the other rows of the call and T.  So does
  *     csa_index_scores* under its exactness precondition (every score exact
@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define CSA_VERSION 105
+#define CSA_VERSION 106
 
 enum {
     CSA_OK = 0,
@@ -390,21 +390,26 @@ int hca_dense_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos, int
  *
  *   q [T][H][d] bf16, out [T][H][d] fp32, lse [T][H] fp32: the forward's
  *   inputs and outputs; dout [T][H][d] fp32;  dq [T][H][d] fp32 (written)
- *   dcomp [comp rows][d], dwin [win rows][d] fp32: indexed by the same cache
+ *   dcomp [comp_rows][d], dwin [win_rows][d] fp32: indexed by the same cache
  *            row as the entries (seq * cap + slot, or through the page
- *            table); ACCUMULATED into (the caller clears them).  dwin may be
- *            null when window == 0.
+ *            table); ACCUMULATED into (the caller clears them); every row
+ *            an entry of the key sets lives at must be < comp_rows / win_rows.
+ *            dwin may be null (win_rows ignored) when window == 0.
  * H in {16, 32, 64}; d = 512 only; 16-byte aligned q, out, dout, dq.
- * Entries shared by rows and heads are summed with fp32 atomics, so the
- * summation order (and the last bits of dcomp / dwin) varies between runs.
+ * Determinism: entries shared by rows and heads are summed in 64-bit fixed
+ * point (each term rounded to a multiple of 2^-40; |partial sums| < 2^23), so
+ * dcomp and dwin do not depend on the order the terms arrive in: repeated
+ * calls give the same bits.  dq is summed in a fixed order per row.
  * The output gradient is scaled by a power of two per (row, 16 heads) inside;
  * entries with |e|_2 above ~3e4 may overflow the fp16 products.
- * No workspace.
+ * Workspace: csa_mqa_bwd_workspace(comp_rows, win_rows, d) bytes (win_rows 0
+ * when window == 0), 8-byte aligned, cleared by the call.
  */
+size_t csa_mqa_bwd_workspace(int64_t comp_rows, int64_t win_rows, int32_t d);
 int csa_mqa_bwd(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int32_t H, int32_t d,
                 const int32_t* idx, int32_t k, int32_t m, csa_kv_t comp, csa_kv_t win, int32_t window, float sm_scale,
                 float rope_base, const float* out, const float* lse, const float* dout, float* dq, float* dcomp,
-                float* dwin, csa_stream_t stream);
+                int64_t comp_rows, float* dwin, int64_t win_rows, void* ws, size_t ws_bytes, csa_stream_t stream);
 
 /* Text of the last error on the calling thread ("" if none). */
 const char* csa_last_error(void);

@@ -146,9 +146,14 @@ def test_mqa_bwd_validation(csa):
     def bwd(**o):
         a = dict(args, **o)
         return L.csa_mqa_bwd(p, p, p, a["T"], a["H"], a["d"], a.get("idx", p), a["k"], a["m"], kv, kv, a["window"],
-                             0.04, 10000.0, a.get("out", p), p, p, p, p, a.get("dwin", p), None)
+                             0.04, 10000.0, a.get("out", p), p, p, p, p, a.get("comp_rows", 100), a.get("dwin", p),
+                             a.get("win_rows", 100), a.get("ws", p), a.get("ws_bytes", 1 << 30), None)
 
     assert bwd(d=128) == csa.CSA_EUNSUPPORTED and b"d=128" in L.csa_last_error()
+    assert bwd(comp_rows=0) == csa.CSA_EINVAL and b"comp_rows" in L.csa_last_error()
+    assert bwd(ws_bytes=100) == csa.CSA_EWORKSPACE
+    assert bwd(ws=ctypes.c_void_p(260)) == csa.CSA_EINVAL and b"8-byte" in L.csa_last_error()
+    assert csa.csa_mqa_bwd_workspace(100, 100, 512) == 200 * 512 * 8
     assert bwd(H=48) == csa.CSA_EUNSUPPORTED
     assert bwd(k=4096) == csa.CSA_EUNSUPPORTED
     assert bwd(out=None) == csa.CSA_EINVAL
@@ -162,3 +167,26 @@ def test_workspace_sizes(csa):
     # decode shapes split the key list; big batches do not
     assert csa.csa_mqa_workspace(4, 64, 512, 1152) > 0
     assert csa.csa_mqa_workspace(8192, 64, 512, 1152) == 0
+
+
+def test_index_topk_and_index_bwd_validation(csa):
+    L = csa._lib
+    p = ctypes.c_void_p(256)
+    keys = csa._IdxKeys(256, 256, 4096)
+    # csa_index_topk: k range, workspace
+    rc = L.csa_index_topk(p, p, p, p, p, 4, 8, 128, keys, 4, 4096, 4096, p, p, 1 << 30, None)
+    assert rc == csa.CSA_EUNSUPPORTED and b"k=4096" in L.csa_last_error()
+    rc = L.csa_index_topk(p, p, p, p, p, 4, 8, 128, keys, 4, 4096, 1024, p, p, 16, None)
+    assert rc == csa.CSA_EWORKSPACE
+    rc = L.csa_index_topk(p, p, p, p, p, 4, 8, 96, keys, 4, 4096, 1024, p, p, 1 << 30, None)
+    assert rc == csa.CSA_EUNSUPPORTED
+    assert csa.csa_index_topk_workspace(4, 262144, 1024, 8) > 0
+    assert csa.csa_index_topk_workspace(4, 262144, 4096, 8) == 0
+    # csa_index_bwd: shapes, workspace
+    rc = L.csa_index_bwd(p, p, p, p, p, 4, 8, 128, keys, 4, p, p, 0, p, p, p, 100, p, 1 << 30, None)
+    assert rc == csa.CSA_EINVAL and b"n_sel" in L.csa_last_error()
+    rc = L.csa_index_bwd(p, p, p, p, p, 4, 8, 128, keys, 4, p, p, 16, p, p, p, 100, p, 64, None)
+    assert rc == csa.CSA_EWORKSPACE
+    rc = L.csa_index_bwd(p, p, p, p, p, 4, 3, 128, keys, 4, p, p, 16, p, p, p, 100, p, 1 << 30, None)
+    assert rc == csa.CSA_EUNSUPPORTED
+    assert csa.csa_index_bwd_workspace(100, 128) == 100 * 128 * 8

@@ -31,7 +31,8 @@ class _Kv(ctypes.Structure):
 
 
 class _IdxKeys(ctypes.Structure):
-    _fields_ = [("data", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("cap", ctypes.c_int64)]
+    _fields_ = [("data", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("cap", ctypes.c_int64),
+                ("pages", ctypes.c_void_p), ("page", ctypes.c_int32)]
 
 
 _vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
@@ -64,12 +65,17 @@ _lib.csa_mqa_bwd_workspace.restype = _sz
 _lib.csa_mqa_bwd_workspace.argtypes = [_i64, _i64, _i32]
 _lib.csa_mqa_bwd.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _i32, _Kv, _Kv, _i32, _f32, _f32, _vp, _vp,
                              _vp, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp]
+_lib.csa_pages_bytes.restype = _sz
+_lib.csa_pages_bytes.argtypes = [_i32, _i32, _i32]
+_lib.csa_pages_store.argtypes = [_Kv, _IdxKeys, _i32, _i32, _vp, _i32, _vp, _sz, _vp]
+_lib.csa_pages_load.argtypes = [_Kv, _IdxKeys, _i32, _i32, _vp, _i32, _vp, _sz, _vp]
 _lib.csa_last_error.restype = ctypes.c_char_p
 _lib.csa_version.restype = ctypes.c_int
 
 EXPORTS = ["csa_compress", "csa_compress_channel", "csa_compress_index_keys", "csa_index_scores", "csa_index_scores_grouped", "csa_index_topk_workspace", "csa_index_topk", "csa_index_bwd_workspace",
            "csa_index_bwd", "csa_topk_workspace", "csa_topk", "csa_topk_noalloc", "csa_mqa_workspace",
-           "csa_sparse_mqa", "hca_dense_mqa", "csa_mqa_bwd_workspace", "csa_mqa_bwd", "csa_last_error", "csa_version"]
+           "csa_sparse_mqa", "hca_dense_mqa", "csa_mqa_bwd_workspace", "csa_mqa_bwd", "csa_pages_bytes", "csa_pages_store", "csa_pages_load",
+           "csa_last_error", "csa_version"]
 
 
 class CsaError(RuntimeError):
@@ -150,21 +156,32 @@ class KvCache:
 
 
 class IndexKeys:
-    """MXFP4 indexer keys: data uint8 [rows, d_i/2], scale uint8 [rows, d_i/32]; rows = n_seq*cap."""
+    """MXFP4 indexer keys: data uint8 [rows, d_i/2], scale uint8 [rows, d_i/32].
 
-    def __init__(self, data, scale, cap):
+    Contiguous: rows = n_seq*cap, key of entry j of sequence s at row s*cap + j.  Paged (pages int32
+    [n_seq, cap // page], page a power of two): at row pages[s, j // page] * page + j % page."""
+
+    def __init__(self, data, scale, cap, pages=None, page=0):
         _need(data, "keys.data", torch.uint8, 2)
         _need(scale, "keys.scale", torch.uint8, 2)
         if data.shape[0] != scale.shape[0] or data.shape[1] != scale.shape[1] * 16:
             raise ValueError("inconsistent IndexKeys arrays")
+        if pages is not None:
+            _need(pages, "keys.pages", torch.int32, 2)
+            if page <= 0 or page & (page - 1) or cap % page or pages.shape[1] != cap // page:
+                raise ValueError("page must be a power of two dividing cap; pages [n_seq, cap // page]")
+            if data.shape[0] % page:
+                raise ValueError("rows must be whole pages")
         self.data, self.scale, self.cap = data, scale, int(cap)
+        self.pages, self.page = pages, int(page) if pages is not None else 0
 
     @property
     def d_i(self):
         return self.data.shape[1] * 2
 
     def c(self):
-        return _IdxKeys(self.data.data_ptr(), self.scale.data_ptr(), self.cap)
+        return _IdxKeys(self.data.data_ptr(), self.scale.data_ptr(), self.cap,
+                        self.pages.data_ptr() if self.pages is not None else None, self.page)
 
 
 def csa_compress(kv, logits, tok0, m, seq, out, rope_base=10000.0):
@@ -457,3 +474,69 @@ def csa_mqa_bwd(q, seq, pos, idx, m, comp, win, window, sm_scale, out, lse, dout
                             int(window), float(sm_scale), float(rope_base), _ptr(out), _ptr(lse), _ptr(dout),
                             _ptr(dq), _ptr(dcomp), comp_rows, _ptr(dwin), win_rows, _ptr(ws), ws.numel(), _stream()))
     return dq, dcomp, dwin
+
+
+# ---- shared-prefix pages on the host and on disk ----
+_PAGES_MAGIC = b"CSAPAGE1"
+
+
+def _page_args(kv, keys):
+    d = kv.d
+    d_i = keys.d_i if keys is not None else 0
+    kc = keys.c() if keys is not None else _IdxKeys(None, None, 0, None, 0)
+    return d, d_i, kc
+
+
+def csa_pages_bytes(page, d, d_i):
+    return int(_lib.csa_pages_bytes(int(page), int(d), int(d_i)))
+
+
+def csa_pages_store(kv, keys, page_ids, host):
+    """Copy physical pages page_ids of kv (KvCache, paged) and keys (IndexKeys or None) into host
+    (a uint8 CPU tensor, pinned for asynchronous copies); synchronise before reading it."""
+    d, d_i, kc = _page_args(kv, keys)
+    ids = (ctypes.c_int32 * len(page_ids))(*[int(p) for p in page_ids])
+    _check(_lib.csa_pages_store(kv.c(), kc, d, d_i, ids, len(page_ids), ctypes.c_void_p(host.data_ptr()),
+                                host.numel(), _stream()))
+
+
+def csa_pages_load(kv, keys, page_ids, host):
+    """Copy host (the layout csa_pages_store writes) into physical pages page_ids of kv and keys."""
+    d, d_i, kc = _page_args(kv, keys)
+    ids = (ctypes.c_int32 * len(page_ids))(*[int(p) for p in page_ids])
+    _check(_lib.csa_pages_load(kv.c(), kc, d, d_i, ids, len(page_ids), ctypes.c_void_p(host.data_ptr()),
+                               host.numel(), _stream()))
+
+
+def save_pages(path, kv, keys, page_ids):
+    """Write pages page_ids of kv and keys to a file: an 8-byte tag, (d, d_i, page, n) as int32, then
+    the pages in the layout of csa_pages_store."""
+    import numpy as np
+
+    d, d_i, _ = _page_args(kv, keys)
+    n = len(page_ids)
+    host = torch.empty(csa_pages_bytes(kv.page, d, d_i) * n, dtype=torch.uint8, pin_memory=True)
+    csa_pages_store(kv, keys, page_ids, host)
+    torch.cuda.current_stream().synchronize()
+    with open(path, "wb") as f:
+        f.write(_PAGES_MAGIC)
+        f.write(np.array([d, d_i, kv.page, n], np.int32).tobytes())
+        f.write(host.numpy().tobytes())
+
+
+def load_pages(path, kv, keys, page_ids):
+    """Read a file written by save_pages into pages page_ids of kv and keys (same d, d_i, page and count)."""
+    import numpy as np
+
+    with open(path, "rb") as f:
+        if f.read(8) != _PAGES_MAGIC:
+            raise ValueError(f"{path}: not a page file")
+        d, d_i, page, n = (int(x) for x in np.frombuffer(f.read(16), np.int32))
+        exp = _page_args(kv, keys)
+        if (d, d_i, page, n) != (exp[0], exp[1], kv.page, len(page_ids)):
+            raise ValueError(f"{path}: holds d={d} d_i={d_i} page={page} x{n}, the destination differs")
+        data = f.read()
+    host = torch.empty(len(data), dtype=torch.uint8, pin_memory=True)
+    host.numpy()[:] = np.frombuffer(data, np.uint8)
+    csa_pages_load(kv, keys, page_ids, host)
+    torch.cuda.current_stream().synchronize()

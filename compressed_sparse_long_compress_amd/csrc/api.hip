@@ -48,6 +48,22 @@ int check_kv(const csa_kv_t& kv, int d, const char* what, const char* fn) {
     return CSA_OK;
 }
 
+int check_keys_pages(const csa_index_keys_t& keys, const char* fn) {
+    if (!keys.pages) return CSA_OK;
+    if (keys.page < 1 || (keys.page & (keys.page - 1)) != 0)
+        return fail(CSA_EINVAL, "%s: keys.page (%d) must be a power of two", fn, keys.page);
+    if (keys.cap % keys.page != 0)
+        return fail(CSA_EINVAL, "%s: keys.page (%d) must divide keys.cap (%lld)", fn, keys.page, (long long)keys.cap);
+    return CSA_OK;
+}
+
+int page_shift(const int32_t* pages, int32_t page) {
+    int sh = 0;
+    if (pages)
+        while ((1 << sh) < page) ++sh;
+    return sh;
+}
+
 csa::KvView view(const csa_kv_t& kv) {
     int sh = 0;
     if (kv.pages)
@@ -178,8 +194,10 @@ int csa_compress_index_keys(const uint16_t* k, const float* logits, int64_t tok0
     if (n_tok / m > out.cap)
         return fail(CSA_EINVAL, "%s: %lld new entries exceed out.cap (%lld): slots would collide", fn,
                     (long long)(n_tok / m), (long long)out.cap);
-    hipError_t e = csa::launch_compress_index_keys(k, logits, tok0, n_tok, m, d_i, (int64_t)seq * out.cap, out.cap,
-                                                   out.data, out.scale, (hipStream_t)stream);
+    if (int rc = check_keys_pages(out, fn)) return rc;
+    hipError_t e = csa::launch_compress_index_keys(k, logits, tok0, n_tok, m, d_i, seq, out.cap, out.pages,
+                                                   page_shift(out.pages, out.page), out.data, out.scale,
+                                                   (hipStream_t)stream);
     return hip_status(e, fn);
 }
 
@@ -203,6 +221,7 @@ static int index_args(const char* fn, const uint8_t* q, const uint8_t* q_scale, 
     if (keys.cap < n_cols) return fail(CSA_EINVAL, "%s: n_cols (%lld) > keys.cap (%lld)", fn, (long long)n_cols,
                                        (long long)keys.cap);
     if (!aligned16(q) || !aligned16(keys.data)) return fail(CSA_EINVAL, "%s: q and keys.data must be 16-byte aligned", fn);
+    if (int rc = check_keys_pages(keys, fn)) return rc;
     if (topk_ws && csa::topk_uses_summary(T, n_cols)) {
         // the row summaries are the top-k workspace
         if (topk_ws_bytes < csa::topk_workspace_bytes(T, n_cols, 1))
@@ -222,7 +241,8 @@ int csa_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, c
     const int rc = index_args(fn, q, q_scale, w, seq, pos, T, h_i, d_i, keys, m, n_cols, scores, topk_ws,
                               topk_ws_bytes, &gmax, &nothing);
     if (rc != CSA_OK || nothing) return rc;
-    hipError_t e = csa::launch_index_scores(q, q_scale, w, seq, pos, T, h_i, d_i, keys.data, keys.scale, keys.cap, m,
+    hipError_t e = csa::launch_index_scores(q, q_scale, w, seq, pos, T, h_i, d_i, keys.data, keys.scale, keys.cap,
+                                            keys.pages, page_shift(keys.pages, keys.page), m,
                                             n_cols, scores, gmax, (hipStream_t)stream);
     return hip_status(e, fn);
 }
@@ -241,7 +261,8 @@ int csa_index_scores_grouped(const uint8_t* q, const uint8_t* q_scale, const flo
                               topk_ws_bytes, &gmax, &nothing);
     if (rc != CSA_OK || nothing) return rc;
     hipError_t e = csa::launch_index_scores_grouped(q, q_scale, w, seq, pos, T, h_i, d_i, keys.data, keys.scale,
-                                                    keys.cap, m, n_cols, group, scores, gmax, (hipStream_t)stream);
+                                                    keys.cap, keys.pages, page_shift(keys.pages, keys.page), m, n_cols,
+                                                    group, scores, gmax, (hipStream_t)stream);
     return hip_status(e, fn);
 }
 
@@ -272,7 +293,8 @@ int csa_index_topk(const uint8_t* q, const uint8_t* q_scale, const float* w, con
     if (ws_bytes < need || !ws)
         return fail(CSA_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
     if (((uintptr_t)ws & 255u) != 0) return fail(CSA_EINVAL, "%s: workspace must be 256-byte aligned", fn);
-    hipError_t e = csa::launch_index_topk(q, q_scale, w, seq, pos, T, h_i, d_i, keys.data, keys.scale, keys.cap, m,
+    hipError_t e = csa::launch_index_topk(q, q_scale, w, seq, pos, T, h_i, d_i, keys.data, keys.scale, keys.cap,
+                                          keys.pages, page_shift(keys.pages, keys.page), m,
                                           n_cols, k, idx, ws, (hipStream_t)stream);
     return hip_status(e, fn);
 }
@@ -297,13 +319,73 @@ int csa_index_bwd(const uint8_t* q, const uint8_t* q_scale, const float* w, cons
     if (!q || !q_scale || !w || !seq || !pos || !keys.data || !keys.scale || !idx || !g || !dq || !dw || !dkeys)
         return fail(CSA_EINVAL, "%s: null pointer argument", fn);
     if (keys.cap < 1) return fail(CSA_EINVAL, "%s: keys.cap must be >= 1", fn);
+    if (int rc = check_keys_pages(keys, fn)) return rc;
     const size_t need = csa_index_bwd_workspace(key_rows, d_i);
     if (ws_bytes < need || !ws)
         return fail(CSA_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
     if (((uintptr_t)ws & 7u) != 0) return fail(CSA_EINVAL, "%s: workspace must be 8-byte aligned", fn);
-    hipError_t e = csa::launch_index_bwd(q, q_scale, w, seq, pos, T, h_i, d_i, keys.data, keys.scale, keys.cap, m, idx,
+    hipError_t e = csa::launch_index_bwd(q, q_scale, w, seq, pos, T, h_i, d_i, keys.data, keys.scale, keys.cap,
+                                         keys.pages, page_shift(keys.pages, keys.page), m, idx,
                                          g, n_sel, dq, dw, dkeys, key_rows, ws, (hipStream_t)stream);
     return hip_status(e, fn);
+}
+
+size_t csa_pages_bytes(int32_t page, int32_t d, int32_t d_i) {
+    if (page < 1 || (d != 128 && d != 512) || (d_i != 0 && d_i != 64 && d_i != 128)) return 0;
+    return (size_t)page * ((size_t)(d - 64) + 64 * 2 + 4 + (size_t)d_i / 2 + (size_t)d_i / 32);
+}
+
+// one page's arrays in the host layout, in order: nope, rope, scale, key data, key scales
+static int pages_copy(const char* fn, const csa_kv_t& kv, const csa_index_keys_t& keys, int32_t d, int32_t d_i,
+                      const int32_t* pages, int32_t n_pages, char* host, size_t host_bytes, bool to_host,
+                      hipStream_t st) {
+    if (d != 128 && d != 512) return fail(CSA_EUNSUPPORTED, "%s: d=%d unsupported (128 or 512)", fn, d);
+    if (d_i != 0 && d_i != 64 && d_i != 128) return fail(CSA_EUNSUPPORTED, "%s: d_i=%d unsupported (0, 64, 128)", fn, d_i);
+    if (n_pages < 0) return fail(CSA_EINVAL, "%s: n_pages must be >= 0", fn);
+    if (n_pages == 0) return ok();
+    const int32_t page = kv.page;
+    if (page < 1 || (page & (page - 1)) != 0)
+        return fail(CSA_EINVAL, "%s: kv.page (%d) must be a power of two (rows per page)", fn, page);
+    if (!kv.nope || !kv.rope || !kv.scale || !pages || !host) return fail(CSA_EINVAL, "%s: null pointer argument", fn);
+    if (d_i > 0) {
+        if (!keys.data || !keys.scale) return fail(CSA_EINVAL, "%s: null key arrays", fn);
+        if (keys.page != page) return fail(CSA_EINVAL, "%s: keys.page (%d) must equal kv.page (%d)", fn, keys.page, page);
+    }
+    const size_t per = csa_pages_bytes(page, d, d_i);
+    if (host_bytes < per * (size_t)n_pages)
+        return fail(CSA_EWORKSPACE, "%s: host buffer of %zu bytes needed, %zu given", fn, per * (size_t)n_pages, host_bytes);
+    const size_t dn = (size_t)(d - 64);
+    struct Arr {
+        char* dev;
+        size_t row;
+    } arrs[5] = {{(char*)kv.nope, dn}, {(char*)kv.rope, 128}, {(char*)kv.scale, 4},
+                 {(char*)keys.data, (size_t)d_i / 2}, {(char*)keys.scale, (size_t)d_i / 32}};
+    const int na = d_i > 0 ? 5 : 3;
+    for (int32_t i = 0; i < n_pages; ++i) {
+        if (pages[i] < 0) return fail(CSA_EINVAL, "%s: negative page number", fn);
+        char* h = host + per * (size_t)i;
+        for (int a = 0; a < na; ++a) {
+            const size_t bytes = arrs[a].row * (size_t)page;
+            char* dv = arrs[a].dev + (size_t)pages[i] * bytes;
+            const hipError_t e = to_host ? hipMemcpyAsync(h, dv, bytes, hipMemcpyDeviceToHost, st)
+                                         : hipMemcpyAsync(dv, h, bytes, hipMemcpyHostToDevice, st);
+            if (e != hipSuccess) return fail(CSA_EHIP, "%s: copy failed: %s", fn, hipGetErrorString(e));
+            h += bytes;
+        }
+    }
+    return ok();
+}
+
+int csa_pages_store(csa_kv_t kv, csa_index_keys_t keys, int32_t d, int32_t d_i, const int32_t* pages,
+                    int32_t n_pages, void* host, size_t host_bytes, csa_stream_t stream) {
+    return pages_copy("csa_pages_store", kv, keys, d, d_i, pages, n_pages, (char*)host, host_bytes, true,
+                      (hipStream_t)stream);
+}
+
+int csa_pages_load(csa_kv_t kv, csa_index_keys_t keys, int32_t d, int32_t d_i, const int32_t* pages,
+                   int32_t n_pages, const void* host, size_t host_bytes, csa_stream_t stream) {
+    return pages_copy("csa_pages_load", kv, keys, d, d_i, pages, n_pages, (char*)host, host_bytes, false,
+                      (hipStream_t)stream);
 }
 
 size_t csa_topk_workspace(int64_t T, int64_t n_cols, int32_t k) { return csa::topk_workspace_bytes(T, n_cols, k); }

@@ -241,7 +241,8 @@ __device__ __forceinline__ uint32_t e2m1_code(double v) {
 
 template <int DI>
 __global__ __launch_bounds__(256) void k_compress_ikey(const uint16_t* __restrict__ k, const float* __restrict__ logits,
-                                                       int64_t tok0, int64_t n_blk, int m, int64_t row0, int64_t cap,
+                                                       int64_t tok0, int64_t n_blk, int m, int64_t seq, int64_t cap,
+                                                       const int32_t* __restrict__ pages, int pshift,
                                                        uint8_t* __restrict__ data, uint8_t* __restrict__ kscale) {
     static_assert(DI == 64 || DI == 128, "two elements per lane");
     __shared__ double wbuf[4][kMaxM];
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(256) void k_compress_ikey(const uint16_t* __restric
         sb = sb < 0 ? 0 : (sb > 254 ? 254 : sb);
     }
     const double inv = ldexp(1.0, 127 - sb);  // exact power of two
-    const int64_t row = row0 + ((tok0 / m + b) % cap);
+    const int64_t row = kv_row(pages, pshift, cap, seq, (tok0 / m + b) % cap);
     if (live) {
         const uint32_t lo = am > 0.0 ? e2m1_code(c0 * inv) : 0u, hi = am > 0.0 ? e2m1_code(c1 * inv) : 0u;
         data[row * (DI / 2) + lane] = (uint8_t)(lo | (hi << 4));
@@ -305,16 +306,17 @@ hipError_t launch_compress_channel(const uint16_t* kv, const float* logits, int6
 }
 
 hipError_t launch_compress_index_keys(const uint16_t* k, const float* logits, int64_t tok0, int64_t n_tok, int m,
-                                      int d_i, int64_t row0, int64_t cap, uint8_t* data, uint8_t* kscale,
+                                      int d_i, int64_t seq, int64_t cap, const int32_t* pages, int pshift,
+                                      uint8_t* data, uint8_t* kscale,
                                       hipStream_t st) {
     const int64_t n_blk = n_tok / m;
     if (n_blk == 0) return hipSuccess;
     dim3 grid((unsigned)((n_blk + 3) / 4)), block(256);
     if (d_i == 128)
-        hipLaunchKernelGGL(k_compress_ikey<128>, grid, block, 0, st, k, logits, tok0, n_blk, m, row0, cap, data,
+        hipLaunchKernelGGL(k_compress_ikey<128>, grid, block, 0, st, k, logits, tok0, n_blk, m, seq, cap, pages, pshift, data,
                            kscale);
     else
-        hipLaunchKernelGGL(k_compress_ikey<64>, grid, block, 0, st, k, logits, tok0, n_blk, m, row0, cap, data,
+        hipLaunchKernelGGL(k_compress_ikey<64>, grid, block, 0, st, k, logits, tok0, n_blk, m, seq, cap, pages, pshift, data,
                            kscale);
     return hipGetLastError();
 }

@@ -45,27 +45,27 @@ hipError_t launch_compress_channel(const uint16_t* kv, const float* logits, int6
                                    float* scale, hipStream_t st);
 // raw bf16 index keys -> MXFP4 rows
 hipError_t launch_compress_index_keys(const uint16_t* k, const float* logits, int64_t tok0, int64_t n_tok, int m,
-                                      int d_i, int64_t row0, int64_t cap, uint8_t* data, uint8_t* kscale,
-                                      hipStream_t st);
+                                      int d_i, int64_t seq, int64_t cap, const int32_t* pages, int pshift,
+                                      uint8_t* data, uint8_t* kscale, hipStream_t st);
 
 // gmax != nullptr: also write each row's summary (the largest order key of
 // the visible columns of every kTopkGroup-column group) to gmax[T][groups]
 hipError_t launch_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
                                const int64_t* pos, int64_t T, int h_i, int d_i, const uint8_t* kdata,
-                               const uint8_t* kscale, int64_t kcap, int m, int64_t n_cols, float* scores,
-                               uint32_t* gmax, hipStream_t st);
+                               const uint8_t* kscale, int64_t kcap, const int32_t* kpages, int kpshift, int m,
+                               int64_t n_cols, float* scores, uint32_t* gmax, hipStream_t st);
 // rows g*group .. g*group+group-1 share each key stream (group 1, 2 or 4; T % group == 0)
 hipError_t launch_index_scores_grouped(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
                                        const int64_t* pos, int64_t T, int h_i, int d_i, const uint8_t* kdata,
-                                       const uint8_t* kscale, int64_t kcap, int m, int64_t n_cols, int group,
-                                       float* scores, uint32_t* gmax, hipStream_t st);
+                                       const uint8_t* kscale, int64_t kcap, const int32_t* kpages, int kpshift, int m,
+                                       int64_t n_cols, int group, float* scores, uint32_t* gmax, hipStream_t st);
 
 // fused indexer + top-k (no score row written): workspace and launch
 size_t index_topk_workspace_bytes(int64_t T, int64_t n_cols, int k, int h_i);
 hipError_t launch_index_topk(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
                              const int64_t* pos, int64_t T, int h_i, int d_i, const uint8_t* kdata,
-                             const uint8_t* kscale, int64_t kcap, int m, int64_t n_cols, int k, int32_t* idx, void* ws,
-                             hipStream_t st);
+                             const uint8_t* kscale, int64_t kcap, const int32_t* kpages, int kpshift, int m,
+                             int64_t n_cols, int k, int32_t* idx, void* ws, hipStream_t st);
 
 size_t topk_workspace_bytes(int64_t T, int64_t n_cols, int k);
 // true when the top-k for this shape uses the row summaries (few long rows)
@@ -88,8 +88,9 @@ hipError_t launch_fx_flush(const unsigned long long* src, float* dst, int64_t n,
 // gradient of the indexer scores at the selected columns; ws: key_rows x d_i x 8 bytes
 hipError_t launch_index_bwd(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
                             const int64_t* pos, int64_t T, int h_i, int d_i, const uint8_t* kdata,
-                            const uint8_t* kscale, int64_t kcap, int m, const int32_t* idx, const float* g, int n_sel,
-                            float* dq, float* dw, float* dkeys, int64_t key_rows, void* ws, hipStream_t st);
+                            const uint8_t* kscale, int64_t kcap, const int32_t* kpages, int kpshift, int m,
+                            const int32_t* idx, const float* g, int n_sel, float* dq, float* dw, float* dkeys,
+                            int64_t key_rows, void* ws, hipStream_t st);
 
 size_t mqa_workspace_bytes(int64_t T, int H, int d, int64_t max_keys);
 // idx == nullptr selects the dense (HCA) key set

@@ -38,7 +38,8 @@ template <int DI>
 __global__ __launch_bounds__(kIbThreads) void k_index_bwd(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ q_scale, const float* __restrict__ w,
     const int32_t* __restrict__ seq, const int64_t* __restrict__ pos, int h_i, const uint8_t* __restrict__ kdata,
-    const uint8_t* __restrict__ kscale, int64_t kcap, int m, const int32_t* __restrict__ idx,
+    const uint8_t* __restrict__ kscale, int64_t kcap, const int32_t* __restrict__ kpages, int kpshift, int m,
+    const int32_t* __restrict__ idx,
     const float* __restrict__ gsel, int n_sel, float* __restrict__ dq, float* __restrict__ dw,
     unsigned long long* __restrict__ dk_fx) {
     constexpr int NT = kIbThreads;
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(kIbThreads) void k_index_bwd(
     const int tid = threadIdx.x;
     const int64_t t = blockIdx.x;
     const int64_t nv = (pos[t] + 1) / m;
-    const int64_t base = (int64_t)seq[t] * kcap;
+    const int32_t sq = seq[t];
     for (int e = tid; e < 8 * DI; e += NT) {
         const int h = e / DI, c = e % DI;
         qs[h][c] = h < h_i ? mx_elem<DI>(q, q_scale, t * h_i + h, c) : 0.f;
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(kIbThreads) void k_index_bwd(
                 for (int h = 0; h < 8; ++h) coef[h][a] = 0.f;
                 continue;
             }
-            const int64_t r = base + j;
+            const int64_t r = kv_row(kpages, kpshift, kcap, sq, j);
             const float gv = gsel[t * (int64_t)n_sel + a0 + a];
             float dot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             for (int c = 0; c < DI; ++c) {
@@ -131,8 +132,9 @@ __global__ __launch_bounds__(kIbThreads) void k_index_bwd(
 
 hipError_t launch_index_bwd(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
                             const int64_t* pos, int64_t T, int h_i, int d_i, const uint8_t* kdata,
-                            const uint8_t* kscale, int64_t kcap, int m, const int32_t* idx, const float* g, int n_sel,
-                            float* dq, float* dw, float* dkeys, int64_t key_rows, void* ws, hipStream_t st) {
+                            const uint8_t* kscale, int64_t kcap, const int32_t* kpages, int kpshift, int m,
+                            const int32_t* idx, const float* g, int n_sel, float* dq, float* dw, float* dkeys,
+                            int64_t key_rows, void* ws, hipStream_t st) {
     if (T == 0) return hipSuccess;
     unsigned long long* fx = (unsigned long long*)ws;
     const int64_t n_fx = key_rows * d_i;
@@ -140,10 +142,10 @@ hipError_t launch_index_bwd(const uint8_t* q, const uint8_t* q_scale, const floa
     if (e != hipSuccess) return e;
     if (d_i == 128)
         hipLaunchKernelGGL(k_index_bwd<128>, dim3((unsigned)T), dim3(kIbThreads), 0, st, q, q_scale, w, seq, pos, h_i,
-                           kdata, kscale, kcap, m, idx, g, n_sel, dq, dw, fx);
+                           kdata, kscale, kcap, kpages, kpshift, m, idx, g, n_sel, dq, dw, fx);
     else
         hipLaunchKernelGGL(k_index_bwd<64>, dim3((unsigned)T), dim3(kIbThreads), 0, st, q, q_scale, w, seq, pos, h_i,
-                           kdata, kscale, kcap, m, idx, g, n_sel, dq, dw, fx);
+                           kdata, kscale, kcap, kpages, kpshift, m, idx, g, n_sel, dq, dw, fx);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_fx_flush(fx, dkeys, n_fx, st);

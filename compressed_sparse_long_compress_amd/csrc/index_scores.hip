@@ -72,7 +72,8 @@ __global__ __launch_bounds__(256) void k_index_rows(const uint8_t* __restrict__ 
                                                     const float* __restrict__ w, const int32_t* __restrict__ seq,
                                                     const int64_t* __restrict__ pos, int h_i,
                                                     const uint8_t* __restrict__ kdata,
-                                                    const uint8_t* __restrict__ kscale, int64_t kcap, int m,
+                                                    const uint8_t* __restrict__ kscale, int64_t kcap,
+                                                    const int32_t* __restrict__ kpages, int kpshift, int m,
                                                     int64_t n_cols, int64_t chunk, float* __restrict__ scores,
                                                     uint32_t* __restrict__ gmax, ItkArgs ia = {}) {
     // kSample: the loop runs over the n_cols = n_s sample columns, each mapped to its score column
@@ -102,7 +103,8 @@ __global__ __launch_bounds__(256) void k_index_rows(const uint8_t* __restrict__ 
     int64_t nv = (pos[t] + 1) / m;
     const int64_t ncl = MODE == kSample ? ia.n_real : n_cols;
     if (nv > ncl) nv = ncl;
-    const int64_t base = (int64_t)seq[t] * kcap;
+    const int32_t sq = seq[t];
+    auto krow = [&](int64_t j) { return kv_row(kpages, kpshift, kcap, sq, j); };  // row of entry j's key
     const int64_t c0 = (int64_t)blockIdx.x * chunk;
     const int64_t c1 = c0 + chunk < n_cols ? c0 + chunk : n_cols;
     float* out = scores + t * n_cols;
@@ -117,8 +119,9 @@ __global__ __launch_bounds__(256) void k_index_rows(const uint8_t* __restrict__ 
             const int64_t j = real(j0 + u * 16 + r);
             if (j < nv && g < NB) {
                 // streamed once: nontemporal, so the keys do not displace cached lines
-                bk[u] = __builtin_nontemporal_load((const v4i*)(kdata + (base + j) * KB + g * 16));
-                sb[u] = kscale[(base + j) * NB + g];
+                const int64_t kr = krow(j);
+                bk[u] = __builtin_nontemporal_load((const v4i*)(kdata + kr * KB + g * 16));
+                sb[u] = kscale[kr * NB + g];
             } else {
                 bk[u] = v4i{0, 0, 0, 0};
                 sb[u] = 127;
@@ -216,7 +219,8 @@ __global__ __launch_bounds__(256) void k_index_rows_grp(const uint8_t* __restric
                                                         const float* __restrict__ w, const int32_t* __restrict__ seq,
                                                         const int64_t* __restrict__ pos,
                                                         const uint8_t* __restrict__ kdata,
-                                                        const uint8_t* __restrict__ kscale, int64_t kcap, int m,
+                                                        const uint8_t* __restrict__ kscale, int64_t kcap,
+                                                        const int32_t* __restrict__ kpages, int kpshift, int m,
                                                         int64_t n_cols, int64_t chunk, float* __restrict__ scores,
                                                         uint32_t* __restrict__ gmax) {
     constexpr int KB = DI / 2;            // bytes per key
@@ -285,8 +289,6 @@ __global__ __launch_bounds__(256) void k_index_rows_grp(const uint8_t* __restric
 #pragma unroll
             for (int i = 0; i < 4; ++i) wr[at][i] = live ? w[(t0 + qg) * HI + hb + i] : 0.f;
         }
-        const int64_t base = (int64_t)s * kcap;
-
         for (int64_t j0 = c0 + (int64_t)wave * 16 * U; j0 < c1; j0 += 4 * 16 * U) {
             uint32_t gm[NA][4];  // per tile and summary group of this step: the lane group's largest visible key
 #pragma unroll
@@ -297,8 +299,9 @@ __global__ __launch_bounds__(256) void k_index_rows_grp(const uint8_t* __restric
             for (int u = 0; u < U; ++u) {
                 const int64_t j = j0 + u * 16 + r;
                 if (j < nv_max && g < NB) {
-                    bk[u] = __builtin_nontemporal_load((const v4i*)(kdata + (base + j) * KB + g * 16));
-                    sb[u] = kscale[(base + j) * NB + g];
+                    const int64_t kr = kv_row(kpages, kpshift, kcap, s, j);
+                    bk[u] = __builtin_nontemporal_load((const v4i*)(kdata + kr * KB + g * 16));
+                    sb[u] = kscale[kr * NB + g];
                 } else {
                     bk[u] = v4i{0, 0, 0, 0};
                     sb[u] = 127;
@@ -365,7 +368,8 @@ __global__ __launch_bounds__(256, HI == 8 ? 2 : 1) void k_index_gemm(const uint8
                                                     const float* __restrict__ w, const int32_t* __restrict__ seq,
                                                     const int64_t* __restrict__ pos, int64_t T,
                                                     const uint8_t* __restrict__ kdata,
-                                                    const uint8_t* __restrict__ kscale, int64_t kcap, int m,
+                                                    const uint8_t* __restrict__ kscale, int64_t kcap,
+                                                    const int32_t* __restrict__ kpages, int kpshift, int m,
                                                     int64_t n_cols, int64_t chunk, float* __restrict__ scores,
                                                     ItkArgs ia = {}) {
     constexpr int KB = DI / 2, NB = DI / 32;
@@ -465,7 +469,6 @@ __global__ __launch_bounds__(256, HI == 8 ? 2 : 1) void k_index_gemm(const uint8
                 nv_max = nv > nv_max ? nv : nv_max;
                 nv_min = nv < nv_min ? nv : nv_min;
             }
-        const int64_t base = (int64_t)s * kcap;
         // one score (or sample key, or candidate) of query slot (at, i) at tile column j (jr: score column)
         auto put = [&](int at, int i, int64_t j, int64_t jr, float v) {
             const int qj = at * QA + (HI == 8 ? 2 * g2 + i : 2 * i + g2);
@@ -515,8 +518,9 @@ __global__ __launch_bounds__(256, HI == 8 ? 2 : 1) void k_index_gemm(const uint8
             for (int ks = 0; ks < KS; ++ks) {
                 const int blk = 2 * ks + g2;
                 if (kload) {
-                    b[ks] = frag16(kdata + (base + jr) * KB + blk * 16);
-                    sb[ks] = kscale[(base + jr) * NB + blk];
+                    const int64_t kr = kv_row(kpages, kpshift, kcap, s, jr);
+                    b[ks] = frag16(kdata + kr * KB + blk * 16);
+                    sb[ks] = kscale[kr * NB + blk];
                 } else {
                     b[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
                     sb[ks] = 127;
@@ -578,8 +582,8 @@ __global__ __launch_bounds__(256, HI == 8 ? 2 : 1) void k_index_gemm(const uint8
 
 hipError_t launch_index_scores(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
                                const int64_t* pos, int64_t T, int h_i, int d_i, const uint8_t* kdata,
-                               const uint8_t* kscale, int64_t kcap, int m, int64_t n_cols, float* scores,
-                               uint32_t* gmax, hipStream_t st) {
+                               const uint8_t* kscale, int64_t kcap, const int32_t* kpages, int kpshift, int m,
+                               int64_t n_cols, float* scores, uint32_t* gmax, hipStream_t st) {
     if (T == 0 || n_cols == 0) return hipSuccess;
     if (T <= 64 || gmax) {
         // aim for >= 2048 workgroups (one 128-key step per wave at the 1M-context decode shape);
@@ -591,10 +595,10 @@ hipError_t launch_index_scores(const uint8_t* q, const uint8_t* q_scale, const f
         dim3 grid((unsigned)((n_cols + chunk - 1) / chunk), (unsigned)T), block(256);
         if (d_i == 128)
             hipLaunchKernelGGL((k_index_rows<128, 8>), grid, block, 0, st, q, q_scale, w, seq, pos, h_i, kdata, kscale,
-                               kcap, m, n_cols, chunk, scores, gmax);
+                               kcap, kpages, kpshift, m, n_cols, chunk, scores, gmax);
         else
             hipLaunchKernelGGL((k_index_rows<64, 8>), grid, block, 0, st, q, q_scale, w, seq, pos, h_i, kdata, kscale,
-                               kcap, m, n_cols, chunk, scores, gmax);
+                               kcap, kpages, kpshift, m, n_cols, chunk, scores, gmax);
         return hipGetLastError();
     }
     const int qwg = 4 * 4 * (32 / h_i);  // queries per workgroup
@@ -605,7 +609,7 @@ hipError_t launch_index_scores(const uint8_t* q, const uint8_t* q_scale, const f
     dim3 grid((unsigned)((n_cols + chunk - 1) / chunk), (unsigned)qtiles), block(256);
 #define CSA_GEMM(DI, HI)                                                                                          \
     hipLaunchKernelGGL((k_index_gemm<DI, HI>), grid, block, 0, st, q, q_scale, w, seq, pos, T, kdata, kscale, kcap, \
-                       m, n_cols, chunk, scores)
+                       kpages, kpshift, m, n_cols, chunk, scores)
     if (d_i == 128 && h_i == 8) CSA_GEMM(128, 8);
     else if (d_i == 128 && h_i == 4) CSA_GEMM(128, 4);
     else if (d_i == 64 && h_i == 8) CSA_GEMM(64, 8);
@@ -616,10 +620,10 @@ hipError_t launch_index_scores(const uint8_t* q, const uint8_t* q_scale, const f
 
 hipError_t launch_index_scores_grouped(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
                                        const int64_t* pos, int64_t T, int h_i, int d_i, const uint8_t* kdata,
-                                       const uint8_t* kscale, int64_t kcap, int m, int64_t n_cols, int group,
-                                       float* scores, uint32_t* gmax, hipStream_t st) {
+                                       const uint8_t* kscale, int64_t kcap, const int32_t* kpages, int kpshift, int m,
+                                       int64_t n_cols, int group, float* scores, uint32_t* gmax, hipStream_t st) {
     if (group == 1)
-        return launch_index_scores(q, q_scale, w, seq, pos, T, h_i, d_i, kdata, kscale, kcap, m, n_cols, scores, gmax,
+        return launch_index_scores(q, q_scale, w, seq, pos, T, h_i, d_i, kdata, kscale, kcap, kpages, kpshift, m, n_cols, scores, gmax,
                                    st);
     if (T == 0 || n_cols == 0) return hipSuccess;
     const int64_t G = T / group;
@@ -631,7 +635,7 @@ hipError_t launch_index_scores_grouped(const uint8_t* q, const uint8_t* q_scale,
     const dim3 grid((unsigned)((n_cols + chunk - 1) / chunk), (unsigned)G), block(256);
 #define CSA_GRP(DI, R, HI)                                                                                         \
     hipLaunchKernelGGL((k_index_rows_grp<DI, R, HI>), grid, block, 0, st, q, q_scale, w, seq, pos, kdata, kscale, \
-                       kcap, m, n_cols, chunk, scores, gmax)
+                       kcap, kpages, kpshift, m, n_cols, chunk, scores, gmax)
     if (d_i == 128) {
         if (h_i == 8) {
             if (group == 2) CSA_GRP(128, 2, 8);
@@ -912,8 +916,9 @@ __global__ __launch_bounds__(NT) void k_itk_pick(const uint32_t* __restrict__ cn
 __global__ __launch_bounds__(kTopkThreads) void k_itk_fallback(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ q_scale, const float* __restrict__ w,
     const int32_t* __restrict__ seq, const int64_t* __restrict__ pos, int h_i, int d_i,
-    const uint8_t* __restrict__ kdata, const uint8_t* __restrict__ kscale, int64_t kcap, int m, int64_t n_cols, int k,
-    int32_t* __restrict__ idx, uint32_t* __restrict__ fb, float* __restrict__ fbrow) {
+    const uint8_t* __restrict__ kdata, const uint8_t* __restrict__ kscale, int64_t kcap,
+    const int32_t* __restrict__ kpages, int kpshift, int m, int64_t n_cols, int k, int32_t* __restrict__ idx,
+    uint32_t* __restrict__ fb, float* __restrict__ fbrow) {
     constexpr int NT = kTopkThreads;
     __shared__ uint32_t hist[4096];
     __shared__ __align__(16) uint32_t cache[kItkFbCache];
@@ -942,10 +947,11 @@ __global__ __launch_bounds__(kTopkThreads) void k_itk_fallback(
         }
         if (tid < h_i) wh[tid] = w[t * h_i + tid];
         __syncthreads();
-        const int64_t base = (int64_t)seq[t] * kcap;
+        const int32_t sq = seq[t];
         for (int j = tid; j < nv; j += NT) {
-            const uint8_t* kd = kdata + (base + j) * KB;
-            const uint8_t* ks = kscale + (base + j) * NB;
+            const int64_t kr = kv_row(kpages, kpshift, kcap, sq, j);
+            const uint8_t* kd = kdata + kr * KB;
+            const uint8_t* ks = kscale + kr * NB;
             float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             for (int b = 0; b < NB; ++b) {
                 const int sc = (int)ks[b] - 127;
@@ -971,8 +977,8 @@ __global__ __launch_bounds__(kTopkThreads) void k_itk_fallback(
 
 hipError_t launch_index_topk(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* seq,
                              const int64_t* pos, int64_t T, int h_i, int d_i, const uint8_t* kdata,
-                             const uint8_t* kscale, int64_t kcap, int m, int64_t n_cols, int k, int32_t* idx, void* ws,
-                             hipStream_t st) {
+                             const uint8_t* kscale, int64_t kcap, const int32_t* kpages, int kpshift, int m,
+                             int64_t n_cols, int k, int32_t* idx, void* ws, hipStream_t st) {
     if (T == 0) return hipSuccess;
     const ItkPlan p = itk_plan(T, n_cols, k, h_i);
     if (p.S < 1 || p.S > 64) return hipErrorInvalidValue;  // k_itk_pick reads at most 64 segment counts
@@ -999,7 +1005,7 @@ hipError_t launch_index_topk(const uint8_t* q, const uint8_t* q_scale, const flo
             const dim3 grid((unsigned)((n + chunk - 1) / chunk), (unsigned)T), block(256);
 #define CSA_ROWS(DI, MD)                                                                                              \
     hipLaunchKernelGGL((k_index_rows<DI, 8, MD>), grid, block, 0, st, q, q_scale, w, seq, pos, h_i, kdata, kscale, kcap, \
-                       m, n, chunk, nullptr, nullptr, ia)
+                       kpages, kpshift, m, n, chunk, nullptr, nullptr, ia)
             if (d_i == 128) {
                 if (mode == kSample) CSA_ROWS(128, kSample);
                 else CSA_ROWS(128, kEmit);
@@ -1013,7 +1019,7 @@ hipError_t launch_index_topk(const uint8_t* q, const uint8_t* q_scale, const flo
             const dim3 grid((unsigned)((n + chunk - 1) / chunk), (unsigned)((T + qwg - 1) / qwg)), block(256);
 #define CSA_GEMM(DI, HI, MD)                                                                                      \
     hipLaunchKernelGGL((k_index_gemm<DI, HI, MD>), grid, block, 0, st, q, q_scale, w, seq, pos, T, kdata, kscale, \
-                       kcap, m, n, chunk, nullptr, ia)
+                       kcap, kpages, kpshift, m, n, chunk, nullptr, ia)
 #define CSA_GEMM_M(DI, HI)                   \
     if (mode == kSample) CSA_GEMM(DI, HI, kSample); \
     else CSA_GEMM(DI, HI, kEmit)
@@ -1054,7 +1060,7 @@ hipError_t launch_index_topk(const uint8_t* q, const uint8_t* q_scale, const flo
                            p.S, p.cap, pos, m, n_cols, k, idx, fb);
     const int G = (int)(T < kItkFbGroups ? T : kItkFbGroups);
     hipLaunchKernelGGL(k_itk_fallback, dim3((unsigned)G), dim3(kTopkThreads), 0, st, q, q_scale, w, seq, pos, h_i, d_i,
-                       kdata, kscale, kcap, m, n_cols, k, idx, fb, fbrow);
+                       kdata, kscale, kcap, kpages, kpshift, m, n_cols, k, idx, fb, fbrow);
     return hipGetLastError();
 }
 

@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define CSA_VERSION 106
+#define CSA_VERSION 108
 
 enum {
     CSA_OK = 0,
@@ -114,14 +114,21 @@ typedef struct csa_kv {
 
 /*
  * MXFP4 indexer keys, one per compressed entry, n_seq*cap rows:
- *   data  [n_seq*cap][d_i / 2]  packed E2M1
- *   scale [n_seq*cap][d_i / 32] E8M0
+ *   data  [rows][d_i / 2]  packed E2M1
+ *   scale [rows][d_i / 32] E8M0
  * Key of entry j of sequence s is row s*cap + j.  16-byte aligned data.
+ * Paged layout (as csa_kv_t): with `pages` non-NULL the key of entry j of
+ * sequence s lives at row pages[s * (cap / page) + j / page] * page + j % page;
+ * page a power of two dividing cap; sequences may share pages.  A compressed
+ * cache and its keys can use one page table, so an entry and its key share a
+ * page number (what csa_pages_store / csa_pages_load move).
  */
 typedef struct csa_index_keys {
     uint8_t* data;
     uint8_t* scale;
     int64_t cap;
+    const int32_t* pages; /* NULL: contiguous rows */
+    int32_t page;         /* slots per page when paged */
 } csa_index_keys_t;
 
 /*
@@ -173,7 +180,8 @@ int csa_compress_channel(const uint16_t* kv, const float* logits, int64_t tok0, 
  * mantissa bit, saturating at 6, zero stored as +0.  Merge in fp64.
  *   k      [n_tok][d_i] bf16 raw key tokens tok0 .. tok0+n_tok-1 of sequence seq
  *   logits [n_tok] fp32 (one per token, as csa_compress)
- *   out    entry J = tok0/m + b at row seq*out.cap + J % out.cap
+ *   out    entry J = tok0/m + b at slot J % out.cap of sequence seq (through
+ *          out.pages when paged)
  * d_i in {64, 128}; 1 <= m <= 1024; tok0 and n_tok multiples of m.
  */
 int csa_compress_index_keys(const uint16_t* k, const float* logits, int64_t tok0, int64_t n_tok, int32_t m,
@@ -410,6 +418,32 @@ int csa_mqa_bwd(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64
                 const int32_t* idx, int32_t k, int32_t m, csa_kv_t comp, csa_kv_t win, int32_t window, float sm_scale,
                 float rope_base, const float* out, const float* lse, const float* dout, float* dq, float* dcomp,
                 int64_t comp_rows, float* dwin, int64_t win_rows, void* ws, size_t ws_bytes, csa_stream_t stream);
+
+/*
+ * csa_pages_store / csa_pages_load — move physical pages of a compressed cache
+ * and of its index keys between the GPU and a host buffer, for reuse of a
+ * shared prefix beyond the GPU's memory (the pages keep the compressed
+ * entries of a two-level KV cache and store them on disk for shared-prefix
+ * reuse: [xmsumi] § 百万Token 长上下文真实表现).
+ *
+ * Physical page p is rows p*page .. p*page+page-1 of every array (page =
+ * kv.page, a power of two; keys.page must be the same, so an entry and its
+ * index key share a page number; the page tables are not read).  The host
+ * layout holds the n_pages pages in the order given, each as its arrays one
+ * after the other: nope [page][d-64], rope [page][64] bf16, scale [page] fp32,
+ * then (d_i > 0) key data [page][d_i/2] and key scales [page][d_i/32];
+ * csa_pages_bytes(page, d, d_i) bytes per page.  d_i = 0 moves entries only.
+ *   pages      HOST array of n_pages physical page numbers
+ *   host       host buffer (pinned memory lets the copies run asynchronously)
+ * The copies are enqueued on `stream`; the caller synchronises before it
+ * reads (store) or reuses (load) the host buffer.  A load followed by a
+ * store of the same pages gives back the same bytes.
+ */
+size_t csa_pages_bytes(int32_t page, int32_t d, int32_t d_i);
+int csa_pages_store(csa_kv_t kv, csa_index_keys_t keys, int32_t d, int32_t d_i, const int32_t* pages,
+                    int32_t n_pages, void* host, size_t host_bytes, csa_stream_t stream);
+int csa_pages_load(csa_kv_t kv, csa_index_keys_t keys, int32_t d, int32_t d_i, const int32_t* pages,
+                   int32_t n_pages, const void* host, size_t host_bytes, csa_stream_t stream);
 
 /* Text of the last error on the calling thread ("" if none). */
 const char* csa_last_error(void);

@@ -1140,3 +1140,94 @@ def test_index_bwd(lib, dev, gen, orc, T, h_i, d_i, N, B, m, n_sel, layout):
         v = idx[t][(idx[t] >= 0) & (idx[t] < nv[t])]
         used[seq[t] * N + v] = True
     assert not dk.cpu().numpy()[~used].any(), "gradient on key rows no row selected"
+
+
+# --------------------------------------------------------------------------
+# paged index keys, and compressed pages stored on the host / on disk and loaded back
+# --------------------------------------------------------------------------
+def test_paged_index_keys_and_page_files(lib, dev, gen, orc, tmp_path):
+    """Index keys compressed into a paged layout (pages in a shuffled order, shared page table with
+    the compressed entries) equal the oracle's keys; the indexer and the fused selection read them
+    bit-exactly against the oracle.  Sequence 0's pages (entries and keys) go to a file and come back
+    into a fresh cache at other physical pages byte for byte, and a sequence reading the reloaded
+    prefix gets the same scores, selection and attention as the original."""
+    import torch
+
+    _say("paged index keys, page files")
+    B, m, d, d_i, h_i, cap, page, k, W, H = 2, 4, 512, 128, 8, 1024, 128, 256, 128, 64
+    L, npp = cap * m, cap // page
+    rng = np.random.default_rng(12)
+    perm = rng.permutation(B * npp + 3)[: B * npp].astype(np.int32)
+    pages = torch.tensor(perm.reshape(B, npp), device="cuda")
+    n_phys = (B * npp + 3) * page
+    kv = lib.KvCache(torch.zeros(n_phys, d - 64, dtype=torch.uint8, device="cuda"),
+                     torch.zeros(n_phys, 64, dtype=torch.bfloat16, device="cuda"),
+                     torch.zeros(n_phys, dtype=torch.float32, device="cuda"), cap, pages=pages, page=page)
+    keys = lib.IndexKeys(torch.zeros(n_phys, d_i // 2, dtype=torch.uint8, device="cuda"),
+                         torch.zeros(n_phys, d_i // 32, dtype=torch.uint8, device="cuda"), cap, pages=pages, page=page)
+    toks = [gen.normal_bf16(830 + b, 1, (L, d)) for b in range(B)]
+    ikt = [gen.normal_bf16(830 + b, 2, (L, d_i)) for b in range(B)]
+    lgs = [gen.normal_f32(830 + b, 3, (L,)) for b in range(B)]
+    for b in range(B):
+        lib.csa_compress(dev.bf16(toks[b]), dev.t(lgs[b]), 0, m, b, kv)
+        lib.csa_compress_index_keys(dev.bf16(ikt[b]), dev.t(lgs[b]), 0, m, b, keys)
+    torch.cuda.synchronize()
+    # logical key rows (seq * cap + j) against the oracle's compression
+    ref_d = np.zeros((B * cap, d_i // 2), np.uint8)
+    ref_s = np.zeros((B * cap, d_i // 32), np.uint8)
+    for b in range(B):
+        ref_d[b * cap:(b + 1) * cap], ref_s[b * cap:(b + 1) * cap] = orc.compress_index_keys(ikt[b], lgs[b], 0, m)
+    phys = (perm.reshape(B, npp)[:, :, None] * page + np.arange(page)[None, None, :]).reshape(-1)
+    assert np.array_equal(keys.data.cpu().numpy()[phys], ref_d) and np.array_equal(keys.scale.cpu().numpy()[phys], ref_s)
+    # indexer and fused selection through the page table, against the oracle on the logical keys
+    T = 6
+    seq = (np.arange(T) % B).astype(np.int32)
+    pos = np.array([L - 1, L - 1, L - 9, 1500, 700, L // 2], np.int64)
+    qd, qs, _ = gen.mxfp4(831, 1, T * h_i, d_i)
+    qd, qs = qd.reshape(T, h_i, -1), qs.reshape(T, h_i, -1)
+    w = gen.pow2_weights(831, 2, (T, h_i))
+    ref = orc.index_scores(qd, qs, w, seq, pos, ref_d, ref_s, cap, m, cap).astype(np.float32)
+    ref_i = orc.topk(ref, pos, m, k)
+    args = (dev.t(qd), dev.t(qs), dev.t(w), dev.t(seq), dev.t(pos), keys, m, cap)
+    sc = lib.csa_index_scores(*args)
+    fused = lib.csa_index_topk(*args, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), ref.view(np.uint32)), "paged index scores"
+    assert np.array_equal(fused.cpu().numpy(), ref_i), "fused selection over paged keys"
+    # sequence 0's pages to a file, back into a fresh cache at other physical pages
+    path = str(tmp_path / "prefix.pages")
+    lib.save_pages(path, kv, keys, perm[:npp].tolist())
+    perm2 = rng.permutation(npp + 2)[:npp].astype(np.int32)
+    n2 = (npp + 2) * page
+    kv2 = lib.KvCache(torch.zeros(n2, d - 64, dtype=torch.uint8, device="cuda"),
+                      torch.zeros(n2, 64, dtype=torch.bfloat16, device="cuda"),
+                      torch.zeros(n2, dtype=torch.float32, device="cuda"), cap,
+                      pages=torch.tensor(perm2[None, :], device="cuda"), page=page)
+    keys2 = lib.IndexKeys(torch.zeros(n2, d_i // 2, dtype=torch.uint8, device="cuda"),
+                          torch.zeros(n2, d_i // 32, dtype=torch.uint8, device="cuda"), cap,
+                          pages=torch.tensor(perm2[None, :], device="cuda"), page=page)
+    lib.load_pages(path, kv2, keys2, perm2.tolist())
+    for i in range(npp):
+        a = torch.arange(page, device="cuda")
+        r1, r2 = int(perm[i]) * page + a, int(perm2[i]) * page + a
+        for x, y in ((kv.nope, kv2.nope), (kv.rope, kv2.rope), (kv.scale, kv2.scale), (keys.data, keys2.data),
+                     (keys.scale, keys2.scale)):
+            assert torch.equal(x[r1], y[r2]), f"page {i} differs after the round trip"
+    # the reloaded prefix as sequence 0 of its own cache: same scores, selection and attention
+    rows = np.where(seq == 0)[0]
+    sub = lambda a: np.ascontiguousarray(a[rows])  # noqa: E731
+    a2 = (dev.t(sub(qd)), dev.t(sub(qs)), dev.t(sub(w)), dev.t(np.zeros(len(rows), np.int32)), dev.t(sub(pos)), keys2,
+          m, cap)
+    sc2 = lib.csa_index_scores(*a2)
+    ix2 = lib.csa_index_topk(*a2, k)
+    win = dev.kv_cache(gen.entries(832, 1, B * W, d - 64), W)
+    q = gen.normal_bf16(833, 1, (len(rows), H, d))
+    sm = 1.0 / math.sqrt(d)
+    o1, l1 = lib.csa_sparse_mqa(dev.bf16(q), dev.t(np.zeros(len(rows), np.int32)), dev.t(sub(pos)),
+                                fused[torch.tensor(rows, device="cuda")].contiguous(), m, kv, win, W, sm)
+    o2, l2 = lib.csa_sparse_mqa(dev.bf16(q), dev.t(np.zeros(len(rows), np.int32)), dev.t(sub(pos)), ix2, m, kv2, win,
+                                W, sm)
+    torch.cuda.synchronize()
+    assert np.array_equal(sc2.cpu().numpy().view(np.uint32), ref[rows].view(np.uint32))
+    assert np.array_equal(ix2.cpu().numpy(), ref_i[rows])
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

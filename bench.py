@@ -678,6 +678,9 @@ def main():
                           "mfma": {"achieved": tot / (sec / args.steps) / 1e12, "peak": 2500.0, "unit": "TFLOP/s",
                                    "frac": tot / (sec / args.steps) / 1e12 / 2500.0}}))
         return
+    if args.workload == "prefill_chunk":
+        print(json.dumps(prefill_measure(args.steps)), flush=True)
+        return
     if args.workload != "csa_decode_1m":
         wl, ds, sec = run_workload(args.workload, args.steps, args.warmup)
         unit = "tokens/s" if args.workload == "prefill_chunk" else "queries/s"

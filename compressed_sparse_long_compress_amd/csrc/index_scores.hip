@@ -58,6 +58,11 @@ __device__ __forceinline__ float order_key_floor(uint32_t key) {
     return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
+// max(x, 0) as one v_med3_f32 (median of x, 0 and FLT_MAX); fmaxf costs a canonicalising max
+// first.  The argument is always a dot product accumulated from +0, which is never -0 (an exact
+// zero sum rounds to +0) and is finite for finite inputs: there both forms give the same bits.
+__device__ __forceinline__ float relu1(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, 3.402823466e38f); }
+
 __device__ __forceinline__ v8i frag16(const uint8_t* p) {
     v4i x = *(const v4i*)p;
     v8i r = {x[0], x[1], x[2], x[3], 0, 0, 0, 0};
@@ -133,10 +138,10 @@ __global__ __launch_bounds__(256) void k_index_rows(const uint8_t* __restrict__ 
             v4f acc = {0.f, 0.f, 0.f, 0.f};
             const v8i bf = {bk[u][0], bk[u][1], bk[u][2], bk[u][3], 0, 0, 0, 0};
             acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bf, acc, 4, 4, 0, sa, 0, sb[u]);
-            float p = wr[0] * fmaxf(acc[0], 0.f);
-            p = fmaf(wr[1], fmaxf(acc[1], 0.f), p);
-            p = fmaf(wr[2], fmaxf(acc[2], 0.f), p);
-            p = fmaf(wr[3], fmaxf(acc[3], 0.f), p);
+            float p = wr[0] * relu1(acc[0]);
+            p = fmaf(wr[1], relu1(acc[1]), p);
+            p = fmaf(wr[2], relu1(acc[2]), p);
+            p = fmaf(wr[3], relu1(acc[3]), p);
             p = rows4_sum(p);  // the four head groups (exact: every partial sum is representable)
             const int64_t j = j0 + u * 16 + r;
             pv[u] = real(j) < nv ? p : -INFINITY;
@@ -315,10 +320,10 @@ __global__ __launch_bounds__(256) void k_index_rows_grp(const uint8_t* __restric
                 for (int at = 0; at < NA; ++at) {
                     v4f acc = {0.f, 0.f, 0.f, 0.f};
                     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[at], bf, acc, 4, 4, 0, sa[at], 0, sb[u]);
-                    float p = wr[at][0] * fmaxf(acc[0], 0.f);
-                    p = fmaf(wr[at][1], fmaxf(acc[1], 0.f), p);
-                    p = fmaf(wr[at][2], fmaxf(acc[2], 0.f), p);
-                    p = fmaf(wr[at][3], fmaxf(acc[3], 0.f), p);
+                    float p = wr[at][0] * relu1(acc[0]);
+                    p = fmaf(wr[at][1], relu1(acc[1]), p);
+                    p = fmaf(wr[at][2], relu1(acc[2]), p);
+                    p = fmaf(wr[at][3], relu1(acc[3]), p);
                     if (GPQ == 2) {
                         // the row's two lane groups (exact: every partial sum is representable)
                         const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(p), __float_as_uint(p), false, false);
@@ -537,21 +542,24 @@ __global__ __launch_bounds__(256, HI == 8 ? 2 : 1) void k_index_gemm(const uint8
                 const float* wr = kLdsW ? lw[wave][at][g2] : wt[kLdsW ? 0 : at];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float p = wr[4 * i] * fmaxf(acc[4 * i], 0.f);
-                    p = fmaf(wr[4 * i + 1], fmaxf(acc[4 * i + 1], 0.f), p);
-                    p = fmaf(wr[4 * i + 2], fmaxf(acc[4 * i + 2], 0.f), p);
-                    p = fmaf(wr[4 * i + 3], fmaxf(acc[4 * i + 3], 0.f), p);
+                    float p = wr[4 * i] * relu1(acc[4 * i]);
+                    p = fmaf(wr[4 * i + 1], relu1(acc[4 * i + 1]), p);
+                    p = fmaf(wr[4 * i + 2], relu1(acc[4 * i + 2]), p);
+                    p = fmaf(wr[4 * i + 3], relu1(acc[4 * i + 3]), p);
                     part[i] = p;
                 }
                 if constexpr (HI == 8) {
-                    // query i of the tile = regs 4i..4i+3; heads split over lane halves
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) part[i] += __shfl_xor(part[i], 32);
-                    // lanes < 32 store queries 0,1; lanes >= 32 store queries 2,3
+                    // query i of the tile = regs 4i..4i+3, its heads split over the lane halves.
+                    // Lanes < 32 keep queries 0, 1 and lanes >= 32 queries 2, 3: one swap of the
+                    // halves of (part[i], part[2 + i]) hands each lane its partner's half of the
+                    // query it keeps, and the two results sum to it (own + partner, either order)
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
-                        if constexpr (MODE == kEmit) emit(at, i, j, g2 ? part[2 + i] : part[i]);
-                        else if (nvq[at][i] >= 0 && j < c1) put(at, i, j, jr, g2 ? part[2 + i] : part[i]);
+                        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[i]),
+                                                                         __float_as_uint(part[2 + i]), false, false);
+                        const float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                        if constexpr (MODE == kEmit) emit(at, i, j, v);
+                        else if (nvq[at][i] >= 0 && j < c1) put(at, i, j, jr, v);
                     }
                 } else {
                     // query 2i+g2 complete in regs 4i..4i+3
@@ -966,7 +974,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_itk_fallback(
             float p = 0.f;
 #pragma unroll
             for (int hh = 0; hh < 8; ++hh)
-                if (hh < h_i) p = fmaf(wh[hh], fmaxf(acc[hh], 0.f), p);
+                if (hh < h_i) p = fmaf(wh[hh], relu1(acc[hh]), p);
             srow[j] = p;
         }
         __syncthreads();  // the scratch row is complete (and qf no longer read)

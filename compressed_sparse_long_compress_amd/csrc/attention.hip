@@ -907,6 +907,29 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
     }
     lds_barrier();
     const float sfin = s_ref > 0.f ? s_ref : 1.f;
+    if (S > 1) {
+        // the split's partial in the accumulators' own order (k_mqa_combine_sw reads it): lane
+        // (l16, g4) of wave w puts heads 16 ht + 4 g4 + i, i < 4, at its dim of tile dt as 8 bytes
+        // at (((w * 4 + ht) * DT + dt) * 64 + lane) * 4; each head normalised by its own sum
+        _Float16* pw = (_Float16*)part_o + (t * S + s) * (int64_t)H * D;
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) {
+            float inv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float l = sm.lfin[16 * ht + 4 * g4 + i];
+                inv[i] = l > 0.f ? 1.f / l : 0.f;
+            }
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const float f = dt < NN ? sfin : 1.f;
+                const v4h o = {(_Float16)(acc[ht][dt][0] * f * inv[0]), (_Float16)(acc[ht][dt][1] * f * inv[1]),
+                               (_Float16)(acc[ht][dt][2] * f * inv[2]), (_Float16)(acc[ht][dt][3] * f * inv[3])};
+                *(v4h*)(pw + (((wave * 4 + ht) * DT + dt) * 64 + lane) * 4) = o;
+            }
+        }
+        return;
+    }
     float* ob = (float*)&sm.kv[0][0];  // the tiles are no longer read
     static_assert(32 * kOutStride<D> * sizeof(float) <= sizeof(sm.kv), "32 staged output rows fit the tile buffers");
 #pragma unroll
@@ -1528,6 +1551,95 @@ __global__ __launch_bounds__(128) void k_mqa_combine16(const _Float16* __restric
     if (tid == 0) lse[th] = L > 0.f ? M + __logf(L) : -INFINITY;
 }
 
+// Merge of k_mqa64's split partials, stored in its accumulators' order (see its epilogue): one
+// one-wave workgroup per (row, 16-head tile ht, producer wave w, dim tile dt), a lane per 8-byte
+// quad (heads 16 ht + 4 g4 + i, i < 4, at one dim), so each split's load is one 512-byte wave
+// row; small workgroups spread the partials' lines over many CUs (a CU keeps only so many
+// misses in flight).  The 16 heads' weights e^(m_s - M) l_s / L (L summed in a fixed order) go
+// through LDS while the quads' loads are in flight.
+template <int D>
+__global__ __launch_bounds__(64) void k_mqa_combine_sw(const _Float16* __restrict__ part_o,
+                                                       const float* __restrict__ part_ml,
+                                                       const int64_t* __restrict__ pos, int S, RopeTab rt,
+                                                       float* __restrict__ out, float* __restrict__ lse) {
+    constexpr int H = 64, DN = D - 64, NN = DN / 64, DT = NN + 1, NTH = 64;
+    constexpr int SMAX = 64;
+    __shared__ float wg[16][SMAX];
+    static_assert(NTH == 4 * 16, "four lanes per head for the weights");
+    const int64_t t = blockIdx.x / (16 * DT);
+    const int r = blockIdx.x % (16 * DT);
+    const int ht = r / (4 * DT), w = (r / DT) & 3, dt = r % DT;
+    const int tid = threadIdx.x;
+    const int lane = tid, l16 = lane & 15, g4 = lane >> 4;
+    const _Float16* base = part_o + t * (int64_t)S * H * D + (((w * 4 + ht) * DT + dt) * 64 + lane) * 4;
+    v4h v[kC16Reg];
+#pragma unroll
+    for (int s = 0; s < kC16Reg; ++s)
+        if (s < S) v[s] = *(const v4h*)(base + (int64_t)s * H * D);
+    // the 16 heads' merge weights: lane (h = lane / 4, q = lane % 4) takes splits q, q + 4, ...
+    // (every (m, l) load in flight at once); M and L over the four lanes of a head by a fixed
+    // butterfly, so every lane of the quad holds the same bits
+    {
+        constexpr int PERL = SMAX / 4;
+        const int h = tid >> 2, q = tid & 3;
+        float2 ml[PERL];
+#pragma unroll
+        for (int i = 0; i < PERL; ++i) {
+            const int sp = q + 4 * i;
+            ml[i] = sp < S ? *(const float2*)(part_ml + ((t * S + sp) * H + 16 * ht + h) * 2)
+                           : make_float2(-INFINITY, 0.f);
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < PERL; ++i) M = fmaxf(M, ml[i].x);
+        M = fmaxf(M, __shfl_xor(M, 1));
+        M = fmaxf(M, __shfl_xor(M, 2));
+        float ls[PERL];
+        float L = 0.f;
+#pragma unroll
+        for (int i = 0; i < PERL; ++i) {
+            ls[i] = ml[i].x == -INFINITY ? 0.f : ml[i].y * __expf(ml[i].x - M);
+            L += ls[i];
+        }
+        L += __shfl_xor(L, 1);
+        L += __shfl_xor(L, 2);
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+        for (int i = 0; i < PERL; ++i)
+            if (q + 4 * i < S) wg[h][q + 4 * i] = ls[i] * inv;
+        if (q == 0 && w == 0 && dt == 0) lse[t * H + 16 * ht + h] = L > 0.f ? M + __logf(L) : -INFINITY;
+    }
+    __syncthreads();
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+    auto acc = [&](const v4h x, int sp) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = fmaf(wg[4 * g4 + i][sp], (float)x[i], o[i]);
+    };
+#pragma unroll
+    for (int s = 0; s < kC16Reg; ++s)
+        if (s < S) acc(v[s], s);
+    for (int s = kC16Reg; s < S; ++s) acc(*(const v4h*)(base + (int64_t)s * H * D), s);
+    int d;
+    if (dt < NN) {
+        d = 16 * (NN * w + dt) + l16;
+    } else {
+        // RoPE dims: undo the rotation by tp; the pair's other dim is in lane l16 ^ 1
+        d = DN + 16 * w + l16;
+        float cs, sn;
+        angle_cs((double)pos[t], rt.theta[(d - DN) >> 1], cs, sn);
+        sn = -sn;
+        const bool odd = (l16 & 1) != 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float p = __shfl_xor(o[i], 1);
+            const float x0 = odd ? p : o[i], x1 = odd ? o[i] : p;
+            o[i] = odd ? x0 * sn + x1 * cs : x0 * cs - x1 * sn;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[(t * H + 16 * ht + 4 * g4 + i) * (int64_t)D + d] = o[i];
+}
+
 // Range check of the entries a call reads (debug builds of a caller's pipeline): the
 // 64-head kernels stage the bf16 RoPE dims as fp16 with truncation, so a value of magnitude
 // above 65504 (or a NaN / infinity) would be clamped.  One workgroup per row walks the row's
@@ -1596,13 +1708,20 @@ static void launch_mqa_t(const uint16_t* q, const int32_t* seq, const int64_t* p
         CSA_MQA_LAUNCH((k_mqa<H, D>), 256);
     }
 #undef CSA_MQA_LAUNCH
-    if (S > 1)
-        if constexpr (H == 64)
-            hipLaunchKernelGGL((k_mqa_combine16<D>), dim3((unsigned)(T * H)), dim3(128), 0, st, (const _Float16*)po, pml,
-                               pos, H, S, rt, out, lse);
-        else
-        hipLaunchKernelGGL((k_mqa_combine<D>), dim3((unsigned)(T * H)), dim3(128), 0, st, po, pml, pos, H, S, rt, out,
-                           lse);
+    if (S > 1) {
+        if constexpr (H == 64) {
+            // the two-role kernel writes head-major partials, k_mqa64 its accumulators' order
+            if (D == 512 && long_splits)
+                hipLaunchKernelGGL((k_mqa_combine16<D>), dim3((unsigned)(T * H)), dim3(128), 0, st, (const _Float16*)po,
+                                   pml, pos, H, S, rt, out, lse);
+            else
+                hipLaunchKernelGGL((k_mqa_combine_sw<D>), dim3((unsigned)(T * 16 * (D / 64))), dim3(64), 0, st,
+                                   (const _Float16*)po, pml, pos, S, rt, out, lse);
+        } else {
+            hipLaunchKernelGGL((k_mqa_combine<D>), dim3((unsigned)(T * H)), dim3(128), 0, st, po, pml, pos, H, S, rt,
+                               out, lse);
+        }
+    }
 }
 
 hipError_t launch_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, int H, int d,

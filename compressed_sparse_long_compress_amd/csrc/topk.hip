@@ -109,6 +109,37 @@ __device__ __forceinline__ uint32_t jth_largest8(const uint32_t* v, int j) {
     return r;
 }
 
+// Keys of B 16-byte pieces (4 columns from col[b]; 0 past nv) of a row.  Aligned rows: every
+// piece's load is issued before the first is used (a load per piece inside the branch that
+// handles a partial piece would wait for each in turn); a piece reaching past nv loads the
+// row's first 16 bytes instead and is re-read by element.
+template <int B>
+__device__ __forceinline__ void group_pieces(const float* __restrict__ row, int nv, bool vec, const int (&col)[B],
+                                             uint32_t (&key)[B][4]) {
+    if (vec) {
+        float4 x[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) x[b] = *(const float4*)(row + (col[b] + 4 <= nv ? col[b] : 0));
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (col[b] + 4 <= nv) {
+                key[b][0] = f32_order_key(x[b].x);
+                key[b][1] = f32_order_key(x[b].y);
+                key[b][2] = f32_order_key(x[b].z);
+                key[b][3] = f32_order_key(x[b].w);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) key[b][e] = col[b] + e < nv ? f32_order_key(row[col[b] + e]) : 0u;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) key[b][e] = col[b] + e < nv ? f32_order_key(row[col[b] + e]) : 0u;
+    }
+}
+
 struct TcRec {  // per (row, slice): candidates written (may exceed the slice), tau, the row's largest key
     uint32_t n, tau, hi, pad;
 };
@@ -231,17 +262,8 @@ __global__ __launch_bounds__(kTcThreads) void k_topk_cand(const float* __restric
             for (int b = 0; b < B; ++b) {
                 const int u = u0 + b * NT + tid;
                 col[b] = u < nq * 8 ? (int)glist[u >> 3] * GS + (u & 7) * 4 : nv;
-                if (vec && col[b] + 4 <= nv) {
-                    const float4 x = *(const float4*)(row + col[b]);
-                    key[b][0] = f32_order_key(x.x);
-                    key[b][1] = f32_order_key(x.y);
-                    key[b][2] = f32_order_key(x.z);
-                    key[b][3] = f32_order_key(x.w);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) key[b][e] = col[b] + e < nv ? f32_order_key(row[col[b] + e]) : 0u;
-                }
             }
+            group_pieces<B>(row, nv, vec, col, key);
             int c = 0;
 #pragma unroll
             for (int b = 0; b < B; ++b)

@@ -428,6 +428,8 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
 // ---------------------------------------------------------------------------
 constexpr float kLazy = 8.f;     // e^8 ~ 2981
 constexpr float kSRatio = 16.f;  // 2981 * 16 < 65504
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
@@ -985,6 +987,8 @@ struct __align__(16) MqaWsSmem {
     float sfin;
     const uint8_t* kaddr[2][RB][2];
     float kscl[2][RB];  // entry scale, -1 for a masked position
+    float tmax[2][RB / KT];     // per tile: the largest entry scale (-1: no position visible)
+    uint32_t tfull[2][RB / KT];  // per tile: every position visible
     float cs[64];
     int restart;
 };
@@ -1065,7 +1069,18 @@ __global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q,
     auto publish = [&](int b, const Res& r, float sc) {
         sm.kaddr[b][vt][0] = r.an;
         sm.kaddr[b][vt][1] = r.ar;
-        sm.kscl[b][vt] = r.ok ? sc : -1.f;
+        const float v = r.ok ? sc : -1.f;
+        sm.kscl[b][vt] = v;
+        // per 32-position tile (a half of this wave): the largest entry scale (-1 when none is
+        // visible) and whether every position is visible, so the scores role skips its masking
+        float mx = v;
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        const uint64_t bad = __ballot(v < 0.f);
+        if ((vt & 31) == 0) {
+            sm.tmax[b][vt >> 5] = mx;
+            sm.tfull[b][vt >> 5] = (uint32_t)(bad >> (lane & 32)) == 0u ? 1 : 0;
+        }
     };
 
     if (tid < 32) {
@@ -1204,7 +1219,7 @@ __global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q,
                 int shq = mx > 0.f ? 15 - ex : 0;
                 shq = shq < -100 ? -100 : (shq > 100 ? 100 : shq);
                 const float qs = ldexpf(1.f, shq);
-                sm_q = sm_scale * ldexpf(1.f, -shq);
+                sm_q = sm_scale * ldexpf(1.f, -shq) * kLog2e;  // scores kept in log2 units
 #pragma unroll
                 for (int st = 0; st < DSTEP; ++st) {
                     const uint16_t* hv = (const uint16_t*)&raw[st];
@@ -1215,6 +1230,7 @@ __global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q,
                 }
             }
             float m_ref = m_seen, s_ref = s_seen, l_run = 0.f;
+            float inv_s = s_ref > 0.f ? 1.f / s_ref : 0.f;
             constexpr int QG = 2;
             static_assert(DSTEP % QG == 0, "whole groups");
             for (int it = 0; it <= nt; ++it) {
@@ -1224,6 +1240,8 @@ __global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q,
                     const int j = it;
                     const float* tscl = sm.kscl[(j / TPB) & 1] + (j % TPB) * KT;
                     const float4 s0 = *(const float4*)(tscl + 4 * g4), s1 = *(const float4*)(tscl + 16 + 4 * g4);
+                    const float st_max = fmaxf(sm.tmax[(j / TPB) & 1][j % TPB], 0.f);  // over the tile's 32 keys
+                    const bool full = __builtin_amdgcn_readfirstlane(sm.tfull[(j / TPB) & 1][j % TPB]) != 0;
                     // S^T (keys x heads) of tile j for this wave's 16 heads: FP8-dim and RoPE-dim parts
                     v4f an[2], ar[2];
                     {
@@ -1263,13 +1281,15 @@ __global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q,
                     // scores and P of tile j for head hq: lane (l16, g4) holds keys 4 g4 + i and 16 + 4 g4 + i
                     const float kscl[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
                     float sv[8];
-                    float st_max = 0.f;
+                    if (full) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        sv[i] = kscl[i] >= 0.f ? sm_q * fmaf(kscl[i], an[i >> 2][i & 3], ar[i >> 2][i & 3]) : -INFINITY;
-                        st_max = fmaxf(st_max, kscl[i]);
+                        for (int i = 0; i < 8; ++i) sv[i] = sm_q * fmaf(kscl[i], an[i >> 2][i & 3], ar[i >> 2][i & 3]);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            sv[i] = kscl[i] >= 0.f ? sm_q * fmaf(kscl[i], an[i >> 2][i & 3], ar[i >> 2][i & 3])
+                                                   : -INFINITY;
                     }
-                    st_max = rows4_max(st_max);  // over the tile's 32 keys
                     float mx = sv[0];
 #pragma unroll
                     for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
@@ -1277,14 +1297,16 @@ __global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q,
                     m_seen = fmaxf(m_seen, mx);
                     s_seen = fmaxf(s_seen, st_max);
                     m_ref = m_ref == -INFINITY ? mx : m_ref;  // first tile with visible keys (accumulators still zero)
-                    s_ref = s_ref == 0.f ? st_max : s_ref;
-                    if (mx > m_ref + kLazy || st_max > kSRatio * s_ref) sm.restart = 1;
-                    const float inv_s = s_ref > 0.f ? 1.f / s_ref : 0.f;
+                    if (s_ref == 0.f && st_max > 0.f) {     // (the same in every lane)
+                        s_ref = st_max;
+                        inv_s = 1.f / s_ref;
+                    }
+                    if (mx > m_ref + kLazy * kLog2e || st_max > kSRatio * s_ref) sm.restart = 1;
                     v8h pn, pr;
                     float sum = 0.f;
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
-                        const float p = m_ref == -INFINITY ? 0.f : __expf(sv[i] - m_ref);
+                        const float p = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_ref);
                         sum += p;
                         pr[i] = (_Float16)p;
                         pn[i] = (_Float16)(p * (kscl[i] * inv_s));
@@ -1296,16 +1318,17 @@ __global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q,
                 lds_barrier();
             }
             // hand the head's references and sum to the values role; lse / partial statistics
+            const float m_nat = m_ref * kLn2;  // back to natural units
             if (g4 == 0) {
-                sm.mfin[hq] = m_ref;
+                sm.mfin[hq] = m_nat;
                 sm.lfin[hq] = l_run;
             }
             if (tid == 0) sm.sfin = s_ref > 0.f ? s_ref : 1.f;
             const bool redo = !second && sm.restart != 0;
             if (!redo && g4 == 0) {
-                if (S == 1) lse[t * H + hq] = l_run > 0.f ? m_ref + __logf(l_run) : -INFINITY;
+                if (S == 1) lse[t * H + hq] = l_run > 0.f ? m_nat + __logf(l_run) : -INFINITY;
                 else {
-                    part_ml[((t * S + s) * H + hq) * 2 + 0] = m_ref;
+                    part_ml[((t * S + s) * H + hq) * 2 + 0] = m_nat;
                     part_ml[((t * S + s) * H + hq) * 2 + 1] = l_run;
                 }
             }

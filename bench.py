@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (scaled by a 256 MiB copy: fetch x2.0,
 # write x1.0; see profiles/csa_decode_1m_hbm_counters.md), valid for the kernel
 # source with this SHA-256 only.
-INDEX_TRAFFIC = {"sha256": "980df2241730cd3587bdaeb5eb0fed177402d1296f473bae0aa8db8bb13c9afe", "bytes": 75732059}
+INDEX_TRAFFIC = {"sha256": "63b040e9ed4e8f8c64eb6e9163c9425101ff0e95577726c0c68239beca0d7573", "bytes": 75746388}
 
 
 def log(msg):

@@ -1172,13 +1172,19 @@ __global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q,
     float* ob = (float*)&sm.kv[0][0];  // output staging, once the tiles are no longer read
     static_assert(32 * kOutStride<D> * sizeof(float) <= sizeof(sm.kv), "32 staged output rows fit the tile buffers");
     auto run_pass = [&](bool second) -> bool {
-        // batch 0 of the positions, tile 0 staged, tile 1 in flight
+        // batch 0 of the positions: row addresses published at once, the entry scales once tile
+        // 0's loads are in flight; then tile 0 staged, tile 1 in flight
+        Res r0{g_zero_entry, g_zero_entry + DN, nullptr, false};
+        float sc0 = 0.f;
         if (!scores_role) {
-            const Res r = resolve_at(u0 + vt, fetch(u0 + vt));
-            publish(0, r, r.ok ? gload<float>((const uint8_t*)r.sp) : 0.f);
+            r0 = resolve_at(u0 + vt, fetch(u0 + vt));
+            sm.kaddr[0][vt][0] = r0.an;
+            sm.kaddr[0][vt][1] = r0.ar;
+            if (r0.ok) sc0 = gload<float>((const uint8_t*)r0.sp);
         }
         lds_barrier();
         if (nt > 0) issue(0);
+        if (!scores_role) publish(0, r0, sc0);
         if (nt > 0) stage(0);
         if (nt > 1) issue(1);
         lds_barrier();

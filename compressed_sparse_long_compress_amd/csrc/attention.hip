@@ -927,7 +927,10 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
                 const float f = dt < NN ? sfin : 1.f;
                 const v4h o = {(_Float16)(acc[ht][dt][0] * f * inv[0]), (_Float16)(acc[ht][dt][1] * f * inv[1]),
                                (_Float16)(acc[ht][dt][2] * f * inv[2]), (_Float16)(acc[ht][dt][3] * f * inv[3])};
-                *(v4h*)(pw + (((wave * 4 + ht) * DT + dt) * 64 + lane) * 4) = o;
+                // streamed past the L2 (read once, by the merge kernel): less to write back at the
+                // kernel's end, which the merge would otherwise wait for
+                __builtin_nontemporal_store(__builtin_bit_cast(v2u, o),
+                                            (v2u*)(pw + (((wave * 4 + ht) * DT + dt) * 64 + lane) * 4));
             }
         }
         return;

@@ -501,7 +501,9 @@ __device__ __forceinline__ void store_out(const float* ob, const float* cs, int 
                 const float c0 = cs[2 * p], s0 = -cs[2 * p + 1], c1 = cs[2 * p + 2], s1 = -cs[2 * p + 3];
                 v = make_float4(v.x * c0 - v.y * s0, v.x * s0 + v.y * c0, v.z * c1 - v.w * s1, v.z * s1 + v.w * c1);
             }
-            *(float4*)(out + (t * H + h0 + r) * (int64_t)D + d) = v;
+            // streamed past the L2: the output is not read again here, and the L2 keeps the
+            // entries the other rows gather
+            __builtin_nontemporal_store(v4f{v.x, v.y, v.z, v.w}, (v4f*)(out + (t * H + h0 + r) * (int64_t)D + d));
         }
     } else {
 #pragma unroll

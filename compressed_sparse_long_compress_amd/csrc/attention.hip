@@ -1202,7 +1202,8 @@ __global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q,
                 const uint16_t* qrow = q + (t * H + hq) * (int64_t)D;
                 v4i raw[DSTEP];
 #pragma unroll
-                for (int st = 0; st < DSTEP; ++st) raw[st] = *(const v4i*)(qrow + 32 * st + 8 * g4);
+                for (int st = 0; st < DSTEP; ++st)  // read once: nontemporal, the L2 keeps the entries
+                    raw[st] = __builtin_nontemporal_load((const v4i*)(qrow + 32 * st + 8 * g4));
                 float xr[DSTEP - NSTEP][8];
                 float mx = 0.f;
 #pragma unroll

@@ -484,6 +484,15 @@ __global__ __launch_bounds__(256, HI == 8 ? 2 : 1) void k_index_gemm(const uint8
                 ia.samp[(tq0 + qj) * ia.n_s + j] = jr < nv ? f32_order_key(v) : 0u;
             }
         };
+        // kEmit: first candidate slot of query slot (at, i) in this workgroup's segment, split
+        // into a part common to the wave (scalar registers) and the lane half's offset
+        int64_t cbu[NA][NI];
+#pragma unroll
+        for (int at = 0; at < NA; ++at)
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+                cbu[at][i] = ((tq0 + at * QA + (HI == 8 ? i : 2 * i)) * (int64_t)gridDim.x + blockIdx.x) * ia.cap;
+        const int64_t cg2 = (HI == 8 ? 2 : 1) * (int64_t)g2 * gridDim.x * ia.cap;
         // kEmit: the candidates of query slot (at, i), both half-waves (every lane calls it)
         auto emit = [&](int at, int i, int64_t j, float v) {
             const bool pass = nvq[at][i] >= 0 && j < c1 && j < nvq[at][i] && v >= tq[at][i];
@@ -492,11 +501,8 @@ __global__ __launch_bounds__(256, HI == 8 ? 2 : 1) void k_index_gemm(const uint8
             const uint32_t lo = (uint32_t)mk, hi = (uint32_t)(mk >> 32);
             if (pass) {
                 const uint32_t sl = (g2 ? ec[at][i][1] : ec[at][i][0]) + (uint32_t)__popc((g2 ? hi : lo) & ((1u << r) - 1u));
-                if (sl < (uint32_t)ia.cap) {
-                    const int qj = at * QA + (HI == 8 ? 2 * g2 + i : 2 * i + g2);
-                    ia.cand[((tq0 + qj) * (int64_t)gridDim.x + blockIdx.x) * ia.cap + sl] =
-                        ((uint64_t)f32_order_key(v) << 32) | (uint32_t)~(uint32_t)j;
-                }
+                if (sl < (uint32_t)ia.cap)
+                    ia.cand[cbu[at][i] + cg2 + sl] = ((uint64_t)f32_order_key(v) << 32) | (uint32_t)~(uint32_t)j;
             }
             ec[at][i][0] = __builtin_amdgcn_readfirstlane(ec[at][i][0] + (uint32_t)__popc(lo));
             ec[at][i][1] = __builtin_amdgcn_readfirstlane(ec[at][i][1] + (uint32_t)__popc(hi));

@@ -415,6 +415,15 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
 // K-slot order (both MFMAs): lane group g holds keys 4g..4g+3 and
 // 16+4g..16+4g+3, exactly the keys of its QK accumulator rows.
 //
+// Head split (HS = 2, for grids that would leave most CUs idle): a pair of
+// workgroups shares a (row, split), each taking 32 of the heads, so each
+// stages the same tiles but does half the MFMA work per tile.  Wave w then
+// computes S^T for the 16 heads 16 (w & 1) of its half over keys
+// 16 (w >> 1)..+15 of the tile, P goes through LDS in natural key order, and
+// the two key halves of a head meet through LDS: their maxima at the first
+// visible tile (the reference) and before a second pass, their sums at the end.
+// PV is split over dims as above, for the workgroup's 32 heads.
+//
 // Fixed references instead of a running rescale: each head's reference max
 // m_ref is the max of the first tile with visible keys, and S_ref (the FP8
 // part's scale reference) is that tile's largest entry scale.  P = exp(s -
@@ -447,6 +456,7 @@ struct __align__(16) Mqa64Smem {
     _Float16 pn[64 * PS];  // [head][K slot] P * scale_j / S_ref (FP8 dims)
     _Float16 pr[64 * PS];  // [head][K slot] P (RoPE dims)
     float lfin[64];
+    float hx[2][32];  // two workgroups per row: per key half, the maxima one half hands the other
     // two batches of resolved key-list positions: FP8-row and RoPE-row
     // addresses, entry scale (0 when masked) and visibility
     const uint8_t* kaddr[2][RB][2];
@@ -517,13 +527,15 @@ __device__ __forceinline__ void store_out(const float* ob, const float* cs, int 
     }
 }
 
-template <int D, bool PG>  // PG: a view is paged
+template <int D, bool PG, int HS>  // PG: a view is paged; HS: workgroups per (row, split), 1 or 2
 __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, const int32_t* __restrict__ seq,
                                                const int64_t* __restrict__ pos, const int32_t* __restrict__ idx, int k,
                                                int m, KvView comp, KvView win, int window, float sm_scale, RopeTab rt,
                                                int S, float* __restrict__ out, float* __restrict__ lse,
                                                float* __restrict__ part_o, float* __restrict__ part_ml) {
     constexpr int H = 64;
+    static_assert(HS == 1 || HS == 2, "64 or 32 heads per workgroup");
+    constexpr int NHT = 4 / HS;  // 16-head tiles of the workgroup in PV
     using Sm = Mqa64Smem<D>;
     constexpr int KS = Sm::KS;
     constexpr int DN = D - 64;
@@ -539,10 +551,15 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
     __shared__ Sm sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
-    const int64_t t = blockIdx.x / S;
-    const int s = blockIdx.x % S;
+    // HS == 2: workgroups 2p and 2p + 1 take heads [0, 32) and [32, 64) of pair p = (row, split)
+    const int hh = HS == 1 ? 0 : (int)(blockIdx.x & 1);
+    const unsigned pair = blockIdx.x / HS;
+    const int64_t t = pair / (unsigned)S;
+    const int s = (int)(pair % (unsigned)S);
+    const int kh = HS == 1 ? 0 : wave >> 1;                            // HS == 2: the wave's key half
+    const int hl = HS == 1 ? wave * 16 + l16 : 16 * (wave & 1) + l16;  // the lane's head in the workgroup
     // the query's loads go first: they depend on nothing but the row
-    const int hq = wave * 16 + l16;
+    const int hq = 32 * hh + hl;
     v4i qraw[DSTEP];
     {
         const uint16_t* qrow = q + (t * H + hq) * (int64_t)D;
@@ -717,47 +734,50 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
         }
     };
 
-    v4f acc[4][DT];
+    v4f acc[NHT][DT];
     float m_ref = -INFINITY, l_run = 0.f, s_ref = 0.f;
     float m_seen = -INFINITY, s_seen = 0.f;  // maxima over every tile seen (second-pass references)
     int64_t nraw = 0;  // this thread's position in the next batch: selected index, then resolved
     Res nres{g_zero_entry, g_zero_entry + DN, nullptr, false};
     float nscl = 0.f;
 
-    // S^T (keys x heads) of tile j for this wave's 16 heads: FP8-dim and RoPE-dim parts
-    // K fragments go in groups of QG dim steps, the next group's loads issued before this
-    // group's MFMAs (the scheduler is not allowed to sink them: 2 QG loads in flight).
-    constexpr int QG = 4;
+    // S^T (keys x heads) of tile j for this wave's 16 heads: FP8-dim and RoPE-dim parts, over
+    // NKB 16-key blocks (HS == 1: both of the tile; HS == 2: the wave's key half).
+    // K fragments go in groups of QG dim steps (8 loads a group), the next group's loads issued
+    // before this group's MFMAs (the scheduler is not allowed to sink them: two groups in flight).
+    constexpr int NKB = 2 / HS;
+    constexpr int QG = 8 / NKB < DSTEP ? 8 / NKB : DSTEP;
     static_assert(DSTEP % QG == 0, "whole groups");
-    auto qk = [&](int j, v4f (&an)[2], v4f (&ar)[2]) {
-        const _Float16* kb = sm.kv[j % 3] + l16 * KS + 8 * g4;
-        an[0] = an[1] = ar[0] = ar[1] = v4f{0.f, 0.f, 0.f, 0.f};
-        v8h kf[2][2 * QG];
+    auto qk = [&](int j, v4f (&an)[NKB], v4f (&ar)[NKB]) {
+        const _Float16* kb = sm.kv[j % 3] + (16 * kh + l16) * KS + 8 * g4;
 #pragma unroll
-        for (int e = 0; e < QG; ++e) {
-            kf[0][2 * e] = *(const v8h*)(kb + 32 * e);
-            kf[0][2 * e + 1] = *(const v8h*)(kb + 16 * KS + 32 * e);
-        }
+        for (int b = 0; b < NKB; ++b) an[b] = ar[b] = v4f{0.f, 0.f, 0.f, 0.f};
+        v8h kf[2][NKB * QG];
+#pragma unroll
+        for (int e = 0; e < QG; ++e)
+#pragma unroll
+            for (int b = 0; b < NKB; ++b) kf[0][NKB * e + b] = *(const v8h*)(kb + 16 * KS * b + 32 * e);
 #pragma unroll
         for (int g = 0; g < DSTEP / QG; ++g) {
             if (g + 1 < DSTEP / QG) {
 #pragma unroll
                 for (int e = 0; e < QG; ++e) {
                     const int st = (g + 1) * QG + e;
-                    kf[(g + 1) & 1][2 * e] = *(const v8h*)(kb + 32 * st);
-                    kf[(g + 1) & 1][2 * e + 1] = *(const v8h*)(kb + 16 * KS + 32 * st);
+#pragma unroll
+                    for (int b = 0; b < NKB; ++b)
+                        kf[(g + 1) & 1][NKB * e + b] = *(const v8h*)(kb + 16 * KS * b + 32 * st);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int e = 0; e < QG; ++e) {
                 const int st = g * QG + e;
-                if (st < NSTEP) {
-                    an[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[g & 1][2 * e], qf[st], an[0], 0, 0, 0);
-                    an[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[g & 1][2 * e + 1], qf[st], an[1], 0, 0, 0);
-                } else {
-                    ar[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[g & 1][2 * e], qf[st], ar[0], 0, 0, 0);
-                    ar[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[g & 1][2 * e + 1], qf[st], ar[1], 0, 0, 0);
+#pragma unroll
+                for (int b = 0; b < NKB; ++b) {
+                    if (st < NSTEP)
+                        an[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[g & 1][NKB * e + b], qf[st], an[b], 0, 0, 0);
+                    else
+                        ar[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[g & 1][NKB * e + b], qf[st], ar[b], 0, 0, 0);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -769,7 +789,7 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
         s0 = *(const float4*)(tscl + 4 * g4);
         s1 = *(const float4*)(tscl + 16 + 4 * g4);
     };
-    // scores and P of tile j for head hq; returns whether a reference is exceeded
+    // scores and P of tile j for head hl; returns whether a reference is exceeded
     auto softmax = [&](const float4& s0, const float4& s1, const v4f (&an)[2], const v4f (&ar)[2]) -> bool {
         const float kscl[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
         float sv[8];
@@ -800,25 +820,71 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
             pn[i] = (_Float16)(p * (kscl[i] * inv_s));
         }
         l_run += rows4_sum(sum);
-        *(v8h*)(sm.pn + hq * Sm::PS + 8 * g4) = pn;
-        *(v8h*)(sm.pr + hq * Sm::PS + 8 * g4) = pr;
+        *(v8h*)(sm.pn + hl * Sm::PS + 8 * g4) = pn;
+        *(v8h*)(sm.pr + hl * Sm::PS + 8 * g4) = pr;
         return over;
     };
-    // O[heads x dims] += P V (tile j) for all heads over this wave's dims
+    // HS == 2: the same over the wave's key half (keys 16 kh + 4 g4 + i of the lane); the
+    // references are the maxima over both halves, which meet in LDS at the first tile with
+    // visible keys (a tile-wide condition, so every wave takes that barrier or none does).
+    // P is stored in natural key order.  l_run sums the wave's half only.
+    bool have_ref = false;
+    auto softmax2 = [&](const float4& s0, const float4& s1, const v4f (&an)[NKB], const v4f (&ar)[NKB]) -> bool {
+        const float4 sk = kh ? s1 : s0;
+        const float kscl[4] = {sk.x, sk.y, sk.z, sk.w};
+        // the tile's largest entry scale, -1 when no key is visible
+        float smx = fmaxf(fmaxf(fmaxf(s0.x, s0.y), fmaxf(s0.z, s0.w)), fmaxf(fmaxf(s1.x, s1.y), fmaxf(s1.z, s1.w)));
+        smx = rows4_max(smx);
+        const float st_max = fmaxf(smx, 0.f);
+        float sv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            sv[i] = kscl[i] >= 0.f ? sm_q * fmaf(kscl[i], an[0][i], ar[0][i]) : -INFINITY;
+        float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        mx = rows4_max(mx);
+        m_seen = fmaxf(m_seen, mx);
+        s_seen = fmaxf(s_seen, st_max);
+        if (!have_ref && __builtin_amdgcn_readfirstlane(smx >= 0.f ? 1 : 0)) {
+            if (g4 == 0) sm.hx[kh][hl] = mx;
+            lds_barrier();
+            m_ref = fmaxf(mx, sm.hx[kh ^ 1][hl]);
+            have_ref = true;
+        }
+        s_ref = s_ref == 0.f ? st_max : s_ref;
+        const bool over = mx > m_ref + kLazy || st_max > kSRatio * s_ref;
+        const float inv_s = s_ref > 0.f ? 1.f / s_ref : 0.f;
+        v4h pn, pr;
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float p = m_ref == -INFINITY ? 0.f : __expf(sv[i] - m_ref);
+            sum += p;
+            pr[i] = (_Float16)p;
+            pn[i] = (_Float16)(p * (kscl[i] * inv_s));
+        }
+        l_run += rows4_sum(sum);
+        *(v4h*)(sm.pn + hl * Sm::PS + 16 * kh + 4 * g4) = pn;
+        *(v4h*)(sm.pr + hl * Sm::PS + 16 * kh + 4 * g4) = pr;
+        return over;
+    };
+    // O[heads x dims] += P V (tile j) for the workgroup's heads over this wave's dims.  The B
+    // fragment of lane (l16, g4) holds the keys of P's K slots 8 g4..8 g4 + 7: keys 4 g4 + r
+    // and 16 + 4 g4 + r (HS == 1), or 8 g4 + r and 8 g4 + 4 + r (HS == 2, natural order).
     auto pv = [&](int j) {
-        const _Float16* vb = sm.kv[j % 3] + (4 * g4 + (l16 >> 2)) * KS + 4 * (l16 & 3);
+        constexpr int VH = HS == 1 ? 16 : 4;  // key offset of the fragment's second half
+        const _Float16* vb = sm.kv[j % 3] + (4 * HS * g4 + (l16 >> 2)) * KS + 4 * (l16 & 3);
         v8h vf[DT];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             const int d0 = dt < NN ? 16 * (NN * wave + dt) : DN + 16 * wave;
             const v4s lo = lds_read_tr16(vb + d0);
-            const v4s hi = lds_read_tr16(vb + 16 * KS + d0);
+            const v4s hi = lds_read_tr16(vb + VH * KS + d0);
             const v8u16 c = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
                              (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
             vf[dt] = __builtin_bit_cast(v8h, c);
         }
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) {
+        for (int ht = 0; ht < NHT; ++ht) {
             const int hr = 16 * ht + l16;
             const v8h pnf = *(const v8h*)(sm.pn + hr * Sm::PS + 8 * g4);
             const v8h prf = *(const v8h*)(sm.pr + hr * Sm::PS + 8 * g4);
@@ -866,22 +932,26 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
             if (nt > 0) issue(0);
         }
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < NHT; ++a)
 #pragma unroll
             for (int b = 0; b < DT; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
         m_ref = m_seen;
         s_ref = s_seen;
         l_run = 0.f;
+        have_ref = m_ref > -INFINITY;  // (the second pass, when a tile was visible: the same in every lane)
         if (nt > 0) stage(0);
         if (nt > 1) issue(1);
         lds_barrier();
         for (int j = 0; j < nt; ++j) {
-            v4f sn[2], sr[2];
+            v4f sn[NKB], sr[NKB];
             batch_begin(j);
             float4 s0, s1;
             tile_scales(j, s0, s1);
             qk(j, sn, sr);
-            if (softmax(s0, s1, sn, sr)) sm.restart = 1;
+            bool over;
+            if constexpr (HS == 1) over = softmax(s0, s1, sn, sr);
+            else over = softmax2(s0, s1, sn, sr);
+            if (over) sm.restart = 1;
             lds_barrier();
             if (j + 1 < nt) stage(j + 1);
             if (j + 2 < nt) issue(j + 2);
@@ -895,21 +965,29 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
         // a tile broke the references: run the split again with the maxima of every tile as the
         // references (no tile can break them); every wave has read the flag before the last barrier
         m_seen = rows4_max(m_seen);
+        if constexpr (HS == 2) {  // and over both key halves
+            if (g4 == 0) sm.hx[kh][hl] = m_seen;
+            lds_barrier();
+            m_seen = fmaxf(m_seen, sm.hx[kh ^ 1][hl]);
+        }
         lds_barrier();
         if (tid == 0) sm.restart = 0;
         run_pass(false);
     }
 
     // ---- epilogue: lane holds heads 16 ht + 4 g4 + i at one dim of each of its dim tiles ----
-    if (g4 == 0) {
-        sm.lfin[hq] = l_run;
-        if (S == 1) lse[t * H + hq] = l_run > 0.f ? m_ref + __logf(l_run) : -INFINITY;
+    // The sum of the workgroup's head h (HS == 2: over both key halves).
+    auto head_sum = [&](int h) { return HS == 1 ? sm.lfin[h] : sm.lfin[h] + sm.lfin[32 + h]; };
+    if (g4 == 0) sm.lfin[HS == 1 ? hl : 32 * kh + hl] = l_run;
+    lds_barrier();
+    if (g4 == 0 && kh == 0) {
+        const float l = head_sum(hl);
+        if (S == 1) lse[t * H + hq] = l > 0.f ? m_ref + __logf(l) : -INFINITY;
         else {
             part_ml[((t * S + s) * H + hq) * 2 + 0] = m_ref;
-            part_ml[((t * S + s) * H + hq) * 2 + 1] = l_run;
+            part_ml[((t * S + s) * H + hq) * 2 + 1] = l;
         }
     }
-    lds_barrier();
     const float sfin = s_ref > 0.f ? s_ref : 1.f;
     if (S > 1) {
         // the split's partial in the accumulators' own order (k_mqa_combine_sw reads it): lane
@@ -917,13 +995,14 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
         // at (((w * 4 + ht) * DT + dt) * 64 + lane) * 4; each head normalised by its own sum
         _Float16* pw = (_Float16*)part_o + (t * S + s) * (int64_t)H * D;
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) {
+        for (int ht = 0; ht < NHT; ++ht) {
             float inv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float l = sm.lfin[16 * ht + 4 * g4 + i];
+                const float l = head_sum(16 * ht + 4 * g4 + i);
                 inv[i] = l > 0.f ? 1.f / l : 0.f;
             }
+            const int htg = NHT * hh + ht;  // the head tile among the row's 64 heads
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const float f = dt < NN ? sfin : 1.f;
@@ -932,7 +1011,7 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
                 // streamed past the L2 (read once, by the merge kernel): less to write back at the
                 // kernel's end, which the merge would otherwise wait for
                 __builtin_nontemporal_store(__builtin_bit_cast(v2u, o),
-                                            (v2u*)(pw + (((wave * 4 + ht) * DT + dt) * 64 + lane) * 4));
+                                            (v2u*)(pw + (((wave * 4 + htg) * DT + dt) * 64 + lane) * 4));
             }
         }
         return;
@@ -940,14 +1019,14 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
     float* ob = (float*)&sm.kv[0][0];  // the tiles are no longer read
     static_assert(32 * kOutStride<D> * sizeof(float) <= sizeof(sm.kv), "32 staged output rows fit the tile buffers");
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < 2 / HS; ++half) {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int ht = 2 * half + hh;
+        for (int hb = 0; hb < 2; ++hb) {
+            const int ht = 2 * half + hb;
             float inv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float l = sm.lfin[16 * ht + 4 * g4 + i];
+                const float l = head_sum(16 * ht + 4 * g4 + i);
                 inv[i] = l > 0.f ? 1.f / l : 0.f;
             }
 #pragma unroll
@@ -957,12 +1036,12 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
                 float o[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) o[i] = acc[ht][dt][i] * (nope ? sfin : 1.f) * inv[i];
-                stage_out(ob, kOutStride<D>, hh, g4, d, o);
+                stage_out(ob, kOutStride<D>, hb, g4, d, o);
             }
         }
         lds_barrier();
-        store_out<D, 256>(ob, sm.cs, 32 * half, tid, t, s, S, out, (_Float16*)part_o);
-        if (half == 0) lds_barrier();
+        store_out<D, 256>(ob, sm.cs, HS == 1 ? 32 * half : 32 * hh, tid, t, s, S, out, (_Float16*)part_o);
+        if (half + 1 < 2 / HS) lds_barrier();
     }
 }
 
@@ -1730,17 +1809,24 @@ static void launch_mqa_t(const uint16_t* q, const int32_t* seq, const int64_t* p
     // splits of more than a few tiles: the two-role kernel (its pipeline costs a step at either end)
     const bool long_splits = (max_keys + S - 1) / S > 12 * KT;
     const bool paged = comp.pages || win.pages;  // paged views: their own instantiation
-#define CSA_MQA_LAUNCH(KERN, NTH)                                                                                  \
-    hipLaunchKernelGGL((KERN), dim3((unsigned)(T * S)), dim3(NTH), 0, st, q, seq, pos, idx, k, m, comp, win, window, \
+    // short splits in a grid of at most half the CUs: two workgroups per (row, split), 32 heads each
+    const bool hsplit = !long_splits && T * S <= 128;
+#define CSA_MQA_LAUNCH(KERN, NTH, NWG)                                                                              \
+    hipLaunchKernelGGL((KERN), dim3((unsigned)(NWG)), dim3(NTH), 0, st, q, seq, pos, idx, k, m, comp, win, window, \
                        sm_scale, rt, S, out, lse, po, pml)
     if (H == 64 && D == 512 && long_splits) {
-        if (paged) CSA_MQA_LAUNCH((k_mqa64ws<512, true>), 512);
-        else CSA_MQA_LAUNCH((k_mqa64ws<512, false>), 512);
+        if (paged) CSA_MQA_LAUNCH((k_mqa64ws<512, true>), 512, T * S);
+        else CSA_MQA_LAUNCH((k_mqa64ws<512, false>), 512, T * S);
     } else if constexpr (H == 64) {
-        if (paged) CSA_MQA_LAUNCH((k_mqa64<D, true>), 256);
-        else CSA_MQA_LAUNCH((k_mqa64<D, false>), 256);
+        if (hsplit) {
+            if (paged) CSA_MQA_LAUNCH((k_mqa64<D, true, 2>), 256, 2 * T * S);
+            else CSA_MQA_LAUNCH((k_mqa64<D, false, 2>), 256, 2 * T * S);
+        } else {
+            if (paged) CSA_MQA_LAUNCH((k_mqa64<D, true, 1>), 256, T * S);
+            else CSA_MQA_LAUNCH((k_mqa64<D, false, 1>), 256, T * S);
+        }
     } else {
-        CSA_MQA_LAUNCH((k_mqa<H, D>), 256);
+        CSA_MQA_LAUNCH((k_mqa<H, D>), 256, T * S);
     }
 #undef CSA_MQA_LAUNCH
     if (S > 1) {

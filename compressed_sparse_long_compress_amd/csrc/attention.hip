@@ -419,7 +419,7 @@ __global__ __launch_bounds__(256) void k_mqa(const uint16_t* __restrict__ q, con
 // workgroups shares a (row, split), each taking 32 of the heads, so each
 // stages the same tiles but does half the MFMA work per tile.  Wave w then
 // computes S^T for the 16 heads 16 (w & 1) of its half over keys
-// 16 (w >> 1)..+15 of the tile, P goes through LDS in natural key order, and
+// 16 (w >> 1)..+15 of the tile, P goes through LDS in the same K-slot order, and
 // the two key halves of a head meet through LDS: their maxima at the first
 // visible tile (the reference) and before a second pass, their sums at the end.
 // PV is split over dims as above, for the workgroup's 32 heads.
@@ -827,7 +827,7 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
     // HS == 2: the same over the wave's key half (keys 16 kh + 4 g4 + i of the lane); the
     // references are the maxima over both halves, which meet in LDS at the first tile with
     // visible keys (a tile-wide condition, so every wave takes that barrier or none does).
-    // P is stored in natural key order.  l_run sums the wave's half only.
+    // P goes to K slots 8 g4 + 4 kh + i, the order of HS == 1.  l_run sums the wave's half only.
     bool have_ref = false;
     auto softmax2 = [&](const float4& s0, const float4& s1, const v4f (&an)[NKB], const v4f (&ar)[NKB]) -> bool {
         const float4 sk = kh ? s1 : s0;
@@ -863,22 +863,21 @@ __global__ __launch_bounds__(256) void k_mqa64(const uint16_t* __restrict__ q, c
             pn[i] = (_Float16)(p * (kscl[i] * inv_s));
         }
         l_run += rows4_sum(sum);
-        *(v4h*)(sm.pn + hl * Sm::PS + 16 * kh + 4 * g4) = pn;
-        *(v4h*)(sm.pr + hl * Sm::PS + 16 * kh + 4 * g4) = pr;
+        *(v4h*)(sm.pn + hl * Sm::PS + 8 * g4 + 4 * kh) = pn;
+        *(v4h*)(sm.pr + hl * Sm::PS + 8 * g4 + 4 * kh) = pr;
         return over;
     };
     // O[heads x dims] += P V (tile j) for the workgroup's heads over this wave's dims.  The B
     // fragment of lane (l16, g4) holds the keys of P's K slots 8 g4..8 g4 + 7: keys 4 g4 + r
-    // and 16 + 4 g4 + r (HS == 1), or 8 g4 + r and 8 g4 + 4 + r (HS == 2, natural order).
+    // and 16 + 4 g4 + r.
     auto pv = [&](int j) {
-        constexpr int VH = HS == 1 ? 16 : 4;  // key offset of the fragment's second half
-        const _Float16* vb = sm.kv[j % 3] + (4 * HS * g4 + (l16 >> 2)) * KS + 4 * (l16 & 3);
+        const _Float16* vb = sm.kv[j % 3] + (4 * g4 + (l16 >> 2)) * KS + 4 * (l16 & 3);
         v8h vf[DT];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             const int d0 = dt < NN ? 16 * (NN * wave + dt) : DN + 16 * wave;
             const v4s lo = lds_read_tr16(vb + d0);
-            const v4s hi = lds_read_tr16(vb + VH * KS + d0);
+            const v4s hi = lds_read_tr16(vb + 16 * KS + d0);
             const v8u16 c = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
                              (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
             vf[dt] = __builtin_bit_cast(v8h, c);

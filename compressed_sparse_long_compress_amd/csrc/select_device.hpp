@@ -12,7 +12,8 @@ namespace csa {
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkCache = 36608;  // keys cached in LDS (143 KB)
 
-// exclusive prefix sum over the block; returns the block total in `total`
+// exclusive prefix sum over the block (NT threads); returns the block total in `total`
+template <int NT = kTopkThreads>
 __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int x = wave_incl_scan(v);
@@ -20,7 +21,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
     __syncthreads();
     int off = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < kTopkThreads / 64; ++i) {
+    for (int i = 0; i < NT / 64; ++i) {
         int s = wsum[i];
         off += i < wave ? s : 0;
         tot += s;
@@ -32,16 +33,16 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
 
 // Find, scanning bins from the top, the bin where the running count reaches
 // `need`.  Returns the bin; `above` receives the count in higher bins.
-template <int NBINS>
+template <int NBINS, int NT = kTopkThreads>
 __device__ int find_bin(const uint32_t* hist, int need, int* wsum, int* bcast, int& above) {
-    constexpr int PER = NBINS / kTopkThreads > 0 ? NBINS / kTopkThreads : 1;
+    constexpr int PER = NBINS / NT > 0 ? NBINS / NT : 1;
     const int tid = threadIdx.x;
     // thread tid owns bins counted from the top: [tid*PER, tid*PER + PER) in descending order
     int local = 0;
     if (tid * PER < NBINS)
         for (int i = 0; i < PER; ++i) local += (int)hist[NBINS - 1 - (tid * PER + i)];
     int total;
-    int before = block_excl_scan(local, wsum, total);
+    int before = block_excl_scan<NT>(local, wsum, total);
     if (tid * PER < NBINS && before < need && before + local >= need) {
         int run = before;
         for (int i = 0; i < PER; ++i) {
@@ -62,23 +63,24 @@ __device__ int find_bin(const uint32_t* hist, int need, int* wsum, int* bcast, i
     return bin;
 }
 
-// Exact top-k of one row (nv > k visible columns) by one kTopkThreads-thread
-// workgroup.  The keys are cached in `cache` when the row fits (`cap` keys);
-// otherwise every pass re-reads global memory.  hist: 4096 words; wsum:
-// 2 * kTopkThreads / 64 ints; bcast: 4 ints.
-static __device__ void row_select(const float* __restrict__ row, int nv, int k, int32_t* __restrict__ out, uint32_t* hist,
+// Exact top-k of one row (nv > k visible columns) by one NT-thread workgroup.
+// The keys are cached in `cache` when the row fits (`cap` keys); otherwise
+// every pass re-reads global memory.  hist: 4096 words; wsum: 2 * NT / 64
+// ints; bcast: 4 ints.
+template <int NT = kTopkThreads>
+__device__ void row_select(const float* __restrict__ row, int nv, int k, int32_t* __restrict__ out, uint32_t* hist,
                            uint32_t* cache, int cap, int* wsum, int* bcast) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool cached = nv <= cap;
     auto key_at = [&](int j) -> uint32_t { return cached ? cache[j] : f32_order_key(row[j]); };
-    for (int i = tid; i < 4096; i += kTopkThreads) hist[i] = 0;
+    for (int i = tid; i < 4096; i += NT) hist[i] = 0;
     __syncthreads();
 
     // load the row into LDS (16-byte loads when aligned, several in flight) and histogram the top 12 bits
     if (cached && (((uintptr_t)row & 15) == 0)) {
         const int n4 = nv >> 2;
 #pragma unroll 4
-        for (int j4 = tid; j4 < n4; j4 += kTopkThreads) {
+        for (int j4 = tid; j4 < n4; j4 += NT) {
             const float4 v = ((const float4*)row)[j4];
             const uint4 kk = make_uint4(f32_order_key(v.x), f32_order_key(v.y), f32_order_key(v.z), f32_order_key(v.w));
             *(uint4*)&cache[4 * j4] = kk;
@@ -87,13 +89,13 @@ static __device__ void row_select(const float* __restrict__ row, int nv, int k, 
             atomicAdd(&hist[kk.z >> 20], 1u);
             atomicAdd(&hist[kk.w >> 20], 1u);
         }
-        for (int j = 4 * n4 + tid; j < nv; j += kTopkThreads) {
+        for (int j = 4 * n4 + tid; j < nv; j += NT) {
             const uint32_t kk = f32_order_key(row[j]);
             cache[j] = kk;
             atomicAdd(&hist[kk >> 20], 1u);
         }
     } else {
-        for (int j = tid; j < nv; j += kTopkThreads) {
+        for (int j = tid; j < nv; j += NT) {
             const uint32_t kk = f32_order_key(row[j]);
             if (cached) cache[j] = kk;
             atomicAdd(&hist[kk >> 20], 1u);
@@ -101,25 +103,25 @@ static __device__ void row_select(const float* __restrict__ row, int nv, int k, 
     }
     __syncthreads();
     int above1;
-    const uint32_t b1 = (uint32_t)find_bin<4096>(hist, k, wsum, bcast, above1);
+    const uint32_t b1 = (uint32_t)find_bin<4096, NT>(hist, k, wsum, bcast, above1);
 
     // refinement passes over the keys whose prefix matches (LDS read 4 keys at a time)
     auto refine = [&](auto match, auto bin) {
         if (cached) {
             const int n4 = nv >> 2;
-            for (int j4 = tid; j4 < n4; j4 += kTopkThreads) {
+            for (int j4 = tid; j4 < n4; j4 += NT) {
                 const uint4 kk = *(const uint4*)&cache[4 * j4];
                 if (match(kk.x)) atomicAdd(&hist[bin(kk.x)], 1u);
                 if (match(kk.y)) atomicAdd(&hist[bin(kk.y)], 1u);
                 if (match(kk.z)) atomicAdd(&hist[bin(kk.z)], 1u);
                 if (match(kk.w)) atomicAdd(&hist[bin(kk.w)], 1u);
             }
-            for (int j = 4 * n4 + tid; j < nv; j += kTopkThreads) {
+            for (int j = 4 * n4 + tid; j < nv; j += NT) {
                 const uint32_t kk = cache[j];
                 if (match(kk)) atomicAdd(&hist[bin(kk)], 1u);
             }
         } else {
-            for (int j = tid; j < nv; j += kTopkThreads) {
+            for (int j = tid; j < nv; j += NT) {
                 const uint32_t kk = f32_order_key(row[j]);
                 if (match(kk)) atomicAdd(&hist[bin(kk)], 1u);
             }
@@ -127,27 +129,27 @@ static __device__ void row_select(const float* __restrict__ row, int nv, int k, 
     };
 
     // pass 2: middle 12 bits among keys with prefix b1
-    for (int i = tid; i < 4096; i += kTopkThreads) hist[i] = 0;
+    for (int i = tid; i < 4096; i += NT) hist[i] = 0;
     __syncthreads();
     refine([&](uint32_t kk) { return (kk >> 20) == b1; }, [](uint32_t kk) { return (kk >> 8) & 0xFFFu; });
     __syncthreads();
     int above2;
-    const uint32_t b2 = (uint32_t)find_bin<4096>(hist, k - above1, wsum, bcast, above2);
+    const uint32_t b2 = (uint32_t)find_bin<4096, NT>(hist, k - above1, wsum, bcast, above2);
     const uint32_t p2 = (b1 << 12) | b2;
 
     // pass 3: low 8 bits among keys with prefix p2
-    for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
+    for (int i = tid; i < 256; i += NT) hist[i] = 0;
     __syncthreads();
     refine([&](uint32_t kk) { return (kk >> 8) == p2; }, [](uint32_t kk) { return kk & 0xFFu; });
     __syncthreads();
     int above3;
-    const uint32_t b3 = (uint32_t)find_bin<256>(hist, k - above1 - above2, wsum, bcast, above3);
+    const uint32_t b3 = (uint32_t)find_bin<256, NT>(hist, k - above1 - above2, wsum, bcast, above3);
     const uint32_t thr = (p2 << 8) | b3;
     const int need_eq = k - (above1 + above2 + above3);
 
     // ordered compaction: wave w owns the contiguous columns [w seg, (w+1) seg); ranks within a
     // wave come from ballots, across waves from one exchange of (#greater, #equal) per wave
-    constexpr int NW = kTopkThreads / 64;
+    constexpr int NW = NT / 64;
     const int seg = (nv + NW * 64 - 1) / (NW * 64) * 64;
     const int s0 = wave * seg < nv ? wave * seg : nv;
     const int s1 = s0 + seg < nv ? s0 + seg : nv;

@@ -63,6 +63,8 @@ constexpr int kTgThreads = 256;      // k_topk_gmax: 8 consecutive columns per t
 constexpr int kTcThreads = 1024;     // k_topk_cand
 constexpr int kTcChunks = 1;         // 8-group chunks per k_topk_cand thread held in registers
 constexpr int kTqCand = 8192;        // candidates k_topk_pick holds in LDS
+constexpr int kMaxSlices = 32;       // k_topk_cand workgroups (slices) per row, at most
+constexpr int kTpThreads = 1024;     // k_topk_pick
 constexpr int kBitmapWords = 16384;  // k_topk_pick's row bitmap: rows up to 524,288 columns
 
 __global__ __launch_bounds__(kTgThreads) void k_topk_gmax(const float* __restrict__ scores, int64_t n_cols,
@@ -294,19 +296,20 @@ __global__ __launch_bounds__(kTcThreads) void k_topk_cand(const float* __restric
     }
 }
 
-__global__ __launch_bounds__(kTopkThreads) void k_topk_pick(const float* __restrict__ scores, int64_t n_cols,
-                                                            const int64_t* __restrict__ pos, int m, int k, int S,
-                                                            int cap, const TcRec* __restrict__ recs,
-                                                            const uint64_t* __restrict__ cands,
-                                                            int32_t* __restrict__ idx) {
-    constexpr int NT = kTopkThreads, NW = NT / 64;
+template <int NT>
+__global__ __launch_bounds__(NT) void k_topk_pick(const float* __restrict__ scores, int64_t n_cols,
+                                                  const int64_t* __restrict__ pos, int m, int k, int S, int cap,
+                                                  const TcRec* __restrict__ recs, const uint64_t* __restrict__ cands,
+                                                  int32_t* __restrict__ idx) {
+    constexpr int NW = NT / 64;
+    constexpr int SPW = (kMaxSlices + NW - 1) / NW;  // slices per wave
     __shared__ uint32_t h[4096];
     __shared__ __align__(16) uint32_t big[2 * kTqCand + kBitmapWords];  // candidates, then the row bitmap
     __shared__ uint64_t tie[kTieLds];
     __shared__ int wsum[2 * NW];
     __shared__ int bc[4];
     __shared__ uint32_t lctr[4];
-    __shared__ uint32_t scnt[2 * NW];
+    __shared__ uint32_t scnt[kMaxSlices];
     uint64_t* cl = (uint64_t*)big;
     uint32_t* bm = big + 2 * kTqCand;  // row bitmap, or the list of winners to sort
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -319,11 +322,11 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_pick(const float* __restr
         return;
     }
     // slice records and the first 128 candidates of each slice are requested together
-    // (wave w: slices w and w + NW; S <= 2 NW, kSliceCap >= 128)
-    uint64_t pre[2][2];
-    TcRec rr[2];
+    // (wave w: slices w + i NW, i < SPW; S <= kMaxSlices, kSliceCap >= 128)
+    uint64_t pre[SPW][2];
+    TcRec rr[SPW];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < SPW; ++i) {
         const int s = wave + i * NW;
         rr[i] = TcRec{0, 0, 0, 0};
         pre[i][0] = pre[i][1] = 0;
@@ -343,9 +346,9 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_pick(const float* __restr
         for (int i = tid; i < perw * NT; i += NT) bm[i] = 0;
     for (int i = tid; i < 4096; i += NT) h[i] = 0;
     if (tid < 2) lctr[tid] = 0;
-    uint32_t rn[2];
+    uint32_t rn[SPW];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < SPW; ++i) {
         const int s = wave + i * NW;
         rn[i] = rr[i].n;
         if (s < S && lane == 0) scnt[s] = rn[i];
@@ -360,16 +363,16 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_pick(const float* __restr
     const bool sbad = sn > (uint32_t)cap;
     const int sx = wave_incl_scan(sbad ? 0 : (int)sn);
     const int n_cand = __shfl(sx, 63);
-    int off[2];
-    off[0] = __shfl(sx - (int)sn, wave & 63);
-    off[1] = __shfl(sx - (int)sn, (wave + NW) & 63);
+    int off[SPW];
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) off[i] = __shfl(sx - (int)sn, (wave + i * NW) & 63);
     if (__ballot(sbad) != 0 || n_cand > kTqCand) {
-        row_select(row, nv, k, out, h, big, 2 * kTqCand + kBitmapWords, wsum, bc);
+        row_select<NT>(row, nv, k, out, h, big, 2 * kTqCand + kBitmapWords, wsum, bc);
         return;
     }
     const uint32_t tau = lctr[2], hi = lctr[3];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < SPW; ++i) {
         const int s = wave + i * NW;
         if (s >= S) continue;
         const int n = (int)rn[i];
@@ -855,7 +858,7 @@ __global__ __launch_bounds__(kTrThreads) void k_topk_reg(const float* __restrict
 // few rows longer than k_topk_stream takes: selection from the row summary
 static bool topk_summ(int64_t T, int64_t n_cols) { return T < kTopkMaxRows && n_cols > kTsMaxCols; }
 // k_topk_cand workgroups per row (about 256 in all) and candidates each may write
-static int topk_slices(int64_t T) { return T >= 256 ? 1 : (int)(256 / T < 32 ? 256 / T : 32); }  // <= 32
+static int topk_slices(int64_t T) { return T >= 256 ? 1 : (int)(256 / T < kMaxSlices ? 256 / T : kMaxSlices); }
 constexpr int kSliceCap = 4096;  // >= 128
 
 // workspace: summaries [T][groups], slice records [T][S], candidates [T][S][kSliceCap]
@@ -882,8 +885,8 @@ hipError_t launch_topk(const float* scores, int64_t T, int64_t n_cols, const int
                                dim3(kTgThreads), 0, st, scores, n_cols, pos, m, k, summ);
         hipLaunchKernelGGL(k_topk_cand, dim3((unsigned)S, (unsigned)T), dim3(kTcThreads), 0, st, scores, n_cols, pos, m, k,
                            summ, S, kSliceCap, recs, cands);
-        hipLaunchKernelGGL(k_topk_pick, dim3((unsigned)T), dim3(kTopkThreads), 0, st, scores, n_cols, pos, m, k, S,
-                           kSliceCap, recs, cands, idx);
+        hipLaunchKernelGGL(k_topk_pick<kTpThreads>, dim3((unsigned)T), dim3(kTpThreads), 0, st, scores, n_cols, pos, m,
+                           k, S, kSliceCap, recs, cands, idx);
     } else if (n_cols <= kTrMaxCols) {
         const dim3 g((unsigned)T), b(kTrThreads);
         if (n_cols <= kTrThreads * 4)

@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (scaled by a 256 MiB copy: fetch x2.0,
 # write x1.0; see profiles/csa_decode_1m_hbm_counters.md), valid for the kernel
 # source with this SHA-256 only.
-INDEX_TRAFFIC = {"sha256": "63b040e9ed4e8f8c64eb6e9163c9425101ff0e95577726c0c68239beca0d7573", "bytes": 75746388}
+INDEX_TRAFFIC = {"sha256": "3973129218bf2d9cf2927b33702057df3b1c3ebd01d700822ae154ca460491b9", "bytes": 75746347}
 
 
 def log(msg):
@@ -465,6 +465,28 @@ def time_index_launches(ds, n):
     return e0.elapsed_time(e1) / n / 1e3
 
 
+def measure_copy_gbs(n=20):
+    """Bandwidth of a plain device-to-device copy on this GPU (1 GiB read + 1 GiB written per
+    copy, torch's copy kernel), as context for the HBM roofline: what a streaming kernel
+    reaches here, against the 8 TB/s published peak."""
+    import torch
+
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / n
+    del a, b
+    return 2.0 * (1 << 30) / sec / 1e9
+
+
 def cpu_model():
     try:
         for ln in open("/proc/cpuinfo"):
@@ -749,6 +771,10 @@ def main():
                      "kernel_us": idx_sec * 1e6},
     }
     del ds
+    copy_gbs = measure_copy_gbs()
+    result["roofline"]["copy_gbs_measured"] = copy_gbs
+    result["roofline"]["frac_of_copy"] = achieved / copy_gbs
+    log(f"device copy: {copy_gbs:.0f} GB/s (read + write); the indexer reaches {achieved / copy_gbs:.2f} of it")
     if not args.no_prefill:
         log("timing the chunked prefill (8,192 tokens after 131,072)")
         result["prefill"] = prefill_measure(max(args.steps // 4, 3))

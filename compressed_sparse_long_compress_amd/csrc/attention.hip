@@ -1689,6 +1689,10 @@ __global__ __launch_bounds__(64) void k_mqa_combine_sw(const _Float16* __restric
 #pragma unroll
     for (int s = 0; s < kC16Reg; ++s)
         if (s < S) v[s] = *(const v4h*)(base + (int64_t)s * H * D);
+    // RoPE dims: the rotation by tp, while the partials are in flight
+    const int d = dt < NN ? 16 * (NN * w + dt) + l16 : DN + 16 * w + l16;
+    float cs = 1.f, sn = 0.f;
+    if (dt == NN) angle_cs((double)pos[t], rt.theta[(d - DN) >> 1], cs, sn);
     // the 16 heads' merge weights: lane (h = lane / 4, q = lane % 4) takes splits q, q + 4, ...
     // (every (m, l) load in flight at once); M and L over the four lanes of a head by a fixed
     // butterfly, so every lane of the quad holds the same bits
@@ -1732,14 +1736,8 @@ __global__ __launch_bounds__(64) void k_mqa_combine_sw(const _Float16* __restric
     for (int s = 0; s < kC16Reg; ++s)
         if (s < S) acc(v[s], s);
     for (int s = kC16Reg; s < S; ++s) acc(*(const v4h*)(base + (int64_t)s * H * D), s);
-    int d;
-    if (dt < NN) {
-        d = 16 * (NN * w + dt) + l16;
-    } else {
+    if (dt == NN) {
         // RoPE dims: undo the rotation by tp; the pair's other dim is in lane l16 ^ 1
-        d = DN + 16 * w + l16;
-        float cs, sn;
-        angle_cs((double)pos[t], rt.theta[(d - DN) >> 1], cs, sn);
         sn = -sn;
         const bool odd = (l16 & 1) != 0;
 #pragma unroll

@@ -473,6 +473,39 @@ def test_sparse_mqa_decode(lib, dev, gen, orc, T, B, L, H, d, k, W, m, win_cap):
     assert_attn_close(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "sparse_mqa")
 
 
+@pytest.mark.parametrize("path", ["sparse", "dense"])
+@pytest.mark.parametrize("T", [4, 8])
+def test_attention_short_rows_in_a_split_batch(lib, dev, gen, orc, path, T):
+    """Rows whose key lists are far shorter than the split partition (set by T and the key
+    bound: 18 splits here) next to full rows.  T=4 runs two workgroups per split (32 heads
+    each), T=8 one.  Sparse: a row at position 5 has 1 valid selected entry and 1,023 masked
+    ones, so whole splits see no visible key.  Dense: its key list is 6 window tokens, so most
+    splits are empty.  Every row against the oracle."""
+    import torch
+
+    _say(f"short rows in a split batch path={path} T={T}")
+    H, d, W = 64, 512, 128
+    if path == "sparse":
+        m, B, L, k = 4, 4, 8192, 1024
+    else:
+        m, B, L, k = 128, 4, 131072, 0
+    N = L // m
+    comp, win, q = _attn_inputs(gen, 480 + T, B, N, W, H, d, T, L, W)
+    seq = (np.arange(T) % B).astype(np.int32)
+    pos = np.array([L - 1, 5, 300, 2000, L - 1, 130, 7, 4000], np.int64)[:T]
+    sm = 1.0 / math.sqrt(d)
+    kvc, kvw = dev.kv_cache(comp, N), dev.kv_cache(win, W)
+    if path == "sparse":
+        idx = gen.random_idx(481 + T, 1, (pos + 1) // m, k)
+        out, lse = lib.csa_sparse_mqa(dev.bf16(q), dev.t(seq), dev.t(pos), dev.t(idx), m, kvc, kvw, W, sm)
+    else:
+        idx = None
+        out, lse = lib.hca_dense_mqa(dev.bf16(q), dev.t(seq), dev.t(pos), m, N, kvc, kvw, W, sm)
+    torch.cuda.synchronize()
+    ref_o, ref_l = orc.attend(q, seq, pos, comp, N, win, W, W, m, sm, idx=idx)
+    assert_attn_close(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, f"short rows {path} T={T}")
+
+
 def test_sparse_mqa_ignores_invalid_idx(lib, dev, gen, orc):
     import torch
 

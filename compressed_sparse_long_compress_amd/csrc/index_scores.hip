@@ -368,8 +368,15 @@ __global__ __launch_bounds__(256) void k_index_rows_grp(const uint8_t* __restric
 // kEmit: segment s = blockIdx.x of every query row collects the candidates of this column
 // chunk.  A wave owns its queries, so it counts their candidates itself (ballots into
 // wave-uniform counters: no atomics, a fixed order) and writes the counts to cnt[t][s].
+// Row tiles per wave: four for the store code (each key fragment feeds four MFMAs); two for
+// the sample and emit codes, whose smaller register set leaves room for three waves per SIMD
+// to hide the latency of their longer epilogue (measured: the fused call 0.85 -> 0.80 ms;
+// the store code is faster with four, 0.51 against 0.70 ms).
+constexpr int gemm_row_tiles(int mode) { return mode == kStore ? 4 : 2; }
+constexpr int gemm_min_blocks(int hi, int mode) { return hi == 8 ? (mode == kStore ? 2 : 3) : 1; }
+
 template <int DI, int HI, int MODE = kStore>
-__global__ __launch_bounds__(256, HI == 8 ? 2 : 1) void k_index_gemm(const uint8_t* __restrict__ q, const uint8_t* __restrict__ q_scale,
+__global__ __launch_bounds__(256, gemm_min_blocks(HI, MODE)) void k_index_gemm(const uint8_t* __restrict__ q, const uint8_t* __restrict__ q_scale,
                                                     const float* __restrict__ w, const int32_t* __restrict__ seq,
                                                     const int64_t* __restrict__ pos, int64_t T,
                                                     const uint8_t* __restrict__ kdata,
@@ -380,11 +387,11 @@ __global__ __launch_bounds__(256, HI == 8 ? 2 : 1) void k_index_gemm(const uint8
     constexpr int KB = DI / 2, NB = DI / 32;
     constexpr int KS = DI / 64;       // 32x32x64 MFMA steps per score
     constexpr int QA = 32 / HI;       // queries per row tile
-    constexpr int NA = 4;             // row tiles per wave
+    constexpr int NA = gemm_row_tiles(MODE);  // row tiles per wave
     // kEmit: the head weights come from LDS (a lane's 16 per row tile depend only on its
-    // half-wave), freeing the registers the emission needs to stay at two waves per SIMD
+    // half-wave), freeing the registers the emission needs to stay at three waves per SIMD
     constexpr bool kLdsW = MODE == kEmit;
-    constexpr int QW = QA * NA;       // queries per wave (16 or 32)
+    constexpr int QW = QA * NA;       // queries per wave (at most 32)
     using NvT = typename std::conditional<MODE == kEmit, int32_t, int64_t>::type;  // kEmit: n_cols < 2^31
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 31, g2 = lane >> 5;
@@ -615,7 +622,7 @@ hipError_t launch_index_scores(const uint8_t* q, const uint8_t* q_scale, const f
                                kcap, kpages, kpshift, m, n_cols, chunk, scores, gmax);
         return hipGetLastError();
     }
-    const int qwg = 4 * 4 * (32 / h_i);  // queries per workgroup
+    const int qwg = 4 * gemm_row_tiles(kStore) * (32 / h_i);  // queries per workgroup
     const int64_t qtiles = (T + qwg - 1) / qwg;
     int64_t chunk = (n_cols * qtiles + 1023) / 1024;
     chunk = ((chunk + 31) / 32) * 32;
@@ -1029,7 +1036,7 @@ hipError_t launch_index_topk(const uint8_t* q, const uint8_t* q_scale, const flo
             }
 #undef CSA_ROWS
         } else {
-            const int qwg = 4 * 4 * (32 / h_i);
+            const int qwg = 4 * gemm_row_tiles(kEmit) * (32 / h_i);  // (sample and emit alike)
             const dim3 grid((unsigned)((n + chunk - 1) / chunk), (unsigned)((T + qwg - 1) / qwg)), block(256);
 #define CSA_GEMM(DI, HI, MD)                                                                                      \
     hipLaunchKernelGGL((k_index_gemm<DI, HI, MD>), grid, block, 0, st, q, q_scale, w, seq, pos, T, kdata, kscale, \

@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (scaled by a 256 MiB copy: fetch x2.0,
 # write x1.0; see profiles/csa_decode_1m_hbm_counters.md), valid for the kernel
 # source with this SHA-256 only.
-INDEX_TRAFFIC = {"sha256": "3973129218bf2d9cf2927b33702057df3b1c3ebd01d700822ae154ca460491b9", "bytes": 75746347}
+INDEX_TRAFFIC = {"sha256": "10e790318e3c527e99fb4ff21dfc6255cc7c53cfa88a321f69301154b1fd9c34", "bytes": 75746305}
 
 
 def log(msg):

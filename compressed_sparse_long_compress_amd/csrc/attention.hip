@@ -1793,6 +1793,26 @@ static int choose_splits(int64_t T, int64_t max_keys) {
     return (int)s;
 }
 
+// The 64-head kernels share a split between two workgroups of 32 heads when the grid would
+// otherwise leave at least half the CUs idle: at T x S <= 128 with splits of up to 12 tiles;
+// else, when half the splits would hold at most 4 tiles each and T x ceil(S/2) <= 128, with
+// half the splits (measured: 8 rows at 1M context, 53.1 -> 51.0 us per decode step; longer
+// halved splits were slower).  The workspace is sized for choose_splits' S, never smaller.
+static void choose_partition(int64_t T, int H, int64_t max_keys, int& S, bool& hsplit) {
+    S = choose_splits(T, max_keys);
+    hsplit = false;
+    if (H != 64) return;
+    if (T * S <= 128 && (max_keys + S - 1) / S <= 12 * KT) {
+        hsplit = true;
+        return;
+    }
+    const int S2 = (S + 1) / 2;
+    if (T * S2 <= 128 && (max_keys + S2 - 1) / S2 <= 4 * KT) {
+        S = S2;
+        hsplit = true;
+    }
+}
+
 size_t mqa_workspace_bytes(int64_t T, int H, int d, int64_t max_keys) {
     const int S = choose_splits(T, max_keys);
     if (S == 1) return 0;
@@ -1802,12 +1822,11 @@ size_t mqa_workspace_bytes(int64_t T, int H, int d, int64_t max_keys) {
 template <int H, int D>
 static void launch_mqa_t(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64_t T, const int32_t* idx,
                          int k, int m, KvView comp, KvView win, int window, float sm_scale, const RopeTab& rt, int S,
-                         int64_t max_keys, float* out, float* lse, float* po, float* pml, hipStream_t st) {
+                         bool hsplit, int64_t max_keys, float* out, float* lse, float* po, float* pml,
+                         hipStream_t st) {
     // splits of more than a few tiles: the two-role kernel (its pipeline costs a step at either end)
     const bool long_splits = (max_keys + S - 1) / S > 12 * KT;
     const bool paged = comp.pages || win.pages;  // paged views: their own instantiation
-    // short splits in a grid of at most half the CUs: two workgroups per (row, split), 32 heads each
-    const bool hsplit = !long_splits && T * S <= 128;
 #define CSA_MQA_LAUNCH(KERN, NTH, NWG)                                                                              \
     hipLaunchKernelGGL((KERN), dim3((unsigned)(NWG)), dim3(NTH), 0, st, q, seq, pos, idx, k, m, comp, win, window, \
                        sm_scale, rt, S, out, lse, po, pml)
@@ -1846,15 +1865,18 @@ hipError_t launch_mqa(const uint16_t* q, const int32_t* seq, const int64_t* pos,
                       const int32_t* idx, int k, int m, int64_t max_keys, KvView comp, KvView win, int window,
                       float sm_scale, const RopeTab& rt, float* out, float* lse, void* ws, hipStream_t st) {
     if (T == 0) return hipSuccess;
-    const int S = choose_splits(T, max_keys);
+    int S;
+    bool hsplit;
+    choose_partition(T, H, max_keys, S, hsplit);
     float* po = nullptr;
     float* pml = nullptr;
     if (S > 1) {
         po = (float*)ws;
         pml = po + (size_t)T * S * H * d;
     }
-#define CSA_MQA(HH, DD) \
-    launch_mqa_t<HH, DD>(q, seq, pos, T, idx, k, m, comp, win, window, sm_scale, rt, S, max_keys, out, lse, po, pml, st)
+#define CSA_MQA(HH, DD)                                                                                          \
+    launch_mqa_t<HH, DD>(q, seq, pos, T, idx, k, m, comp, win, window, sm_scale, rt, S, hsplit, max_keys, out, lse, \
+                         po, pml, st)
     if (d == 512) {
         if (H == 64) CSA_MQA(64, 512);
         else if (H == 32) CSA_MQA(32, 512);

@@ -41,15 +41,17 @@
  *     [n*s/S, n*(s+1)/S) of the row's n keys, with
  *       S = min(ceil(256 / T), ceil(bound / 64), 64),
  *       bound = k + window (csa_sparse_mqa) or max_vis + window (hca_dense_mqa),
- *     and the partial results are merged in split order.  With 64 heads, splits
- *     of at most 384 keys and T * S <= 128, each split's heads are shared by
- *     two workgroups (another summation order).  A row's out and lse are
- *     bit-identical across calls that give the same S and the same side of
- *     T * S <= 128 (at k = 1024, window = 128: S = 18 for any T <= 15, so
- *     T <= 7 is one class and 8 <= T <= 15 another); otherwise the fp16
- *     partials and P round differently and the results agree to about 3e-4
- *     relative RMS (each meets the 2e-3 relative-RMS bar against the fp64
- *     reference).
+ *     and the partial results are merged in split order.  With 64 heads the
+ *     heads of a split are shared by two workgroups (another summation order)
+ *     when T * S <= 128 and the splits hold at most 384 keys; otherwise, when
+ *     S' = ceil(S / 2) splits would hold at most 128 keys each and
+ *     T * S' <= 128, the row takes S' splits, shared the same way.  A row's
+ *     out and lse are bit-identical across calls that give the same splits
+ *     and the same sharing (at k = 1024, window = 128: T <= 7 takes 18 shared
+ *     splits, 8 <= T <= 14 takes 9 shared splits, T = 15 takes 18 splits of
+ *     one workgroup); otherwise the fp16 partials and P round differently
+ *     and the results agree to about 3e-4 relative RMS (each meets the 2e-3
+ *     relative-RMS bar against the fp64 reference).
  *
  * Storage formats
  *   - Compressed KV entry (and window-ring entry), d = d_nope + 64:

@@ -474,13 +474,14 @@ def test_sparse_mqa_decode(lib, dev, gen, orc, T, B, L, H, d, k, W, m, win_cap):
 
 
 @pytest.mark.parametrize("path", ["sparse", "dense"])
-@pytest.mark.parametrize("T", [4, 8])
+@pytest.mark.parametrize("T", [4, 8, 16])
 def test_attention_short_rows_in_a_split_batch(lib, dev, gen, orc, path, T):
     """Rows whose key lists are far shorter than the split partition (set by T and the key
-    bound: 18 splits here) next to full rows.  T=4 runs two workgroups per split (32 heads
-    each), T=8 one.  Sparse: a row at position 5 has 1 valid selected entry and 1,023 masked
-    ones, so whole splits see no visible key.  Dense: its key list is 6 window tokens, so most
-    splits are empty.  Every row against the oracle."""
+    bound) next to full rows.  T=4: 18 splits, two workgroups of 32 heads per split; T=8: 9
+    splits, shared the same way; T=16: 16 splits of one workgroup.  Sparse: a row at
+    position 5 has 1 valid selected entry and 1,023 masked ones, so whole splits see no
+    visible key.  Dense: its key list is 6 window tokens, so most splits are empty.  Every
+    row against the oracle."""
     import torch
 
     _say(f"short rows in a split batch path={path} T={T}")
@@ -492,7 +493,7 @@ def test_attention_short_rows_in_a_split_batch(lib, dev, gen, orc, path, T):
     N = L // m
     comp, win, q = _attn_inputs(gen, 480 + T, B, N, W, H, d, T, L, W)
     seq = (np.arange(T) % B).astype(np.int32)
-    pos = np.array([L - 1, 5, 300, 2000, L - 1, 130, 7, 4000], np.int64)[:T]
+    pos = np.array([L - 1, 5, 300, 2000, L - 1, 130, 7, 4000] * 2, np.int64)[:T]
     sm = 1.0 / math.sqrt(d)
     kvc, kvw = dev.kv_cache(comp, N), dev.kv_cache(win, W)
     if path == "sparse":
@@ -917,14 +918,14 @@ def test_mqa_bwd(lib, dev, gen, orc, T, B, L, H, k, W, m, win_cap, sel, same_seq
 # determinism and batch invariance (the rule stated at the top of csa.h)
 # --------------------------------------------------------------------------
 def test_batch_invariance_and_determinism(lib, dev, gen, orc):
-    """Row 0 of a decode batch, run alone and inside batches of 4, 7, 8, 15, 32 and 200 rows:
-    its index scores and top-k indices are the same bits in every batch; its attention
+    """Row 0 of a decode batch, run alone and inside batches of 4, 7, 8, 14, 15, 32 and 200
+    rows: its index scores and top-k indices are the same bits in every batch; its attention
     output is the same bits whenever the split-KV partition and the head split are the same
-    (S = 18 for T <= 15 at k = 1024, window = 128; two workgroups per split while T S <= 128,
-    so T <= 7 and 8 <= T <= 15 form two classes), agrees within the attention bar otherwise,
-    does not change when the other rows' inputs change, and repeats bit for bit run to run.
-    HCA with max_vis at 1x and 8x the visible count: within the attention bar (the bound sets
-    the partition)."""
+    (at k = 1024, window = 128: T <= 7 takes 18 splits shared by two workgroups, 8 <= T <= 14
+    takes 9 shared splits, T = 15 takes 18 splits of one workgroup), agrees within the
+    attention bar otherwise, does not change when the other rows' inputs change, and repeats
+    bit for bit run to run.  HCA with max_vis at 1x and 8x the visible count: within the
+    attention bar (the bound sets the partition)."""
     import torch
 
     _say("batch invariance")
@@ -941,7 +942,7 @@ def test_batch_invariance_and_determinism(lib, dev, gen, orc):
     kvc, kvw = dev.kv_cache(comp, N), dev.kv_cache(win, W)
     sm = 1.0 / math.sqrt(d)
     res = {}
-    for T in (1, 4, 7, 8, 15, 32, Tmax):
+    for T in (1, 4, 7, 8, 14, 15, 32, Tmax):
         sl = slice(0, T)
         sc = lib.csa_index_scores(dev.t(qd[sl]), dev.t(qs[sl]), dev.t(w[sl]), dev.t(seq[sl]), dev.t(pos[sl]), keys, m, N)
         ix = lib.csa_topk(sc, dev.t(pos[sl]), m, k)
@@ -953,8 +954,8 @@ def test_batch_invariance_and_determinism(lib, dev, gen, orc):
     wit = orc.index_exact_witness(qd[:1], qs[:1], w[:1], seq[:1], pos[:1], kd, ks, N, m, N)
     assert wit < 24
     s0, i0, o0, l0 = res[1]
-    same = {4: 1, 7: 1, 15: 8}  # T -> a batch size with the same partition and head split
-    for T in (4, 7, 8, 15, 32, Tmax):
+    same = {4: 1, 7: 1, 14: 8}  # T -> a batch size with the same partition and head split
+    for T in (4, 7, 8, 14, 15, 32, Tmax):
         s, i, o, l = res[T]
         assert np.array_equal(s.view(np.uint32), s0.view(np.uint32)), f"T={T}: index scores of row 0 differ"
         assert np.array_equal(i, i0), f"T={T}: top-k of row 0 differs"

@@ -1228,25 +1228,34 @@ __global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q,
             *(uint4*)(kv + (ch / CPN) * KS + (ch % CPN) * 16 + (vt & 1) * 8) = fp8x8_to_f16(pre_h[0], pre_h[1]);
         }
     };
-    int64_t nraw = 0;  // this thread's position in the next batch: selected index, then resolved
-    Res nres{g_zero_entry, g_zero_entry + DN, nullptr, false};
-    float nscl = 0.f;
-    // next batch, one step per tile: each load is issued at the start of a tile and consumed at
-    // its end (no load but the tile prefetch in flight across the loop's back edge)
+    Res nres{g_zero_entry, g_zero_entry + DN, nullptr, false};  // this thread's position in the next batch
+    int32_t pend_i = 0;  // the tile's selected-index load
+    float pend_s = 0.f;  // the tile's entry-scale load
+    // next batch, one step per tile: the selected index is loaded on tile 1 of a batch, the
+    // entry scale on tile 2, each used at the tile's end.  Both loads are issued on every tile
+    // (from the zero entry when not needed) and waited for before the tile prefetch leaves: a
+    // load issued on some paths only made the compiler wait for every load, the tile prefetch
+    // included, before the first LDS read of P V.
     auto batch_begin = [&](int j) {
         const int b1 = j / TPB + 1;
         const int64_t u = u0 + (int64_t)b1 * RB + vt;
-        if (b1 * TPB < nt) {
-            if (j % TPB == 1) nraw = fetch(u);
-            if (j % TPB == 2) nscl = nres.ok ? gload<float>((const uint8_t*)nres.sp) : 0.f;
-        }
+        const bool more = b1 * TPB < nt;
+        const bool li = more && j % TPB == 1 && idx && u < u1 && u < rk.n_c;
+        const bool ls = more && j % TPB == 2 && nres.ok;
+        pend_i = gload<int32_t>(li ? (const uint8_t*)(idx + t * k + u) : g_zero_entry);
+        pend_s = gload<float>(ls ? (const uint8_t*)nres.sp : g_zero_entry);
     };
+    // both loads complete here, on every path: before the tile prefetch is issued, so that no
+    // wait for them covers the prefetch
+    auto batch_take = [&]() { asm volatile("" ::"v"(pend_i), "v"(pend_s)); };
     auto batch_end = [&](int j) {
         const int b1 = j / TPB + 1;
         const int64_t u = u0 + (int64_t)b1 * RB + vt;
+        const int32_t iv = pend_i;
+        const float sv = pend_s;
         if (b1 * TPB < nt) {
-            if (j % TPB == 1) nres = resolve_at(u, nraw);
-            if (j % TPB == 2) publish(b1 & 1, nres, nscl);
+            if (j % TPB == 1) nres = resolve_at(u, (u < u1 && u < rk.n_c) ? (idx ? (int64_t)iv : u) : 0);
+            if (j % TPB == 2) publish(b1 & 1, nres, nres.ok ? sv : 0.f);
         }
     };
 
@@ -1441,7 +1450,9 @@ __global__ __launch_bounds__(512) void k_mqa64ws(const uint16_t* __restrict__ q,
             for (int it = 0; it <= nt; ++it) {
                 batch_begin(it);
                 if (it + 1 < nt) stage(it + 1);
+                batch_take();
                 if (it + 2 < nt) issue(it + 2);
+                __builtin_amdgcn_sched_barrier(0);  // the prefetch leaves before P V, not after it
                 if (it >= 1) {
                     // O[heads x dims] += P V (tile it - 1) for all heads over this wave's dims
                     const int j = it - 1;

@@ -209,6 +209,7 @@ static int index_args(const char* fn, const uint8_t* q, const uint8_t* q_scale, 
     *gmax = nullptr;
     *nothing = false;
     if (T < 0 || n_cols < 0) return fail(CSA_EINVAL, "%s: T and n_cols must be >= 0", fn);
+    if (n_cols >= ((int64_t)1 << 31)) return fail(CSA_EUNSUPPORTED, "%s: n_cols must be < 2^31", fn);
     if (h_i != 4 && h_i != 8) return fail(CSA_EUNSUPPORTED, "%s: h_i=%d unsupported (4 or 8)", fn, h_i);
     if (d_i != 64 && d_i != 128) return fail(CSA_EUNSUPPORTED, "%s: d_i=%d unsupported (64 or 128)", fn, d_i);
     if (m < 1) return fail(CSA_EINVAL, "%s: m must be >= 1", fn);

@@ -388,11 +388,12 @@ __global__ __launch_bounds__(256, gemm_min_blocks(HI, MODE)) void k_index_gemm(c
     constexpr int KS = DI / 64;       // 32x32x64 MFMA steps per score
     constexpr int QA = 32 / HI;       // queries per row tile
     constexpr int NA = gemm_row_tiles(MODE);  // row tiles per wave
-    // kEmit: the head weights come from LDS (a lane's 16 per row tile depend only on its
-    // half-wave), freeing the registers the emission needs to stay at three waves per SIMD
-    constexpr bool kLdsW = MODE == kEmit;
+    // The head weights come from LDS (a lane's 16 per row tile depend only on its half-wave),
+    // freeing registers: for the emission's third wave per SIMD, and for the store code's
+    // prefetched key tile
+    constexpr bool kLdsW = MODE != kSample;
     constexpr int QW = QA * NA;       // queries per wave (at most 32)
-    using NvT = typename std::conditional<MODE == kEmit, int32_t, int64_t>::type;  // kEmit: n_cols < 2^31
+    using NvT = int32_t;              // visible counts (n_cols < 2^31)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 31, g2 = lane >> 5;
     const int64_t tq0 = ((int64_t)blockIdx.y * 4 + wave) * QW;  // first query of this wave
@@ -515,7 +516,66 @@ __global__ __launch_bounds__(256, gemm_min_blocks(HI, MODE)) void k_index_gemm(c
             ec[at][i][1] = __builtin_amdgcn_readfirstlane(ec[at][i][1] + (uint32_t)__popc(hi));
         };
 
-        for (int64_t j0 = c0; j0 < c1; j0 += 32) {
+        // Key tiles of 32 columns: fragments of one tile, then per row tile two MFMAs and the
+        // epilogue (ReLU, weighted head sum, store / sample / emit).
+        auto load_tile = [&](int64_t j0n, v8i (&bb)[KS], int (&sbb)[KS]) {
+            const int64_t jrn = real(j0n + r);
+            const bool kload = j0n < c1 && jrn < nv_max;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int blk = 2 * ks + g2;
+                if (kload) {
+                    const int64_t kr = kv_row(kpages, kpshift, kcap, s, jrn);
+                    bb[ks] = frag16(kdata + kr * KB + blk * 16);
+                    sbb[ks] = kscale[kr * NB + blk];
+                } else {
+                    bb[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+                    sbb[ks] = 127;
+                }
+            }
+        };
+        auto mma = [&](int at, const v8i (&bb)[KS], const int (&sbb)[KS]) -> v16f {
+            v16f acc = {};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[at][ks], bb[ks], acc, 4, 4, 0, sa[at][ks], 0,
+                                                                      sbb[ks]);
+            return acc;
+        };
+        auto epilogue = [&](int at, const v16f& acc, int64_t j, int64_t jr) {
+            float part[4];
+            const float* wr = kLdsW ? lw[wave][at][g2] : wt[kLdsW ? 0 : at];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float p = wr[4 * i] * relu1(acc[4 * i]);
+                p = fmaf(wr[4 * i + 1], relu1(acc[4 * i + 1]), p);
+                p = fmaf(wr[4 * i + 2], relu1(acc[4 * i + 2]), p);
+                p = fmaf(wr[4 * i + 3], relu1(acc[4 * i + 3]), p);
+                part[i] = p;
+            }
+            if constexpr (HI == 8) {
+                // query i of the tile = regs 4i..4i+3, its heads split over the lane halves.
+                // Lanes < 32 keep queries 0, 1 and lanes >= 32 queries 2, 3: one swap of the
+                // halves of (part[i], part[2 + i]) hands each lane its partner's half of the
+                // query it keeps, and the two results sum to it (own + partner, either order)
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[i]),
+                                                                     __float_as_uint(part[2 + i]), false, false);
+                    const float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                    if constexpr (MODE == kEmit) emit(at, i, j, v);
+                    else if (nvq[at][i] >= 0 && j < c1) put(at, i, j, jr, v);
+                }
+            } else {
+                // query 2i+g2 complete in regs 4i..4i+3
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if constexpr (MODE == kEmit) emit(at, i, j, part[i]);
+                    else if (nvq[at][i] >= 0 && j < c1) put(at, i, j, jr, part[i]);
+                }
+            }
+        };
+        auto tile = [&](int64_t j0, const v8i (&bb)[KS], const int (&sbb)[KS]) {
             const int64_t j = j0 + r;
             const int64_t jr = real(j);  // a 32-column tile maps to 32 consecutive score columns
             if (real(j0) >= nv_max) {
@@ -527,61 +587,31 @@ __global__ __launch_bounds__(256, gemm_min_blocks(HI, MODE)) void k_index_gemm(c
                         for (int i = 0; i < 4; ++i)
                             if (nvq[at][i] >= 0 && j < c1) put(at, i, j, jr, -INFINITY);
                 }
-                continue;
-            }
-            v8i b[KS];
-            int sb[KS];
-            const bool kload = jr < nv_max;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int blk = 2 * ks + g2;
-                if (kload) {
-                    const int64_t kr = kv_row(kpages, kpshift, kcap, s, jr);
-                    b[ks] = frag16(kdata + kr * KB + blk * 16);
-                    sb[ks] = kscale[kr * NB + blk];
-                } else {
-                    b[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-                    sb[ks] = 127;
-                }
+                return;
             }
 #pragma unroll
-            for (int at = 0; at < NA; ++at) {
-                v16f acc = {};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[at][ks], b[ks], acc, 4, 4, 0, sa[at][ks], 0,
-                                                                          sb[ks]);
-                float part[4];
-                const float* wr = kLdsW ? lw[wave][at][g2] : wt[kLdsW ? 0 : at];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float p = wr[4 * i] * relu1(acc[4 * i]);
-                    p = fmaf(wr[4 * i + 1], relu1(acc[4 * i + 1]), p);
-                    p = fmaf(wr[4 * i + 2], relu1(acc[4 * i + 2]), p);
-                    p = fmaf(wr[4 * i + 3], relu1(acc[4 * i + 3]), p);
-                    part[i] = p;
-                }
-                if constexpr (HI == 8) {
-                    // query i of the tile = regs 4i..4i+3, its heads split over the lane halves.
-                    // Lanes < 32 keep queries 0, 1 and lanes >= 32 queries 2, 3: one swap of the
-                    // halves of (part[i], part[2 + i]) hands each lane its partner's half of the
-                    // query it keeps, and the two results sum to it (own + partner, either order)
-#pragma unroll
-                    for (int i = 0; i < 2; ++i) {
-                        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[i]),
-                                                                         __float_as_uint(part[2 + i]), false, false);
-                        const float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-                        if constexpr (MODE == kEmit) emit(at, i, j, v);
-                        else if (nvq[at][i] >= 0 && j < c1) put(at, i, j, jr, v);
-                    }
-                } else {
-                    // query 2i+g2 complete in regs 4i..4i+3
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        if constexpr (MODE == kEmit) emit(at, i, j, part[i]);
-                        else if (nvq[at][i] >= 0 && j < c1) put(at, i, j, jr, part[i]);
-                    }
-                }
+            for (int at = 0; at < NA; ++at) epilogue(at, mma(at, bb, sbb), j, jr);
+        };
+
+        if constexpr (MODE == kStore) {
+            // the next tile's fragments in flight while this one computes (two register sets)
+            v8i b0[KS], b1[KS];
+            int sb0[KS], sb1[KS];
+            load_tile(c0, b0, sb0);
+            for (int64_t j0 = c0; j0 < c1; j0 += 64) {
+                load_tile(j0 + 32, b1, sb1);
+                tile(j0, b0, sb0);
+                if (j0 + 32 >= c1) break;
+                load_tile(j0 + 64, b0, sb0);
+                tile(j0 + 32, b1, sb1);
+            }
+        } else {
+            // (the sample and emit codes keep their registers for a third wave per SIMD)
+            for (int64_t j0 = c0; j0 < c1; j0 += 32) {
+                v8i b0[KS];
+                int sb0[KS];
+                load_tile(j0, b0, sb0);
+                tile(j0, b0, sb0);
             }
         }
         (void)nv_min;

@@ -206,7 +206,7 @@ int csa_compress_index_keys(const uint16_t* k, const float* logits, int64_t tok0
  *   w        [T][h_i] fp32 head weights
  *   seq      [T] int32 sequence of each row;  pos [T] int64 position
  *   keys     index keys (key of entry j of seq s at row s*cap + j)
- *   n_cols   columns written per row (<= keys.cap)
+ *   n_cols   columns written per row (<= keys.cap, < 2^31)
  *   scores   [T][n_cols] fp32
  *   topk_ws  optional (NULL, 0 to skip): the workspace of the csa_topk call
  *            that will read these scores.  When given, the indexer also

@@ -69,13 +69,16 @@ _lib.csa_pages_bytes.restype = _sz
 _lib.csa_pages_bytes.argtypes = [_i32, _i32, _i32]
 _lib.csa_pages_store.argtypes = [_Kv, _IdxKeys, _i32, _i32, _vp, _i32, _vp, _sz, _vp]
 _lib.csa_pages_load.argtypes = [_Kv, _IdxKeys, _i32, _i32, _vp, _i32, _vp, _sz, _vp]
+_lib.csa_mfma_probe_flops.restype = _i64
+_lib.csa_mfma_probe_flops.argtypes = [_i32, _i32, _i64]
+_lib.csa_mfma_probe.argtypes = [_i32, _i32, _i64, _vp, _i64, _vp]
 _lib.csa_last_error.restype = ctypes.c_char_p
 _lib.csa_version.restype = ctypes.c_int
 
 EXPORTS = ["csa_compress", "csa_compress_channel", "csa_compress_index_keys", "csa_index_scores", "csa_index_scores_grouped", "csa_index_topk_workspace", "csa_index_topk", "csa_index_bwd_workspace",
            "csa_index_bwd", "csa_topk_workspace", "csa_topk", "csa_topk_noalloc", "csa_mqa_workspace",
            "csa_sparse_mqa", "hca_dense_mqa", "csa_mqa_bwd_workspace", "csa_mqa_bwd", "csa_pages_bytes", "csa_pages_store", "csa_pages_load",
-           "csa_last_error", "csa_version"]
+           "csa_mfma_probe_flops", "csa_mfma_probe", "csa_last_error", "csa_version"]
 
 
 class CsaError(RuntimeError):
@@ -112,6 +115,15 @@ def _need(t, name, dtype, ndim=None):
 
 def version():
     return _lib.csa_version()
+
+
+def mfma_probe(kind, blocks, iters, sink):
+    """One launch of the matrix-core throughput probe (kind 0: fp16 16x16x32, 1: MXFP4 32x32x64)
+    on the current stream; sink: float32 tensor of >= blocks x 256 elements.  Returns the
+    launch's flop count."""
+    _need(sink, "sink", torch.float32, 1)
+    _check(_lib.csa_mfma_probe(int(kind), int(blocks), int(iters), _ptr(sink), sink.numel(), _stream()))
+    return int(_lib.csa_mfma_probe_flops(int(kind), int(blocks), int(iters)))
 
 
 class KvCache:

@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libcsa.so")
-SOURCES = ["api.hip", "compress.hip", "index_scores.hip", "topk.hip", "attention.hip", "index_backward.hip"]
+SOURCES = ["api.hip", "compress.hip", "index_scores.hip", "topk.hip", "attention.hip", "index_backward.hip", "probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -428,6 +428,22 @@ int csa_topk_noalloc(const float* scores, int64_t T, int64_t n_cols, const int64
     return hip_status(e, fn);
 }
 
+int64_t csa_mfma_probe_flops(int32_t kind, int32_t blocks, int64_t iters) {
+    if ((kind != 0 && kind != 1) || blocks < 1 || iters < 1 || iters % 4 != 0) return -1;
+    const int64_t per = kind == 0 ? 16 * 16 * 32 * 2 : 32 * 32 * 64 * 2;
+    return per * csa::kProbeChains * iters * (int64_t)blocks * (csa::kProbeThreads / 64);
+}
+
+int csa_mfma_probe(int32_t kind, int32_t blocks, int64_t iters, float* sink, int64_t sink_len, csa_stream_t stream) {
+    const char* fn = "csa_mfma_probe";
+    if (kind != 0 && kind != 1) return fail(CSA_EUNSUPPORTED, "%s: kind=%d (0: fp16, 1: MXFP4)", fn, kind);
+    if (blocks < 1 || iters < 1 || iters % 4 != 0)
+        return fail(CSA_EINVAL, "%s: blocks must be >= 1 and iters a positive multiple of 4", fn);
+    if (!sink || sink_len < (int64_t)blocks * csa::kProbeThreads)
+        return fail(CSA_EINVAL, "%s: sink must hold blocks x %d floats", fn, csa::kProbeThreads);
+    return hip_status(csa::launch_mfma_probe(kind, blocks, iters, sink, (hipStream_t)stream), fn);
+}
+
 size_t csa_mqa_workspace(int64_t T, int32_t H, int32_t d, int64_t max_keys) {
     return csa::mqa_workspace_bytes(T, H, d, max_keys);
 }

@@ -107,4 +107,11 @@ hipError_t launch_mqa_bwd(const uint16_t* q, const int32_t* seq, const int64_t* 
                           const RopeTab& rt, const float* out, const float* lse, const float* dout, float* dq,
                           float* dcomp, int64_t comp_rows, float* dwin, int64_t win_rows, void* ws, hipStream_t st);
 
+// matrix-core throughput probe: `blocks` workgroups of kProbeThreads threads, each wave
+// issuing iters x kProbeChains MFMAs (kind 0: fp16 16x16x32, kind 1: MXFP4 32x32x64);
+// sink: blocks x kProbeThreads floats
+constexpr int kProbeThreads = 256;
+constexpr int kProbeChains = 4;
+hipError_t launch_mfma_probe(int kind, int blocks, int64_t iters, float* sink, hipStream_t st);
+
 }  // namespace csa

@@ -451,6 +451,21 @@ int csa_pages_store(csa_kv_t kv, csa_index_keys_t keys, int32_t d, int32_t d_i, 
 int csa_pages_load(csa_kv_t kv, csa_index_keys_t keys, int32_t d, int32_t d_i, const int32_t* pages,
                    int32_t n_pages, const void* host, size_t host_bytes, csa_stream_t stream);
 
+/*
+ * csa_mfma_probe — a measurement helper, not a step of the path: `blocks`
+ * workgroups of 256 threads issue MFMAs back to back with no memory traffic
+ * (each wave iters x 4 of them in four independent chains; iters a multiple
+ * of 4) and write one
+ * float per thread to sink (blocks x 256 floats, meaningless values).  A
+ * timed launch gives the rate the matrix cores sustain on this GPU for the
+ * shapes the path uses:
+ *   kind 0: fp16 16x16x32 (the attention);  kind 1: MXFP4 32x32x64 (the indexer)
+ * csa_mfma_probe_flops returns the flop count of such a launch (-1 for a bad
+ * argument).
+ */
+int64_t csa_mfma_probe_flops(int32_t kind, int32_t blocks, int64_t iters);
+int csa_mfma_probe(int32_t kind, int32_t blocks, int64_t iters, float* sink, int64_t sink_len, csa_stream_t stream);
+
 /* Text of the last error on the calling thread ("" if none). */
 const char* csa_last_error(void);
 

@@ -190,3 +190,15 @@ def test_index_topk_and_index_bwd_validation(csa):
     rc = L.csa_index_bwd(p, p, p, p, p, 4, 3, 128, keys, 4, p, p, 16, p, p, p, 100, p, 1 << 30, None)
     assert rc == csa.CSA_EUNSUPPORTED
     assert csa.csa_index_bwd_workspace(100, 128) == 100 * 128 * 8
+
+
+def test_mfma_probe_validation(csa):
+    lib = csa._lib
+    assert lib.csa_mfma_probe_flops(0, 2, 8) == 16 * 16 * 32 * 2 * 4 * 8 * 2 * 4
+    assert lib.csa_mfma_probe_flops(1, 1, 4) == 32 * 32 * 64 * 2 * 4 * 4 * 4
+    assert lib.csa_mfma_probe_flops(0, 1, 6) == -1
+    assert lib.csa_mfma_probe_flops(2, 1, 1) == -1
+    assert lib.csa_mfma_probe_flops(0, 0, 1) == -1
+    assert lib.csa_mfma_probe(2, 1, 4, None, 256, None) == -2
+    assert lib.csa_mfma_probe(0, 1, 4, None, 256, None) == -1
+    assert b"sink" in lib.csa_last_error()

@@ -1269,3 +1269,21 @@ def test_paged_index_keys_and_page_files(lib, dev, gen, orc, tmp_path):
     assert np.array_equal(sc2.cpu().numpy().view(np.uint32), ref[rows].view(np.uint32))
     assert np.array_equal(ix2.cpu().numpy(), ref_i[rows])
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.gpu
+def test_mfma_probe_runs():
+    """The matrix-core probe the benchmark uses for context: one small launch of each kind
+    completes, reports its flop count and writes a finite value per thread."""
+    import torch
+
+    import compressed_sparse_long_compress_amd as csa
+
+    sink = torch.full((8 * 256,), float("nan"), dtype=torch.float32, device="cuda")
+    assert csa.mfma_probe(0, 8, 16, sink) == 16 * 16 * 32 * 2 * 4 * 16 * 8 * 4
+    torch.cuda.synchronize()
+    assert torch.isfinite(sink).all()
+    sink.fill_(float("nan"))
+    assert csa.mfma_probe(1, 8, 16, sink) == 32 * 32 * 64 * 2 * 4 * 16 * 8 * 4
+    torch.cuda.synchronize()
+    assert torch.isfinite(sink).all()

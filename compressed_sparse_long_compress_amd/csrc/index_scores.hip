@@ -501,10 +501,12 @@ __global__ __launch_bounds__(256, gemm_min_blocks(HI, MODE)) void k_index_gemm(c
             for (int i = 0; i < NI; ++i)
                 cbu[at][i] = ((tq0 + at * QA + (HI == 8 ? i : 2 * i)) * (int64_t)gridDim.x + blockIdx.x) * ia.cap;
         const int64_t cg2 = (HI == 8 ? 2 : 1) * (int64_t)g2 * gridDim.x * ia.cap;
+        const int32_t c1_32 = (int32_t)c1;
         // kEmit: the candidates of query slot (at, i), both half-waves (every lane calls it)
         auto emit = [&](int at, int i, int64_t j, float v) {
-            const bool pass = nvq[at][i] >= 0 && j < c1 && j < nvq[at][i] && v >= tq[at][i];
-            const uint64_t mk = __ballot(pass);
+            // (columns < 2^31: 32-bit compares; a dead slot's count is -1)
+            const bool pass = (int32_t)j < c1_32 && (int32_t)j < nvq[at][i] && v >= tq[at][i];
+            const uint64_t mk = __builtin_amdgcn_ballot_w64(pass);
             if (mk == 0) return;
             const uint32_t lo = (uint32_t)mk, hi = (uint32_t)(mk >> 32);
             if (pass) {
@@ -512,8 +514,8 @@ __global__ __launch_bounds__(256, gemm_min_blocks(HI, MODE)) void k_index_gemm(c
                 if (sl < (uint32_t)ia.cap)
                     ia.cand[cbu[at][i] + cg2 + sl] = ((uint64_t)f32_order_key(v) << 32) | (uint32_t)~(uint32_t)j;
             }
-            ec[at][i][0] = __builtin_amdgcn_readfirstlane(ec[at][i][0] + (uint32_t)__popc(lo));
-            ec[at][i][1] = __builtin_amdgcn_readfirstlane(ec[at][i][1] + (uint32_t)__popc(hi));
+            ec[at][i][0] += (uint32_t)__builtin_popcount(lo);
+            ec[at][i][1] += (uint32_t)__builtin_popcount(hi);
         };
 
         // Key tiles of 32 columns: fragments of one tile, then per row tile two MFMAs and the

@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (scaled by a 256 MiB copy: fetch x2.0,
 # write x1.0; see profiles/csa_decode_1m_hbm_counters.md), valid for the kernel
 # source with this SHA-256 only.
-INDEX_TRAFFIC = {"sha256": "10e790318e3c527e99fb4ff21dfc6255cc7c53cfa88a321f69301154b1fd9c34", "bytes": 75746305}
+INDEX_TRAFFIC = {"sha256": "824834adfb747df9b4d9209436b4a815bb0115ec04f2da06644237b14222bc6a", "bytes": 75746284}
 
 
 def log(msg):

@@ -362,8 +362,10 @@ static int pages_copy(const char* fn, const csa_kv_t& kv, const csa_index_keys_t
     } arrs[5] = {{(char*)kv.nope, dn}, {(char*)kv.rope, 128}, {(char*)kv.scale, 4},
                  {(char*)keys.data, (size_t)d_i / 2}, {(char*)keys.scale, (size_t)d_i / 32}};
     const int na = d_i > 0 ? 5 : 3;
+    // every page number checked before the first copy, so a bad list enqueues nothing
+    for (int32_t i = 0; i < n_pages; ++i)
+        if (pages[i] < 0) return fail(CSA_EINVAL, "%s: negative page number at %d", fn, i);
     for (int32_t i = 0; i < n_pages; ++i) {
-        if (pages[i] < 0) return fail(CSA_EINVAL, "%s: negative page number", fn);
         char* h = host + per * (size_t)i;
         for (int a = 0; a < na; ++a) {
             const size_t bytes = arrs[a].row * (size_t)page;

@@ -439,7 +439,10 @@ int csa_mqa_bwd(const uint16_t* q, const int32_t* seq, const int64_t* pos, int64
  * after the other: nope [page][d-64], rope [page][64] bf16, scale [page] fp32,
  * then (d_i > 0) key data [page][d_i/2] and key scales [page][d_i/32];
  * csa_pages_bytes(page, d, d_i) bytes per page.  d_i = 0 moves entries only.
- *   pages      HOST array of n_pages physical page numbers
+ *   pages      HOST array of n_pages physical page numbers, each >= 0 and
+ *              within the arrays (the library cannot see their extent: that
+ *              bound is the caller's); all are checked to be >= 0 before
+ *              any copy is enqueued
  *   host       host buffer (pinned memory lets the copies run asynchronously)
  * The copies are enqueued on `stream`; the caller synchronises before it
  * reads (store) or reuses (load) the host buffer.  A load followed by a

@@ -202,3 +202,29 @@ def test_mfma_probe_validation(csa):
     assert lib.csa_mfma_probe(2, 1, 4, None, 256, None) == -2
     assert lib.csa_mfma_probe(0, 1, 4, None, 256, None) == -1
     assert b"sink" in lib.csa_last_error()
+
+
+def test_pages_copy_validation(csa):
+    """csa_pages_store / csa_pages_load refuse bad arguments before any copy is enqueued: a
+    negative page number anywhere in the list, a host buffer too small, a page size that is
+    not a power of two, index keys on another page size."""
+    L = csa._lib
+    p = ctypes.c_void_p(256)
+    kv = csa._Kv(256, 256, 256, 1024, None, 64)
+    keys = csa._IdxKeys(256, 256, 1024, None, 64)
+    per = L.csa_pages_bytes(64, 512, 128)
+    assert per == 64 * (448 + 128 + 4 + 64 + 4)
+    pages = (ctypes.c_int32 * 3)(0, 5, -1)
+    host = ctypes.create_string_buffer(3 * per)
+    rc = L.csa_pages_store(kv, keys, 512, 128, pages, 3, host, 3 * per, None)
+    assert rc == csa.CSA_EINVAL and b"negative page number at 2" in L.csa_last_error()
+    rc = L.csa_pages_load(kv, keys, 512, 128, pages, 3, host, 3 * per, None)
+    assert rc == csa.CSA_EINVAL and b"negative page" in L.csa_last_error()
+    ok_pages = (ctypes.c_int32 * 3)(0, 5, 1)
+    rc = L.csa_pages_store(kv, keys, 512, 128, ok_pages, 3, host, 3 * per - 1, None)
+    assert rc == csa.CSA_EWORKSPACE
+    rc = L.csa_pages_store(csa._Kv(256, 256, 256, 1024, None, 48), keys, 512, 128, ok_pages, 3, host, 3 * per, None)
+    assert rc == csa.CSA_EINVAL and b"power of two" in L.csa_last_error()
+    rc = L.csa_pages_store(kv, csa._IdxKeys(256, 256, 1024, None, 32), 512, 128, ok_pages, 3, host, 3 * per, None)
+    assert rc == csa.CSA_EINVAL and b"keys.page" in L.csa_last_error()
+    assert L.csa_pages_store(kv, keys, 512, 128, ok_pages, 0, host, 0, None) == 0

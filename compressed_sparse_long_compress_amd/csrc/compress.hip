@@ -28,7 +28,10 @@ __device__ __forceinline__ float f64_to_f32_odd(double d) {
     return f;
 }
 
-template <int D>
+// UN: token rows in flight per lane (8, or 32 for long blocks, whose merge would otherwise
+// wait on one memory round trip per 8 tokens).  Short blocks (m < 32) keep a small weight
+// buffer, so that LDS does not cap the waves per CU on the streaming shapes (m = 1, 4).
+template <int D, int UN>
 __global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ kv, const float* __restrict__ logits,
                                                   int64_t tok0, int64_t n_blk, int m, RopeTab rt, int64_t seq,
                                                   int64_t cap, const int32_t* __restrict__ pages, int pshift,
@@ -36,7 +39,8 @@ __global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ k
                                                   float* __restrict__ scale) {
     constexpr int DN = D - 64;
     constexpr int PER = D / 64;  // dims per lane (2 or 8)
-    __shared__ double wbuf[4][kMaxM];
+    constexpr int MAXM = UN >= 32 ? kMaxM : 32;
+    __shared__ double wbuf[4][MAXM];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t b = (int64_t)blockIdx.x * 4 + wv;
     if (b >= n_blk) return;
@@ -44,38 +48,56 @@ __global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ k
     const uint16_t* x = kv + b * m * (int64_t)D + lane * PER;
     double* wb = wbuf[wv];
 
+    // token rows i0 .. i0+UN-1 of the block into v (rows past the block's end load its last
+    // row, unused: no branch, so the loads stay in flight across what follows)
+    auto load_rows = [&](int i0, uint16_t (&v)[UN][PER]) {
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            const int64_t i = i0 + u < m ? i0 + u : m - 1;
+            if constexpr (PER == 8) {
+                *(v4i*)v[u] = *(const v4i*)(x + i * D);
+            } else {
+                uint32_t raw = *(const uint32_t*)(x + i * D);
+                v[u][0] = (uint16_t)raw;
+                v[u][1] = (uint16_t)(raw >> 16);
+            }
+        }
+    };
+    // the lane's first logit, then the first token rows, are requested before the weights are
+    // computed, so the two memory round trips overlap (loads return in order: the logit first)
+    const float lg0 = lg[lane < m ? lane : m - 1];
+    uint16_t v[UN][PER];
+    load_rows(0, v);
+
     // block softmax weights in fp64: exp terms by lanes, their sum in token order
-    double mx = -INFINITY;
-    for (int i = 0; i < m; ++i) mx = fmax(mx, (double)lg[i]);
-    for (int i = lane; i < m; i += 64) wb[i] = exp((double)lg[i] - mx);
+    double mx = lane < m ? (double)lg0 : -INFINITY;  // (a maximum: any order gives the same value)
+    if constexpr (UN >= 32)  // m < 32 otherwise
+        for (int i = lane + 64; i < m; i += 64) mx = fmax(mx, (double)lg[i]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+    if (lane < m) wb[lane] = exp((double)lg0 - mx);
+    if constexpr (UN >= 32)
+        for (int i = lane + 64; i < m; i += 64) wb[i] = exp((double)lg[i] - mx);
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     double z = 0.0;
     for (int i = 0; i < m; ++i) z = __dadd_rn(z, wb[i]);
+    // the normalised weights, each divided once (by the lane that owns it) instead of per lane
+    __builtin_amdgcn_wave_barrier();
+    for (int i = lane; i < m; i += 64) wb[i] = wb[i] / z;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
     // weighted merge in fp64, tokens in order, no fused multiply-add
     double c[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) c[e] = 0.0;
-    constexpr int UN = 8;  // token rows in flight per lane
     for (int i0 = 0; i0 < m; i0 += UN) {
-        uint16_t v[UN][PER];
+        if (i0 > 0) load_rows(i0, v);
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
             if (i0 + u < m) {
-                if constexpr (PER == 8) {
-                    *(v4i*)v[u] = *(const v4i*)(x + (int64_t)(i0 + u) * D);
-                } else {
-                    uint32_t raw = *(const uint32_t*)(x + (int64_t)(i0 + u) * D);
-                    v[u][0] = (uint16_t)raw;
-                    v[u][1] = (uint16_t)(raw >> 16);
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < UN; ++u) {
-            if (i0 + u < m) {
-                const double wi = wb[i0 + u] / z;
+                const double wi = wb[i0 + u];
 #pragma unroll
                 for (int e = 0; e < PER; ++e)
                     c[e] = __dadd_rn(c[e], __dmul_rn(wi, (double)bf16_bits_to_f32(v[u][e])));
@@ -87,17 +109,22 @@ __global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ k
     const int dim0 = lane * PER;
     const bool is_rope = dim0 >= DN;
 
-    // RoPE on the last 64 dims at the last covered token, fp64
-    if (is_rope) {
+    // RoPE on the last 64 dims at the last covered token, fp64.  Lane i < 32 evaluates the
+    // cosine and sine of frequency pair i (one fp64 sin / cos per lane, in parallel); the
+    // lanes holding the RoPE dims take theirs by shuffles.
+    {
         const double p = (double)((J + 1) * (int64_t)m - 1);
+        double cs_i = 1.0, sn_i = 0.0;
+        if (lane < 32) sincos(__dmul_rn(p, rt.theta[lane]), &sn_i, &cs_i);  // one shared range reduction
 #pragma unroll
         for (int e = 0; e < PER; e += 2) {
-            const double theta = rt.theta[(dim0 - DN + e) >> 1];
-            const double a = __dmul_rn(p, theta);
-            const double cs = cos(a), sn = sin(a);
-            const double x0 = c[e], x1 = c[e + 1];
-            c[e] = __dsub_rn(__dmul_rn(x0, cs), __dmul_rn(x1, sn));
-            c[e + 1] = __dadd_rn(__dmul_rn(x0, sn), __dmul_rn(x1, cs));
+            const int pair = is_rope ? (dim0 - DN + e) >> 1 : 0;
+            const double cs = __shfl(cs_i, pair), sn = __shfl(sn_i, pair);
+            if (is_rope) {
+                const double x0 = c[e], x1 = c[e + 1];
+                c[e] = __dsub_rn(__dmul_rn(x0, cs), __dmul_rn(x1, sn));
+                c[e + 1] = __dadd_rn(__dmul_rn(x0, sn), __dmul_rn(x1, cs));
+            }
         }
     }
 
@@ -327,12 +354,17 @@ hipError_t launch_compress(const uint16_t* kv, const float* logits, int64_t tok0
     const int64_t n_blk = n_tok / m;
     if (n_blk == 0) return hipSuccess;
     dim3 grid((unsigned)((n_blk + 3) / 4)), block(256);
-    if (d == 512)
-        hipLaunchKernelGGL(k_compress<512>, grid, block, 0, st, kv, logits, tok0, n_blk, m, rt, seq, out.cap, out.pages, out.pshift, nope,
-                           rope, scale);
-    else
-        hipLaunchKernelGGL(k_compress<128>, grid, block, 0, st, kv, logits, tok0, n_blk, m, rt, seq, out.cap, out.pages, out.pshift, nope,
-                           rope, scale);
+#define CSA_COMPRESS(D, UN)                                                                                         \
+    hipLaunchKernelGGL((k_compress<D, UN>), grid, block, 0, st, kv, logits, tok0, n_blk, m, rt, seq, out.cap, out.pages, \
+                       out.pshift, nope, rope, scale)
+    if (d == 512) {
+        if (m >= 32) CSA_COMPRESS(512, 32);
+        else CSA_COMPRESS(512, 8);
+    } else {
+        if (m >= 32) CSA_COMPRESS(128, 32);
+        else CSA_COMPRESS(128, 8);
+    }
+#undef CSA_COMPRESS
     return hipGetLastError();
 }
 

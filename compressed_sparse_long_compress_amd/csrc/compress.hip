@@ -209,16 +209,20 @@ __global__ __launch_bounds__(256) void k_compress_ch(const uint16_t* __restrict_
 
     const int64_t J = tok0 / m + b;
     const bool is_rope = dim0 >= DN;
-    if (is_rope) {
+    {
+        // one frequency pair's fp64 sincos per lane below 32; the RoPE lanes take theirs by shuffles
         const double p = (double)((J + 1) * (int64_t)m - 1);
+        double cs_i = 1.0, sn_i = 0.0;
+        if (lane < 32) sincos(__dmul_rn(p, rt.theta[lane]), &sn_i, &cs_i);
 #pragma unroll
         for (int e = 0; e < PER; e += 2) {
-            const double theta = rt.theta[(dim0 - DN + e) >> 1];
-            const double a = __dmul_rn(p, theta);
-            const double cs = cos(a), sn = sin(a);
-            const double x0 = c[e], x1 = c[e + 1];
-            c[e] = __dsub_rn(__dmul_rn(x0, cs), __dmul_rn(x1, sn));
-            c[e + 1] = __dadd_rn(__dmul_rn(x0, sn), __dmul_rn(x1, cs));
+            const int pair = is_rope ? (dim0 - DN + e) >> 1 : 0;
+            const double cs = __shfl(cs_i, pair), sn = __shfl(sn_i, pair);
+            if (is_rope) {
+                const double x0 = c[e], x1 = c[e + 1];
+                c[e] = __dsub_rn(__dmul_rn(x0, cs), __dmul_rn(x1, sn));
+                c[e + 1] = __dadd_rn(__dmul_rn(x0, sn), __dmul_rn(x1, cs));
+            }
         }
     }
     double am = 0.0;
@@ -278,13 +282,20 @@ __global__ __launch_bounds__(256) void k_compress_ikey(const uint16_t* __restric
     if (b >= n_blk) return;
     const float* lg = logits + b * m;
     double* wb = wbuf[wv];
-    double mx = -INFINITY;
-    for (int i = 0; i < m; ++i) mx = fmax(mx, (double)lg[i]);
+    double mx = -INFINITY;  // (a maximum: any order gives the same value)
+    for (int i = lane; i < m; i += 64) mx = fmax(mx, (double)lg[i]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
     for (int i = lane; i < m; i += 64) wb[i] = exp((double)lg[i] - mx);
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     double z = 0.0;
     for (int i = 0; i < m; ++i) z = __dadd_rn(z, wb[i]);
+    // the normalised weights, each divided once (by the lane that owns it)
+    __builtin_amdgcn_wave_barrier();
+    for (int i = lane; i < m; i += 64) wb[i] = wb[i] / z;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
     const bool live = 2 * lane < DI;
     double c0 = 0.0, c1 = 0.0;
@@ -292,7 +303,7 @@ __global__ __launch_bounds__(256) void k_compress_ikey(const uint16_t* __restric
         const uint16_t* x = k + b * m * (int64_t)DI + 2 * lane;
         for (int i = 0; i < m; ++i) {
             const uint32_t raw = *(const uint32_t*)(x + (int64_t)i * DI);
-            const double wi = wb[i] / z;
+            const double wi = wb[i];
             c0 = __dadd_rn(c0, __dmul_rn(wi, (double)bf16_bits_to_f32((uint16_t)raw)));
             c1 = __dadd_rn(c1, __dmul_rn(wi, (double)bf16_bits_to_f32((uint16_t)(raw >> 16))));
         }

@@ -793,7 +793,9 @@ static ItkPlan itk_plan(int64_t T, int64_t n_cols, int k, int h_i) {
         if (c < 1024) c = 1024;
         if (c > p.chunk_e) c = p.chunk_e;
         p.cap = (int)c;
-        p.lcap = p.target_far <= 2048 ? 4096 : 8192;
+        // candidates held in LDS: 3,072 leaves room for three picking workgroups per CU (the
+        // count sits within a few sd of target_far; a row beyond the space falls back)
+        p.lcap = p.target_far + 8 * sd <= 3072 ? 3072 : (p.target_far <= 2048 ? 4096 : 8192);
     }
     const int G = (int)(T < kItkFbGroups ? T : kItkFbGroups);
     p.off_samp = 0;
@@ -1105,7 +1107,10 @@ hipError_t launch_index_topk(const uint8_t* q, const uint8_t* q_scale, const flo
 #undef CSA_TAU
     }
     indexer(kEmit);
-    if (p.lcap == 4096)
+    if (p.lcap == 3072)
+        hipLaunchKernelGGL((k_itk_pick<512, 3072, 2048>), dim3((unsigned)T), dim3(512), 0, st, ia.cnt, ia.cand, tau,
+                           p.S, p.cap, pos, m, n_cols, k, idx, fb);
+    else if (p.lcap == 4096)
         hipLaunchKernelGGL((k_itk_pick<512, 4096, 2048>), dim3((unsigned)T), dim3(512), 0, st, ia.cnt, ia.cand, tau,
                            p.S, p.cap, pos, m, n_cols, k, idx, fb);
     else

@@ -360,7 +360,7 @@ __device__ void hist_descend(ForEach for_each, uint32_t lo, uint32_t hi, int nee
 // up to a power of two (sorted by a bitonic network).  h: 4096 words, zero;
 // lctr[0..1] zero; tie: kTieLds entries; a barrier passed since all were set.
 template <int NT>
-__device__ void pick_candidates(const uint64_t* cl, int n_cand, uint32_t lo, uint32_t hi, int k, int32_t* out,
+__device__ __forceinline__ void pick_candidates(const uint64_t* cl, int n_cand, uint32_t lo, uint32_t hi, int k, int32_t* out,
                                 uint32_t* bm, bool use_bm, int perw, uint32_t* h, uint64_t* tie, int* wsum, int* bc,
                                 uint32_t* lctr) {
     const int tid = threadIdx.x;

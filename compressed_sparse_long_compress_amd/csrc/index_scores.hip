@@ -1097,6 +1097,7 @@ hipError_t launch_index_topk(const uint8_t* q, const uint8_t* q_scale, const flo
                        k, p.D, p.F, p.target_far, tau, cr, fb)
         if (nt == 256) {
             if (per <= 8) CSA_TAU(256, 8);
+            else if (per <= 16) CSA_TAU(256, 16);  // (the chunked-prefill shape: fewer registers, more waves)
             else if (per <= 24) CSA_TAU(256, 24);
             else CSA_TAU(256, 0);
         } else {

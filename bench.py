@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (scaled by a 256 MiB copy: fetch x2.0,
 # write x1.0; see profiles/csa_decode_1m_hbm_counters.md), valid for the kernel
 # source with this SHA-256 only.
-INDEX_TRAFFIC = {"sha256": "824834adfb747df9b4d9209436b4a815bb0115ec04f2da06644237b14222bc6a", "bytes": 75746284}
+INDEX_TRAFFIC = {"sha256": "b18be7603c59c00594d3057c40396d74df1b4e5c589746bd8420d3e41bffbdee", "bytes": 75746141}
 
 
 def log(msg):

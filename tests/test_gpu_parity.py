@@ -96,6 +96,9 @@ def compare_entries(orc, got, ref, what):
     (512, 1, 130944, 256, 8320),
     (128, 1, 0, 300, 300),
     (512, 4, 131072, 64, 40),    # slots wrap: entry J at J % cap
+    (128, 31, 0, 310, 16),       # the longest block of the short-block kernel (31 <= 32 weights)
+    (512, 33, 66, 330, 16),      # long-block kernel: a group of 32 rows, then a ragged one
+    (512, 200, 0, 1000, 8),      # more logits than lanes: the second logit pass
 ])
 def test_compress(lib, dev, gen, orc, d, m, tok0, n_tok, cap):
     import torch
@@ -143,6 +146,7 @@ def test_compress_channel(lib, dev, gen, orc, d, m, tok0, n_tok, cap):
     (64, 4, 12, 400, 200),
     (128, 1, 5, 77, 100),
     (128, 128, 0, 1024, 8),
+    (64, 100, 0, 500, 8),        # more logits than lanes
 ])
 def test_compress_index_keys(lib, dev, gen, orc, d_i, m, tok0, n_tok, cap):
     """Raw key tokens -> MXFP4 index keys: codes and scales equal the oracle's bit for bit

@@ -1044,7 +1044,8 @@ def test_debug_check_rejects_rope_beyond_fp16(lib, dev, gen, orc, monkeypatch):
     (300, 8, 128, 3000, 1, 4, 3000, 1024, "prefill", 0.0),
     (200, 8, 128, 9000, 3, 4, 9000, 256, "mixed", 0.0),       # several sequences in a tile
     (130, 8, 128, 40000, 1, 4, 40000, 1024, "prefill", 0.05),
-    (100, 8, 64, 5000, 1, 4, 5000, 2048, "prefill", 0.0),
+    (100, 8, 64, 5000, 1, 4, 5000, 2048, "prefill", 0.0),    # 8,192 candidates in LDS
+    (130, 8, 128, 12000, 1, 4, 12000, 1100, "prefill", 0.02), # 4,096 (k = 1024 and below: 3,072)
 ])
 def test_index_topk_bit_exact(lib, dev, gen, orc, T, h_i, d_i, N, B, m, n_cols, k, mode, plant):
     import torch

@@ -177,6 +177,28 @@ class DecodeSet:
         torch.cuda.synchronize()
         return want
 
+    def step_median(self, n):
+        """Median duration of one step: one HIP graph per replica set, each holding a single
+        step, replayed n times in rotation with an event pair around every replay."""
+        import torch
+
+        graphs = []
+        for r in range(self.replicas):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(r)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record()
+            graphs[i % self.replicas].replay()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) / 1e3 for a, b in ev)
+        del graphs
+        return t[n // 2]
+
     def check(self, want, what):
         import torch
 
@@ -770,6 +792,8 @@ def main():
     log("per-call ms: " + ", ".join(f"{k} {v * 1e3:.4f}" for k, v in kern.items()))
     idx_sec = time_index_launches(ds, args.steps)
     log(f"indexer kernel, back-to-back launches: {idx_sec * 1e6:.2f} us")
+    med_sec = ds.step_median(max(args.steps, 100))
+    log(f"one-step graphs, median of {max(args.steps, 100)} replays: {med_sec * 1e3:.4f} ms/step")
 
     B, N, h_i, d_i, k, W, H, d = (wl[x] for x in ("B", "N", "h_i", "d_i", "k", "W", "H", "d"))
     qps = B * args.steps / sec
@@ -793,6 +817,7 @@ def main():
                    "k": k, "window": W, "heads": H, "head_dim": d, "indexer": f"{h_i}x{d_i} mxfp4",
                    "replicas": ds.replicas, "timing": "the timed steps replayed as one HIP graph (replica sets rotated)"},
         "eager_ms_per_step": eager_sec / args.steps * 1e3,
+        "median_ms_per_step": med_sec * 1e3,  # one step per graph, events around each replay
         "step_bytes": step_bytes,
         "step_hbm_gbs": step_bytes * args.steps / sec / 1e9,
         "step_hbm_frac": step_bytes * args.steps / sec / 1e9 / HBM_PEAK_GBS,

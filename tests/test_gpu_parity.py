@@ -1188,6 +1188,60 @@ def test_index_bwd(lib, dev, gen, orc, T, h_i, d_i, N, B, m, n_sel, layout):
 # --------------------------------------------------------------------------
 # paged index keys, and compressed pages stored on the host / on disk and loaded back
 # --------------------------------------------------------------------------
+@pytest.mark.parametrize("page", [64, 1024])
+def test_paged_index_keys_all_paths(lib, dev, gen, orc, page):
+    """Index keys in a paged layout (pages in a shuffled order, spare pages unused) read by
+    every indexer path.  The prefill matrix-core kernel writes score rows, and the fused
+    selection runs its sample and emit passes, over two sequences in one batch.  The grouped
+    multi-token kernel also reads them.  Scores and indices equal the oracle's on the logical
+    keys bit for bit.  The indexer backward equals the contiguous layout's bit for bit, its key
+    gradients landing on the physical rows."""
+    import torch
+
+    _say(f"paged index keys, every indexer path, page {page}")
+    B, m, d_i, h_i, N, k = 2, 4, 128, 8, 4096, 256
+    npp = N // page
+    rng = np.random.default_rng(page)
+    perm = rng.permutation(B * npp + 2)[: B * npp].astype(np.int32)
+    n_phys = (B * npp + 2) * page
+    phys = (perm.reshape(B, npp)[:, :, None] * page + np.arange(page)[None, None, :]).reshape(-1)  # logical -> physical
+    # the prefill rows: sequence 0, then sequence 1 (both inside one 64-query tile at the seam)
+    T = 130
+    seq = (np.arange(T) >= 65).astype(np.int32)
+    pos = np.concatenate([np.sort(rng.integers(m * 8, m * N, size=65)), np.sort(rng.integers(m * 8, m * N, size=T - 65))])
+    qd, qs, w, seq, pos, kd, ks = _index_case(gen, 870 + page, T, h_i, d_i, N, B, pos, seq, plant=0.02)
+    assert orc.index_exact_witness(qd, qs, w, seq, pos, kd, ks, N, m, N) < 24
+    pd = np.zeros((n_phys, d_i // 2), np.uint8)
+    ps = np.full((n_phys, d_i // 32), 127, np.uint8)
+    pd[phys], ps[phys] = kd, ks
+    keys_p = lib.IndexKeys(dev.t(pd), dev.t(ps), N, pages=torch.tensor(perm.reshape(B, npp), device="cuda"), page=page)
+    keys_c = dev.index_keys((kd, ks), N)
+    ref = orc.index_scores(qd, qs, w, seq, pos, kd, ks, N, m, N).astype(np.float32)
+    ref_i = orc.topk(ref, pos, m, k)
+    tq, tqs, tw, tseq, tpos = dev.t(qd), dev.t(qs), dev.t(w), dev.t(seq), dev.t(pos)
+    sc = lib.csa_index_scores(tq, tqs, tw, tseq, tpos, keys_p, m, N)
+    ix = lib.csa_index_topk(tq, tqs, tw, tseq, tpos, keys_p, m, N, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), ref.view(np.uint32)), "paged prefill scores"
+    assert np.array_equal(ix.cpu().numpy(), ref_i), "paged prefill fused selection"
+    # grouped multi-token rows: two rows per sequence share each key stream
+    rows = np.array([64, 63, 129, 128])  # near the ends of the two sequences
+    g_args = [dev.t(np.ascontiguousarray(a[rows])) for a in (qd, qs, w, seq, pos)]
+    gsc = lib.csa_index_scores_grouped(*g_args, keys_p, m, N, 2)
+    torch.cuda.synchronize()
+    assert np.array_equal(gsc.cpu().numpy().view(np.uint32), ref[rows].view(np.uint32)), "paged grouped scores"
+    # backward: paged against contiguous, key gradients compared through the page table
+    G = gen.normal_f32(872 + page, 1, (T, k))
+    dq_p, dw_p, dk_p = lib.csa_index_bwd(tq, tqs, tw, tseq, tpos, keys_p, m, ix, dev.t(G), key_rows=n_phys)
+    dq_c, dw_c, dk_c = lib.csa_index_bwd(tq, tqs, tw, tseq, tpos, keys_c, m, ix, dev.t(G))
+    torch.cuda.synchronize()
+    assert torch.equal(dq_p, dq_c) and torch.equal(dw_p, dw_c), "paged backward: dq / dw"
+    dk_p = dk_p.cpu().numpy()
+    assert np.array_equal(dk_p[phys], dk_c.cpu().numpy()), "paged backward: key gradients"
+    spare = np.setdiff1d(np.arange(n_phys), phys)
+    assert not dk_p[spare].any(), "gradient on a spare page"
+
+
 def test_paged_index_keys_and_page_files(lib, dev, gen, orc, tmp_path):
     """Index keys compressed into a paged layout (pages in a shuffled order, shared page table with
     the compressed entries) equal the oracle's keys; the indexer and the fused selection read them

@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define CSA_VERSION 108
+#define CSA_VERSION 109
 
 enum {
     CSA_OK = 0,

@@ -548,6 +548,41 @@ def cpu_model():
     return platform.processor() or "unknown"
 
 
+ORACLE_SMALL_ONE_THREAD = r"""
+import sys, time
+sys.path.insert(0, sys.argv[1])
+import numpy as np
+import oracle
+from gen import configs
+wl = configs.named("prefill_small")
+m, k, W = wl["m"], wl["k"], wl["W"]
+t0 = time.perf_counter()
+comp = oracle.compress(wl["kv"], wl["logits"], 0, m)
+win = oracle.compress(wl["kv"], wl["logits"], 0, 1)
+hca = oracle.compress(wl["kv"], wl["logits"], 0, wl["m_hca"])
+sc = oracle.index_scores(wl["iq"][0], wl["iq"][1], wl["w"], wl["seq"], wl["pos"], wl["keys"][0], wl["keys"][1],
+                         wl["N"], m, wl["n_cols"]).astype(np.float32)
+idx = oracle.topk(sc, wl["pos"], m, k)
+oracle.attend(wl["q"], wl["seq"], wl["pos"], comp, wl["comp_cap"], win, wl["T"], W, m, wl["sm_scale"], idx=idx)
+oracle.attend(wl["q"], wl["seq"], wl["pos"], hca, wl["hca_cap"], win, wl["T"], W, wl["m_hca"], wl["sm_scale"])
+print(time.perf_counter() - t0)
+"""
+
+
+def oracle_small_one_thread():
+    """Seconds the fp64 oracle takes, on one thread (a child process with OMP_NUM_THREADS=1),
+    for the whole small prefill case: compress (m=4, m=1, m'=128), index scores, top-k and
+    both attentions over 2,048 query rows."""
+    import subprocess
+
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", ORACLE_SMALL_ONE_THREAD, ROOT], env=env, capture_output=True, text=True,
+                       timeout=600)
+    if r.returncode != 0:
+        raise RuntimeError("single-thread oracle run failed: " + r.stderr[-500:])
+    return float(r.stdout.strip().splitlines()[-1])
+
+
 def cpu_baseline(wl):
     """The fp64 oracle (as written, untuned) on the same batch: index scores,
     top-k and sparse attention for every query row of the workload, repeated
@@ -572,6 +607,7 @@ def cpu_baseline(wl):
     threads = int(os.environ.get("OMP_NUM_THREADS", ncpu))
     return {"value": T * reps / dt, "unit": "queries/s", "cores": min(threads, ncpu), "host_cpus": ncpu,
             "cpu_model": cpu_model(), "kind": "oracle",
+            "small_prefill_one_thread_s": oracle_small_one_thread(),
             "sample": f"all {T} query rows of the batch (full 1M-context rows), {reps} passes, {dt:.1f} s wall; "
                       f"OpenMP threads {min(threads, ncpu)} of {ncpu} host CPUs"}
 

@@ -721,7 +721,26 @@ def secondary(steps, warmup):
     res = {}
     for name in ("csa_decode_1m_mtp2", "csa_decode_64k", "hca_decode_1m"):
         wl, ds, sec = run_workload(name, steps, warmup)
-        res[name] = {"queries_per_s": wl["T"] * steps / sec, "ms_per_step": sec / steps * 1e3}
+        T, N, W, H, d = (wl[x] for x in ("T", "N", "W", "H", "d"))
+        entry = (d - 64) + 64 * 2 + 4
+        if wl["kind"] == "hca_decode":
+            # every visible entry and the window per query, the bf16 query and fp32 output; 4 d flop
+            # per (query, head, key)
+            step_bytes = T * ((N + W) * entry + H * d * 2 + H * d * 4)
+            flops = T * H * (N + W) * 4 * d
+        else:
+            # the keys once per sequence (rows of a sequence share them), each row's query, gathered
+            # entries, query and output
+            B, h_i, d_i, k = wl["B"], wl["h_i"], wl["d_i"], wl["k"]
+            key = d_i // 2 + d_i // 32
+            step_bytes = B * N * key + T * (h_i * (key + 4) + (k + W) * entry + H * d * 2 + H * d * 4)
+            flops = None
+        gbs = step_bytes * steps / sec / 1e9
+        res[name] = {"queries_per_s": T * steps / sec, "ms_per_step": sec / steps * 1e3, "step_bytes": step_bytes,
+                     "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+        if flops is not None:
+            tf = flops * steps / sec / 1e12
+            res[name].update({"mfma_tflops": tf, "mfma_frac": tf / FP16_PEAK_TFLOPS})
         del ds
     return res
 

@@ -229,10 +229,11 @@ class PrefillSet:
         self.win_h = csa.KvCache.empty(1, wl["win_cap"], d)
         self.kv, self.lg = dev.bf16(wl["kv"]), dev.t(wl["logits"])
         self.kvh, self.lgh = dev.bf16(wl["kv_hca"]), dev.t(wl["logits_hca"])
-        csa.csa_compress(self.kv[:L0], self.lg[:L0], 0, m, 0, self.comp)
-        csa.csa_compress(self.kvh[:L0], self.lgh[:L0], 0, mh, 0, self.hca)
-        csa.csa_compress(self.kv[L0 - W:L0], self.lg[L0 - W:L0], L0 - W, 1, 0, self.win)
-        csa.csa_compress(self.kvh[L0 - W:L0], self.lgh[L0 - W:L0], L0 - W, 1, 0, self.win_h)
+        if L0 > 0:  # the older context (none for the small prefill case)
+            csa.csa_compress(self.kv[:L0], self.lg[:L0], 0, m, 0, self.comp)
+            csa.csa_compress(self.kvh[:L0], self.lgh[:L0], 0, mh, 0, self.hca)
+            csa.csa_compress(self.kv[L0 - W:L0], self.lg[L0 - W:L0], L0 - W, 1, 0, self.win)
+            csa.csa_compress(self.kvh[L0 - W:L0], self.lgh[L0 - W:L0], L0 - W, 1, 0, self.win_h)
         self.seq, self.pos = dev.t(wl["seq"]), dev.t(wl["pos"])
         self.iq, self.iqs, self.w = dev.t(wl["iq"][0]), dev.t(wl["iq"][1]), dev.t(wl["w"])
         self.keys = dev.index_keys(wl["keys"], wl["N"])
@@ -754,7 +755,7 @@ def main():
     ap.add_argument("--workload", default="csa_decode_1m",
                     choices=["csa_decode_1m", "csa_decode_1m_mtp2", "csa_decode_1m_paged", "csa_decode_64k",
                              "prefill_chunk_bwd",
-                             "hca_decode_1m", "prefill_chunk", "compress_chunk"],
+                             "hca_decode_1m", "prefill_chunk", "prefill_small", "compress_chunk"],
                     help="time only this workload and print its line (profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill object")
@@ -814,7 +815,7 @@ def main():
         return
     if args.workload != "csa_decode_1m":
         wl, ds, sec = run_workload(args.workload, args.steps, args.warmup)
-        unit = "tokens/s" if args.workload == "prefill_chunk" else "queries/s"
+        unit = "tokens/s" if args.workload.startswith("prefill") else "queries/s"
         print(json.dumps({"workload": args.workload, "value": wl["T"] * args.steps / sec, "unit": unit,
                           "ms_per_step": sec / args.steps * 1e3, "steps": args.steps}))
         return

@@ -30,3 +30,15 @@ def test_index_excess_bytes():
     # the fp32 score row and one 4-byte summary key per 32 columns
     assert bench.index_excess_bytes_per_query(262144) == 262144 * 4 + 8192 * 4
     assert bench.index_excess_bytes_per_query(33) == 33 * 4 + 2 * 4
+
+
+def test_more_than_one_gpu_is_refused():
+    # the benchmark measures one GPU; asking for more exits with a message and status 2 before
+    # anything touches a device
+    import subprocess
+
+    for argv, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + argv, capture_output=True, text=True,
+                           timeout=300, env=dict(os.environ, **env))
+        assert r.returncode == 2
+        assert "one GPU" in r.stderr and r.stdout == ""
